@@ -1,0 +1,14 @@
+"""fp64 CPU oracle for varlen FlashAttention forward/backward.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
+CPU-baseline leg of bench.py, never by the product library.  It shares no code
+with the HIP path.  Parity status of each function is recorded in the design
+notes; every function here is pinned by CPU tests against closed forms,
+library routines or finite differences, except the two conventions the pages
+leave open (keep-mask bit order, band alignment when Lq != Lkv), which are
+"parity unpinned" by the pages and only checked for self-consistency.
+"""
+from .attention import (INT_MAX_TOKENS, allowed, alibi_pse, keep_bits, forward, backward,
+                        probabilities)
+
+__all__ = ["INT_MAX_TOKENS", "allowed", "alibi_pse", "keep_bits", "forward", "backward", "probabilities"]

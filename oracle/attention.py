@@ -1,0 +1,223 @@
+"""Plain fp64 CPU oracle for training-time varlen (TND) FlashAttention.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path imports this module:
+only tests/, __graft_entry__.smoke() and bench.py's cpu_baseline leg use it.
+It shares no code with the HIP library and imports nothing from it.
+
+What it computes follows the Ascend CANN pages:
+  * aclnnFlashAttentionUnpaddingScoreGrad, section "Function / Formula":
+    forward S = Mask(scaled QK^T + pse), P = Dropout(Softmax(S), keep_prob),
+    Y = P V; backward dV = P^T dY, dQ = dS K * scale, dK = dS^T Q * scale.
+  * aclnnFlashAttentionScoreV2, section "Formula" (pseType other than 1):
+    S = scale * (Q K^T) + pse, i.e. the bias is added after scaling.
+  * aclnnFlashAttentionUnpaddingScoreGradV5, sink formulas: the running max
+    includes the sink logit, the softmax denominator gains exp(sink - m), and
+    dSink is a reduction of -P*dP*SimpleSoftmax(sink, max, sum).
+  * aclnnFlashAttentionUnpaddingScoreGrad, sparseMode list: 0 no mask,
+    2 leftUpCausal, 3 rightDownCausal, 4 band between preTokens/nextTokens.
+
+Readings taken where the pages are silent (each is listed with its reason in
+the design notes):
+  * dS is the softmax Jacobian applied through dropout:
+    dS = P * (dP - rowsum(P * dP)), dP = (dY V^T) * z / keep_prob.
+  * Dropout is inverted dropout: P~ = P * z / keep_prob; softmax max/sum are
+    taken before dropout.  Keep bits: one flat stream over batch, query head,
+    query row, key (the page's size formula), LSB first in each byte.
+  * "scale" replaces 1/sqrt(d) everywhere (scaleValue is "the Muls scalar").
+  * ALiBi (pseType 2, slopes per query head): pse = -slope_h * (i - j) with
+    i, j local to the sequence.
+  * The sink logit is compared with the scaled, biased logits and is not
+    itself scaled.
+  * GQA: query head h uses kv head h // (Nq / Nkv).
+  * Rows with no allowed key and no sink: O = 0, m = -inf, l = 0, dQ = 0.
+  * Band (mode 4) and rightDownCausal (mode 3) align on the bottom-right
+    corner (delta = Lkv - Lq); leftUpCausal (mode 2) on the top-left.
+  * softmax max/sum are per (row, head) fp32 in natural-log units; the
+    page's trailing x8 replication is dropped.
+
+Everything is fp64 numpy; S and P are materialised per (sequence, head).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+INT_MAX_TOKENS = 2147483647
+
+
+def allowed(lq: int, lkv: int, sparse_mode: int, pre_tokens: int = INT_MAX_TOKENS,
+            next_tokens: int = INT_MAX_TOKENS) -> np.ndarray:
+    """Boolean [lq, lkv]: True where query row i may attend key j (sparseMode list)."""
+    i = np.arange(lq, dtype=np.int64)[:, None]
+    j = np.arange(lkv, dtype=np.int64)[None, :]
+    delta = lkv - lq
+    if sparse_mode == 0:
+        return np.ones((lq, lkv), dtype=bool)
+    if sparse_mode == 2:            # leftUpCausal: lower triangle from the top-left corner
+        return j <= i
+    if sparse_mode == 3:            # rightDownCausal: lower triangle from the bottom-right corner
+        return j <= i + delta
+    if sparse_mode == 4:            # band: preTokens to the left, nextTokens to the right
+        return (j >= i + delta - pre_tokens) & (j <= i + delta + next_tokens)
+    raise ValueError(f"sparse_mode {sparse_mode} not covered")
+
+
+def alibi_pse(lq: int, lkv: int, slope: float) -> np.ndarray:
+    """pseType 2 bias for one head: -slope * (i - j), local row/key indices."""
+    i = np.arange(lq, dtype=np.float64)[:, None]
+    j = np.arange(lkv, dtype=np.float64)[None, :]
+    return -float(slope) * (i - j)
+
+
+def keep_bits(drop_mask: np.ndarray, bit_base: int, lq: int, lkv: int) -> np.ndarray:
+    """Keep bits z[i, j] for one (sequence, head) block starting at bit `bit_base`
+    of the packed mask; bit n lives in byte n // 8 at position n % 8 (LSB first)."""
+    idx = bit_base + np.arange(lq * lkv, dtype=np.int64)
+    byte = drop_mask[idx >> 3].astype(np.int64)
+    return ((byte >> (idx & 7)) & 1).astype(bool).reshape(lq, lkv)
+
+
+class _Problem:
+    """Inputs of one call, upcast to fp64, with the per-sequence bookkeeping."""
+
+    def __init__(self, q, k, v, cu_q, cu_kv, head_num, kv_heads, scale, keep_prob, sparse_mode,
+                 pre_tokens, next_tokens, drop_mask, alibi_slopes, sink):
+        self.q = np.asarray(q, dtype=np.float64)
+        self.k = np.asarray(k, dtype=np.float64)
+        self.v = np.asarray(v, dtype=np.float64)
+        self.cu_q = np.asarray(cu_q, dtype=np.int64)
+        self.cu_kv = np.asarray(cu_kv, dtype=np.int64)
+        self.nq = int(head_num)
+        self.nkv = int(kv_heads)
+        if self.nq % self.nkv != 0:
+            raise ValueError("Nq must be a multiple of Nkv")
+        self.group = self.nq // self.nkv
+        self.scale = float(scale)
+        self.keep = float(keep_prob)
+        self.mode = int(sparse_mode)
+        self.pre = int(pre_tokens)
+        self.next = int(next_tokens)
+        self.drop_mask = None if drop_mask is None else np.asarray(drop_mask, dtype=np.uint8)
+        self.slopes = None if alibi_slopes is None else np.asarray(alibi_slopes, dtype=np.float32).astype(np.float64)
+        self.sink = None if sink is None else np.asarray(sink, dtype=np.float32).astype(np.float64)
+        self.batch = len(self.cu_q) - 1
+        self.lens_q = np.diff(self.cu_q)
+        self.lens_kv = np.diff(self.cu_kv)
+        # start bit of each sequence's block in the packed keep mask
+        self.bit_base = np.concatenate([[0], np.cumsum(self.nq * self.lens_q * self.lens_kv)]).astype(np.int64)
+
+    def probs(self, b: int, h: int):
+        """S, P (pre-dropout), P~ (post-dropout), m, l, p_sink for sequence b, query head h."""
+        q0, q1 = self.cu_q[b], self.cu_q[b + 1]
+        k0, k1 = self.cu_kv[b], self.cu_kv[b + 1]
+        lq, lkv = int(q1 - q0), int(k1 - k0)
+        g = h // self.group
+        qb = self.q[q0:q1, h, :]
+        kb = self.k[k0:k1, g, :]
+        s = self.scale * (qb @ kb.T)
+        if self.slopes is not None:
+            s = s + alibi_pse(lq, lkv, self.slopes[h])
+        ok = allowed(lq, lkv, self.mode, self.pre, self.next)
+        s = np.where(ok, s, -np.inf)
+        m = s.max(axis=1) if lkv > 0 else np.full(lq, -np.inf)
+        if self.sink is not None:
+            m = np.maximum(m, self.sink[h])
+        finite = np.isfinite(m)
+        e = np.where(ok & finite[:, None], np.exp(s - np.where(finite, m, 0.0)[:, None]), 0.0)
+        l = e.sum(axis=1)
+        p_sink = np.zeros(lq)
+        if self.sink is not None:
+            es = np.exp(self.sink[h] - m)
+            l = l + es
+        nz = l > 0
+        p = np.where(nz[:, None], e / np.where(nz, l, 1.0)[:, None], 0.0)
+        if self.sink is not None:
+            p_sink = np.where(nz, np.exp(self.sink[h] - m) / np.where(nz, l, 1.0), 0.0)
+        if self.keep < 1.0:
+            z = keep_bits(self.drop_mask, int(self.bit_base[b] + h * lq * lkv), lq, lkv)
+            pt = p * z / self.keep
+        else:
+            z = None
+            pt = p
+        return dict(s=s, p=p, pt=pt, z=z, m=m, l=l, p_sink=p_sink, lq=lq, lkv=lkv,
+                    q0=q0, q1=q1, k0=k0, k1=k1, g=g)
+
+
+def _problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob=1.0,
+             sparse_mode=0, pre_tokens=INT_MAX_TOKENS, next_tokens=INT_MAX_TOKENS, drop_mask=None,
+             alibi_slopes=None, sink=None):
+    return _Problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob,
+                    sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink)
+
+
+def _selected(batches, n):
+    return range(n) if batches is None else list(batches)
+
+
+def forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob=1.0,
+            sparse_mode=0, pre_tokens=INT_MAX_TOKENS, next_tokens=INT_MAX_TOKENS, drop_mask=None,
+            alibi_slopes=None, sink=None, batches=None):
+    """Attention forward.  Returns O [T_q, Nq, D], softmax max m [T_q, Nq] and
+    softmax sum l [T_q, Nq] (fp64).  With `batches`, only those sequences are
+    computed and every other row is NaN."""
+    pr = _problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob,
+                  sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink)
+    tq, d = pr.q.shape[0], pr.v.shape[2]
+    out = np.full((tq, pr.nq, d), np.nan)
+    mx = np.full((tq, pr.nq), np.nan)
+    sm = np.full((tq, pr.nq), np.nan)
+    for b in _selected(batches, pr.batch):
+        for h in range(pr.nq):
+            st = pr.probs(b, h)
+            out[st["q0"]:st["q1"], h, :] = st["pt"] @ pr.v[st["k0"]:st["k1"], st["g"], :]
+            mx[st["q0"]:st["q1"], h] = st["m"]
+            sm[st["q0"]:st["q1"], h] = st["l"]
+    return out, mx, sm
+
+
+def backward(q, k, v, dy, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob=1.0,
+             sparse_mode=0, pre_tokens=INT_MAX_TOKENS, next_tokens=INT_MAX_TOKENS, drop_mask=None,
+             alibi_slopes=None, sink=None, batches=None):
+    """Attention backward.  Returns dQ [T_q, Nq, D], dK, dV [T_kv, Nkv, D] and
+    dSink [Nq] (None without a sink).  With `batches`, only those sequences
+    contribute (rows/keys of other sequences are NaN; dSink sums the chosen ones)."""
+    pr = _problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob,
+                  sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink)
+    dy = np.asarray(dy, dtype=np.float64)
+    dq = np.full(pr.q.shape, np.nan)
+    dk = np.full(pr.k.shape, np.nan)
+    dv = np.full(pr.v.shape, np.nan)
+    dsink = np.zeros(pr.nq) if pr.sink is not None else None
+    for b in _selected(batches, pr.batch):
+        q0, q1, k0, k1 = pr.cu_q[b], pr.cu_q[b + 1], pr.cu_kv[b], pr.cu_kv[b + 1]
+        dq[q0:q1] = 0.0
+        dk[k0:k1] = 0.0
+        dv[k0:k1] = 0.0
+        for h in range(pr.nq):
+            st = pr.probs(b, h)
+            g = st["g"]
+            dyb = dy[q0:q1, h, :]
+            vb = pr.v[k0:k1, g, :]
+            kb = pr.k[k0:k1, g, :]
+            qb = pr.q[q0:q1, h, :]
+            # dV = P~^T dY
+            dv[k0:k1, g, :] += st["pt"].T @ dyb
+            # dP = (dY V^T) * z / keep  (gradient w.r.t. the pre-dropout P)
+            dp = dyb @ vb.T
+            if st["z"] is not None:
+                dp = dp * st["z"] / pr.keep
+            p = st["p"]
+            # softmax Jacobian: dS = P * (dP - rowsum(P * dP)); the sink column has dP = 0
+            row = np.sum(p * dp, axis=1)
+            ds = p * (dp - row[:, None])
+            dq[q0:q1, h, :] = pr.scale * (ds @ kb)
+            dk[k0:k1, g, :] += pr.scale * (ds.T @ qb)
+            if dsink is not None:
+                # dSink = sum over rows of -p_sink * rowsum(P * dP)
+                dsink[h] += float(np.sum(-st["p_sink"] * row))
+    return dq, dk, dv, dsink
+
+
+def probabilities(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, b, h, **kw):
+    """The materialised S, P, P~, m, l and sink probability of one (sequence, head)."""
+    pr = _problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, **kw)
+    return pr.probs(b, h)

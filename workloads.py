@@ -1,0 +1,239 @@
+"""Seeded synthetic inputs for varlen (TND) FlashAttention forward/backward.
+
+This module only draws and lays out inputs: sequence lengths, Q/K/V/dY, the
+bit-packed dropout keep-mask, ALiBi slopes and per-head sink logits.  It holds
+none of the attention arithmetic, so both the fp64 oracle and the HIP path can
+consume the same inputs without sharing any of the method's code.
+
+Layout (TND, as on the Ascend pages' aclnnFlashAttentionUnpaddingScoreGrad,
+parameter list and the TND note under "Constraints"): Q, dY are [T_q, Nq, D],
+K, V are [T_kv, Nkv, D], row-major and contiguous.  Sequence boundaries are
+cumulative offsets cu_seqlens (B+1 entries, leading 0).
+
+Dropout mask (same page, dropMaskOptional): one flat bit stream of
+sum_b sum_n Sq_b*Skv_b bits, batch-major, then query head, then query row,
+then key; bit 1 = keep.  Bits are packed least-significant-bit first.
+
+Seeds: the lengths of workload k come from numpy.random.default_rng(k); tensor
+t (1 Q, 2 K, 3 V, 4 dY, 5 sink, 6 dropout mask) from default_rng([k, t]).
+bf16 tensors are the fp32 draws rounded to nearest-even by torch.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+INT_MAX_TOKENS = 2147483647
+
+# sparse modes built here (aclnnFlashAttentionUnpaddingScoreGrad, sparseMode list)
+MODE_NONE = 0
+MODE_LEFT_UP_CAUSAL = 2
+MODE_RIGHT_DOWN_CAUSAL = 3
+MODE_BAND = 4
+
+
+@dataclass
+class Case:
+    """One attention problem: host-side inputs plus its attributes."""
+    name: str
+    dtype: torch.dtype
+    cu_seqlens_q: np.ndarray          # int64 [B+1]
+    cu_seqlens_kv: np.ndarray         # int64 [B+1]
+    head_num: int
+    kv_heads: int
+    head_dim: int
+    scale: float
+    q: torch.Tensor                   # [T_q, Nq, D] (cpu)
+    k: torch.Tensor                   # [T_kv, Nkv, D]
+    v: torch.Tensor
+    dy: torch.Tensor                  # [T_q, Nq, D]
+    keep_prob: float = 1.0
+    sparse_mode: int = MODE_NONE
+    pre_tokens: int = INT_MAX_TOKENS
+    next_tokens: int = INT_MAX_TOKENS
+    drop_mask: Optional[np.ndarray] = None     # uint8 packed bits
+    alibi_slopes: Optional[np.ndarray] = None  # float32 [Nq]
+    sink: Optional[np.ndarray] = None          # float32 [Nq]
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def batch(self) -> int:
+        return len(self.cu_seqlens_q) - 1
+
+    @property
+    def lens_q(self) -> np.ndarray:
+        return np.diff(self.cu_seqlens_q)
+
+    @property
+    def lens_kv(self) -> np.ndarray:
+        return np.diff(self.cu_seqlens_kv)
+
+
+def cu_from_lengths(lengths) -> np.ndarray:
+    lengths = np.asarray(lengths, dtype=np.int64)
+    return np.concatenate([np.zeros(1, np.int64), np.cumsum(lengths)]).astype(np.int64)
+
+
+def _normal(seed, shape, dtype: torch.dtype, mult: float = 1.0) -> torch.Tensor:
+    x = np.random.default_rng(seed).standard_normal(shape, dtype=np.float32)
+    if mult != 1.0:
+        x = (x * np.float32(mult)).astype(np.float32)
+    return torch.from_numpy(x).to(dtype)
+
+
+def dropout_bits_total(lens_q, lens_kv, head_num) -> int:
+    """Bit count of the packed keep-mask: head_num * sum_b Sq_b * Skv_b."""
+    lens_q = np.asarray(lens_q, dtype=np.int64)
+    lens_kv = np.asarray(lens_kv, dtype=np.int64)
+    return int(head_num * int(np.sum(lens_q * lens_kv)))
+
+
+def draw_keep_mask(seed, nbits: int, keep_prob: float, chunk: int = 1 << 24) -> np.ndarray:
+    """Bernoulli(keep_prob) keep bits, packed LSB-first into ceil(nbits/8) bytes."""
+    rng = np.random.default_rng(seed)
+    nbytes = (nbits + 7) // 8
+    out = np.empty(nbytes, dtype=np.uint8)
+    done = 0
+    while done < nbits:
+        n = min(chunk, nbits - done)           # chunk is a multiple of 8
+        bits = rng.random(n) < keep_prob
+        packed = np.packbits(bits, bitorder="little")
+        out[done // 8: done // 8 + packed.size] = packed
+        done += n
+    return out
+
+
+def alibi_slopes(head_num: int) -> np.ndarray:
+    """slope_h = 2^(-8(h+1)/N), h = query head, computed in fp64 then rounded to fp32."""
+    h = np.arange(head_num, dtype=np.float64)
+    return np.power(2.0, -8.0 * (h + 1.0) / head_num).astype(np.float32)
+
+
+def lognormal_lengths(seed, total: int, batch: int, median: float, lo: int, hi: int) -> np.ndarray:
+    """Lognormal lengths (median `median`, sigma sqrt(2 ln 2) so the mean is 2*median),
+    clipped to [lo, hi], rescaled to sum to `total`, rounded, and the residual
+    spread one token at a time over sequences in stable descending-length order."""
+    rng = np.random.default_rng(seed)
+    x = rng.lognormal(math.log(median), math.sqrt(2.0 * math.log(2.0)), batch)
+    x = np.clip(x, lo, hi)
+    x = x * (total / x.sum())
+    n = np.clip(np.rint(x), lo, hi).astype(np.int64)
+    order = np.argsort(-n, kind="stable")
+    guard = 0
+    while n.sum() != total:
+        step = 1 if n.sum() < total else -1
+        moved = False
+        for idx in order:
+            if n.sum() == total:
+                break
+            if lo <= n[idx] + step <= hi:
+                n[idx] += step
+                moved = True
+        guard += 1
+        if not moved or guard > 10 * total:
+            raise ValueError("cannot distribute residual within bounds")
+    return n
+
+
+def make_case(name, lens_q, lens_kv=None, *, head_num, kv_heads, head_dim, dtype=torch.bfloat16,
+              scale=None, keep_prob=1.0, sparse_mode=MODE_NONE, pre_tokens=INT_MAX_TOKENS,
+              next_tokens=INT_MAX_TOKENS, alibi=False, sink=False, seed=0, dy_mult=1.0,
+              drop_mask=None) -> Case:
+    """A case built from explicit lengths; every tensor is drawn from default_rng([seed, t])."""
+    lens_q = np.asarray(lens_q, dtype=np.int64)
+    lens_kv = lens_q.copy() if lens_kv is None else np.asarray(lens_kv, dtype=np.int64)
+    cu_q, cu_kv = cu_from_lengths(lens_q), cu_from_lengths(lens_kv)
+    tq, tkv = int(cu_q[-1]), int(cu_kv[-1])
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    q = _normal([seed, 1], (tq, head_num, head_dim), dtype)
+    k = _normal([seed, 2], (tkv, kv_heads, head_dim), dtype)
+    v = _normal([seed, 3], (tkv, kv_heads, head_dim), dtype)
+    dy = _normal([seed, 4], (tq, head_num, head_dim), dtype, dy_mult)
+    sink_v = None
+    if sink:
+        sink_v = np.random.default_rng([seed, 5]).standard_normal(head_num, dtype=np.float32)
+    if keep_prob < 1.0 and drop_mask is None:
+        drop_mask = draw_keep_mask([seed, 6], dropout_bits_total(lens_q, lens_kv, head_num), keep_prob)
+    return Case(name=name, dtype=dtype, cu_seqlens_q=cu_q, cu_seqlens_kv=cu_kv, head_num=head_num,
+                kv_heads=kv_heads, head_dim=head_dim, scale=float(scale), q=q, k=k, v=v, dy=dy,
+                keep_prob=float(keep_prob), sparse_mode=sparse_mode, pre_tokens=int(pre_tokens),
+                next_tokens=int(next_tokens), drop_mask=drop_mask,
+                alibi_slopes=alibi_slopes(head_num) if alibi else None, sink=sink_v)
+
+
+WORKLOAD_NAMES = {
+    1: "tiny varlen fp32 {37,64} Nq=Nkv=2 D=64 no mask",
+    2: "varlen bf16 B=8 U[128,2048] Nq=32 Nkv=8 D=128 causal",
+    3: "bf16 B=4 S=8192 Nq=Nkv=32 D=128 window pre=2048 next=0",
+    4: "bf16 B=16 S=2048 Nq=Nkv=16 D=128 causal alibi dropout keep=0.9",
+    5: "packed varlen bf16 T=131072 B=64 lognormal Nq=64 Nkv=8 D=128 causal sink",
+}
+
+
+def workload_lengths(k: int) -> np.ndarray:
+    if k == 1:
+        return np.array([37, 64], dtype=np.int64)
+    if k == 2:
+        return np.random.default_rng(2).integers(128, 2048, 8, endpoint=True).astype(np.int64)
+    if k == 3:
+        return np.full(4, 8192, dtype=np.int64)
+    if k == 4:
+        return np.full(16, 2048, dtype=np.int64)
+    if k == 5:
+        return lognormal_lengths(5, 131072, 64, 1024.0, 64, 16384)
+    raise ValueError(f"unknown workload {k}")
+
+
+def make_workload(k: int) -> Case:
+    """The five fixed workloads (sizes, masks and features as listed in WORKLOAD_NAMES)."""
+    lens = workload_lengths(k)
+    if k == 1:
+        c = make_case(WORKLOAD_NAMES[1], lens, head_num=2, kv_heads=2, head_dim=64, dtype=torch.float32,
+                      scale=1.0 / 8.0, seed=1)
+    elif k == 2:
+        c = make_case(WORKLOAD_NAMES[2], lens, head_num=32, kv_heads=8, head_dim=128,
+                      sparse_mode=MODE_RIGHT_DOWN_CAUSAL, seed=2)
+    elif k == 3:
+        c = make_case(WORKLOAD_NAMES[3], lens, head_num=32, kv_heads=32, head_dim=128,
+                      sparse_mode=MODE_BAND, pre_tokens=2048, next_tokens=0, seed=3, dy_mult=0.1)
+    elif k == 4:
+        c = make_case(WORKLOAD_NAMES[4], lens, head_num=16, kv_heads=16, head_dim=128,
+                      sparse_mode=MODE_RIGHT_DOWN_CAUSAL, keep_prob=0.9, alibi=True, seed=4)
+    elif k == 5:
+        c = make_case(WORKLOAD_NAMES[5], lens, head_num=64, kv_heads=8, head_dim=128,
+                      sparse_mode=MODE_RIGHT_DOWN_CAUSAL, sink=True, seed=5)
+    else:
+        raise ValueError(k)
+    c.meta["workload"] = k
+    return c
+
+
+def allowed_pairs(lens_q, lens_kv, head_num, sparse_mode, pre_tokens=INT_MAX_TOKENS,
+                  next_tokens=INT_MAX_TOKENS) -> int:
+    """Count of allowed (row, key, query-head) triples, by closed-form interval
+    lengths per row (used for the mask-aware FLOP count)."""
+    total = 0
+    for lq, lkv in zip(np.asarray(lens_q, np.int64), np.asarray(lens_kv, np.int64)):
+        lq, lkv = int(lq), int(lkv)
+        if lq == 0 or lkv == 0:
+            continue
+        i = np.arange(lq, dtype=np.int64)
+        delta = lkv - lq
+        if sparse_mode == MODE_NONE:
+            lo = np.zeros(lq, np.int64); hi = np.full(lq, lkv - 1, np.int64)
+        elif sparse_mode == MODE_LEFT_UP_CAUSAL:
+            lo = np.zeros(lq, np.int64); hi = i
+        elif sparse_mode == MODE_RIGHT_DOWN_CAUSAL:
+            lo = np.zeros(lq, np.int64); hi = i + delta
+        elif sparse_mode == MODE_BAND:
+            lo = i + delta - pre_tokens; hi = i + delta + next_tokens
+        else:
+            raise ValueError(sparse_mode)
+        lo = np.maximum(lo, 0); hi = np.minimum(hi, lkv - 1)
+        total += int(np.sum(np.maximum(hi - lo + 1, 0)))
+    return total * int(head_num)
