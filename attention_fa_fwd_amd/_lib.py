@@ -1,0 +1,250 @@
+"""ctypes binding of libfa.so (include/fa.h).  Argument marshalling only: every
+step of the computation runs in the library's HIP kernels.  torch supplies
+device memory and the stream handle.
+
+The library must have been built (python -m attention_fa_fwd_amd.build); there
+is no fallback: loading fails loudly when libfa.so is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+import numpy as np
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libfa.so")
+
+FA_OK = 0
+FA_ERR_PARAM_NULLPTR = 161001
+FA_ERR_PARAM_INVALID = 161002
+FA_ERR_WORKSPACE = 1
+FA_ERR_HIP = 2
+
+FA_DTYPE_FP32 = 0
+FA_DTYPE_BF16 = 1
+TOKENS_DEFAULT = 2147483647
+
+EXPORTED = ("fa_fwd_workspace_size", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd", "fa_status_string",
+            "fa_debug_schedule", "fa_profile_enable", "fa_profile_read", "fa_profile_kernel_count")
+
+
+class FaConfig(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("cu_seqlens_q", ctypes.POINTER(ctypes.c_int64)),
+        ("cu_seqlens_kv", ctypes.POINTER(ctypes.c_int64)),
+        ("head_num", ctypes.c_int64),
+        ("num_kv_heads", ctypes.c_int64),
+        ("head_dim", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("sparse_mode", ctypes.c_int32),
+        ("scale", ctypes.c_double),
+        ("keep_prob", ctypes.c_double),
+        ("pre_tokens", ctypes.c_int64),
+        ("next_tokens", ctypes.c_int64),
+        ("deterministic", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
+    ]
+
+
+class FaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if libfa.so was not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m attention_fa_fwd_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, u64p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint64)
+        cfgp = ctypes.POINTER(FaConfig)
+        L.fa_fwd_workspace_size.argtypes = [cfgp, u64p]
+        L.fa_bwd_workspace_size.argtypes = [cfgp, u64p]
+        L.fa_fwd.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
+        L.fa_bwd.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
+        L.fa_status_string.argtypes = [ctypes.c_int32]
+        L.fa_status_string.restype = ctypes.c_char_p
+        L.fa_debug_schedule.argtypes = [cfgp, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
+                                        ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32),
+                                        ctypes.POINTER(ctypes.c_int32)]
+        L.fa_profile_enable.argtypes = [ctypes.c_int32]
+        L.fa_profile_read.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_char_p),
+                                      ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+        L.fa_profile_kernel_count.restype = ctypes.c_int32
+        for name in ("fa_fwd_workspace_size", "fa_bwd_workspace_size", "fa_fwd", "fa_bwd", "fa_debug_schedule",
+                     "fa_profile_enable", "fa_profile_read"):
+            getattr(L, name).restype = ctypes.c_int32
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().fa_status_string(int(status)).decode()
+
+
+class Config:
+    """Owns the host cu_seqlens arrays for the lifetime of a fa_config."""
+
+    def __init__(self, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, head_dim, dtype, scale, keep_prob=1.0,
+                 sparse_mode=0, pre_tokens=TOKENS_DEFAULT, next_tokens=TOKENS_DEFAULT, deterministic=True):
+        self.cu_q = np.ascontiguousarray(np.asarray(cu_seqlens_q, dtype=np.int64))
+        self.cu_kv = np.ascontiguousarray(np.asarray(cu_seqlens_kv, dtype=np.int64))
+        if isinstance(dtype, torch.dtype):
+            dtype = {torch.float32: FA_DTYPE_FP32, torch.bfloat16: FA_DTYPE_BF16}.get(dtype, -1)
+        self.c = FaConfig(
+            batch=len(self.cu_q) - 1,
+            cu_seqlens_q=self.cu_q.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+            cu_seqlens_kv=self.cu_kv.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+            head_num=int(head_num), num_kv_heads=int(kv_heads), head_dim=int(head_dim), dtype=int(dtype),
+            sparse_mode=int(sparse_mode), scale=float(scale), keep_prob=float(keep_prob),
+            pre_tokens=int(pre_tokens), next_tokens=int(next_tokens), deterministic=1 if deterministic else 0,
+            flags=0)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check(status: int, where: str):
+    if status != FA_OK:
+        raise FaError(status, where)
+
+
+def _stream_handle(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check_tensor(name, t, shape, dtype, device):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def fa_fwd_workspace_size(cfg: Config) -> int:
+    n = ctypes.c_uint64(0)
+    _check(lib().fa_fwd_workspace_size(cfg.ref, ctypes.byref(n)), "fa_fwd_workspace_size")
+    return n.value
+
+
+def fa_bwd_workspace_size(cfg: Config) -> int:
+    n = ctypes.c_uint64(0)
+    _check(lib().fa_bwd_workspace_size(cfg.ref, ctypes.byref(n)), "fa_bwd_workspace_size")
+    return n.value
+
+
+def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.Tensor:
+    if workspace is not None and workspace.numel() * workspace.element_size() >= nbytes:
+        return workspace
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def _common_checks(q, k, v, cfg: Config):
+    dev = q.device
+    tq, tkv = int(cfg.cu_q[-1]), int(cfg.cu_kv[-1])
+    nq, nkv, d = cfg.c.head_num, cfg.c.num_kv_heads or cfg.c.head_num, cfg.c.head_dim
+    _check_tensor("q", q, (tq, nq, d), q.dtype, dev)
+    _check_tensor("k", k, (tkv, nkv, d), q.dtype, dev)
+    _check_tensor("v", v, (tkv, nkv, d), q.dtype, dev)
+    return dev, tq, tkv, nq, nkv, d
+
+
+def fa_fwd(cfg: Config, q, k, v, drop_mask=None, alibi_slopes=None, sink=None, out=None, softmax_max=None,
+           softmax_sum=None, workspace=None):
+    """Forward through libfa.so on the current stream; returns (out, softmax_max, softmax_sum)."""
+    dev, tq, tkv, nq, nkv, d = _common_checks(q, k, v, cfg)
+    if out is None:
+        out = torch.empty_like(q)
+    if softmax_max is None:
+        softmax_max = torch.empty((tq, nq), dtype=torch.float32, device=dev)
+    if softmax_sum is None:
+        softmax_sum = torch.empty((tq, nq), dtype=torch.float32, device=dev)
+    _check_tensor("out", out, (tq, nq, d), q.dtype, dev)
+    _check_tensor("softmax_max", softmax_max, (tq, nq), torch.float32, dev)
+    _check_tensor("softmax_sum", softmax_sum, (tq, nq), torch.float32, dev)
+    for name, t in (("alibi_slopes", alibi_slopes), ("sink", sink)):
+        if t is not None:
+            _check_tensor(name, t, (nq,), torch.float32, dev)
+    if drop_mask is not None and (drop_mask.dtype != torch.uint8 or drop_mask.device != dev):
+        raise ValueError("drop_mask must be a uint8 tensor on the same device")
+    ws = _workspace(fa_fwd_workspace_size(cfg), dev, workspace)
+    st = lib().fa_fwd(cfg.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(drop_mask), _ptr(alibi_slopes), _ptr(sink),
+                      _ptr(out), _ptr(softmax_max), _ptr(softmax_sum), _ptr(ws),
+                      ctypes.c_uint64(ws.numel()), _stream_handle(dev))
+    _check(st, "fa_fwd")
+    return out, softmax_max, softmax_sum
+
+
+def fa_bwd(cfg: Config, q, k, v, dy, out, softmax_max, softmax_sum, drop_mask=None, alibi_slopes=None, sink=None,
+           dq=None, dk=None, dv=None, dsink=None, workspace=None):
+    """Backward through libfa.so on the current stream; returns (dq, dk, dv, dsink or None)."""
+    dev, tq, tkv, nq, nkv, d = _common_checks(q, k, v, cfg)
+    _check_tensor("dy", dy, (tq, nq, d), q.dtype, dev)
+    _check_tensor("out", out, (tq, nq, d), q.dtype, dev)
+    _check_tensor("softmax_max", softmax_max, (tq, nq), torch.float32, dev)
+    _check_tensor("softmax_sum", softmax_sum, (tq, nq), torch.float32, dev)
+    if dq is None:
+        dq = torch.empty_like(q)
+    if dk is None:
+        dk = torch.empty_like(k)
+    if dv is None:
+        dv = torch.empty_like(v)
+    if sink is not None and dsink is None:
+        dsink = torch.empty((nq,), dtype=torch.float32, device=dev)
+    _check_tensor("dq", dq, (tq, nq, d), q.dtype, dev)
+    _check_tensor("dk", dk, (tkv, nkv, d), q.dtype, dev)
+    _check_tensor("dv", dv, (tkv, nkv, d), q.dtype, dev)
+    ws = _workspace(fa_bwd_workspace_size(cfg), dev, workspace)
+    st = lib().fa_bwd(cfg.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(dy), _ptr(out), _ptr(softmax_max),
+                      _ptr(softmax_sum), _ptr(drop_mask), _ptr(alibi_slopes), _ptr(sink), _ptr(dq), _ptr(dk),
+                      _ptr(dv), _ptr(dsink), _ptr(ws), ctypes.c_uint64(ws.numel()), _stream_handle(dev))
+    _check(st, "fa_bwd")
+    return dq, dk, dv, dsink
+
+
+def fa_debug_schedule(cfg: Config, pass_id: int):
+    """Host-side work list of a pass: (items [n, 4] int64, (tile_rows, tile_cols))."""
+    n = ctypes.c_int64(0)
+    br, bc = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(lib().fa_debug_schedule(cfg.ref, int(pass_id), None, 0, ctypes.byref(n), ctypes.byref(br),
+                                   ctypes.byref(bc)), "fa_debug_schedule")
+    items = np.zeros((n.value, 4), dtype=np.int64)
+    _check(lib().fa_debug_schedule(cfg.ref, int(pass_id), items.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),
+                                   n.value, ctypes.byref(n), None, None), "fa_debug_schedule")
+    return items, (br.value, bc.value)
+
+
+def fa_profile_enable(on: bool):
+    _check(lib().fa_profile_enable(1 if on else 0), "fa_profile_enable")
+
+
+def fa_profile_read() -> dict:
+    """{kernel name: (total_ms, launches)} since the last read; synchronises the recorded events."""
+    res = {}
+    for k in range(lib().fa_profile_kernel_count()):
+        name = ctypes.c_char_p()
+        ms = ctypes.c_double(0)
+        cnt = ctypes.c_int64(0)
+        _check(lib().fa_profile_read(k, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(cnt)), "fa_profile_read")
+        res[name.value.decode()] = (ms.value, cnt.value)
+    return res

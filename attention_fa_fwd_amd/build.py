@@ -1,0 +1,63 @@
+"""Compile the HIP sources of this package into libfa.so for gfx950 (in-tree).
+
+Usage: python -m attention_fa_fwd_amd.build   (or call build()).
+"""
+from __future__ import annotations
+
+import os
+import subprocess
+import sys
+from concurrent.futures import ThreadPoolExecutor
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(PKG, "csrc")
+ROOT = os.path.dirname(PKG)
+LIB = os.path.join(PKG, "libfa.so")
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip"]
+ARCH = "gfx950"
+
+
+def hipcc() -> str:
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    return os.path.join(rocm, "bin", "hipcc")
+
+
+def common_flags():
+    return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"),
+            # no packed-fp32 instructions in any generated code
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            "-Wno-unused-result"]
+
+
+def _run(cmd):
+    r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    lines = [ln for ln in r.stdout.splitlines() if "packed-fp32-ops" not in ln]
+    return r.returncode, "\n".join(lines)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link libfa.so; returns the library path."""
+    build_dir = os.path.join(PKG, "_build")
+    os.makedirs(build_dir, exist_ok=True)
+    objs, cmds = [], []
+    for src in SOURCES:
+        obj = os.path.join(build_dir, src.replace(".hip", ".o"))
+        objs.append(obj)
+        cmds.append([hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj])
+    with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
+        results = list(ex.map(_run, cmds))
+    for cmd, (rc, out) in zip(cmds, results):
+        if verbose and out.strip():
+            print(out)
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed ({rc}) for {cmd[-3]}:\n{out}")
+    tmp = LIB + ".tmp"
+    rc, out = _run([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs)
+    if rc != 0:
+        raise RuntimeError(f"link failed ({rc}):\n{out}")
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,464 @@
+// Host runtime of libfa.so: argument validation, the varlen tile scheduler,
+// workspace layout, kernel launch sequences and the C ABI declared in fa.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <mutex>
+#include <vector>
+
+#include "../../include/fa.h"
+#include "fa_kernels.h"
+#include "fa_sched.h"
+
+namespace {
+
+using fa::WorkItem;
+
+constexpr int64_t kMaxTokens = int64_t(1) << 20;   // T and S limits of the grad pages ("Constraints")
+constexpr int64_t kMaxBatch = 20000;               // B limit of the V5 grad page
+constexpr int64_t kMaxHeads = 256;                 // Nq limit ("Nq ranges from 1 to 256")
+
+struct Problem {
+  int64_t batch = 0, nq = 0, nkv = 0, d = 0, tq = 0, tkv = 0;
+  int dtype = 0, mode = 0;
+  double scale = 0, keep = 1;
+  int64_t pre = 0, next = 0;
+  bool deterministic = true;
+  std::vector<int32_t> cu_q, cu_kv;
+  std::vector<int64_t> bit_base;   // first keep bit of each sequence
+  int64_t drop_bits = 0;
+};
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+fa_status parse(const fa_config* cfg, Problem* pr) {
+  if (!cfg || !cfg->cu_seqlens_q || !cfg->cu_seqlens_kv) return FA_ERR_PARAM_NULLPTR;
+  if (cfg->batch < 1 || cfg->batch > kMaxBatch) return FA_ERR_PARAM_INVALID;
+  if (cfg->head_num < 1 || cfg->head_num > kMaxHeads) return FA_ERR_PARAM_INVALID;
+  const int64_t nkv = cfg->num_kv_heads == 0 ? cfg->head_num : cfg->num_kv_heads;
+  if (nkv < 1 || cfg->head_num % nkv != 0) return FA_ERR_PARAM_INVALID;
+  if (cfg->head_dim != 64 && cfg->head_dim != 128) return FA_ERR_PARAM_INVALID;
+  if (cfg->dtype != FA_DTYPE_FP32 && cfg->dtype != FA_DTYPE_BF16) return FA_ERR_PARAM_INVALID;
+  const int mode = cfg->sparse_mode;
+  if (mode != FA_SPARSE_NONE && mode != FA_SPARSE_LEFT_UP_CAUSAL && mode != FA_SPARSE_RIGHT_DOWN_CAUSAL &&
+      mode != FA_SPARSE_BAND)
+    return FA_ERR_PARAM_INVALID;
+  if (!(cfg->keep_prob > 0.0 && cfg->keep_prob <= 1.0)) return FA_ERR_PARAM_INVALID;
+  if (!std::isfinite(cfg->scale)) return FA_ERR_PARAM_INVALID;
+  if (mode == FA_SPARSE_BAND && cfg->pre_tokens + cfg->next_tokens < 0) return FA_ERR_PARAM_INVALID;
+  if (cfg->deterministic != 0 && cfg->deterministic != 1) return FA_ERR_PARAM_INVALID;
+  if (cfg->flags != 0) return FA_ERR_PARAM_INVALID;
+
+  pr->batch = cfg->batch;
+  pr->nq = cfg->head_num;
+  pr->nkv = nkv;
+  pr->d = cfg->head_dim;
+  pr->dtype = cfg->dtype;
+  pr->mode = mode;
+  pr->scale = cfg->scale;
+  pr->keep = cfg->keep_prob;
+  pr->pre = cfg->pre_tokens;
+  pr->next = cfg->next_tokens;
+  pr->deterministic = cfg->deterministic != 0;
+  const int64_t* cq = cfg->cu_seqlens_q;
+  const int64_t* ck = cfg->cu_seqlens_kv;
+  if (cq[0] != 0 || ck[0] != 0) return FA_ERR_PARAM_INVALID;
+  pr->cu_q.resize(pr->batch + 1);
+  pr->cu_kv.resize(pr->batch + 1);
+  pr->bit_base.resize(pr->batch);
+  int64_t bits = 0;
+  for (int64_t b = 0; b <= pr->batch; ++b) {
+    if (cq[b] < 0 || ck[b] < 0 || cq[b] > kMaxTokens || ck[b] > kMaxTokens) return FA_ERR_PARAM_INVALID;
+    if (b > 0 && (cq[b] < cq[b - 1] || ck[b] < ck[b - 1])) return FA_ERR_PARAM_INVALID;
+    pr->cu_q[b] = (int32_t)cq[b];
+    pr->cu_kv[b] = (int32_t)ck[b];
+    if (b < pr->batch) {
+      pr->bit_base[b] = bits;
+      // cq, ck are bounded by 2^20 here, so the products stay far below 2^63
+      bits += pr->nq * (cq[b + 1] - cq[b]) * (ck[b + 1] - ck[b]);
+    }
+  }
+  pr->tq = cq[pr->batch];
+  pr->tkv = ck[pr->batch];
+  if (pr->tq < 1 || pr->tkv < 1) return FA_ERR_PARAM_INVALID;
+  pr->drop_bits = bits;
+  return FA_OK;
+}
+
+fa_status check_alibi(const Problem& pr) {
+  // pseType 2 needs Sq == Skv per sequence, and no zero-length sequence carries a pse
+  for (int64_t b = 0; b < pr.batch; ++b) {
+    const int32_t lq = pr.cu_q[b + 1] - pr.cu_q[b], lkv = pr.cu_kv[b + 1] - pr.cu_kv[b];
+    if (lq != lkv || lq == 0) return FA_ERR_PARAM_INVALID;
+  }
+  return FA_OK;
+}
+
+FaWindow window_of(const Problem& pr, int64_t b) {
+  const int32_t lq = pr.cu_q[b + 1] - pr.cu_q[b], lkv = pr.cu_kv[b + 1] - pr.cu_kv[b];
+  return fa_make_window(pr.mode, pr.pre, pr.next, lq, lkv);
+}
+
+// Work list of one pass; longest items first (stable), so the dispatcher starts
+// the heaviest tiles early and the short ones fill the tail.
+std::vector<WorkItem> schedule(const Problem& pr, int pass, int* bm_out, int* bn_out) {
+  std::vector<WorkItem> items;
+  int bm, bn;
+  if (pass == 0) { bm = fa::kFwdBM; bn = fa::kFwdBN; }
+  else if (pass == 1) { bm = fa::kKvBM; bn = fa::kKvBN; }
+  else { bm = fa::kDqBM; bn = fa::kDqBN; }
+  if (bm_out) *bm_out = bm;
+  if (bn_out) *bn_out = bn;
+  for (int64_t b = 0; b < pr.batch; ++b) {
+    const int32_t lq = pr.cu_q[b + 1] - pr.cu_q[b], lkv = pr.cu_kv[b + 1] - pr.cu_kv[b];
+    const FaWindow w = window_of(pr, b);
+    if (pass == 1) {
+      const int32_t nt = (lkv + bn - 1) / bn;
+      for (int32_t t = 0; t < nt; ++t) {
+        int32_t lo, hi;
+        fa_q_tile_range(w, t * bn, std::min(t * bn + bn, lkv), lq, bm, &lo, &hi);
+        items.push_back({(int32_t)b, t, lo, hi});
+      }
+    } else {
+      const int32_t nt = (lq + bm - 1) / bm;
+      for (int32_t t = 0; t < nt; ++t) {
+        int32_t lo, hi;
+        fa_kv_tile_range(w, t * bm, std::min(t * bm + bm, lq), lkv, bn, &lo, &hi);
+        items.push_back({(int32_t)b, t, lo, hi});
+      }
+    }
+  }
+  std::stable_sort(items.begin(), items.end(),
+                   [](const WorkItem& a, const WorkItem& b) { return (a.hi - a.lo) > (b.hi - b.lo); });
+  return items;
+}
+
+// ---- workspace layout ----
+constexpr uint64_t kAlign = 256;
+uint64_t align_up(uint64_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+
+struct Layout {
+  uint64_t cu_q = 0, cu_kv = 0, bit_base = 0, items0 = 0, items1 = 0;   // host-staged block
+  uint64_t staged_bytes = 0;
+  uint64_t delta = 0, lse = 0, dsink_part = 0, dq_acc = 0;
+  uint64_t total = 0;
+  int64_t n_items0 = 0, n_items1 = 0;
+  int n_pre_blocks = 0;
+};
+
+Layout layout_fwd(const Problem& pr, int64_t n_items) {
+  Layout L;
+  uint64_t off = 0;
+  L.cu_q = off; off = align_up(off + 4 * (pr.batch + 1));
+  L.cu_kv = off; off = align_up(off + 4 * (pr.batch + 1));
+  L.bit_base = off; off = align_up(off + 8 * pr.batch);
+  L.items0 = off; off = align_up(off + sizeof(WorkItem) * n_items);
+  L.staged_bytes = off;
+  L.n_items0 = n_items;
+  L.total = std::max<uint64_t>(off, kAlign);
+  return L;
+}
+
+// sum_b ceil(L_b / tile) <= T / tile + B
+int64_t upper_items(const Problem& pr, int tile) { return pr.batch + (std::max(pr.tq, pr.tkv) + tile - 1) / tile; }
+
+Layout layout_bwd(const Problem& pr, int64_t n_kv_items, int64_t n_dq_items) {
+  Layout L;
+  uint64_t off = 0;
+  L.cu_q = off; off = align_up(off + 4 * (pr.batch + 1));
+  L.cu_kv = off; off = align_up(off + 4 * (pr.batch + 1));
+  L.bit_base = off; off = align_up(off + 8 * pr.batch);
+  L.items0 = off; off = align_up(off + sizeof(WorkItem) * n_kv_items);
+  L.items1 = off; off = align_up(off + sizeof(WorkItem) * n_dq_items);
+  L.staged_bytes = off;
+  L.n_items0 = n_kv_items;
+  L.n_items1 = n_dq_items;
+  L.delta = off; off = align_up(off + 4 * (uint64_t)pr.tq * pr.nq);
+  L.lse = off; off = align_up(off + 4 * (uint64_t)pr.tq * pr.nq);
+  L.n_pre_blocks = (int)((pr.tq + fa::kPreRowsPerBlock - 1) / fa::kPreRowsPerBlock);
+  L.dsink_part = off; off = align_up(off + 4 * (uint64_t)L.n_pre_blocks * pr.nq);
+  if (!pr.deterministic) {
+    L.dq_acc = off;
+    off = align_up(off + 4 * (uint64_t)pr.tq * pr.nq * pr.d);
+  }
+  L.total = off;
+  return L;
+}
+
+// Sizes are computed from upper bounds on the item counts so that the size
+// query does not depend on anything but the configuration.
+Layout fwd_layout_bound(const Problem& pr) { return layout_fwd(pr, upper_items(pr, fa::kFwdBM)); }
+Layout bwd_layout_bound(const Problem& pr) {
+  return layout_bwd(pr, upper_items(pr, fa::kKvBN), upper_items(pr, fa::kDqBM));
+}
+
+// ---- kernel timing (measurement hook) ----
+enum KernelId { K_FWD = 0, K_PRE, K_KV, K_DQ, K_CONVERT, K_DSINK, K_ZERO, K_COUNT };
+const char* kKernelNames[K_COUNT] = {"fa_fwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
+                                     "fa_bwd_dq_convert", "fa_bwd_dsink_reduce", "fa_zero_f32"};
+struct ProfState {
+  std::mutex mu;
+  bool on = false;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> ev[K_COUNT];
+  double total_ms[K_COUNT] = {};
+  int64_t launches[K_COUNT] = {};
+};
+ProfState& prof() {
+  static ProfState s;
+  return s;
+}
+
+template <typename F>
+hipError_t timed(KernelId id, hipStream_t s, F&& launch) {
+  ProfState& P = prof();
+  bool on;
+  {
+    std::lock_guard<std::mutex> g(P.mu);
+    on = P.on;
+  }
+  if (!on) return launch();
+  hipEvent_t a, b;
+  if (hipEventCreate(&a) != hipSuccess) return hipErrorUnknown;
+  if (hipEventCreate(&b) != hipSuccess) return hipErrorUnknown;
+  hipError_t e = hipEventRecord(a, s);
+  if (e == hipSuccess) e = launch();
+  if (e == hipSuccess) e = hipEventRecord(b, s);
+  std::lock_guard<std::mutex> g(P.mu);
+  P.ev[id].push_back({a, b});
+  return e;
+}
+
+fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+void fill_common_fwd(const Problem& pr, fa::FwdParams& p) {
+  p.nq = (int32_t)pr.nq;
+  p.nkv = (int32_t)pr.nkv;
+  p.group = (int32_t)(pr.nq / pr.nkv);
+  p.mode = pr.mode;
+  p.pre = (int32_t)fa_clamp_window(pr.pre);
+  p.next = (int32_t)fa_clamp_window(pr.next);
+  p.scale_log2 = (float)(pr.scale * 1.4426950408889634);
+  p.inv_keep = (float)(1.0 / pr.keep);
+  p.use_dropout = pr.keep < 1.0 ? 1 : 0;
+  p.head_swizzle = (pr.nq % 8 == 0) ? 1 : 0;
+}
+
+std::vector<char> stage_block(const Problem& pr, const Layout& L, const std::vector<WorkItem>& i0,
+                              const std::vector<WorkItem>* i1) {
+  std::vector<char> host(L.staged_bytes, 0);
+  std::memcpy(host.data() + L.cu_q, pr.cu_q.data(), 4 * pr.cu_q.size());
+  std::memcpy(host.data() + L.cu_kv, pr.cu_kv.data(), 4 * pr.cu_kv.size());
+  std::memcpy(host.data() + L.bit_base, pr.bit_base.data(), 8 * pr.bit_base.size());
+  std::memcpy(host.data() + L.items0, i0.data(), sizeof(WorkItem) * i0.size());
+  if (i1) std::memcpy(host.data() + L.items1, i1->data(), sizeof(WorkItem) * i1->size());
+  return host;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_status_string(fa_status s) {
+  switch (s) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_PARAM_NULLPTR: return "FA_ERR_PARAM_NULLPTR: a required pointer argument is NULL";
+    case FA_ERR_PARAM_INVALID: return "FA_ERR_PARAM_INVALID: unsupported attribute, shape, dtype or alignment";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace smaller than the size query returned";
+    case FA_ERR_HIP: return "FA_ERR_HIP: a HIP runtime call or kernel launch failed";
+    default: return "unknown fa_status";
+  }
+}
+
+fa_status fa_fwd_workspace_size(const fa_config* cfg, uint64_t* bytes) {
+  if (!bytes) return FA_ERR_PARAM_NULLPTR;
+  Problem pr;
+  fa_status st = parse(cfg, &pr);
+  if (st != FA_OK) return st;
+  *bytes = fwd_layout_bound(pr).total;
+  return FA_OK;
+}
+
+fa_status fa_bwd_workspace_size(const fa_config* cfg, uint64_t* bytes) {
+  if (!bytes) return FA_ERR_PARAM_NULLPTR;
+  Problem pr;
+  fa_status st = parse(cfg, &pr);
+  if (st != FA_OK) return st;
+  *bytes = bwd_layout_bound(pr).total;
+  return FA_OK;
+}
+
+fa_status fa_fwd(const fa_config* cfg, const void* q, const void* k, const void* v, const uint8_t* drop_mask,
+                 const float* alibi_slopes, const float* sink, void* out, float* softmax_max, float* softmax_sum,
+                 void* workspace, uint64_t workspace_bytes, void* stream) {
+  Problem pr;
+  fa_status st = parse(cfg, &pr);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !out || !softmax_max || !softmax_sum) return FA_ERR_PARAM_NULLPTR;
+  if (pr.keep < 1.0 && !drop_mask) return FA_ERR_PARAM_NULLPTR;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16) || !aligned(softmax_max, 4) ||
+      !aligned(softmax_sum, 4) || (drop_mask && !aligned(drop_mask, 4)) || (alibi_slopes && !aligned(alibi_slopes, 4)) ||
+      (sink && !aligned(sink, 4)))
+    return FA_ERR_PARAM_INVALID;
+  if (alibi_slopes && (st = check_alibi(pr)) != FA_OK) return st;
+  const Layout bound = fwd_layout_bound(pr);
+  if (!workspace) return FA_ERR_PARAM_NULLPTR;
+  if (workspace_bytes < bound.total) return FA_ERR_WORKSPACE;
+
+  std::vector<WorkItem> items = schedule(pr, 0, nullptr, nullptr);
+  const Layout L = layout_fwd(pr, (int64_t)items.size());
+  std::vector<char> host = stage_block(pr, L, items, nullptr);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  hipError_t e = hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return FA_ERR_HIP;
+
+  fa::FwdParams p{};
+  fill_common_fwd(pr, p);
+  p.q = q; p.k = k; p.v = v; p.o = out;
+  p.m_out = softmax_max; p.l_out = softmax_sum;
+  p.drop = pr.keep < 1.0 ? drop_mask : nullptr;
+  p.drop_bytes = (pr.drop_bits + 7) / 8;
+  p.slopes = alibi_slopes; p.sink = sink;
+  p.cu_q = reinterpret_cast<const int32_t*>(ws + L.cu_q);
+  p.cu_kv = reinterpret_cast<const int32_t*>(ws + L.cu_kv);
+  p.bit_base = reinterpret_cast<const int64_t*>(ws + L.bit_base);
+  p.items = reinterpret_cast<const WorkItem*>(ws + L.items0);
+  p.n_items = (int32_t)items.size();
+  return hip_status(timed(K_FWD, s, [&] { return fa::launch_fwd(pr.dtype, (int)pr.d, p, s); }));
+}
+
+fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void* v, const void* dy, const void* out,
+                 const float* softmax_max, const float* softmax_sum, const uint8_t* drop_mask,
+                 const float* alibi_slopes, const float* sink, void* dq, void* dk, void* dv, float* dsink,
+                 void* workspace, uint64_t workspace_bytes, void* stream) {
+  Problem pr;
+  fa_status st = parse(cfg, &pr);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !dy || !out || !softmax_max || !softmax_sum || !dq || !dk || !dv)
+    return FA_ERR_PARAM_NULLPTR;
+  if (pr.keep < 1.0 && !drop_mask) return FA_ERR_PARAM_NULLPTR;
+  if (sink && !dsink) return FA_ERR_PARAM_NULLPTR;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(dy, 16) || !aligned(out, 16) ||
+      !aligned(dq, 16) || !aligned(dk, 16) || !aligned(dv, 16) || !aligned(softmax_max, 4) ||
+      !aligned(softmax_sum, 4) || (drop_mask && !aligned(drop_mask, 4)) ||
+      (alibi_slopes && !aligned(alibi_slopes, 4)) || (sink && !aligned(sink, 4)) || (dsink && !aligned(dsink, 4)))
+    return FA_ERR_PARAM_INVALID;
+  if (alibi_slopes && (st = check_alibi(pr)) != FA_OK) return st;
+  const Layout bound = bwd_layout_bound(pr);
+  if (!workspace) return FA_ERR_PARAM_NULLPTR;
+  if (workspace_bytes < bound.total) return FA_ERR_WORKSPACE;
+
+  std::vector<WorkItem> kv_items = schedule(pr, 1, nullptr, nullptr);
+  std::vector<WorkItem> dq_items = schedule(pr, 2, nullptr, nullptr);
+  const Layout L = layout_bwd(pr, (int64_t)kv_items.size(), (int64_t)dq_items.size());
+  std::vector<char> host = stage_block(pr, L, kv_items, &dq_items);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  hipError_t e = hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, s);
+  if (e != hipSuccess) return FA_ERR_HIP;
+
+  fa::BwdParams p{};
+  p.q = q; p.k = k; p.v = v; p.dy = dy; p.o = out;
+  p.m_in = softmax_max; p.l_in = softmax_sum;
+  p.dq = dq; p.dk = dk; p.dv = dv; p.dsink = sink ? dsink : nullptr;
+  p.delta = reinterpret_cast<float*>(ws + L.delta);
+  p.lse = reinterpret_cast<float*>(ws + L.lse);
+  p.dsink_part = reinterpret_cast<float*>(ws + L.dsink_part);
+  p.dq_acc = pr.deterministic ? nullptr : reinterpret_cast<float*>(ws + L.dq_acc);
+  p.drop = pr.keep < 1.0 ? drop_mask : nullptr;
+  p.drop_bytes = (pr.drop_bits + 7) / 8;
+  p.slopes = alibi_slopes; p.sink = sink;
+  p.cu_q = reinterpret_cast<const int32_t*>(ws + L.cu_q);
+  p.cu_kv = reinterpret_cast<const int32_t*>(ws + L.cu_kv);
+  p.bit_base = reinterpret_cast<const int64_t*>(ws + L.bit_base);
+  p.kv_items = reinterpret_cast<const WorkItem*>(ws + L.items0);
+  p.dq_items = reinterpret_cast<const WorkItem*>(ws + L.items1);
+  p.n_kv_items = (int32_t)kv_items.size();
+  p.n_dq_items = (int32_t)dq_items.size();
+  p.total_q = (int32_t)pr.tq;
+  p.nq = (int32_t)pr.nq;
+  p.nkv = (int32_t)pr.nkv;
+  p.group = (int32_t)(pr.nq / pr.nkv);
+  p.mode = pr.mode;
+  p.pre = (int32_t)fa_clamp_window(pr.pre);
+  p.next = (int32_t)fa_clamp_window(pr.next);
+  p.scale = (float)pr.scale;
+  p.scale_log2 = (float)(pr.scale * 1.4426950408889634);
+  p.inv_keep = (float)(1.0 / pr.keep);
+  p.use_dropout = pr.keep < 1.0 ? 1 : 0;
+  p.head_swizzle = (pr.nq % 8 == 0) ? 1 : 0;
+  p.n_pre_blocks = L.n_pre_blocks;
+  const int dt = pr.dtype, d = (int)pr.d;
+
+  e = timed(K_PRE, s, [&] { return fa::launch_bwd_pre(dt, d, p, s); });
+  if (e == hipSuccess && !pr.deterministic)
+    e = timed(K_ZERO, s, [&] { return fa::launch_zero_f32(p.dq_acc, pr.tq * pr.nq * pr.d, s); });
+  if (e == hipSuccess) e = timed(K_KV, s, [&] { return fa::launch_bwd_kv(dt, d, !pr.deterministic, p, s); });
+  if (e == hipSuccess) {
+    if (pr.deterministic)
+      e = timed(K_DQ, s, [&] { return fa::launch_bwd_dq(dt, d, p, s); });
+    else
+      e = timed(K_CONVERT, s, [&] { return fa::launch_bwd_dq_convert(dt, d, p, s); });
+  }
+  if (e == hipSuccess && sink) e = timed(K_DSINK, s, [&] { return fa::launch_bwd_dsink(p, s); });
+  return hip_status(e);
+}
+
+fa_status fa_debug_schedule(const fa_config* cfg, int32_t pass, int64_t* items, int64_t cap, int64_t* n,
+                            int32_t* tile_rows, int32_t* tile_cols) {
+  if (!n) return FA_ERR_PARAM_NULLPTR;
+  if (pass < 0 || pass > 2) return FA_ERR_PARAM_INVALID;
+  Problem pr;
+  fa_status st = parse(cfg, &pr);
+  if (st != FA_OK) return st;
+  int bm, bn;
+  std::vector<WorkItem> v = schedule(pr, pass, &bm, &bn);
+  *n = (int64_t)v.size();
+  if (tile_rows) *tile_rows = bm;
+  if (tile_cols) *tile_cols = bn;
+  if (items) {
+    const int64_t m = std::min<int64_t>(cap, (int64_t)v.size());
+    for (int64_t i = 0; i < m; ++i) {
+      items[4 * i + 0] = v[i].b;
+      items[4 * i + 1] = v[i].tile;
+      items[4 * i + 2] = v[i].lo;
+      items[4 * i + 3] = v[i].hi;
+    }
+  }
+  return FA_OK;
+}
+
+fa_status fa_profile_enable(int32_t on) {
+  ProfState& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  P.on = on != 0;
+  return FA_OK;
+}
+
+int32_t fa_profile_kernel_count(void) { return K_COUNT; }
+
+fa_status fa_profile_read(int32_t k, const char** name, double* total_ms, int64_t* launches) {
+  if (k < 0 || k >= K_COUNT) return FA_ERR_PARAM_INVALID;
+  ProfState& P = prof();
+  std::lock_guard<std::mutex> g(P.mu);
+  for (auto& pr : P.ev[k]) {
+    if (hipEventSynchronize(pr.second) != hipSuccess) return FA_ERR_HIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess) return FA_ERR_HIP;
+    P.total_ms[k] += ms;
+    P.launches[k] += 1;
+    (void)hipEventDestroy(pr.first);
+    (void)hipEventDestroy(pr.second);
+  }
+  P.ev[k].clear();
+  if (name) *name = kKernelNames[k];
+  if (total_ms) *total_ms = P.total_ms[k];
+  if (launches) *launches = P.launches[k];
+  P.total_ms[k] = 0;
+  P.launches[k] = 0;
+  return FA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,99 @@
+// Device helpers for the gfx950 (CDNA4) attention kernels: MFMA operand types,
+// the LDS transpose read, bf16 rounding and the dropout keep-bit window.
+//
+// MFMA lane layouts used throughout (checked on the device):
+//   v_mfma_f32_32x32x16_bf16  A[m][k]: lane l holds m = l%32, k = 8*(l/32) + 0..7
+//                             B[k][n]: lane l holds n = l%32, k = 8*(l/32) + 0..7
+//                             C[m][n]: lane l, reg r holds n = l%32,
+//                                      m = 8*(r/4) + 4*(l/32) + r%4
+//   v_mfma_f32_32x32x2_f32    A: m = l%32, k = l/32;  B: n = l%32, k = l/32; C as above.
+// ds_read_b64_tr_b16: inside each group of 16 lanes, element e of lane i's
+// result is element i%4 of the 8-byte row addressed by lane 4*e + i/4 of the group.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(float a, float b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Two transposing LDS reads -> one bf16x8 operand (see layout note above).
+__device__ __forceinline__ bf16x8 lds_read_tr_x2(const char* p0, const char* p1) {
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(
+      (lds_char*)(uintptr_t)p0));
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(
+      (lds_char*)(uintptr_t)p1));
+  bf16x8 r;
+  s16x4* rp = reinterpret_cast<s16x4*>(&r);
+  rp[0] = lo;
+  rp[1] = hi;
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 lds_read_b128(const char* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float wave_xor32(float v) { return __shfl_xor(v, 32, 64); }
+
+// bf16 <-> f32 (round to nearest even)
+__device__ __forceinline__ __bf16 to_bf16(float f) { return (__bf16)f; }
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
+  return __uint_as_float(((uint32_t)b) << 16);
+}
+
+template <typename T>
+struct ElemTraits;
+template <>
+struct ElemTraits<__bf16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kChunk = 16;  // k per MFMA
+};
+template <>
+struct ElemTraits<float> {
+  static constexpr int kBytes = 4;
+  static constexpr int kChunk = 2;
+};
+
+// Load one 32-bit word of the packed keep mask; words that reach past the end
+// of the buffer are assembled from the bytes that exist.
+__device__ __forceinline__ uint32_t load_mask_word(const uint8_t* mask, int64_t nbytes, int64_t word) {
+  int64_t byte = word * 4;
+  if (byte + 4 <= nbytes) return *reinterpret_cast<const uint32_t*>(mask + byte);
+  uint32_t v = 0;
+  for (int i = 0; i < 4; ++i)
+    if (byte + i < nbytes && byte + i >= 0) v |= ((uint32_t)mask[byte + i]) << (8 * i);
+  return v;
+}
+
+// 64 consecutive keep bits starting at bit `pos` (LSB = bit pos).
+__device__ __forceinline__ uint64_t load_mask_window(const uint8_t* mask, int64_t nbytes, int64_t pos) {
+  int64_t w = pos >> 5;
+  uint32_t sh = (uint32_t)(pos & 31);
+  uint64_t lo = (uint64_t)load_mask_word(mask, nbytes, w) | ((uint64_t)load_mask_word(mask, nbytes, w + 1) << 32);
+  uint64_t hi = (uint64_t)load_mask_word(mask, nbytes, w + 2);
+  return sh ? ((lo >> sh) | (hi << (64 - sh))) : lo;
+}
+
+}  // namespace fa

@@ -1,0 +1,92 @@
+// Kernel parameter blocks and launch declarations shared by the kernels and
+// the host runtime.  All pointers are device pointers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+// Work item of the forward and dQ passes: one query tile of one sequence,
+// with the half-open range of key tiles that hold at least one allowed pair.
+// For the dK/dV pass `tile` is a key tile and [lo, hi) a range of query tiles.
+struct WorkItem {
+  int32_t b, tile, lo, hi;
+};
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* m_out;
+  float* l_out;
+  const uint8_t* drop;
+  int64_t drop_bytes;
+  const float* slopes;
+  const float* sink;
+  const int32_t* cu_q;
+  const int32_t* cu_kv;
+  const int64_t* bit_base;
+  const WorkItem* items;
+  int32_t n_items;
+  int32_t nq, nkv, group;
+  int32_t mode, pre, next;
+  float scale_log2;   // scale * log2(e)
+  float inv_keep;     // 1 / keep_prob
+  int32_t use_dropout;
+  int32_t head_swizzle;
+};
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dy;
+  const void* o;
+  const float* m_in;
+  const float* l_in;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dsink;
+  float* dq_acc;       // fp32 [T_q, Nq, D] accumulator (atomic variant)
+  float* delta;        // fp32 [T_q, Nq]  rowsum(dY * O)
+  float* lse;          // fp32 [T_q, Nq]  log2-domain log-sum-exp (+inf for empty rows)
+  float* dsink_part;   // fp32 [n_pre_blocks, Nq]
+  const uint8_t* drop;
+  int64_t drop_bytes;
+  const float* slopes;
+  const float* sink;
+  const int32_t* cu_q;
+  const int32_t* cu_kv;
+  const int64_t* bit_base;
+  const int32_t* row_seq;   // sequence index of each query token (preprocess)
+  const WorkItem* kv_items;
+  const WorkItem* dq_items;
+  int32_t n_kv_items, n_dq_items;
+  int32_t total_q;
+  int32_t nq, nkv, group;
+  int32_t mode, pre, next;
+  float scale;
+  float scale_log2;
+  float inv_keep;
+  int32_t use_dropout;
+  int32_t head_swizzle;
+  int32_t n_pre_blocks;
+};
+
+// Tile shapes (rows x keys) of each pass; the host scheduler uses the same numbers.
+constexpr int kFwdBM = 128, kFwdBN = 64;
+constexpr int kKvBN = 128, kKvBM = 32;
+constexpr int kDqBM = 128, kDqBN = 32;
+constexpr int kPreRowsPerBlock = 64;
+
+hipError_t launch_fwd(int dtype, int d, const FwdParams& p, hipStream_t s);
+hipError_t launch_bwd_pre(int dtype, int d, const BwdParams& p, hipStream_t s);
+hipError_t launch_bwd_kv(int dtype, int d, bool atomic_dq, const BwdParams& p, hipStream_t s);
+hipError_t launch_bwd_dq(int dtype, int d, const BwdParams& p, hipStream_t s);
+hipError_t launch_bwd_dq_convert(int dtype, int d, const BwdParams& p, hipStream_t s);
+hipError_t launch_bwd_dsink(const BwdParams& p, hipStream_t s);
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
+
+}  // namespace fa

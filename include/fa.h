@@ -1,0 +1,148 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) varlen FlashAttention library (libfa.so).
+ *
+ * Operations (semantics from the Ascend CANN pages):
+ *   fa_fwd  -- training forward of aclnnFlashAttentionScoreV2 ("Formula",
+ *              pseType 2) in TND layout: O = Dropout(Softmax(Mask(scale*QK^T
+ *              + pse)), keep_prob) V, plus the per-row softmax max and sum,
+ *              with the optional attention sink of
+ *              aclnnFlashAttentionUnpaddingScoreGradV5 (sink formulas).
+ *   fa_bwd  -- training backward of aclnnFlashAttentionUnpaddingScoreGrad
+ *              ("Formula"): dV = P^T dY, dQ = scale * dS K, dK = scale * dS^T Q,
+ *              and dSink of aclnnFlashAttentionUnpaddingScoreGradV5.
+ *
+ * Two phases, as on the pages ("Prototype": GetWorkspaceSize, then execute):
+ * call fa_*_workspace_size for the device workspace a call needs, then fa_fwd /
+ * fa_bwd with a workspace at least that large.
+ *
+ * Layout (TND, the only layout of the varlen grad page): Q, O, dY, dQ are
+ * [T_q, Nq, D], K, V, dK, dV are [T_kv, Nkv, D], contiguous row-major;
+ * element (t, n, d) at (t*N + n)*D + d.  softmax_max / softmax_sum are fp32
+ * [T_q, Nq] (the pages' trailing x8 replication is not stored).  The max is in
+ * natural-log units of the scaled, biased, masked logits (including the sink);
+ * the sum is sum_j exp(s_ij - max) (+ exp(sink - max)), both before dropout.
+ * Rows with no allowed key and no sink get max = -inf, sum = 0, O = 0.
+ *
+ * Ownership: the caller owns every buffer and the stream.  The library
+ * allocates no device memory and keeps no per-call state.  Calls enqueue work
+ * on `stream` (a hipStream_t; NULL = default stream) and return without
+ * synchronising.  cu_seqlens arrays are HOST memory, read during the call and
+ * copied into the workspace, so they may be freed when the call returns.
+ * Two calls that share a workspace must be ordered on the same stream.
+ *
+ * Errors: every argument is validated before anything is enqueued; on error
+ * nothing is written.  Codes 161001 / 161002 mirror ACLNN_ERR_PARAM_NULLPTR /
+ * ACLNN_ERR_PARAM_INVALID of the aclnnFlashAttentionScoreV2 page ("Returns"
+ * table).
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t fa_status;
+#define FA_OK 0
+#define FA_ERR_PARAM_NULLPTR 161001 /* a required pointer argument is NULL */
+#define FA_ERR_PARAM_INVALID 161002 /* an attribute, shape, dtype or alignment is unsupported */
+#define FA_ERR_WORKSPACE 1          /* workspace_bytes smaller than the size query returned */
+#define FA_ERR_HIP 2                /* a HIP runtime call or kernel launch failed */
+
+/* element type of Q, K, V, dY, O, dQ, dK, dV */
+#define FA_DTYPE_FP32 0
+#define FA_DTYPE_BF16 1
+
+/* sparse modes (aclnnFlashAttentionUnpaddingScoreGrad, "sparseMode" parameter) */
+#define FA_SPARSE_NONE 0             /* every pair allowed                                   */
+#define FA_SPARSE_LEFT_UP_CAUSAL 2   /* j <= i                                               */
+#define FA_SPARSE_RIGHT_DOWN_CAUSAL 3 /* j <= i + (Lkv - Lq)                                  */
+#define FA_SPARSE_BAND 4             /* i+(Lkv-Lq)-pre <= j <= i+(Lkv-Lq)+next (inclusive)    */
+
+#define FA_TOKENS_DEFAULT 2147483647 /* preTokens / nextTokens default of the pages */
+
+typedef struct fa_config {
+  int64_t batch;                 /* B >= 1 sequences                                          */
+  const int64_t* cu_seqlens_q;   /* HOST, B+1 entries: [0] = 0, non-decreasing, [B] = T_q     */
+  const int64_t* cu_seqlens_kv;  /* HOST, B+1 entries, same rules, [B] = T_kv               */
+  int64_t head_num;              /* Nq in [1, 256] (headNum)                                  */
+  int64_t num_kv_heads;          /* Nkv; 0 means Nkv = Nq; Nq % Nkv == 0 (GQA)                */
+  int64_t head_dim;              /* D in {64, 128}                                            */
+  int32_t dtype;                 /* FA_DTYPE_*                                                */
+  int32_t sparse_mode;           /* FA_SPARSE_*                                               */
+  double scale;                  /* scaleValue: multiplies Q K^T (usually D^-0.5)             */
+  double keep_prob;              /* keepProb in (0, 1]; < 1 needs drop_mask                   */
+  int64_t pre_tokens;            /* band only: keys allowed left of the diagonal              */
+  int64_t next_tokens;           /* band only: keys allowed right of the diagonal             */
+  int32_t deterministic;         /* bwd: 1 = separate dQ pass (bitwise reproducible),
+                                    0 = fp32 atomic dQ accumulation                           */
+  int32_t flags;                 /* reserved, must be 0                                       */
+} fa_config;
+
+/* Device workspace bytes needed by fa_fwd for this configuration (>= 256). */
+fa_status fa_fwd_workspace_size(const fa_config* cfg, uint64_t* bytes);
+
+/*
+ * Forward.  Inputs (device): q [T_q,Nq,D], k, v [T_kv,Nkv,D] of cfg->dtype.
+ * drop_mask: device uint8, required iff keep_prob < 1: the keep bits of
+ *   aclnnFlashAttentionUnpaddingScoreGrad "dropMaskOptional", one flat stream of
+ *   Nq * sum_b Lq_b*Lkv_b bits ordered (sequence, query head, row, key), bit n in
+ *   byte n/8 at position n%8 (LSB first), 1 = keep; ceil(bits/8) bytes, 4-byte aligned.
+ * alibi_slopes: device fp32 [Nq] or NULL: adds -slope_h*(i-j) after scaling
+ *   (pseType 2, i and j local to the sequence; requires Lq_b == Lkv_b).
+ * sink: device fp32 [Nq] or NULL: per-head sink logit in the softmax denominator.
+ * Outputs (device): out [T_q,Nq,D] of cfg->dtype; softmax_max, softmax_sum fp32 [T_q,Nq].
+ * All tensor pointers must be 16-byte aligned.
+ */
+fa_status fa_fwd(const fa_config* cfg, const void* q, const void* k, const void* v,
+                 const uint8_t* drop_mask, const float* alibi_slopes, const float* sink,
+                 void* out, float* softmax_max, float* softmax_sum,
+                 void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* Device workspace bytes needed by fa_bwd for this configuration. */
+fa_status fa_bwd_workspace_size(const fa_config* cfg, uint64_t* bytes);
+
+/*
+ * Backward.  Inputs are the forward's inputs plus dy [T_q,Nq,D] and the
+ * forward's out, softmax_max and softmax_sum (attentionIn / softmaxMax / softmaxSum).
+ * Outputs (device): dq [T_q,Nq,D], dk, dv [T_kv,Nkv,D] of cfg->dtype, fully
+ * overwritten; dsink fp32 [Nq], required iff sink != NULL.
+ */
+fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void* v, const void* dy,
+                 const void* out, const float* softmax_max, const float* softmax_sum,
+                 const uint8_t* drop_mask, const float* alibi_slopes, const float* sink,
+                 void* dq, void* dk, void* dv, float* dsink,
+                 void* workspace, uint64_t workspace_bytes, void* stream);
+
+/* Static text for a status code. */
+const char* fa_status_string(fa_status status);
+
+/*
+ * Host-only view of the tile scheduler (no device calls).  pass 0 = forward,
+ * 1 = backward dK/dV pass, 2 = backward dQ pass.  Writes up to `cap` items of
+ * 4 int64 each: (sequence, tile, lo, hi) where tile is a query tile (passes 0, 2)
+ * or a key tile (pass 1) and [lo, hi) the range of the other axis' tiles that
+ * hold at least one allowed pair; *n receives the item count.  Items are in
+ * launch order (longest first).  tile_rows / tile_cols receive the pass's tile
+ * shape (query rows, keys) when non-NULL.
+ */
+fa_status fa_debug_schedule(const fa_config* cfg, int32_t pass, int64_t* items, int64_t cap, int64_t* n,
+                            int32_t* tile_rows, int32_t* tile_cols);
+
+/*
+ * Kernel timing for measurement: while enabled, every kernel the library
+ * launches is bracketed by HIP events on its stream.  fa_profile_read
+ * synchronises those events and returns, for kernel index k in [0, count),
+ * its name, total milliseconds and launch count, then clears the record.
+ */
+fa_status fa_profile_enable(int32_t on);
+fa_status fa_profile_read(int32_t k, const char** name, double* total_ms, int64_t* launches);
+int32_t fa_profile_kernel_count(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */

@@ -81,9 +81,10 @@ class _Problem:
 
     def __init__(self, q, k, v, cu_q, cu_kv, head_num, kv_heads, scale, keep_prob, sparse_mode,
                  pre_tokens, next_tokens, drop_mask, alibi_slopes, sink):
-        self.q = np.asarray(q, dtype=np.float64)
-        self.k = np.asarray(k, dtype=np.float64)
-        self.v = np.asarray(v, dtype=np.float64)
+        # kept in their given precision; each (sequence, head) slice is upcast to fp64 when used
+        self.q = np.asarray(q)
+        self.k = np.asarray(k)
+        self.v = np.asarray(v)
         self.cu_q = np.asarray(cu_q, dtype=np.int64)
         self.cu_kv = np.asarray(cu_kv, dtype=np.int64)
         self.nq = int(head_num)
@@ -111,8 +112,8 @@ class _Problem:
         k0, k1 = self.cu_kv[b], self.cu_kv[b + 1]
         lq, lkv = int(q1 - q0), int(k1 - k0)
         g = h // self.group
-        qb = self.q[q0:q1, h, :]
-        kb = self.k[k0:k1, g, :]
+        qb = self.q[q0:q1, h, :].astype(np.float64)
+        kb = self.k[k0:k1, g, :].astype(np.float64)
         s = self.scale * (qb @ kb.T)
         if self.slopes is not None:
             s = s + alibi_pse(lq, lkv, self.slopes[h])
@@ -149,16 +150,16 @@ def _problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, ke
                     sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink)
 
 
-def _selected(batches, n):
-    return range(n) if batches is None else list(batches)
+def _selected(subset, n):
+    return range(n) if subset is None else list(subset)
 
 
 def forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob=1.0,
             sparse_mode=0, pre_tokens=INT_MAX_TOKENS, next_tokens=INT_MAX_TOKENS, drop_mask=None,
-            alibi_slopes=None, sink=None, batches=None):
+            alibi_slopes=None, sink=None, batches=None, heads=None):
     """Attention forward.  Returns O [T_q, Nq, D], softmax max m [T_q, Nq] and
-    softmax sum l [T_q, Nq] (fp64).  With `batches`, only those sequences are
-    computed and every other row is NaN."""
+    softmax sum l [T_q, Nq] (fp64).  With `batches` / `heads`, only those
+    sequences / query heads are computed and every other entry is NaN."""
     pr = _problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob,
                   sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink)
     tq, d = pr.q.shape[0], pr.v.shape[2]
@@ -166,9 +167,9 @@ def forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, kee
     mx = np.full((tq, pr.nq), np.nan)
     sm = np.full((tq, pr.nq), np.nan)
     for b in _selected(batches, pr.batch):
-        for h in range(pr.nq):
+        for h in _selected(heads, pr.nq):
             st = pr.probs(b, h)
-            out[st["q0"]:st["q1"], h, :] = st["pt"] @ pr.v[st["k0"]:st["k1"], st["g"], :]
+            out[st["q0"]:st["q1"], h, :] = st["pt"] @ pr.v[st["k0"]:st["k1"], st["g"], :].astype(np.float64)
             mx[st["q0"]:st["q1"], h] = st["m"]
             sm[st["q0"]:st["q1"], h] = st["l"]
     return out, mx, sm
@@ -176,13 +177,15 @@ def forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, kee
 
 def backward(q, k, v, dy, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob=1.0,
              sparse_mode=0, pre_tokens=INT_MAX_TOKENS, next_tokens=INT_MAX_TOKENS, drop_mask=None,
-             alibi_slopes=None, sink=None, batches=None):
+             alibi_slopes=None, sink=None, batches=None, heads=None):
     """Attention backward.  Returns dQ [T_q, Nq, D], dK, dV [T_kv, Nkv, D] and
-    dSink [Nq] (None without a sink).  With `batches`, only those sequences
-    contribute (rows/keys of other sequences are NaN; dSink sums the chosen ones)."""
+    dSink [Nq] (None without a sink).  With `batches` / `heads`, only those
+    sequences / query heads contribute: rows and keys of other sequences are NaN,
+    dK/dV of a kv head are complete only if all of its query heads are chosen,
+    and dSink sums the chosen sequences."""
     pr = _problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob,
                   sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink)
-    dy = np.asarray(dy, dtype=np.float64)
+    dy = np.asarray(dy)
     dq = np.full(pr.q.shape, np.nan)
     dk = np.full(pr.k.shape, np.nan)
     dv = np.full(pr.v.shape, np.nan)
@@ -192,13 +195,13 @@ def backward(q, k, v, dy, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale
         dq[q0:q1] = 0.0
         dk[k0:k1] = 0.0
         dv[k0:k1] = 0.0
-        for h in range(pr.nq):
+        for h in _selected(heads, pr.nq):
             st = pr.probs(b, h)
             g = st["g"]
-            dyb = dy[q0:q1, h, :]
-            vb = pr.v[k0:k1, g, :]
-            kb = pr.k[k0:k1, g, :]
-            qb = pr.q[q0:q1, h, :]
+            dyb = dy[q0:q1, h, :].astype(np.float64)
+            vb = pr.v[k0:k1, g, :].astype(np.float64)
+            kb = pr.k[k0:k1, g, :].astype(np.float64)
+            qb = pr.q[q0:q1, h, :].astype(np.float64)
             # dV = P~^T dY
             dv[k0:k1, g, :] += st["pt"].T @ dyb
             # dP = (dY V^T) * z / keep  (gradient w.r.t. the pre-dropout P)

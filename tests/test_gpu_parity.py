@@ -1,0 +1,153 @@
+"""GPU parity: libfa.so (through the C ABI) against the fp64 oracle on the same
+seeded inputs.  Tolerances: max relative L2 error 1e-5 for fp32 inputs and
+2e-2 for bf16 inputs (fp32 accumulation), per output tensor."""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from harness import TOL, compare, device_inputs, kv_heads_complete, run_gpu, run_oracle, say
+
+pytestmark = pytest.mark.gpu
+
+F32, BF16 = torch.float32, torch.bfloat16
+
+# small cases spanning several tiles, ragged tails and the degenerate situations
+EDGE_CASES = {
+    "cross_attn_nomask": dict(lens_q=[5, 130, 64], lens_kv=[70, 33, 200], head_num=4, kv_heads=2, head_dim=64,
+                              sparse_mode=0),
+    "rdcausal_lq_gt_lkv": dict(lens_q=[150, 40], lens_kv=[60, 40], head_num=2, kv_heads=1, head_dim=128,
+                               sparse_mode=3),
+    "lucausal_lq_ne_lkv": dict(lens_q=[90, 200], lens_kv=[300, 65], head_num=2, kv_heads=2, head_dim=128,
+                               sparse_mode=2),
+    "band_gqa": dict(lens_q=[300, 129, 1], head_num=6, kv_heads=3, head_dim=128, sparse_mode=4, pre_tokens=37,
+                     next_tokens=11),
+    "band_neg_pre": dict(lens_q=[257, 64], head_num=2, kv_heads=2, head_dim=64, sparse_mode=4, pre_tokens=-5,
+                         next_tokens=40),
+    "zero_length_seqs": dict(lens_q=[0, 77, 0, 150], lens_kv=[10, 77, 0, 150], head_num=3, kv_heads=1,
+                             head_dim=128, sparse_mode=3),
+    "all_features": dict(lens_q=[37, 200, 129], head_num=4, kv_heads=2, head_dim=128, sparse_mode=3,
+                         keep_prob=0.8, alibi=True, sink=True),
+    "d64_causal_varlen": dict(lens_q=[33, 513, 128], head_num=8, kv_heads=2, head_dim=64, sparse_mode=3),
+    "single_tokens": dict(lens_q=[1, 1, 2], head_num=2, kv_heads=1, head_dim=128, sparse_mode=3, sink=True),
+    "sink_dropout_band": dict(lens_q=[190, 67], head_num=2, kv_heads=1, head_dim=64, sparse_mode=4,
+                              pre_tokens=50, next_tokens=3, keep_prob=0.7, sink=True),
+}
+
+
+def _edge(name, dtype, seed):
+    kw = dict(EDGE_CASES[name])
+    lq = kw.pop("lens_q")
+    lkv = kw.pop("lens_kv", None)
+    return wl.make_case(name, lq, lkv, dtype=dtype, seed=seed, **kw)
+
+
+@pytest.mark.parametrize("deterministic", [True, False])
+@pytest.mark.parametrize("dtype", [F32, BF16])
+@pytest.mark.parametrize("name", list(EDGE_CASES))
+def test_edge_case(name, dtype, deterministic):
+    seed = 100 + list(EDGE_CASES).index(name)
+    case = _edge(name, dtype, seed)
+    say(f"edge {name} dtype={dtype} det={deterministic} seed={seed} lens={list(case.lens_q)}/{list(case.lens_kv)}")
+    gpu = run_gpu(case, deterministic)
+    ref = run_oracle(case)
+    compare(gpu, ref, TOL[dtype])
+
+
+@pytest.mark.parametrize("deterministic", [True, False])
+def test_workload1_fp32_full(deterministic):
+    case = wl.make_workload(1)
+    say(f"workload 1 full det={deterministic}")
+    compare(run_gpu(case, deterministic), run_oracle(case), TOL[F32])
+
+
+@pytest.fixture(scope="module")
+def workload2():
+    return wl.make_workload(2)
+
+
+@pytest.mark.parametrize("deterministic", [True, False])
+def test_workload2_sampled_sequences(workload2, deterministic):
+    case = workload2
+    batches = [2, 7, 1]   # lengths 337, 304, 630; every head
+    say(f"workload 2 det={deterministic} batches={batches}")
+    gpu = run_gpu(case, deterministic)
+    ref = run_oracle(case, batches=batches)
+    compare(gpu, ref, TOL[BF16])
+
+
+def test_deterministic_is_bitwise_reproducible(workload2):
+    case = workload2
+    say("workload 2 determinism")
+    x = device_inputs(case)
+    a = run_gpu(case, True, inputs=x)
+    b = run_gpu(case, True, inputs=x)
+    for key in ("out", "m", "l", "dq", "dk", "dv"):
+        assert np.array_equal(a[key], b[key]), key
+
+
+def test_dropout_keep_bits_bit_exact():
+    # Q = 0 makes every allowed logit equal, and V = I maps key j to column j, so
+    # O[i, j] = z_ij / (keep * n_i): its non-zero pattern is the keep bits.
+    lens = [37, 128, 101]
+    keep = 0.6
+    case = wl.make_case("dropout_probe", lens, head_num=2, kv_heads=1, head_dim=128, dtype=BF16, keep_prob=keep,
+                        seed=7)
+    case.q.zero_()
+    v = torch.zeros_like(case.v)
+    for b in range(len(lens)):
+        s = int(case.cu_seqlens_kv[b])
+        for j in range(lens[b]):
+            v[s + j, 0, j] = 1.0
+    case.v = v
+    say("dropout bit-exact probe")
+    gpu = run_gpu(case, True, backward=False)
+    bits = np.unpackbits(case.drop_mask, bitorder="little")
+    off = 0
+    for b, L in enumerate(lens):
+        s = int(case.cu_seqlens_q[b])
+        for h in range(2):
+            z = bits[off:off + L * L].reshape(L, L).astype(bool)
+            off += L * L
+            got = gpu["out"][s:s + L, h, :L] != 0
+            assert np.array_equal(got, z), (b, h)
+
+
+@pytest.mark.parametrize("deterministic", [True, False])
+def test_workload3_sampled_heads(deterministic):
+    case = wl.make_workload(3)
+    batches, heads = [0], [0, 21]
+    say(f"workload 3 det={deterministic} batches={batches} heads={heads}")
+    gpu = run_gpu(case, deterministic)
+    ref = run_oracle(case, batches=batches, heads=heads)
+    compare(gpu, ref, TOL[BF16], kv_select=kv_heads_complete(case, heads))
+
+
+@pytest.mark.parametrize("deterministic", [True, False])
+def test_workload4_sampled_heads(deterministic):
+    case = wl.make_workload(4)
+    batches, heads = [0, 15], [0, 9]
+    say(f"workload 4 det={deterministic} batches={batches} heads={heads}")
+    gpu = run_gpu(case, deterministic)
+    ref = run_oracle(case, batches=batches, heads=heads)
+    compare(gpu, ref, TOL[BF16], kv_select=kv_heads_complete(case, heads))
+
+
+def test_workload5_sampled_sequences_and_dsink_identity():
+    case = wl.make_workload(5)
+    lens = case.lens_q
+    order = np.argsort(lens)
+    batches = [int(order[0]), int(order[1]), int(order[len(order) // 2])]
+    say(f"workload 5 batches={batches} lens={[int(lens[b]) for b in batches]}")
+    gpu = run_gpu(case, True)
+    ref = run_oracle(case, batches=batches)
+    compare(gpu, ref, TOL[BF16], keys=("out", "m", "l", "dq", "dk", "dv"))
+    # dSink over the whole batch: -sum_i exp(sink_h - m_i) / l_i * rowsum(dY * O), from the
+    # device's own O, m, l (each checked against the oracle above) in fp64
+    dy = case.dy.double().numpy()
+    delta = np.einsum("tnd,tnd->tn", dy, gpu["out"])
+    p_sink = np.exp(case.sink.astype(np.float64)[None, :] - gpu["m"]) / gpu["l"]
+    expect = -(p_sink * delta).sum(axis=0)
+    err = np.linalg.norm(gpu["dsink"] - expect) / np.linalg.norm(expect)
+    say(f"dsink identity relL2={err:.2e}")
+    assert err <= TOL[BF16]
