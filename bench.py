@@ -1,0 +1,230 @@
+"""Throughput benchmark of the varlen FlashAttention forward + backward on one MI355X.
+
+One step = one full pass of the path over the packed workload: host validation
+and tile scheduling, the forward kernel, the backward preprocess, the dK/dV
+pass, the dQ pass and the dSink reduction.  Inputs are generated once, are
+resident in HBM before timing starts, and are synthetic (seeded normal draws of
+the workload's shapes; the pages name no dataset).
+
+Prints ONE JSON line (metric, value, roofline of the dominant kernel, CPU
+baseline of the fp64 oracle on a bounded sample).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 5] [--atomic-dq]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA (published)
+PEAK_FP32_TFLOPS = 157.3       # MI355X fp32 (published)
+HBM_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "attention_fa_fwd_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def flops_of(case):
+    import workloads as wl
+    pairs = wl.allowed_pairs(case.lens_q, case.lens_kv, case.head_num, case.sparse_mode, case.pre_tokens,
+                             case.next_tokens)
+    d = case.head_dim
+    return pairs, 4.0 * d * pairs, 10.0 * d * pairs
+
+
+def cpu_baseline(case, budget_s: float = 12.0):
+    """The fp64 oracle (as it stands) on a bounded sample of the same workload:
+    (sequence, kv-group) units taken in a fixed order (sequences nearest the
+    median length first) until the time budget is spent."""
+    import oracle
+    import workloads as wl
+    cores = len(os.sched_getaffinity(0))
+    g = case.head_num // case.kv_heads
+    lens = case.lens_q
+    order = np.argsort(np.abs(lens - np.median(lens)), kind="stable")
+    q = case.q.float().numpy()
+    k = case.k.float().numpy()
+    v = case.v.float().numpy()
+    dy = case.dy.float().numpy()
+    kw = dict(keep_prob=case.keep_prob, sparse_mode=case.sparse_mode, pre_tokens=case.pre_tokens,
+              next_tokens=case.next_tokens, drop_mask=case.drop_mask, alibi_slopes=case.alibi_slopes,
+              sink=case.sink)
+    done_pairs, units, t_total = 0, [], 0.0
+    for b in order:
+        for grp in range(case.kv_heads):
+            heads = list(range(grp * g, grp * g + g))
+            t0 = time.perf_counter()
+            oracle.forward(q, k, v, case.cu_seqlens_q, case.cu_seqlens_kv, case.head_num, case.kv_heads,
+                           case.scale, batches=[int(b)], heads=heads, **kw)
+            oracle.backward(q, k, v, dy, case.cu_seqlens_q, case.cu_seqlens_kv, case.head_num, case.kv_heads,
+                            case.scale, batches=[int(b)], heads=heads, **kw)
+            t_total += time.perf_counter() - t0
+            L = int(lens[b])
+            done_pairs += wl.allowed_pairs([L], [int(case.lens_kv[b])], len(heads), case.sparse_mode,
+                                           case.pre_tokens, case.next_tokens)
+            units.append((int(b), grp, L))
+            if t_total >= budget_s:
+                break
+        if t_total >= budget_s:
+            break
+    fl = 14.0 * case.head_dim * done_pairs
+    return {
+        "value": fl / t_total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"fp64 numpy oracle fwd+bwd on {len(units)} (sequence, kv-group) units of this workload "
+                   f"(lengths {sorted(set(u[2] for u in units))}, {g} query heads each), {done_pairs} allowed "
+                   f"pairs in {t_total:.1f} s; mask-aware 14*D FLOP per pair"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=5)
+    ap.add_argument("--atomic-dq", action="store_true", help="time the fp32-atomic dQ variant")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the path is a single-GPU kernel library and no multi-GPU "
+              f"run is part of this build (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import attention_fa_fwd_amd as fa
+    import workloads as wl
+
+    fa.lib()   # fail loudly if libfa.so was not built
+    dev = torch.device("cuda:0")
+    log(f"generating workload {args.workload}")
+    case = wl.make_workload(args.workload)
+    pairs, f_fwd, f_bwd = flops_of(case)
+    deterministic = not args.atomic_dq
+    cfg = fa.Config(case.cu_seqlens_q, case.cu_seqlens_kv, case.head_num, case.kv_heads, case.head_dim,
+                    case.dtype, case.scale, case.keep_prob, case.sparse_mode, case.pre_tokens, case.next_tokens,
+                    deterministic)
+    q, k, v, dy = (t.to(dev) for t in (case.q, case.k, case.v, case.dy))
+    drop = torch.from_numpy(case.drop_mask).to(dev) if case.drop_mask is not None else None
+    slopes = torch.from_numpy(case.alibi_slopes).to(dev) if case.alibi_slopes is not None else None
+    sink = torch.from_numpy(case.sink).to(dev) if case.sink is not None else None
+    out = torch.empty_like(q)
+    tq = q.shape[0]
+    m = torch.empty((tq, case.head_num), dtype=torch.float32, device=dev)
+    l = torch.empty_like(m)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    dsink = torch.empty((case.head_num,), dtype=torch.float32, device=dev) if sink is not None else None
+    ws_f = torch.empty(fa.fa_fwd_workspace_size(cfg), dtype=torch.uint8, device=dev)
+    ws_b = torch.empty(fa.fa_bwd_workspace_size(cfg), dtype=torch.uint8, device=dev)
+
+    def step():
+        fa.fa_fwd(cfg, q, k, v, drop, slopes, sink, out, m, l, workspace=ws_f)
+        fa.fa_bwd(cfg, q, k, v, dy, out, m, l, drop, slopes, sink, dq, dk, dv, dsink, workspace=ws_b)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    log(f"timing {args.steps} steps")
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    log(f"{ms_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f})")
+
+    # per-kernel durations: HIP events the library records around each launch, over the same
+    # number of steps, on the stream each kernel is launched on
+    fa.fa_profile_read()
+    fa.fa_profile_enable(True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    kern = fa.fa_profile_read()
+    fa.fa_profile_enable(False)
+    kern = {name: (ms, n) for name, (ms, n) in kern.items() if n > 0}
+    fwd_ms = kern["fa_fwd"][0] / kern["fa_fwd"][1]
+    dom = max(kern, key=lambda n: kern[n][0])
+    dom_ms = kern[dom][0] / kern[dom][1]
+    d = case.head_dim
+    # algorithmic FLOP of each kernel per launch (mask-aware pair count x per-pair work)
+    per_pair = {"fa_fwd": 4 * d, "fa_bwd_dkdv": (10 if not deterministic else 8) * d, "fa_bwd_dq": 2 * d}
+    peak = PEAK_BF16_TFLOPS if case.dtype.is_floating_point and case.q.element_size() == 2 else PEAK_FP32_TFLOPS
+    if dom in per_pair:
+        achieved = per_pair[dom] * pairs / (dom_ms * 1e-3) / 1e12
+        bound, unit, pk = "mfma", "TFLOP/s", peak
+    else:
+        achieved, bound, unit, pk = None, "hbm", "GB/s", HBM_GBS
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        tf = json.load(open(TRAFFIC_FILE))
+        ent = tf.get(f"workload{args.workload}", {}).get(dom)
+        if ent and ent.get("source_hash") == kernel_source_hash():
+            traffic = ent.get("bytes_per_launch")
+
+    total_flops = f_fwd + f_bwd
+    value = total_flops / (ms_step * 1e-3) / 1e12
+    res = {
+        "metric": "attention fwd+bwd TFLOP/s (mask-aware) bf16 D=128; % of MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if case.q.element_size() == 2 else "fp32",
+        "data": "synthetic",
+        "config": {"workload": wl.WORKLOAD_NAMES[args.workload], "total_tokens": int(tq),
+                   "sequences": int(case.batch), "heads_q": case.head_num, "heads_kv": case.kv_heads,
+                   "head_dim": d, "allowed_pairs": int(pairs),
+                   "dq_variant": "deterministic" if deterministic else "atomic"},
+        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+        "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
+        "kernels_ms": {n: round(ms / c, 4) for n, (ms, c) in kern.items()},
+        "roofline": {"bound": bound, "kernel": dom,
+                     "achieved": None if achieved is None else round(achieved, 2),
+                     "peak": pk, "unit": unit,
+                     "frac": None if achieved is None else round(achieved / pk, 4),
+                     "traffic": traffic},
+        "note": "the pages give API constraints but no throughput figures of their own",
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 oracle, bounded sample)")
+        res["cpu_baseline"] = cpu_baseline(case)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -192,10 +192,11 @@ def backward(q, k, v, dy, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale
     dsink = np.zeros(pr.nq) if pr.sink is not None else None
     for b in _selected(batches, pr.batch):
         q0, q1, k0, k1 = pr.cu_q[b], pr.cu_q[b + 1], pr.cu_kv[b], pr.cu_kv[b + 1]
-        dq[q0:q1] = 0.0
-        dk[k0:k1] = 0.0
-        dv[k0:k1] = 0.0
-        for h in _selected(heads, pr.nq):
+        chosen = list(_selected(heads, pr.nq))
+        for g in sorted({h // pr.group for h in chosen}):
+            dk[k0:k1, g] = 0.0
+            dv[k0:k1, g] = 0.0
+        for h in chosen:
             st = pr.probs(b, h)
             g = st["g"]
             dyb = dy[q0:q1, h, :].astype(np.float64)

@@ -422,3 +422,22 @@ def test_workload_lengths_and_pairs():
         bf = sum(int(oracle.allowed(L, L, mode, pre, nxt).sum()) for L in lens) * 3
         assert wl.allowed_pairs(lens, lens, 3, mode, pre, nxt) == bf
     assert wl.dropout_bits_total(wl.workload_lengths(4), wl.workload_lengths(4), 16) == 2 ** 30
+
+
+def test_subset_selection_matches_full_run():
+    lens = [9, 6, 11]
+    cu = _cu(lens)
+    t, nq, nkv, d = cu[-1], 4, 2, 4
+    q, k, v, dy = _rand(60, t, nq, d), _rand(61, t, nkv, d), _rand(62, t, nkv, d), _rand(63, t, nq, d)
+    full = oracle.backward(q, k, v, dy, cu, cu, nq, nkv, 0.5, sparse_mode=3)
+    fo = oracle.forward(q, k, v, cu, cu, nq, nkv, 0.5, sparse_mode=3)
+    sub = oracle.backward(q, k, v, dy, cu, cu, nq, nkv, 0.5, sparse_mode=3, batches=[2, 0], heads=[2, 3])
+    so = oracle.forward(q, k, v, cu, cu, nq, nkv, 0.5, sparse_mode=3, batches=[2, 0], heads=[2, 3])
+    rows = np.r_[cu[0]:cu[1], cu[2]:cu[3]]
+    for a, b in ((fo[0], so[0]), (full[0], sub[0])):
+        np.testing.assert_array_equal(b[rows][:, 2:], a[rows][:, 2:])
+        assert np.all(np.isnan(b[rows][:, :2])) and np.all(np.isnan(b[cu[1]:cu[2]]))
+    # kv head 1 owns query heads 2 and 3: complete; kv head 0 untouched (NaN)
+    for a, b in ((full[1], sub[1]), (full[2], sub[2])):
+        np.testing.assert_array_equal(b[rows][:, 1], a[rows][:, 1])
+        assert np.all(np.isnan(b[rows][:, 0]))
