@@ -108,6 +108,8 @@ def main():
     ap.add_argument("--workload", type=int, default=5)
     ap.add_argument("--atomic-dq", action="store_true", help="time the fp32-atomic dQ variant")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes (calibrates the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: the path is a single-GPU kernel library and no multi-GPU "
@@ -120,6 +122,14 @@ def main():
 
     fa.lib()   # fail loudly if libfa.so was not built
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        src = torch.ones(args.copy_calibration // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_calibration}), flush=True)
+        return
     log(f"generating workload {args.workload}")
     case = wl.make_workload(args.workload)
     pairs, f_fwd, f_bwd = flops_of(case)

@@ -1,0 +1,199 @@
+"""CPU-only checks of the C ABI: exported symbols, argument validation (every
+rejected call returns before any device work), and the tile scheduler's
+work lists against brute-force enumeration of the oracle's mask."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import attention_fa_fwd_amd as fa
+import oracle
+import workloads as wl
+from attention_fa_fwd_amd._lib import FaConfig
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+def test_library_exports_every_declared_symbol():
+    text = open(HEADER).read()
+    declared = set(re.findall(r"^\s*(?:fa_status|const char\*|int32_t)\s+(fa_\w+)\s*\(", text, re.M))
+    assert declared == set(fa.EXPORTED), declared ^ set(fa.EXPORTED)
+    L = fa.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    for code in (fa.FA_OK, fa.FA_ERR_PARAM_NULLPTR, fa.FA_ERR_PARAM_INVALID, fa.FA_ERR_WORKSPACE, fa.FA_ERR_HIP):
+        assert fa.status_string(code).startswith("FA_")
+    assert fa.FA_ERR_PARAM_NULLPTR == 161001 and fa.FA_ERR_PARAM_INVALID == 161002
+
+
+def _cfg(**over):
+    base = dict(cu_seqlens_q=[0, 5, 12], cu_seqlens_kv=[0, 5, 12], head_num=4, kv_heads=2, head_dim=128,
+                dtype=fa.FA_DTYPE_BF16, scale=0.1, keep_prob=1.0, sparse_mode=3, pre_tokens=fa.TOKENS_DEFAULT,
+                next_tokens=fa.TOKENS_DEFAULT, deterministic=True)
+    base.update(over)
+    return fa.Config(**base)
+
+
+FAKE = ctypes.c_void_p(0x10000)   # aligned, never dereferenced: every call below fails validation first
+
+
+def _fwd(cfg, **ptr):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, drop=None, slopes=None, sink=None, out=FAKE, m=FAKE, l=FAKE, ws=FAKE,
+             ws_bytes=1 << 40)
+    p.update(ptr)
+    c = None if cfg is None else cfg.ref
+    return fa.lib().fa_fwd(c, p["q"], p["k"], p["v"], p["drop"], p["slopes"], p["sink"], p["out"], p["m"],
+                           p["l"], p["ws"], ctypes.c_uint64(p["ws_bytes"]), None)
+
+
+def _bwd(cfg, **ptr):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, dy=FAKE, out=FAKE, m=FAKE, l=FAKE, drop=None, slopes=None, sink=None,
+             dq=FAKE, dk=FAKE, dv=FAKE, dsink=None, ws=FAKE, ws_bytes=1 << 40)
+    p.update(ptr)
+    return fa.lib().fa_bwd(cfg.ref, p["q"], p["k"], p["v"], p["dy"], p["out"], p["m"], p["l"], p["drop"],
+                           p["slopes"], p["sink"], p["dq"], p["dk"], p["dv"], p["dsink"], p["ws"],
+                           ctypes.c_uint64(p["ws_bytes"]), None)
+
+
+INVALID_CONFIGS = {
+    "head_dim_96": dict(head_dim=96),
+    "gqa_not_divisible": dict(head_num=4, kv_heads=3),
+    "too_many_heads": dict(head_num=512, kv_heads=512),
+    "keep_zero": dict(keep_prob=0.0),
+    "keep_above_one": dict(keep_prob=1.5),
+    "mode_1": dict(sparse_mode=1),
+    "mode_5": dict(sparse_mode=5),
+    "mode_6": dict(sparse_mode=6),
+    "band_without_intersection": dict(sparse_mode=4, pre_tokens=-3, next_tokens=2),
+    "cu_not_monotone": dict(cu_seqlens_q=[0, 7, 5], cu_seqlens_kv=[0, 7, 5]),
+    "cu_not_starting_at_zero": dict(cu_seqlens_q=[1, 5, 12]),
+    "too_many_tokens": dict(cu_seqlens_q=[0, 1 << 20, (1 << 20) + 1], cu_seqlens_kv=[0, 5, 12]),
+    "empty_batch": dict(cu_seqlens_q=[0, 0, 0], cu_seqlens_kv=[0, 0, 0]),
+    "bad_dtype": dict(dtype=7),
+    "non_finite_scale": dict(scale=float("inf")),
+}
+
+
+@pytest.mark.parametrize("name", list(INVALID_CONFIGS))
+def test_invalid_configs_rejected(name):
+    cfg = _cfg(**INVALID_CONFIGS[name])
+    assert _fwd(cfg) == fa.FA_ERR_PARAM_INVALID
+    assert _bwd(cfg) == fa.FA_ERR_PARAM_INVALID
+    n = ctypes.c_uint64(0)
+    assert fa.lib().fa_fwd_workspace_size(cfg.ref, ctypes.byref(n)) == fa.FA_ERR_PARAM_INVALID
+
+
+def test_bad_flags_and_batch_limits():
+    cfg = _cfg()
+    cfg.c.flags = 1
+    assert _fwd(cfg) == fa.FA_ERR_PARAM_INVALID
+    cfg = _cfg()
+    cfg.c.deterministic = 2
+    assert _bwd(cfg) == fa.FA_ERR_PARAM_INVALID
+    cu = np.zeros(20002, np.int64)
+    cu[1:] = np.arange(1, 20002)
+    assert _fwd(_cfg(cu_seqlens_q=cu, cu_seqlens_kv=cu)) == fa.FA_ERR_PARAM_INVALID
+
+
+def test_null_pointers():
+    assert _fwd(None) == fa.FA_ERR_PARAM_NULLPTR
+    cfg = _cfg()
+    cfg.c.cu_seqlens_q = None
+    assert _fwd(cfg) == fa.FA_ERR_PARAM_NULLPTR
+    for key in ("q", "k", "v", "out", "m", "l", "ws"):
+        assert _fwd(_cfg(), **{key: None}) == fa.FA_ERR_PARAM_NULLPTR, key
+    for key in ("q", "k", "v", "dy", "out", "m", "l", "dq", "dk", "dv", "ws"):
+        assert _bwd(_cfg(), **{key: None}) == fa.FA_ERR_PARAM_NULLPTR, key
+    # keep_prob < 1 needs the keep mask; a sink needs a dSink output
+    assert _fwd(_cfg(keep_prob=0.9)) == fa.FA_ERR_PARAM_NULLPTR
+    assert _bwd(_cfg(), sink=FAKE) == fa.FA_ERR_PARAM_NULLPTR
+    n = ctypes.c_uint64(0)
+    assert fa.lib().fa_fwd_workspace_size(_cfg().ref, None) == fa.FA_ERR_PARAM_NULLPTR
+    assert fa.lib().fa_fwd_workspace_size(_cfg().ref, ctypes.byref(n)) == fa.FA_OK and n.value > 0
+
+
+def test_alignment_alibi_and_workspace_rules():
+    odd = ctypes.c_void_p(0x10008)
+    assert _fwd(_cfg(), q=odd) == fa.FA_ERR_PARAM_INVALID
+    assert _fwd(_cfg(keep_prob=0.5), drop=ctypes.c_void_p(0x10002)) == fa.FA_ERR_PARAM_INVALID
+    # ALiBi (pseType 2) needs Lq == Lkv per sequence and no empty sequence
+    assert _fwd(_cfg(cu_seqlens_kv=[0, 6, 12]), slopes=FAKE) == fa.FA_ERR_PARAM_INVALID
+    assert _fwd(_cfg(cu_seqlens_q=[0, 0, 12], cu_seqlens_kv=[0, 0, 12]), slopes=FAKE) == fa.FA_ERR_PARAM_INVALID
+    assert _fwd(_cfg(), ws_bytes=16) == fa.FA_ERR_WORKSPACE
+    assert _bwd(_cfg(), ws_bytes=16) == fa.FA_ERR_WORKSPACE
+    assert _bwd(_cfg(deterministic=False), ws_bytes=fa.fa_bwd_workspace_size(_cfg())) == fa.FA_ERR_WORKSPACE
+
+
+def test_atomic_variant_needs_a_larger_workspace():
+    det = fa.fa_bwd_workspace_size(_cfg(deterministic=True))
+    atom = fa.fa_bwd_workspace_size(_cfg(deterministic=False))
+    assert atom >= det + 4 * 12 * 4 * 128
+
+
+# --------------------------------------------------------------------------- scheduler
+
+def _brute_ranges(lq, lkv, mode, pre, nxt, bm, bn, by_kv):
+    ok = oracle.allowed(lq, lkv, mode, pre, nxt)
+    res = []
+    if by_kv:
+        for t in range((lkv + bn - 1) // bn):
+            cols = ok[:, t * bn:(t + 1) * bn].any(axis=1)
+            tiles = sorted({i // bm for i in np.nonzero(cols)[0]})
+            res.append((t, tiles))
+    else:
+        for t in range((lq + bm - 1) // bm):
+            rows = ok[t * bm:(t + 1) * bm, :].any(axis=0)
+            tiles = sorted({j // bn for j in np.nonzero(rows)[0]})
+            res.append((t, tiles))
+    return res
+
+
+SCHED_CASES = [
+    ([300, 0, 129, 1000], [300, 0, 129, 1000], 3, 0, 0),
+    ([300, 77, 129], [500, 10, 129], 3, 0, 0),
+    ([90, 200, 513], [300, 65, 513], 2, 0, 0),
+    ([600, 129, 1], None, 4, 37, 11),
+    ([1000, 257], None, 4, -20, 70),
+    ([1000, 257], [700, 300], 4, 100, 0),
+    ([333, 64], [129, 500], 0, 0, 0),
+    ([2048, 2048], None, 4, 2048, 0),
+]
+
+
+@pytest.mark.parametrize("lq,lkv,mode,pre,nxt", SCHED_CASES)
+@pytest.mark.parametrize("pass_id", [0, 1, 2])
+def test_schedule_matches_brute_force(lq, lkv, mode, pre, nxt, pass_id):
+    lkv = lq if lkv is None else lkv
+    cfg = _cfg(cu_seqlens_q=wl.cu_from_lengths(lq), cu_seqlens_kv=wl.cu_from_lengths(lkv), sparse_mode=mode,
+               pre_tokens=pre, next_tokens=nxt)
+    items, (bm, bn) = fa.fa_debug_schedule(cfg, pass_id)
+    costs = items[:, 3] - items[:, 2]
+    assert np.all(np.diff(costs) <= 0), "items must be ordered longest first"
+    seen = {}
+    for b, tile, lo, hi in items.tolist():
+        seen[(b, tile)] = (lo, hi)
+    expect_keys = set()
+    for b in range(len(lq)):
+        for t, tiles in _brute_ranges(lq[b], lkv[b], mode, pre, nxt, bm, bn, by_kv=(pass_id == 1)):
+            expect_keys.add((b, t))
+            lo, hi = seen[(b, t)]
+            got = list(range(lo, hi))
+            assert got == tiles, (b, t, got, tiles)
+    assert set(seen) == expect_keys and len(items) == len(expect_keys)
+
+
+def test_schedule_of_workload5_skips_upper_triangle():
+    lens = wl.workload_lengths(5)
+    cfg = _cfg(cu_seqlens_q=wl.cu_from_lengths(lens), cu_seqlens_kv=wl.cu_from_lengths(lens), head_num=64,
+               kv_heads=8)
+    items, (bm, bn) = fa.fa_debug_schedule(cfg, 0)
+    visited = int((items[:, 3] - items[:, 2]).sum())
+    dense = int(sum(((L + bm - 1) // bm) * ((L + bn - 1) // bn) for L in lens))
+    # a causal mask keeps a little over half of the tiles
+    assert 0.45 * dense < visited < 0.56 * dense
