@@ -15,7 +15,8 @@ import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libfa.so")
+# FA_LIBRARY selects another build of the same library (tuning experiments)
+LIB_PATH = os.environ.get("FA_LIBRARY") or os.path.join(_PKG, "libfa.so")
 
 FA_OK = 0
 FA_ERR_PARAM_NULLPTR = 161001

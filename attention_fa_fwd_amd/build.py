@@ -35,15 +35,17 @@ def _run(cmd):
     return r.returncode, "\n".join(lines)
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link libfa.so; returns the library path."""
-    build_dir = os.path.join(PKG, "_build")
+def build(verbose: bool = False, target: str = LIB, defines=()) -> str:
+    """Compile every source and link libfa.so (or `target`); returns the library path."""
+    build_dir = (os.path.join(PKG, "_build") if target == LIB
+                 else os.path.join(os.path.dirname(target), "_build_" + os.path.basename(target)))
     os.makedirs(build_dir, exist_ok=True)
     objs, cmds = [], []
     for src in SOURCES:
         obj = os.path.join(build_dir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([hipcc()] + common_flags() + ["-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([hipcc()] + common_flags() + [f"-D{d}" for d in defines] +
+                    ["-c", os.path.join(CSRC, src), "-o", obj])
     with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
         results = list(ex.map(_run, cmds))
     for cmd, (rc, out) in zip(cmds, results):
@@ -51,12 +53,12 @@ def build(verbose: bool = False) -> str:
             print(out)
         if rc != 0:
             raise RuntimeError(f"hipcc failed ({rc}) for {cmd[-3]}:\n{out}")
-    tmp = LIB + ".tmp"
+    tmp = target + ".tmp"
     rc, out = _run([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs)
     if rc != 0:
         raise RuntimeError(f"link failed ({rc}):\n{out}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, target)
+    return target
 
 
 if __name__ == "__main__":

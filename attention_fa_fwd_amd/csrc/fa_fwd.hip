@@ -8,47 +8,49 @@
 //   O_i  = sum_j e^(s_ij - m_i) z_ij v_j / (keep * l_i)
 // with the online (running max / running sum) softmax over key tiles.
 //
-// Work decomposition: one workgroup = 4 waves = one 128-row query tile of one
-// (sequence, head); each wave owns 32 rows.  Key/value tiles of 64 keys are
-// staged in LDS, double buffered, prefetched through registers one tile ahead.
-// Per wave and key tile:
+// Work decomposition: one workgroup = 4 waves = one query tile of one
+// (sequence, head); each wave owns MB blocks of 32 rows.  Key/value tiles of 64
+// keys are copied global -> LDS by global_load_lds into two stage buffers (two
+// distinct LDS arrays, so reads of one never wait on the copy into the other),
+// one tile ahead of the compute.  Per wave and key tile:
 //   S^T (64 keys x 32 rows) = K Q^T      A = K rows from LDS, B = Q in registers
 //   O^T (D x 32 rows)      += V^T P^T    A = V via the transposing LDS read,
 //                                         B = P taken straight from the S^T accumulator
 // Every accumulator keeps one query row per lane (lanes l and l+32 share a row),
 // so row max / row sum need only in-lane work plus one cross-half exchange.
+// Tiles that are fully inside the mask skip all mask arithmetic.
 #include "fa_device.h"
 #include "fa_kernels.h"
 #include "fa_sched.h"
 
 namespace fa {
 
-template <typename T, int D>
+template <typename T, int D, int MB>
 struct FwdShape {
   static constexpr int EB = sizeof(T);
-  static constexpr int RB = D * EB;                 // bytes per K/V row
-  static constexpr int KP = RB + 16;                // LDS pitch of K rows
-  static constexpr int VP = RB + 64;                // LDS pitch of V rows (transposed reads)
-  static constexpr int KBYTES = kFwdBN * KP;
-  static constexpr int VBYTES = kFwdBN * VP;
-  static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int LDS = 2 * STAGE;
-  static constexpr int CPR = RB / 16;               // 16-byte chunks per row
-  static constexpr int NCH = kFwdBN * CPR / 256;    // chunks per thread per tensor
-  static constexpr int NQ = D / ElemTraits<T>::kChunk;  // Q operand registers
-  static constexpr int NDB = D / 32;                // 32-wide d blocks of O
+  static constexpr int RB = D * EB;                     // bytes per K/V row
+  static constexpr int KP = RB + 16;                    // LDS pitch of K rows (16-byte row reads)
+  static constexpr int VP = RB + (EB == 2 ? 32 : 16);   // LDS pitch of V rows (transposing reads)
+  static constexpr int BM = 128 * MB;                   // query rows per workgroup
+  static constexpr int KT = kFwdBN * KP;
+  static constexpr int VT = kFwdBN * VP;
+  static constexpr int STAGE = KT + VT;
+  static constexpr int NQ = D / ElemTraits<T>::kChunk;  // Q operand registers per row block
+  static constexpr int NDB = D / 32;                    // 32-wide d blocks of O
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void fa_fwd_kernel(FwdParams p) {
-  using S = FwdShape<T, D>;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+template <typename T, int D, int MB, bool DROP, bool ALIBI>
+__global__ __launch_bounds__(256, MB == 1 ? 2 : 1) void fa_fwd_kernel(FwdParams p) {
+  using S = FwdShape<T, D, MB>;
+  __shared__ __attribute__((aligned(16))) char st0[S::STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[S::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int hh = lane >> 5;        // which half of the wave (k-group of MFMA operands)
   const int lrow = lane & 31;
+  const int grp = lane >> 4, sl = lane & 15;
 
   const int item_idx = blockIdx.x / p.nq;
   const int hl = blockIdx.x - item_idx * p.nq;
@@ -61,231 +63,258 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(FwdParams p) {
   const int k0 = p.cu_kv[b], lkv = p.cu_kv[b + 1] - k0;
   const FaWindow win = fa_make_window(p.mode, p.pre, p.next, lq, lkv);
 
-  const int wr0 = it.tile * kFwdBM + wave * 32;   // first row of this wave (in sequence)
-  const int i = wr0 + lrow;                        // this lane's row
-  const bool row_ok = i < lq;
-  const int64_t qrow_g = (int64_t)(q0 + (row_ok ? i : 0));
+  const int wr0 = it.tile * S::BM + wave * 32 * MB;   // first row of this wave (in sequence)
 
   // ---- Q operand in registers (B of S^T = K Q^T) ----
   using QReg = typename std::conditional<sizeof(T) == 2, bf16x8, float>::type;
-  QReg qf[S::NQ];
-  {
-    const T* qp = reinterpret_cast<const T*>(p.q) + (qrow_g * p.nq + h) * D;
+  QReg qf[MB][S::NQ];
+#pragma unroll
+  for (int mb = 0; mb < MB; ++mb) {
+    const int i = wr0 + 32 * mb + lrow;
+    const bool ok = i < lq;
+    const T* qp = reinterpret_cast<const T*>(p.q) + ((int64_t)(q0 + (ok ? i : 0)) * p.nq + h) * D;
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int c = 0; c < S::NQ; ++c) {
         bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 16 * c + 8 * hh);
-        if (!row_ok) v = bf16x8{};
-        qf[c] = v;
+        qf[mb][c] = ok ? v : bf16x8{};
       }
     } else {
 #pragma unroll
-      for (int c = 0; c < S::NQ; ++c) qf[c] = row_ok ? qp[2 * c + hh] : 0.f;
+      for (int c = 0; c < S::NQ; ++c) qf[mb][c] = ok ? qp[2 * c + hh] : 0.f;
     }
   }
 
-  const float slope_l2 = p.slopes ? p.slopes[h] * kLog2e : 0.f;
+  const float slope_l2 = ALIBI ? p.slopes[h] * kLog2e : 0.f;
   const bool has_sink = p.sink != nullptr;
-  float m_run = has_sink ? p.sink[h] * kLog2e : kNegInf;
-  float l_run = (has_sink && hh == 0) ? 1.f : 0.f;   // the two half-lanes are summed at the end
-  f32x16 o[S::NDB];
+  float m_run[MB], l_run[MB];
+  f32x16 o[MB][S::NDB];
 #pragma unroll
-  for (int db = 0; db < S::NDB; ++db) o[db] = f32x16{};
+  for (int mb = 0; mb < MB; ++mb) {
+    m_run[mb] = has_sink ? p.sink[h] * kLog2e : kNegInf;
+    l_run[mb] = (has_sink && hh == 0) ? 1.f : 0.f;   // the two half-lanes are summed at the end
+#pragma unroll
+    for (int db = 0; db < S::NDB; ++db) o[mb][db] = f32x16{};
+  }
 
-  const int64_t drop_row = p.use_dropout ? p.bit_base[b] + ((int64_t)h * lq + i) * lkv : 0;
-
-  // ---- cooperative tile loads (global -> registers -> LDS) ----
   const char* kbase = reinterpret_cast<const char*>(p.k) + ((int64_t)k0 * p.nkv + g) * S::RB;
   const char* vbase = reinterpret_cast<const char*>(p.v) + ((int64_t)k0 * p.nkv + g) * S::RB;
   const int64_t kv_stride = (int64_t)p.nkv * S::RB;
-  u32x4 kreg[S::NCH], vreg[S::NCH];
+  // per-lane LDS byte offsets; every other offset below is a compile-time immediate
+  const int k_lane = lrow * S::KP + 16 * hh;                                      // K row reads
+  const int v_lane = (4 * (grp >> 1) + (sl >> 2)) * S::VP + (16 * (grp & 1) + 4 * (sl & 3)) * 2;  // V^T reads
 
-  auto load_tile = [&](int t) {
-    const int c0 = t * kFwdBN;
-#pragma unroll
-    for (int n = 0; n < S::NCH; ++n) {
-      const int ci = tid + 256 * n;
-      const int r = ci / S::CPR, cc = ci % S::CPR;
-      const bool ok = c0 + r < lkv;
-      const int64_t off = (int64_t)(ok ? c0 + r : 0) * kv_stride + cc * 16;
-      u32x4 kv = *reinterpret_cast<const u32x4*>(kbase + off);
-      u32x4 vv = *reinterpret_cast<const u32x4*>(vbase + off);
-      kreg[n] = ok ? kv : u32x4{};
-      vreg[n] = ok ? vv : u32x4{};
-    }
-  };
-  auto store_tile = [&](int stage) {
-    char* ks = smem + stage * S::STAGE;
-    char* vs = ks + S::KBYTES;
-#pragma unroll
-    for (int n = 0; n < S::NCH; ++n) {
-      const int ci = tid + 256 * n;
-      const int r = ci / S::CPR, cc = ci % S::CPR;
-      *reinterpret_cast<u32x4*>(ks + r * S::KP + cc * 16) = kreg[n];
-      *reinterpret_cast<u32x4*>(vs + r * S::VP + cc * 16) = vreg[n];
-    }
+  auto load = [&](char* st, int t) {
+    dma_rows<kFwdBN, S::RB, S::KP>(st, kbase, kv_stride, t * kFwdBN, lkv, wave, lane);
+    dma_rows<kFwdBN, S::RB, S::VP>(st + S::KT, vbase, kv_stride, t * kFwdBN, lkv, wave, lane);
   };
 
-  const int t_lo = it.lo, t_hi = it.hi;
-  if (t_lo < t_hi) {
-    load_tile(t_lo);
-    store_tile(0);
-  }
-  __syncthreads();
-
-  for (int t = t_lo; t < t_hi; ++t) {
-    const int stage = (t - t_lo) & 1;
-    const bool more = t + 1 < t_hi;
-    if (more) load_tile(t + 1);
-
+  // One key tile: everything a wave does between two barriers.
+  auto tile = [&](int t, const char* ks) {
+    const char* vs = ks + S::KT;
     const int c0 = t * kFwdBN;
-    const char* ks = smem + stage * S::STAGE;
-    const char* vs = ks + S::KBYTES;
-
-    bool wave_empty = wr0 >= lq;
-    if (!wave_empty) {
-      const int r1 = min(wr0 + 32, lq), c1 = min(c0 + kFwdBN, lkv);
-      wave_empty = fa_tile_empty(win, wr0, r1, c0, c1);
+    bool empty[MB], full[MB], any = false;
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int r0 = wr0 + 32 * mb;
+      empty[mb] = r0 >= lq || fa_tile_empty(win, r0, min(r0 + 32, lq), c0, min(c0 + kFwdBN, lkv));
+      full[mb] = fa_tile_full(win, r0, 32, c0, kFwdBN, lq, lkv);
+      any |= !empty[mb];
     }
-    if (!wave_empty) {
-      const bool full = fa_tile_full(win, wr0, 32, c0, kFwdBN, lq, lkv);
-      // ---- S^T = K Q^T for two 32-key blocks ----
-      f32x16 s[2];
+    if (!any) return;
+    // ---- S^T = K Q^T for two 32-key blocks (each K fragment feeds every row block) ----
+    f32x16 s[MB][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        f32x16 acc = f32x16{};
-        const char* krow = ks + (32 * kb + lrow) * S::KP;
-        if constexpr (sizeof(T) == 2) {
+    for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-          for (int c = 0; c < S::NQ; ++c) acc = mfma32(lds_read_b128(krow + (16 * c + 8 * hh) * 2), qf[c], acc);
-        } else {
-#pragma unroll
-          for (int c = 0; c < S::NQ; ++c)
-            acc = mfma32(*reinterpret_cast<const float*>(krow + (2 * c + hh) * 4), qf[c], acc);
-        }
-        s[kb] = acc;
-      }
-      // ---- scale, bias, mask (log2 domain) ----
-      float mt = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int j = c0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          float x = s[kb][r] * p.scale_log2;
-          if (p.slopes) x = __builtin_fmaf(slope_l2, (float)(j - i), x);
-          if (!full && !fa_allowed(win, i, j, lq, lkv)) x = kNegInf;
-          s[kb][r] = x;
-          mt = fmaxf(mt, x);
-        }
-      }
-      mt = fmaxf(mt, wave_xor32(mt));
-      const float m_new = fmaxf(m_run, mt);
-      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      m_run = m_new;
-      float lsum = 0.f;
-      uint64_t bits = ~0ull;
-      if (p.use_dropout) bits = load_mask_window(p.drop, p.drop_bytes, drop_row + c0);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = fast_exp2(s[kb][r] - m_use);
-          lsum += e;
-          const int bit = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-          s[kb][r] = ((bits >> bit) & 1ull) ? e : 0.f;
-        }
-      }
-      l_run = l_run * alpha + lsum;
-#pragma unroll
-      for (int db = 0; db < S::NDB; ++db) o[db] *= alpha;
-
-      // ---- O^T += V^T P^T ----
+      for (int mb = 0; mb < MB; ++mb) s[mb][kb] = f32x16{};
       if constexpr (sizeof(T) == 2) {
-        const int grp = lane >> 4, sl = lane & 15;
+        bf16x8 a[S::NQ];
 #pragma unroll
-        for (int c2 = 0; c2 < 4; ++c2) {
-          const int kb = c2 >> 1, sub = c2 & 1;
-          bf16x8 pb;
+        for (int c = 0; c < S::NQ; ++c) a[c] = lds_read_b128(ks + k_lane + kb * 32 * S::KP + 32 * c);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) pb[j] = to_bf16(s[kb][8 * sub + j]);
-          const int row0 = 32 * kb + 16 * sub + 4 * (grp >> 1) + (sl >> 2);
+        for (int c = 0; c < S::NQ; ++c)
 #pragma unroll
-          for (int db = 0; db < S::NDB; ++db) {
-            const int col = 32 * db + 16 * (grp & 1) + 4 * (sl & 3);
-            const bf16x8 a = lds_read_tr_x2(vs + row0 * S::VP + col * 2, vs + (row0 + 8) * S::VP + col * 2);
-            o[db] = mfma32(a, pb, o[db]);
-          }
+          for (int mb = 0; mb < MB; ++mb) s[mb][kb] = mfma32(a[c], qf[mb][c], s[mb][kb]);
+      } else {
+#pragma unroll
+        for (int c = 0; c < S::NQ; ++c) {
+          const float a = *reinterpret_cast<const float*>(ks + lrow * S::KP + kb * 32 * S::KP + (2 * c + hh) * 4);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) s[mb][kb] = mfma32(a, qf[mb][c], s[mb][kb]);
         }
+      }
+    }
+    // ---- online softmax per row block (log2 domain) ----
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int i = wr0 + 32 * mb + lrow;
+      float mt = kNegInf;
+      if (!ALIBI && full[mb]) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            s[mb][kb][r] *= p.scale_log2;
+            mt = fmaxf(mt, s[mb][kb][r]);
+          }
       } else {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            const float pb = s[kb][r];
+            const int j = c0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            float x = s[mb][kb][r] * p.scale_log2;
+            if (ALIBI) x = __builtin_fmaf(slope_l2, (float)(j - i), x);
+            if (!full[mb] && !fa_allowed(win, i, j, lq, lkv)) x = kNegInf;
+            s[mb][kb][r] = x;
+            mt = fmaxf(mt, x);
+          }
+        }
+      }
+      mt = fmaxf(mt, wave_xor32(mt));
+      const float m_new = fmaxf(m_run[mb], mt);
+      const float m_use = (m_new == kNegInf) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run[mb] - m_use);
+      m_run[mb] = m_new;
+      float lsum = 0.f;
+      if constexpr (DROP) {
+        const int64_t pos = p.bit_base[b] + ((int64_t)h * lq + i) * lkv + c0;
+        const uint64_t bits = load_mask_window(p.drop, p.drop_bytes, pos);
 #pragma unroll
-            for (int db = 0; db < S::NDB; ++db) {
-              const float a = *reinterpret_cast<const float*>(vs + key * S::VP + (32 * db + lrow) * 4);
-              o[db] = mfma32(a, pb, o[db]);
-            }
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = fast_exp2(s[mb][kb][r] - m_use);
+            lsum += e;
+            const int bit = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            s[mb][kb][r] = ((bits >> bit) & 1ull) ? e : 0.f;
+          }
+      } else {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float e = fast_exp2(s[mb][kb][r] - m_use);
+            lsum += e;
+            s[mb][kb][r] = e;
+          }
+      }
+      l_run[mb] = l_run[mb] * alpha + lsum;
+#pragma unroll
+      for (int db = 0; db < S::NDB; ++db) o[mb][db] *= alpha;
+    }
+
+    // ---- O^T += V^T P^T ----
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int c2 = 0; c2 < 4; ++c2) {
+        const int kb = c2 >> 1, sub = c2 & 1;
+        bf16x8 pb[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) pb[mb][j] = to_bf16(s[mb][kb][8 * sub + j]);
+        bf16x8 a[S::NDB];
+        const char* vrow = vs + v_lane + (16 * c2) * S::VP;
+        if constexpr (S::NDB == 4)
+          lds_read_tr_8<0, 8 * S::VP, 64, 64 + 8 * S::VP, 128, 128 + 8 * S::VP, 192, 192 + 8 * S::VP>(
+              vrow, a[0], a[1], a[2], a[3]);
+        else
+          lds_read_tr_4<0, 8 * S::VP, 64, 64 + 8 * S::VP>(vrow, a[0], a[1]);
+#pragma unroll
+        for (int db = 0; db < S::NDB; ++db)
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) o[mb][db] = mfma32(a[db], pb[mb], o[mb][db]);
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int key = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+#pragma unroll
+          for (int db = 0; db < S::NDB; ++db) {
+            const float a = *reinterpret_cast<const float*>(vs + key * S::VP + (32 * db + lrow) * 4);
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb) o[mb][db] = mfma32(a, s[mb][kb][r], o[mb][db]);
           }
         }
       }
     }
-    if (more) store_tile(stage ^ 1);
+  };
+
+  const int t_lo = it.lo, t_hi = it.hi;
+  if (t_lo < t_hi) load(st0, t_lo);
+  __syncthreads();
+  for (int t = t_lo; t < t_hi; t += 2) {
+    if (t + 1 < t_hi) load(st1, t + 1);
+    tile(t, st0);
     __syncthreads();
+    if (t + 1 < t_hi) {
+      if (t + 2 < t_hi) load(st0, t + 2);
+      tile(t + 1, st1);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue ----
-  const float l_tot = l_run + wave_xor32(l_run);
-  if (row_ok) {
-    const float inv = l_tot > 0.f ? p.inv_keep / l_tot : 0.f;
-    T* op = reinterpret_cast<T*>(p.o) + (qrow_g * p.nq + h) * D;
 #pragma unroll
-    for (int db = 0; db < S::NDB; ++db) {
+  for (int mb = 0; mb < MB; ++mb) {
+    const int i = wr0 + 32 * mb + lrow;
+    const float l_tot = l_run[mb] + wave_xor32(l_run[mb]);
+    if (i < lq) {
+      const int64_t rowg = q0 + i;
+      const float inv = l_tot > 0.f ? p.inv_keep / l_tot : 0.f;
+      T* op = reinterpret_cast<T*>(p.o) + (rowg * p.nq + h) * D;
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int d = 32 * db + 8 * a + 4 * hh;
-        if constexpr (sizeof(T) == 2) {
-          bf16x4 v;
+      for (int db = 0; db < S::NDB; ++db) {
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = to_bf16(o[db][4 * a + e] * inv);
-          *reinterpret_cast<bf16x4*>(op + d) = v;
-        } else {
-          f32x4 v;
+        for (int a = 0; a < 4; ++a) {
+          const int d = 32 * db + 8 * a + 4 * hh;
+          if constexpr (sizeof(T) == 2) {
+            bf16x4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = o[db][4 * a + e] * inv;
-          *reinterpret_cast<f32x4*>(op + d) = v;
+            for (int e = 0; e < 4; ++e) v[e] = to_bf16(o[mb][db][4 * a + e] * inv);
+            *reinterpret_cast<bf16x4*>(op + d) = v;
+          } else {
+            f32x4 v;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) v[e] = o[mb][db][4 * a + e] * inv;
+            *reinterpret_cast<f32x4*>(op + d) = v;
+          }
         }
       }
-    }
-    if (hh == 0) {
-      p.m_out[qrow_g * p.nq + h] = m_run * kLn2;
-      p.l_out[qrow_g * p.nq + h] = l_tot;
+      if (hh == 0) {
+        p.m_out[rowg * p.nq + h] = m_run[mb] * kLn2;
+        p.l_out[rowg * p.nq + h] = l_tot;
+      }
     }
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, int MB>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
-  using S = FwdShape<T, D>;
-  static_assert(S::NCH * 256 == kFwdBN * S::CPR, "tile load split");
   const int64_t blocks = (int64_t)p.n_items * p.nq;
   if (blocks == 0) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute((const void*)fa_fwd_kernel<T, D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     S::LDS);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa_fwd_kernel<T, D>), dim3((unsigned)blocks), dim3(256), S::LDS, s, p);
+  const dim3 grid((unsigned)blocks), block(256);
+  const bool drop = p.use_dropout != 0, alibi = p.slopes != nullptr;
+  if (drop && alibi)
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, MB, true, true>), grid, block, 0, s, p);
+  else if (drop)
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, MB, true, false>), grid, block, 0, s, p);
+  else if (alibi)
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, MB, false, true>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, MB, false, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(int dtype, int d, const FwdParams& p, hipStream_t s) {
-  if (dtype == 1 && d == 128) return launch_fwd_t<__bf16, 128>(p, s);
-  if (dtype == 1 && d == 64) return launch_fwd_t<__bf16, 64>(p, s);
-  if (dtype == 0 && d == 128) return launch_fwd_t<float, 128>(p, s);
-  if (dtype == 0 && d == 64) return launch_fwd_t<float, 64>(p, s);
+  if (dtype == 1 && d == 128) return launch_fwd_t<__bf16, 128, kFwdMB>(p, s);
+  if (dtype == 1 && d == 64) return launch_fwd_t<__bf16, 64, kFwdMB>(p, s);
+  if (dtype == 0 && d == 128) return launch_fwd_t<float, 128, kFwdMB>(p, s);
+  if (dtype == 0 && d == 64) return launch_fwd_t<float, 64, kFwdMB>(p, s);
   return hipErrorInvalidValue;
 }
 

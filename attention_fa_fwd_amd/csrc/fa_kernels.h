@@ -76,7 +76,11 @@ struct BwdParams {
 };
 
 // Tile shapes (rows x keys) of each pass; the host scheduler uses the same numbers.
-constexpr int kFwdBM = 128, kFwdBN = 64;
+#ifndef FA_FWD_MB
+#define FA_FWD_MB 1
+#endif
+constexpr int kFwdMB = FA_FWD_MB;   // 32-row blocks per wave in the forward
+constexpr int kFwdBM = 128 * kFwdMB, kFwdBN = 64;
 constexpr int kKvBN = 128, kKvBM = 32;
 constexpr int kDqBM = 128, kDqBN = 32;
 constexpr int kPreRowsPerBlock = 64;
