@@ -5,6 +5,7 @@ Usage: python -m attention_fa_fwd_amd.build   (or call build()).
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -35,6 +36,24 @@ def _run(cmd):
     return r.returncode, "\n".join(lines)
 
 
+def check_no_spill_with_dma(asm_path: str) -> None:
+    """Fail the build if a kernel that issues global_load_lds also spills registers
+    to scratch: in-flight LDS DMA and scratch reloads together give wrong values."""
+    text = open(asm_path).read()
+    bodies = {}
+    for m in re.finditer(r"^(_Z\w+):[^\n]*\n(.*?)^\s*s_endpgm", text, re.M | re.S):
+        bodies[m.group(1)] = "global_load_lds" in m.group(2)
+    bad = []
+    for m in re.finditer(r"\.name:\s+(_Z\w+)(.*?)\.vgpr_spill_count:\s+(\d+)", text, re.S):
+        name, spills = m.group(1), int(m.group(3))
+        sgpr = re.search(r"\.sgpr_spill_count:\s+(\d+)", m.group(2))
+        spills += int(sgpr.group(1)) if sgpr else 0
+        if spills and bodies.get(name, True):
+            bad.append(f"{name} ({spills} spills)")
+    if bad:
+        raise RuntimeError("kernels with LDS DMA must not spill: " + ", ".join(bad))
+
+
 def build(verbose: bool = False, target: str = LIB, defines=()) -> str:
     """Compile every source and link libfa.so (or `target`); returns the library path."""
     build_dir = (os.path.join(PKG, "_build") if target == LIB
@@ -46,13 +65,18 @@ def build(verbose: bool = False, target: str = LIB, defines=()) -> str:
         objs.append(obj)
         cmds.append([hipcc()] + common_flags() + [f"-D{d}" for d in defines] +
                     ["-c", os.path.join(CSRC, src), "-o", obj])
-    with ThreadPoolExecutor(max_workers=len(cmds)) as ex:
-        results = list(ex.map(_run, cmds))
+    asm_cmds = [[hipcc()] + common_flags() + [f"-D{d}" for d in defines] +
+                ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o",
+                 os.path.join(build_dir, src.replace(".hip", ".s"))] for src in SOURCES]
+    with ThreadPoolExecutor(max_workers=2 * len(cmds)) as ex:
+        results = list(ex.map(_run, cmds + asm_cmds))[:len(cmds)]
     for cmd, (rc, out) in zip(cmds, results):
         if verbose and out.strip():
             print(out)
         if rc != 0:
             raise RuntimeError(f"hipcc failed ({rc}) for {cmd[-3]}:\n{out}")
+    for src in SOURCES:
+        check_no_spill_with_dma(os.path.join(build_dir, src.replace(".hip", ".s")))
     tmp = target + ".tmp"
     rc, out = _run([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs)
     if rc != 0:

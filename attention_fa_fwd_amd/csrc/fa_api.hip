@@ -61,7 +61,10 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   pr->keep = cfg->keep_prob;
   pr->pre = cfg->pre_tokens;
   pr->next = cfg->next_tokens;
-  pr->deterministic = cfg->deterministic != 0;
+  // The fp32-atomic dQ variant is built for bf16 and for fp32 with D = 64; fp32 with
+  // D = 128 runs the deterministic passes, whose result is one of the results the
+  // non-deterministic mode allows.
+  pr->deterministic = cfg->deterministic != 0 || (cfg->dtype == FA_DTYPE_FP32 && cfg->head_dim == 128);
   const int64_t* cq = cfg->cu_seqlens_q;
   const int64_t* ck = cfg->cu_seqlens_kv;
   if (cq[0] != 0 || ck[0] != 0) return FA_ERR_PARAM_INVALID;

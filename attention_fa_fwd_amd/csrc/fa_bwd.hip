@@ -106,30 +106,28 @@ struct KvShape {
   static constexpr int EB = sizeof(T);
   static constexpr int RB = D * EB;
   static constexpr int P = RB + 16;                 // LDS pitch of Q / dY / K rows
-  static constexpr int QT = kKvBM * P;              // one 32-row tile
+  static constexpr int QT = kKvBM * P;              // one 64-row Q (or dY) tile
+  // stage layout: Q | dY | lse2[64] | D_i[64] | keep bits[64][4]
+  static constexpr int OFF_DY = QT;
+  static constexpr int OFF_LSE = 2 * QT;
+  static constexpr int OFF_DEL = OFF_LSE + 4 * kKvBM;
+  static constexpr int OFF_BITS = OFF_DEL + 4 * kKvBM;
+  static constexpr int STAGE = OFF_BITS + 16 * kKvBM;
   static constexpr int KT = kKvBN * P;              // the 128-key K tile (atomic dQ only)
   static constexpr int DSP = kKvBM * EB + 16;       // pitch of dS^T rows (one row per key)
   static constexpr int DST = kKvBN * DSP;
-  static constexpr int CPR = RB / 16;
-  static constexpr int NQC = kKvBM * CPR / 256;     // 16-byte chunks per thread for a 32-row tile
-  static constexpr int NKC = kKvBN * CPR / 256;     // ... for the 128-key tile
   static constexpr int NOP = D / ElemTraits<T>::kChunk;
   static constexpr int NDB = D / 32;
-  // LDS: Q | dY | lse[32] delta[32] | bits[32][4] | K tile | dS^T
-  static constexpr int OFF_DY = QT;
-  static constexpr int OFF_STAT = 2 * QT;
-  static constexpr int OFF_BITS = OFF_STAT + 64 * 4;
-  static constexpr int OFF_K = OFF_BITS + 32 * 4 * 4;
-  static constexpr int OFF_DS = OFF_K + KT;
-  static constexpr int LDS_BASE = OFF_K;
-  static constexpr int LDS_ATOMIC = OFF_DS + DST;
 };
 
-template <typename T, int D, bool ATOMIC>
+template <typename T, int D, bool ATOMIC, bool DROP, bool ALIBI>
 __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
   using S = KvShape<T, D>;
   using Op = typename std::conditional<sizeof(T) == 2, bf16x8, float>::type;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ __attribute__((aligned(16))) char st0[S::STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[S::STAGE];
+  __shared__ __attribute__((aligned(16))) char kt[ATOMIC ? S::KT : 16];
+  __shared__ __attribute__((aligned(16))) char dst[ATOMIC ? S::DST : 16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, lrow = lane & 31;
   const int grp = lane >> 4, sl = lane & 15;
@@ -167,16 +165,15 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
     }
   }
   const int64_t kv_stride = (int64_t)p.nkv * S::RB;
+  // fp32 stages tiles through registers (no LDS DMA in flight): its register
+  // footprint may need scratch, which must not overlap in-flight DMA
+  constexpr bool kDma = sizeof(T) == 2;
   if constexpr (ATOMIC) {
     const char* kb = reinterpret_cast<const char*>(p.k) + ((int64_t)k0 * p.nkv + g) * S::RB;
-#pragma unroll
-    for (int n = 0; n < S::NKC; ++n) {
-      const int ci = tid + 256 * n;
-      const int r = ci / S::CPR, cc = ci % S::CPR;
-      const bool ok = c0 + r < lkv;
-      u32x4 v = *reinterpret_cast<const u32x4*>(kb + (int64_t)(ok ? c0 + r : 0) * kv_stride + cc * 16);
-      *reinterpret_cast<u32x4*>(smem + S::OFF_K + r * S::P + cc * 16) = ok ? v : u32x4{};
-    }
+    if constexpr (kDma)
+      dma_rows<kKvBN, S::RB, S::P>(kt, kb, kv_stride, c0, lkv, wave, lane);
+    else
+      copy_rows<kKvBN, S::RB, S::P>(kt, kb, kv_stride, c0, lkv, tid);
   }
 
   f32x16 dk[S::NDB], dv[S::NDB];
@@ -185,176 +182,258 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
     dk[db] = f32x16{};
     dv[db] = f32x16{};
   }
-  float* lse_s = reinterpret_cast<float*>(smem + S::OFF_STAT);
-  float* del_s = lse_s + 32;
-  uint32_t* bits_s = reinterpret_cast<uint32_t*>(smem + S::OFF_BITS);
 
-  for (int hq = 0; hq < p.group; ++hq) {
-    const int h = g * p.group + hq;
-    const float slope_l2 = p.slopes ? p.slopes[h] * kLog2e : 0.f;
+  const int nqt = it.hi - it.lo;
+  const int nsteps = p.group * nqt;
+  const int64_t q_stride = (int64_t)p.nq * S::RB;
+  // per-lane LDS offsets: A-operand row reads and transposing B-operand reads
+  const int a_lane = lrow * S::P + 16 * hh;
+  const int t_lane = (4 * (grp >> 1) + (sl >> 2)) * S::P + (16 * (grp & 1) + 4 * (sl & 3)) * 2;
+
+  auto step_head = [&](int n) { return g * p.group + n / nqt; };
+  auto step_row0 = [&](int n) { return (it.lo + n % nqt) * kKvBM; };
+
+  auto load = [&](char* st, int n) {
+    const int h = step_head(n), r0 = step_row0(n);
     const char* qb = reinterpret_cast<const char*>(p.q) + ((int64_t)q0 * p.nq + h) * S::RB;
     const char* dyb = reinterpret_cast<const char*>(p.dy) + ((int64_t)q0 * p.nq + h) * S::RB;
-    const int64_t q_stride = (int64_t)p.nq * S::RB;
-    for (int qt = it.lo; qt < it.hi; ++qt) {
-      const int r0 = qt * kKvBM;
-      __syncthreads();
-      // ---- stage the Q / dY tile, row statistics and keep bits ----
-#pragma unroll
-      for (int n = 0; n < S::NQC; ++n) {
-        const int ci = tid + 256 * n;
-        const int r = ci / S::CPR, cc = ci % S::CPR;
-        const bool ok = r0 + r < lq;
-        const int64_t off = (int64_t)(ok ? r0 + r : 0) * q_stride + cc * 16;
-        u32x4 a = *reinterpret_cast<const u32x4*>(qb + off);
-        u32x4 c = *reinterpret_cast<const u32x4*>(dyb + off);
-        *reinterpret_cast<u32x4*>(smem + r * S::P + cc * 16) = ok ? a : u32x4{};
-        *reinterpret_cast<u32x4*>(smem + S::OFF_DY + r * S::P + cc * 16) = ok ? c : u32x4{};
+    if constexpr (!kDma) {
+      copy_rows<kKvBM, S::RB, S::P>(st, qb, q_stride, r0, lq, tid);
+      copy_rows<kKvBM, S::RB, S::P>(st + S::OFF_DY, dyb, q_stride, r0, lq, tid);
+      if (tid < 2 * kKvBM) {
+        const int rl = tid & (kKvBM - 1);
+        const int rr = (r0 + rl < lq) ? r0 + rl : 0;
+        const float v = (tid < kKvBM ? p.lse : p.delta)[(int64_t)(q0 + rr) * p.nq + h];
+        reinterpret_cast<float*>(st + (tid < kKvBM ? S::OFF_LSE : S::OFF_DEL))[rl] = v;
       }
-      if (tid < 32) {
-        const bool ok = r0 + tid < lq;
-        const int64_t idx = (int64_t)(q0 + (ok ? r0 + tid : 0)) * p.nq + h;
-        lse_s[tid] = ok ? p.lse[idx] : __builtin_inff();
-        del_s[tid] = ok ? p.delta[idx] : 0.f;
-      }
-      if (p.use_dropout && tid < 128) {
-        const int r = tid >> 2, w = tid & 3;
-        uint32_t word = 0;
-        if (r0 + r < lq) {
-          const int64_t pos = p.bit_base[b] + ((int64_t)h * lq + r0 + r) * lkv + c0 + 32 * w;
-          word = (uint32_t)load_mask_window(p.drop, p.drop_bytes, pos);
-        }
-        bits_s[r * 4 + w] = word;
-      }
-      __syncthreads();
+      return;
+    }
+    dma_rows<kKvBM, S::RB, S::P>(st, qb, q_stride, r0, lq, wave, lane);
+    dma_rows<kKvBM, S::RB, S::P>(st + S::OFF_DY, dyb, q_stride, r0, lq, wave, lane);
+    if (wave < 2) {
+      // lse2 (wave 0) and D_i (wave 1) of the 64 rows, one dword per lane
+      const int rr = (r0 + lane < lq) ? r0 + lane : 0;
+      const float* src = (wave == 0 ? p.lse : p.delta) + ((int64_t)(q0 + rr) * p.nq + h);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(lds_char*)(uintptr_t)(
+                                           st + (wave == 0 ? S::OFF_LSE : S::OFF_DEL)),
+                                       4, 0, 0);
+    }
+  };
+  // keep bits of the next step: 64 rows x 128 keys = 256 words, one per thread
+  auto bits_word = [&](int n) -> uint32_t {
+    const int h = step_head(n), r0 = step_row0(n);
+    const int r = tid >> 2, w = tid & 3;
+    if (r0 + r >= lq) return 0u;
+    const int64_t pos = p.bit_base[b] + ((int64_t)h * lq + r0 + r) * lkv + c0 + 32 * w;
+    return (uint32_t)load_mask_window(p.drop, p.drop_bytes, pos);
+  };
 
-      bool wave_empty = wc0 >= lkv || r0 >= lq;
-      if (!wave_empty) wave_empty = fa_tile_empty(win, r0, min(r0 + kKvBM, lq), wc0, min(wc0 + 32, lkv));
-      f32x16 ds = f32x16{};
-      if (!wave_empty) {
-        const bool full = fa_tile_full(win, r0, kKvBM, wc0, 32, lq, lkv);
-        // ---- S = Q K^T and dP~ = dY V^T (lane = key, registers = rows) ----
-        f32x16 s = f32x16{}, dp = f32x16{};
-        const char* qrow = smem + lrow * S::P;
-        const char* dyrow = smem + S::OFF_DY + lrow * S::P;
-        if constexpr (sizeof(T) == 2) {
+  auto compute = [&](const char* st, int n) {
+    const int h = step_head(n), r0 = step_row0(n);
+    const float slope_l2 = ALIBI ? p.slopes[h] * kLog2e : 0.f;
+    const float* lse_s = reinterpret_cast<const float*>(st + S::OFF_LSE);
+    const float* del_s = reinterpret_cast<const float*>(st + S::OFF_DEL);
+    const uint32_t* bits_s = reinterpret_cast<const uint32_t*>(st + S::OFF_BITS);
+    bf16x8 da_keep[2][2];   // dS of both row blocks (atomic dQ)
 #pragma unroll
-          for (int c = 0; c < S::NOP; ++c) {
-            s = mfma32(lds_read_b128(qrow + (16 * c + 8 * hh) * 2), kf[c], s);
-            dp = mfma32(lds_read_b128(dyrow + (16 * c + 8 * hh) * 2), vf[c], dp);
+    for (int rb = 0; rb < 2; ++rb) {
+      const int rb0 = r0 + 32 * rb;
+      bool empty = rb0 >= lq || wc0 >= lkv;
+      if (!empty) empty = fa_tile_empty(win, rb0, min(rb0 + 32, lq), wc0, min(wc0 + 32, lkv));
+      if constexpr (ATOMIC && sizeof(T) == 2) {
+        da_keep[rb][0] = bf16x8{};
+        da_keep[rb][1] = bf16x8{};
+      }
+      if (empty) continue;
+      const bool full = fa_tile_full(win, rb0, 32, wc0, 32, lq, lkv);
+      // ---- S = Q K^T and dP~ = dY V^T (lane = key, registers = rows) ----
+      f32x16 s = f32x16{}, dp = f32x16{};
+      if constexpr (sizeof(T) == 2) {
+        bf16x8 qa[S::NOP];
+#pragma unroll
+        for (int c = 0; c < S::NOP; ++c) qa[c] = lds_read_b128(st + a_lane + 32 * rb * S::P + 32 * c);
+#pragma unroll
+        for (int c = 0; c < S::NOP; ++c) s = mfma32(qa[c], kf[c], s);
+#pragma unroll
+        for (int c = 0; c < S::NOP; ++c) qa[c] = lds_read_b128(st + S::OFF_DY + a_lane + 32 * rb * S::P + 32 * c);
+#pragma unroll
+        for (int c = 0; c < S::NOP; ++c) dp = mfma32(qa[c], vf[c], dp);
+      } else {
+        const char* qrow = st + (32 * rb + lrow) * S::P;
+#pragma unroll
+        for (int c = 0; c < S::NOP; ++c) {
+          s = mfma32(*reinterpret_cast<const float*>(qrow + (2 * c + hh) * 4), kf[c], s);
+          dp = mfma32(*reinterpret_cast<const float*>(qrow + S::OFF_DY + (2 * c + hh) * 4), vf[c], dp);
+        }
+      }
+      // ---- P, P~, dS ----
+      f32x16 pt, ds;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rr = 32 * rb + 8 * (r >> 2) + 4 * hh + (r & 3);
+        float x = s[r] * p.scale_log2;
+        if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, (float)(j - (r0 + rr)), x);
+        if (!full && !fa_allowed(win, r0 + rr, j, lq, lkv)) x = kNegInf;
+        const float pr = fast_exp2(x - lse_s[rr]);
+        float dpv = dp[r], ptv = pr;
+        if constexpr (DROP) {
+          const bool keep = (bits_s[rr * 4 + wave] >> lrow) & 1u;
+          dpv = keep ? dpv * p.inv_keep : 0.f;
+          ptv = keep ? pr * p.inv_keep : 0.f;
+        }
+        pt[r] = ptv;
+        ds[r] = pr * (dpv - del_s[rr]);
+      }
+      // ---- dV += P~^T dY, dK += dS^T Q  (B operands through the transposing read) ----
+      if constexpr (sizeof(T) == 2) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          bf16x8 pa, da;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pa[e] = to_bf16(pt[8 * c + e]);
+            da[e] = to_bf16(ds[8 * c + e]);
           }
-        } else {
+          if constexpr (ATOMIC) da_keep[rb][c] = da;
+          const char* base = st + t_lane + (32 * rb + 16 * c) * S::P;
+          bf16x8 dyo[S::NDB], qo[S::NDB];
+          if constexpr (S::NDB == 4) {
+            lds_read_tr_8<S::OFF_DY, S::OFF_DY + 8 * S::P, S::OFF_DY + 64, S::OFF_DY + 64 + 8 * S::P,
+                          S::OFF_DY + 128, S::OFF_DY + 128 + 8 * S::P, S::OFF_DY + 192, S::OFF_DY + 192 + 8 * S::P>(
+                base, dyo[0], dyo[1], dyo[2], dyo[3]);
+            lds_read_tr_8<0, 8 * S::P, 64, 64 + 8 * S::P, 128, 128 + 8 * S::P, 192, 192 + 8 * S::P>(
+                base, qo[0], qo[1], qo[2], qo[3]);
+          } else {
+            lds_read_tr_4<S::OFF_DY, S::OFF_DY + 8 * S::P, S::OFF_DY + 64, S::OFF_DY + 64 + 8 * S::P>(base, dyo[0],
+                                                                                                      dyo[1]);
+            lds_read_tr_4<0, 8 * S::P, 64, 64 + 8 * S::P>(base, qo[0], qo[1]);
+          }
 #pragma unroll
-          for (int c = 0; c < S::NOP; ++c) {
-            s = mfma32(*reinterpret_cast<const float*>(qrow + (2 * c + hh) * 4), kf[c], s);
-            dp = mfma32(*reinterpret_cast<const float*>(dyrow + (2 * c + hh) * 4), vf[c], dp);
+          for (int db = 0; db < S::NDB; ++db) {
+            dv[db] = mfma32(pa, dyo[db], dv[db]);
+            dk[db] = mfma32(da, qo[db], dk[db]);
           }
         }
-        // ---- P, P~, dS ----
-        f32x16 pt;
+      } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int rr = 8 * (r >> 2) + 4 * hh + (r & 3);
-          const int i = r0 + rr;
-          float x = s[r] * p.scale_log2;
-          if (p.slopes) x = __builtin_fmaf(slope_l2, (float)(j - i), x);
-          if (!full && !fa_allowed(win, i, j, lq, lkv)) x = kNegInf;
-          const float pr = fast_exp2(x - lse_s[rr]);
-          float dpv = dp[r], ptv = pr;
-          if (p.use_dropout) {
-            const bool keep = (bits_s[rr * 4 + wave] >> lrow) & 1u;
-            dpv = keep ? dpv * p.inv_keep : 0.f;
-            ptv = keep ? pr * p.inv_keep : 0.f;
+          const int rr = 32 * rb + 8 * (r >> 2) + 4 * hh + (r & 3);
+#pragma unroll
+          for (int db = 0; db < S::NDB; ++db) {
+            const float dyo = *reinterpret_cast<const float*>(st + S::OFF_DY + rr * S::P + (32 * db + lrow) * 4);
+            const float qo = *reinterpret_cast<const float*>(st + rr * S::P + (32 * db + lrow) * 4);
+            dv[db] = mfma32(pt[r], dyo, dv[db]);
+            dk[db] = mfma32(ds[r], qo, dk[db]);
           }
-          pt[r] = ptv;
-          ds[r] = pr * (dpv - del_s[rr]);
+          // keep the scheduler from hoisting every LDS read of the loop (register pressure)
+          __builtin_amdgcn_sched_barrier(0);
         }
-        // ---- dV += P~^T dY, dK += dS^T Q  (B operands through the transposing read) ----
-        if constexpr (sizeof(T) == 2) {
+        if constexpr (ATOMIC) {
+          // fp32: dS^T[key][row] written directly from the accumulator layout
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            bf16x8 pa, da;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              pa[e] = to_bf16(pt[8 * c + e]);
-              da[e] = to_bf16(ds[8 * c + e]);
-            }
-            const int row0 = 16 * c + 4 * (grp >> 1) + (sl >> 2);
-#pragma unroll
-            for (int db = 0; db < S::NDB; ++db) {
-              const int col = (32 * db + 16 * (grp & 1) + 4 * (sl & 3)) * 2;
-              const bf16x8 dyo = lds_read_tr_x2(smem + S::OFF_DY + row0 * S::P + col,
-                                                smem + S::OFF_DY + (row0 + 8) * S::P + col);
-              const bf16x8 qo = lds_read_tr_x2(smem + row0 * S::P + col, smem + (row0 + 8) * S::P + col);
-              dv[db] = mfma32(pa, dyo, dv[db]);
-              dk[db] = mfma32(da, qo, dk[db]);
-            }
-          }
-        } else {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rr = 8 * (r >> 2) + 4 * hh + (r & 3);
-#pragma unroll
-            for (int db = 0; db < S::NDB; ++db) {
-              const float dyo = *reinterpret_cast<const float*>(smem + S::OFF_DY + rr * S::P + (32 * db + lrow) * 4);
-              const float qo = *reinterpret_cast<const float*>(smem + rr * S::P + (32 * db + lrow) * 4);
-              dv[db] = mfma32(pt[r], dyo, dv[db]);
-              dk[db] = mfma32(ds[r], qo, dk[db]);
-            }
-          }
-        }
-      }
-      if constexpr (ATOMIC) {
-        // ---- dQ(rows x d-block of this wave) += dS K over the 128 keys ----
-        char* dst = smem + S::OFF_DS;
-        // dS^T[key][row]: lane writes its key's rows 8a + 4hh + 0..3
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int key = 32 * wave + lrow, row = 8 * a + 4 * hh;
-          if constexpr (sizeof(T) == 2) {
-            bf16x4 v;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) v[e] = to_bf16(ds[4 * a + e]);
-            *reinterpret_cast<bf16x4*>(dst + key * S::DSP + row * 2) = v;
-          } else {
+          for (int a = 0; a < 4; ++a) {
             f32x4 v;
 #pragma unroll
             for (int e = 0; e < 4; ++e) v[e] = ds[4 * a + e];
-            *reinterpret_cast<f32x4*>(dst + key * S::DSP + row * 4) = v;
-          }
-        }
-        __syncthreads();
-        const int dcol = 32 * wave;   // this wave's 32-wide d block
-        if (r0 < lq && dcol < D) {
-          f32x16 acc = f32x16{};
-          if constexpr (sizeof(T) == 2) {
-#pragma unroll
-            for (int c = 0; c < kKvBN / 16; ++c) {
-              const int krow = 16 * c + 4 * (grp >> 1) + (sl >> 2);
-              const int coln = (16 * (grp & 1) + 4 * (sl & 3)) * 2;
-              const bf16x8 a = lds_read_tr_x2(dst + krow * S::DSP + coln, dst + (krow + 8) * S::DSP + coln);
-              const int colk = (dcol + 16 * (grp & 1) + 4 * (sl & 3)) * 2;
-              const bf16x8 bo = lds_read_tr_x2(smem + S::OFF_K + krow * S::P + colk,
-                                               smem + S::OFF_K + (krow + 8) * S::P + colk);
-              acc = mfma32(a, bo, acc);
-            }
-          } else {
-#pragma unroll 8
-            for (int c = 0; c < kKvBN / 2; ++c) {
-              const int key = 2 * c + hh;
-              const float a = *reinterpret_cast<const float*>(dst + key * S::DSP + lrow * 4);
-              const float bo = *reinterpret_cast<const float*>(smem + S::OFF_K + key * S::P + (dcol + lrow) * 4);
-              acc = mfma32(a, bo, acc);
-            }
-          }
-          // acc: lane = d (dcol + lrow), registers = rows 8(r/4) + 4hh + r%4
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rr = 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (r0 + rr < lq)
-              atomicAdd(p.dq_acc + ((int64_t)(q0 + r0 + rr) * p.nq + h) * D + dcol + lrow, acc[r]);
+            *reinterpret_cast<f32x4*>(dst + (32 * wave + lrow) * S::DSP + (32 * rb + 8 * a + 4 * hh) * 4) = v;
           }
         }
       }
+    }
+    if constexpr (ATOMIC) {
+      if constexpr (sizeof(T) == 2) {
+        // dS^T[key][row] from the kept bf16 operands: register 8c + 4t + e holds row 16c + 8t + 4hh + e
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int c = 0; c < 2; ++c)
+#pragma unroll
+            for (int t2 = 0; t2 < 2; ++t2) {
+              bf16x4 v;
+#pragma unroll
+              for (int e = 0; e < 4; ++e) v[e] = da_keep[rb][c][4 * t2 + e];
+              *reinterpret_cast<bf16x4*>(dst + (32 * wave + lrow) * S::DSP +
+                                         (32 * rb + 16 * c + 8 * t2 + 4 * hh) * 2) = v;
+            }
+      } else {
+        // rows of empty blocks were never written: clear them
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          const int rb0 = r0 + 32 * rb;
+          bool empty = rb0 >= lq || wc0 >= lkv;
+          if (!empty) empty = fa_tile_empty(win, rb0, min(rb0 + 32, lq), wc0, min(wc0 + 32, lkv));
+          if (empty)
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+              *reinterpret_cast<f32x4*>(dst + (32 * wave + lrow) * S::DSP + (32 * rb + 8 * a + 4 * hh) * 4) =
+                  f32x4{};
+        }
+      }
+      __syncthreads();
+      // ---- dQ(64 rows x this wave's 32-wide d block) += dS K over the 128 keys ----
+      const int dcol = 32 * wave;
+      if (r0 < lq && dcol < D) {
+        f32x16 acc[2] = {f32x16{}, f32x16{}};
+        if constexpr (sizeof(T) == 2) {
+#pragma unroll
+          for (int kc = 0; kc < kKvBN / 16; ++kc) {
+            const int krow = 16 * kc + 4 * (grp >> 1) + (sl >> 2);
+            const int coln = (16 * (grp & 1) + 4 * (sl & 3)) * 2;
+            const bf16x8 a0 = lds_read_tr_x2(dst + krow * S::DSP + coln, dst + (krow + 8) * S::DSP + coln);
+            const bf16x8 a1 = lds_read_tr_x2(dst + krow * S::DSP + coln + 64, dst + (krow + 8) * S::DSP + coln + 64);
+            const int colk = (dcol + 16 * (grp & 1) + 4 * (sl & 3)) * 2;
+            const bf16x8 bo = lds_read_tr_x2(kt + krow * S::P + colk, kt + (krow + 8) * S::P + colk);
+            acc[0] = mfma32(a0, bo, acc[0]);
+            acc[1] = mfma32(a1, bo, acc[1]);
+          }
+        } else {
+#pragma unroll 8
+          for (int kc = 0; kc < kKvBN / 2; ++kc) {
+            const int key = 2 * kc + hh;
+            const float bo = *reinterpret_cast<const float*>(kt + key * S::P + (dcol + lrow) * 4);
+            acc[0] = mfma32(*reinterpret_cast<const float*>(dst + key * S::DSP + lrow * 4), bo, acc[0]);
+            acc[1] = mfma32(*reinterpret_cast<const float*>(dst + key * S::DSP + (32 + lrow) * 4), bo, acc[1]);
+          }
+        }
+        // acc[rb]: lane = d (dcol + lrow), registers = rows 32rb + 8(r/4) + 4hh + r%4
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rr = 32 * rb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            if (r0 + rr < lq)
+              atomicAdd(p.dq_acc + ((int64_t)(q0 + r0 + rr) * p.nq + h) * D + dcol + lrow, acc[rb][r]);
+          }
+      }
+    }
+  };
+
+  if (nsteps > 0) load(st0, 0);
+  uint32_t word = 0;
+  if constexpr (DROP) {
+    if (nsteps > 0) word = bits_word(0);
+    reinterpret_cast<uint32_t*>(st0 + S::OFF_BITS)[tid] = word;
+  }
+  __syncthreads();
+  for (int n = 0; n < nsteps; n += 2) {
+    if (n + 1 < nsteps) {
+      load(st1, n + 1);
+      if constexpr (DROP) word = bits_word(n + 1);
+    }
+    compute(st0, n);
+    if constexpr (DROP)
+      if (n + 1 < nsteps) reinterpret_cast<uint32_t*>(st1 + S::OFF_BITS)[tid] = word;
+    __syncthreads();
+    if (n + 1 < nsteps) {
+      if (n + 2 < nsteps) {
+        load(st0, n + 2);
+        if constexpr (DROP) word = bits_word(n + 2);
+      }
+      compute(st1, n + 1);
+      if constexpr (DROP)
+        if (n + 2 < nsteps) reinterpret_cast<uint32_t*>(st0 + S::OFF_BITS)[tid] = word;
+      __syncthreads();
     }
   }
 
@@ -386,18 +465,17 @@ struct DqShape {
   static constexpr int RB = D * EB;
   static constexpr int P = RB + 16;
   static constexpr int TILE = kDqBN * P;
-  static constexpr int CPR = RB / 16;
-  static constexpr int NCH = kDqBN * CPR / 256;
+  static constexpr int STAGE = 2 * TILE;    // K | V
   static constexpr int NOP = D / ElemTraits<T>::kChunk;
   static constexpr int NDB = D / 32;
-  static constexpr int LDS = 2 * TILE;   // K | V
 };
 
-template <typename T, int D>
-__global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
+template <typename T, int D, bool DROP, bool ALIBI>
+__global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams p) {
   using S = DqShape<T, D>;
   using Op = typename std::conditional<sizeof(T) == 2, bf16x8, float>::type;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ __attribute__((aligned(16))) char st0[S::STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[S::STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hh = lane >> 5, lrow = lane & 31;
   const int grp = lane >> 4, sl = lane & 15;
@@ -435,8 +513,7 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
   }
   const float lse2 = row_ok ? p.lse[rowg * p.nq + h] : __builtin_inff();
   const float di = row_ok ? p.delta[rowg * p.nq + h] : 0.f;
-  const float slope_l2 = p.slopes ? p.slopes[h] * kLog2e : 0.f;
-  const int64_t drop_row = p.use_dropout ? p.bit_base[b] + ((int64_t)h * lq + i) * lkv : 0;
+  const float slope_l2 = ALIBI ? p.slopes[h] * kLog2e : 0.f;
   f32x16 acc[S::NDB];
 #pragma unroll
   for (int db = 0; db < S::NDB; ++db) acc[db] = f32x16{};
@@ -444,83 +521,102 @@ __global__ __launch_bounds__(256, 2) void fa_bwd_dq_kernel(BwdParams p) {
   const char* kbase = reinterpret_cast<const char*>(p.k) + ((int64_t)k0 * p.nkv + g) * S::RB;
   const char* vbase = reinterpret_cast<const char*>(p.v) + ((int64_t)k0 * p.nkv + g) * S::RB;
   const int64_t kv_stride = (int64_t)p.nkv * S::RB;
+  const int a_lane = lrow * S::P + 16 * hh;
+  const int t_lane = (4 * (grp >> 1) + (sl >> 2)) * S::P + (16 * (grp & 1) + 4 * (sl & 3)) * 2;
 
-  for (int t = it.lo; t < it.hi; ++t) {
+  auto load = [&](char* st, int t) {
+    dma_rows<kDqBN, S::RB, S::P>(st, kbase, kv_stride, t * kDqBN, lkv, wave, lane);
+    dma_rows<kDqBN, S::RB, S::P>(st + S::TILE, vbase, kv_stride, t * kDqBN, lkv, wave, lane);
+  };
+
+  auto tile = [&](int t, const char* ks) {
+    const char* vs = ks + S::TILE;
     const int c0 = t * kDqBN;
-    __syncthreads();
-#pragma unroll
-    for (int n = 0; n < S::NCH; ++n) {
-      const int ci = tid + 256 * n;
-      const int r = ci / S::CPR, cc = ci % S::CPR;
-      const bool ok = c0 + r < lkv;
-      const int64_t off = (int64_t)(ok ? c0 + r : 0) * kv_stride + cc * 16;
-      u32x4 kv = *reinterpret_cast<const u32x4*>(kbase + off);
-      u32x4 vv = *reinterpret_cast<const u32x4*>(vbase + off);
-      *reinterpret_cast<u32x4*>(smem + r * S::P + cc * 16) = ok ? kv : u32x4{};
-      *reinterpret_cast<u32x4*>(smem + S::TILE + r * S::P + cc * 16) = ok ? vv : u32x4{};
-    }
-    __syncthreads();
-    bool wave_empty = wr0 >= lq;
-    if (!wave_empty) wave_empty = fa_tile_empty(win, wr0, min(wr0 + 32, lq), c0, min(c0 + kDqBN, lkv));
-    if (wave_empty) continue;
+    if (wr0 >= lq || fa_tile_empty(win, wr0, min(wr0 + 32, lq), c0, min(c0 + kDqBN, lkv))) return;
     const bool full = fa_tile_full(win, wr0, 32, c0, kDqBN, lq, lkv);
-    // ---- S^T = K Q^T, dP~^T = V dY^T (lane = row, registers = keys) ----
-    f32x16 s = f32x16{}, dp = f32x16{};
-    const char* krow = smem + lrow * S::P;
-    const char* vrow = smem + S::TILE + lrow * S::P;
-    if constexpr (sizeof(T) == 2) {
-#pragma unroll
-      for (int c = 0; c < S::NOP; ++c) {
-        s = mfma32(lds_read_b128(krow + (16 * c + 8 * hh) * 2), qf[c], s);
-        dp = mfma32(lds_read_b128(vrow + (16 * c + 8 * hh) * 2), df[c], dp);
-      }
-    } else {
-#pragma unroll
-      for (int c = 0; c < S::NOP; ++c) {
-        s = mfma32(*reinterpret_cast<const float*>(krow + (2 * c + hh) * 4), qf[c], s);
-        dp = mfma32(*reinterpret_cast<const float*>(vrow + (2 * c + hh) * 4), df[c], dp);
-      }
-    }
     uint64_t bits = ~0ull;
-    if (p.use_dropout) bits = load_mask_window(p.drop, p.drop_bytes, drop_row + c0);
-    f32x16 ds;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kk = 8 * (r >> 2) + 4 * hh + (r & 3);
-      const int jj = c0 + kk;
-      float x = s[r] * p.scale_log2;
-      if (p.slopes) x = __builtin_fmaf(slope_l2, (float)(jj - i), x);
-      if (!full && !fa_allowed(win, i, jj, lq, lkv)) x = kNegInf;
-      const float pr = fast_exp2(x - lse2);
-      float dpv = dp[r];
-      if (p.use_dropout) dpv = ((bits >> kk) & 1ull) ? dpv * p.inv_keep : 0.f;
-      ds[r] = pr * (dpv - di);
+    if constexpr (DROP) {
+      const int64_t pos = p.bit_base[b] + ((int64_t)h * lq + i) * lkv + c0;
+      bits = load_mask_window(p.drop, p.drop_bytes, pos);
     }
-    // ---- dQ^T += K^T dS^T (A = K through the transposing read, B = dS from registers) ----
-    if constexpr (sizeof(T) == 2) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        bf16x8 bs;
+    for (int kb = 0; kb < kDqBN / 32; ++kb) {
+      // ---- S^T = K Q^T, dP~^T = V dY^T for 32 keys (lane = row, registers = keys) ----
+      f32x16 s = f32x16{}, dp = f32x16{};
+      if constexpr (sizeof(T) == 2) {
+        bf16x8 ka[S::NOP];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) bs[e] = to_bf16(ds[8 * c + e]);
-        const int row0 = 16 * c + 4 * (grp >> 1) + (sl >> 2);
+        for (int c = 0; c < S::NOP; ++c) ka[c] = lds_read_b128(ks + a_lane + 32 * kb * S::P + 32 * c);
 #pragma unroll
-        for (int db = 0; db < S::NDB; ++db) {
-          const int col = (32 * db + 16 * (grp & 1) + 4 * (sl & 3)) * 2;
-          const bf16x8 a = lds_read_tr_x2(smem + row0 * S::P + col, smem + (row0 + 8) * S::P + col);
-          acc[db] = mfma32(a, bs, acc[db]);
+        for (int c = 0; c < S::NOP; ++c) s = mfma32(ka[c], qf[c], s);
+#pragma unroll
+        for (int c = 0; c < S::NOP; ++c) ka[c] = lds_read_b128(vs + a_lane + 32 * kb * S::P + 32 * c);
+#pragma unroll
+        for (int c = 0; c < S::NOP; ++c) dp = mfma32(ka[c], df[c], dp);
+      } else {
+        const char* krow = ks + (32 * kb + lrow) * S::P;
+        const char* vrow = vs + (32 * kb + lrow) * S::P;
+#pragma unroll
+        for (int c = 0; c < S::NOP; ++c) {
+          s = mfma32(*reinterpret_cast<const float*>(krow + (2 * c + hh) * 4), qf[c], s);
+          dp = mfma32(*reinterpret_cast<const float*>(vrow + (2 * c + hh) * 4), df[c], dp);
         }
       }
-    } else {
+      f32x16 ds;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int kk = 8 * (r >> 2) + 4 * hh + (r & 3);
+        const int kk = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+        const int jj = c0 + kk;
+        float x = s[r] * p.scale_log2;
+        if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, (float)(jj - i), x);
+        if (!full && !fa_allowed(win, i, jj, lq, lkv)) x = kNegInf;
+        const float pr = fast_exp2(x - lse2);
+        float dpv = dp[r];
+        if constexpr (DROP) dpv = ((bits >> kk) & 1ull) ? dpv * p.inv_keep : 0.f;
+        ds[r] = pr * (dpv - di);
+      }
+      // ---- dQ^T += K^T dS^T (A = K through the transposing read, B = dS from registers) ----
+      if constexpr (sizeof(T) == 2) {
 #pragma unroll
-        for (int db = 0; db < S::NDB; ++db) {
-          const float a = *reinterpret_cast<const float*>(smem + kk * S::P + (32 * db + lrow) * 4);
-          acc[db] = mfma32(a, ds[r], acc[db]);
+        for (int c = 0; c < 2; ++c) {
+          bf16x8 bs;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bs[e] = to_bf16(ds[8 * c + e]);
+          const char* base = ks + t_lane + (32 * kb + 16 * c) * S::P;
+          bf16x8 a[S::NDB];
+          if constexpr (S::NDB == 4)
+            lds_read_tr_8<0, 8 * S::P, 64, 64 + 8 * S::P, 128, 128 + 8 * S::P, 192, 192 + 8 * S::P>(
+                base, a[0], a[1], a[2], a[3]);
+          else
+            lds_read_tr_4<0, 8 * S::P, 64, 64 + 8 * S::P>(base, a[0], a[1]);
+#pragma unroll
+          for (int db = 0; db < S::NDB; ++db) acc[db] = mfma32(a[db], bs, acc[db]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kk = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+#pragma unroll
+          for (int db = 0; db < S::NDB; ++db) {
+            const float a = *reinterpret_cast<const float*>(ks + kk * S::P + (32 * db + lrow) * 4);
+            acc[db] = mfma32(a, ds[r], acc[db]);
+          }
         }
       }
+    }
+  };
+
+  const int t_lo = it.lo, t_hi = it.hi;
+  if (t_lo < t_hi) load(st0, t_lo);
+  __syncthreads();
+  for (int t = t_lo; t < t_hi; t += 2) {
+    if (t + 1 < t_hi) load(st1, t + 1);
+    tile(t, st0);
+    __syncthreads();
+    if (t + 1 < t_hi) {
+      if (t + 2 < t_hi) load(st0, t + 2);
+      tile(t + 1, st1);
+      __syncthreads();
     }
   }
   if (row_ok) {
@@ -575,14 +671,18 @@ hipError_t launch_bwd_pre(int dtype, int d, const BwdParams& p, hipStream_t s) {
 
 template <typename T, int D, bool ATOMIC>
 static hipError_t launch_kv_t(const BwdParams& p, hipStream_t s) {
-  using S = KvShape<T, D>;
-  const int lds = ATOMIC ? S::LDS_ATOMIC : S::LDS_BASE;
   const int64_t blocks = (int64_t)p.n_kv_items * p.nkv;
   if (blocks == 0) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute((const void*)fa_bwd_kv_kernel<T, D, ATOMIC>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC>), dim3((unsigned)blocks), dim3(256), lds, s, p);
+  const dim3 grid((unsigned)blocks), block(256);
+  const bool drop = p.use_dropout != 0, alibi = p.slopes != nullptr;
+  if (drop && alibi)
+    hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, true, true>), grid, block, 0, s, p);
+  else if (drop)
+    hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, true, false>), grid, block, 0, s, p);
+  else if (alibi)
+    hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, false, true>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, false, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
@@ -590,7 +690,8 @@ hipError_t launch_bwd_kv(int dtype, int d, bool atomic_dq, const BwdParams& p, h
   if (atomic_dq) {
     if (dtype == 1 && d == 128) return launch_kv_t<__bf16, 128, true>(p, s);
     if (dtype == 1 && d == 64) return launch_kv_t<__bf16, 64, true>(p, s);
-    if (dtype == 0 && d == 128) return launch_kv_t<float, 128, true>(p, s);
+    // fp32 with D = 128 would need more LDS than a CU has; the host runs the
+    // deterministic passes for it instead
     if (dtype == 0 && d == 64) return launch_kv_t<float, 64, true>(p, s);
   } else {
     if (dtype == 1 && d == 128) return launch_kv_t<__bf16, 128, false>(p, s);
@@ -603,13 +704,18 @@ hipError_t launch_bwd_kv(int dtype, int d, bool atomic_dq, const BwdParams& p, h
 
 template <typename T, int D>
 static hipError_t launch_dq_t(const BwdParams& p, hipStream_t s) {
-  using S = DqShape<T, D>;
   const int64_t blocks = (int64_t)p.n_dq_items * p.nq;
   if (blocks == 0) return hipSuccess;
-  hipError_t e = hipFuncSetAttribute((const void*)fa_bwd_dq_kernel<T, D>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, S::LDS);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D>), dim3((unsigned)blocks), dim3(256), S::LDS, s, p);
+  const dim3 grid((unsigned)blocks), block(256);
+  const bool drop = p.use_dropout != 0, alibi = p.slopes != nullptr;
+  if (drop && alibi)
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, true, true>), grid, block, 0, s, p);
+  else if (drop)
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, true, false>), grid, block, 0, s, p);
+  else if (alibi)
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, false, true>), grid, block, 0, s, p);
+  else
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, false, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 

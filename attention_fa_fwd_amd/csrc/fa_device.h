@@ -175,4 +175,22 @@ __device__ __forceinline__ void dma_rows(char* lds, const char* gbase, int64_t g
   }
 }
 
+// Same tile layout as dma_rows, copied through registers (global load, then LDS
+// store) so that no copy is in flight once it returns.  Used by kernels that may
+// keep scratch spills, which must never coexist with in-flight LDS DMA.
+template <int ROWS, int RB, int P>
+__device__ __forceinline__ void copy_rows(char* lds, const char* gbase, int64_t gstride, int row0, int valid,
+                                          int tid) {
+  constexpr int CPR = RB / 16;                       // 16-byte chunks per row
+  static_assert((ROWS * CPR) % 256 == 0, "chunks split over 256 threads");
+#pragma unroll
+  for (int n = 0; n < ROWS * CPR / 256; ++n) {
+    const int ci = tid + 256 * n;
+    const int r = ci / CPR, cc = ci % CPR;
+    const int gr = (row0 + r < valid) ? row0 + r : 0;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(gbase + (int64_t)gr * gstride + 16 * cc);
+    *reinterpret_cast<u32x4*>(lds + r * P + 16 * cc) = v;
+  }
+}
+
 }  // namespace fa

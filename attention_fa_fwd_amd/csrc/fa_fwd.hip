@@ -39,8 +39,9 @@ struct FwdShape {
   static constexpr int NDB = D / 32;                    // 32-wide d blocks of O
 };
 
+// Two workgroups per CU except where the dropout path would not fit 256 registers.
 template <typename T, int D, int MB, bool DROP, bool ALIBI>
-__global__ __launch_bounds__(256, MB == 1 ? 2 : 1) void fa_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(256, (MB == 1 && !DROP) ? 2 : 1) void fa_fwd_kernel(FwdParams p) {
   using S = FwdShape<T, D, MB>;
   __shared__ __attribute__((aligned(16))) char st0[S::STAGE];
   __shared__ __attribute__((aligned(16))) char st1[S::STAGE];

@@ -81,8 +81,8 @@ struct BwdParams {
 #endif
 constexpr int kFwdMB = FA_FWD_MB;   // 32-row blocks per wave in the forward
 constexpr int kFwdBM = 128 * kFwdMB, kFwdBN = 64;
-constexpr int kKvBN = 128, kKvBM = 32;
-constexpr int kDqBM = 128, kDqBN = 32;
+constexpr int kKvBN = 128, kKvBM = 64;
+constexpr int kDqBM = 128, kDqBN = 64;
 constexpr int kPreRowsPerBlock = 64;
 
 hipError_t launch_fwd(int dtype, int d, const FwdParams& p, hipStream_t s);

@@ -86,6 +86,16 @@ def test_deterministic_is_bitwise_reproducible(workload2):
         assert np.array_equal(a[key], b[key]), key
 
 
+def test_deterministic_bitwise_with_dropout_and_alibi():
+    case = wl.make_workload(4)
+    say("workload 4 determinism")
+    x = device_inputs(case)
+    runs = [run_gpu(case, True, inputs=x) for _ in range(3)]
+    for key in ("out", "m", "l", "dq", "dk", "dv"):
+        for r in runs[1:]:
+            assert np.array_equal(runs[0][key], r[key]), key
+
+
 def test_dropout_keep_bits_bit_exact():
     # Q = 0 makes every allowed logit equal, and V = I maps key j to column j, so
     # O[i, j] = z_ij / (keep * n_i): its non-zero pattern is the keep bits.
