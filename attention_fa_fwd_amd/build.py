@@ -37,21 +37,22 @@ def _run(cmd):
 
 
 def check_no_spill_with_dma(asm_path: str) -> None:
-    """Fail the build if a kernel that issues global_load_lds also spills registers
-    to scratch: in-flight LDS DMA and scratch reloads together give wrong values."""
+    """Fail the build if a kernel that issues global_load_lds also uses scratch
+    memory (register spills): in-flight LDS DMA and scratch reloads together give
+    wrong values.  SGPR spills into VGPR lanes use no memory and are allowed."""
     text = open(asm_path).read()
     bodies = {}
     for m in re.finditer(r"^(_Z\w+):[^\n]*\n(.*?)^\s*s_endpgm", text, re.M | re.S):
         bodies[m.group(1)] = "global_load_lds" in m.group(2)
     bad = []
-    for m in re.finditer(r"\.name:\s+(_Z\w+)(.*?)\.vgpr_spill_count:\s+(\d+)", text, re.S):
-        name, spills = m.group(1), int(m.group(3))
-        sgpr = re.search(r"\.sgpr_spill_count:\s+(\d+)", m.group(2))
-        spills += int(sgpr.group(1)) if sgpr else 0
-        if spills and bodies.get(name, True):
-            bad.append(f"{name} ({spills} spills)")
+    meta = text[text.find("amdhsa.kernels:"):]
+    for entry in re.split(r"\n  - \.", meta)[1:]:
+        name = re.search(r"\.name:\s+(\S+)", entry)
+        scratch = re.search(r"\.private_segment_fixed_size:\s+(\d+)", entry)
+        if name and scratch and int(scratch.group(1)) > 0 and bodies.get(name.group(1), True):
+            bad.append(f"{name.group(1)} ({scratch.group(1)} bytes of scratch per lane)")
     if bad:
-        raise RuntimeError("kernels with LDS DMA must not spill: " + ", ".join(bad))
+        raise RuntimeError("kernels with LDS DMA must not use scratch: " + ", ".join(bad))
 
 
 def build(verbose: bool = False, target: str = LIB, defines=()) -> str:

@@ -109,7 +109,7 @@ FaWindow window_of(const Problem& pr, int64_t b) {
 std::vector<WorkItem> schedule(const Problem& pr, int pass, int* bm_out, int* bn_out) {
   std::vector<WorkItem> items;
   int bm, bn;
-  if (pass == 0) { bm = fa::kFwdBM; bn = fa::kFwdBN; }
+  if (pass == 0) { bm = fa::fwd_rows(pr.keep < 1.0); bn = fa::kFwdBN; }
   else if (pass == 1) { bm = fa::kKvBM; bn = fa::kKvBN; }
   else { bm = fa::kDqBM; bn = fa::kDqBN; }
   if (bm_out) *bm_out = bm;
@@ -192,7 +192,7 @@ Layout layout_bwd(const Problem& pr, int64_t n_kv_items, int64_t n_dq_items) {
 
 // Sizes are computed from upper bounds on the item counts so that the size
 // query does not depend on anything but the configuration.
-Layout fwd_layout_bound(const Problem& pr) { return layout_fwd(pr, upper_items(pr, fa::kFwdBM)); }
+Layout fwd_layout_bound(const Problem& pr) { return layout_fwd(pr, upper_items(pr, fa::fwd_rows(pr.keep < 1.0))); }
 Layout bwd_layout_bound(const Problem& pr) {
   return layout_bwd(pr, upper_items(pr, fa::kKvBN), upper_items(pr, fa::kDqBM));
 }

@@ -210,14 +210,12 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
     }
     dma_rows<kKvBM, S::RB, S::P>(st, qb, q_stride, r0, lq, wave, lane);
     dma_rows<kKvBM, S::RB, S::P>(st + S::OFF_DY, dyb, q_stride, r0, lq, wave, lane);
-    if (wave < 2) {
+    const int w = __builtin_amdgcn_readfirstlane(wave);
+    if (w < 2) {
       // lse2 (wave 0) and D_i (wave 1) of the 64 rows, one dword per lane
       const int rr = (r0 + lane < lq) ? r0 + lane : 0;
-      const float* src = (wave == 0 ? p.lse : p.delta) + ((int64_t)(q0 + rr) * p.nq + h);
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(lds_char*)(uintptr_t)(
-                                           st + (wave == 0 ? S::OFF_LSE : S::OFF_DEL)),
-                                       4, 0, 0);
+      dma_dword(st + (w == 0 ? S::OFF_LSE : S::OFF_DEL), w == 0 ? p.lse : p.delta,
+                (uint32_t)(((int64_t)(q0 + rr) * p.nq + h) * 4));
     }
   };
   // keep bits of the next step: 64 rows x 128 keys = 256 words, one per thread
@@ -298,22 +296,19 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
           if constexpr (ATOMIC) da_keep[rb][c] = da;
           const char* base = st + t_lane + (32 * rb + 16 * c) * S::P;
           bf16x8 dyo[S::NDB], qo[S::NDB];
-          if constexpr (S::NDB == 4) {
-            lds_read_tr_8<S::OFF_DY, S::OFF_DY + 8 * S::P, S::OFF_DY + 64, S::OFF_DY + 64 + 8 * S::P,
-                          S::OFF_DY + 128, S::OFF_DY + 128 + 8 * S::P, S::OFF_DY + 192, S::OFF_DY + 192 + 8 * S::P>(
-                base, dyo[0], dyo[1], dyo[2], dyo[3]);
-            lds_read_tr_8<0, 8 * S::P, 64, 64 + 8 * S::P, 128, 128 + 8 * S::P, 192, 192 + 8 * S::P>(
-                base, qo[0], qo[1], qo[2], qo[3]);
-          } else {
-            lds_read_tr_4<S::OFF_DY, S::OFF_DY + 8 * S::P, S::OFF_DY + 64, S::OFF_DY + 64 + 8 * S::P>(base, dyo[0],
-                                                                                                      dyo[1]);
-            lds_read_tr_4<0, 8 * S::P, 64, 64 + 8 * S::P>(base, qo[0], qo[1]);
+#pragma unroll
+          for (int db = 0; db < S::NDB; ++db) {
+            dyo[db] = lds_read_tr_x2(base + S::OFF_DY + 64 * db, base + S::OFF_DY + 8 * S::P + 64 * db);
+            qo[db] = lds_read_tr_x2(base + 64 * db, base + 8 * S::P + 64 * db);
           }
 #pragma unroll
           for (int db = 0; db < S::NDB; ++db) {
             dv[db] = mfma32(pa, dyo[db], dv[db]);
             dk[db] = mfma32(da, qo[db], dk[db]);
           }
+          // the dropout variants sit at the register limit: keep the next chunk's
+          // LDS reads from being hoisted above these MFMAs
+          if constexpr (DROP) __builtin_amdgcn_sched_barrier(0);
         }
       } else {
 #pragma unroll
@@ -415,6 +410,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
     if (nsteps > 0) word = bits_word(0);
     reinterpret_cast<uint32_t*>(st0 + S::OFF_BITS)[tid] = word;
   }
+  dma_wait();
   __syncthreads();
   for (int n = 0; n < nsteps; n += 2) {
     if (n + 1 < nsteps) {
@@ -424,6 +420,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
     compute(st0, n);
     if constexpr (DROP)
       if (n + 1 < nsteps) reinterpret_cast<uint32_t*>(st1 + S::OFF_BITS)[tid] = word;
+    dma_wait();
     __syncthreads();
     if (n + 1 < nsteps) {
       if (n + 2 < nsteps) {
@@ -433,6 +430,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
       compute(st1, n + 1);
       if constexpr (DROP)
         if (n + 2 < nsteps) reinterpret_cast<uint32_t*>(st0 + S::OFF_BITS)[tid] = word;
+      dma_wait();
       __syncthreads();
     }
   }
@@ -584,11 +582,8 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
           for (int e = 0; e < 8; ++e) bs[e] = to_bf16(ds[8 * c + e]);
           const char* base = ks + t_lane + (32 * kb + 16 * c) * S::P;
           bf16x8 a[S::NDB];
-          if constexpr (S::NDB == 4)
-            lds_read_tr_8<0, 8 * S::P, 64, 64 + 8 * S::P, 128, 128 + 8 * S::P, 192, 192 + 8 * S::P>(
-                base, a[0], a[1], a[2], a[3]);
-          else
-            lds_read_tr_4<0, 8 * S::P, 64, 64 + 8 * S::P>(base, a[0], a[1]);
+#pragma unroll
+          for (int db = 0; db < S::NDB; ++db) a[db] = lds_read_tr_x2(base + 64 * db, base + 8 * S::P + 64 * db);
 #pragma unroll
           for (int db = 0; db < S::NDB; ++db) acc[db] = mfma32(a[db], bs, acc[db]);
         }
@@ -608,14 +603,17 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
 
   const int t_lo = it.lo, t_hi = it.hi;
   if (t_lo < t_hi) load(st0, t_lo);
+  dma_wait();
   __syncthreads();
   for (int t = t_lo; t < t_hi; t += 2) {
     if (t + 1 < t_hi) load(st1, t + 1);
     tile(t, st0);
+    dma_wait();
     __syncthreads();
     if (t + 1 < t_hi) {
       if (t + 2 < t_hi) load(st0, t + 2);
       tile(t + 1, st1);
+      dma_wait();
       __syncthreads();
     }
   }

@@ -49,53 +49,6 @@ __device__ __forceinline__ bf16x8 lds_read_tr_x2(const char* p0, const char* p1)
   return r;
 }
 
-// N/2 bf16x8 operands (N transposing 8-byte reads) from one LDS base address and
-// compile-time byte offsets; operand k pairs the reads at offsets OFF[2k], OFF[2k+1].
-// The reads and their completion wait live in one asm block, so every output is
-// complete when the block ends.  Keeping these reads out of the compiler's view
-// also keeps it from waiting on global_load_lds copies into other LDS buffers.
-template <int O0, int O1, int O2, int O3>
-__device__ __forceinline__ void lds_read_tr_4(const char* base, bf16x8& a0, bf16x8& a1) {
-  u32x2 r0, r1, r2, r3;
-  const uint32_t addr = (uint32_t)(uintptr_t)(lds_char*)(uintptr_t)base;
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %4 offset:%5\n\t"
-      "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
-      "ds_read_b64_tr_b16 %2, %4 offset:%7\n\t"
-      "ds_read_b64_tr_b16 %3, %4 offset:%8\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3)
-      : "v"(addr), "i"(O0), "i"(O1), "i"(O2), "i"(O3)
-      : "memory");
-  u32x4 x0 = {r0[0], r0[1], r1[0], r1[1]};
-  u32x4 x1 = {r2[0], r2[1], r3[0], r3[1]};
-  a0 = __builtin_bit_cast(bf16x8, x0);
-  a1 = __builtin_bit_cast(bf16x8, x1);
-}
-
-template <int O0, int O1, int O2, int O3, int O4, int O5, int O6, int O7>
-__device__ __forceinline__ void lds_read_tr_8(const char* base, bf16x8& a0, bf16x8& a1, bf16x8& a2, bf16x8& a3) {
-  u32x2 r0, r1, r2, r3, r4, r5, r6, r7;
-  const uint32_t addr = (uint32_t)(uintptr_t)(lds_char*)(uintptr_t)base;
-  asm volatile(
-      "ds_read_b64_tr_b16 %0, %8 offset:%9\n\t"
-      "ds_read_b64_tr_b16 %1, %8 offset:%10\n\t"
-      "ds_read_b64_tr_b16 %2, %8 offset:%11\n\t"
-      "ds_read_b64_tr_b16 %3, %8 offset:%12\n\t"
-      "ds_read_b64_tr_b16 %4, %8 offset:%13\n\t"
-      "ds_read_b64_tr_b16 %5, %8 offset:%14\n\t"
-      "ds_read_b64_tr_b16 %6, %8 offset:%15\n\t"
-      "ds_read_b64_tr_b16 %7, %8 offset:%16\n\t"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(r0), "=&v"(r1), "=&v"(r2), "=&v"(r3), "=&v"(r4), "=&v"(r5), "=&v"(r6), "=&v"(r7)
-      : "v"(addr), "i"(O0), "i"(O1), "i"(O2), "i"(O3), "i"(O4), "i"(O5), "i"(O6), "i"(O7)
-      : "memory");
-  a0 = __builtin_bit_cast(bf16x8, (u32x4){r0[0], r0[1], r1[0], r1[1]});
-  a1 = __builtin_bit_cast(bf16x8, (u32x4){r2[0], r2[1], r3[0], r3[1]});
-  a2 = __builtin_bit_cast(bf16x8, (u32x4){r4[0], r4[1], r5[0], r5[1]});
-  a3 = __builtin_bit_cast(bf16x8, (u32x4){r6[0], r6[1], r7[0], r7[1]});
-}
-
 __device__ __forceinline__ bf16x8 lds_read_b128(const char* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
@@ -134,6 +87,15 @@ __device__ __forceinline__ uint32_t load_mask_word(const uint8_t* mask, int64_t 
   return v;
 }
 
+// 32 consecutive keep bits starting at bit `pos` (LSB = bit pos).
+__device__ __forceinline__ uint32_t load_mask_bits32(const uint8_t* mask, int64_t nbytes, int64_t pos) {
+  const int64_t w = pos >> 5;
+  const uint32_t sh = (uint32_t)(pos & 31);
+  const uint32_t lo = load_mask_word(mask, nbytes, w);
+  const uint32_t hi = sh ? load_mask_word(mask, nbytes, w + 1) : 0u;
+  return sh ? ((lo >> sh) | (hi << (32 - sh))) : lo;
+}
+
 // 64 consecutive keep bits starting at bit `pos` (LSB = bit pos).
 __device__ __forceinline__ uint64_t load_mask_window(const uint8_t* mask, int64_t nbytes, int64_t pos) {
   int64_t w = pos >> 5;
@@ -143,34 +105,43 @@ __device__ __forceinline__ uint64_t load_mask_window(const uint8_t* mask, int64_
   return sh ? ((lo >> sh) | (hi << (64 - sh))) : lo;
 }
 
-// The four waves of a 256-thread workgroup copy ROWS rows of RB bytes straight
-// from global memory into an LDS tile whose rows are P bytes apart, one row per
-// global_load_lds_dword instruction (each lane moves 4 bytes into LDS slot
-// base + 4*lane; rows of 128 bytes use the first 32 lanes, rows of 512 bytes take
-// two instructions).  Wave w copies rows [w*ROWS/4, (w+1)*ROWS/4); every address
-// is wave-uniform, so the copy costs scalar arithmetic only.  Row r is read from
-// gbase + r' * gstride with r' = row0 + r, or r' = 0 when row0 + r is not below
-// `valid` (finite data that the caller masks); valid must be >= 1.
-template <int ROWS, int RB, int P>
+// One global_load_lds_dword issued from asm: 64 lanes copy 4 bytes each from
+// gbase + voff (gbase wave-uniform, voff per lane) into LDS at lds + 4*lane.
+// The compiler does not see these copies, so it never makes LDS reads wait for
+// them; the kernel drains them itself with dma_wait() before the barrier that
+// publishes the tile.
+__device__ __forceinline__ void dma_dword(const char* lds, const void* gbase, uint32_t voff) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_char*)(uintptr_t)lds;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dword %1, %2" ::"{m0}"(m0), "v"(voff), "s"(gbase) : "memory");
+}
+
+// Wait until every LDS copy this wave issued has landed.
+__device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// The NW waves of a workgroup copy ROWS rows of RB bytes straight from global
+// memory into an LDS tile whose rows are P bytes apart, one dword-per-lane copy
+// per row (rows of 128 bytes use the first 32 lanes, rows of 512 bytes take two
+// copies).  Wave w copies rows [w*ROWS/NW, (w+1)*ROWS/NW); every address is
+// wave-uniform apart from the lane offset.  Row r is read from gbase + r' * gstride
+// with r' = row0 + r, or r' = 0 when row0 + r is not below `valid` (finite data
+// that the caller masks); valid must be >= 1.
+template <int ROWS, int RB, int P, int NW = 4>
 __device__ __forceinline__ void dma_rows(char* lds, const char* gbase, int64_t gstride, int row0, int valid,
                                          int wave, int lane) {
-  static_assert(ROWS % 4 == 0, "rows split over four waves");
+  static_assert(ROWS % NW == 0, "rows split over the waves");
   static_assert(RB == 128 || RB % 256 == 0, "row size");
-  constexpr int RPW = ROWS / 4;
-  constexpr int LANES = RB >= 256 ? 64 : RB / 4;  // active lanes per instruction
-  constexpr int IPR = RB >= 256 ? RB / 256 : 1;   // instructions per row
+  constexpr int RPW = ROWS / NW;
+  constexpr int LANES = RB >= 256 ? 64 : RB / 4;  // active lanes per copy
+  constexpr int IPR = RB >= 256 ? RB / 256 : 1;   // copies per row
   const int w = __builtin_amdgcn_readfirstlane(wave);
   if (lane < LANES) {
 #pragma unroll
     for (int k = 0; k < RPW; ++k) {
       const int r = w * RPW + k;
       const int gr = (row0 + r < valid) ? row0 + r : 0;
-      const char* src = gbase + (int64_t)gr * gstride + 4 * lane;
+      const char* src = gbase + (int64_t)gr * gstride;
 #pragma unroll
-      for (int u = 0; u < IPR; ++u)
-        __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(src + 256 * u),
-                                         (__attribute__((address_space(3))) void*)(lds_char*)(uintptr_t)(lds + r * P + 256 * u),
-                                         4, 0, 0);
+      for (int u = 0; u < IPR; ++u) dma_dword(lds + r * P + 256 * u, src + 256 * u, 4 * lane);
     }
   }
 }

@@ -76,11 +76,10 @@ struct BwdParams {
 };
 
 // Tile shapes (rows x keys) of each pass; the host scheduler uses the same numbers.
-#ifndef FA_FWD_MB
-#define FA_FWD_MB 1
-#endif
-constexpr int kFwdMB = FA_FWD_MB;   // 32-row blocks per wave in the forward
-constexpr int kFwdBM = 128 * kFwdMB, kFwdBN = 64;
+// waves per forward workgroup (32 query rows each): 8, or 4 with dropout
+constexpr int fwd_waves(bool dropout) { return dropout ? 4 : 8; }
+constexpr int fwd_rows(bool dropout) { return 32 * fwd_waves(dropout); }
+constexpr int kFwdBN = 64;
 constexpr int kKvBN = 128, kKvBM = 64;
 constexpr int kDqBM = 128, kDqBN = 64;
 constexpr int kPreRowsPerBlock = 64;

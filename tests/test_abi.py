@@ -202,8 +202,8 @@ def test_schedule_of_workload5_skips_upper_triangle():
 def test_build_rejects_spilling_kernels_with_lds_dma(tmp_path):
     from attention_fa_fwd_amd.build import check_no_spill_with_dma
     body = "_Zk1: ; @_Zk1\n  global_load_lds_dword v[0:1], off\n  s_endpgm\n_Zk2: ; @_Zk2\n  v_mov_b32 v0, 0\n  s_endpgm\n"
-    meta = ("  - .name: _Zk1\n    .sgpr_spill_count: 0\n    .vgpr_spill_count: {a}\n"
-            "  - .name: _Zk2\n    .sgpr_spill_count: 0\n    .vgpr_spill_count: {b}\n")
+    meta = ("amdhsa.kernels:\n  - .agpr_count: 0\n    .name: _Zk1\n    .private_segment_fixed_size: {a}\n"
+            "  - .agpr_count: 0\n    .name: _Zk2\n    .private_segment_fixed_size: {b}\n")
     ok = tmp_path / "ok.s"
     ok.write_text(body + meta.format(a=0, b=7))       # spills only where no DMA is issued
     check_no_spill_with_dma(str(ok))
