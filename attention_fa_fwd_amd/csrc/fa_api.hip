@@ -109,7 +109,7 @@ FaWindow window_of(const Problem& pr, int64_t b) {
 std::vector<WorkItem> schedule(const Problem& pr, int pass, int* bm_out, int* bn_out) {
   std::vector<WorkItem> items;
   int bm, bn;
-  if (pass == 0) { bm = fa::fwd_rows(pr.keep < 1.0); bn = fa::kFwdBN; }
+  if (pass == 0) { bm = fa::fwd_rows(pr.keep < 1.0, pr.dtype == FA_DTYPE_FP32); bn = fa::kFwdBN; }
   else if (pass == 1) { bm = fa::kKvBM; bn = fa::kKvBN; }
   else { bm = fa::kDqBM; bn = fa::kDqBN; }
   if (bm_out) *bm_out = bm;
@@ -192,7 +192,7 @@ Layout layout_bwd(const Problem& pr, int64_t n_kv_items, int64_t n_dq_items) {
 
 // Sizes are computed from upper bounds on the item counts so that the size
 // query does not depend on anything but the configuration.
-Layout fwd_layout_bound(const Problem& pr) { return layout_fwd(pr, upper_items(pr, fa::fwd_rows(pr.keep < 1.0))); }
+Layout fwd_layout_bound(const Problem& pr) { return layout_fwd(pr, upper_items(pr, fa::fwd_rows(pr.keep < 1.0, pr.dtype == FA_DTYPE_FP32))); }
 Layout bwd_layout_bound(const Problem& pr) {
   return layout_bwd(pr, upper_items(pr, fa::kKvBN), upper_items(pr, fa::kDqBM));
 }
@@ -353,6 +353,9 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
   if (!workspace) return FA_ERR_PARAM_NULLPTR;
   if (workspace_bytes < bound.total) return FA_ERR_WORKSPACE;
 
+  // the atomic dK/dV kernel for bf16 D = 128 has no alibi variant (its registers
+  // do not fit one): run the deterministic passes, which need less workspace
+  if (alibi_slopes && pr.dtype == FA_DTYPE_BF16 && pr.d == 128) pr.deterministic = true;
   std::vector<WorkItem> kv_items = schedule(pr, 1, nullptr, nullptr);
   std::vector<WorkItem> dq_items = schedule(pr, 2, nullptr, nullptr);
   const Layout L = layout_bwd(pr, (int64_t)kv_items.size(), (int64_t)dq_items.size());

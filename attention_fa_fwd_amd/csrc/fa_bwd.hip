@@ -24,6 +24,10 @@
 
 namespace fa {
 
+#ifndef FA_KV_OVERLAP
+#define FA_KV_OVERLAP 0
+#endif
+
 // ------------------------------------------------------------------ preprocess
 template <typename T, int D>
 __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(BwdParams p) {
@@ -128,7 +132,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) char st1[S::STAGE];
   __shared__ __attribute__((aligned(16))) char kt[ATOMIC ? S::KT : 16];
   __shared__ __attribute__((aligned(16))) char dst[ATOMIC ? S::DST : 16];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, lrow = lane & 31;
   const int grp = lane >> 4, sl = lane & 15;
 
@@ -218,13 +222,196 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
                 (uint32_t)(((int64_t)(q0 + rr) * p.nq + h) * 4));
     }
   };
-  // keep bits of the next step: 64 rows x 128 keys = 256 words, one per thread
+  // keep bits of the next step: 64 rows x 128 keys = 256 words, one per thread;
+  // stored per wave (32 keys) and row, so a lane reads 4 consecutive rows at once
+  const int bits_slot = (tid & 3) * kKvBM + (tid >> 2);
   auto bits_word = [&](int n) -> uint32_t {
     const int h = step_head(n), r0 = step_row0(n);
     const int r = tid >> 2, w = tid & 3;
     if (r0 + r >= lq) return 0u;
     const int64_t pos = p.bit_base[b] + ((int64_t)h * lq + r0 + r) * lkv + c0 + 32 * w;
     return (uint32_t)load_mask_window(p.drop, p.drop_bytes, pos);
+  };
+
+  // atomic dQ of one bf16 step: store_ds() puts each block's dS^T into LDS right
+  // after it is formed; atomic_dq() then adds dQ(64 rows x 32-wide d block of this
+  // wave) += dS K over the 128 keys to the fp32 accumulator
+  auto store_ds = [&](int rb, const auto& d) {
+    // register 8c + 4t + e holds row 32rb + 16c + 8t + 4hh + e
+#pragma unroll
+    for (int c = 0; c < 2; ++c)
+#pragma unroll
+      for (int t2 = 0; t2 < 2; ++t2) {
+        bf16x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = d[c][4 * t2 + e];
+        *reinterpret_cast<bf16x4*>(dst + (32 * wave + lrow) * S::DSP + (32 * rb + 16 * c + 8 * t2 + 4 * hh) * 2) = v;
+      }
+  };
+  auto atomic_dq = [&](auto n) {
+    const int h = step_head(n), r0 = step_row0(n);
+    __syncthreads();
+    const int dcol = 32 * wave;
+    if (r0 < lq && dcol < D) {
+      f32x16 acc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+      for (int kc = 0; kc < kKvBN / 16; ++kc) {
+        const int krow = 16 * kc + 4 * (grp >> 1) + (sl >> 2);
+        const int coln = (16 * (grp & 1) + 4 * (sl & 3)) * 2;
+        const bf16x8 a0 = lds_read_tr_x2(dst + krow * S::DSP + coln, dst + (krow + 8) * S::DSP + coln);
+        const bf16x8 a1 = lds_read_tr_x2(dst + krow * S::DSP + coln + 64, dst + (krow + 8) * S::DSP + coln + 64);
+        const int colk = (dcol + 16 * (grp & 1) + 4 * (sl & 3)) * 2;
+        const bf16x8 bo = lds_read_tr_x2(kt + krow * S::P + colk, kt + (krow + 8) * S::P + colk);
+        acc[0] = mfma32(a0, bo, acc[0]);
+        acc[1] = mfma32(a1, bo, acc[1]);
+      }
+      // acc[rb]: lane = d (dcol + lrow), registers = rows 32rb + 8(r/4) + 4hh + r%4
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rr = 32 * rb + 8 * (r >> 2) + 4 * hh + (r & 3);
+          if (r0 + rr < lq)
+            atomicAdd(p.dq_acc + ((int64_t)(q0 + r0 + rr) * p.nq + h) * D + dcol + lrow, acc[rb][r]);
+        }
+    }
+  };
+  // ---- bf16 steps: software pipeline over the step's two 32-row blocks ----
+  //   [S, dP of block 0]  [S, dP of block 1 | P, dS of block 0]
+  //   [dV, dK of block 0 | P, dS of block 1]  [dV, dK of block 1]
+  // Scheduling-group barriers interleave each region's matrix work with the
+  // VALU work beside it and keep the LDS reads a few MFMAs ahead of their use.
+  // Blocks outside the mask are computed like masked ones (every probability
+  // is zero): the waves of a workgroup wait for each other at every step anyway.
+  auto sdp = [&](const char* st, int rb, auto& s, auto& dp) {
+    s = f32x16{};
+    dp = f32x16{};
+#pragma unroll
+    for (int c = 0; c < S::NOP; ++c) {
+      const bf16x8 qa = lds_read_b128(st + a_lane + 32 * rb * S::P + 32 * c);
+      const bf16x8 ya = lds_read_b128(st + S::OFF_DY + a_lane + 32 * rb * S::P + 32 * c);
+      s = mfma32(qa, kf[c], s);
+      dp = mfma32(ya, vf[c], dp);
+    }
+  };
+  // P~ and dS of one block as bf16 A operands (lane = key, registers = rows)
+  auto elem = [&](auto full_c, const char* st, int r0, int rb, const f32x16& s, const f32x16& dp, float slope_l2,
+                  bf16x8 (&pa)[2], bf16x8 (&da)[2]) {
+    constexpr bool plain = !ALIBI && decltype(full_c)::value;
+    const float* lse_s = reinterpret_cast<const float*>(st + S::OFF_LSE);
+    const float* del_s = reinterpret_cast<const float*>(st + S::OFF_DEL);
+    const uint32_t* bits_s = reinterpret_cast<const uint32_t*>(st + S::OFF_BITS);
+    const float sc = p.scale_log2;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int rq = 32 * rb + 8 * a + 4 * hh;   // rows rq .. rq+3 sit in registers 4a .. 4a+3
+      const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lse_s + rq);
+      const f32x4 del4 = *reinterpret_cast<const f32x4*>(del_s + rq);
+      u32x4 bits4;
+      if constexpr (DROP) bits4 = *reinterpret_cast<const u32x4*>(bits_s + wave * kKvBM + rq);
+      const float jmi = (float)(j - r0 - rq);   // j - i of register 4a; minus e for register 4a + e
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 4 * a + e, rr = rq + e, i = r0 + rr;
+        float pr;
+        if constexpr (plain) {
+          pr = fast_exp2(__builtin_fmaf(s[r], sc, -lse4[e]));
+        } else {
+          float x = s[r] * sc;
+          if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, jmi - (float)e, x);
+          if constexpr (!decltype(full_c)::value) {
+            const bool ok = (i < lq) & key_ok & (j >= fa_row_lo(win, i)) & (j <= fa_row_hi(win, i));
+            x = ok ? x : kNegInf;
+          }
+          pr = fast_exp2(x - lse4[e]);
+        }
+        float dpv = dp[r], ptv = pr;
+        if constexpr (DROP) {
+          const bool keep = (bits4[e] >> lrow) & 1u;
+          dpv = keep ? dpv * p.inv_keep : 0.f;
+          ptv = keep ? pr * p.inv_keep : 0.f;
+        }
+        const float dsv = pr * (dpv - del4[e]);
+        pa[r >> 3][r & 7] = to_bf16(ptv);
+        da[r >> 3][r & 7] = to_bf16(dsv);
+      }
+    }
+  };
+  // dV += P~^T dY, dK += dS^T Q  (B operands through the transposing read)
+  auto grads = [&](const char* st, int rb, const auto& pa, const auto& da) {
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      const char* base = st + t_lane + (32 * rb + 16 * c) * S::P;
+#pragma unroll
+      for (int db = 0; db < S::NDB; ++db) {
+        const bf16x8 yo = lds_read_tr_x2(base + S::OFF_DY + 64 * db, base + S::OFF_DY + 8 * S::P + 64 * db);
+        const bf16x8 qo = lds_read_tr_x2(base + 64 * db, base + 8 * S::P + 64 * db);
+        dv[db] = mfma32(pa[c], yo, dv[db]);
+        dk[db] = mfma32(da[c], qo, dk[db]);
+      }
+    }
+  };
+  constexpr int kSdpMfma = 2 * S::NOP, kSdpReads = 2 * S::NOP;
+  constexpr int kGradMfma = 4 * S::NDB, kGradReads = 8 * S::NDB;
+  constexpr int kElemValu = DROP ? 160 : (ALIBI ? 120 : 90);
+
+  auto compute_bf16 = [&](const char* st, auto n) {
+    const int h = step_head(n), r0 = step_row0(n);
+    const float slope_l2 = ALIBI ? p.slopes[h] * kLog2e : 0.f;
+    const bool full0 = fa_tile_full(win, r0, 32, wc0, 32, lq, lkv);
+    const bool full1 = fa_tile_full(win, r0 + 32, 32, wc0, 32, lq, lkv);
+    f32x16 s0, dp0, s1, dp1;
+    bf16x8 pa0[2], da0[2], pa1[2], da1[2];
+#if FA_KV_OVERLAP
+    __builtin_amdgcn_sched_barrier(0);
+    sdp(st, 0, s0, dp0);
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    sched_alternate<kSdpMfma, 0x008, 0x100>();
+    __builtin_amdgcn_sched_barrier(0);
+    auto region2 = [&](auto full_c) {
+      elem(full_c, st, r0, 0, s0, dp0, slope_l2, pa0, da0);
+      if constexpr (ATOMIC) store_ds(0, da0);
+      sdp(st, 1, s1, dp1);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      sched_alternate3<kSdpMfma, 0x008, 1, 0x002, kElemValu / kSdpMfma, 0x100, 1>();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (full0) region2(std::true_type{});
+    else region2(std::false_type{});
+    auto region3 = [&](auto full_c) {
+      elem(full_c, st, r0, 1, s1, dp1, slope_l2, pa1, da1);
+      if constexpr (ATOMIC) store_ds(1, da1);
+      grads(st, 0, pa0, da0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      sched_alternate3<kGradMfma, 0x008, 1, 0x002, kElemValu / kGradMfma, 0x100, 2>();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    if (full1) region3(std::true_type{});
+    else region3(std::false_type{});
+    grads(st, 1, pa1, da1);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    sched_alternate<kGradMfma, 0x008, 0x100, 2>();
+    __builtin_amdgcn_sched_barrier(0);
+#else
+    auto block = [&](int rb, bool full, auto& sx, auto& dpx, auto& pax, auto& dax) {
+      __builtin_amdgcn_sched_barrier(0);
+      sdp(st, rb, sx, dpx);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      sched_alternate<kSdpMfma, 0x008, 0x100>();
+      __builtin_amdgcn_sched_barrier(0);
+      if (full) elem(std::true_type{}, st, r0, rb, sx, dpx, slope_l2, pax, dax);
+      else elem(std::false_type{}, st, r0, rb, sx, dpx, slope_l2, pax, dax);
+      if constexpr (ATOMIC) store_ds(rb, dax);
+      __builtin_amdgcn_sched_barrier(0);
+      grads(st, rb, pax, dax);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      sched_alternate<kGradMfma, 0x008, 0x100, 2>();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    block(0, full0, s0, dp0, pa0, da0);
+    block(1, full1, s1, dp1, pa1, da1);
+#endif
+    if constexpr (ATOMIC) atomic_dq(n);
   };
 
   auto compute = [&](const char* st, int n) {
@@ -276,7 +463,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
         const float pr = fast_exp2(x - lse_s[rr]);
         float dpv = dp[r], ptv = pr;
         if constexpr (DROP) {
-          const bool keep = (bits_s[rr * 4 + wave] >> lrow) & 1u;
+          const bool keep = (bits_s[wave * kKvBM + rr] >> lrow) & 1u;
           dpv = keep ? dpv * p.inv_keep : 0.f;
           ptv = keep ? pr * p.inv_keep : 0.f;
         }
@@ -408,7 +595,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
   uint32_t word = 0;
   if constexpr (DROP) {
     if (nsteps > 0) word = bits_word(0);
-    reinterpret_cast<uint32_t*>(st0 + S::OFF_BITS)[tid] = word;
+    reinterpret_cast<uint32_t*>(st0 + S::OFF_BITS)[bits_slot] = word;
   }
   dma_wait();
   __syncthreads();
@@ -417,9 +604,10 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
       load(st1, n + 1);
       if constexpr (DROP) word = bits_word(n + 1);
     }
-    compute(st0, n);
+    if constexpr (sizeof(T) == 2) compute_bf16(st0, n);
+    else compute(st0, n);
     if constexpr (DROP)
-      if (n + 1 < nsteps) reinterpret_cast<uint32_t*>(st1 + S::OFF_BITS)[tid] = word;
+      if (n + 1 < nsteps) reinterpret_cast<uint32_t*>(st1 + S::OFF_BITS)[bits_slot] = word;
     dma_wait();
     __syncthreads();
     if (n + 1 < nsteps) {
@@ -427,9 +615,10 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
         load(st0, n + 2);
         if constexpr (DROP) word = bits_word(n + 2);
       }
-      compute(st1, n + 1);
+      if constexpr (sizeof(T) == 2) compute_bf16(st1, n + 1);
+      else compute(st1, n + 1);
       if constexpr (DROP)
-        if (n + 2 < nsteps) reinterpret_cast<uint32_t*>(st0 + S::OFF_BITS)[tid] = word;
+        if (n + 2 < nsteps) reinterpret_cast<uint32_t*>(st0 + S::OFF_BITS)[bits_slot] = word;
       dma_wait();
       __syncthreads();
     }
@@ -673,12 +862,15 @@ static hipError_t launch_kv_t(const BwdParams& p, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(256);
   const bool drop = p.use_dropout != 0, alibi = p.slopes != nullptr;
+  // no alibi instance of the atomic bf16 D = 128 kernel (see launch_bwd_kv)
+  constexpr bool kAlibi = !(ATOMIC && sizeof(T) == 2 && D == 128);
+  if (alibi && !kAlibi) return hipErrorInvalidValue;
   if (drop && alibi)
-    hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, true, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, true, kAlibi>), grid, block, 0, s, p);
   else if (drop)
     hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, true, false>), grid, block, 0, s, p);
   else if (alibi)
-    hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, false, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, false, kAlibi>), grid, block, 0, s, p);
   else
     hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, false, false>), grid, block, 0, s, p);
   return hipGetLastError();
@@ -686,7 +878,8 @@ static hipError_t launch_kv_t(const BwdParams& p, hipStream_t s) {
 
 hipError_t launch_bwd_kv(int dtype, int d, bool atomic_dq, const BwdParams& p, hipStream_t s) {
   if (atomic_dq) {
-    if (dtype == 1 && d == 128) return launch_kv_t<__bf16, 128, true>(p, s);
+    // bf16 D = 128 with alibi runs the deterministic passes (the host routes it)
+    if (dtype == 1 && d == 128 && p.slopes == nullptr) return launch_kv_t<__bf16, 128, true>(p, s);
     if (dtype == 1 && d == 64) return launch_kv_t<__bf16, 64, true>(p, s);
     // fp32 with D = 128 would need more LDS than a CU has; the host runs the
     // deterministic passes for it instead

@@ -55,7 +55,17 @@ __device__ __forceinline__ bf16x8 lds_read_b128(const char* p) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float wave_xor32(float v) { return __shfl_xor(v, 32, 64); }
+// Combine lane l with lane l^32 (the two halves of a wave hold the two k-groups
+// of one MFMA row): one v_permlane32_swap, no LDS round trip.  Both lanes of a
+// pair get the same bits (the sum is formed in the same order on both).
+__device__ __forceinline__ float half_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // bf16 <-> f32 (round to nearest even)
 __device__ __forceinline__ __bf16 to_bf16(float f) { return (__bf16)f; }
@@ -75,6 +85,28 @@ struct ElemTraits<float> {
   static constexpr int kBytes = 4;
   static constexpr int kChunk = 2;
 };
+
+// Scheduling-group patterns for __builtin_amdgcn_sched_group_barrier (instruction
+// classes: 0x002 VALU, 0x008 MFMA, 0x100 LDS read).
+//   sched_alternate<N, A, B, NB>:            N times { 1 of A, NB of B }
+//   sched_alternate3<N, A, NA, B, NB, C, NC>: N times { NA of A, NB of B, NC of C }
+template <int N, int A, int B, int NB = 1>
+__device__ __forceinline__ void sched_alternate() {
+  if constexpr (N > 0) {
+    __builtin_amdgcn_sched_group_barrier(A, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(B, NB, 0);
+    sched_alternate<N - 1, A, B, NB>();
+  }
+}
+template <int N, int A, int NA, int B, int NB, int C, int NC>
+__device__ __forceinline__ void sched_alternate3() {
+  if constexpr (N > 0) {
+    __builtin_amdgcn_sched_group_barrier(A, NA, 0);
+    if constexpr (NB > 0) __builtin_amdgcn_sched_group_barrier(B, NB, 0);
+    if constexpr (NC > 0) __builtin_amdgcn_sched_group_barrier(C, NC, 0);
+    sched_alternate3<N - 1, A, NA, B, NB, C, NC>();
+  }
+}
 
 // Load one 32-bit word of the packed keep mask; words that reach past the end
 // of the buffer are assembled from the bytes that exist.
@@ -124,7 +156,8 @@ __device__ __forceinline__ void dma_wait() { asm volatile("s_waitcnt vmcnt(0)" :
 // copies).  Wave w copies rows [w*ROWS/NW, (w+1)*ROWS/NW); every address is
 // wave-uniform apart from the lane offset.  Row r is read from gbase + r' * gstride
 // with r' = row0 + r, or r' = 0 when row0 + r is not below `valid` (finite data
-// that the caller masks); valid must be >= 1.
+// that the caller masks); valid must be >= 1.  When all of a wave's rows are
+// valid the source address of full-wave rows just steps by gstride.
 template <int ROWS, int RB, int P, int NW = 4>
 __device__ __forceinline__ void dma_rows(char* lds, const char* gbase, int64_t gstride, int row0, int valid,
                                          int wave, int lane) {
@@ -133,15 +166,33 @@ __device__ __forceinline__ void dma_rows(char* lds, const char* gbase, int64_t g
   constexpr int RPW = ROWS / NW;
   constexpr int LANES = RB >= 256 ? 64 : RB / 4;  // active lanes per copy
   constexpr int IPR = RB >= 256 ? RB / 256 : 1;   // copies per row
+  // the row numbers are wave-uniform; say so, so the copy addresses stay scalar
   const int w = __builtin_amdgcn_readfirstlane(wave);
-  if (lane < LANES) {
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  valid = __builtin_amdgcn_readfirstlane(valid);
+  const int r0 = w * RPW;
+  char* dst = lds + r0 * P;
+  if constexpr (LANES == 64) {
+    if (row0 + r0 + RPW <= valid) {
+      const char* src = gbase + (int64_t)(row0 + r0) * gstride;
+#pragma unroll
+      for (int k = 0; k < RPW; ++k) {
+#pragma unroll
+        for (int u = 0; u < IPR; ++u) dma_dword(dst + k * P + 256 * u, src + 256 * u, 4 * lane);
+        src += gstride;
+      }
+      return;
+    }
+  }
+  // short rows (a partial wave copies each row: the address must stay scalar
+  // inside the lane-masked region) and the sequence tail
+  if (LANES == 64 || lane < LANES) {
 #pragma unroll
     for (int k = 0; k < RPW; ++k) {
-      const int r = w * RPW + k;
-      const int gr = (row0 + r < valid) ? row0 + r : 0;
+      const int gr = (row0 + r0 + k < valid) ? row0 + r0 + k : 0;
       const char* src = gbase + (int64_t)gr * gstride;
 #pragma unroll
-      for (int u = 0; u < IPR; ++u) dma_dword(lds + r * P + 256 * u, src + 256 * u, 4 * lane);
+      for (int u = 0; u < IPR; ++u) dma_dword(dst + k * P + 256 * u, src + 256 * u, 4 * lane);
     }
   }
 }

@@ -8,22 +8,35 @@
 //   O_i  = sum_j e^(s_ij - m_i) z_ij v_j / (keep * l_i)
 // with an online softmax over key tiles.
 //
-// Work decomposition: one workgroup = NW waves = one query tile of 32*NW rows of
-// one (sequence, head); each wave owns 32 rows, and all waves share each K/V
-// tile.  Key/value tiles of 64 keys are copied global -> LDS by global_load_lds
-// into two stage buffers, one tile ahead of the compute; each wave drains its own
-// copies just before the barrier that publishes a tile.  Per wave and tile:
+// Work decomposition: one workgroup = NW waves = one query tile of 32*NW rows
+// of one (sequence, head); each wave owns 32 rows, and all waves share each K/V
+// tile of 64 keys.  Per wave and tile:
 //   S^T (64 keys x 32 rows) = K Q^T      A = K rows from LDS, B = Q in registers
 //   O^T (D x 32 rows)      += V^T P^T    A = V via the transposing LDS read,
 //                                         B = P taken straight from the S^T accumulator
 // Every accumulator keeps one query row per lane (lanes l and l+32 share a row),
 // so row max / row sum need only in-lane work plus one cross-half exchange.
 //
+// Two phase-shifted wave groups (8 waves: two per SIMD).  Both groups see the
+// same K/V tiles between the same barriers, but the second group runs one step
+// behind: during key tile t the first group computes S(t), its softmax and
+// P V(t), while the second group finishes the softmax and P V of tile t-1 and
+// then computes S(t).  So on every SIMD one wave is mostly on the matrix cores
+// while the other is mostly on the VALU.  K tiles have two LDS stages, V tiles
+// three (the lagging group still reads V(t-1)); global_load_lds fills them one
+// tile ahead and each wave drains its own copies just before the barrier that
+// ends the tile.  Dropout and fp32 use one group of 4 waves (their registers
+// do not fit two waves per SIMD).
+//
 // Softmax bookkeeping (log2 units): the exponent offset m_run only moves when a
 // row's maximum exceeds it by more than kLazy, so most tiles skip the rescale of
 // O and l (probabilities stay below 2^kLazy); the true maximum is tracked apart
 // and l is brought to it in the epilogue.  Tiles fully inside the mask skip all
-// mask arithmetic and fold the scale into the exponent's FMA.
+// mask arithmetic and fold the scale into the exponent's FMA; a negative scale
+// is applied as a positive one to -Q (exact), so the row maximum of the raw
+// scores always gives the maximum logit.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 #include "fa_sched.h"
@@ -40,27 +53,34 @@ struct FwdShape {
   static constexpr int VP = RB + (EB == 2 ? 64 : 16);   // LDS pitch of V rows (transposing reads)
   static constexpr int KT = kFwdBN * KP;
   static constexpr int VT = kFwdBN * VP;
-  static constexpr int STAGE = KT + VT;
-  static constexpr int NQ = D / ElemTraits<T>::kChunk;  // Q operand registers
+  static constexpr int NQ = D / ElemTraits<T>::kChunk;  // Q operand registers per row block
   static constexpr int NDB = D / 32;                    // 32-wide d blocks of O
 };
 
-// NW = 8 waves share each K/V tile; the dropout variants need more than 256
-// registers and run 4-wave workgroups with one wave per SIMD instead.
-template <typename T, int D, bool DROP, bool ALIBI>
-__global__ __launch_bounds__(64 * fwd_waves(DROP), 1) void fa_fwd_kernel(FwdParams p) {
+// One wave's view of one key tile.
+struct RowTile {
+  bool live;          // the wave's 32 rows hold at least one allowed pair in the tile
+  bool full;          // every (row, key) pair of the wave's rows is inside the mask
+  uint32_t bits[2];   // keep bits of the lane's row for keys 0-31 and 32-63 of the tile
+};
+
+template <typename T, int D, int NW, int OCC, bool DROP, bool ALIBI>
+__global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
   using S = FwdShape<T, D>;
-  constexpr int NW = fwd_waves(DROP);
   constexpr int BM = 32 * NW;
-  __shared__ __attribute__((aligned(16))) char st0[S::STAGE];
-  __shared__ __attribute__((aligned(16))) char st1[S::STAGE];
+  constexpr bool kLagGroup = NW == 8;       // second, phase-shifted wave group
+  constexpr int NVB = kLagGroup ? 3 : 2;    // V stages
+  constexpr bool kBf16 = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) char kst[2][S::KT];
+  __shared__ __attribute__((aligned(16))) char vst[NVB][S::VT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int hh = lane >> 5;        // which half of the wave (k-group of MFMA operands)
   const int lrow = lane & 31;
   const int grp = lane >> 4, sl = lane & 15;
+  const bool lag = kLagGroup && wave >= 4;
 
   const int item_idx = blockIdx.x / p.nq;
   const int hl = blockIdx.x - item_idx * p.nq;
@@ -77,24 +97,29 @@ __global__ __launch_bounds__(64 * fwd_waves(DROP), 1) void fa_fwd_kernel(FwdPara
   const int i = wr0 + lrow;                        // this lane's row
   const bool row_ok = i < lq;
 
-  // ---- Q operand in registers (B of S^T = K Q^T) ----
-  using QReg = typename std::conditional<sizeof(T) == 2, bf16x8, float>::type;
+  // ---- Q operand in registers (B of S^T = K Q^T), negated for a negative scale ----
+  const bool neg = p.scale_log2 < 0.f;
+  const float sc = neg ? -p.scale_log2 : p.scale_log2;
+  using QReg = typename std::conditional<kBf16, bf16x8, float>::type;
   QReg qf[S::NQ];
   {
     const T* qp = reinterpret_cast<const T*>(p.q) + ((int64_t)(q0 + (row_ok ? i : 0)) * p.nq + h) * D;
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (kBf16) {
 #pragma unroll
       for (int c = 0; c < S::NQ; ++c) {
         bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 16 * c + 8 * hh);
+        if (neg) v = -v;
         qf[c] = row_ok ? v : bf16x8{};
       }
     } else {
 #pragma unroll
-      for (int c = 0; c < S::NQ; ++c) qf[c] = row_ok ? qp[2 * c + hh] : 0.f;
+      for (int c = 0; c < S::NQ; ++c) {
+        const float v = qp[2 * c + hh];
+        qf[c] = row_ok ? (neg ? -v : v) : 0.f;
+      }
     }
   }
 
-  const float sc = p.scale_log2;
   const float slope_l2 = ALIBI ? p.slopes[h] * kLog2e : 0.f;
   const bool has_sink = p.sink != nullptr;
   float m_run = has_sink ? p.sink[h] * kLog2e : kNegInf;   // exponent offset
@@ -111,36 +136,47 @@ __global__ __launch_bounds__(64 * fwd_waves(DROP), 1) void fa_fwd_kernel(FwdPara
   const int k_lane = lrow * S::KP + 16 * hh;                                      // K row reads
   const int v_lane = (4 * (grp >> 1) + (sl >> 2)) * S::VP + (16 * (grp & 1) + 4 * (sl & 3)) * 2;  // V^T reads
 
-  auto load = [&](char* st, int t) {
-    dma_rows<kFwdBN, S::RB, S::KP, NW>(st, kbase, kv_stride, t * kFwdBN, lkv, wave, lane);
-    dma_rows<kFwdBN, S::RB, S::VP, NW>(st + S::KT, vbase, kv_stride, t * kFwdBN, lkv, wave, lane);
+  auto classify = [&](int t) {
+    RowTile rt;
+    const int c0 = t * kFwdBN;
+    rt.live = wr0 < lq && !fa_tile_empty(win, wr0, min(wr0 + 32, lq), c0, min(c0 + kFwdBN, lkv));
+    rt.full = fa_tile_full(win, wr0, 32, c0, kFwdBN, lq, lkv);
+    rt.bits[0] = rt.bits[1] = ~0u;
+    if constexpr (DROP) {
+      if (rt.live) {
+        const int64_t pos = p.bit_base[b] + ((int64_t)h * lq + i) * lkv + c0;
+        rt.bits[0] = load_mask_bits32(p.drop, p.drop_bytes, pos);
+        rt.bits[1] = load_mask_bits32(p.drop, p.drop_bytes, pos + 32);
+      }
+    }
+    return rt;
   };
 
-  // One key tile: everything a wave does between two barriers.
-  auto tile = [&](int t, const char* ks) {
-    const char* vs = ks + S::KT;
-    const int c0 = t * kFwdBN;
-    if (wr0 >= lq || fa_tile_empty(win, wr0, min(wr0 + 32, lq), c0, min(c0 + kFwdBN, lkv))) return;
-    const bool full = fa_tile_full(win, wr0, 32, c0, kFwdBN, lq, lkv);
-    uint32_t bits[2] = {~0u, ~0u};
-    if constexpr (DROP) {
-      // issued before the MFMAs so the global latency overlaps them
-      const int64_t pos = p.bit_base[b] + ((int64_t)h * lq + i) * lkv + c0;
-      bits[0] = load_mask_bits32(p.drop, p.drop_bytes, pos);
-      bits[1] = load_mask_bits32(p.drop, p.drop_bytes, pos + 32);
-    }
-    // ---- S^T = K Q^T for two 32-key blocks ----
-    f32x16 s[2];
+  // S^T = K Q^T for the tile's two 32-key blocks.  The LDS reads of block 1 are
+  // issued between the MFMAs of block 0, so only the first reads wait on LDS.
+  auto scores = [&](const char* ks, f32x16 (&s)[2]) {
+    if constexpr (kBf16) {
+      bf16x8 a0[S::NQ], a1[S::NQ];
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      if constexpr (sizeof(T) == 2) {
-        bf16x8 a[S::NQ];
+      for (int c = 0; c < S::NQ; ++c) a0[c] = lds_read_b128(ks + k_lane + 32 * c);
 #pragma unroll
-        for (int c = 0; c < S::NQ; ++c) a[c] = lds_read_b128(ks + k_lane + kb * 32 * S::KP + 32 * c);
+      for (int c = 0; c < S::NQ; ++c) a1[c] = lds_read_b128(ks + k_lane + 32 * S::KP + 32 * c);
+      s[0] = f32x16{};
+      s[1] = f32x16{};
 #pragma unroll
-        for (int c = 0; c < S::NQ; ++c) s[kb] = mfma32(a[c], qf[c], s[kb]);
-      } else {
+      for (int c = 0; c < S::NQ; ++c) s[0] = mfma32(a0[c], qf[c], s[0]);
+#pragma unroll
+      for (int c = 0; c < S::NQ; ++c) s[1] = mfma32(a1[c], qf[c], s[1]);
+      // all reads of block 0, then one read of block 1 after each MFMA of block 0
+      __builtin_amdgcn_sched_group_barrier(0x100, S::NQ, 0);
+      sched_alternate<S::NQ, 0x008, 0x100>();
+      __builtin_amdgcn_sched_group_barrier(0x008, S::NQ, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
 #pragma unroll
         for (int c = 0; c < S::NQ; ++c) {
           const float a = *reinterpret_cast<const float*>(ks + lrow * S::KP + kb * 32 * S::KP + (2 * c + hh) * 4);
@@ -148,26 +184,21 @@ __global__ __launch_bounds__(64 * fwd_waves(DROP), 1) void fa_fwd_kernel(FwdPara
         }
       }
     }
-    // ---- row maximum of the scaled (biased, masked) logits ----
-    const bool plain = !ALIBI && full;   // logits are just sc * s
-    float mt;
-    if (plain) {
-      // max(sc * s) is sc * max(s) for sc >= 0 and sc * min(s) otherwise
-      float ext = sc >= 0.f ? kNegInf : __builtin_inff();
-      if (sc >= 0.f) {
+  };
+
+  // Online-softmax step on key tile c0..c0+63: turns the scores into
+  // probabilities (the post-dropout operand of P V), updates m / l and rescales O
+  // when the exponent offset moves.
+  auto softmax = [&](auto full_c, f32x16 (&s)[2], int c0, const RowTile& rt) {
+    constexpr bool plain = !ALIBI && decltype(full_c)::value;   // logits are just sc * s
+    float mt = kNegInf;
+    if constexpr (plain) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) ext = fmaxf(ext, s[kb][r]);
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) ext = fminf(ext, s[kb][r]);
-      }
-      mt = ext * sc;
+        for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
+      mt *= sc;
     } else {
-      mt = kNegInf;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
@@ -175,57 +206,67 @@ __global__ __launch_bounds__(64 * fwd_waves(DROP), 1) void fa_fwd_kernel(FwdPara
           const int j = c0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
           float x = s[kb][r] * sc;
           if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, (float)(j - i), x);
-          if (!full && !fa_allowed(win, i, j, lq, lkv)) x = kNegInf;
+          if (!decltype(full_c)::value && !fa_allowed(win, i, j, lq, lkv)) x = kNegInf;
           s[kb][r] = x;
           mt = fmaxf(mt, x);
         }
       }
     }
-    mt = fmaxf(mt, wave_xor32(mt));
+    mt = half_max(mt);
     m_true = fmaxf(m_true, mt);
-    const bool need = mt > m_run + kLazy;      // also true on the first finite maximum
-    float alpha = 1.f;
-    if (need) {
-      alpha = fast_exp2(m_run - mt);           // 0 when m_run = -inf
-      m_run = mt;
-    }
+    const bool need = mt > m_run + kLazy;   // also true on the first finite maximum
+    const float alpha = need ? fast_exp2(m_run - mt) : 1.f;   // 0 when m_run = -inf
+    m_run = need ? mt : m_run;
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
-    // ---- probabilities (pre-dropout sum, post-dropout operand) ----
-    float lsum = 0.f;
+    float lsum[2] = {0.f, 0.f};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float e = plain ? fast_exp2(__builtin_fmaf(s[kb][r], sc, -m_use)) : fast_exp2(s[kb][r] - m_use);
-        lsum += e;
+        lsum[kb] += e;
         if constexpr (DROP) {
           const int bit = 8 * (r >> 2) + 4 * hh + (r & 3);
-          s[kb][r] = ((bits[kb] >> bit) & 1u) ? e : 0.f;
+          s[kb][r] = ((rt.bits[kb] >> bit) & 1u) ? e : 0.f;
         } else {
           s[kb][r] = e;
         }
       }
-    l_run = l_run * alpha + lsum;
+    l_run = l_run * alpha + (lsum[0] + lsum[1]);
     if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
       for (int db = 0; db < S::NDB; ++db) o[db] *= alpha;
     }
+  };
 
-    // ---- O^T += V^T P^T ----
-    if constexpr (sizeof(T) == 2) {
+  // O^T += V^T P^T.  The transposing reads of each 16-key step are issued
+  // between the MFMAs of the previous step.
+  auto pv = [&](const char* vs, f32x16 (&s)[2]) {
+    if constexpr (kBf16) {
+      bf16x8 pb[4];
 #pragma unroll
       for (int c2 = 0; c2 < 4; ++c2) {
         const int kb = c2 >> 1, sub = c2 & 1;
-        bf16x8 pb;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pb[j] = to_bf16(s[kb][8 * sub + j]);
-        bf16x8 a[S::NDB];
+        for (int j = 0; j < 8; ++j) pb[c2][j] = to_bf16(s[kb][8 * sub + j]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      bf16x8 a[4][S::NDB];
+#pragma unroll
+      for (int c2 = 0; c2 < 4; ++c2) {
         const char* vrow = vs + v_lane + (16 * c2) * S::VP;
 #pragma unroll
-        for (int db = 0; db < S::NDB; ++db) a[db] = lds_read_tr_x2(vrow + 64 * db, vrow + 8 * S::VP + 64 * db);
-#pragma unroll
-        for (int db = 0; db < S::NDB; ++db) o[db] = mfma32(a[db], pb, o[db]);
+        for (int db = 0; db < S::NDB; ++db) a[c2][db] = lds_read_tr_x2(vrow + 64 * db, vrow + 8 * S::VP + 64 * db);
       }
+#pragma unroll
+      for (int c2 = 0; c2 < 4; ++c2)
+#pragma unroll
+        for (int db = 0; db < S::NDB; ++db) o[db] = mfma32(a[c2][db], pb[c2], o[db]);
+      // reads of step 0, then two reads (one operand of step c2+1) after each MFMA of step c2
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * S::NDB, 0);
+      sched_alternate<3 * S::NDB, 0x008, 0x100, 2>();
+      __builtin_amdgcn_sched_group_barrier(0x008, S::NDB, 0);
+      __builtin_amdgcn_sched_barrier(0);
     } else {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -242,25 +283,73 @@ __global__ __launch_bounds__(64 * fwd_waves(DROP), 1) void fa_fwd_kernel(FwdPara
     }
   };
 
+  // softmax + P V of one tile whose scores are in s
+  auto finish = [&](f32x16 (&s)[2], int t, const RowTile& rt, const char* vs) {
+    if (rt.full) softmax(std::true_type{}, s, t * kFwdBN, rt);
+    else softmax(std::false_type{}, s, t * kFwdBN, rt);
+    pv(vs, s);
+  };
+
+  auto load_k = [&](char* dst, int t) {
+    dma_rows<kFwdBN, S::RB, S::KP, NW>(dst, kbase, kv_stride, t * kFwdBN, lkv, wave, lane);
+  };
+  auto load_v = [&](char* dst, int t) {
+    dma_rows<kFwdBN, S::RB, S::VP, NW>(dst, vbase, kv_stride, t * kFwdBN, lkv, wave, lane);
+  };
+
   const int t_lo = it.lo, t_hi = it.hi;
-  if (t_lo < t_hi) load(st0, t_lo);
-  dma_wait();
-  __syncthreads();
-  for (int t = t_lo; t < t_hi; t += 2) {
-    if (t + 1 < t_hi) load(st1, t + 1);
-    tile(t, st0);
+  // stage pointers: K(t) in kc, V(t) in vc, V(t-1) in vp; kn / vn receive tile t+1
+  char* kc = kst[0];
+  char* kn = kst[1];
+  char* vp = vst[NVB - 1];
+  char* vc = vst[0];
+  char* vn = vst[1];
+  f32x16 sl_[2];          // lagging group: scores of the previous tile
+  RowTile rl;             // lagging group: flags of the previous tile
+  rl.live = false;
+  if (t_lo < t_hi) {
+    load_k(kc, t_lo);
+    load_v(vc, t_lo);
     dma_wait();
     __syncthreads();
+  }
+  for (int t = t_lo; t < t_hi; ++t) {
     if (t + 1 < t_hi) {
-      if (t + 2 < t_hi) load(st0, t + 2);
-      tile(t + 1, st1);
-      dma_wait();
-      __syncthreads();
+      load_k(kn, t + 1);
+      load_v(vn, t + 1);
+    }
+    if (!lag) {
+      const RowTile rt = classify(t);
+      if (rt.live) {
+        f32x16 s[2];
+        scores(kc, s);
+        finish(s, t, rt, vc);
+      }
+    } else {
+      if (rl.live) finish(sl_, t - 1, rl, vp);
+      rl = classify(t);
+      if (rl.live) scores(kc, sl_);
+    }
+    dma_wait();
+    __syncthreads();
+    char* tk = kc;
+    kc = kn;
+    kn = tk;
+    if constexpr (NVB == 3) {
+      char* tv = vp;
+      vp = vc;
+      vc = vn;
+      vn = tv;
+    } else {
+      char* tv = vc;
+      vc = vn;
+      vn = tv;
     }
   }
+  if (lag && rl.live) finish(sl_, t_hi - 1, rl, vp);
 
   // ---- epilogue: O = o / (keep * l_run); l reported against the true maximum ----
-  const float l_tot = l_run + wave_xor32(l_run);
+  const float l_tot = half_sum(l_run);
   if (row_ok) {
     const int64_t rowg = q0 + i;
     const float inv = l_tot > 0.f ? p.inv_keep / l_tot : 0.f;
@@ -270,7 +359,7 @@ __global__ __launch_bounds__(64 * fwd_waves(DROP), 1) void fa_fwd_kernel(FwdPara
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int d = 32 * db + 8 * a + 4 * hh;
-        if constexpr (sizeof(T) == 2) {
+        if constexpr (kBf16) {
           bf16x4 v;
 #pragma unroll
           for (int e = 0; e < 4; ++e) v[e] = to_bf16(o[db][4 * a + e] * inv);
@@ -295,17 +384,19 @@ template <typename T, int D>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
   const int64_t blocks = (int64_t)p.n_items * p.nq;
   if (blocks == 0) return hipSuccess;
-  const dim3 grid((unsigned)blocks);
   const bool drop = p.use_dropout != 0, alibi = p.slopes != nullptr;
-  const dim3 block(64 * fwd_waves(drop));
+  constexpr bool F32 = sizeof(T) == 4;
+  constexpr int NWD = fwd_waves(true, F32), NWP = fwd_waves(false, F32);
+  constexpr int OCD = fwd_occupancy(true, F32), OCP = fwd_occupancy(false, F32);
+  const dim3 grid((unsigned)blocks), block(64 * (drop ? NWD : NWP));
   if (drop && alibi)
-    hipLaunchKernelGGL((fa_fwd_kernel<T, D, true, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, NWD, OCD, true, true>), grid, block, 0, s, p);
   else if (drop)
-    hipLaunchKernelGGL((fa_fwd_kernel<T, D, true, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, NWD, OCD, true, false>), grid, block, 0, s, p);
   else if (alibi)
-    hipLaunchKernelGGL((fa_fwd_kernel<T, D, false, true>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, NWP, OCP, false, true>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((fa_fwd_kernel<T, D, false, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, NWP, OCP, false, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 

@@ -76,9 +76,19 @@ struct BwdParams {
 };
 
 // Tile shapes (rows x keys) of each pass; the host scheduler uses the same numbers.
-// waves per forward workgroup (32 query rows each): 8, or 4 with dropout
-constexpr int fwd_waves(bool dropout) { return dropout ? 4 : 8; }
-constexpr int fwd_rows(bool dropout) { return 32 * fwd_waves(dropout); }
+// Forward workgroup: waves of 32 query rows each.  bf16 without dropout takes
+// FA_FWD_WAVES waves (8: two phase-shifted groups, two waves per SIMD) with
+// FA_FWD_OCC workgroups per CU; dropout and fp32 inputs take 4 waves, whose
+// registers need a whole SIMD per wave.
+#ifndef FA_FWD_WAVES
+#define FA_FWD_WAVES 4
+#endif
+#ifndef FA_FWD_OCC
+#define FA_FWD_OCC 2
+#endif
+constexpr int fwd_waves(bool dropout, bool fp32) { return (dropout || fp32) ? 4 : FA_FWD_WAVES; }
+constexpr int fwd_occupancy(bool dropout, bool fp32) { return (dropout || fp32) ? 1 : FA_FWD_OCC; }
+constexpr int fwd_rows(bool dropout, bool fp32) { return 32 * fwd_waves(dropout, fp32); }
 constexpr int kFwdBN = 64;
 constexpr int kKvBN = 128, kKvBM = 64;
 constexpr int kDqBM = 128, kDqBN = 64;

@@ -77,7 +77,9 @@ typedef struct fa_config {
   int64_t pre_tokens;            /* band only: keys allowed left of the diagonal              */
   int64_t next_tokens;           /* band only: keys allowed right of the diagonal             */
   int32_t deterministic;         /* bwd: 1 = separate dQ pass (bitwise reproducible),
-                                    0 = fp32 atomic dQ accumulation                           */
+                                    0 = fp32 atomic dQ accumulation where available (fp32
+                                    with D = 128, and bf16 with D = 128 and alibi, always
+                                    take the deterministic passes)                            */
   int32_t flags;                 /* reserved, must be 0                                       */
 } fa_config;
 
