@@ -27,6 +27,9 @@ def common_flags():
     return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"),
             # no packed-fp32 instructions in any generated code
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+            # MFMA results in VGPRs: the kernels read their accumulators with VALU
+            # code, and the default placement shuttled them through AGPRs
+            "-mllvm", "-amdgpu-mfma-vgpr-form=true",
             "-Wno-unused-result"]
 
 

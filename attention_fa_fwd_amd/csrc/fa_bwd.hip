@@ -663,7 +663,7 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
   using Op = typename std::conditional<sizeof(T) == 2, bf16x8, float>::type;
   __shared__ __attribute__((aligned(16))) char st0[S::STAGE];
   __shared__ __attribute__((aligned(16))) char st1[S::STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5, lrow = lane & 31;
   const int grp = lane >> 4, sl = lane & 15;
 
@@ -731,15 +731,18 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
       // ---- S^T = K Q^T, dP~^T = V dY^T for 32 keys (lane = row, registers = keys) ----
       f32x16 s = f32x16{}, dp = f32x16{};
       if constexpr (sizeof(T) == 2) {
-        bf16x8 ka[S::NOP];
+        // K and V reads run a few MFMAs ahead of their use
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int c = 0; c < S::NOP; ++c) ka[c] = lds_read_b128(ks + a_lane + 32 * kb * S::P + 32 * c);
-#pragma unroll
-        for (int c = 0; c < S::NOP; ++c) s = mfma32(ka[c], qf[c], s);
-#pragma unroll
-        for (int c = 0; c < S::NOP; ++c) ka[c] = lds_read_b128(vs + a_lane + 32 * kb * S::P + 32 * c);
-#pragma unroll
-        for (int c = 0; c < S::NOP; ++c) dp = mfma32(ka[c], df[c], dp);
+        for (int c = 0; c < S::NOP; ++c) {
+          const bf16x8 ka = lds_read_b128(ks + a_lane + 32 * kb * S::P + 32 * c);
+          const bf16x8 va = lds_read_b128(vs + a_lane + 32 * kb * S::P + 32 * c);
+          s = mfma32(ka, qf[c], s);
+          dp = mfma32(va, df[c], dp);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        sched_alternate<2 * S::NOP, 0x008, 0x100>();
+        __builtin_amdgcn_sched_barrier(0);
       } else {
         const char* krow = ks + (32 * kb + lrow) * S::P;
         const char* vrow = vs + (32 * kb + lrow) * S::P;
@@ -750,32 +753,45 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
         }
       }
       f32x16 ds;
+      const float jmi = (float)(c0 + 32 * kb + 4 * hh - i);   // j - i of register 0
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kk = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
         const int jj = c0 + kk;
-        float x = s[r] * p.scale_log2;
-        if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, (float)(jj - i), x);
-        if (!full && !fa_allowed(win, i, jj, lq, lkv)) x = kNegInf;
-        const float pr = fast_exp2(x - lse2);
+        float pr;
+        if (full && !ALIBI) {
+          pr = fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -lse2));
+        } else {
+          float x = s[r] * p.scale_log2;
+          if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, jmi + (float)(8 * (r >> 2) + (r & 3)), x);
+          if (!full) {
+            const bool ok = row_ok & (jj < lkv) & (jj >= fa_row_lo(win, i)) & (jj <= fa_row_hi(win, i));
+            x = ok ? x : kNegInf;
+          }
+          pr = fast_exp2(x - lse2);
+        }
         float dpv = dp[r];
         if constexpr (DROP) dpv = ((bits >> kk) & 1ull) ? dpv * p.inv_keep : 0.f;
         ds[r] = pr * (dpv - di);
       }
       // ---- dQ^T += K^T dS^T (A = K through the transposing read, B = dS from registers) ----
       if constexpr (sizeof(T) == 2) {
+        bf16x8 bs[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) bs[c][e] = to_bf16(ds[8 * c + e]);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          bf16x8 bs;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) bs[e] = to_bf16(ds[8 * c + e]);
           const char* base = ks + t_lane + (32 * kb + 16 * c) * S::P;
-          bf16x8 a[S::NDB];
 #pragma unroll
-          for (int db = 0; db < S::NDB; ++db) a[db] = lds_read_tr_x2(base + 64 * db, base + 8 * S::P + 64 * db);
-#pragma unroll
-          for (int db = 0; db < S::NDB; ++db) acc[db] = mfma32(a[db], bs, acc[db]);
+          for (int db = 0; db < S::NDB; ++db)
+            acc[db] = mfma32(lds_read_tr_x2(base + 64 * db, base + 8 * S::P + 64 * db), bs[c], acc[db]);
         }
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        sched_alternate<2 * S::NDB, 0x008, 0x100, 2>();
+        __builtin_amdgcn_sched_barrier(0);
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
