@@ -104,8 +104,11 @@ FaWindow window_of(const Problem& pr, int64_t b) {
   return fa_make_window(pr.mode, pr.pre, pr.next, lq, lkv);
 }
 
-// Work list of one pass; longest items first (stable), so the dispatcher starts
-// the heaviest tiles early and the short ones fill the tail.
+// Work list of one pass.  The items of one sequence are consecutive, so the
+// workgroups running at the same time on an XCD (the grid maps each kv head to
+// one XCD) share that sequence's K/V (forward, dQ) or Q/dY (dK/dV) in L2;
+// sequences come heaviest first and, inside a sequence, items heaviest first,
+// so the dispatcher starts long work early and short work fills the tail.
 std::vector<WorkItem> schedule(const Problem& pr, int pass, int* bm_out, int* bn_out) {
   std::vector<WorkItem> items;
   int bm, bn;
@@ -133,8 +136,12 @@ std::vector<WorkItem> schedule(const Problem& pr, int pass, int* bm_out, int* bn
       }
     }
   }
-  std::stable_sort(items.begin(), items.end(),
-                   [](const WorkItem& a, const WorkItem& b) { return (a.hi - a.lo) > (b.hi - b.lo); });
+  std::vector<int64_t> seq_work(pr.batch, 0);
+  for (const WorkItem& x : items) seq_work[x.b] += x.hi - x.lo;
+  std::stable_sort(items.begin(), items.end(), [&](const WorkItem& x, const WorkItem& y) {
+    if (x.b != y.b) return seq_work[x.b] != seq_work[y.b] ? seq_work[x.b] > seq_work[y.b] : x.b < y.b;
+    return (x.hi - x.lo) > (y.hi - y.lo);
+  });
   return items;
 }
 

@@ -194,8 +194,11 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
   const int a_lane = lrow * S::P + 16 * hh;
   const int t_lane = (4 * (grp >> 1) + (sl >> 2)) * S::P + (16 * (grp & 1) + 4 * (sl & 3)) * 2;
 
-  auto step_head = [&](int n) { return g * p.group + n / nqt; };
-  auto step_row0 = [&](int n) { return (it.lo + n % nqt) * kKvBM; };
+  // steps walk the query tiles from the last one down, the heads of the group
+  // innermost: every key tile of a sequence then starts on the same rows at the
+  // same time, and the workgroups running together share those Q/dY rows in L2
+  auto step_head = [&](int n) { return g * p.group + n % p.group; };
+  auto step_row0 = [&](int n) { return (it.hi - 1 - n / p.group) * kKvBM; };
 
   auto load = [&](char* st, int n) {
     const int h = step_head(n), r0 = step_row0(n);

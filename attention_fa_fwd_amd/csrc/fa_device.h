@@ -197,6 +197,54 @@ __device__ __forceinline__ void dma_rows(char* lds, const char* gbase, int64_t g
   }
 }
 
+// ---- swizzled bf16 tiles ----
+// Rows of RB = 128 or 256 bytes are stored back to back (no padding); the
+// 16-byte chunk q of row r sits at r*RB + 16*(q ^ tile_swz<RB>(r)).  Under this
+// XOR pattern both operand reads of the kernels are free of LDS bank conflicts:
+// 16-byte row reads (16 lanes = 16 consecutive rows, one chunk) and the
+// transposing 8-byte reads (each half-wave covers 4 consecutive rows x 64 bytes).
+template <int RB>
+__device__ __forceinline__ int tile_swz(int r) {
+  static_assert(RB == 128 || RB == 256, "row size");
+  if constexpr (RB == 256) return ((r & 3) << 2) | ((r >> 2) & 3);
+  else return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+}
+
+// One global_load_lds_dwordx4: lane i copies 16 bytes from gbase + voff into
+// LDS at lds + 16*i (1 KB per wave).  Drained like dma_dword.
+__device__ __forceinline__ void dma_x4(const char* lds, const void* gbase, uint32_t voff) {
+  const uint32_t m0 = (uint32_t)(uintptr_t)(lds_char*)(uintptr_t)lds;
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"{m0}"(m0), "v"(voff), "s"(gbase) : "memory");
+}
+
+// The NW waves copy ROWS rows of RB bytes (row r' = row0 + r read from
+// gbase + r' * gstride) into a swizzled LDS tile, 1 KB per instruction: lane i
+// writes chunk slot i % (RB/16) of tile row r = base + i / (RB/16) and so
+// fetches chunk (slot ^ tile_swz(r)) of that row.  Rows at or beyond `valid`
+// repeat row valid - 1 (finite data that the caller masks); row0 < valid.
+template <int ROWS, int RB, int NW>
+__device__ __forceinline__ void dma_tile_swz(char* lds, const char* gbase, int64_t gstride, int row0, int valid,
+                                             int wave, int lane) {
+  constexpr int RPI = 1024 / RB;   // rows per instruction
+  constexpr int CPR = RB / 16;     // chunks per row
+  constexpr int NI = ROWS / RPI;   // instructions per tile
+  static_assert(NI % NW == 0, "instructions split over the waves");
+  constexpr int IPW = NI / NW;
+  const int w = __builtin_amdgcn_readfirstlane(wave);
+  row0 = __builtin_amdgcn_readfirstlane(row0);
+  valid = __builtin_amdgcn_readfirstlane(valid);
+  const char* src = gbase + (int64_t)row0 * gstride;
+  const int lr = lane / CPR, slot = lane % CPR;
+  const int last = valid - 1 - row0;   // last valid tile row (>= 0)
+#pragma unroll
+  for (int k = 0; k < IPW; ++k) {
+    const int r = (w * IPW + k) * RPI + lr;   // this lane's tile row
+    const int rc = r < last ? r : last;
+    const uint32_t voff = (uint32_t)rc * (uint32_t)gstride + 16u * (uint32_t)(slot ^ tile_swz<RB>(r));
+    dma_x4(lds + (w * IPW + k) * 1024, src, voff);
+  }
+}
+
 // Same tile layout as dma_rows, copied through registers (global load, then LDS
 // store) so that no copy is in flight once it returns.  Used by kernels that may
 // keep scratch spills, which must never coexist with in-flight LDS DMA.

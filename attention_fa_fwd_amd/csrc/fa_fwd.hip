@@ -10,7 +10,9 @@
 //
 // Work decomposition: one workgroup = NW waves = one query tile of 32*NW rows
 // of one (sequence, head); each wave owns 32 rows, and all waves share each K/V
-// tile of 64 keys.  Per wave and tile:
+// tile of 64 keys.  bf16 tiles sit in LDS unpadded with an XOR swizzle of their
+// 16-byte chunks and arrive by 16-byte-per-lane LDS DMA (four rows per
+// instruction); fp32 tiles use padded rows and 4-byte DMA.  Per wave and tile:
 //   S^T (64 keys x 32 rows) = K Q^T      A = K rows from LDS, B = Q in registers
 //   O^T (D x 32 rows)      += V^T P^T    A = V via the transposing LDS read,
 //                                         B = P taken straight from the S^T accumulator
@@ -45,12 +47,18 @@ namespace fa {
 
 constexpr float kLazy = 8.0f;
 
+#ifndef FA_FWD_PIPE
+#define FA_FWD_PIPE 0
+#endif
+
 template <typename T, int D>
 struct FwdShape {
   static constexpr int EB = sizeof(T);
   static constexpr int RB = D * EB;                     // bytes per K/V row
-  static constexpr int KP = RB + 16;                    // LDS pitch of K rows (16-byte row reads)
-  static constexpr int VP = RB + (EB == 2 ? 64 : 16);   // LDS pitch of V rows (transposing reads)
+  // bf16 tiles are swizzled and unpadded; fp32 tiles use padded rows
+  static constexpr bool kSwz = EB == 2;
+  static constexpr int KP = kSwz ? RB : RB + 16;        // LDS pitch of K rows
+  static constexpr int VP = kSwz ? RB : RB + 16;        // LDS pitch of V rows
   static constexpr int KT = kFwdBN * KP;
   static constexpr int VT = kFwdBN * VP;
   static constexpr int NQ = D / ElemTraits<T>::kChunk;  // Q operand registers per row block
@@ -71,6 +79,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
   constexpr bool kLagGroup = NW == 8;       // second, phase-shifted wave group
   constexpr int NVB = kLagGroup ? 3 : 2;    // V stages
   constexpr bool kBf16 = sizeof(T) == 2;
+  constexpr bool kPipe = FA_FWD_PIPE && !kLagGroup && kBf16;   // in-wave software pipeline
   __shared__ __attribute__((aligned(16))) char kst[2][S::KT];
   __shared__ __attribute__((aligned(16))) char vst[NVB][S::VT];
 
@@ -135,6 +144,19 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
   // per-lane LDS byte offsets; every other offset below is a compile-time immediate
   const int k_lane = lrow * S::KP + 16 * hh;                                      // K row reads
   const int v_lane = (4 * (grp >> 1) + (sl >> 2)) * S::VP + (16 * (grp & 1) + 4 * (sl & 3)) * 2;  // V^T reads
+  // swizzled bf16 tiles: K chunk 2c + hh of row lrow (+32 for the second key block),
+  // V^T reads of rows rv and rv + 8 (+16 per 16-key step), chunk 4db + qv
+  int koff[S::kSwz ? S::NQ : 1], voff[2][S::kSwz ? S::NDB : 1];
+  if constexpr (S::kSwz) {
+#pragma unroll
+    for (int c = 0; c < S::NQ; ++c) koff[c] = lrow * S::RB + 16 * ((2 * c + hh) ^ tile_swz<S::RB>(lrow));
+    const int rv = 4 * (grp >> 1) + (sl >> 2), qv = 2 * (grp & 1) + ((sl & 3) >> 1), bv = 8 * (sl & 1);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int db = 0; db < S::NDB; ++db)
+        voff[hf][db] = (rv + 8 * hf) * S::RB + 16 * ((4 * db + qv) ^ tile_swz<S::RB>(rv + 8 * hf)) + bv;
+  }
 
   auto classify = [&](int t) {
     RowTile rt;
@@ -154,25 +176,28 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
 
   // S^T = K Q^T for the tile's two 32-key blocks.  The LDS reads of block 1 are
   // issued between the MFMAs of block 0, so only the first reads wait on LDS.
-  auto scores = [&](const char* ks, f32x16 (&s)[2]) {
+  auto scores = [&](const char* ks, f32x16 (&s)[2], auto fence_c) {
+    constexpr bool kFence = decltype(fence_c)::value;   // own scheduling region
     if constexpr (kBf16) {
       bf16x8 a0[S::NQ], a1[S::NQ];
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kFence) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int c = 0; c < S::NQ; ++c) a0[c] = lds_read_b128(ks + k_lane + 32 * c);
+      for (int c = 0; c < S::NQ; ++c) a0[c] = lds_read_b128(ks + koff[c]);
 #pragma unroll
-      for (int c = 0; c < S::NQ; ++c) a1[c] = lds_read_b128(ks + k_lane + 32 * S::KP + 32 * c);
+      for (int c = 0; c < S::NQ; ++c) a1[c] = lds_read_b128(ks + koff[c] + 32 * S::RB);
       s[0] = f32x16{};
       s[1] = f32x16{};
 #pragma unroll
       for (int c = 0; c < S::NQ; ++c) s[0] = mfma32(a0[c], qf[c], s[0]);
 #pragma unroll
       for (int c = 0; c < S::NQ; ++c) s[1] = mfma32(a1[c], qf[c], s[1]);
-      // all reads of block 0, then one read of block 1 after each MFMA of block 0
-      __builtin_amdgcn_sched_group_barrier(0x100, S::NQ, 0);
-      sched_alternate<S::NQ, 0x008, 0x100>();
-      __builtin_amdgcn_sched_group_barrier(0x008, S::NQ, 0);
-      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (kFence) {
+        // all reads of block 0, then one read of block 1 after each MFMA of block 0
+        __builtin_amdgcn_sched_group_barrier(0x100, S::NQ, 0);
+        sched_alternate<S::NQ, 0x008, 0x100>();
+        __builtin_amdgcn_sched_group_barrier(0x008, S::NQ, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     } else {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -189,7 +214,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
   // Online-softmax step on key tile c0..c0+63: turns the scores into
   // probabilities (the post-dropout operand of P V), updates m / l and rescales O
   // when the exponent offset moves.
-  auto softmax = [&](auto full_c, f32x16 (&s)[2], int c0, const RowTile& rt) {
+  auto softmax_core = [&](auto full_c, f32x16 (&s)[2], int c0, const RowTile& rt, bool& need) -> float {
     constexpr bool plain = !ALIBI && decltype(full_c)::value;   // logits are just sc * s
     float mt = kNegInf;
     if constexpr (plain) {
@@ -214,7 +239,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
     }
     mt = half_max(mt);
     m_true = fmaxf(m_true, mt);
-    const bool need = mt > m_run + kLazy;   // also true on the first finite maximum
+    need = mt > m_run + kLazy;   // also true on the first finite maximum
     const float alpha = need ? fast_exp2(m_run - mt) : 1.f;   // 0 when m_run = -inf
     m_run = need ? mt : m_run;
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
@@ -233,10 +258,18 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
         }
       }
     l_run = l_run * alpha + (lsum[0] + lsum[1]);
+    return alpha;
+  };
+  auto rescale = [&](bool need, float alpha) {
     if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
       for (int db = 0; db < S::NDB; ++db) o[db] *= alpha;
     }
+  };
+  auto softmax = [&](auto full_c, f32x16 (&s)[2], int c0, const RowTile& rt) {
+    bool need;
+    const float alpha = softmax_core(full_c, s, c0, rt, need);
+    rescale(need, alpha);
   };
 
   // O^T += V^T P^T.  The transposing reads of each 16-key step are issued
@@ -254,9 +287,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
       bf16x8 a[4][S::NDB];
 #pragma unroll
       for (int c2 = 0; c2 < 4; ++c2) {
-        const char* vrow = vs + v_lane + (16 * c2) * S::VP;
+        const char* vrow = vs + (16 * c2) * S::RB;
 #pragma unroll
-        for (int db = 0; db < S::NDB; ++db) a[c2][db] = lds_read_tr_x2(vrow + 64 * db, vrow + 8 * S::VP + 64 * db);
+        for (int db = 0; db < S::NDB; ++db) a[c2][db] = lds_read_tr_x2(vrow + voff[0][db], vrow + voff[1][db]);
       }
 #pragma unroll
       for (int c2 = 0; c2 < 4; ++c2)
@@ -291,13 +324,71 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
   };
 
   auto load_k = [&](char* dst, int t) {
-    dma_rows<kFwdBN, S::RB, S::KP, NW>(dst, kbase, kv_stride, t * kFwdBN, lkv, wave, lane);
+    if constexpr (S::kSwz) dma_tile_swz<kFwdBN, S::RB, NW>(dst, kbase, kv_stride, t * kFwdBN, lkv, wave, lane);
+    else dma_rows<kFwdBN, S::RB, S::KP, NW>(dst, kbase, kv_stride, t * kFwdBN, lkv, wave, lane);
   };
   auto load_v = [&](char* dst, int t) {
-    dma_rows<kFwdBN, S::RB, S::VP, NW>(dst, vbase, kv_stride, t * kFwdBN, lkv, wave, lane);
+    if constexpr (S::kSwz) dma_tile_swz<kFwdBN, S::RB, NW>(dst, vbase, kv_stride, t * kFwdBN, lkv, wave, lane);
+    else dma_rows<kFwdBN, S::RB, S::VP, NW>(dst, vbase, kv_stride, t * kFwdBN, lkv, wave, lane);
   };
 
   const int t_lo = it.lo, t_hi = it.hi;
+  if constexpr (kPipe) {
+    // Software pipeline inside each wave: the scores of tile t+1 are computed
+    // on the matrix cores while the VALU runs the softmax of tile t (K tiles are
+    // copied two tiles ahead, V tiles one).
+    const int n = t_hi - t_lo;
+    f32x16 sa[2], sb[2];
+    RowTile ra, rb;
+    ra.live = rb.live = false;
+    if (n > 0) {
+      load_k(kst[0], t_lo);
+      load_v(vst[0], t_lo);
+      if (n > 1) load_k(kst[1], t_lo + 1);
+      dma_wait();
+      __syncthreads();
+      ra = classify(t_lo);
+      if (ra.live) scores(kst[0], sa, std::true_type{});
+      __syncthreads();   // K(t_lo) is read by every wave before K(t_lo + 2) replaces it
+    }
+    constexpr int kSoftValu = DROP ? 200 : 150;
+    auto body = [&](auto cb_c, int j, f32x16 (&sc_)[2], f32x16 (&sn)[2], RowTile& rc, RowTile& rn) {
+      constexpr int cb = decltype(cb_c)::value, nb = cb ^ 1;
+      const int t = t_lo + j;
+      const bool has_next = j + 1 < n;
+      if (j + 2 < n) load_k(kst[cb], t + 2);
+      rn.live = false;
+      if (has_next) {
+        load_v(vst[nb], t + 1);
+        rn = classify(t + 1);
+      }
+      bool need = false;
+      float alpha = 1.f;
+      if (rn.live && rc.live && rc.full) {
+        scores(kst[nb], sn, std::false_type{});
+        alpha = softmax_core(std::true_type{}, sc_, t * kFwdBN, rc, need);
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        sched_alternate3<2 * S::NQ, 0x008, 1, 0x002, kSoftValu / (2 * S::NQ), 0x100, 1>();
+        __builtin_amdgcn_sched_barrier(0);
+      } else {
+        if (rn.live) scores(kst[nb], sn, std::true_type{});
+        if (rc.live) {
+          if (rc.full) alpha = softmax_core(std::true_type{}, sc_, t * kFwdBN, rc, need);
+          else alpha = softmax_core(std::false_type{}, sc_, t * kFwdBN, rc, need);
+        }
+      }
+      if (rc.live) {
+        rescale(need, alpha);
+        pv(vst[cb], sc_);
+      }
+      dma_wait();
+      __syncthreads();
+    };
+    for (int j = 0; j < n; j += 2) {
+      body(std::integral_constant<int, 0>{}, j, sa, sb, ra, rb);
+      if (j + 1 < n) body(std::integral_constant<int, 1>{}, j + 1, sb, sa, rb, ra);
+    }
+  } else {
   // stage pointers: K(t) in kc, V(t) in vc, V(t-1) in vp; kn / vn receive tile t+1
   char* kc = kst[0];
   char* kn = kst[1];
@@ -322,13 +413,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
       const RowTile rt = classify(t);
       if (rt.live) {
         f32x16 s[2];
-        scores(kc, s);
+        scores(kc, s, std::true_type{});
         finish(s, t, rt, vc);
       }
     } else {
       if (rl.live) finish(sl_, t - 1, rl, vp);
       rl = classify(t);
-      if (rl.live) scores(kc, sl_);
+      if (rl.live) scores(kc, sl_, std::true_type{});
     }
     dma_wait();
     __syncthreads();
@@ -347,6 +438,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
     }
   }
   if (lag && rl.live) finish(sl_, t_hi - 1, rl, vp);
+  }
 
   // ---- epilogue: O = o / (keep * l_run); l reported against the true maximum ----
   const float l_tot = half_sum(l_run);

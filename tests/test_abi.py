@@ -174,7 +174,15 @@ def test_schedule_matches_brute_force(lq, lkv, mode, pre, nxt, pass_id):
                pre_tokens=pre, next_tokens=nxt)
     items, (bm, bn) = fa.fa_debug_schedule(cfg, pass_id)
     costs = items[:, 3] - items[:, 2]
-    assert np.all(np.diff(costs) <= 0), "items must be ordered longest first"
+    # items of one sequence are consecutive; sequences heaviest first, and
+    # inside a sequence items heaviest first
+    seqs = [int(b) for i, b in enumerate(items[:, 0]) if i == 0 or b != items[i - 1, 0]]
+    assert len(seqs) == len(set(seqs)), "items of a sequence must be consecutive"
+    seq_cost = [int(costs[items[:, 0] == b].sum()) for b in seqs]
+    assert all(x >= y for x, y in zip(seq_cost, seq_cost[1:])), "sequences heaviest first"
+    for b in seqs:
+        c = costs[items[:, 0] == b]
+        assert np.all(np.diff(c) <= 0), "items of a sequence heaviest first"
     seen = {}
     for b, tile, lo, hi in items.tolist():
         seen[(b, tile)] = (lo, hi)
