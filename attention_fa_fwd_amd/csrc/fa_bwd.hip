@@ -109,7 +109,11 @@ template <typename T, int D>
 struct KvShape {
   static constexpr int EB = sizeof(T);
   static constexpr int RB = D * EB;
-  static constexpr int P = RB + 16;                 // LDS pitch of Q / dY / K rows
+  // bf16 Q / dY tiles are swizzled and unpadded (see tile_swz); fp32 tiles and
+  // the K tile of the atomic variant use padded rows
+  static constexpr bool kSwz = EB == 2;
+  static constexpr int P = kSwz ? RB : RB + 16;     // LDS pitch of Q / dY rows
+  static constexpr int KTP = RB + 16;               // LDS pitch of K rows (atomic dQ)
   static constexpr int QT = kKvBM * P;              // one 64-row Q (or dY) tile
   // stage layout: Q | dY | lse2[64] | D_i[64] | keep bits[64][4]
   static constexpr int OFF_DY = QT;
@@ -117,7 +121,7 @@ struct KvShape {
   static constexpr int OFF_DEL = OFF_LSE + 4 * kKvBM;
   static constexpr int OFF_BITS = OFF_DEL + 4 * kKvBM;
   static constexpr int STAGE = OFF_BITS + 16 * kKvBM;
-  static constexpr int KT = kKvBN * P;              // the 128-key K tile (atomic dQ only)
+  static constexpr int KT = kKvBN * KTP;            // the 128-key K tile (atomic dQ only)
   static constexpr int DSP = kKvBM * EB + 16;       // pitch of dS^T rows (one row per key)
   static constexpr int DST = kKvBN * DSP;
   static constexpr int NOP = D / ElemTraits<T>::kChunk;
@@ -175,9 +179,9 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
   if constexpr (ATOMIC) {
     const char* kb = reinterpret_cast<const char*>(p.k) + ((int64_t)k0 * p.nkv + g) * S::RB;
     if constexpr (kDma)
-      dma_rows<kKvBN, S::RB, S::P>(kt, kb, kv_stride, c0, lkv, wave, lane);
+      dma_rows<kKvBN, S::RB, S::KTP>(kt, kb, kv_stride, c0, lkv, wave, lane);
     else
-      copy_rows<kKvBN, S::RB, S::P>(kt, kb, kv_stride, c0, lkv, tid);
+      copy_rows<kKvBN, S::RB, S::KTP>(kt, kb, kv_stride, c0, lkv, tid);
   }
 
   f32x16 dk[S::NDB], dv[S::NDB];
@@ -193,6 +197,19 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
   // per-lane LDS offsets: A-operand row reads and transposing B-operand reads
   const int a_lane = lrow * S::P + 16 * hh;
   const int t_lane = (4 * (grp >> 1) + (sl >> 2)) * S::P + (16 * (grp & 1) + 4 * (sl & 3)) * 2;
+  // swizzled bf16 tiles: row reads of chunk 2c + hh of row lrow (+32 per row
+  // block), transposing reads of rows rv and rv + 8 (+16 per step), chunk 4db + qv
+  int qoff[S::kSwz ? S::NOP : 1], toff[2][S::kSwz ? S::NDB : 1];
+  if constexpr (S::kSwz) {
+#pragma unroll
+    for (int c = 0; c < S::NOP; ++c) qoff[c] = lrow * S::RB + 16 * ((2 * c + hh) ^ tile_swz<S::RB>(lrow));
+    const int rv = 4 * (grp >> 1) + (sl >> 2), qv = 2 * (grp & 1) + ((sl & 3) >> 1), bv = 8 * (sl & 1);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int db = 0; db < S::NDB; ++db)
+        toff[hf][db] = (rv + 8 * hf) * S::RB + 16 * ((4 * db + qv) ^ tile_swz<S::RB>(rv + 8 * hf)) + bv;
+  }
 
   // steps walk the query tiles from the last one down, the heads of the group
   // innermost: every key tile of a sequence then starts on the same rows at the
@@ -213,16 +230,16 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
         const float v = (tid < kKvBM ? p.lse : p.delta)[(int64_t)(q0 + rr) * p.nq + h];
         reinterpret_cast<float*>(st + (tid < kKvBM ? S::OFF_LSE : S::OFF_DEL))[rl] = v;
       }
-      return;
-    }
-    dma_rows<kKvBM, S::RB, S::P>(st, qb, q_stride, r0, lq, wave, lane);
-    dma_rows<kKvBM, S::RB, S::P>(st + S::OFF_DY, dyb, q_stride, r0, lq, wave, lane);
-    const int w = __builtin_amdgcn_readfirstlane(wave);
-    if (w < 2) {
-      // lse2 (wave 0) and D_i (wave 1) of the 64 rows, one dword per lane
-      const int rr = (r0 + lane < lq) ? r0 + lane : 0;
-      dma_dword(st + (w == 0 ? S::OFF_LSE : S::OFF_DEL), w == 0 ? p.lse : p.delta,
-                (uint32_t)(((int64_t)(q0 + rr) * p.nq + h) * 4));
+    } else {
+      dma_tile_swz<kKvBM, S::RB, 4>(st, qb, q_stride, r0, lq, wave, lane);
+      dma_tile_swz<kKvBM, S::RB, 4>(st + S::OFF_DY, dyb, q_stride, r0, lq, wave, lane);
+      const int w = __builtin_amdgcn_readfirstlane(wave);
+      if (w < 2) {
+        // lse2 (wave 0) and D_i (wave 1) of the 64 rows, one dword per lane
+        const int rr = (r0 + lane < lq) ? r0 + lane : 0;
+        dma_dword(st + (w == 0 ? S::OFF_LSE : S::OFF_DEL), w == 0 ? p.lse : p.delta,
+                  (uint32_t)(((int64_t)(q0 + rr) * p.nq + h) * 4));
+      }
     }
   };
   // keep bits of the next step: 64 rows x 128 keys = 256 words, one per thread;
@@ -264,7 +281,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
         const bf16x8 a0 = lds_read_tr_x2(dst + krow * S::DSP + coln, dst + (krow + 8) * S::DSP + coln);
         const bf16x8 a1 = lds_read_tr_x2(dst + krow * S::DSP + coln + 64, dst + (krow + 8) * S::DSP + coln + 64);
         const int colk = (dcol + 16 * (grp & 1) + 4 * (sl & 3)) * 2;
-        const bf16x8 bo = lds_read_tr_x2(kt + krow * S::P + colk, kt + (krow + 8) * S::P + colk);
+        const bf16x8 bo = lds_read_tr_x2(kt + krow * S::KTP + colk, kt + (krow + 8) * S::KTP + colk);
         acc[0] = mfma32(a0, bo, acc[0]);
         acc[1] = mfma32(a1, bo, acc[1]);
       }
@@ -291,8 +308,8 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
     dp = f32x16{};
 #pragma unroll
     for (int c = 0; c < S::NOP; ++c) {
-      const bf16x8 qa = lds_read_b128(st + a_lane + 32 * rb * S::P + 32 * c);
-      const bf16x8 ya = lds_read_b128(st + S::OFF_DY + a_lane + 32 * rb * S::P + 32 * c);
+      const bf16x8 qa = lds_read_b128(st + qoff[c] + 32 * rb * S::RB);
+      const bf16x8 ya = lds_read_b128(st + S::OFF_DY + qoff[c] + 32 * rb * S::RB);
       s = mfma32(qa, kf[c], s);
       dp = mfma32(ya, vf[c], dp);
     }
@@ -344,11 +361,11 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
   auto grads = [&](const char* st, int rb, const auto& pa, const auto& da) {
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      const char* base = st + t_lane + (32 * rb + 16 * c) * S::P;
+      const char* base = st + (32 * rb + 16 * c) * S::RB;
 #pragma unroll
       for (int db = 0; db < S::NDB; ++db) {
-        const bf16x8 yo = lds_read_tr_x2(base + S::OFF_DY + 64 * db, base + S::OFF_DY + 8 * S::P + 64 * db);
-        const bf16x8 qo = lds_read_tr_x2(base + 64 * db, base + 8 * S::P + 64 * db);
+        const bf16x8 yo = lds_read_tr_x2(base + S::OFF_DY + toff[0][db], base + S::OFF_DY + toff[1][db]);
+        const bf16x8 qo = lds_read_tr_x2(base + toff[0][db], base + toff[1][db]);
         dv[db] = mfma32(pa[c], yo, dv[db]);
         dk[db] = mfma32(da[c], qo, dk[db]);
       }
@@ -568,7 +585,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
             const bf16x8 a0 = lds_read_tr_x2(dst + krow * S::DSP + coln, dst + (krow + 8) * S::DSP + coln);
             const bf16x8 a1 = lds_read_tr_x2(dst + krow * S::DSP + coln + 64, dst + (krow + 8) * S::DSP + coln + 64);
             const int colk = (dcol + 16 * (grp & 1) + 4 * (sl & 3)) * 2;
-            const bf16x8 bo = lds_read_tr_x2(kt + krow * S::P + colk, kt + (krow + 8) * S::P + colk);
+            const bf16x8 bo = lds_read_tr_x2(kt + krow * S::KTP + colk, kt + (krow + 8) * S::KTP + colk);
             acc[0] = mfma32(a0, bo, acc[0]);
             acc[1] = mfma32(a1, bo, acc[1]);
           }
@@ -576,7 +593,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
 #pragma unroll 8
           for (int kc = 0; kc < kKvBN / 2; ++kc) {
             const int key = 2 * kc + hh;
-            const float bo = *reinterpret_cast<const float*>(kt + key * S::P + (dcol + lrow) * 4);
+            const float bo = *reinterpret_cast<const float*>(kt + key * S::KTP + (dcol + lrow) * 4);
             acc[0] = mfma32(*reinterpret_cast<const float*>(dst + key * S::DSP + lrow * 4), bo, acc[0]);
             acc[1] = mfma32(*reinterpret_cast<const float*>(dst + key * S::DSP + (32 + lrow) * 4), bo, acc[1]);
           }
@@ -653,7 +670,8 @@ template <typename T, int D>
 struct DqShape {
   static constexpr int EB = sizeof(T);
   static constexpr int RB = D * EB;
-  static constexpr int P = RB + 16;
+  static constexpr bool kSwz = EB == 2;     // bf16 tiles swizzled and unpadded
+  static constexpr int P = kSwz ? RB : RB + 16;
   static constexpr int TILE = kDqBN * P;
   static constexpr int STAGE = 2 * TILE;    // K | V
   static constexpr int NOP = D / ElemTraits<T>::kChunk;
@@ -713,10 +731,28 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
   const int64_t kv_stride = (int64_t)p.nkv * S::RB;
   const int a_lane = lrow * S::P + 16 * hh;
   const int t_lane = (4 * (grp >> 1) + (sl >> 2)) * S::P + (16 * (grp & 1) + 4 * (sl & 3)) * 2;
+  // swizzled bf16 tiles: row reads of chunk 2c + hh of row lrow (+32 per key
+  // block), transposing reads of rows rv and rv + 8 (+16 per step), chunk 4db + qv
+  int koff[S::kSwz ? S::NOP : 1], toff[2][S::kSwz ? S::NDB : 1];
+  if constexpr (S::kSwz) {
+#pragma unroll
+    for (int c = 0; c < S::NOP; ++c) koff[c] = lrow * S::RB + 16 * ((2 * c + hh) ^ tile_swz<S::RB>(lrow));
+    const int rv = 4 * (grp >> 1) + (sl >> 2), qv = 2 * (grp & 1) + ((sl & 3) >> 1), bv = 8 * (sl & 1);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int db = 0; db < S::NDB; ++db)
+        toff[hf][db] = (rv + 8 * hf) * S::RB + 16 * ((4 * db + qv) ^ tile_swz<S::RB>(rv + 8 * hf)) + bv;
+  }
 
   auto load = [&](char* st, int t) {
-    dma_rows<kDqBN, S::RB, S::P>(st, kbase, kv_stride, t * kDqBN, lkv, wave, lane);
-    dma_rows<kDqBN, S::RB, S::P>(st + S::TILE, vbase, kv_stride, t * kDqBN, lkv, wave, lane);
+    if constexpr (S::kSwz) {
+      dma_tile_swz<kDqBN, S::RB, 4>(st, kbase, kv_stride, t * kDqBN, lkv, wave, lane);
+      dma_tile_swz<kDqBN, S::RB, 4>(st + S::TILE, vbase, kv_stride, t * kDqBN, lkv, wave, lane);
+    } else {
+      dma_rows<kDqBN, S::RB, S::P>(st, kbase, kv_stride, t * kDqBN, lkv, wave, lane);
+      dma_rows<kDqBN, S::RB, S::P>(st + S::TILE, vbase, kv_stride, t * kDqBN, lkv, wave, lane);
+    }
   };
 
   auto tile = [&](int t, const char* ks) {
@@ -738,8 +774,8 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < S::NOP; ++c) {
-          const bf16x8 ka = lds_read_b128(ks + a_lane + 32 * kb * S::P + 32 * c);
-          const bf16x8 va = lds_read_b128(vs + a_lane + 32 * kb * S::P + 32 * c);
+          const bf16x8 ka = lds_read_b128(ks + koff[c] + 32 * kb * S::RB);
+          const bf16x8 va = lds_read_b128(vs + koff[c] + 32 * kb * S::RB);
           s = mfma32(ka, qf[c], s);
           dp = mfma32(va, df[c], dp);
         }
@@ -787,10 +823,10 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          const char* base = ks + t_lane + (32 * kb + 16 * c) * S::P;
+          const char* base = ks + (32 * kb + 16 * c) * S::RB;
 #pragma unroll
           for (int db = 0; db < S::NDB; ++db)
-            acc[db] = mfma32(lds_read_tr_x2(base + 64 * db, base + 8 * S::P + 64 * db), bs[c], acc[db]);
+            acc[db] = mfma32(lds_read_tr_x2(base + toff[0][db], base + toff[1][db]), bs[c], acc[db]);
         }
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
         sched_alternate<2 * S::NDB, 0x008, 0x100, 2>();
