@@ -46,11 +46,24 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(BwdParams p) {
   const int64_t npairs = rows * nq;
   const char* dyb = reinterpret_cast<const char*>(p.dy);
   const char* ob = reinterpret_cast<const char*>(p.o);
-  for (int64_t pi = grp; pi < npairs; pi += GROUPS) {
+  constexpr int U = 4;   // pairs in flight per thread
+  for (int64_t pb = grp; pb < npairs; pb += GROUPS * U) {
+    u32x4 av[U], cv[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t pi = pb + (int64_t)u * GROUPS;
+      const int64_t idx = row0 * nq + (pi < npairs ? pi : pb);
+      av[u] = *reinterpret_cast<const u32x4*>(dyb + idx * (D * EB) + sub * 16);
+      cv[u] = *reinterpret_cast<const u32x4*>(ob + idx * (D * EB) + sub * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+    const int64_t pi = pb + (int64_t)u * GROUPS;
+    if (pi >= npairs) break;
     const int64_t idx = row0 * nq + pi;            // (t * nq + h)
     const int h = (int)(pi % nq);
-    const u32x4 a = *reinterpret_cast<const u32x4*>(dyb + idx * (D * EB) + sub * 16);
-    const u32x4 c = *reinterpret_cast<const u32x4*>(ob + idx * (D * EB) + sub * 16);
+    const u32x4 a = av[u];
+    const u32x4 c = cv[u];
     float acc = 0.f;
     if constexpr (EB == 2) {
 #pragma unroll
@@ -71,6 +84,7 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(BwdParams p) {
       p.lse[idx] = l > 0.f ? m * kLog2e + __log2f(l) : __builtin_inff();
       if (p.sink && l > 0.f) part[grp * nq + h] -= fast_exp2((p.sink[h] - m) * kLog2e) / l * acc;
     }
+    }
   }
   if (p.sink) {
     __syncthreads();
@@ -82,12 +96,21 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(BwdParams p) {
   }
 }
 
+// dSink of head blockIdx.x: thread t sums partial blocks t, t + 256, ... in
+// order, then a fixed tree adds the 256 thread sums (bitwise reproducible).
 __global__ __launch_bounds__(256) void fa_dsink_reduce_kernel(const float* part, int nblocks, int nq, float* out) {
-  for (int h = blockIdx.x * 256 + threadIdx.x; h < nq; h += gridDim.x * 256) {
-    float s = 0.f;
-    for (int b = 0; b < nblocks; ++b) s += part[(int64_t)b * nq + h];
-    out[h] = s;
+  __shared__ float red[256];
+  const int h = blockIdx.x, t = threadIdx.x;
+  float s = 0.f;
+  for (int b = t; b < nblocks; b += 256) s += part[(int64_t)b * nq + h];
+  red[t] = s;
+  __syncthreads();
+#pragma unroll
+  for (int w = 128; w > 0; w >>= 1) {
+    if (t < w) red[t] += red[t + w];
+    __syncthreads();
   }
+  if (t == 0) out[h] = red[0];
 }
 
 __global__ __launch_bounds__(256) void fa_zero_kernel(float* p, int64_t n) {
@@ -985,7 +1008,7 @@ hipError_t launch_bwd_dq_convert(int dtype, int d, const BwdParams& p, hipStream
 }
 
 hipError_t launch_bwd_dsink(const BwdParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(fa_dsink_reduce_kernel, dim3(1), dim3(256), 0, s, p.dsink_part, p.n_pre_blocks, p.nq, p.dsink);
+  hipLaunchKernelGGL(fa_dsink_reduce_kernel, dim3(p.nq), dim3(256), 0, s, p.dsink_part, p.n_pre_blocks, p.nq, p.dsink);
   return hipGetLastError();
 }
 
