@@ -14,7 +14,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_kv.hip", "fa_bwd_kv_atomic.hip"]
+# sources whose MFMA results are kept in VGPRs (see common_flags)
+VGPR_FORM_SOURCES = {s for s in os.environ.get("FA_VGPR_FORM", "fa_fwd.hip,fa_bwd.hip,fa_bwd_kv_atomic.hip").split(",") if s}
 ARCH = "gfx950"
 
 
@@ -23,14 +25,16 @@ def hipcc() -> str:
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def common_flags():
-    return ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"),
-            # no packed-fp32 instructions in any generated code
-            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-            # MFMA results in VGPRs: the kernels read their accumulators with VALU
-            # code, and the default placement shuttled them through AGPRs
-            "-mllvm", "-amdgpu-mfma-vgpr-form=true",
-            "-Wno-unused-result"]
+def common_flags(src: str = ""):
+    flags = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"),
+             # no packed-fp32 instructions in any generated code
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wno-unused-result"]
+    if src in VGPR_FORM_SOURCES:
+        # MFMA results in VGPRs: these kernels read their accumulators with VALU
+        # code, and the default placement shuttled them through AGPRs
+        flags += ["-mllvm", "-amdgpu-mfma-vgpr-form=true"]
+    return flags
 
 
 def _run(cmd):
@@ -67,9 +71,9 @@ def build(verbose: bool = False, target: str = LIB, defines=()) -> str:
     for src in SOURCES:
         obj = os.path.join(build_dir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmds.append([hipcc()] + common_flags() + [f"-D{d}" for d in defines] +
+        cmds.append([hipcc()] + common_flags(src) + [f"-D{d}" for d in defines] +
                     ["-c", os.path.join(CSRC, src), "-o", obj])
-    asm_cmds = [[hipcc()] + common_flags() + [f"-D{d}" for d in defines] +
+    asm_cmds = [[hipcc()] + common_flags(src) + [f"-D{d}" for d in defines] +
                 ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o",
                  os.path.join(build_dir, src.replace(".hip", ".s"))] for src in SOURCES]
     with ThreadPoolExecutor(max_workers=2 * len(cmds)) as ex:

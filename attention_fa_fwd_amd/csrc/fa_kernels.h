@@ -97,6 +97,7 @@ constexpr int kPreRowsPerBlock = 64;
 hipError_t launch_fwd(int dtype, int d, const FwdParams& p, hipStream_t s);
 hipError_t launch_bwd_pre(int dtype, int d, const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_kv(int dtype, int d, bool atomic_dq, const BwdParams& p, hipStream_t s);
+hipError_t launch_bwd_kv_atomic(int dtype, int d, const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_dq(int dtype, int d, const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_dq_convert(int dtype, int d, const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_dsink(const BwdParams& p, hipStream_t s);
