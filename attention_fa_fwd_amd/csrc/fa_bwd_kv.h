@@ -19,9 +19,6 @@
 
 namespace fa {
 
-#ifndef FA_KV_OVERLAP
-#define FA_KV_OVERLAP 0
-#endif
 // ------------------------------------------------------------------ dK / dV (+ atomic dQ)
 template <typename T, int D>
 struct KvShape {
@@ -221,13 +218,11 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
         }
     }
   };
-  // ---- bf16 steps: software pipeline over the step's two 32-row blocks ----
-  //   [S, dP of block 0]  [S, dP of block 1 | P, dS of block 0]
-  //   [dV, dK of block 0 | P, dS of block 1]  [dV, dK of block 1]
-  // Scheduling-group barriers interleave each region's matrix work with the
-  // VALU work beside it and keep the LDS reads a few MFMAs ahead of their use.
-  // Blocks outside the mask are computed like masked ones (every probability
-  // is zero): the waves of a workgroup wait for each other at every step anyway.
+  // ---- bf16 steps: per 32-row block [S, dP MFMAs] [P, dS] [dV, dK MFMAs] ----
+  // Scheduling-group barriers keep the LDS operand reads of each MFMA group a
+  // few MFMAs ahead of their use.  Blocks outside the mask are computed like
+  // masked ones (every probability is zero): the waves of a workgroup wait for
+  // each other at every step anyway.
   auto sdp = [&](const char* st, int rb, auto& s, auto& dp) {
     s = f32x16{};
     dp = f32x16{};
@@ -296,9 +291,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
       }
     }
   };
-  constexpr int kSdpMfma = 2 * S::NOP, kSdpReads = 2 * S::NOP;
-  constexpr int kGradMfma = 4 * S::NDB, kGradReads = 8 * S::NDB;
-  constexpr int kElemValu = DROP ? 160 : (ALIBI ? 120 : 90);
+  constexpr int kSdpMfma = 2 * S::NOP, kGradMfma = 4 * S::NDB;
 
   auto compute_bf16 = [&](const char* st, auto n) {
     const int h = step_head(n), r0 = step_row0(n);
@@ -307,37 +300,6 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
     const bool full1 = fa_tile_full(win, r0 + 32, 32, wc0, 32, lq, lkv);
     f32x16 s0, dp0, s1, dp1;
     bf16x8 pa0[2], da0[2], pa1[2], da1[2];
-#if FA_KV_OVERLAP
-    __builtin_amdgcn_sched_barrier(0);
-    sdp(st, 0, s0, dp0);
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-    sched_alternate<kSdpMfma, 0x008, 0x100>();
-    __builtin_amdgcn_sched_barrier(0);
-    auto region2 = [&](auto full_c) {
-      elem(full_c, st, r0, 0, s0, dp0, slope_l2, pa0, da0);
-      if constexpr (ATOMIC) store_ds(0, da0);
-      sdp(st, 1, s1, dp1);
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-      sched_alternate3<kSdpMfma, 0x008, 1, 0x002, kElemValu / kSdpMfma, 0x100, 1>();
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    if (full0) region2(std::true_type{});
-    else region2(std::false_type{});
-    auto region3 = [&](auto full_c) {
-      elem(full_c, st, r0, 1, s1, dp1, slope_l2, pa1, da1);
-      if constexpr (ATOMIC) store_ds(1, da1);
-      grads(st, 0, pa0, da0);
-      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-      sched_alternate3<kGradMfma, 0x008, 1, 0x002, kElemValu / kGradMfma, 0x100, 2>();
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    if (full1) region3(std::true_type{});
-    else region3(std::false_type{});
-    grads(st, 1, pa1, da1);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-    sched_alternate<kGradMfma, 0x008, 0x100, 2>();
-    __builtin_amdgcn_sched_barrier(0);
-#else
     auto block = [&](int rb, bool full, auto& sx, auto& dpx, auto& pax, auto& dax) {
       __builtin_amdgcn_sched_barrier(0);
       sdp(st, rb, sx, dpx);
@@ -355,7 +317,6 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
     };
     block(0, full0, s0, dp0, pa0, da0);
     block(1, full1, s1, dp1, pa1, da1);
-#endif
     if constexpr (ATOMIC) atomic_dq(n);
   };
 

@@ -86,10 +86,8 @@ struct ElemTraits<float> {
   static constexpr int kChunk = 2;
 };
 
-// Scheduling-group patterns for __builtin_amdgcn_sched_group_barrier (instruction
-// classes: 0x002 VALU, 0x008 MFMA, 0x100 LDS read).
-//   sched_alternate<N, A, B, NB>:            N times { 1 of A, NB of B }
-//   sched_alternate3<N, A, NA, B, NB, C, NC>: N times { NA of A, NB of B, NC of C }
+// Scheduling-group pattern for __builtin_amdgcn_sched_group_barrier (instruction
+// classes: 0x002 VALU, 0x008 MFMA, 0x100 LDS read): N times { 1 of A, NB of B }.
 template <int N, int A, int B, int NB = 1>
 __device__ __forceinline__ void sched_alternate() {
   if constexpr (N > 0) {
@@ -98,16 +96,6 @@ __device__ __forceinline__ void sched_alternate() {
     sched_alternate<N - 1, A, B, NB>();
   }
 }
-template <int N, int A, int NA, int B, int NB, int C, int NC>
-__device__ __forceinline__ void sched_alternate3() {
-  if constexpr (N > 0) {
-    __builtin_amdgcn_sched_group_barrier(A, NA, 0);
-    if constexpr (NB > 0) __builtin_amdgcn_sched_group_barrier(B, NB, 0);
-    if constexpr (NC > 0) __builtin_amdgcn_sched_group_barrier(C, NC, 0);
-    sched_alternate3<N - 1, A, NA, B, NB, C, NC>();
-  }
-}
-
 // Load one 32-bit word of the packed keep mask; words that reach past the end
 // of the buffer are assembled from the bytes that exist.
 __device__ __forceinline__ uint32_t load_mask_word(const uint8_t* mask, int64_t nbytes, int64_t word) {

@@ -19,16 +19,13 @@
 // Every accumulator keeps one query row per lane (lanes l and l+32 share a row),
 // so row max / row sum need only in-lane work plus one cross-half exchange.
 //
-// Two phase-shifted wave groups (8 waves: two per SIMD).  Both groups see the
-// same K/V tiles between the same barriers, but the second group runs one step
-// behind: during key tile t the first group computes S(t), its softmax and
-// P V(t), while the second group finishes the softmax and P V of tile t-1 and
-// then computes S(t).  So on every SIMD one wave is mostly on the matrix cores
-// while the other is mostly on the VALU.  K tiles have two LDS stages, V tiles
-// three (the lagging group still reads V(t-1)); global_load_lds fills them one
-// tile ahead and each wave drains its own copies just before the barrier that
-// ends the tile.  Dropout and fp32 use one group of 4 waves (their registers
-// do not fit two waves per SIMD).
+// bf16 runs 4 waves per workgroup at two workgroups per CU, so one workgroup's
+// softmax (VALU) overlaps the other's matrix work; fp32 runs one workgroup per
+// CU.  K and V tiles have two LDS stages each; global_load_lds fills stage t+1
+// while tile t is computed, and each wave drains its own copies just before
+// the barrier that ends the tile.  Inside a tile the LDS operand reads of each
+// MFMA group are issued a few MFMAs ahead of their use (scheduling-group
+// barriers).
 //
 // Softmax bookkeeping (log2 units): the exponent offset m_run only moves when a
 // row's maximum exceeds it by more than kLazy, so most tiles skip the rescale of
@@ -46,10 +43,6 @@
 namespace fa {
 
 constexpr float kLazy = 8.0f;
-
-#ifndef FA_FWD_PIPE
-#define FA_FWD_PIPE 0
-#endif
 
 template <typename T, int D>
 struct FwdShape {
@@ -76,12 +69,9 @@ template <typename T, int D, int NW, int OCC, bool DROP, bool ALIBI>
 __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
   using S = FwdShape<T, D>;
   constexpr int BM = 32 * NW;
-  constexpr bool kLagGroup = NW == 8;       // second, phase-shifted wave group
-  constexpr int NVB = kLagGroup ? 3 : 2;    // V stages
   constexpr bool kBf16 = sizeof(T) == 2;
-  constexpr bool kPipe = FA_FWD_PIPE && !kLagGroup && kBf16;   // in-wave software pipeline
   __shared__ __attribute__((aligned(16))) char kst[2][S::KT];
-  __shared__ __attribute__((aligned(16))) char vst[NVB][S::VT];
+  __shared__ __attribute__((aligned(16))) char vst[2][S::VT];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -89,7 +79,6 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
   const int hh = lane >> 5;        // which half of the wave (k-group of MFMA operands)
   const int lrow = lane & 31;
   const int grp = lane >> 4, sl = lane & 15;
-  const bool lag = kLagGroup && wave >= 4;
 
   const int item_idx = blockIdx.x / p.nq;
   const int hl = blockIdx.x - item_idx * p.nq;
@@ -176,11 +165,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
 
   // S^T = K Q^T for the tile's two 32-key blocks.  The LDS reads of block 1 are
   // issued between the MFMAs of block 0, so only the first reads wait on LDS.
-  auto scores = [&](const char* ks, f32x16 (&s)[2], auto fence_c) {
-    constexpr bool kFence = decltype(fence_c)::value;   // own scheduling region
+  auto scores = [&](const char* ks, f32x16 (&s)[2]) {
     if constexpr (kBf16) {
       bf16x8 a0[S::NQ], a1[S::NQ];
-      if constexpr (kFence) __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int c = 0; c < S::NQ; ++c) a0[c] = lds_read_b128(ks + koff[c]);
 #pragma unroll
@@ -191,13 +179,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
       for (int c = 0; c < S::NQ; ++c) s[0] = mfma32(a0[c], qf[c], s[0]);
 #pragma unroll
       for (int c = 0; c < S::NQ; ++c) s[1] = mfma32(a1[c], qf[c], s[1]);
-      if constexpr (kFence) {
-        // all reads of block 0, then one read of block 1 after each MFMA of block 0
-        __builtin_amdgcn_sched_group_barrier(0x100, S::NQ, 0);
-        sched_alternate<S::NQ, 0x008, 0x100>();
-        __builtin_amdgcn_sched_group_barrier(0x008, S::NQ, 0);
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      // all reads of block 0, then one read of block 1 after each MFMA of block 0
+      __builtin_amdgcn_sched_group_barrier(0x100, S::NQ, 0);
+      sched_alternate<S::NQ, 0x008, 0x100>();
+      __builtin_amdgcn_sched_group_barrier(0x008, S::NQ, 0);
+      __builtin_amdgcn_sched_barrier(0);
     } else {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -214,7 +200,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
   // Online-softmax step on key tile c0..c0+63: turns the scores into
   // probabilities (the post-dropout operand of P V), updates m / l and rescales O
   // when the exponent offset moves.
-  auto softmax_core = [&](auto full_c, f32x16 (&s)[2], int c0, const RowTile& rt, bool& need) -> float {
+  auto softmax = [&](auto full_c, f32x16 (&s)[2], int c0, const RowTile& rt) {
     constexpr bool plain = !ALIBI && decltype(full_c)::value;   // logits are just sc * s
     float mt = kNegInf;
     if constexpr (plain) {
@@ -239,7 +225,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
     }
     mt = half_max(mt);
     m_true = fmaxf(m_true, mt);
-    need = mt > m_run + kLazy;   // also true on the first finite maximum
+    const bool need = mt > m_run + kLazy;   // also true on the first finite maximum
     const float alpha = need ? fast_exp2(m_run - mt) : 1.f;   // 0 when m_run = -inf
     m_run = need ? mt : m_run;
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
@@ -258,18 +244,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
         }
       }
     l_run = l_run * alpha + (lsum[0] + lsum[1]);
-    return alpha;
-  };
-  auto rescale = [&](bool need, float alpha) {
     if (__builtin_amdgcn_ballot_w64(need)) {
 #pragma unroll
       for (int db = 0; db < S::NDB; ++db) o[db] *= alpha;
     }
-  };
-  auto softmax = [&](auto full_c, f32x16 (&s)[2], int c0, const RowTile& rt) {
-    bool need;
-    const float alpha = softmax_core(full_c, s, c0, rt, need);
-    rescale(need, alpha);
   };
 
   // O^T += V^T P^T.  The transposing reads of each 16-key step are issued
@@ -333,111 +311,37 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
   };
 
   const int t_lo = it.lo, t_hi = it.hi;
-  if constexpr (kPipe) {
-    // Software pipeline inside each wave: the scores of tile t+1 are computed
-    // on the matrix cores while the VALU runs the softmax of tile t (K tiles are
-    // copied two tiles ahead, V tiles one).
-    const int n = t_hi - t_lo;
-    f32x16 sa[2], sb[2];
-    RowTile ra, rb;
-    ra.live = rb.live = false;
-    if (n > 0) {
-      load_k(kst[0], t_lo);
-      load_v(vst[0], t_lo);
-      if (n > 1) load_k(kst[1], t_lo + 1);
-      dma_wait();
-      __syncthreads();
-      ra = classify(t_lo);
-      if (ra.live) scores(kst[0], sa, std::true_type{});
-      __syncthreads();   // K(t_lo) is read by every wave before K(t_lo + 2) replaces it
-    }
-    constexpr int kSoftValu = DROP ? 200 : 150;
-    auto body = [&](auto cb_c, int j, f32x16 (&sc_)[2], f32x16 (&sn)[2], RowTile& rc, RowTile& rn) {
-      constexpr int cb = decltype(cb_c)::value, nb = cb ^ 1;
-      const int t = t_lo + j;
-      const bool has_next = j + 1 < n;
-      if (j + 2 < n) load_k(kst[cb], t + 2);
-      rn.live = false;
-      if (has_next) {
-        load_v(vst[nb], t + 1);
-        rn = classify(t + 1);
-      }
-      bool need = false;
-      float alpha = 1.f;
-      if (rn.live && rc.live && rc.full) {
-        scores(kst[nb], sn, std::false_type{});
-        alpha = softmax_core(std::true_type{}, sc_, t * kFwdBN, rc, need);
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-        sched_alternate3<2 * S::NQ, 0x008, 1, 0x002, kSoftValu / (2 * S::NQ), 0x100, 1>();
-        __builtin_amdgcn_sched_barrier(0);
-      } else {
-        if (rn.live) scores(kst[nb], sn, std::true_type{});
-        if (rc.live) {
-          if (rc.full) alpha = softmax_core(std::true_type{}, sc_, t * kFwdBN, rc, need);
-          else alpha = softmax_core(std::false_type{}, sc_, t * kFwdBN, rc, need);
-        }
-      }
-      if (rc.live) {
-        rescale(need, alpha);
-        pv(vst[cb], sc_);
-      }
-      dma_wait();
-      __syncthreads();
-    };
-    for (int j = 0; j < n; j += 2) {
-      body(std::integral_constant<int, 0>{}, j, sa, sb, ra, rb);
-      if (j + 1 < n) body(std::integral_constant<int, 1>{}, j + 1, sb, sa, rb, ra);
-    }
-  } else {
-  // stage pointers: K(t) in kc, V(t) in vc, V(t-1) in vp; kn / vn receive tile t+1
-  char* kc = kst[0];
-  char* kn = kst[1];
-  char* vp = vst[NVB - 1];
-  char* vc = vst[0];
-  char* vn = vst[1];
-  f32x16 sl_[2];          // lagging group: scores of the previous tile
-  RowTile rl;             // lagging group: flags of the previous tile
-  rl.live = false;
   if (t_lo < t_hi) {
-    load_k(kc, t_lo);
-    load_v(vc, t_lo);
+    load_k(kst[0], t_lo);
+    load_v(vst[0], t_lo);
     dma_wait();
     __syncthreads();
   }
+  // two stages: the copies of tile t+1 (into kn, vn) are in flight while tile t
+  // (kc, vc) is computed
+  char* kc = kst[0];
+  char* kn = kst[1];
+  char* vc = vst[0];
+  char* vn = vst[1];
   for (int t = t_lo; t < t_hi; ++t) {
     if (t + 1 < t_hi) {
       load_k(kn, t + 1);
       load_v(vn, t + 1);
     }
-    if (!lag) {
-      const RowTile rt = classify(t);
-      if (rt.live) {
-        f32x16 s[2];
-        scores(kc, s, std::true_type{});
-        finish(s, t, rt, vc);
-      }
-    } else {
-      if (rl.live) finish(sl_, t - 1, rl, vp);
-      rl = classify(t);
-      if (rl.live) scores(kc, sl_, std::true_type{});
+    const RowTile rt = classify(t);
+    if (rt.live) {
+      f32x16 s[2];
+      scores(kc, s);
+      finish(s, t, rt, vc);
     }
     dma_wait();
     __syncthreads();
     char* tk = kc;
     kc = kn;
     kn = tk;
-    if constexpr (NVB == 3) {
-      char* tv = vp;
-      vp = vc;
-      vc = vn;
-      vn = tv;
-    } else {
-      char* tv = vc;
-      vc = vn;
-      vn = tv;
-    }
-  }
-  if (lag && rl.live) finish(sl_, t_hi - 1, rl, vp);
+    char* tv = vc;
+    vc = vn;
+    vn = tv;
   }
 
   // ---- epilogue: O = o / (keep * l_run); l reported against the true maximum ----

@@ -76,18 +76,10 @@ struct BwdParams {
 };
 
 // Tile shapes (rows x keys) of each pass; the host scheduler uses the same numbers.
-// Forward workgroup: waves of 32 query rows each.  bf16 takes FA_FWD_WAVES waves
-// (4; 8 selects two phase-shifted groups, two waves per SIMD) without dropout
-// and 4 with it, FA_FWD_OCC workgroups per CU; fp32 takes 4 waves, one
-// workgroup per CU (its tiles fill the LDS).
-#ifndef FA_FWD_WAVES
-#define FA_FWD_WAVES 4
-#endif
-#ifndef FA_FWD_OCC
-#define FA_FWD_OCC 2
-#endif
-constexpr int fwd_waves(bool dropout, bool fp32) { return (dropout || fp32) ? 4 : FA_FWD_WAVES; }
-constexpr int fwd_occupancy(bool dropout, bool fp32) { return fp32 ? 1 : FA_FWD_OCC; }
+// Forward workgroup: 4 waves of 32 query rows each; bf16 runs two workgroups
+// per CU, fp32 one (its tiles fill the LDS).
+constexpr int fwd_waves(bool dropout, bool fp32) { return 4; }
+constexpr int fwd_occupancy(bool dropout, bool fp32) { return fp32 ? 1 : 2; }
 constexpr int fwd_rows(bool dropout, bool fp32) { return 32 * fwd_waves(dropout, fp32); }
 constexpr int kFwdBN = 64;
 constexpr int kKvBN = 128, kKvBM = 64;
