@@ -5,11 +5,13 @@
 //   dP = (dY V^T) * z / keep,  dS = P * (dP - D_i),  P = 2^(x - lse2).
 // One workgroup per (128-key tile, kv head) loops over the heads of its GQA
 // group and every query tile with an allowed pair; dK and dV accumulate in
-// registers across the whole group (no atomics).  The deterministic instances
-// (fa_bwd_kv.hip) are compiled with the compiler's own MFMA register placement,
-// which keeps the dK/dV accumulators in AGPRs and leaves the VGPRs to operands
-// and staging; the atomic-dQ instances (fa_bwd_kv_atomic.hip) keep MFMA results
-// in VGPRs, which is what fits their extra dQ stage.
+// registers across the whole group (no atomics).
+//   fa_bwd_kv_kernel       one wave per 32-key group; fp32, and the atomic-dQ
+//                          variant (fa_bwd_kv_atomic.hip, MFMA results in VGPRs)
+//   fa_bwd_kv_pair_kernel  bf16 deterministic: two waves per 32-key group that
+//                          split the rows of S / dP and the columns of dK / dV
+// The deterministic instances (fa_bwd_kv.hip) are compiled with the compiler's
+// own MFMA register placement.
 #pragma once
 #include <type_traits>
 
@@ -546,6 +548,250 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
           reinterpret_cast<float*>(p.dk)[off] = dk[db][r] * p.scale;
           reinterpret_cast<float*>(p.dv)[off] = dv[db][r];
         }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- paired waves
+// bf16 deterministic dK/dV with two waves per 32-key group (8 waves, two per
+// SIMD).  Wave w = 2*kg + half owns keys 32kg .. 32kg+31 of the tile:
+//   - it computes S, dP, P~ and dS for rows block `half` of each 64-row step,
+//   - the pair swaps those bf16 P~ / dS operands through LDS, and
+//   - it accumulates dV, dK over both row blocks for d columns
+//     [half * D/2, (half + 1) * D/2).
+// So no MFMA is done twice, and each wave holds half of the dK/dV accumulators:
+// small enough for two waves per SIMD, whose VALU and MFMA work then overlap.
+template <int D, bool DROP, bool ALIBI>
+__global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
+  using S = KvShape<__bf16, D>;
+  constexpr int NW = 8;
+  constexpr int HDB = S::NDB / 2;   // d blocks (32 wide) of this wave's dK / dV half
+  constexpr int XB = 4 * 1024;      // exchange bytes per wave: P~ and dS, two operands each
+  __shared__ __attribute__((aligned(16))) char st0[S::STAGE];
+  __shared__ __attribute__((aligned(16))) char st1[S::STAGE];
+  __shared__ __attribute__((aligned(16))) char xch[NW * XB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5, lrow = lane & 31;
+  const int grp = lane >> 4, sl = lane & 15;
+  const int kg = wave >> 1, half = wave & 1;
+
+  const int item_idx = blockIdx.x / p.nkv;
+  const int gl = blockIdx.x - item_idx * p.nkv;
+  const int g = (p.nkv % 8 == 0) ? (gl & 7) * (p.nkv >> 3) + (gl >> 3) : gl;
+  const WorkItem it = p.kv_items[item_idx];
+  const int b = it.b;
+  const int q0 = p.cu_q[b], lq = p.cu_q[b + 1] - q0;
+  const int k0 = p.cu_kv[b], lkv = p.cu_kv[b + 1] - k0;
+  const FaWindow win = fa_make_window(p.mode, p.pre, p.next, lq, lkv);
+  const int c0 = it.tile * kKvBN;          // first key of the workgroup tile
+  const int wc0 = c0 + 32 * kg;            // first key of this wave's group
+  const int j = wc0 + lrow;                // this lane's key
+  const bool key_ok = j < lkv;
+
+  // K and V rows of the group's keys as B operands (lane = key, registers = d)
+  bf16x8 kf[S::NOP], vf[S::NOP];
+  {
+    const int64_t kr = (int64_t)(k0 + (key_ok ? j : 0)) * p.nkv + g;
+    const __bf16* kp = reinterpret_cast<const __bf16*>(p.k) + kr * D;
+    const __bf16* vp = reinterpret_cast<const __bf16*>(p.v) + kr * D;
+#pragma unroll
+    for (int c = 0; c < S::NOP; ++c) {
+      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + 16 * c + 8 * hh);
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(vp + 16 * c + 8 * hh);
+      kf[c] = key_ok ? a : bf16x8{};
+      vf[c] = key_ok ? v : bf16x8{};
+    }
+  }
+  f32x16 dk[HDB], dv[HDB];
+#pragma unroll
+  for (int db = 0; db < HDB; ++db) {
+    // zeros produced by an MFMA: the accumulators start in the MFMA register class
+    dk[db] = mfma32(bf16x8{}, bf16x8{}, f32x16{});
+    dv[db] = mfma32(bf16x8{}, bf16x8{}, f32x16{});
+  }
+
+  const int nqt = it.hi - it.lo;
+  const int nsteps = p.group * nqt;
+  const int64_t q_stride = (int64_t)p.nq * S::RB;
+  // swizzled tiles: row reads of chunk 2c + hh of row lrow (+32 for block 1),
+  // transposing reads of rows rv and rv + 8 (+16 per step), chunk 4db + qv
+  // (the row-read offset of chunk 2c + hh is qrow + 16 * ((2c + hh) ^ qsw), formed per read)
+  const int qrow = lrow * S::RB, qsw = tile_swz<S::RB>(lrow) ^ hh;
+  int toff[2][HDB];
+  {
+    const int rv = 4 * (grp >> 1) + (sl >> 2), qv = 2 * (grp & 1) + ((sl & 3) >> 1), bv = 8 * (sl & 1);
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int db = 0; db < HDB; ++db)
+        toff[hf][db] = (rv + 8 * hf) * S::RB + 16 * ((4 * (half * HDB + db) + qv) ^ tile_swz<S::RB>(rv + 8 * hf)) + bv;
+  }
+  char* const xmine = xch + wave * XB + 16 * lane;             // this lane's slots in its own exchange area
+  const char* const xpair = xch + 2 * kg * XB + 16 * lane;     // and in the pair's first one
+
+  // steps walk the query tiles from the last one down, the heads of the group
+  // innermost (every key tile of a sequence starts on the same rows together)
+  auto step_head = [&](int n) { return g * p.group + n % p.group; };
+  auto step_row0 = [&](int n) { return (it.hi - 1 - n / p.group) * kKvBM; };
+
+  auto load = [&](char* st, int n) {
+    const int h = step_head(n), r0 = step_row0(n);
+    const char* qb = reinterpret_cast<const char*>(p.q) + ((int64_t)q0 * p.nq + h) * S::RB;
+    const char* dyb = reinterpret_cast<const char*>(p.dy) + ((int64_t)q0 * p.nq + h) * S::RB;
+    dma_tile_swz<kKvBM, S::RB, NW>(st, qb, q_stride, r0, lq, wave, lane);
+    dma_tile_swz<kKvBM, S::RB, NW>(st + S::OFF_DY, dyb, q_stride, r0, lq, wave, lane);
+    if (wave < 2) {
+      // lse2 (wave 0) and D_i (wave 1) of the 64 rows, one dword per lane
+      const int rr = (r0 + lane < lq) ? r0 + lane : 0;
+      dma_dword(st + (wave == 0 ? S::OFF_LSE : S::OFF_DEL), wave == 0 ? p.lse : p.delta,
+                (uint32_t)(((int64_t)(q0 + rr) * p.nq + h) * 4));
+    }
+  };
+  // keep bits of a step: 64 rows x 128 keys = 256 words, loaded by the first 256
+  // threads and stored per key group and row
+  const int bits_slot = (tid & 3) * kKvBM + ((tid >> 2) & (kKvBM - 1));
+  auto bits_word = [&](int n) -> uint32_t {
+    const int h = step_head(n), r0 = step_row0(n);
+    const int r = (tid >> 2) & (kKvBM - 1), w = tid & 3;
+    if (tid >= 4 * kKvBM || r0 + r >= lq) return 0u;
+    const int64_t pos = p.bit_base[b] + ((int64_t)h * lq + r0 + r) * lkv + c0 + 32 * w;
+    return (uint32_t)load_mask_window(p.drop, p.drop_bytes, pos);
+  };
+
+  auto compute = [&](const char* st, int n) {
+    const int h = step_head(n), r0 = step_row0(n);
+    const float slope_l2 = ALIBI ? p.slopes[h] * kLog2e : 0.f;
+    const float sc = p.scale_log2;
+    const int rb = half;                     // the row block whose P~ / dS this wave forms
+    // ---- S = Q K^T, dP~ = dY V^T for rows block rb (lane = key, registers = rows) ----
+    f32x16 s = f32x16{}, dp = f32x16{};
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int c = 0; c < S::NOP; ++c) {
+      const int qo = qrow + 16 * ((2 * c) ^ qsw) + 32 * rb * S::RB;
+      const bf16x8 qa = lds_read_b128(st + qo);
+      const bf16x8 ya = lds_read_b128(st + S::OFF_DY + qo);
+      s = mfma32(qa, kf[c], s);
+      dp = mfma32(ya, vf[c], dp);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    sched_alternate<2 * S::NOP, 0x008, 0x100>();
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- P~ and dS of the block as bf16 A operands, stored to this wave's exchange area ----
+    const float* lse_s = reinterpret_cast<const float*>(st + S::OFF_LSE);
+    const float* del_s = reinterpret_cast<const float*>(st + S::OFF_DEL);
+    const uint32_t* bits_s = reinterpret_cast<const uint32_t*>(st + S::OFF_BITS);
+    auto elem = [&](auto full_c) {
+      constexpr bool plain = !ALIBI && decltype(full_c)::value;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        bf16x8 pa, da;
+#pragma unroll
+        for (int a = 2 * c; a < 2 * c + 2; ++a) {
+          const int rq = 32 * rb + 8 * a + 4 * hh;   // rows rq .. rq+3 sit in registers 4a .. 4a+3
+          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lse_s + rq);
+          const f32x4 del4 = *reinterpret_cast<const f32x4*>(del_s + rq);
+          u32x4 bits4;
+          if constexpr (DROP) bits4 = *reinterpret_cast<const u32x4*>(bits_s + kg * kKvBM + rq);
+          const float jmi = (float)(j - r0 - rq);   // j - i of register 4a; minus e for register 4a + e
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * a + e, i = r0 + rq + e;
+            float pr;
+            if constexpr (plain) {
+              pr = fast_exp2(__builtin_fmaf(s[r], sc, -lse4[e]));
+            } else {
+              float x = s[r] * sc;
+              if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, jmi - (float)e, x);
+              if constexpr (!decltype(full_c)::value) {
+                const bool ok = (i < lq) & key_ok & (j >= fa_row_lo(win, i)) & (j <= fa_row_hi(win, i));
+                x = ok ? x : kNegInf;
+              }
+              pr = fast_exp2(x - lse4[e]);
+            }
+            float dpv = dp[r], ptv = pr;
+            if constexpr (DROP) {
+              const bool keep = (bits4[e] >> lrow) & 1u;
+              dpv = keep ? dpv * p.inv_keep : 0.f;
+              ptv = keep ? pr * p.inv_keep : 0.f;
+            }
+            const float dsv = pr * (dpv - del4[e]);
+            pa[r & 7] = to_bf16(ptv);
+            da[r & 7] = to_bf16(dsv);
+          }
+        }
+        *reinterpret_cast<bf16x8*>(xmine + 1024 * c) = pa;
+        *reinterpret_cast<bf16x8*>(xmine + 1024 * (2 + c)) = da;
+      }
+    };
+    if (fa_tile_full(win, r0 + 32 * rb, 32, wc0, 32, lq, lkv)) elem(std::true_type{});
+    else elem(std::false_type{});
+    __syncthreads();
+    // ---- dV += P~^T dY, dK += dS^T Q over both row blocks, this wave's d half ----
+    // (block blk's operands sit in the exchange area of wave 2kg + blk)
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const bf16x8 pt = *reinterpret_cast<const bf16x8*>(xpair + blk * XB + 1024 * c);
+        const bf16x8 ds = *reinterpret_cast<const bf16x8*>(xpair + blk * XB + 1024 * (2 + c));
+        const char* base = st + (32 * blk + 16 * c) * S::RB;
+#pragma unroll
+        for (int db = 0; db < HDB; ++db) {
+          const bf16x8 yo = lds_read_tr_x2(base + S::OFF_DY + toff[0][db], base + S::OFF_DY + toff[1][db]);
+          const bf16x8 qo = lds_read_tr_x2(base + toff[0][db], base + toff[1][db]);
+          dv[db] = mfma32(pt, yo, dv[db]);
+          dk[db] = mfma32(ds, qo, dk[db]);
+        }
+      }
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+    sched_alternate<8 * HDB, 0x008, 0x100, 2>();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  if (nsteps > 0) load(st0, 0);
+  uint32_t word = 0;
+  if constexpr (DROP) {
+    if (nsteps > 0) word = bits_word(0);
+    if (tid < 4 * kKvBM) reinterpret_cast<uint32_t*>(st0 + S::OFF_BITS)[bits_slot] = word;
+  }
+  dma_wait();
+  __syncthreads();
+  for (int n = 0; n < nsteps; n += 2) {
+    if (n + 1 < nsteps) {
+      load(st1, n + 1);
+      if constexpr (DROP) word = bits_word(n + 1);
+    }
+    compute(st0, n);
+    if constexpr (DROP)
+      if (n + 1 < nsteps && tid < 4 * kKvBM) reinterpret_cast<uint32_t*>(st1 + S::OFF_BITS)[bits_slot] = word;
+    dma_wait();
+    __syncthreads();
+    if (n + 1 < nsteps) {
+      if (n + 2 < nsteps) {
+        load(st0, n + 2);
+        if constexpr (DROP) word = bits_word(n + 2);
+      }
+      compute(st1, n + 1);
+      if constexpr (DROP)
+        if (n + 2 < nsteps && tid < 4 * kKvBM) reinterpret_cast<uint32_t*>(st0 + S::OFF_BITS)[bits_slot] = word;
+      dma_wait();
+      __syncthreads();
+    }
+  }
+
+  // ---- epilogue: dK *= scale; write this wave's d half of dK, dV (lane = d, registers = keys) ----
+#pragma unroll
+  for (int db = 0; db < HDB; ++db) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int jj = wc0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+      if (jj < lkv) {
+        const int64_t off = ((int64_t)(k0 + jj) * p.nkv + g) * D + 32 * (half * HDB + db) + lrow;
+        reinterpret_cast<__bf16*>(p.dk)[off] = to_bf16(dk[db][r] * p.scale);
+        reinterpret_cast<__bf16*>(p.dv)[off] = to_bf16(dv[db][r]);
       }
     }
   }

@@ -38,10 +38,9 @@ __device__ __forceinline__ f32x16 mfma32(float a, float b, const f32x16& c) {
 
 // Two transposing LDS reads -> one bf16x8 operand (see layout note above).
 __device__ __forceinline__ bf16x8 lds_read_tr_x2(const char* p0, const char* p1) {
-  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(
-      (lds_char*)(uintptr_t)p0));
-  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(
-      (lds_char*)(uintptr_t)p1));
+  // address-space casts (not integer round trips) keep constant offsets foldable into the instruction
+  s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p0);
+  s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p1);
   bf16x8 r;
   s16x4* rp = reinterpret_cast<s16x4*>(&r);
   rp[0] = lo;
