@@ -48,6 +48,7 @@ class FaConfig(ctypes.Structure):
         ("next_tokens", ctypes.c_int64),
         ("deterministic", ctypes.c_int32),
         ("flags", ctypes.c_int32),
+        ("prefix", ctypes.POINTER(ctypes.c_int64)),
     ]
 
 
@@ -97,9 +98,12 @@ class Config:
     """Owns the host cu_seqlens arrays for the lifetime of a fa_config."""
 
     def __init__(self, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, head_dim, dtype, scale, keep_prob=1.0,
-                 sparse_mode=0, pre_tokens=TOKENS_DEFAULT, next_tokens=TOKENS_DEFAULT, deterministic=True):
+                 sparse_mode=0, pre_tokens=TOKENS_DEFAULT, next_tokens=TOKENS_DEFAULT, deterministic=True,
+                 prefix=None):
         self.cu_q = np.ascontiguousarray(np.asarray(cu_seqlens_q, dtype=np.int64))
         self.cu_kv = np.ascontiguousarray(np.asarray(cu_seqlens_kv, dtype=np.int64))
+        # per-sequence prefix N of sparse mode 6 (prefixOptional); NULL when None
+        self.prefix = None if prefix is None else np.ascontiguousarray(np.asarray(prefix, dtype=np.int64))
         if isinstance(dtype, torch.dtype):
             dtype = {torch.float32: FA_DTYPE_FP32, torch.bfloat16: FA_DTYPE_BF16}.get(dtype, -1)
         self.c = FaConfig(
@@ -109,7 +113,8 @@ class Config:
             head_num=int(head_num), num_kv_heads=int(kv_heads), head_dim=int(head_dim), dtype=int(dtype),
             sparse_mode=int(sparse_mode), scale=float(scale), keep_prob=float(keep_prob),
             pre_tokens=int(pre_tokens), next_tokens=int(next_tokens), deterministic=1 if deterministic else 0,
-            flags=0)
+            flags=0,
+            prefix=(None if self.prefix is None else self.prefix.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
 
     @property
     def ref(self):

@@ -19,6 +19,7 @@ using fa::WorkItem;
 constexpr int64_t kMaxTokens = int64_t(1) << 20;   // T and S limits of the grad pages ("Constraints")
 constexpr int64_t kMaxBatch = 20000;               // B limit of the V5 grad page
 constexpr int64_t kMaxHeads = 256;                 // Nq limit ("Nq ranges from 1 to 256")
+constexpr int64_t kMaxPrefixBatch = 1024;          // B limit with prefixOptional (grad page "Constraints")
 
 struct Problem {
   int64_t batch = 0, nq = 0, nkv = 0, d = 0, tq = 0, tkv = 0;
@@ -28,6 +29,7 @@ struct Problem {
   bool deterministic = true;
   std::vector<int32_t> cu_q, cu_kv;
   std::vector<int64_t> bit_base;   // first keep bit of each sequence
+  std::vector<int32_t> prefix;     // prefix N of each sequence (sparse mode 6; zeros otherwise)
   int64_t drop_bits = 0;
 };
 
@@ -43,8 +45,10 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   if (cfg->dtype != FA_DTYPE_FP32 && cfg->dtype != FA_DTYPE_BF16) return FA_ERR_PARAM_INVALID;
   const int mode = cfg->sparse_mode;
   if (mode != FA_SPARSE_NONE && mode != FA_SPARSE_LEFT_UP_CAUSAL && mode != FA_SPARSE_RIGHT_DOWN_CAUSAL &&
-      mode != FA_SPARSE_BAND)
+      mode != FA_SPARSE_BAND && mode != FA_SPARSE_PREFIX)
     return FA_ERR_PARAM_INVALID;
+  if (mode == FA_SPARSE_PREFIX && !cfg->prefix) return FA_ERR_PARAM_NULLPTR;
+  if (mode == FA_SPARSE_PREFIX && cfg->batch > kMaxPrefixBatch) return FA_ERR_PARAM_INVALID;
   if (!(cfg->keep_prob > 0.0 && cfg->keep_prob <= 1.0)) return FA_ERR_PARAM_INVALID;
   if (!std::isfinite(cfg->scale)) return FA_ERR_PARAM_INVALID;
   if (mode == FA_SPARSE_BAND && cfg->pre_tokens + cfg->next_tokens < 0) return FA_ERR_PARAM_INVALID;
@@ -83,6 +87,16 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
       bits += pr->nq * (cq[b + 1] - cq[b]) * (ck[b + 1] - ck[b]);
     }
   }
+  pr->prefix.assign(pr->batch, 0);
+  if (mode == FA_SPARSE_PREFIX) {
+    for (int64_t b = 0; b < pr->batch; ++b) {
+      // prefix N range of the pages: [0, Lkv] when Lq > Lkv, else [Lkv - Lq, Lkv]
+      const int64_t lq = cq[b + 1] - cq[b], lkv = ck[b + 1] - ck[b], n = cfg->prefix[b];
+      const int64_t lo = lq > lkv ? 0 : lkv - lq;
+      if (n < lo || n > lkv) return FA_ERR_PARAM_INVALID;
+      pr->prefix[b] = (int32_t)n;
+    }
+  }
   pr->tq = cq[pr->batch];
   pr->tkv = ck[pr->batch];
   if (pr->tq < 1 || pr->tkv < 1) return FA_ERR_PARAM_INVALID;
@@ -101,7 +115,7 @@ fa_status check_alibi(const Problem& pr) {
 
 FaWindow window_of(const Problem& pr, int64_t b) {
   const int32_t lq = pr.cu_q[b + 1] - pr.cu_q[b], lkv = pr.cu_kv[b + 1] - pr.cu_kv[b];
-  return fa_make_window(pr.mode, pr.pre, pr.next, lq, lkv);
+  return fa_make_window(pr.mode, pr.pre, pr.next, lq, lkv, pr.prefix[b]);
 }
 
 // Work list of one pass.  The items of one sequence are consecutive, so the
@@ -150,7 +164,7 @@ constexpr uint64_t kAlign = 256;
 uint64_t align_up(uint64_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 
 struct Layout {
-  uint64_t cu_q = 0, cu_kv = 0, bit_base = 0, items0 = 0, items1 = 0;   // host-staged block
+  uint64_t cu_q = 0, cu_kv = 0, bit_base = 0, prefix = 0, items0 = 0, items1 = 0;   // host-staged block
   uint64_t staged_bytes = 0;
   uint64_t delta = 0, lse = 0, dsink_part = 0, dq_acc = 0;
   uint64_t total = 0;
@@ -164,6 +178,7 @@ Layout layout_fwd(const Problem& pr, int64_t n_items) {
   L.cu_q = off; off = align_up(off + 4 * (pr.batch + 1));
   L.cu_kv = off; off = align_up(off + 4 * (pr.batch + 1));
   L.bit_base = off; off = align_up(off + 8 * pr.batch);
+  L.prefix = off; off = align_up(off + 4 * pr.batch);
   L.items0 = off; off = align_up(off + sizeof(WorkItem) * n_items);
   L.staged_bytes = off;
   L.n_items0 = n_items;
@@ -180,6 +195,7 @@ Layout layout_bwd(const Problem& pr, int64_t n_kv_items, int64_t n_dq_items) {
   L.cu_q = off; off = align_up(off + 4 * (pr.batch + 1));
   L.cu_kv = off; off = align_up(off + 4 * (pr.batch + 1));
   L.bit_base = off; off = align_up(off + 8 * pr.batch);
+  L.prefix = off; off = align_up(off + 4 * pr.batch);
   L.items0 = off; off = align_up(off + sizeof(WorkItem) * n_kv_items);
   L.items1 = off; off = align_up(off + sizeof(WorkItem) * n_dq_items);
   L.staged_bytes = off;
@@ -261,6 +277,7 @@ std::vector<char> stage_block(const Problem& pr, const Layout& L, const std::vec
   std::memcpy(host.data() + L.cu_q, pr.cu_q.data(), 4 * pr.cu_q.size());
   std::memcpy(host.data() + L.cu_kv, pr.cu_kv.data(), 4 * pr.cu_kv.size());
   std::memcpy(host.data() + L.bit_base, pr.bit_base.data(), 8 * pr.bit_base.size());
+  std::memcpy(host.data() + L.prefix, pr.prefix.data(), 4 * pr.prefix.size());
   std::memcpy(host.data() + L.items0, i0.data(), sizeof(WorkItem) * i0.size());
   if (i1) std::memcpy(host.data() + L.items1, i1->data(), sizeof(WorkItem) * i1->size());
   return host;
@@ -334,6 +351,7 @@ fa_status fa_fwd(const fa_config* cfg, const void* q, const void* k, const void*
   p.cu_q = reinterpret_cast<const int32_t*>(ws + L.cu_q);
   p.cu_kv = reinterpret_cast<const int32_t*>(ws + L.cu_kv);
   p.bit_base = reinterpret_cast<const int64_t*>(ws + L.bit_base);
+  p.prefix = reinterpret_cast<const int32_t*>(ws + L.prefix);
   p.items = reinterpret_cast<const WorkItem*>(ws + L.items0);
   p.n_items = (int32_t)items.size();
   return hip_status(timed(K_FWD, s, [&] { return fa::launch_fwd(pr.dtype, (int)pr.d, p, s); }));
@@ -386,6 +404,7 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
   p.cu_q = reinterpret_cast<const int32_t*>(ws + L.cu_q);
   p.cu_kv = reinterpret_cast<const int32_t*>(ws + L.cu_kv);
   p.bit_base = reinterpret_cast<const int64_t*>(ws + L.bit_base);
+  p.prefix = reinterpret_cast<const int32_t*>(ws + L.prefix);
   p.kv_items = reinterpret_cast<const WorkItem*>(ws + L.items0);
   p.dq_items = reinterpret_cast<const WorkItem*>(ws + L.items1);
   p.n_kv_items = (int32_t)kv_items.size();

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
   const int b = it.b;
   const int q0 = p.cu_q[b], lq = p.cu_q[b + 1] - q0;
   const int k0 = p.cu_kv[b], lkv = p.cu_kv[b + 1] - k0;
-  const FaWindow win = fa_make_window(p.mode, p.pre, p.next, lq, lkv);
+  const FaWindow win = fa_make_window(p.mode, p.pre, p.next, lq, lkv, p.prefix[b]);
   const int c0 = it.tile * kKvBN;          // first key of the workgroup tile
   const int wc0 = c0 + 32 * wave;          // first key of this wave
   const int j = wc0 + lrow;                // this lane's key
@@ -583,7 +583,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
   const int b = it.b;
   const int q0 = p.cu_q[b], lq = p.cu_q[b + 1] - q0;
   const int k0 = p.cu_kv[b], lkv = p.cu_kv[b + 1] - k0;
-  const FaWindow win = fa_make_window(p.mode, p.pre, p.next, lq, lkv);
+  const FaWindow win = fa_make_window(p.mode, p.pre, p.next, lq, lkv, p.prefix[b]);
   const int c0 = it.tile * kKvBN;          // first key of the workgroup tile
   const int wc0 = c0 + 32 * kg;            // first key of this wave's group
   const int j = wc0 + lrow;                // this lane's key

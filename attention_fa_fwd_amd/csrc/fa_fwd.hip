@@ -89,7 +89,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
   const int b = it.b;
   const int q0 = p.cu_q[b], lq = p.cu_q[b + 1] - q0;
   const int k0 = p.cu_kv[b], lkv = p.cu_kv[b + 1] - k0;
-  const FaWindow win = fa_make_window(p.mode, p.pre, p.next, lq, lkv);
+  const FaWindow win = fa_make_window(p.mode, p.pre, p.next, lq, lkv, p.prefix[b]);
 
   const int wr0 = it.tile * BM + wave * 32;       // first row of this wave (in sequence)
   const int i = wr0 + lrow;                        // this lane's row

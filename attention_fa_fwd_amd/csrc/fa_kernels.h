@@ -27,6 +27,7 @@ struct FwdParams {
   const int32_t* cu_q;
   const int32_t* cu_kv;
   const int64_t* bit_base;
+  const int32_t* prefix;    // per sequence: prefix N of sparse mode 6 (0 otherwise)
   const WorkItem* items;
   int32_t n_items;
   int32_t nq, nkv, group;
@@ -60,6 +61,7 @@ struct BwdParams {
   const int32_t* cu_q;
   const int32_t* cu_kv;
   const int64_t* bit_base;
+  const int32_t* prefix;    // per sequence: prefix N of sparse mode 6 (0 otherwise)
   const int32_t* row_seq;   // sequence index of each query token (preprocess)
   const WorkItem* kv_items;
   const WorkItem* dq_items;

@@ -10,11 +10,15 @@
 //   mode 2 (leftUpCausal)     : pre = FA_WINDOW_INF, next = 0, delta = 0
 //   mode 3 (rightDownCausal)  : pre = FA_WINDOW_INF, next = 0, delta = Lkv - Lq
 //   mode 4 (band)             : pre, next as given,        delta = Lkv - Lq
-// Both interval ends grow by exactly one per row and pre + next >= 0, so the
-// allowed set of a rectangular tile is empty iff hi(last row) < first key or
-// lo(first row) > last key, and full iff lo(last row) <= first key and
-// last key <= hi(first row).  Windows are clamped to +-2^30, which leaves
-// every allowed set unchanged because sequences are at most 2^20 long.
+//   mode 6 (prefix N)         : as mode 3, and hi(i) >= N - 1 ("floor"): the
+//                               sequence's first N keys are visible to every row
+// Both interval ends are non-decreasing in the row and every non-empty row
+// interval meets its neighbours' (they grow by one per row; the prefix floor
+// only raises hi where lo is unbounded), so the allowed set of a rectangular
+// tile is empty iff hi(last row) < first key or lo(first row) > last key, and
+// full iff lo(last row) <= first key and last key <= hi(first row).  Windows
+// are clamped to +-2^30, which leaves every allowed set unchanged because
+// sequences are at most 2^20 long.
 #pragma once
 #include <stdint.h>
 
@@ -30,18 +34,30 @@ struct FaWindow {
   int32_t delta;  // diagonal offset (Lkv - Lq for bottom-right aligned modes)
   int32_t pre;    // keys allowed to the left of the diagonal
   int32_t next;   // keys allowed to the right of the diagonal
+  int32_t floor;  // every row may also see keys [0, floor] (prefix mode: N - 1; else -1)
 };
 
 FA_HD int64_t fa_clamp_window(int64_t w) {
   return w > FA_WINDOW_INF ? FA_WINDOW_INF : (w < -FA_WINDOW_INF ? -FA_WINDOW_INF : w);
 }
 
-FA_HD FaWindow fa_make_window(int mode, int64_t pre, int64_t next, int32_t lq, int32_t lkv) {
+// Allowed keys of query row i (local indices) form one interval [lo(i), hi(i)],
+// both ends non-decreasing in i:
+//   mode 0: all keys; mode 2: j <= i; mode 3: j <= i + (Lkv - Lq);
+//   mode 4: i + (Lkv - Lq) - pre <= j <= i + (Lkv - Lq) + next;
+//   mode 6 (prefix N of the sequence): j <= max(i + (Lkv - Lq), N - 1), i.e. the
+//   bottom-right causal triangle plus the first N keys for every row.
+FA_HD FaWindow fa_make_window(int mode, int64_t pre, int64_t next, int32_t lq, int32_t lkv, int32_t prefix = 0) {
   FaWindow w;
   w.delta = 0;
   w.pre = FA_WINDOW_INF;
   w.next = FA_WINDOW_INF;
-  if (mode == 2) {
+  w.floor = -1;
+  if (mode == 6) {
+    w.next = 0;
+    w.delta = lkv - lq;
+    w.floor = prefix - 1;
+  } else if (mode == 2) {
     w.next = 0;
   } else if (mode == 3) {
     w.next = 0;
@@ -55,7 +71,10 @@ FA_HD FaWindow fa_make_window(int mode, int64_t pre, int64_t next, int32_t lq, i
 }
 
 FA_HD int32_t fa_row_lo(const FaWindow& w, int32_t i) { return i + w.delta - w.pre; }
-FA_HD int32_t fa_row_hi(const FaWindow& w, int32_t i) { return i + w.delta + w.next; }
+FA_HD int32_t fa_row_hi(const FaWindow& w, int32_t i) {
+  const int32_t h = i + w.delta + w.next;
+  return h > w.floor ? h : w.floor;
+}
 
 FA_HD bool fa_allowed(const FaWindow& w, int32_t i, int32_t j, int32_t lq, int32_t lkv) {
   return i < lq && j < lkv && j >= fa_row_lo(w, i) && j <= fa_row_hi(w, i);
@@ -99,8 +118,8 @@ FA_HD void fa_kv_tile_range(const FaWindow& w, int32_t r0, int32_t r1, int32_t l
 FA_HD void fa_q_tile_range(const FaWindow& w, int32_t c0, int32_t c1, int32_t lq, int32_t bm,
                            int32_t* t_lo, int32_t* t_hi) {
   int32_t ntiles = (lq + bm - 1) / bm;
-  // rows i with hi(i) >= c0 and lo(i) <= c1 - 1
-  int32_t ilo = c0 - w.delta - w.next;
+  // rows i with hi(i) >= c0 and lo(i) <= c1 - 1 (every row reaches c0 when the floor does)
+  int32_t ilo = w.floor >= c0 ? 0 : c0 - w.delta - w.next;
   int32_t ihi = c1 - 1 - w.delta + w.pre;
   if (ilo < 0) ilo = 0;
   if (ihi > lq - 1) ihi = lq - 1;

@@ -60,6 +60,7 @@ typedef int32_t fa_status;
 #define FA_SPARSE_LEFT_UP_CAUSAL 2   /* j <= i                                               */
 #define FA_SPARSE_RIGHT_DOWN_CAUSAL 3 /* j <= i + (Lkv - Lq)                                  */
 #define FA_SPARSE_BAND 4             /* i+(Lkv-Lq)-pre <= j <= i+(Lkv-Lq)+next (inclusive)    */
+#define FA_SPARSE_PREFIX 6           /* j <= i + (Lkv - Lq)  or  j < N_b (prefix, see below)  */
 
 #define FA_TOKENS_DEFAULT 2147483647 /* preTokens / nextTokens default of the pages */
 
@@ -81,6 +82,15 @@ typedef struct fa_config {
                                     with D = 128, and bf16 with D = 128 and alibi, always
                                     take the deterministic passes)                            */
   int32_t flags;                 /* reserved, must be 0                                       */
+  const int64_t* prefix;         /* HOST, B entries, read in FA_SPARSE_PREFIX only (ignored
+                                    otherwise): N_b of the prefix-compressed mask
+                                    (aclnnFlashAttentionUnpaddingScoreGrad "prefixOptional";
+                                    sparseMode 6).  Row i of sequence b keeps keys
+                                    j <= i + (Lkv_b - Lq_b) and every key j < N_b.  Range
+                                    ("Constraints"): N_b in [0, Lkv_b] when Lq_b > Lkv_b,
+                                    else [Lkv_b - Lq_b, Lkv_b]; B <= 1024 with a prefix.
+                                    NULL in mode 6 -> FA_ERR_PARAM_NULLPTR; out of range
+                                    -> FA_ERR_PARAM_INVALID.                                 */
 } fa_config;
 
 /* Device workspace bytes needed by fa_fwd for this configuration (>= 256). */

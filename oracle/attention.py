@@ -14,7 +14,8 @@ What it computes follows the Ascend CANN pages:
     includes the sink logit, the softmax denominator gains exp(sink - m), and
     dSink is a reduction of -P*dP*SimpleSoftmax(sink, max, sum).
   * aclnnFlashAttentionUnpaddingScoreGrad, sparseMode list: 0 no mask,
-    2 leftUpCausal, 3 rightDownCausal, 4 band between preTokens/nextTokens.
+    2 leftUpCausal, 3 rightDownCausal, 4 band between preTokens/nextTokens,
+    6 prefix (with prefixOptional, one N per sequence).
 
 Readings taken where the pages are silent (each is listed with its reason in
 the design notes):
@@ -32,6 +33,10 @@ the design notes):
   * Rows with no allowed key and no sink: O = 0, m = -inf, l = 0, dQ = 0.
   * Band (mode 4) and rightDownCausal (mode 3) align on the bottom-right
     corner (delta = Lkv - Lq); leftUpCausal (mode 2) on the top-left.
+  * Prefix (mode 6): the compressed mask the page describes is a lower
+    triangle over a block whose left half is kept; read as: row i keeps
+    j <= i + delta (the rightDownCausal triangle) and every key j < N of its
+    sequence.
   * softmax max/sum are per (row, head) fp32 in natural-log units; the
     page's trailing x8 replication is dropped.
 
@@ -45,8 +50,9 @@ INT_MAX_TOKENS = 2147483647
 
 
 def allowed(lq: int, lkv: int, sparse_mode: int, pre_tokens: int = INT_MAX_TOKENS,
-            next_tokens: int = INT_MAX_TOKENS) -> np.ndarray:
-    """Boolean [lq, lkv]: True where query row i may attend key j (sparseMode list)."""
+            next_tokens: int = INT_MAX_TOKENS, prefix: int = 0) -> np.ndarray:
+    """Boolean [lq, lkv]: True where query row i may attend key j (sparseMode list;
+    `prefix` is the sequence's N for mode 6)."""
     i = np.arange(lq, dtype=np.int64)[:, None]
     j = np.arange(lkv, dtype=np.int64)[None, :]
     delta = lkv - lq
@@ -58,6 +64,8 @@ def allowed(lq: int, lkv: int, sparse_mode: int, pre_tokens: int = INT_MAX_TOKEN
         return j <= i + delta
     if sparse_mode == 4:            # band: preTokens to the left, nextTokens to the right
         return (j >= i + delta - pre_tokens) & (j <= i + delta + next_tokens)
+    if sparse_mode == 6:            # prefix: rightDownCausal plus the first N keys for every row
+        return (j <= i + delta) | (j < prefix)
     raise ValueError(f"sparse_mode {sparse_mode} not covered")
 
 
@@ -80,7 +88,7 @@ class _Problem:
     """Inputs of one call, upcast to fp64, with the per-sequence bookkeeping."""
 
     def __init__(self, q, k, v, cu_q, cu_kv, head_num, kv_heads, scale, keep_prob, sparse_mode,
-                 pre_tokens, next_tokens, drop_mask, alibi_slopes, sink):
+                 pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix=None):
         # kept in their given precision; each (sequence, head) slice is upcast to fp64 when used
         self.q = np.asarray(q)
         self.k = np.asarray(k)
@@ -101,6 +109,7 @@ class _Problem:
         self.slopes = None if alibi_slopes is None else np.asarray(alibi_slopes, dtype=np.float32).astype(np.float64)
         self.sink = None if sink is None else np.asarray(sink, dtype=np.float32).astype(np.float64)
         self.batch = len(self.cu_q) - 1
+        self.prefix = np.zeros(self.batch, dtype=np.int64) if prefix is None else np.asarray(prefix, dtype=np.int64)
         self.lens_q = np.diff(self.cu_q)
         self.lens_kv = np.diff(self.cu_kv)
         # start bit of each sequence's block in the packed keep mask
@@ -117,7 +126,7 @@ class _Problem:
         s = self.scale * (qb @ kb.T)
         if self.slopes is not None:
             s = s + alibi_pse(lq, lkv, self.slopes[h])
-        ok = allowed(lq, lkv, self.mode, self.pre, self.next)
+        ok = allowed(lq, lkv, self.mode, self.pre, self.next, int(self.prefix[b]))
         s = np.where(ok, s, -np.inf)
         m = s.max(axis=1) if lkv > 0 else np.full(lq, -np.inf)
         if self.sink is not None:
@@ -145,9 +154,9 @@ class _Problem:
 
 def _problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob=1.0,
              sparse_mode=0, pre_tokens=INT_MAX_TOKENS, next_tokens=INT_MAX_TOKENS, drop_mask=None,
-             alibi_slopes=None, sink=None):
+             alibi_slopes=None, sink=None, prefix=None):
     return _Problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob,
-                    sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink)
+                    sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix)
 
 
 def _selected(subset, n):
@@ -156,12 +165,12 @@ def _selected(subset, n):
 
 def forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob=1.0,
             sparse_mode=0, pre_tokens=INT_MAX_TOKENS, next_tokens=INT_MAX_TOKENS, drop_mask=None,
-            alibi_slopes=None, sink=None, batches=None, heads=None):
+            alibi_slopes=None, sink=None, batches=None, heads=None, prefix=None):
     """Attention forward.  Returns O [T_q, Nq, D], softmax max m [T_q, Nq] and
     softmax sum l [T_q, Nq] (fp64).  With `batches` / `heads`, only those
     sequences / query heads are computed and every other entry is NaN."""
     pr = _problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob,
-                  sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink)
+                  sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix)
     tq, d = pr.q.shape[0], pr.v.shape[2]
     out = np.full((tq, pr.nq, d), np.nan)
     mx = np.full((tq, pr.nq), np.nan)
@@ -177,14 +186,14 @@ def forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, kee
 
 def backward(q, k, v, dy, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob=1.0,
              sparse_mode=0, pre_tokens=INT_MAX_TOKENS, next_tokens=INT_MAX_TOKENS, drop_mask=None,
-             alibi_slopes=None, sink=None, batches=None, heads=None):
+             alibi_slopes=None, sink=None, batches=None, heads=None, prefix=None):
     """Attention backward.  Returns dQ [T_q, Nq, D], dK, dV [T_kv, Nkv, D] and
     dSink [Nq] (None without a sink).  With `batches` / `heads`, only those
     sequences / query heads contribute: rows and keys of other sequences are NaN,
     dK/dV of a kv head are complete only if all of its query heads are chosen,
     and dSink sums the chosen sequences."""
     pr = _problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob,
-                  sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink)
+                  sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix)
     dy = np.asarray(dy)
     dq = np.full(pr.q.shape, np.nan)
     dk = np.full(pr.k.shape, np.nan)

@@ -69,7 +69,8 @@ INVALID_CONFIGS = {
     "keep_above_one": dict(keep_prob=1.5),
     "mode_1": dict(sparse_mode=1),
     "mode_5": dict(sparse_mode=5),
-    "mode_6": dict(sparse_mode=6),
+    "mode_7": dict(sparse_mode=7),
+    "mode_8": dict(sparse_mode=8),
     "band_without_intersection": dict(sparse_mode=4, pre_tokens=-3, next_tokens=2),
     "cu_not_monotone": dict(cu_seqlens_q=[0, 7, 5], cu_seqlens_kv=[0, 7, 5]),
     "cu_not_starting_at_zero": dict(cu_seqlens_q=[1, 5, 12]),
@@ -118,6 +119,30 @@ def test_null_pointers():
     assert fa.lib().fa_fwd_workspace_size(_cfg().ref, ctypes.byref(n)) == fa.FA_OK and n.value > 0
 
 
+def test_prefix_mode_validation():
+    # sparse mode 6 needs prefixOptional, one N per sequence
+    assert _fwd(_cfg(sparse_mode=6)) == fa.FA_ERR_PARAM_NULLPTR
+    assert _bwd(_cfg(sparse_mode=6)) == fa.FA_ERR_PARAM_NULLPTR
+    n = ctypes.c_uint64(0)
+
+    def size(cfg):
+        return fa.lib().fa_fwd_workspace_size(cfg.ref, ctypes.byref(n))
+
+    # N range ("Constraints"): [Lkv - Lq, Lkv] when Lq <= Lkv, [0, Lkv] when Lq > Lkv
+    cq, ck = [0, 5, 12], [0, 8, 12]        # (Lq, Lkv) = (5, 8) and (7, 4)
+    for good in ([3, 0], [8, 4], [5, 2]):
+        assert size(_cfg(sparse_mode=6, cu_seqlens_q=cq, cu_seqlens_kv=ck, prefix=good)) == fa.FA_OK, good
+    for bad in ([2, 0], [9, 0], [3, 5], [3, -1]):
+        cfg = _cfg(sparse_mode=6, cu_seqlens_q=cq, cu_seqlens_kv=ck, prefix=bad)
+        assert size(cfg) == fa.FA_ERR_PARAM_INVALID, bad
+        assert _fwd(cfg) == fa.FA_ERR_PARAM_INVALID and _bwd(cfg) == fa.FA_ERR_PARAM_INVALID
+    # at most 1024 sequences with a prefix; the prefix is ignored by the other modes
+    cu = np.arange(1026, dtype=np.int64)
+    assert size(_cfg(sparse_mode=6, cu_seqlens_q=cu[:1025], cu_seqlens_kv=cu[:1025], prefix=np.ones(1024))) == fa.FA_OK
+    assert size(_cfg(sparse_mode=6, cu_seqlens_q=cu, cu_seqlens_kv=cu, prefix=np.ones(1025))) == fa.FA_ERR_PARAM_INVALID
+    assert size(_cfg(sparse_mode=3, prefix=[100, 100])) == fa.FA_OK
+
+
 def test_alignment_alibi_and_workspace_rules():
     odd = ctypes.c_void_p(0x10008)
     assert _fwd(_cfg(), q=odd) == fa.FA_ERR_PARAM_INVALID
@@ -138,8 +163,8 @@ def test_atomic_variant_needs_a_larger_workspace():
 
 # --------------------------------------------------------------------------- scheduler
 
-def _brute_ranges(lq, lkv, mode, pre, nxt, bm, bn, by_kv):
-    ok = oracle.allowed(lq, lkv, mode, pre, nxt)
+def _brute_ranges(lq, lkv, mode, pre, nxt, bm, bn, by_kv, prefix=0):
+    ok = oracle.allowed(lq, lkv, mode, pre, nxt, prefix)
     res = []
     if by_kv:
         for t in range((lkv + bn - 1) // bn):
@@ -163,15 +188,21 @@ SCHED_CASES = [
     ([1000, 257], [700, 300], 4, 100, 0),
     ([333, 64], [129, 500], 0, 0, 0),
     ([2048, 2048], None, 4, 2048, 0),
+    # prefix (mode 6) with the N of each sequence last
+    ([300, 77, 129, 1000, 5], [500, 10, 129, 1000, 64], 6, 0, 0, [200, 0, 64, 0, 60]),
+    ([513, 600, 64], [513, 600, 2000], 6, 0, 0, [513, 300, 1999]),
+    ([700, 129], [129, 700], 6, 0, 0, [129, 650]),
 ]
 
 
-@pytest.mark.parametrize("lq,lkv,mode,pre,nxt", SCHED_CASES)
+@pytest.mark.parametrize("case", SCHED_CASES)
 @pytest.mark.parametrize("pass_id", [0, 1, 2])
-def test_schedule_matches_brute_force(lq, lkv, mode, pre, nxt, pass_id):
+def test_schedule_matches_brute_force(case, pass_id):
+    lq, lkv, mode, pre, nxt = case[:5]
+    prefix = case[5] if len(case) > 5 else [0] * len(lq)
     lkv = lq if lkv is None else lkv
     cfg = _cfg(cu_seqlens_q=wl.cu_from_lengths(lq), cu_seqlens_kv=wl.cu_from_lengths(lkv), sparse_mode=mode,
-               pre_tokens=pre, next_tokens=nxt)
+               pre_tokens=pre, next_tokens=nxt, prefix=prefix if mode == 6 else None)
     items, (bm, bn) = fa.fa_debug_schedule(cfg, pass_id)
     costs = items[:, 3] - items[:, 2]
     # items of one sequence are consecutive; sequences heaviest first, and
@@ -188,7 +219,8 @@ def test_schedule_matches_brute_force(lq, lkv, mode, pre, nxt, pass_id):
         seen[(b, tile)] = (lo, hi)
     expect_keys = set()
     for b in range(len(lq)):
-        for t, tiles in _brute_ranges(lq[b], lkv[b], mode, pre, nxt, bm, bn, by_kv=(pass_id == 1)):
+        for t, tiles in _brute_ranges(lq[b], lkv[b], mode, pre, nxt, bm, bn, by_kv=(pass_id == 1),
+                                      prefix=prefix[b]):
             expect_keys.add((b, t))
             lo, hi = seen[(b, t)]
             got = list(range(lo, hi))

@@ -32,6 +32,13 @@ EDGE_CASES = {
     "single_tokens": dict(lens_q=[1, 1, 2], head_num=2, kv_heads=1, head_dim=128, sparse_mode=3, sink=True),
     "sink_dropout_band": dict(lens_q=[190, 67], head_num=2, kv_heads=1, head_dim=64, sparse_mode=4,
                               pre_tokens=50, next_tokens=3, keep_prob=0.7, sink=True),
+    # prefix (mode 6): N in [Lkv - Lq, Lkv] (Lq <= Lkv) or [0, Lkv] (Lq > Lkv)
+    "prefix_varlen": dict(lens_q=[200, 77, 129, 5], lens_kv=[300, 40, 129, 64], head_num=4, kv_heads=2,
+                          head_dim=128, sparse_mode=6, prefix=[150, 17, 64, 60]),
+    "prefix_edges_sink_dropout": dict(lens_q=[190, 67, 300], head_num=2, kv_heads=1, head_dim=64, sparse_mode=6,
+                                      prefix=[0, 67, 299], keep_prob=0.8, sink=True),
+    "prefix_alibi": dict(lens_q=[150, 300], head_num=4, kv_heads=1, head_dim=128, sparse_mode=6,
+                         prefix=[30, 129], alibi=True),
 }
 
 

@@ -158,6 +158,20 @@ def test_sdpa_right_down_causal_rectangular():
     np.testing.assert_allclose(o, ref.numpy(), rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("lq,lkv,n", [(9, 14, 8), (14, 9, 3), (11, 11, 0), (11, 11, 11)])
+def test_sdpa_prefix_mask(lq, lkv, n):
+    # prefix (mode 6): the bottom-right causal triangle, plus a block of the first N
+    # keys kept for every row (the left part of the page's compressed mask)
+    d = 8
+    q, k, v = _rand(40 + n, lq, 2, d), _rand(41 + n, lkv, 2, d), _rand(42 + n, lkv, 2, d)
+    o, _, _ = oracle.forward(q, k, v, [0, lq], [0, lkv], 2, 2, 0.35, sparse_mode=6, prefix=[n])
+    keep = torch.ones(lq, lkv, dtype=torch.bool).tril(lkv - lq)
+    keep[:, :n] = True
+    ref = _sdpa(q, k, v, 0.35, attn_mask=keep)
+    rows = keep.any(dim=1).numpy()          # SDPA leaves rows without keys undefined
+    np.testing.assert_allclose(o[rows], ref[rows], rtol=1e-12, atol=1e-13)
+
+
 def test_sdpa_gqa_and_band_mask():
     lq, d = 23, 8
     q, k, v = _rand(18, lq, 6, d), _rand(19, lq, 2, d), _rand(20, lq, 2, d)
@@ -233,6 +247,19 @@ def test_mode_equivalences():
         base, rtol=1e-15, atol=0)
     np.testing.assert_array_equal(
         oracle.forward(q, k, v, cu, cu, 2, 2, 0.5, sparse_mode=3, alibi_slopes=np.zeros(2, np.float32))[0], base)
+    # prefix N = Lkv - Lq == rightDownCausal; N = Lkv == no mask (rectangular sequences)
+    lq2, lkv2 = 9, 17
+    q2, k2, v2, dy2 = _rand(35, lq2, 2, d), _rand(36, lkv2, 2, d), _rand(37, lkv2, 2, d), _rand(38, lq2, 2, d)
+    cq2, ck2 = [0, lq2], [0, lkv2]
+    for n, mode in ((lkv2 - lq2, 3), (lkv2, 0)):
+        a = oracle.forward(q2, k2, v2, cq2, ck2, 2, 2, 0.5, sparse_mode=6, prefix=[n])
+        b = oracle.forward(q2, k2, v2, cq2, ck2, 2, 2, 0.5, sparse_mode=mode)
+        for x, y in zip(a, b):
+            np.testing.assert_array_equal(x, y)
+        ga = oracle.backward(q2, k2, v2, dy2, cq2, ck2, 2, 2, 0.5, sparse_mode=6, prefix=[n])
+        gb = oracle.backward(q2, k2, v2, dy2, cq2, ck2, 2, 2, 0.5, sparse_mode=mode)
+        for x, y in zip(ga[:3], gb[:3]):
+            np.testing.assert_array_equal(x, y)
 
 
 def test_dropout_all_keep_scales_output_and_keeps_stats():
@@ -286,7 +313,7 @@ def test_dv_is_pt_transpose_dy():
 
 # --------------------------------------------------------------------------- autograd + finite differences
 
-def _torch_attention(q, k, v, sink, cu_q, cu_kv, nq, nkv, scale, mode, pre, nxt, keep, bits, slopes):
+def _torch_attention(q, k, v, sink, cu_q, cu_kv, nq, nkv, scale, mode, pre, nxt, keep, bits, slopes, prefix=None):
     """A second, plainly written attention in torch: the sink enters as an extra
     softmax column that is dropped afterwards; masks come from tril/triu."""
     outs = []
@@ -309,6 +336,9 @@ def _torch_attention(q, k, v, sink, cu_q, cu_kv, nq, nkv, scale, mode, pre, nxt,
                 ok = ones.tril(0)
             elif mode == 3:
                 ok = ones.tril(lkv - lq)
+            elif mode == 6:
+                ok = ones.tril(lkv - lq)
+                ok[:, :int(prefix[b])] = True
             else:
                 ok = ones.tril(lkv - lq + nxt) & ones.triu(lkv - lq - pre)
             s = s.masked_fill(~ok, float("-inf"))
@@ -344,7 +374,7 @@ def _feature_case(seed, d=4):
                 mask=mask)
 
 
-@pytest.mark.parametrize("mode,pre,nxt", [(3, 0, 0), (4, 2, 1), (0, 0, 0)])
+@pytest.mark.parametrize("mode,pre,nxt", [(3, 0, 0), (4, 2, 1), (0, 0, 0), (6, 0, 0)])
 def test_backward_matches_autograd(mode, pre, nxt):
     c = _feature_case(50 + mode)
     scale = 0.45
@@ -353,11 +383,12 @@ def test_backward_matches_autograd(mode, pre, nxt):
     tv = torch.tensor(c["v"], requires_grad=True)
     ts = torch.tensor(c["sink"].astype(np.float64), requires_grad=True)
     bits = np.unpackbits(c["mask"], bitorder="little")
+    prefix = [2, 5] if mode == 6 else None   # sequence lengths 6 and 9: N in [0, L]
     out = _torch_attention(tq, tk, tv, ts, c["cq"], c["ck"], c["nq"], c["nkv"], scale, mode, pre, nxt,
-                           c["keep"], bits, c["slopes"])
+                           c["keep"], bits, c["slopes"], prefix)
     (out * torch.from_numpy(c["dy"])).sum().backward()
     kw = dict(sparse_mode=mode, pre_tokens=pre, next_tokens=nxt, keep_prob=c["keep"], drop_mask=c["mask"],
-              alibi_slopes=c["slopes"], sink=c["sink"])
+              alibi_slopes=c["slopes"], sink=c["sink"], prefix=prefix)
     o, _, _ = oracle.forward(c["q"], c["k"], c["v"], c["cq"], c["ck"], c["nq"], c["nkv"], scale, **kw)
     np.testing.assert_allclose(o, out.detach().numpy(), rtol=1e-12, atol=1e-13)
     dq, dk, dv, ds = oracle.backward(c["q"], c["k"], c["v"], c["dy"], c["cq"], c["ck"], c["nq"], c["nkv"],

@@ -34,6 +34,7 @@ MODE_NONE = 0
 MODE_LEFT_UP_CAUSAL = 2
 MODE_RIGHT_DOWN_CAUSAL = 3
 MODE_BAND = 4
+MODE_PREFIX = 6
 
 
 @dataclass
@@ -58,6 +59,7 @@ class Case:
     drop_mask: Optional[np.ndarray] = None     # uint8 packed bits
     alibi_slopes: Optional[np.ndarray] = None  # float32 [Nq]
     sink: Optional[np.ndarray] = None          # float32 [Nq]
+    prefix: Optional[np.ndarray] = None        # int64 [B]: prefix N per sequence (sparse mode 6)
     meta: dict = field(default_factory=dict)
 
     @property
@@ -142,7 +144,7 @@ def lognormal_lengths(seed, total: int, batch: int, median: float, lo: int, hi: 
 def make_case(name, lens_q, lens_kv=None, *, head_num, kv_heads, head_dim, dtype=torch.bfloat16,
               scale=None, keep_prob=1.0, sparse_mode=MODE_NONE, pre_tokens=INT_MAX_TOKENS,
               next_tokens=INT_MAX_TOKENS, alibi=False, sink=False, seed=0, dy_mult=1.0,
-              drop_mask=None) -> Case:
+              drop_mask=None, prefix=None) -> Case:
     """A case built from explicit lengths; every tensor is drawn from default_rng([seed, t])."""
     lens_q = np.asarray(lens_q, dtype=np.int64)
     lens_kv = lens_q.copy() if lens_kv is None else np.asarray(lens_kv, dtype=np.int64)
@@ -163,7 +165,8 @@ def make_case(name, lens_q, lens_kv=None, *, head_num, kv_heads, head_dim, dtype
                 kv_heads=kv_heads, head_dim=head_dim, scale=float(scale), q=q, k=k, v=v, dy=dy,
                 keep_prob=float(keep_prob), sparse_mode=sparse_mode, pre_tokens=int(pre_tokens),
                 next_tokens=int(next_tokens), drop_mask=drop_mask,
-                alibi_slopes=alibi_slopes(head_num) if alibi else None, sink=sink_v)
+                alibi_slopes=alibi_slopes(head_num) if alibi else None, sink=sink_v,
+                prefix=None if prefix is None else np.asarray(prefix, dtype=np.int64))
 
 
 WORKLOAD_NAMES = {
