@@ -49,6 +49,9 @@ class FaConfig(ctypes.Structure):
         ("deterministic", ctypes.c_int32),
         ("flags", ctypes.c_int32),
         ("prefix", ctypes.POINTER(ctypes.c_int64)),
+        ("atten_mask", ctypes.c_void_p),
+        ("mask_rows", ctypes.c_int64),
+        ("mask_cols", ctypes.c_int64),
     ]
 
 
@@ -99,11 +102,16 @@ class Config:
 
     def __init__(self, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, head_dim, dtype, scale, keep_prob=1.0,
                  sparse_mode=0, pre_tokens=TOKENS_DEFAULT, next_tokens=TOKENS_DEFAULT, deterministic=True,
-                 prefix=None):
+                 prefix=None, atten_mask=None):
         self.cu_q = np.ascontiguousarray(np.asarray(cu_seqlens_q, dtype=np.int64))
         self.cu_kv = np.ascontiguousarray(np.asarray(cu_seqlens_kv, dtype=np.int64))
         # per-sequence prefix N of sparse mode 6 (prefixOptional); NULL when None
         self.prefix = None if prefix is None else np.ascontiguousarray(np.asarray(prefix, dtype=np.int64))
+        # attenMask: a device tensor of bool / uint8 [S1Max, S2Max], nonzero = masked out (kept alive here)
+        self.atten_mask = atten_mask
+        if atten_mask is not None:
+            if atten_mask.dim() != 2 or atten_mask.dtype not in (torch.uint8, torch.bool) or not atten_mask.is_contiguous():
+                raise ValueError("atten_mask must be a contiguous 2-D bool or uint8 tensor [S1Max, S2Max]")
         if isinstance(dtype, torch.dtype):
             dtype = {torch.float32: FA_DTYPE_FP32, torch.bfloat16: FA_DTYPE_BF16}.get(dtype, -1)
         self.c = FaConfig(
@@ -114,7 +122,10 @@ class Config:
             sparse_mode=int(sparse_mode), scale=float(scale), keep_prob=float(keep_prob),
             pre_tokens=int(pre_tokens), next_tokens=int(next_tokens), deterministic=1 if deterministic else 0,
             flags=0,
-            prefix=(None if self.prefix is None else self.prefix.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+            prefix=(None if self.prefix is None else self.prefix.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))),
+            atten_mask=(None if atten_mask is None else atten_mask.data_ptr()),
+            mask_rows=(0 if atten_mask is None else int(atten_mask.shape[0])),
+            mask_cols=(0 if atten_mask is None else int(atten_mask.shape[1])))
 
     @property
     def ref(self):

@@ -30,6 +30,8 @@ struct Problem {
   std::vector<int32_t> cu_q, cu_kv;
   std::vector<int64_t> bit_base;   // first keep bit of each sequence
   std::vector<int32_t> prefix;     // prefix N of each sequence (sparse mode 6; zeros otherwise)
+  const uint8_t* mask = nullptr;   // attenMask (device) when the mode uses it
+  int64_t mask_rows = 0, mask_cols = 0, mask_words = 0;   // words: 32-key words per packed row
   int64_t drop_bits = 0;
 };
 
@@ -44,9 +46,10 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   if (cfg->head_dim != 64 && cfg->head_dim != 128) return FA_ERR_PARAM_INVALID;
   if (cfg->dtype != FA_DTYPE_FP32 && cfg->dtype != FA_DTYPE_BF16) return FA_ERR_PARAM_INVALID;
   const int mode = cfg->sparse_mode;
-  if (mode != FA_SPARSE_NONE && mode != FA_SPARSE_LEFT_UP_CAUSAL && mode != FA_SPARSE_RIGHT_DOWN_CAUSAL &&
-      mode != FA_SPARSE_BAND && mode != FA_SPARSE_PREFIX)
+  if (mode != FA_SPARSE_NONE && mode != FA_SPARSE_ALL_MASK && mode != FA_SPARSE_LEFT_UP_CAUSAL &&
+      mode != FA_SPARSE_RIGHT_DOWN_CAUSAL && mode != FA_SPARSE_BAND && mode != FA_SPARSE_PREFIX)
     return FA_ERR_PARAM_INVALID;
+  if (mode == FA_SPARSE_ALL_MASK && !cfg->atten_mask) return FA_ERR_PARAM_NULLPTR;
   if (mode == FA_SPARSE_PREFIX && !cfg->prefix) return FA_ERR_PARAM_NULLPTR;
   if (mode == FA_SPARSE_PREFIX && cfg->batch > kMaxPrefixBatch) return FA_ERR_PARAM_INVALID;
   if (!(cfg->keep_prob > 0.0 && cfg->keep_prob <= 1.0)) return FA_ERR_PARAM_INVALID;
@@ -100,6 +103,21 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   pr->tq = cq[pr->batch];
   pr->tkv = ck[pr->batch];
   if (pr->tq < 1 || pr->tkv < 1) return FA_ERR_PARAM_INVALID;
+  const bool uses_mask = mode == FA_SPARSE_NONE || mode == FA_SPARSE_ALL_MASK || mode == FA_SPARSE_BAND;
+  if (cfg->atten_mask && uses_mask) {
+    int64_t max_q = 0, max_kv = 0;
+    for (int64_t b = 0; b < pr->batch; ++b) {
+      max_q = std::max<int64_t>(max_q, cq[b + 1] - cq[b]);
+      max_kv = std::max<int64_t>(max_kv, ck[b + 1] - ck[b]);
+    }
+    if (cfg->mask_rows < max_q || cfg->mask_cols < max_kv || cfg->mask_rows > kMaxTokens ||
+        cfg->mask_cols > kMaxTokens)
+      return FA_ERR_PARAM_INVALID;
+    pr->mask = cfg->atten_mask;
+    pr->mask_rows = cfg->mask_rows;
+    pr->mask_cols = cfg->mask_cols;
+    pr->mask_words = (cfg->mask_cols + 31) / 32;
+  }
   pr->drop_bits = bits;
   return FA_OK;
 }
@@ -166,7 +184,7 @@ uint64_t align_up(uint64_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 struct Layout {
   uint64_t cu_q = 0, cu_kv = 0, bit_base = 0, prefix = 0, items0 = 0, items1 = 0;   // host-staged block
   uint64_t staged_bytes = 0;
-  uint64_t delta = 0, lse = 0, dsink_part = 0, dq_acc = 0;
+  uint64_t delta = 0, lse = 0, dsink_part = 0, dq_acc = 0, mbits = 0;
   uint64_t total = 0;
   int64_t n_items0 = 0, n_items1 = 0;
   int n_pre_blocks = 0;
@@ -182,6 +200,10 @@ Layout layout_fwd(const Problem& pr, int64_t n_items) {
   L.items0 = off; off = align_up(off + sizeof(WorkItem) * n_items);
   L.staged_bytes = off;
   L.n_items0 = n_items;
+  if (pr.mask) {
+    L.mbits = off;
+    off = align_up(off + 4 * (uint64_t)pr.mask_rows * pr.mask_words);
+  }
   L.total = std::max<uint64_t>(off, kAlign);
   return L;
 }
@@ -209,6 +231,10 @@ Layout layout_bwd(const Problem& pr, int64_t n_kv_items, int64_t n_dq_items) {
     L.dq_acc = off;
     off = align_up(off + 4 * (uint64_t)pr.tq * pr.nq * pr.d);
   }
+  if (pr.mask) {
+    L.mbits = off;
+    off = align_up(off + 4 * (uint64_t)pr.mask_rows * pr.mask_words);
+  }
   L.total = off;
   return L;
 }
@@ -221,9 +247,9 @@ Layout bwd_layout_bound(const Problem& pr) {
 }
 
 // ---- kernel timing (measurement hook) ----
-enum KernelId { K_FWD = 0, K_PRE, K_KV, K_DQ, K_CONVERT, K_DSINK, K_ZERO, K_COUNT };
+enum KernelId { K_FWD = 0, K_PRE, K_KV, K_DQ, K_CONVERT, K_DSINK, K_ZERO, K_MASK, K_COUNT };
 const char* kKernelNames[K_COUNT] = {"fa_fwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
-                                     "fa_bwd_dq_convert", "fa_bwd_dsink_reduce", "fa_zero_f32"};
+                                     "fa_bwd_dq_convert", "fa_bwd_dsink_reduce", "fa_zero_f32", "fa_mask_pack"};
 struct ProfState {
   std::mutex mu;
   bool on = false;
@@ -354,6 +380,14 @@ fa_status fa_fwd(const fa_config* cfg, const void* q, const void* k, const void*
   p.prefix = reinterpret_cast<const int32_t*>(ws + L.prefix);
   p.items = reinterpret_cast<const WorkItem*>(ws + L.items0);
   p.n_items = (int32_t)items.size();
+  p.mbits = pr.mask ? reinterpret_cast<const uint32_t*>(ws + L.mbits) : nullptr;
+  p.mwords = (int32_t)pr.mask_words;
+  if (pr.mask) {
+    e = timed(K_MASK, s, [&] {
+      return fa::launch_mask_pack(pr.mask, pr.mask_rows, pr.mask_cols, reinterpret_cast<uint32_t*>(ws + L.mbits), s);
+    });
+    if (e != hipSuccess) return FA_ERR_HIP;
+  }
   return hip_status(timed(K_FWD, s, [&] { return fa::launch_fwd(pr.dtype, (int)pr.d, p, s); }));
 }
 
@@ -381,6 +415,8 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
   // the atomic dK/dV kernel for bf16 D = 128 has no alibi variant (its registers
   // do not fit one): run the deterministic passes, which need less workspace
   if (alibi_slopes && pr.dtype == FA_DTYPE_BF16 && pr.d == 128) pr.deterministic = true;
+  // the attenMask is read by the deterministic passes only (the atomic kernels have no mask instances)
+  if (pr.mask) pr.deterministic = true;
   std::vector<WorkItem> kv_items = schedule(pr, 1, nullptr, nullptr);
   std::vector<WorkItem> dq_items = schedule(pr, 2, nullptr, nullptr);
   const Layout L = layout_bwd(pr, (int64_t)kv_items.size(), (int64_t)dq_items.size());
@@ -422,9 +458,16 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
   p.use_dropout = pr.keep < 1.0 ? 1 : 0;
   p.head_swizzle = (pr.nq % 8 == 0) ? 1 : 0;
   p.n_pre_blocks = L.n_pre_blocks;
+  p.mbits = pr.mask ? reinterpret_cast<const uint32_t*>(ws + L.mbits) : nullptr;
+  p.mwords = (int32_t)pr.mask_words;
   const int dt = pr.dtype, d = (int)pr.d;
 
-  e = timed(K_PRE, s, [&] { return fa::launch_bwd_pre(dt, d, p, s); });
+  e = hipSuccess;
+  if (pr.mask)
+    e = timed(K_MASK, s, [&] {
+      return fa::launch_mask_pack(pr.mask, pr.mask_rows, pr.mask_cols, reinterpret_cast<uint32_t*>(ws + L.mbits), s);
+    });
+  if (e == hipSuccess) e = timed(K_PRE, s, [&] { return fa::launch_bwd_pre(dt, d, p, s); });
   if (e == hipSuccess && !pr.deterministic)
     e = timed(K_ZERO, s, [&] { return fa::launch_zero_f32(p.dq_acc, pr.tq * pr.nq * pr.d, s); });
   if (e == hipSuccess) e = timed(K_KV, s, [&] { return fa::launch_bwd_kv(dt, d, !pr.deterministic, p, s); });

@@ -14,7 +14,7 @@
 //   fa_bwd_kv_kernel    dK, dV (and optionally atomic dQ): fa_bwd_kv.hip
 //   fa_bwd_dq_kernel    deterministic dQ: one 128-row query tile per workgroup,
 //                       recomputes S, dP, dS over its key tiles, dQ in registers
-//   fa_dq_convert_kernel, fa_dsink_reduce_kernel, fa_zero_kernel
+//   fa_dq_convert_kernel, fa_dsink_reduce_kernel, fa_zero_kernel, fa_mask_pack_kernel
 #include "fa_device.h"
 #include "fa_kernels.h"
 #include "fa_sched.h"
@@ -106,6 +106,23 @@ __global__ __launch_bounds__(256) void fa_dsink_reduce_kernel(const float* part,
   if (t == 0) out[h] = red[0];
 }
 
+// attenMask [rows, cols] of bytes (nonzero = masked out) -> one 32-bit word per
+// row and 32 keys, bit k for key 32w + k; keys at or past `cols` read as masked.
+__global__ __launch_bounds__(256) void fa_mask_pack_kernel(const uint8_t* mask, int64_t rows, int64_t cols,
+                                                           int64_t words, uint32_t* bits) {
+  for (int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x; idx < rows * words; idx += (int64_t)gridDim.x * 256) {
+    const int64_t i = idx / words, w = idx - i * words;
+    const uint8_t* row = mask + i * cols;
+    uint32_t acc = 0;
+    for (int k = 0; k < 32; ++k) {
+      const int64_t j = 32 * w + k;
+      const uint32_t m = j < cols ? (row[j] != 0) : 1u;
+      acc |= m << k;
+    }
+    bits[idx] = acc;
+  }
+}
+
 __global__ __launch_bounds__(256) void fa_zero_kernel(float* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
 }
@@ -133,7 +150,7 @@ struct DqShape {
   static constexpr int NDB = D / 32;
 };
 
-template <typename T, int D, bool DROP, bool ALIBI>
+template <typename T, int D, bool DROP, bool ALIBI, bool MASK>
 __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams p) {
   using S = DqShape<T, D>;
   using Op = typename std::conditional<sizeof(T) == 2, bf16x8, float>::type;
@@ -214,7 +231,8 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
     const char* vs = ks + S::TILE;
     const int c0 = t * kDqBN;
     if (wr0 >= lq || fa_tile_empty(win, wr0, min(wr0 + 32, lq), c0, min(c0 + kDqBN, lkv))) return;
-    const bool full = fa_tile_full(win, wr0, 32, c0, kDqBN, lq, lkv);
+    // with an attenMask every tile takes the masked path
+    const bool full = fa_tile_full(win, wr0, 32, c0, kDqBN, lq, lkv) && !MASK;
     uint64_t bits = ~0ull;
     if constexpr (DROP) {
       const int64_t pos = p.bit_base[b] + ((int64_t)h * lq + i) * lkv + c0;
@@ -246,6 +264,14 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
           dp = mfma32(*reinterpret_cast<const float*>(vrow + (2 * c + hh) * 4), df[c], dp);
         }
       }
+      // attenMask bits (1 = masked) of the lane's row for these 32 keys
+      uint32_t mwk = 0;
+      if constexpr (MASK) {
+        if (row_ok) {
+          const int w = (c0 >> 5) + kb;
+          mwk = w < p.mwords ? p.mbits[(int64_t)i * p.mwords + w] : ~0u;
+        }
+      }
       f32x16 ds;
       const float jmi = (float)(c0 + 32 * kb + 4 * hh - i);   // j - i of register 0
 #pragma unroll
@@ -259,7 +285,8 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
           float x = s[r] * p.scale_log2;
           if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, jmi + (float)(8 * (r >> 2) + (r & 3)), x);
           if (!full) {
-            const bool ok = row_ok & (jj < lkv) & (jj >= fa_row_lo(win, i)) & (jj <= fa_row_hi(win, i));
+            const bool ok = row_ok & (jj < lkv) & (jj >= fa_row_lo(win, i)) & (jj <= fa_row_hi(win, i)) &
+                            !((mwk >> (kk - 32 * kb)) & 1u);
             x = ok ? x : kNegInf;
           }
           pr = fast_exp2(x - lse2);
@@ -372,15 +399,11 @@ static hipError_t launch_dq_t(const BwdParams& p, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(256);
   const bool drop = p.use_dropout != 0, alibi = p.slopes != nullptr;
-  if (drop && alibi)
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, true, true>), grid, block, 0, s, p);
-  else if (drop)
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, true, false>), grid, block, 0, s, p);
-  else if (alibi)
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, false, true>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, false, false>), grid, block, 0, s, p);
-  return hipGetLastError();
+  return with_flags(drop, alibi, p.mbits != nullptr, [&](auto dr, auto al, auto mk) {
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, decltype(dr)::value, decltype(al)::value, decltype(mk)::value>),
+                       grid, block, 0, s, p);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_bwd_dq(int dtype, int d, const BwdParams& p, hipStream_t s) {
@@ -404,6 +427,14 @@ hipError_t launch_bwd_dq_convert(int dtype, int d, const BwdParams& p, hipStream
 
 hipError_t launch_bwd_dsink(const BwdParams& p, hipStream_t s) {
   hipLaunchKernelGGL(fa_dsink_reduce_kernel, dim3(p.nq), dim3(256), 0, s, p.dsink_part, p.n_pre_blocks, p.nq, p.dsink);
+  return hipGetLastError();
+}
+
+hipError_t launch_mask_pack(const uint8_t* mask, int64_t rows, int64_t cols, uint32_t* bits, hipStream_t s) {
+  const int64_t words = (cols + 31) / 32, n = rows * words;
+  if (n == 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192;
+  hipLaunchKernelGGL(fa_mask_pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, mask, rows, cols, words, bits);
   return hipGetLastError();
 }
 

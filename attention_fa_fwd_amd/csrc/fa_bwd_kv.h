@@ -32,12 +32,13 @@ struct KvShape {
   static constexpr int P = kSwz ? RB : RB + 16;     // LDS pitch of Q / dY rows
   static constexpr int KTP = RB + 16;               // LDS pitch of K rows (atomic dQ)
   static constexpr int QT = kKvBM * P;              // one 64-row Q (or dY) tile
-  // stage layout: Q | dY | lse2[64] | D_i[64] | keep bits[64][4]
+  // stage layout: Q | dY | lse2[64] | D_i[64] | keep bits[64][4] | attenMask bits[64][4]
   static constexpr int OFF_DY = QT;
   static constexpr int OFF_LSE = 2 * QT;
   static constexpr int OFF_DEL = OFF_LSE + 4 * kKvBM;
   static constexpr int OFF_BITS = OFF_DEL + 4 * kKvBM;
-  static constexpr int STAGE = OFF_BITS + 16 * kKvBM;
+  static constexpr int OFF_MBITS = OFF_BITS + 16 * kKvBM;   // attenMask bits, same layout as the keep bits
+  static constexpr int STAGE = OFF_MBITS + 16 * kKvBM;
   static constexpr int KT = kKvBN * KTP;            // the 128-key K tile (atomic dQ only)
   static constexpr int DSP = kKvBM * EB + 16;       // pitch of dS^T rows (one row per key)
   static constexpr int DST = kKvBN * DSP;
@@ -45,7 +46,7 @@ struct KvShape {
   static constexpr int NDB = D / 32;
 };
 
-template <typename T, int D, bool ATOMIC, bool DROP, bool ALIBI>
+template <typename T, int D, bool ATOMIC, bool DROP, bool ALIBI, bool MASK>
 __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
   using S = KvShape<T, D>;
   using Op = typename std::conditional<sizeof(T) == 2, bf16x8, float>::type;
@@ -176,6 +177,13 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
     const int64_t pos = p.bit_base[b] + ((int64_t)h * lq + r0 + r) * lkv + c0 + 32 * w;
     return (uint32_t)load_mask_window(p.drop, p.drop_bytes, pos);
   };
+  // attenMask bits (1 = masked) of the next step, same slots (only with a mask)
+  auto mask_word = [&](int n) -> uint32_t {
+    const int r0 = step_row0(n);
+    const int r = tid >> 2, w = (c0 >> 5) + (tid & 3);
+    if (r0 + r >= lq || w >= p.mwords) return ~0u;
+    return p.mbits[(int64_t)(r0 + r) * p.mwords + w];
+  };
 
   // atomic dQ of one bf16 step: store_ds() puts each block's dS^T into LDS right
   // after it is formed; atomic_dq() then adds dQ(64 rows x 32-wide d block of this
@@ -249,8 +257,10 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
       const int rq = 32 * rb + 8 * a + 4 * hh;   // rows rq .. rq+3 sit in registers 4a .. 4a+3
       const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lse_s + rq);
       const f32x4 del4 = *reinterpret_cast<const f32x4*>(del_s + rq);
-      u32x4 bits4;
+      u32x4 bits4, mb4 = {};
       if constexpr (DROP) bits4 = *reinterpret_cast<const u32x4*>(bits_s + wave * kKvBM + rq);
+      if constexpr (!decltype(full_c)::value && MASK)
+        mb4 = *reinterpret_cast<const u32x4*>(st + S::OFF_MBITS + 4 * (wave * kKvBM + rq));
       const float jmi = (float)(j - r0 - rq);   // j - i of register 4a; minus e for register 4a + e
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -262,7 +272,8 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
           float x = s[r] * sc;
           if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, jmi - (float)e, x);
           if constexpr (!decltype(full_c)::value) {
-            const bool ok = (i < lq) & key_ok & (j >= fa_row_lo(win, i)) & (j <= fa_row_hi(win, i));
+            const bool ok = (i < lq) & key_ok & (j >= fa_row_lo(win, i)) & (j <= fa_row_hi(win, i)) &
+                            !((mb4[e] >> lrow) & 1u);
             x = ok ? x : kNegInf;
           }
           pr = fast_exp2(x - lse4[e]);
@@ -298,8 +309,9 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
   auto compute_bf16 = [&](const char* st, auto n) {
     const int h = step_head(n), r0 = step_row0(n);
     const float slope_l2 = ALIBI ? p.slopes[h] * kLog2e : 0.f;
-    const bool full0 = fa_tile_full(win, r0, 32, wc0, 32, lq, lkv);
-    const bool full1 = fa_tile_full(win, r0 + 32, 32, wc0, 32, lq, lkv);
+    // with an attenMask every block takes the masked path
+    const bool full0 = fa_tile_full(win, r0, 32, wc0, 32, lq, lkv) && !MASK;
+    const bool full1 = fa_tile_full(win, r0 + 32, 32, wc0, 32, lq, lkv) && !MASK;
     f32x16 s0, dp0, s1, dp1;
     bf16x8 pa0[2], da0[2], pa1[2], da1[2];
     auto block = [&](int rb, bool full, auto& sx, auto& dpx, auto& pax, auto& dax) {
@@ -339,7 +351,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
         da_keep[rb][1] = bf16x8{};
       }
       if (empty) continue;
-      const bool full = fa_tile_full(win, rb0, 32, wc0, 32, lq, lkv);
+      const bool full = fa_tile_full(win, rb0, 32, wc0, 32, lq, lkv) && !MASK;
       // ---- S = Q K^T and dP~ = dY V^T (lane = key, registers = rows) ----
       f32x16 s = f32x16{}, dp = f32x16{};
       if constexpr (sizeof(T) == 2) {
@@ -367,7 +379,9 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
         const int rr = 32 * rb + 8 * (r >> 2) + 4 * hh + (r & 3);
         float x = s[r] * p.scale_log2;
         if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, (float)(j - (r0 + rr)), x);
-        if (!full && !fa_allowed(win, r0 + rr, j, lq, lkv)) x = kNegInf;
+        if (!full && (!fa_allowed(win, r0 + rr, j, lq, lkv) ||
+                      (MASK && ((reinterpret_cast<const uint32_t*>(st + S::OFF_MBITS)[wave * kKvBM + rr] >> lrow) & 1u))))
+          x = kNegInf;
         const float pr = fast_exp2(x - lse_s[rr]);
         float dpv = dp[r], ptv = pr;
         if constexpr (DROP) {
@@ -500,33 +514,38 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
   };
 
   if (nsteps > 0) load(st0, 0);
-  uint32_t word = 0;
+  uint32_t word = 0, mword = 0;
   if constexpr (DROP) {
     if (nsteps > 0) word = bits_word(0);
     reinterpret_cast<uint32_t*>(st0 + S::OFF_BITS)[bits_slot] = word;
   }
+  if (MASK && nsteps > 0) reinterpret_cast<uint32_t*>(st0 + S::OFF_MBITS)[bits_slot] = mask_word(0);
   dma_wait();
   __syncthreads();
   for (int n = 0; n < nsteps; n += 2) {
     if (n + 1 < nsteps) {
       load(st1, n + 1);
       if constexpr (DROP) word = bits_word(n + 1);
+      if constexpr (MASK) mword = mask_word(n + 1);
     }
     if constexpr (sizeof(T) == 2) compute_bf16(st0, n);
     else compute(st0, n);
     if constexpr (DROP)
       if (n + 1 < nsteps) reinterpret_cast<uint32_t*>(st1 + S::OFF_BITS)[bits_slot] = word;
+    if (MASK && n + 1 < nsteps) reinterpret_cast<uint32_t*>(st1 + S::OFF_MBITS)[bits_slot] = mword;
     dma_wait();
     __syncthreads();
     if (n + 1 < nsteps) {
       if (n + 2 < nsteps) {
         load(st0, n + 2);
         if constexpr (DROP) word = bits_word(n + 2);
+        if constexpr (MASK) mword = mask_word(n + 2);
       }
       if constexpr (sizeof(T) == 2) compute_bf16(st1, n + 1);
       else compute(st1, n + 1);
       if constexpr (DROP)
         if (n + 2 < nsteps) reinterpret_cast<uint32_t*>(st0 + S::OFF_BITS)[bits_slot] = word;
+      if (MASK && n + 2 < nsteps) reinterpret_cast<uint32_t*>(st0 + S::OFF_MBITS)[bits_slot] = mword;
       dma_wait();
       __syncthreads();
     }
@@ -562,7 +581,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
 //     [half * D/2, (half + 1) * D/2).
 // So no MFMA is done twice, and each wave holds half of the dK/dV accumulators:
 // small enough for two waves per SIMD, whose VALU and MFMA work then overlap.
-template <int D, bool DROP, bool ALIBI>
+template <int D, bool DROP, bool ALIBI, bool MASK>
 __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
   using S = KvShape<__bf16, D>;
   constexpr int NW = 8;
@@ -658,6 +677,13 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
     const int64_t pos = p.bit_base[b] + ((int64_t)h * lq + r0 + r) * lkv + c0 + 32 * w;
     return (uint32_t)load_mask_window(p.drop, p.drop_bytes, pos);
   };
+  // attenMask bits (1 = masked) of a step, same slots (only with a mask)
+  auto mask_word = [&](int n) -> uint32_t {
+    const int r0 = step_row0(n);
+    const int r = (tid >> 2) & (kKvBM - 1), w = (c0 >> 5) + (tid & 3);
+    if (tid >= 4 * kKvBM || r0 + r >= lq || w >= p.mwords) return ~0u;
+    return p.mbits[(int64_t)(r0 + r) * p.mwords + w];
+  };
 
   auto compute = [&](const char* st, int n) {
     const int h = step_head(n), r0 = step_row0(n);
@@ -692,8 +718,10 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
           const int rq = 32 * rb + 8 * a + 4 * hh;   // rows rq .. rq+3 sit in registers 4a .. 4a+3
           const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lse_s + rq);
           const f32x4 del4 = *reinterpret_cast<const f32x4*>(del_s + rq);
-          u32x4 bits4;
+          u32x4 bits4, mb4 = {};
           if constexpr (DROP) bits4 = *reinterpret_cast<const u32x4*>(bits_s + kg * kKvBM + rq);
+          if constexpr (!decltype(full_c)::value && MASK)
+            mb4 = *reinterpret_cast<const u32x4*>(st + S::OFF_MBITS + 4 * (kg * kKvBM + rq));
           const float jmi = (float)(j - r0 - rq);   // j - i of register 4a; minus e for register 4a + e
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -705,7 +733,8 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
               float x = s[r] * sc;
               if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, jmi - (float)e, x);
               if constexpr (!decltype(full_c)::value) {
-                const bool ok = (i < lq) & key_ok & (j >= fa_row_lo(win, i)) & (j <= fa_row_hi(win, i));
+                const bool ok = (i < lq) & key_ok & (j >= fa_row_lo(win, i)) & (j <= fa_row_hi(win, i)) &
+                                !((mb4[e] >> lrow) & 1u);
                 x = ok ? x : kNegInf;
               }
               pr = fast_exp2(x - lse4[e]);
@@ -725,7 +754,8 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
         *reinterpret_cast<bf16x8*>(xmine + 1024 * (2 + c)) = da;
       }
     };
-    if (fa_tile_full(win, r0 + 32 * rb, 32, wc0, 32, lq, lkv)) elem(std::true_type{});
+    // with an attenMask every block takes the masked path
+    if (fa_tile_full(win, r0 + 32 * rb, 32, wc0, 32, lq, lkv) && !MASK) elem(std::true_type{});
     else elem(std::false_type{});
     __syncthreads();
     // ---- dV += P~^T dY, dK += dS^T Q over both row blocks, this wave's d half ----
@@ -752,31 +782,36 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
   };
 
   if (nsteps > 0) load(st0, 0);
-  uint32_t word = 0;
+  uint32_t word = 0, mword = 0;
   if constexpr (DROP) {
     if (nsteps > 0) word = bits_word(0);
     if (tid < 4 * kKvBM) reinterpret_cast<uint32_t*>(st0 + S::OFF_BITS)[bits_slot] = word;
   }
+  if (MASK && nsteps > 0 && tid < 4 * kKvBM) reinterpret_cast<uint32_t*>(st0 + S::OFF_MBITS)[bits_slot] = mask_word(0);
   dma_wait();
   __syncthreads();
   for (int n = 0; n < nsteps; n += 2) {
     if (n + 1 < nsteps) {
       load(st1, n + 1);
       if constexpr (DROP) word = bits_word(n + 1);
+      if constexpr (MASK) mword = mask_word(n + 1);
     }
     compute(st0, n);
     if constexpr (DROP)
       if (n + 1 < nsteps && tid < 4 * kKvBM) reinterpret_cast<uint32_t*>(st1 + S::OFF_BITS)[bits_slot] = word;
+    if (MASK && n + 1 < nsteps && tid < 4 * kKvBM) reinterpret_cast<uint32_t*>(st1 + S::OFF_MBITS)[bits_slot] = mword;
     dma_wait();
     __syncthreads();
     if (n + 1 < nsteps) {
       if (n + 2 < nsteps) {
         load(st0, n + 2);
         if constexpr (DROP) word = bits_word(n + 2);
+        if constexpr (MASK) mword = mask_word(n + 2);
       }
       compute(st1, n + 1);
       if constexpr (DROP)
         if (n + 2 < nsteps && tid < 4 * kKvBM) reinterpret_cast<uint32_t*>(st0 + S::OFF_BITS)[bits_slot] = word;
+      if (MASK && n + 2 < nsteps && tid < 4 * kKvBM) reinterpret_cast<uint32_t*>(st0 + S::OFF_MBITS)[bits_slot] = mword;
       dma_wait();
       __syncthreads();
     }

@@ -13,13 +13,13 @@ static hipError_t launch_kv_t(const BwdParams& p, hipStream_t s) {
   constexpr bool kAlibi = !(ATOMIC && sizeof(T) == 2 && D == 128);
   if (alibi && !kAlibi) return hipErrorInvalidValue;
   if (drop && alibi)
-    hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, true, kAlibi>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, true, kAlibi, false>), grid, block, 0, s, p);
   else if (drop)
-    hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, true, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, true, false, false>), grid, block, 0, s, p);
   else if (alibi)
-    hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, false, kAlibi>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, false, kAlibi, false>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, false, false>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, false, false, false>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 

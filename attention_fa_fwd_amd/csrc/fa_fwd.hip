@@ -63,9 +63,10 @@ struct RowTile {
   bool live;          // the wave's 32 rows hold at least one allowed pair in the tile
   bool full;          // every (row, key) pair of the wave's rows is inside the mask
   uint32_t bits[2];   // keep bits of the lane's row for keys 0-31 and 32-63 of the tile
+  uint32_t mw[2];     // attenMask bits (1 = masked) of the lane's row, same keys
 };
 
-template <typename T, int D, int NW, int OCC, bool DROP, bool ALIBI>
+template <typename T, int D, int NW, int OCC, bool DROP, bool ALIBI, bool MASK>
 __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
   using S = FwdShape<T, D>;
   constexpr int BM = 32 * NW;
@@ -151,8 +152,17 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
     RowTile rt;
     const int c0 = t * kFwdBN;
     rt.live = wr0 < lq && !fa_tile_empty(win, wr0, min(wr0 + 32, lq), c0, min(c0 + kFwdBN, lkv));
-    rt.full = fa_tile_full(win, wr0, 32, c0, kFwdBN, lq, lkv);
+    // with an attenMask every tile takes the masked path
+    rt.full = fa_tile_full(win, wr0, 32, c0, kFwdBN, lq, lkv) && !MASK;
     rt.bits[0] = rt.bits[1] = ~0u;
+    rt.mw[0] = rt.mw[1] = 0u;
+    if constexpr (MASK) {
+      if (rt.live && row_ok) {
+        const uint32_t* mr = p.mbits + (int64_t)i * p.mwords + (c0 >> 5);
+        rt.mw[0] = mr[0];
+        rt.mw[1] = (c0 >> 5) + 1 < p.mwords ? mr[1] : ~0u;
+      }
+    }
     if constexpr (DROP) {
       if (rt.live) {
         const int64_t pos = p.bit_base[b] + ((int64_t)h * lq + i) * lkv + c0;
@@ -217,7 +227,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
           const int j = c0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
           float x = s[kb][r] * sc;
           if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, (float)(j - i), x);
-          if (!decltype(full_c)::value && !fa_allowed(win, i, j, lq, lkv)) x = kNegInf;
+          if (!decltype(full_c)::value &&
+              (!fa_allowed(win, i, j, lq, lkv) || (MASK && ((rt.mw[kb] >> (8 * (r >> 2) + 4 * hh + (r & 3))) & 1u))))
+            x = kNegInf;
           s[kb][r] = x;
           mt = fmaxf(mt, x);
         }
@@ -385,15 +397,13 @@ static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
   constexpr int NWD = fwd_waves(true, F32), NWP = fwd_waves(false, F32);
   constexpr int OCD = fwd_occupancy(true, F32), OCP = fwd_occupancy(false, F32);
   const dim3 grid((unsigned)blocks), block(64 * (drop ? NWD : NWP));
-  if (drop && alibi)
-    hipLaunchKernelGGL((fa_fwd_kernel<T, D, NWD, OCD, true, true>), grid, block, 0, s, p);
-  else if (drop)
-    hipLaunchKernelGGL((fa_fwd_kernel<T, D, NWD, OCD, true, false>), grid, block, 0, s, p);
-  else if (alibi)
-    hipLaunchKernelGGL((fa_fwd_kernel<T, D, NWP, OCP, false, true>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((fa_fwd_kernel<T, D, NWP, OCP, false, false>), grid, block, 0, s, p);
-  return hipGetLastError();
+  return with_flags(drop, alibi, p.mbits != nullptr, [&](auto dr, auto al, auto mk) {
+    constexpr bool DR = decltype(dr)::value;
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, DR ? NWD : NWP, DR ? OCD : OCP, DR, decltype(al)::value,
+                                      decltype(mk)::value>),
+                       grid, block, 0, s, p);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_fwd(int dtype, int d, const FwdParams& p, hipStream_t s) {

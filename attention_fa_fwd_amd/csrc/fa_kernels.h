@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 // Work item of the forward and dQ passes: one query tile of one sequence,
@@ -28,6 +30,8 @@ struct FwdParams {
   const int32_t* cu_kv;
   const int64_t* bit_base;
   const int32_t* prefix;    // per sequence: prefix N of sparse mode 6 (0 otherwise)
+  const uint32_t* mbits;    // packed attenMask (1 = masked) [mask rows][mwords], or null
+  int32_t mwords;           // 32-key words per packed mask row
   const WorkItem* items;
   int32_t n_items;
   int32_t nq, nkv, group;
@@ -62,6 +66,8 @@ struct BwdParams {
   const int32_t* cu_kv;
   const int64_t* bit_base;
   const int32_t* prefix;    // per sequence: prefix N of sparse mode 6 (0 otherwise)
+  const uint32_t* mbits;    // packed attenMask (1 = masked) [mask rows][mwords], or null
+  int32_t mwords;           // 32-key words per packed mask row
   const int32_t* row_seq;   // sequence index of each query token (preprocess)
   const WorkItem* kv_items;
   const WorkItem* dq_items;
@@ -88,6 +94,20 @@ constexpr int kKvBN = 128, kKvBM = 64;
 constexpr int kDqBM = 128, kDqBN = 64;
 constexpr int kPreRowsPerBlock = 64;
 
+// Calls f(drop, alibi, mask) with each flag as a std::integral_constant<bool, .>,
+// so a launcher names one kernel instance per combination.
+template <typename F>
+hipError_t with_flags(bool drop, bool alibi, bool mask, F&& f) {
+  using T = std::true_type;
+  using N = std::false_type;
+  if (drop) {
+    if (alibi) return mask ? f(T{}, T{}, T{}) : f(T{}, T{}, N{});
+    return mask ? f(T{}, N{}, T{}) : f(T{}, N{}, N{});
+  }
+  if (alibi) return mask ? f(N{}, T{}, T{}) : f(N{}, T{}, N{});
+  return mask ? f(N{}, N{}, T{}) : f(N{}, N{}, N{});
+}
+
 hipError_t launch_fwd(int dtype, int d, const FwdParams& p, hipStream_t s);
 hipError_t launch_bwd_pre(int dtype, int d, const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_kv(int dtype, int d, bool atomic_dq, const BwdParams& p, hipStream_t s);
@@ -96,5 +116,6 @@ hipError_t launch_bwd_dq(int dtype, int d, const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_dq_convert(int dtype, int d, const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_dsink(const BwdParams& p, hipStream_t s);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
+hipError_t launch_mask_pack(const uint8_t* mask, int64_t rows, int64_t cols, uint32_t* bits, hipStream_t s);
 
 }  // namespace fa

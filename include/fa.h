@@ -56,7 +56,8 @@ typedef int32_t fa_status;
 #define FA_DTYPE_BF16 1
 
 /* sparse modes (aclnnFlashAttentionUnpaddingScoreGrad, "sparseMode" parameter) */
-#define FA_SPARSE_NONE 0             /* every pair allowed                                   */
+#define FA_SPARSE_NONE 0             /* every pair allowed (or those the attenMask keeps)    */
+#define FA_SPARSE_ALL_MASK 1         /* the pairs the attenMask keeps (mask required)        */
 #define FA_SPARSE_LEFT_UP_CAUSAL 2   /* j <= i                                               */
 #define FA_SPARSE_RIGHT_DOWN_CAUSAL 3 /* j <= i + (Lkv - Lq)                                  */
 #define FA_SPARSE_BAND 4             /* i+(Lkv-Lq)-pre <= j <= i+(Lkv-Lq)+next (inclusive)    */
@@ -91,6 +92,16 @@ typedef struct fa_config {
                                     else [Lkv_b - Lq_b, Lkv_b]; B <= 1024 with a prefix.
                                     NULL in mode 6 -> FA_ERR_PARAM_NULLPTR; out of range
                                     -> FA_ERR_PARAM_INVALID.                                 */
+  const uint8_t* atten_mask;     /* DEVICE, optional: attenMaskOptional of the grad page, BOOL /
+                                    UINT8 [mask_rows, mask_cols] row-major, shared by every
+                                    sequence and head and indexed by the sequence's local row
+                                    and key; nonzero = the pair is masked out.  Used with
+                                    modes 0 (the mask alone), 1 (required) and 4 (and the
+                                    band); modes 2, 3 and 6 define their own triangle (the
+                                    page's compressed masks for them carry no more) and
+                                    ignore it.  NULL = no mask.                               */
+  int64_t mask_rows;             /* S1Max >= every Lq_b (with atten_mask)                     */
+  int64_t mask_cols;             /* S2Max >= every Lkv_b (with atten_mask)                    */
 } fa_config;
 
 /* Device workspace bytes needed by fa_fwd for this configuration (>= 256). */

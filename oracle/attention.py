@@ -15,7 +15,8 @@ What it computes follows the Ascend CANN pages:
     dSink is a reduction of -P*dP*SimpleSoftmax(sink, max, sum).
   * aclnnFlashAttentionUnpaddingScoreGrad, sparseMode list: 0 no mask,
     2 leftUpCausal, 3 rightDownCausal, 4 band between preTokens/nextTokens,
-    6 prefix (with prefixOptional, one N per sequence).
+    6 prefix (with prefixOptional, one N per sequence); attenMaskOptional
+    (nonzero = masked out), used by modes 0, 1 (all mask) and 4.
 
 Readings taken where the pages are silent (each is listed with its reason in
 the design notes):
@@ -50,9 +51,15 @@ INT_MAX_TOKENS = 2147483647
 
 
 def allowed(lq: int, lkv: int, sparse_mode: int, pre_tokens: int = INT_MAX_TOKENS,
-            next_tokens: int = INT_MAX_TOKENS, prefix: int = 0) -> np.ndarray:
+            next_tokens: int = INT_MAX_TOKENS, prefix: int = 0, atten_mask=None) -> np.ndarray:
     """Boolean [lq, lkv]: True where query row i may attend key j (sparseMode list;
-    `prefix` is the sequence's N for mode 6)."""
+    `prefix` is the sequence's N for mode 6; `atten_mask` [S1Max, S2Max], nonzero =
+    masked out, applies in modes 0, 1 and 4 at the sequence's local indices)."""
+    if atten_mask is not None and sparse_mode in (0, 1, 4):
+        keep = np.asarray(atten_mask)[:lq, :lkv] == 0
+        return keep & allowed(lq, lkv, 0 if sparse_mode == 1 else sparse_mode, pre_tokens, next_tokens)
+    if sparse_mode == 1:
+        raise ValueError("sparse_mode 1 needs atten_mask")
     i = np.arange(lq, dtype=np.int64)[:, None]
     j = np.arange(lkv, dtype=np.int64)[None, :]
     delta = lkv - lq
@@ -88,7 +95,7 @@ class _Problem:
     """Inputs of one call, upcast to fp64, with the per-sequence bookkeeping."""
 
     def __init__(self, q, k, v, cu_q, cu_kv, head_num, kv_heads, scale, keep_prob, sparse_mode,
-                 pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix=None):
+                 pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix=None, atten_mask=None):
         # kept in their given precision; each (sequence, head) slice is upcast to fp64 when used
         self.q = np.asarray(q)
         self.k = np.asarray(k)
@@ -110,6 +117,7 @@ class _Problem:
         self.sink = None if sink is None else np.asarray(sink, dtype=np.float32).astype(np.float64)
         self.batch = len(self.cu_q) - 1
         self.prefix = np.zeros(self.batch, dtype=np.int64) if prefix is None else np.asarray(prefix, dtype=np.int64)
+        self.atten_mask = None if atten_mask is None else np.asarray(atten_mask)
         self.lens_q = np.diff(self.cu_q)
         self.lens_kv = np.diff(self.cu_kv)
         # start bit of each sequence's block in the packed keep mask
@@ -126,7 +134,7 @@ class _Problem:
         s = self.scale * (qb @ kb.T)
         if self.slopes is not None:
             s = s + alibi_pse(lq, lkv, self.slopes[h])
-        ok = allowed(lq, lkv, self.mode, self.pre, self.next, int(self.prefix[b]))
+        ok = allowed(lq, lkv, self.mode, self.pre, self.next, int(self.prefix[b]), self.atten_mask)
         s = np.where(ok, s, -np.inf)
         m = s.max(axis=1) if lkv > 0 else np.full(lq, -np.inf)
         if self.sink is not None:
@@ -154,9 +162,9 @@ class _Problem:
 
 def _problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob=1.0,
              sparse_mode=0, pre_tokens=INT_MAX_TOKENS, next_tokens=INT_MAX_TOKENS, drop_mask=None,
-             alibi_slopes=None, sink=None, prefix=None):
+             alibi_slopes=None, sink=None, prefix=None, atten_mask=None):
     return _Problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob,
-                    sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix)
+                    sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix, atten_mask)
 
 
 def _selected(subset, n):
@@ -165,12 +173,12 @@ def _selected(subset, n):
 
 def forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob=1.0,
             sparse_mode=0, pre_tokens=INT_MAX_TOKENS, next_tokens=INT_MAX_TOKENS, drop_mask=None,
-            alibi_slopes=None, sink=None, batches=None, heads=None, prefix=None):
+            alibi_slopes=None, sink=None, batches=None, heads=None, prefix=None, atten_mask=None):
     """Attention forward.  Returns O [T_q, Nq, D], softmax max m [T_q, Nq] and
     softmax sum l [T_q, Nq] (fp64).  With `batches` / `heads`, only those
     sequences / query heads are computed and every other entry is NaN."""
     pr = _problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob,
-                  sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix)
+                  sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix, atten_mask)
     tq, d = pr.q.shape[0], pr.v.shape[2]
     out = np.full((tq, pr.nq, d), np.nan)
     mx = np.full((tq, pr.nq), np.nan)
@@ -186,14 +194,14 @@ def forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, kee
 
 def backward(q, k, v, dy, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob=1.0,
              sparse_mode=0, pre_tokens=INT_MAX_TOKENS, next_tokens=INT_MAX_TOKENS, drop_mask=None,
-             alibi_slopes=None, sink=None, batches=None, heads=None, prefix=None):
+             alibi_slopes=None, sink=None, batches=None, heads=None, prefix=None, atten_mask=None):
     """Attention backward.  Returns dQ [T_q, Nq, D], dK, dV [T_kv, Nkv, D] and
     dSink [Nq] (None without a sink).  With `batches` / `heads`, only those
     sequences / query heads contribute: rows and keys of other sequences are NaN,
     dK/dV of a kv head are complete only if all of its query heads are chosen,
     and dSink sums the chosen sequences."""
     pr = _problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob,
-                  sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix)
+                  sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix, atten_mask)
     dy = np.asarray(dy)
     dq = np.full(pr.q.shape, np.nan)
     dk = np.full(pr.k.shape, np.nan)

@@ -67,7 +67,6 @@ INVALID_CONFIGS = {
     "too_many_heads": dict(head_num=512, kv_heads=512),
     "keep_zero": dict(keep_prob=0.0),
     "keep_above_one": dict(keep_prob=1.5),
-    "mode_1": dict(sparse_mode=1),
     "mode_5": dict(sparse_mode=5),
     "mode_7": dict(sparse_mode=7),
     "mode_8": dict(sparse_mode=8),
@@ -141,6 +140,32 @@ def test_prefix_mode_validation():
     assert size(_cfg(sparse_mode=6, cu_seqlens_q=cu[:1025], cu_seqlens_kv=cu[:1025], prefix=np.ones(1024))) == fa.FA_OK
     assert size(_cfg(sparse_mode=6, cu_seqlens_q=cu, cu_seqlens_kv=cu, prefix=np.ones(1025))) == fa.FA_ERR_PARAM_INVALID
     assert size(_cfg(sparse_mode=3, prefix=[100, 100])) == fa.FA_OK
+
+
+def test_atten_mask_validation():
+    n = ctypes.c_uint64(0)
+
+    def size(cfg):
+        return fa.lib().fa_fwd_workspace_size(cfg.ref, ctypes.byref(n))
+
+    # mode 1 (allMask) needs the mask
+    assert _fwd(_cfg(sparse_mode=1)) == fa.FA_ERR_PARAM_NULLPTR
+    assert _bwd(_cfg(sparse_mode=1)) == fa.FA_ERR_PARAM_NULLPTR
+
+    def masked(mode, rows, cols):
+        cfg = _cfg(sparse_mode=mode)
+        cfg.c.atten_mask = 0x20000          # never dereferenced by the size query
+        cfg.c.mask_rows, cfg.c.mask_cols = rows, cols
+        return cfg
+
+    # [S1Max, S2Max] must cover every sequence (lengths 5 and 7 here)
+    base = fa.fa_fwd_workspace_size(_cfg(sparse_mode=0))
+    for mode in (0, 1, 4):
+        assert size(masked(mode, 7, 7)) == fa.FA_OK and n.value >= base + 7 * 4, mode
+        assert size(masked(mode, 6, 7)) == fa.FA_ERR_PARAM_INVALID
+        assert size(masked(mode, 7, 6)) == fa.FA_ERR_PARAM_INVALID
+    # modes with their own triangle take no mask workspace
+    assert size(masked(3, 2, 2)) == fa.FA_OK and n.value == fa.fa_fwd_workspace_size(_cfg(sparse_mode=3))
 
 
 def test_alignment_alibi_and_workspace_rules():

@@ -39,6 +39,13 @@ EDGE_CASES = {
                                       prefix=[0, 67, 299], keep_prob=0.8, sink=True),
     "prefix_alibi": dict(lens_q=[150, 300], head_num=4, kv_heads=1, head_dim=128, sparse_mode=6,
                          prefix=[30, 129], alibi=True),
+    # attenMask [S1Max, S2Max] (1 = masked out), shared by the sequences at their local indices
+    "mask_mode1_varlen": dict(lens_q=[200, 77, 129], lens_kv=[130, 300, 129], head_num=4, kv_heads=2,
+                              head_dim=128, sparse_mode=1, mask=(0.3, [5, 100])),
+    "mask_band_drop_sink": dict(lens_q=[190, 67], head_num=2, kv_heads=1, head_dim=64, sparse_mode=4,
+                                pre_tokens=50, next_tokens=3, keep_prob=0.8, sink=True, mask=(0.2, [])),
+    "mask_mode0_alibi_gqa": dict(lens_q=[150, 300], head_num=4, kv_heads=1, head_dim=128, sparse_mode=0,
+                                 alibi=True, mask=(0.5, [7])),
 }
 
 
@@ -46,6 +53,9 @@ def _edge(name, dtype, seed):
     kw = dict(EDGE_CASES[name])
     lq = kw.pop("lens_q")
     lkv = kw.pop("lens_kv", None)
+    if "mask" in kw:
+        p_masked, full_rows = kw.pop("mask")
+        kw["atten_mask"] = wl.random_atten_mask(seed, max(lq), max(lkv or lq), p_masked, full_rows)
     return wl.make_case(name, lq, lkv, dtype=dtype, seed=seed, **kw)
 
 

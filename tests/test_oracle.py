@@ -172,6 +172,20 @@ def test_sdpa_prefix_mask(lq, lkv, n):
     np.testing.assert_allclose(o[rows], ref[rows], rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("lq,lkv", [(13, 13), (9, 20), (20, 9)])
+def test_sdpa_atten_mask(lq, lkv):
+    # mode 1 (allMask): the attenMask alone decides; 1 = masked out
+    d = 8
+    q, k, v = _rand(60 + lq, lq, 2, d), _rand(61 + lq, lkv, 2, d), _rand(62 + lq, lkv, 2, d)
+    mask = wl.random_atten_mask(lq + lkv, 24, 24, 0.4, full_rows=[3])
+    o, _, _ = oracle.forward(q, k, v, [0, lq], [0, lkv], 2, 2, 0.3, sparse_mode=1, atten_mask=mask)
+    keep = torch.from_numpy(mask[:lq, :lkv] == 0)
+    ref = _sdpa(q, k, v, 0.3, attn_mask=keep)
+    rows = keep.any(dim=1).numpy()
+    np.testing.assert_allclose(o[rows], ref[rows], rtol=1e-12, atol=1e-13)
+    assert np.all(o[~rows] == 0)
+
+
 def test_sdpa_gqa_and_band_mask():
     lq, d = 23, 8
     q, k, v = _rand(18, lq, 6, d), _rand(19, lq, 2, d), _rand(20, lq, 2, d)
@@ -247,6 +261,27 @@ def test_mode_equivalences():
         base, rtol=1e-15, atol=0)
     np.testing.assert_array_equal(
         oracle.forward(q, k, v, cu, cu, 2, 2, 0.5, sparse_mode=3, alibi_slopes=np.zeros(2, np.float32))[0], base)
+    # attenMask: all zeros == no mask (modes 0 and 1); a strict upper triangle in mode 1 ==
+    # leftUpCausal for every sequence (the mask is indexed at each sequence's local rows / keys);
+    # in mode 4 the band and the mask both apply
+    lens = [7, 12]
+    cu3 = _cu(lens)
+    q3, k3, v3, dy3 = (_rand(70 + t, cu3[-1], 2, d) for t in range(4))
+    zeros = np.zeros((12, 12), np.uint8)
+    upper = np.triu(np.ones((12, 12), np.uint8), 1)
+    ref0 = oracle.forward(q3, k3, v3, cu3, cu3, 2, 2, 0.5)
+    for mode in (0, 1):
+        for x, y in zip(oracle.forward(q3, k3, v3, cu3, cu3, 2, 2, 0.5, sparse_mode=mode, atten_mask=zeros), ref0):
+            np.testing.assert_array_equal(x, y)
+    for x, y in zip(oracle.forward(q3, k3, v3, cu3, cu3, 2, 2, 0.5, sparse_mode=1, atten_mask=upper),
+                    oracle.forward(q3, k3, v3, cu3, cu3, 2, 2, 0.5, sparse_mode=2)):
+        np.testing.assert_array_equal(x, y)
+    ga = oracle.backward(q3, k3, v3, dy3, cu3, cu3, 2, 2, 0.5, sparse_mode=1, atten_mask=upper)
+    gb = oracle.backward(q3, k3, v3, dy3, cu3, cu3, 2, 2, 0.5, sparse_mode=2)
+    for x, y in zip(ga[:3], gb[:3]):
+        np.testing.assert_array_equal(x, y)
+    band = oracle.allowed(12, 12, 4, 3, 1)
+    np.testing.assert_array_equal(oracle.allowed(12, 12, 4, 3, 1, atten_mask=upper), band & (upper == 0))
     # prefix N = Lkv - Lq == rightDownCausal; N = Lkv == no mask (rectangular sequences)
     lq2, lkv2 = 9, 17
     q2, k2, v2, dy2 = _rand(35, lq2, 2, d), _rand(36, lkv2, 2, d), _rand(37, lkv2, 2, d), _rand(38, lq2, 2, d)
@@ -313,7 +348,8 @@ def test_dv_is_pt_transpose_dy():
 
 # --------------------------------------------------------------------------- autograd + finite differences
 
-def _torch_attention(q, k, v, sink, cu_q, cu_kv, nq, nkv, scale, mode, pre, nxt, keep, bits, slopes, prefix=None):
+def _torch_attention(q, k, v, sink, cu_q, cu_kv, nq, nkv, scale, mode, pre, nxt, keep, bits, slopes, prefix=None,
+                     atten_mask=None):
     """A second, plainly written attention in torch: the sink enters as an extra
     softmax column that is dropped afterwards; masks come from tril/triu."""
     outs = []
@@ -339,6 +375,8 @@ def _torch_attention(q, k, v, sink, cu_q, cu_kv, nq, nkv, scale, mode, pre, nxt,
             elif mode == 6:
                 ok = ones.tril(lkv - lq)
                 ok[:, :int(prefix[b])] = True
+            elif mode == 1:
+                ok = torch.from_numpy(atten_mask[:lq, :lkv] == 0)
             else:
                 ok = ones.tril(lkv - lq + nxt) & ones.triu(lkv - lq - pre)
             s = s.masked_fill(~ok, float("-inf"))
@@ -374,7 +412,7 @@ def _feature_case(seed, d=4):
                 mask=mask)
 
 
-@pytest.mark.parametrize("mode,pre,nxt", [(3, 0, 0), (4, 2, 1), (0, 0, 0), (6, 0, 0)])
+@pytest.mark.parametrize("mode,pre,nxt", [(3, 0, 0), (4, 2, 1), (0, 0, 0), (6, 0, 0), (1, 0, 0)])
 def test_backward_matches_autograd(mode, pre, nxt):
     c = _feature_case(50 + mode)
     scale = 0.45
@@ -384,11 +422,12 @@ def test_backward_matches_autograd(mode, pre, nxt):
     ts = torch.tensor(c["sink"].astype(np.float64), requires_grad=True)
     bits = np.unpackbits(c["mask"], bitorder="little")
     prefix = [2, 5] if mode == 6 else None   # sequence lengths 6 and 9: N in [0, L]
+    amask = wl.random_atten_mask(9, 9, 9, 0.3, full_rows=[4]) if mode == 1 else None
     out = _torch_attention(tq, tk, tv, ts, c["cq"], c["ck"], c["nq"], c["nkv"], scale, mode, pre, nxt,
-                           c["keep"], bits, c["slopes"], prefix)
+                           c["keep"], bits, c["slopes"], prefix, amask)
     (out * torch.from_numpy(c["dy"])).sum().backward()
     kw = dict(sparse_mode=mode, pre_tokens=pre, next_tokens=nxt, keep_prob=c["keep"], drop_mask=c["mask"],
-              alibi_slopes=c["slopes"], sink=c["sink"], prefix=prefix)
+              alibi_slopes=c["slopes"], sink=c["sink"], prefix=prefix, atten_mask=amask)
     o, _, _ = oracle.forward(c["q"], c["k"], c["v"], c["cq"], c["ck"], c["nq"], c["nkv"], scale, **kw)
     np.testing.assert_allclose(o, out.detach().numpy(), rtol=1e-12, atol=1e-13)
     dq, dk, dv, ds = oracle.backward(c["q"], c["k"], c["v"], c["dy"], c["cq"], c["ck"], c["nq"], c["nkv"],

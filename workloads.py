@@ -35,6 +35,7 @@ MODE_LEFT_UP_CAUSAL = 2
 MODE_RIGHT_DOWN_CAUSAL = 3
 MODE_BAND = 4
 MODE_PREFIX = 6
+MODE_ALL_MASK = 1
 
 
 @dataclass
@@ -60,6 +61,7 @@ class Case:
     alibi_slopes: Optional[np.ndarray] = None  # float32 [Nq]
     sink: Optional[np.ndarray] = None          # float32 [Nq]
     prefix: Optional[np.ndarray] = None        # int64 [B]: prefix N per sequence (sparse mode 6)
+    atten_mask: Optional[np.ndarray] = None    # uint8 [S1Max, S2Max], nonzero = masked (modes 0/1/4)
     meta: dict = field(default_factory=dict)
 
     @property
@@ -144,7 +146,7 @@ def lognormal_lengths(seed, total: int, batch: int, median: float, lo: int, hi: 
 def make_case(name, lens_q, lens_kv=None, *, head_num, kv_heads, head_dim, dtype=torch.bfloat16,
               scale=None, keep_prob=1.0, sparse_mode=MODE_NONE, pre_tokens=INT_MAX_TOKENS,
               next_tokens=INT_MAX_TOKENS, alibi=False, sink=False, seed=0, dy_mult=1.0,
-              drop_mask=None, prefix=None) -> Case:
+              drop_mask=None, prefix=None, atten_mask=None) -> Case:
     """A case built from explicit lengths; every tensor is drawn from default_rng([seed, t])."""
     lens_q = np.asarray(lens_q, dtype=np.int64)
     lens_kv = lens_q.copy() if lens_kv is None else np.asarray(lens_kv, dtype=np.int64)
@@ -166,7 +168,17 @@ def make_case(name, lens_q, lens_kv=None, *, head_num, kv_heads, head_dim, dtype
                 keep_prob=float(keep_prob), sparse_mode=sparse_mode, pre_tokens=int(pre_tokens),
                 next_tokens=int(next_tokens), drop_mask=drop_mask,
                 alibi_slopes=alibi_slopes(head_num) if alibi else None, sink=sink_v,
-                prefix=None if prefix is None else np.asarray(prefix, dtype=np.int64))
+                prefix=None if prefix is None else np.asarray(prefix, dtype=np.int64),
+                atten_mask=None if atten_mask is None else np.ascontiguousarray(atten_mask, dtype=np.uint8))
+
+
+def random_atten_mask(seed, rows: int, cols: int, p_masked: float, full_rows=()) -> np.ndarray:
+    """uint8 [rows, cols] attenMask with each pair masked (1) with probability
+    p_masked, and the listed rows masked entirely."""
+    m = (np.random.default_rng([seed, 7]).random((rows, cols)) < p_masked).astype(np.uint8)
+    for r in full_rows:
+        m[r, :] = 1
+    return m
 
 
 WORKLOAD_NAMES = {
