@@ -26,6 +26,7 @@ FA_ERR_HIP = 2
 
 FA_DTYPE_FP32 = 0
 FA_DTYPE_BF16 = 1
+FA_DTYPE_FP16 = 2
 TOKENS_DEFAULT = 2147483647
 
 EXPORTED = ("fa_fwd_workspace_size", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd", "fa_status_string",
@@ -113,7 +114,8 @@ class Config:
             if atten_mask.dim() != 2 or atten_mask.dtype not in (torch.uint8, torch.bool) or not atten_mask.is_contiguous():
                 raise ValueError("atten_mask must be a contiguous 2-D bool or uint8 tensor [S1Max, S2Max]")
         if isinstance(dtype, torch.dtype):
-            dtype = {torch.float32: FA_DTYPE_FP32, torch.bfloat16: FA_DTYPE_BF16}.get(dtype, -1)
+            dtype = {torch.float32: FA_DTYPE_FP32, torch.bfloat16: FA_DTYPE_BF16,
+                     torch.float16: FA_DTYPE_FP16}.get(dtype, -1)
         self.c = FaConfig(
             batch=len(self.cu_q) - 1,
             cu_seqlens_q=self.cu_q.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)),

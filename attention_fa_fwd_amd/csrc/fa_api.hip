@@ -44,7 +44,8 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   const int64_t nkv = cfg->num_kv_heads == 0 ? cfg->head_num : cfg->num_kv_heads;
   if (nkv < 1 || cfg->head_num % nkv != 0) return FA_ERR_PARAM_INVALID;
   if (cfg->head_dim != 64 && cfg->head_dim != 128) return FA_ERR_PARAM_INVALID;
-  if (cfg->dtype != FA_DTYPE_FP32 && cfg->dtype != FA_DTYPE_BF16) return FA_ERR_PARAM_INVALID;
+  if (cfg->dtype != FA_DTYPE_FP32 && cfg->dtype != FA_DTYPE_BF16 && cfg->dtype != FA_DTYPE_FP16)
+    return FA_ERR_PARAM_INVALID;
   const int mode = cfg->sparse_mode;
   if (mode != FA_SPARSE_NONE && mode != FA_SPARSE_ALL_MASK && mode != FA_SPARSE_LEFT_UP_CAUSAL &&
       mode != FA_SPARSE_RIGHT_DOWN_CAUSAL && mode != FA_SPARSE_BAND && mode != FA_SPARSE_PREFIX)
@@ -68,7 +69,7 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   pr->keep = cfg->keep_prob;
   pr->pre = cfg->pre_tokens;
   pr->next = cfg->next_tokens;
-  // The fp32-atomic dQ variant is built for bf16 and for fp32 with D = 64; fp32 with
+  // The fp32-atomic dQ variant is built for bf16, fp16 and for fp32 with D = 64; fp32 with
   // D = 128 runs the deterministic passes, whose result is one of the results the
   // non-deterministic mode allows.
   pr->deterministic = cfg->deterministic != 0 || (cfg->dtype == FA_DTYPE_FP32 && cfg->head_dim == 128);
@@ -412,9 +413,9 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
   if (!workspace) return FA_ERR_PARAM_NULLPTR;
   if (workspace_bytes < bound.total) return FA_ERR_WORKSPACE;
 
-  // the atomic dK/dV kernel for bf16 D = 128 has no alibi variant (its registers
+  // the atomic dK/dV kernel for 16-bit D = 128 has no alibi variant (its registers
   // do not fit one): run the deterministic passes, which need less workspace
-  if (alibi_slopes && pr.dtype == FA_DTYPE_BF16 && pr.d == 128) pr.deterministic = true;
+  if (alibi_slopes && pr.dtype != FA_DTYPE_FP32 && pr.d == 128) pr.deterministic = true;
   // the attenMask is read by the deterministic passes only (the atomic kernels have no mask instances)
   if (pr.mask) pr.deterministic = true;
   std::vector<WorkItem> kv_items = schedule(pr, 1, nullptr, nullptr);

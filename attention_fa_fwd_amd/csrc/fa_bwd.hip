@@ -61,8 +61,8 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(BwdParams p) {
     if constexpr (EB == 2) {
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        acc += bf16_bits_to_f32((uint16_t)(a[w] & 0xffff)) * bf16_bits_to_f32((uint16_t)(c[w] & 0xffff));
-        acc += bf16_bits_to_f32((uint16_t)(a[w] >> 16)) * bf16_bits_to_f32((uint16_t)(c[w] >> 16));
+        acc += bits16_to_f32<T>((uint16_t)(a[w] & 0xffff)) * bits16_to_f32<T>((uint16_t)(c[w] & 0xffff));
+        acc += bits16_to_f32<T>((uint16_t)(a[w] >> 16)) * bits16_to_f32<T>((uint16_t)(c[w] >> 16));
       }
     } else {
 #pragma unroll
@@ -131,7 +131,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void fa_dq_convert_kernel(const float* acc, T* out, float scale, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
     if constexpr (sizeof(T) == 2)
-      out[i] = to_bf16(acc[i] * scale);
+      out[i] = cvt16<T>(acc[i] * scale);
     else
       out[i] = acc[i] * scale;
   }
@@ -142,7 +142,7 @@ template <typename T, int D>
 struct DqShape {
   static constexpr int EB = sizeof(T);
   static constexpr int RB = D * EB;
-  static constexpr bool kSwz = EB == 2;     // bf16 tiles swizzled and unpadded
+  static constexpr bool kSwz = EB == 2;     // 16-bit tiles swizzled and unpadded
   static constexpr int P = kSwz ? RB : RB + 16;
   static constexpr int TILE = kDqBN * P;
   static constexpr int STAGE = 2 * TILE;    // K | V
@@ -153,7 +153,10 @@ struct DqShape {
 template <typename T, int D, bool DROP, bool ALIBI, bool MASK>
 __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams p) {
   using S = DqShape<T, D>;
-  using Op = typename std::conditional<sizeof(T) == 2, bf16x8, float>::type;
+  using E = typename std::conditional<sizeof(T) == 2, T, __bf16>::type;   // 16-bit element type
+  using V8 = typename Vec16<E>::v8;
+  using V4 = typename Vec16<E>::v4;
+  using Op = typename std::conditional<sizeof(T) == 2, V8, float>::type;
   __shared__ __attribute__((aligned(16))) char st0[S::STAGE];
   __shared__ __attribute__((aligned(16))) char st1[S::STAGE];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -181,10 +184,10 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
 #pragma unroll
     for (int c = 0; c < S::NOP; ++c) {
       if constexpr (sizeof(T) == 2) {
-        bf16x8 a = *reinterpret_cast<const bf16x8*>(qp + 16 * c + 8 * hh);
-        bf16x8 d = *reinterpret_cast<const bf16x8*>(dp + 16 * c + 8 * hh);
-        qf[c] = row_ok ? a : bf16x8{};
-        df[c] = row_ok ? d : bf16x8{};
+        V8 a = *reinterpret_cast<const V8*>(qp + 16 * c + 8 * hh);
+        V8 d = *reinterpret_cast<const V8*>(dp + 16 * c + 8 * hh);
+        qf[c] = row_ok ? a : V8{};
+        df[c] = row_ok ? d : V8{};
       } else {
         qf[c] = row_ok ? qp[2 * c + hh] : 0.f;
         df[c] = row_ok ? dp[2 * c + hh] : 0.f;
@@ -203,7 +206,7 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
   const int64_t kv_stride = (int64_t)p.nkv * S::RB;
   const int a_lane = lrow * S::P + 16 * hh;
   const int t_lane = (4 * (grp >> 1) + (sl >> 2)) * S::P + (16 * (grp & 1) + 4 * (sl & 3)) * 2;
-  // swizzled bf16 tiles: row reads of chunk 2c + hh of row lrow (+32 per key
+  // swizzled 16-bit tiles: row reads of chunk 2c + hh of row lrow (+32 per key
   // block), transposing reads of rows rv and rv + 8 (+16 per step), chunk 4db + qv
   int koff[S::kSwz ? S::NOP : 1], toff[2][S::kSwz ? S::NDB : 1];
   if constexpr (S::kSwz) {
@@ -247,8 +250,8 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < S::NOP; ++c) {
-          const bf16x8 ka = lds_read_b128(ks + koff[c] + 32 * kb * S::RB);
-          const bf16x8 va = lds_read_b128(vs + koff[c] + 32 * kb * S::RB);
+          const V8 ka = lds_read_b128<V8>(ks + koff[c] + 32 * kb * S::RB);
+          const V8 va = lds_read_b128<V8>(vs + koff[c] + 32 * kb * S::RB);
           s = mfma32(ka, qf[c], s);
           dp = mfma32(va, df[c], dp);
         }
@@ -297,18 +300,18 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
       }
       // ---- dQ^T += K^T dS^T (A = K through the transposing read, B = dS from registers) ----
       if constexpr (sizeof(T) == 2) {
-        bf16x8 bs[2];
+        V8 bs[2];
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
-          for (int e = 0; e < 8; ++e) bs[c][e] = to_bf16(ds[8 * c + e]);
+          for (int e = 0; e < 8; ++e) bs[c][e] = cvt16<E>(ds[8 * c + e]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
           const char* base = ks + (32 * kb + 16 * c) * S::RB;
 #pragma unroll
           for (int db = 0; db < S::NDB; ++db)
-            acc[db] = mfma32(lds_read_tr_x2(base + toff[0][db], base + toff[1][db]), bs[c], acc[db]);
+            acc[db] = mfma32(lds_read_tr_x2<V8>(base + toff[0][db], base + toff[1][db]), bs[c], acc[db]);
         }
         __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
         sched_alternate<2 * S::NDB, 0x008, 0x100, 2>();
@@ -351,10 +354,10 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
       for (int a = 0; a < 4; ++a) {
         const int d = 32 * db + 8 * a + 4 * hh;
         if constexpr (sizeof(T) == 2) {
-          bf16x4 v;
+          V4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = to_bf16(acc[db][4 * a + e] * p.scale);
-          *reinterpret_cast<bf16x4*>(op + d) = v;
+          for (int e = 0; e < 4; ++e) v[e] = cvt16<E>(acc[db][4 * a + e] * p.scale);
+          *reinterpret_cast<V4*>(op + d) = v;
         } else {
           f32x4 v;
 #pragma unroll
@@ -388,6 +391,8 @@ hipError_t launch_bwd_pre(int dtype, int d, const BwdParams& p, hipStream_t s) {
   if (p.n_pre_blocks == 0) return hipSuccess;
   if (dtype == 1 && d == 128) return launch_pre_t<__bf16, 128>(p, s);
   if (dtype == 1 && d == 64) return launch_pre_t<__bf16, 64>(p, s);
+  if (dtype == 2 && d == 128) return launch_pre_t<_Float16, 128>(p, s);
+  if (dtype == 2 && d == 64) return launch_pre_t<_Float16, 64>(p, s);
   if (dtype == 0 && d == 128) return launch_pre_t<float, 128>(p, s);
   if (dtype == 0 && d == 64) return launch_pre_t<float, 64>(p, s);
   return hipErrorInvalidValue;
@@ -409,6 +414,8 @@ static hipError_t launch_dq_t(const BwdParams& p, hipStream_t s) {
 hipError_t launch_bwd_dq(int dtype, int d, const BwdParams& p, hipStream_t s) {
   if (dtype == 1 && d == 128) return launch_dq_t<__bf16, 128>(p, s);
   if (dtype == 1 && d == 64) return launch_dq_t<__bf16, 64>(p, s);
+  if (dtype == 2 && d == 128) return launch_dq_t<_Float16, 128>(p, s);
+  if (dtype == 2 && d == 64) return launch_dq_t<_Float16, 64>(p, s);
   if (dtype == 0 && d == 128) return launch_dq_t<float, 128>(p, s);
   if (dtype == 0 && d == 64) return launch_dq_t<float, 64>(p, s);
   return hipErrorInvalidValue;
@@ -419,6 +426,9 @@ hipError_t launch_bwd_dq_convert(int dtype, int d, const BwdParams& p, hipStream
   if (dtype == 1)
     hipLaunchKernelGGL((fa_dq_convert_kernel<__bf16>), dim3(grid_for(n)), dim3(256), 0, s, p.dq_acc,
                        reinterpret_cast<__bf16*>(p.dq), p.scale, n);
+  else if (dtype == 2)
+    hipLaunchKernelGGL((fa_dq_convert_kernel<_Float16>), dim3(grid_for(n)), dim3(256), 0, s, p.dq_acc,
+                       reinterpret_cast<_Float16*>(p.dq), p.scale, n);
   else
     hipLaunchKernelGGL((fa_dq_convert_kernel<float>), dim3(grid_for(n)), dim3(256), 0, s, p.dq_acc,
                        reinterpret_cast<float*>(p.dq), p.scale, n);

@@ -8,7 +8,7 @@
 // registers across the whole group (no atomics).
 //   fa_bwd_kv_kernel       one wave per 32-key group; fp32, and the atomic-dQ
 //                          variant (fa_bwd_kv_atomic.hip, MFMA results in VGPRs)
-//   fa_bwd_kv_pair_kernel  bf16 deterministic: two waves per 32-key group that
+//   fa_bwd_kv_pair_kernel  16-bit deterministic: two waves per 32-key group that
 //                          split the rows of S / dP and the columns of dK / dV
 // The deterministic instances (fa_bwd_kv.hip) are compiled with the compiler's
 // own MFMA register placement.
@@ -26,7 +26,7 @@ template <typename T, int D>
 struct KvShape {
   static constexpr int EB = sizeof(T);
   static constexpr int RB = D * EB;
-  // bf16 Q / dY tiles are swizzled and unpadded (see tile_swz); fp32 tiles and
+  // 16-bit Q / dY tiles are swizzled and unpadded (see tile_swz); fp32 tiles and
   // the K tile of the atomic variant use padded rows
   static constexpr bool kSwz = EB == 2;
   static constexpr int P = kSwz ? RB : RB + 16;     // LDS pitch of Q / dY rows
@@ -49,7 +49,10 @@ struct KvShape {
 template <typename T, int D, bool ATOMIC, bool DROP, bool ALIBI, bool MASK>
 __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
   using S = KvShape<T, D>;
-  using Op = typename std::conditional<sizeof(T) == 2, bf16x8, float>::type;
+  using E = typename std::conditional<sizeof(T) == 2, T, __bf16>::type;   // 16-bit element type
+  using V8 = typename Vec16<E>::v8;
+  using V4 = typename Vec16<E>::v4;
+  using Op = typename std::conditional<sizeof(T) == 2, V8, float>::type;
   __shared__ __attribute__((aligned(16))) char st0[S::STAGE];
   __shared__ __attribute__((aligned(16))) char st1[S::STAGE];
   __shared__ __attribute__((aligned(16))) char kt[ATOMIC ? S::KT : 16];
@@ -80,10 +83,10 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
 #pragma unroll
     for (int c = 0; c < S::NOP; ++c) {
       if constexpr (sizeof(T) == 2) {
-        bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + 16 * c + 8 * hh);
-        bf16x8 v = *reinterpret_cast<const bf16x8*>(vp + 16 * c + 8 * hh);
-        kf[c] = key_ok ? a : bf16x8{};
-        vf[c] = key_ok ? v : bf16x8{};
+        V8 a = *reinterpret_cast<const V8*>(kp + 16 * c + 8 * hh);
+        V8 v = *reinterpret_cast<const V8*>(vp + 16 * c + 8 * hh);
+        kf[c] = key_ok ? a : V8{};
+        vf[c] = key_ok ? v : V8{};
       } else {
         kf[c] = key_ok ? kp[2 * c + hh] : 0.f;
         vf[c] = key_ok ? vp[2 * c + hh] : 0.f;
@@ -108,8 +111,8 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
     if constexpr (sizeof(T) == 2) {
       // zeros produced by an MFMA, so the accumulators start in the register
       // class of the MFMAs that update them
-      dk[db] = mfma32(bf16x8{}, bf16x8{}, f32x16{});
-      dv[db] = mfma32(bf16x8{}, bf16x8{}, f32x16{});
+      dk[db] = mfma32(V8{}, V8{}, f32x16{});
+      dv[db] = mfma32(V8{}, V8{}, f32x16{});
     } else {
       dk[db] = f32x16{};
       dv[db] = f32x16{};
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
   // per-lane LDS offsets: A-operand row reads and transposing B-operand reads
   const int a_lane = lrow * S::P + 16 * hh;
   const int t_lane = (4 * (grp >> 1) + (sl >> 2)) * S::P + (16 * (grp & 1) + 4 * (sl & 3)) * 2;
-  // swizzled bf16 tiles: row reads of chunk 2c + hh of row lrow (+32 per row
+  // swizzled 16-bit tiles: row reads of chunk 2c + hh of row lrow (+32 per row
   // block), transposing reads of rows rv and rv + 8 (+16 per step), chunk 4db + qv
   int qoff[S::kSwz ? S::NOP : 1], toff[2][S::kSwz ? S::NDB : 1];
   if constexpr (S::kSwz) {
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
     return p.mbits[(int64_t)(r0 + r) * p.mwords + w];
   };
 
-  // atomic dQ of one bf16 step: store_ds() puts each block's dS^T into LDS right
+  // atomic dQ of one 16-bit step: store_ds() puts each block's dS^T into LDS right
   // after it is formed; atomic_dq() then adds dQ(64 rows x 32-wide d block of this
   // wave) += dS K over the 128 keys to the fp32 accumulator
   auto store_ds = [&](int rb, const auto& d) {
@@ -194,10 +197,10 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
     for (int c = 0; c < 2; ++c)
 #pragma unroll
       for (int t2 = 0; t2 < 2; ++t2) {
-        bf16x4 v;
+        V4 v;
 #pragma unroll
         for (int e = 0; e < 4; ++e) v[e] = d[c][4 * t2 + e];
-        *reinterpret_cast<bf16x4*>(dst + (32 * wave + lrow) * S::DSP + (32 * rb + 16 * c + 8 * t2 + 4 * hh) * 2) = v;
+        *reinterpret_cast<V4*>(dst + (32 * wave + lrow) * S::DSP + (32 * rb + 16 * c + 8 * t2 + 4 * hh) * 2) = v;
       }
   };
   auto atomic_dq = [&](auto n) {
@@ -210,10 +213,10 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
       for (int kc = 0; kc < kKvBN / 16; ++kc) {
         const int krow = 16 * kc + 4 * (grp >> 1) + (sl >> 2);
         const int coln = (16 * (grp & 1) + 4 * (sl & 3)) * 2;
-        const bf16x8 a0 = lds_read_tr_x2(dst + krow * S::DSP + coln, dst + (krow + 8) * S::DSP + coln);
-        const bf16x8 a1 = lds_read_tr_x2(dst + krow * S::DSP + coln + 64, dst + (krow + 8) * S::DSP + coln + 64);
+        const V8 a0 = lds_read_tr_x2<V8>(dst + krow * S::DSP + coln, dst + (krow + 8) * S::DSP + coln);
+        const V8 a1 = lds_read_tr_x2<V8>(dst + krow * S::DSP + coln + 64, dst + (krow + 8) * S::DSP + coln + 64);
         const int colk = (dcol + 16 * (grp & 1) + 4 * (sl & 3)) * 2;
-        const bf16x8 bo = lds_read_tr_x2(kt + krow * S::KTP + colk, kt + (krow + 8) * S::KTP + colk);
+        const V8 bo = lds_read_tr_x2<V8>(kt + krow * S::KTP + colk, kt + (krow + 8) * S::KTP + colk);
         acc[0] = mfma32(a0, bo, acc[0]);
         acc[1] = mfma32(a1, bo, acc[1]);
       }
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
         }
     }
   };
-  // ---- bf16 steps: per 32-row block [S, dP MFMAs] [P, dS] [dV, dK MFMAs] ----
+  // ---- 16-bit steps: per 32-row block [S, dP MFMAs] [P, dS] [dV, dK MFMAs] ----
   // Scheduling-group barriers keep the LDS operand reads of each MFMA group a
   // few MFMAs ahead of their use.  Blocks outside the mask are computed like
   // masked ones (every probability is zero): the waves of a workgroup wait for
@@ -238,15 +241,15 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
     dp = f32x16{};
 #pragma unroll
     for (int c = 0; c < S::NOP; ++c) {
-      const bf16x8 qa = lds_read_b128(st + qoff[c] + 32 * rb * S::RB);
-      const bf16x8 ya = lds_read_b128(st + S::OFF_DY + qoff[c] + 32 * rb * S::RB);
+      const V8 qa = lds_read_b128<V8>(st + qoff[c] + 32 * rb * S::RB);
+      const V8 ya = lds_read_b128<V8>(st + S::OFF_DY + qoff[c] + 32 * rb * S::RB);
       s = mfma32(qa, kf[c], s);
       dp = mfma32(ya, vf[c], dp);
     }
   };
-  // P~ and dS of one block as bf16 A operands (lane = key, registers = rows)
+  // P~ and dS of one block as 16-bit A operands (lane = key, registers = rows)
   auto elem = [&](auto full_c, const char* st, int r0, int rb, const f32x16& s, const f32x16& dp, float slope_l2,
-                  bf16x8 (&pa)[2], bf16x8 (&da)[2]) {
+                  V8 (&pa)[2], V8 (&da)[2]) {
     constexpr bool plain = !ALIBI && decltype(full_c)::value;
     const float* lse_s = reinterpret_cast<const float*>(st + S::OFF_LSE);
     const float* del_s = reinterpret_cast<const float*>(st + S::OFF_DEL);
@@ -285,8 +288,8 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
           ptv = keep ? pr * p.inv_keep : 0.f;
         }
         const float dsv = pr * (dpv - del4[e]);
-        pa[r >> 3][r & 7] = to_bf16(ptv);
-        da[r >> 3][r & 7] = to_bf16(dsv);
+        pa[r >> 3][r & 7] = cvt16<E>(ptv);
+        da[r >> 3][r & 7] = cvt16<E>(dsv);
       }
     }
   };
@@ -297,8 +300,8 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
       const char* base = st + (32 * rb + 16 * c) * S::RB;
 #pragma unroll
       for (int db = 0; db < S::NDB; ++db) {
-        const bf16x8 yo = lds_read_tr_x2(base + S::OFF_DY + toff[0][db], base + S::OFF_DY + toff[1][db]);
-        const bf16x8 qo = lds_read_tr_x2(base + toff[0][db], base + toff[1][db]);
+        const V8 yo = lds_read_tr_x2<V8>(base + S::OFF_DY + toff[0][db], base + S::OFF_DY + toff[1][db]);
+        const V8 qo = lds_read_tr_x2<V8>(base + toff[0][db], base + toff[1][db]);
         dv[db] = mfma32(pa[c], yo, dv[db]);
         dk[db] = mfma32(da[c], qo, dk[db]);
       }
@@ -306,14 +309,14 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
   };
   constexpr int kSdpMfma = 2 * S::NOP, kGradMfma = 4 * S::NDB;
 
-  auto compute_bf16 = [&](const char* st, auto n) {
+  auto compute_16 = [&](const char* st, auto n) {
     const int h = step_head(n), r0 = step_row0(n);
     const float slope_l2 = ALIBI ? p.slopes[h] * kLog2e : 0.f;
     // with an attenMask every block takes the masked path
     const bool full0 = fa_tile_full(win, r0, 32, wc0, 32, lq, lkv) && !MASK;
     const bool full1 = fa_tile_full(win, r0 + 32, 32, wc0, 32, lq, lkv) && !MASK;
     f32x16 s0, dp0, s1, dp1;
-    bf16x8 pa0[2], da0[2], pa1[2], da1[2];
+    V8 pa0[2], da0[2], pa1[2], da1[2];
     auto block = [&](int rb, bool full, auto& sx, auto& dpx, auto& pax, auto& dax) {
       __builtin_amdgcn_sched_barrier(0);
       sdp(st, rb, sx, dpx);
@@ -340,28 +343,28 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
     const float* lse_s = reinterpret_cast<const float*>(st + S::OFF_LSE);
     const float* del_s = reinterpret_cast<const float*>(st + S::OFF_DEL);
     const uint32_t* bits_s = reinterpret_cast<const uint32_t*>(st + S::OFF_BITS);
-    bf16x8 da_keep[2][2];   // dS of both row blocks (atomic dQ)
+    V8 da_keep[2][2];   // dS of both row blocks (atomic dQ)
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       const int rb0 = r0 + 32 * rb;
       bool empty = rb0 >= lq || wc0 >= lkv;
       if (!empty) empty = fa_tile_empty(win, rb0, min(rb0 + 32, lq), wc0, min(wc0 + 32, lkv));
       if constexpr (ATOMIC && sizeof(T) == 2) {
-        da_keep[rb][0] = bf16x8{};
-        da_keep[rb][1] = bf16x8{};
+        da_keep[rb][0] = V8{};
+        da_keep[rb][1] = V8{};
       }
       if (empty) continue;
       const bool full = fa_tile_full(win, rb0, 32, wc0, 32, lq, lkv) && !MASK;
       // ---- S = Q K^T and dP~ = dY V^T (lane = key, registers = rows) ----
       f32x16 s = f32x16{}, dp = f32x16{};
       if constexpr (sizeof(T) == 2) {
-        bf16x8 qa[S::NOP];
+        V8 qa[S::NOP];
 #pragma unroll
-        for (int c = 0; c < S::NOP; ++c) qa[c] = lds_read_b128(st + a_lane + 32 * rb * S::P + 32 * c);
+        for (int c = 0; c < S::NOP; ++c) qa[c] = lds_read_b128<V8>(st + a_lane + 32 * rb * S::P + 32 * c);
 #pragma unroll
         for (int c = 0; c < S::NOP; ++c) s = mfma32(qa[c], kf[c], s);
 #pragma unroll
-        for (int c = 0; c < S::NOP; ++c) qa[c] = lds_read_b128(st + S::OFF_DY + a_lane + 32 * rb * S::P + 32 * c);
+        for (int c = 0; c < S::NOP; ++c) qa[c] = lds_read_b128<V8>(st + S::OFF_DY + a_lane + 32 * rb * S::P + 32 * c);
 #pragma unroll
         for (int c = 0; c < S::NOP; ++c) dp = mfma32(qa[c], vf[c], dp);
       } else {
@@ -396,19 +399,19 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
       if constexpr (sizeof(T) == 2) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-          bf16x8 pa, da;
+          V8 pa, da;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            pa[e] = to_bf16(pt[8 * c + e]);
-            da[e] = to_bf16(ds[8 * c + e]);
+            pa[e] = cvt16<E>(pt[8 * c + e]);
+            da[e] = cvt16<E>(ds[8 * c + e]);
           }
           if constexpr (ATOMIC) da_keep[rb][c] = da;
           const char* base = st + t_lane + (32 * rb + 16 * c) * S::P;
-          bf16x8 dyo[S::NDB], qo[S::NDB];
+          V8 dyo[S::NDB], qo[S::NDB];
 #pragma unroll
           for (int db = 0; db < S::NDB; ++db) {
-            dyo[db] = lds_read_tr_x2(base + S::OFF_DY + 64 * db, base + S::OFF_DY + 8 * S::P + 64 * db);
-            qo[db] = lds_read_tr_x2(base + 64 * db, base + 8 * S::P + 64 * db);
+            dyo[db] = lds_read_tr_x2<V8>(base + S::OFF_DY + 64 * db, base + S::OFF_DY + 8 * S::P + 64 * db);
+            qo[db] = lds_read_tr_x2<V8>(base + 64 * db, base + 8 * S::P + 64 * db);
           }
 #pragma unroll
           for (int db = 0; db < S::NDB; ++db) {
@@ -447,17 +450,17 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
     }
     if constexpr (ATOMIC) {
       if constexpr (sizeof(T) == 2) {
-        // dS^T[key][row] from the kept bf16 operands: register 8c + 4t + e holds row 16c + 8t + 4hh + e
+        // dS^T[key][row] from the kept 16-bit operands: register 8c + 4t + e holds row 16c + 8t + 4hh + e
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
           for (int c = 0; c < 2; ++c)
 #pragma unroll
             for (int t2 = 0; t2 < 2; ++t2) {
-              bf16x4 v;
+              V4 v;
 #pragma unroll
               for (int e = 0; e < 4; ++e) v[e] = da_keep[rb][c][4 * t2 + e];
-              *reinterpret_cast<bf16x4*>(dst + (32 * wave + lrow) * S::DSP +
+              *reinterpret_cast<V4*>(dst + (32 * wave + lrow) * S::DSP +
                                          (32 * rb + 16 * c + 8 * t2 + 4 * hh) * 2) = v;
             }
       } else {
@@ -484,10 +487,10 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
           for (int kc = 0; kc < kKvBN / 16; ++kc) {
             const int krow = 16 * kc + 4 * (grp >> 1) + (sl >> 2);
             const int coln = (16 * (grp & 1) + 4 * (sl & 3)) * 2;
-            const bf16x8 a0 = lds_read_tr_x2(dst + krow * S::DSP + coln, dst + (krow + 8) * S::DSP + coln);
-            const bf16x8 a1 = lds_read_tr_x2(dst + krow * S::DSP + coln + 64, dst + (krow + 8) * S::DSP + coln + 64);
+            const V8 a0 = lds_read_tr_x2<V8>(dst + krow * S::DSP + coln, dst + (krow + 8) * S::DSP + coln);
+            const V8 a1 = lds_read_tr_x2<V8>(dst + krow * S::DSP + coln + 64, dst + (krow + 8) * S::DSP + coln + 64);
             const int colk = (dcol + 16 * (grp & 1) + 4 * (sl & 3)) * 2;
-            const bf16x8 bo = lds_read_tr_x2(kt + krow * S::KTP + colk, kt + (krow + 8) * S::KTP + colk);
+            const V8 bo = lds_read_tr_x2<V8>(kt + krow * S::KTP + colk, kt + (krow + 8) * S::KTP + colk);
             acc[0] = mfma32(a0, bo, acc[0]);
             acc[1] = mfma32(a1, bo, acc[1]);
           }
@@ -528,7 +531,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
       if constexpr (DROP) word = bits_word(n + 1);
       if constexpr (MASK) mword = mask_word(n + 1);
     }
-    if constexpr (sizeof(T) == 2) compute_bf16(st0, n);
+    if constexpr (sizeof(T) == 2) compute_16(st0, n);
     else compute(st0, n);
     if constexpr (DROP)
       if (n + 1 < nsteps) reinterpret_cast<uint32_t*>(st1 + S::OFF_BITS)[bits_slot] = word;
@@ -541,7 +544,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
         if constexpr (DROP) word = bits_word(n + 2);
         if constexpr (MASK) mword = mask_word(n + 2);
       }
-      if constexpr (sizeof(T) == 2) compute_bf16(st1, n + 1);
+      if constexpr (sizeof(T) == 2) compute_16(st1, n + 1);
       else compute(st1, n + 1);
       if constexpr (DROP)
         if (n + 2 < nsteps) reinterpret_cast<uint32_t*>(st0 + S::OFF_BITS)[bits_slot] = word;
@@ -561,8 +564,8 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
       if (jj < lkv) {
         const int64_t off = ((int64_t)(k0 + jj) * p.nkv + g) * D + 32 * db + lrow;
         if constexpr (sizeof(T) == 2) {
-          reinterpret_cast<__bf16*>(p.dk)[off] = to_bf16(dk[db][r] * p.scale);
-          reinterpret_cast<__bf16*>(p.dv)[off] = to_bf16(dv[db][r]);
+          reinterpret_cast<E*>(p.dk)[off] = cvt16<E>(dk[db][r] * p.scale);
+          reinterpret_cast<E*>(p.dv)[off] = cvt16<E>(dv[db][r]);
         } else {
           reinterpret_cast<float*>(p.dk)[off] = dk[db][r] * p.scale;
           reinterpret_cast<float*>(p.dv)[off] = dv[db][r];
@@ -573,17 +576,19 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------- paired waves
-// bf16 deterministic dK/dV with two waves per 32-key group (8 waves, two per
+// 16-bit (bf16, fp16) deterministic dK/dV with two waves per 32-key group (8 waves, two per
 // SIMD).  Wave w = 2*kg + half owns keys 32kg .. 32kg+31 of the tile:
 //   - it computes S, dP, P~ and dS for rows block `half` of each 64-row step,
-//   - the pair swaps those bf16 P~ / dS operands through LDS, and
+//   - the pair swaps those 16-bit P~ / dS operands through LDS, and
 //   - it accumulates dV, dK over both row blocks for d columns
 //     [half * D/2, (half + 1) * D/2).
 // So no MFMA is done twice, and each wave holds half of the dK/dV accumulators:
 // small enough for two waves per SIMD, whose VALU and MFMA work then overlap.
-template <int D, bool DROP, bool ALIBI, bool MASK>
+template <typename E, int D, bool DROP, bool ALIBI, bool MASK>
 __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
-  using S = KvShape<__bf16, D>;
+  using S = KvShape<E, D>;
+  using V8 = typename Vec16<E>::v8;
+  using V4 = typename Vec16<E>::v4;
   constexpr int NW = 8;
   constexpr int HDB = S::NDB / 2;   // d blocks (32 wide) of this wave's dK / dV half
   constexpr int XB = 4 * 1024;      // exchange bytes per wave: P~ and dS, two operands each
@@ -609,25 +614,25 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
   const bool key_ok = j < lkv;
 
   // K and V rows of the group's keys as B operands (lane = key, registers = d)
-  bf16x8 kf[S::NOP], vf[S::NOP];
+  V8 kf[S::NOP], vf[S::NOP];
   {
     const int64_t kr = (int64_t)(k0 + (key_ok ? j : 0)) * p.nkv + g;
-    const __bf16* kp = reinterpret_cast<const __bf16*>(p.k) + kr * D;
-    const __bf16* vp = reinterpret_cast<const __bf16*>(p.v) + kr * D;
+    const E* kp = reinterpret_cast<const E*>(p.k) + kr * D;
+    const E* vp = reinterpret_cast<const E*>(p.v) + kr * D;
 #pragma unroll
     for (int c = 0; c < S::NOP; ++c) {
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(kp + 16 * c + 8 * hh);
-      const bf16x8 v = *reinterpret_cast<const bf16x8*>(vp + 16 * c + 8 * hh);
-      kf[c] = key_ok ? a : bf16x8{};
-      vf[c] = key_ok ? v : bf16x8{};
+      const V8 a = *reinterpret_cast<const V8*>(kp + 16 * c + 8 * hh);
+      const V8 v = *reinterpret_cast<const V8*>(vp + 16 * c + 8 * hh);
+      kf[c] = key_ok ? a : V8{};
+      vf[c] = key_ok ? v : V8{};
     }
   }
   f32x16 dk[HDB], dv[HDB];
 #pragma unroll
   for (int db = 0; db < HDB; ++db) {
     // zeros produced by an MFMA: the accumulators start in the MFMA register class
-    dk[db] = mfma32(bf16x8{}, bf16x8{}, f32x16{});
-    dv[db] = mfma32(bf16x8{}, bf16x8{}, f32x16{});
+    dk[db] = mfma32(V8{}, V8{}, f32x16{});
+    dv[db] = mfma32(V8{}, V8{}, f32x16{});
   }
 
   const int nqt = it.hi - it.lo;
@@ -696,15 +701,15 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
 #pragma unroll
     for (int c = 0; c < S::NOP; ++c) {
       const int qo = qrow + 16 * ((2 * c) ^ qsw) + 32 * rb * S::RB;
-      const bf16x8 qa = lds_read_b128(st + qo);
-      const bf16x8 ya = lds_read_b128(st + S::OFF_DY + qo);
+      const V8 qa = lds_read_b128<V8>(st + qo);
+      const V8 ya = lds_read_b128<V8>(st + S::OFF_DY + qo);
       s = mfma32(qa, kf[c], s);
       dp = mfma32(ya, vf[c], dp);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
     sched_alternate<2 * S::NOP, 0x008, 0x100>();
     __builtin_amdgcn_sched_barrier(0);
-    // ---- P~ and dS of the block as bf16 A operands, stored to this wave's exchange area ----
+    // ---- P~ and dS of the block as 16-bit A operands, stored to this wave's exchange area ----
     const float* lse_s = reinterpret_cast<const float*>(st + S::OFF_LSE);
     const float* del_s = reinterpret_cast<const float*>(st + S::OFF_DEL);
     const uint32_t* bits_s = reinterpret_cast<const uint32_t*>(st + S::OFF_BITS);
@@ -712,7 +717,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
       constexpr bool plain = !ALIBI && decltype(full_c)::value;
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        bf16x8 pa, da;
+        V8 pa, da;
 #pragma unroll
         for (int a = 2 * c; a < 2 * c + 2; ++a) {
           const int rq = 32 * rb + 8 * a + 4 * hh;   // rows rq .. rq+3 sit in registers 4a .. 4a+3
@@ -746,12 +751,12 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
               ptv = keep ? pr * p.inv_keep : 0.f;
             }
             const float dsv = pr * (dpv - del4[e]);
-            pa[r & 7] = to_bf16(ptv);
-            da[r & 7] = to_bf16(dsv);
+            pa[r & 7] = cvt16<E>(ptv);
+            da[r & 7] = cvt16<E>(dsv);
           }
         }
-        *reinterpret_cast<bf16x8*>(xmine + 1024 * c) = pa;
-        *reinterpret_cast<bf16x8*>(xmine + 1024 * (2 + c)) = da;
+        *reinterpret_cast<V8*>(xmine + 1024 * c) = pa;
+        *reinterpret_cast<V8*>(xmine + 1024 * (2 + c)) = da;
       }
     };
     // with an attenMask every block takes the masked path
@@ -765,13 +770,13 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
-        const bf16x8 pt = *reinterpret_cast<const bf16x8*>(xpair + blk * XB + 1024 * c);
-        const bf16x8 ds = *reinterpret_cast<const bf16x8*>(xpair + blk * XB + 1024 * (2 + c));
+        const V8 pt = *reinterpret_cast<const V8*>(xpair + blk * XB + 1024 * c);
+        const V8 ds = *reinterpret_cast<const V8*>(xpair + blk * XB + 1024 * (2 + c));
         const char* base = st + (32 * blk + 16 * c) * S::RB;
 #pragma unroll
         for (int db = 0; db < HDB; ++db) {
-          const bf16x8 yo = lds_read_tr_x2(base + S::OFF_DY + toff[0][db], base + S::OFF_DY + toff[1][db]);
-          const bf16x8 qo = lds_read_tr_x2(base + toff[0][db], base + toff[1][db]);
+          const V8 yo = lds_read_tr_x2<V8>(base + S::OFF_DY + toff[0][db], base + S::OFF_DY + toff[1][db]);
+          const V8 qo = lds_read_tr_x2<V8>(base + toff[0][db], base + toff[1][db]);
           dv[db] = mfma32(pt, yo, dv[db]);
           dk[db] = mfma32(ds, qo, dk[db]);
         }
@@ -825,8 +830,8 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
       const int jj = wc0 + 8 * (r >> 2) + 4 * hh + (r & 3);
       if (jj < lkv) {
         const int64_t off = ((int64_t)(k0 + jj) * p.nkv + g) * D + 32 * (half * HDB + db) + lrow;
-        reinterpret_cast<__bf16*>(p.dk)[off] = to_bf16(dk[db][r] * p.scale);
-        reinterpret_cast<__bf16*>(p.dv)[off] = to_bf16(dv[db][r]);
+        reinterpret_cast<E*>(p.dk)[off] = cvt16<E>(dk[db][r] * p.scale);
+        reinterpret_cast<E*>(p.dv)[off] = cvt16<E>(dv[db][r]);
       }
     }
   }

@@ -15,13 +15,13 @@ static hipError_t launch_kv_t(const BwdParams& p, hipStream_t s) {
   });
 }
 
-template <int D>
+template <typename E, int D>
 static hipError_t launch_kv_pair(const BwdParams& p, hipStream_t s) {
   const int64_t blocks = (int64_t)p.n_kv_items * p.nkv;
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(512);
   return with_flags(p.use_dropout != 0, p.slopes != nullptr, p.mbits != nullptr, [&](auto dr, auto al, auto mk) {
-    hipLaunchKernelGGL((fa_bwd_kv_pair_kernel<D, decltype(dr)::value, decltype(al)::value, decltype(mk)::value>),
+    hipLaunchKernelGGL((fa_bwd_kv_pair_kernel<E, D, decltype(dr)::value, decltype(al)::value, decltype(mk)::value>),
                        grid, block, 0, s, p);
     return hipGetLastError();
   });
@@ -29,8 +29,10 @@ static hipError_t launch_kv_pair(const BwdParams& p, hipStream_t s) {
 
 hipError_t launch_bwd_kv(int dtype, int d, bool atomic_dq, const BwdParams& p, hipStream_t s) {
   if (atomic_dq) return launch_bwd_kv_atomic(dtype, d, p, s);
-  if (dtype == 1 && d == 128) return launch_kv_pair<128>(p, s);
-  if (dtype == 1 && d == 64) return launch_kv_pair<64>(p, s);
+  if (dtype == 1 && d == 128) return launch_kv_pair<__bf16, 128>(p, s);
+  if (dtype == 1 && d == 64) return launch_kv_pair<__bf16, 64>(p, s);
+  if (dtype == 2 && d == 128) return launch_kv_pair<_Float16, 128>(p, s);
+  if (dtype == 2 && d == 64) return launch_kv_pair<_Float16, 64>(p, s);
   if (dtype == 0 && d == 128) return launch_kv_t<float, 128>(p, s);
   if (dtype == 0 && d == 64) return launch_kv_t<float, 64>(p, s);
   return hipErrorInvalidValue;

@@ -9,7 +9,7 @@ static hipError_t launch_kv_t(const BwdParams& p, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(256);
   const bool drop = p.use_dropout != 0, alibi = p.slopes != nullptr;
-  // no alibi instance of the atomic bf16 D = 128 kernel (see launch_bwd_kv)
+  // no alibi instance of the atomic 16-bit D = 128 kernel (see launch_bwd_kv)
   constexpr bool kAlibi = !(ATOMIC && sizeof(T) == 2 && D == 128);
   if (alibi && !kAlibi) return hipErrorInvalidValue;
   if (drop && alibi)
@@ -24,9 +24,11 @@ static hipError_t launch_kv_t(const BwdParams& p, hipStream_t s) {
 }
 
 hipError_t launch_bwd_kv_atomic(int dtype, int d, const BwdParams& p, hipStream_t s) {
-  // bf16 D = 128 with alibi runs the deterministic passes (the host routes it)
+  // 16-bit D = 128 with alibi runs the deterministic passes (the host routes it)
   if (dtype == 1 && d == 128 && p.slopes == nullptr) return launch_kv_t<__bf16, 128, true>(p, s);
   if (dtype == 1 && d == 64) return launch_kv_t<__bf16, 64, true>(p, s);
+  if (dtype == 2 && d == 128 && p.slopes == nullptr) return launch_kv_t<_Float16, 128, true>(p, s);
+  if (dtype == 2 && d == 64) return launch_kv_t<_Float16, 64, true>(p, s);
   // fp32 with D = 128 would need more LDS than a CU has; the host runs the
   // deterministic passes for it instead
   if (dtype == 0 && d == 64) return launch_kv_t<float, 64, true>(p, s);

@@ -1,5 +1,7 @@
 // Device helpers for the gfx950 (CDNA4) attention kernels: MFMA operand types,
-// the LDS transpose read, bf16 rounding and the dropout keep-bit window.
+// the LDS transpose read, 16-bit rounding and the dropout keep-bit window.
+// 16-bit element types: __bf16 and _Float16 share every layout below (their
+// MFMAs, v_mfma_f32_32x32x16_bf16 / _f16, take the same operand shapes).
 //
 // MFMA lane layouts used throughout (checked on the device):
 //   v_mfma_f32_32x32x16_bf16  A[m][k]: lane l holds m = l%32, k = 8*(l/32) + 0..7
@@ -13,10 +15,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -29,27 +35,45 @@ constexpr float kNegInf = -__builtin_inff();
 
 typedef __attribute__((address_space(3))) char lds_char;
 
+// MFMA operand vectors of a 16-bit element type E (the fp32 kernels name bf16
+// vectors in code they never instantiate)
+template <typename E>
+struct Vec16 {
+  using v8 = bf16x8;
+  using v4 = bf16x4;
+};
+template <>
+struct Vec16<_Float16> {
+  using v8 = f16x8;
+  using v4 = f16x4;
+};
+
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32(const f16x8& a, const f16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ f32x16 mfma32(float a, float b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
-// Two transposing LDS reads -> one bf16x8 operand (see layout note above).
-__device__ __forceinline__ bf16x8 lds_read_tr_x2(const char* p0, const char* p1) {
+// Two transposing LDS reads -> one 8-element 16-bit operand V (see layout note above).
+template <typename V = bf16x8>
+__device__ __forceinline__ V lds_read_tr_x2(const char* p0, const char* p1) {
   // address-space casts (not integer round trips) keep constant offsets foldable into the instruction
   s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p0);
   s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)p1);
-  bf16x8 r;
+  V r;
   s16x4* rp = reinterpret_cast<s16x4*>(&r);
   rp[0] = lo;
   rp[1] = hi;
   return r;
 }
 
-__device__ __forceinline__ bf16x8 lds_read_b128(const char* p) {
-  return *reinterpret_cast<const bf16x8*>(p);
+template <typename V = bf16x8>
+__device__ __forceinline__ V lds_read_b128(const char* p) {
+  return *reinterpret_cast<const V*>(p);
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -66,10 +90,13 @@ __device__ __forceinline__ float half_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// bf16 <-> f32 (round to nearest even)
-__device__ __forceinline__ __bf16 to_bf16(float f) { return (__bf16)f; }
-__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
-  return __uint_as_float(((uint32_t)b) << 16);
+// f32 -> 16-bit element (round to nearest even) and 16-bit element bits -> f32
+template <typename E>
+__device__ __forceinline__ E cvt16(float f) { return (E)f; }
+template <typename E>
+__device__ __forceinline__ float bits16_to_f32(uint16_t b) {
+  if constexpr (sizeof(E) == 2 && !std::is_same<E, _Float16>::value) return __uint_as_float(((uint32_t)b) << 16);
+  else return (float)__builtin_bit_cast(_Float16, b);
 }
 
 template <typename T>
@@ -78,6 +105,11 @@ template <>
 struct ElemTraits<__bf16> {
   static constexpr int kBytes = 2;
   static constexpr int kChunk = 16;  // k per MFMA
+};
+template <>
+struct ElemTraits<_Float16> {
+  static constexpr int kBytes = 2;
+  static constexpr int kChunk = 16;
 };
 template <>
 struct ElemTraits<float> {
@@ -184,7 +216,7 @@ __device__ __forceinline__ void dma_rows(char* lds, const char* gbase, int64_t g
   }
 }
 
-// ---- swizzled bf16 tiles ----
+// ---- swizzled 16-bit tiles ----
 // Rows of RB = 128 or 256 bytes are stored back to back (no padding); the
 // 16-byte chunk q of row r sits at r*RB + 16*(q ^ tile_swz<RB>(r)).  Under this
 // XOR pattern both operand reads of the kernels are free of LDS bank conflicts:

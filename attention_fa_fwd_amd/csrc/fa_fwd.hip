@@ -10,7 +10,7 @@
 //
 // Work decomposition: one workgroup = NW waves = one query tile of 32*NW rows
 // of one (sequence, head); each wave owns 32 rows, and all waves share each K/V
-// tile of 64 keys.  bf16 tiles sit in LDS unpadded with an XOR swizzle of their
+// tile of 64 keys.  16-bit (bf16, fp16) tiles sit in LDS unpadded with an XOR swizzle of their
 // 16-byte chunks and arrive by 16-byte-per-lane LDS DMA (four rows per
 // instruction); fp32 tiles use padded rows and 4-byte DMA.  Per wave and tile:
 //   S^T (64 keys x 32 rows) = K Q^T      A = K rows from LDS, B = Q in registers
@@ -19,7 +19,7 @@
 // Every accumulator keeps one query row per lane (lanes l and l+32 share a row),
 // so row max / row sum need only in-lane work plus one cross-half exchange.
 //
-// bf16 runs 4 waves per workgroup at two workgroups per CU, so one workgroup's
+// 16-bit runs 4 waves per workgroup at two workgroups per CU, so one workgroup's
 // softmax (VALU) overlaps the other's matrix work; fp32 runs one workgroup per
 // CU.  K and V tiles have two LDS stages each; global_load_lds fills stage t+1
 // while tile t is computed, and each wave drains its own copies just before
@@ -48,7 +48,7 @@ template <typename T, int D>
 struct FwdShape {
   static constexpr int EB = sizeof(T);
   static constexpr int RB = D * EB;                     // bytes per K/V row
-  // bf16 tiles are swizzled and unpadded; fp32 tiles use padded rows
+  // 16-bit tiles are swizzled and unpadded; fp32 tiles use padded rows
   static constexpr bool kSwz = EB == 2;
   static constexpr int KP = kSwz ? RB : RB + 16;        // LDS pitch of K rows
   static constexpr int VP = kSwz ? RB : RB + 16;        // LDS pitch of V rows
@@ -70,7 +70,10 @@ template <typename T, int D, int NW, int OCC, bool DROP, bool ALIBI, bool MASK>
 __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
   using S = FwdShape<T, D>;
   constexpr int BM = 32 * NW;
-  constexpr bool kBf16 = sizeof(T) == 2;
+  constexpr bool k16 = sizeof(T) == 2;
+  using E = typename std::conditional<sizeof(T) == 2, T, __bf16>::type;   // 16-bit element type
+  using V8 = typename Vec16<E>::v8;
+  using V4 = typename Vec16<E>::v4;
   __shared__ __attribute__((aligned(16))) char kst[2][S::KT];
   __shared__ __attribute__((aligned(16))) char vst[2][S::VT];
 
@@ -99,16 +102,16 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
   // ---- Q operand in registers (B of S^T = K Q^T), negated for a negative scale ----
   const bool neg = p.scale_log2 < 0.f;
   const float sc = neg ? -p.scale_log2 : p.scale_log2;
-  using QReg = typename std::conditional<kBf16, bf16x8, float>::type;
+  using QReg = typename std::conditional<k16, V8, float>::type;
   QReg qf[S::NQ];
   {
     const T* qp = reinterpret_cast<const T*>(p.q) + ((int64_t)(q0 + (row_ok ? i : 0)) * p.nq + h) * D;
-    if constexpr (kBf16) {
+    if constexpr (k16) {
 #pragma unroll
       for (int c = 0; c < S::NQ; ++c) {
-        bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + 16 * c + 8 * hh);
+        V8 v = *reinterpret_cast<const V8*>(qp + 16 * c + 8 * hh);
         if (neg) v = -v;
-        qf[c] = row_ok ? v : bf16x8{};
+        qf[c] = row_ok ? v : V8{};
       }
     } else {
 #pragma unroll
@@ -134,7 +137,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
   // per-lane LDS byte offsets; every other offset below is a compile-time immediate
   const int k_lane = lrow * S::KP + 16 * hh;                                      // K row reads
   const int v_lane = (4 * (grp >> 1) + (sl >> 2)) * S::VP + (16 * (grp & 1) + 4 * (sl & 3)) * 2;  // V^T reads
-  // swizzled bf16 tiles: K chunk 2c + hh of row lrow (+32 for the second key block),
+  // swizzled 16-bit tiles: K chunk 2c + hh of row lrow (+32 for the second key block),
   // V^T reads of rows rv and rv + 8 (+16 per 16-key step), chunk 4db + qv
   int koff[S::kSwz ? S::NQ : 1], voff[2][S::kSwz ? S::NDB : 1];
   if constexpr (S::kSwz) {
@@ -176,13 +179,13 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
   // S^T = K Q^T for the tile's two 32-key blocks.  The LDS reads of block 1 are
   // issued between the MFMAs of block 0, so only the first reads wait on LDS.
   auto scores = [&](const char* ks, f32x16 (&s)[2]) {
-    if constexpr (kBf16) {
-      bf16x8 a0[S::NQ], a1[S::NQ];
+    if constexpr (k16) {
+      V8 a0[S::NQ], a1[S::NQ];
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int c = 0; c < S::NQ; ++c) a0[c] = lds_read_b128(ks + koff[c]);
+      for (int c = 0; c < S::NQ; ++c) a0[c] = lds_read_b128<V8>(ks + koff[c]);
 #pragma unroll
-      for (int c = 0; c < S::NQ; ++c) a1[c] = lds_read_b128(ks + koff[c] + 32 * S::RB);
+      for (int c = 0; c < S::NQ; ++c) a1[c] = lds_read_b128<V8>(ks + koff[c] + 32 * S::RB);
       s[0] = f32x16{};
       s[1] = f32x16{};
 #pragma unroll
@@ -265,21 +268,21 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
   // O^T += V^T P^T.  The transposing reads of each 16-key step are issued
   // between the MFMAs of the previous step.
   auto pv = [&](const char* vs, f32x16 (&s)[2]) {
-    if constexpr (kBf16) {
-      bf16x8 pb[4];
+    if constexpr (k16) {
+      V8 pb[4];
 #pragma unroll
       for (int c2 = 0; c2 < 4; ++c2) {
         const int kb = c2 >> 1, sub = c2 & 1;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pb[c2][j] = to_bf16(s[kb][8 * sub + j]);
+        for (int j = 0; j < 8; ++j) pb[c2][j] = cvt16<E>(s[kb][8 * sub + j]);
       }
       __builtin_amdgcn_sched_barrier(0);
-      bf16x8 a[4][S::NDB];
+      V8 a[4][S::NDB];
 #pragma unroll
       for (int c2 = 0; c2 < 4; ++c2) {
         const char* vrow = vs + (16 * c2) * S::RB;
 #pragma unroll
-        for (int db = 0; db < S::NDB; ++db) a[c2][db] = lds_read_tr_x2(vrow + voff[0][db], vrow + voff[1][db]);
+        for (int db = 0; db < S::NDB; ++db) a[c2][db] = lds_read_tr_x2<V8>(vrow + voff[0][db], vrow + voff[1][db]);
       }
 #pragma unroll
       for (int c2 = 0; c2 < 4; ++c2)
@@ -367,11 +370,11 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         const int d = 32 * db + 8 * a + 4 * hh;
-        if constexpr (kBf16) {
-          bf16x4 v;
+        if constexpr (k16) {
+          V4 v;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) v[e] = to_bf16(o[db][4 * a + e] * inv);
-          *reinterpret_cast<bf16x4*>(op + d) = v;
+          for (int e = 0; e < 4; ++e) v[e] = cvt16<E>(o[db][4 * a + e] * inv);
+          *reinterpret_cast<V4*>(op + d) = v;
         } else {
           f32x4 v;
 #pragma unroll
@@ -409,6 +412,8 @@ static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
 hipError_t launch_fwd(int dtype, int d, const FwdParams& p, hipStream_t s) {
   if (dtype == 1 && d == 128) return launch_fwd_t<__bf16, 128>(p, s);
   if (dtype == 1 && d == 64) return launch_fwd_t<__bf16, 64>(p, s);
+  if (dtype == 2 && d == 128) return launch_fwd_t<_Float16, 128>(p, s);
+  if (dtype == 2 && d == 64) return launch_fwd_t<_Float16, 64>(p, s);
   if (dtype == 0 && d == 128) return launch_fwd_t<float, 128>(p, s);
   if (dtype == 0 && d == 64) return launch_fwd_t<float, 64>(p, s);
   return hipErrorInvalidValue;

@@ -107,6 +107,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=5)
     ap.add_argument("--atomic-dq", action="store_true", help="time the fp32-atomic dQ variant")
+    ap.add_argument("--dtype", choices=("bf16", "fp16"), default="bf16",
+                    help="16-bit element type of workloads 2-5 (fp16 draws the same samples in fp16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (calibrates the HBM byte counters)")
@@ -131,7 +133,7 @@ def main():
         print(json.dumps({"copy_bytes": args.copy_calibration}), flush=True)
         return
     log(f"generating workload {args.workload}")
-    case = wl.make_workload(args.workload)
+    case = wl.make_workload(args.workload, torch.float16 if args.dtype == "fp16" else None)
     pairs, f_fwd, f_bwd = flops_of(case)
     deterministic = not args.atomic_dq
     cfg = fa.Config(case.cu_seqlens_q, case.cu_seqlens_kv, case.head_num, case.kv_heads, case.head_dim,
@@ -197,14 +199,15 @@ def main():
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         tf = json.load(open(TRAFFIC_FILE))
-        ent = tf.get(f"workload{args.workload}", {}).get(dom)
+        ent = tf.get(f"workload{args.workload}" + ("_fp16" if args.dtype == "fp16" else ""), {}).get(dom)
         if ent and ent.get("source_hash") == kernel_source_hash():
             traffic = ent.get("bytes_per_launch")
 
     total_flops = f_fwd + f_bwd
+    dt_name = {torch.bfloat16: "bf16", torch.float16: "fp16", torch.float32: "fp32"}[case.dtype]
     value = total_flops / (ms_step * 1e-3) / 1e12
     res = {
-        "metric": "attention fwd+bwd TFLOP/s (mask-aware) bf16 D=128; % of MFMA peak",
+        "metric": f"attention fwd+bwd TFLOP/s (mask-aware) {dt_name} D=128; % of MFMA peak",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -214,9 +217,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if case.q.element_size() == 2 else "fp32",
+        "dtype": dt_name,
         "data": "synthetic",
-        "config": {"workload": wl.WORKLOAD_NAMES[args.workload], "total_tokens": int(tq),
+        "config": {"workload": wl.workload_name(args.workload, case.dtype), "total_tokens": int(tq),
                    "sequences": int(case.batch), "heads_q": case.head_num, "heads_kv": case.kv_heads,
                    "head_dim": d, "allowed_pairs": int(pairs),
                    "dq_variant": "deterministic" if deterministic else "atomic"},

@@ -51,9 +51,13 @@ typedef int32_t fa_status;
 #define FA_ERR_WORKSPACE 1          /* workspace_bytes smaller than the size query returned */
 #define FA_ERR_HIP 2                /* a HIP runtime call or kernel launch failed */
 
-/* element type of Q, K, V, dY, O, dQ, dK, dV */
+/* element type of Q, K, V, dY, O, dQ, dK, dV (the pages list FLOAT16, BFLOAT16 and
+   FLOAT32 for these tensors: aclnnFlashAttentionUnpaddingScoreGrad, parameter table).
+   16-bit inputs are multiplied on the matrix cores in their own type with fp32
+   accumulation; softmax statistics and dQ partial sums stay fp32. */
 #define FA_DTYPE_FP32 0
 #define FA_DTYPE_BF16 1
+#define FA_DTYPE_FP16 2
 
 /* sparse modes (aclnnFlashAttentionUnpaddingScoreGrad, "sparseMode" parameter) */
 #define FA_SPARSE_NONE 0             /* every pair allowed (or those the attenMask keeps)    */

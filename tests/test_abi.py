@@ -7,6 +7,7 @@ import re
 
 import numpy as np
 import pytest
+import torch
 
 import attention_fa_fwd_amd as fa
 import oracle
@@ -87,6 +88,18 @@ def test_invalid_configs_rejected(name):
     assert _bwd(cfg) == fa.FA_ERR_PARAM_INVALID
     n = ctypes.c_uint64(0)
     assert fa.lib().fa_fwd_workspace_size(cfg.ref, ctypes.byref(n)) == fa.FA_ERR_PARAM_INVALID
+
+
+def test_element_types_accepted():
+    # FLOAT32, BFLOAT16 and FLOAT16 inputs (aclnnFlashAttentionUnpaddingScoreGrad, parameter table)
+    n = ctypes.c_uint64(0)
+    for dt in (fa.FA_DTYPE_FP32, fa.FA_DTYPE_BF16, fa.FA_DTYPE_FP16):
+        for d in (64, 128):
+            assert fa.lib().fa_bwd_workspace_size(_cfg(dtype=dt, head_dim=d).ref, ctypes.byref(n)) == fa.FA_OK
+            assert n.value > 0
+    for dt in (-1, 3):
+        assert fa.lib().fa_fwd_workspace_size(_cfg(dtype=dt).ref, ctypes.byref(n)) == fa.FA_ERR_PARAM_INVALID
+    assert fa.Config([0, 4], [0, 4], 2, 2, 64, torch.float16, 0.125).c.dtype == fa.FA_DTYPE_FP16
 
 
 def test_bad_flags_and_batch_limits():

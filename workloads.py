@@ -204,23 +204,34 @@ def workload_lengths(k: int) -> np.ndarray:
     raise ValueError(f"unknown workload {k}")
 
 
-def make_workload(k: int) -> Case:
-    """The five fixed workloads (sizes, masks and features as listed in WORKLOAD_NAMES)."""
+def workload_name(k: int, dtype: Optional[torch.dtype] = None) -> str:
+    """Name of workload k; dtype float16 renames the 16-bit workloads."""
+    name = WORKLOAD_NAMES[k]
+    return name.replace("bf16", "fp16") if dtype == torch.float16 else name
+
+
+def make_workload(k: int, dtype: Optional[torch.dtype] = None) -> Case:
+    """The five fixed workloads (sizes, masks and features as listed in WORKLOAD_NAMES).
+    dtype=torch.float16 draws the 16-bit workloads (2-5) in fp16 instead of bf16:
+    the same normal samples, rounded to the other 16-bit type."""
+    if dtype not in (None, torch.bfloat16, torch.float16) or (dtype == torch.float16 and k == 1):
+        raise ValueError(f"workload {k} has no {dtype} variant")
     lens = workload_lengths(k)
+    dt = dict(dtype=dtype) if dtype is not None else {}
     if k == 1:
         c = make_case(WORKLOAD_NAMES[1], lens, head_num=2, kv_heads=2, head_dim=64, dtype=torch.float32,
                       scale=1.0 / 8.0, seed=1)
     elif k == 2:
-        c = make_case(WORKLOAD_NAMES[2], lens, head_num=32, kv_heads=8, head_dim=128,
+        c = make_case(workload_name(2, dtype), lens, **dt, head_num=32, kv_heads=8, head_dim=128,
                       sparse_mode=MODE_RIGHT_DOWN_CAUSAL, seed=2)
     elif k == 3:
-        c = make_case(WORKLOAD_NAMES[3], lens, head_num=32, kv_heads=32, head_dim=128,
+        c = make_case(workload_name(3, dtype), lens, **dt, head_num=32, kv_heads=32, head_dim=128,
                       sparse_mode=MODE_BAND, pre_tokens=2048, next_tokens=0, seed=3, dy_mult=0.1)
     elif k == 4:
-        c = make_case(WORKLOAD_NAMES[4], lens, head_num=16, kv_heads=16, head_dim=128,
+        c = make_case(workload_name(4, dtype), lens, **dt, head_num=16, kv_heads=16, head_dim=128,
                       sparse_mode=MODE_RIGHT_DOWN_CAUSAL, keep_prob=0.9, alibi=True, seed=4)
     elif k == 5:
-        c = make_case(WORKLOAD_NAMES[5], lens, head_num=64, kv_heads=8, head_dim=128,
+        c = make_case(workload_name(5, dtype), lens, **dt, head_num=64, kv_heads=8, head_dim=128,
                       sparse_mode=MODE_RIGHT_DOWN_CAUSAL, sink=True, seed=5)
     else:
         raise ValueError(k)
