@@ -27,6 +27,8 @@ FA_ERR_HIP = 2
 FA_DTYPE_FP32 = 0
 FA_DTYPE_BF16 = 1
 FA_DTYPE_FP16 = 2
+FA_FLAG_PSE_SQRT = 1
+FA_FLAG_SLOPES_PER_BATCH = 2
 TOKENS_DEFAULT = 2147483647
 
 EXPORTED = ("fa_fwd_workspace_size", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd", "fa_status_string",
@@ -103,7 +105,7 @@ class Config:
 
     def __init__(self, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, head_dim, dtype, scale, keep_prob=1.0,
                  sparse_mode=0, pre_tokens=TOKENS_DEFAULT, next_tokens=TOKENS_DEFAULT, deterministic=True,
-                 prefix=None, atten_mask=None):
+                 prefix=None, atten_mask=None, pse_type=2, slopes_per_batch=False):
         self.cu_q = np.ascontiguousarray(np.asarray(cu_seqlens_q, dtype=np.int64))
         self.cu_kv = np.ascontiguousarray(np.asarray(cu_seqlens_kv, dtype=np.int64))
         # per-sequence prefix N of sparse mode 6 (prefixOptional); NULL when None
@@ -113,6 +115,11 @@ class Config:
         if atten_mask is not None:
             if atten_mask.dim() != 2 or atten_mask.dtype not in (torch.uint8, torch.bool) or not atten_mask.is_contiguous():
                 raise ValueError("atten_mask must be a contiguous 2-D bool or uint8 tensor [S1Max, S2Max]")
+        # pseType of the slopes passed to fa_fwd / fa_bwd: 2 (linear distance) or 3 (square root)
+        if pse_type not in (2, 3):
+            raise ValueError("pse_type must be 2 or 3 (generated from alibi slopes)")
+        self.slopes_per_batch = bool(slopes_per_batch)
+        flags = (FA_FLAG_PSE_SQRT if pse_type == 3 else 0) | (FA_FLAG_SLOPES_PER_BATCH if slopes_per_batch else 0)
         if isinstance(dtype, torch.dtype):
             dtype = {torch.float32: FA_DTYPE_FP32, torch.bfloat16: FA_DTYPE_BF16,
                      torch.float16: FA_DTYPE_FP16}.get(dtype, -1)
@@ -123,7 +130,7 @@ class Config:
             head_num=int(head_num), num_kv_heads=int(kv_heads), head_dim=int(head_dim), dtype=int(dtype),
             sparse_mode=int(sparse_mode), scale=float(scale), keep_prob=float(keep_prob),
             pre_tokens=int(pre_tokens), next_tokens=int(next_tokens), deterministic=1 if deterministic else 0,
-            flags=0,
+            flags=flags,
             prefix=(None if self.prefix is None else self.prefix.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))),
             atten_mask=(None if atten_mask is None else atten_mask.data_ptr()),
             mask_rows=(0 if atten_mask is None else int(atten_mask.shape[0])),
@@ -188,6 +195,14 @@ def _common_checks(q, k, v, cfg: Config):
     return dev, tq, tkv, nq, nkv, d
 
 
+def _check_slopes_sink(cfg: Config, alibi_slopes, sink, nq, dev):
+    if alibi_slopes is not None:
+        shape = (cfg.c.batch, nq) if cfg.slopes_per_batch else (nq,)
+        _check_tensor("alibi_slopes", alibi_slopes, shape, torch.float32, dev)
+    if sink is not None:
+        _check_tensor("sink", sink, (nq,), torch.float32, dev)
+
+
 def fa_fwd(cfg: Config, q, k, v, drop_mask=None, alibi_slopes=None, sink=None, out=None, softmax_max=None,
            softmax_sum=None, workspace=None):
     """Forward through libfa.so on the current stream; returns (out, softmax_max, softmax_sum)."""
@@ -201,9 +216,7 @@ def fa_fwd(cfg: Config, q, k, v, drop_mask=None, alibi_slopes=None, sink=None, o
     _check_tensor("out", out, (tq, nq, d), q.dtype, dev)
     _check_tensor("softmax_max", softmax_max, (tq, nq), torch.float32, dev)
     _check_tensor("softmax_sum", softmax_sum, (tq, nq), torch.float32, dev)
-    for name, t in (("alibi_slopes", alibi_slopes), ("sink", sink)):
-        if t is not None:
-            _check_tensor(name, t, (nq,), torch.float32, dev)
+    _check_slopes_sink(cfg, alibi_slopes, sink, nq, dev)
     if drop_mask is not None and (drop_mask.dtype != torch.uint8 or drop_mask.device != dev):
         raise ValueError("drop_mask must be a uint8 tensor on the same device")
     ws = _workspace(fa_fwd_workspace_size(cfg), dev, workspace)
@@ -222,6 +235,7 @@ def fa_bwd(cfg: Config, q, k, v, dy, out, softmax_max, softmax_sum, drop_mask=No
     _check_tensor("out", out, (tq, nq, d), q.dtype, dev)
     _check_tensor("softmax_max", softmax_max, (tq, nq), torch.float32, dev)
     _check_tensor("softmax_sum", softmax_sum, (tq, nq), torch.float32, dev)
+    _check_slopes_sink(cfg, alibi_slopes, sink, nq, dev)
     if dq is None:
         dq = torch.empty_like(q)
     if dk is None:

@@ -27,6 +27,8 @@ struct Problem {
   double scale = 0, keep = 1;
   int64_t pre = 0, next = 0;
   bool deterministic = true;
+  bool pse_sqrt = false;           // FA_FLAG_PSE_SQRT: the slopes generate pseType 3
+  bool slopes_per_batch = false;   // FA_FLAG_SLOPES_PER_BATCH: slopes are [B, Nq]
   std::vector<int32_t> cu_q, cu_kv;
   std::vector<int64_t> bit_base;   // first keep bit of each sequence
   std::vector<int32_t> prefix;     // prefix N of each sequence (sparse mode 6; zeros otherwise)
@@ -57,7 +59,7 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   if (!std::isfinite(cfg->scale)) return FA_ERR_PARAM_INVALID;
   if (mode == FA_SPARSE_BAND && cfg->pre_tokens + cfg->next_tokens < 0) return FA_ERR_PARAM_INVALID;
   if (cfg->deterministic != 0 && cfg->deterministic != 1) return FA_ERR_PARAM_INVALID;
-  if (cfg->flags != 0) return FA_ERR_PARAM_INVALID;
+  if ((cfg->flags & ~(FA_FLAG_PSE_SQRT | FA_FLAG_SLOPES_PER_BATCH)) != 0) return FA_ERR_PARAM_INVALID;
 
   pr->batch = cfg->batch;
   pr->nq = cfg->head_num;
@@ -65,6 +67,8 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   pr->d = cfg->head_dim;
   pr->dtype = cfg->dtype;
   pr->mode = mode;
+  pr->pse_sqrt = (cfg->flags & FA_FLAG_PSE_SQRT) != 0;
+  pr->slopes_per_batch = (cfg->flags & FA_FLAG_SLOPES_PER_BATCH) != 0;
   pr->scale = cfg->scale;
   pr->keep = cfg->keep_prob;
   pr->pre = cfg->pre_tokens;
@@ -375,6 +379,8 @@ fa_status fa_fwd(const fa_config* cfg, const void* q, const void* k, const void*
   p.drop = pr.keep < 1.0 ? drop_mask : nullptr;
   p.drop_bytes = (pr.drop_bits + 7) / 8;
   p.slopes = alibi_slopes; p.sink = sink;
+  p.slope_bstride = pr.slopes_per_batch ? (int32_t)pr.nq : 0;
+  p.pse_sqrt = pr.pse_sqrt ? 1 : 0;
   p.cu_q = reinterpret_cast<const int32_t*>(ws + L.cu_q);
   p.cu_kv = reinterpret_cast<const int32_t*>(ws + L.cu_kv);
   p.bit_base = reinterpret_cast<const int64_t*>(ws + L.bit_base);
@@ -438,6 +444,8 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
   p.drop = pr.keep < 1.0 ? drop_mask : nullptr;
   p.drop_bytes = (pr.drop_bits + 7) / 8;
   p.slopes = alibi_slopes; p.sink = sink;
+  p.slope_bstride = pr.slopes_per_batch ? (int32_t)pr.nq : 0;
+  p.pse_sqrt = pr.pse_sqrt ? 1 : 0;
   p.cu_q = reinterpret_cast<const int32_t*>(ws + L.cu_q);
   p.cu_kv = reinterpret_cast<const int32_t*>(ws + L.cu_kv);
   p.bit_base = reinterpret_cast<const int64_t*>(ws + L.bit_base);

@@ -150,7 +150,7 @@ struct DqShape {
   static constexpr int NDB = D / 32;
 };
 
-template <typename T, int D, bool DROP, bool ALIBI, bool MASK>
+template <typename T, int D, bool DROP, int ALIBI, bool MASK>
 __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams p) {
   using S = DqShape<T, D>;
   using E = typename std::conditional<sizeof(T) == 2, T, __bf16>::type;   // 16-bit element type
@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
   }
   const float lse2 = row_ok ? p.lse[rowg * p.nq + h] : __builtin_inff();
   const float di = row_ok ? p.delta[rowg * p.nq + h] : 0.f;
-  const float slope_l2 = ALIBI ? p.slopes[h] * kLog2e : 0.f;
+  const float slope_l2 = ALIBI ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
   f32x16 acc[S::NDB];
 #pragma unroll
   for (int db = 0; db < S::NDB; ++db) acc[db] = f32x16{};
@@ -286,7 +286,7 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
           pr = fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -lse2));
         } else {
           float x = s[r] * p.scale_log2;
-          if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, jmi + (float)(8 * (r >> 2) + (r & 3)), x);
+          if constexpr (ALIBI != 0) x = add_pse<ALIBI>(x, slope_l2, jmi + (float)(8 * (r >> 2) + (r & 3)));
           if (!full) {
             const bool ok = row_ok & (jj < lkv) & (jj >= fa_row_lo(win, i)) & (jj <= fa_row_hi(win, i)) &
                             !((mwk >> (kk - 32 * kb)) & 1u);
@@ -403,8 +403,8 @@ static hipError_t launch_dq_t(const BwdParams& p, hipStream_t s) {
   const int64_t blocks = (int64_t)p.n_dq_items * p.nq;
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(256);
-  const bool drop = p.use_dropout != 0, alibi = p.slopes != nullptr;
-  return with_flags(drop, alibi, p.mbits != nullptr, [&](auto dr, auto al, auto mk) {
+  const bool drop = p.use_dropout != 0;
+  return with_flags(drop, pse_kind(p), p.mbits != nullptr, [&](auto dr, auto al, auto mk) {
     hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, decltype(dr)::value, decltype(al)::value, decltype(mk)::value>),
                        grid, block, 0, s, p);
     return hipGetLastError();

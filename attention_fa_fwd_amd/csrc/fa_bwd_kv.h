@@ -46,7 +46,7 @@ struct KvShape {
   static constexpr int NDB = D / 32;
 };
 
-template <typename T, int D, bool ATOMIC, bool DROP, bool ALIBI, bool MASK>
+template <typename T, int D, bool ATOMIC, bool DROP, int ALIBI, bool MASK>
 __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
   using S = KvShape<T, D>;
   using E = typename std::conditional<sizeof(T) == 2, T, __bf16>::type;   // 16-bit element type
@@ -273,7 +273,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
           pr = fast_exp2(__builtin_fmaf(s[r], sc, -lse4[e]));
         } else {
           float x = s[r] * sc;
-          if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, jmi - (float)e, x);
+          if constexpr (ALIBI != 0) x = add_pse<ALIBI>(x, slope_l2, jmi - (float)e);
           if constexpr (!decltype(full_c)::value) {
             const bool ok = (i < lq) & key_ok & (j >= fa_row_lo(win, i)) & (j <= fa_row_hi(win, i)) &
                             !((mb4[e] >> lrow) & 1u);
@@ -311,7 +311,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
 
   auto compute_16 = [&](const char* st, auto n) {
     const int h = step_head(n), r0 = step_row0(n);
-    const float slope_l2 = ALIBI ? p.slopes[h] * kLog2e : 0.f;
+    const float slope_l2 = ALIBI ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
     // with an attenMask every block takes the masked path
     const bool full0 = fa_tile_full(win, r0, 32, wc0, 32, lq, lkv) && !MASK;
     const bool full1 = fa_tile_full(win, r0 + 32, 32, wc0, 32, lq, lkv) && !MASK;
@@ -339,7 +339,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
 
   auto compute = [&](const char* st, int n) {
     const int h = step_head(n), r0 = step_row0(n);
-    const float slope_l2 = ALIBI ? p.slopes[h] * kLog2e : 0.f;
+    const float slope_l2 = ALIBI ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
     const float* lse_s = reinterpret_cast<const float*>(st + S::OFF_LSE);
     const float* del_s = reinterpret_cast<const float*>(st + S::OFF_DEL);
     const uint32_t* bits_s = reinterpret_cast<const uint32_t*>(st + S::OFF_BITS);
@@ -381,7 +381,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
       for (int r = 0; r < 16; ++r) {
         const int rr = 32 * rb + 8 * (r >> 2) + 4 * hh + (r & 3);
         float x = s[r] * p.scale_log2;
-        if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, (float)(j - (r0 + rr)), x);
+        if constexpr (ALIBI != 0) x = add_pse<ALIBI>(x, slope_l2, (float)(j - (r0 + rr)));
         if (!full && (!fa_allowed(win, r0 + rr, j, lq, lkv) ||
                       (MASK && ((reinterpret_cast<const uint32_t*>(st + S::OFF_MBITS)[wave * kKvBM + rr] >> lrow) & 1u))))
           x = kNegInf;
@@ -584,7 +584,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
 //     [half * D/2, (half + 1) * D/2).
 // So no MFMA is done twice, and each wave holds half of the dK/dV accumulators:
 // small enough for two waves per SIMD, whose VALU and MFMA work then overlap.
-template <typename E, int D, bool DROP, bool ALIBI, bool MASK>
+template <typename E, int D, bool DROP, int ALIBI, bool MASK>
 __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
   using S = KvShape<E, D>;
   using V8 = typename Vec16<E>::v8;
@@ -692,7 +692,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
 
   auto compute = [&](const char* st, int n) {
     const int h = step_head(n), r0 = step_row0(n);
-    const float slope_l2 = ALIBI ? p.slopes[h] * kLog2e : 0.f;
+    const float slope_l2 = ALIBI ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
     const float sc = p.scale_log2;
     const int rb = half;                     // the row block whose P~ / dS this wave forms
     // ---- S = Q K^T, dP~ = dY V^T for rows block rb (lane = key, registers = rows) ----
@@ -736,7 +736,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
               pr = fast_exp2(__builtin_fmaf(s[r], sc, -lse4[e]));
             } else {
               float x = s[r] * sc;
-              if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, jmi - (float)e, x);
+              if constexpr (ALIBI != 0) x = add_pse<ALIBI>(x, slope_l2, jmi - (float)e);
               if constexpr (!decltype(full_c)::value) {
                 const bool ok = (i < lq) & key_ok & (j >= fa_row_lo(win, i)) & (j <= fa_row_hi(win, i)) &
                                 !((mb4[e] >> lrow) & 1u);

@@ -8,7 +8,7 @@ static hipError_t launch_kv_t(const BwdParams& p, hipStream_t s) {
   const int64_t blocks = (int64_t)p.n_kv_items * p.nkv;
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(256);
-  return with_flags(p.use_dropout != 0, p.slopes != nullptr, p.mbits != nullptr, [&](auto dr, auto al, auto mk) {
+  return with_flags(p.use_dropout != 0, pse_kind(p), p.mbits != nullptr, [&](auto dr, auto al, auto mk) {
     hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, false, decltype(dr)::value, decltype(al)::value, decltype(mk)::value>),
                        grid, block, 0, s, p);
     return hipGetLastError();
@@ -20,7 +20,7 @@ static hipError_t launch_kv_pair(const BwdParams& p, hipStream_t s) {
   const int64_t blocks = (int64_t)p.n_kv_items * p.nkv;
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(512);
-  return with_flags(p.use_dropout != 0, p.slopes != nullptr, p.mbits != nullptr, [&](auto dr, auto al, auto mk) {
+  return with_flags(p.use_dropout != 0, pse_kind(p), p.mbits != nullptr, [&](auto dr, auto al, auto mk) {
     hipLaunchKernelGGL((fa_bwd_kv_pair_kernel<E, D, decltype(dr)::value, decltype(al)::value, decltype(mk)::value>),
                        grid, block, 0, s, p);
     return hipGetLastError();

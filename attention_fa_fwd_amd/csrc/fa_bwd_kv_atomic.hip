@@ -8,19 +8,16 @@ static hipError_t launch_kv_t(const BwdParams& p, hipStream_t s) {
   const int64_t blocks = (int64_t)p.n_kv_items * p.nkv;
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(256);
-  const bool drop = p.use_dropout != 0, alibi = p.slopes != nullptr;
   // no alibi instance of the atomic 16-bit D = 128 kernel (see launch_bwd_kv)
   constexpr bool kAlibi = !(ATOMIC && sizeof(T) == 2 && D == 128);
-  if (alibi && !kAlibi) return hipErrorInvalidValue;
-  if (drop && alibi)
-    hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, true, kAlibi, false>), grid, block, 0, s, p);
-  else if (drop)
-    hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, true, false, false>), grid, block, 0, s, p);
-  else if (alibi)
-    hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, false, kAlibi, false>), grid, block, 0, s, p);
-  else
-    hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, false, false, false>), grid, block, 0, s, p);
-  return hipGetLastError();
+  if (!kAlibi && p.slopes != nullptr) return hipErrorInvalidValue;
+  // no attenMask instances: the host routes masked problems to the deterministic passes
+  if (p.mbits != nullptr) return hipErrorInvalidValue;
+  return with_flags(p.use_dropout != 0, kAlibi ? pse_kind(p) : kPseNone, false, [&](auto dr, auto al, auto mk) {
+    constexpr int AL = kAlibi ? decltype(al)::value : kPseNone;
+    hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, decltype(dr)::value, AL, false>), grid, block, 0, s, p);
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_bwd_kv_atomic(int dtype, int d, const BwdParams& p, hipStream_t s) {

@@ -90,6 +90,17 @@ __device__ __forceinline__ float half_sum(float v) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Generated position bias (pseType 2 / 3 of aclnnFlashAttentionScoreV2, pseType
+// table), added after scaling, in the log2 domain: slope_l2 = slope * log2(e),
+// jmi = j - i (local key minus local row).
+//   KIND 1 (pseType 2): -slope * (i - j)
+//   KIND 2 (pseType 3): -slope * sqrt(|i - j|)
+template <int KIND>
+__device__ __forceinline__ float add_pse(float x, float slope_l2, float jmi) {
+  if constexpr (KIND == 2) return __builtin_fmaf(-slope_l2, __builtin_amdgcn_sqrtf(__builtin_fabsf(jmi)), x);
+  else return __builtin_fmaf(slope_l2, jmi, x);
+}
+
 // f32 -> 16-bit element (round to nearest even) and 16-bit element bits -> f32
 template <typename E>
 __device__ __forceinline__ E cvt16(float f) { return (E)f; }

@@ -66,7 +66,7 @@ struct RowTile {
   uint32_t mw[2];     // attenMask bits (1 = masked) of the lane's row, same keys
 };
 
-template <typename T, int D, int NW, int OCC, bool DROP, bool ALIBI, bool MASK>
+template <typename T, int D, int NW, int OCC, bool DROP, int ALIBI, bool MASK>
 __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
   using S = FwdShape<T, D>;
   constexpr int BM = 32 * NW;
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
     }
   }
 
-  const float slope_l2 = ALIBI ? p.slopes[h] * kLog2e : 0.f;
+  const float slope_l2 = ALIBI ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
   const bool has_sink = p.sink != nullptr;
   float m_run = has_sink ? p.sink[h] * kLog2e : kNegInf;   // exponent offset
   float m_true = m_run;                                     // running maximum
@@ -229,7 +229,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
         for (int r = 0; r < 16; ++r) {
           const int j = c0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
           float x = s[kb][r] * sc;
-          if constexpr (ALIBI) x = __builtin_fmaf(slope_l2, (float)(j - i), x);
+          if constexpr (ALIBI != 0) x = add_pse<ALIBI>(x, slope_l2, (float)(j - i));
           if (!decltype(full_c)::value &&
               (!fa_allowed(win, i, j, lq, lkv) || (MASK && ((rt.mw[kb] >> (8 * (r >> 2) + 4 * hh + (r & 3))) & 1u))))
             x = kNegInf;
@@ -395,12 +395,12 @@ template <typename T, int D>
 static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
   const int64_t blocks = (int64_t)p.n_items * p.nq;
   if (blocks == 0) return hipSuccess;
-  const bool drop = p.use_dropout != 0, alibi = p.slopes != nullptr;
+  const bool drop = p.use_dropout != 0;
   constexpr bool F32 = sizeof(T) == 4;
   constexpr int NWD = fwd_waves(true, F32), NWP = fwd_waves(false, F32);
   constexpr int OCD = fwd_occupancy(true, F32), OCP = fwd_occupancy(false, F32);
   const dim3 grid((unsigned)blocks), block(64 * (drop ? NWD : NWP));
-  return with_flags(drop, alibi, p.mbits != nullptr, [&](auto dr, auto al, auto mk) {
+  return with_flags(drop, pse_kind(p), p.mbits != nullptr, [&](auto dr, auto al, auto mk) {
     constexpr bool DR = decltype(dr)::value;
     hipLaunchKernelGGL((fa_fwd_kernel<T, D, DR ? NWD : NWP, DR ? OCD : OCP, DR, decltype(al)::value,
                                       decltype(mk)::value>),

@@ -25,6 +25,8 @@ struct FwdParams {
   const uint8_t* drop;
   int64_t drop_bytes;
   const float* slopes;
+  int32_t slope_bstride;    // 0: slopes [Nq]; Nq: slopes [B, Nq]
+  int32_t pse_sqrt;         // 1: the slopes generate pseType 3 (square-root distance)
   const float* sink;
   const int32_t* cu_q;
   const int32_t* cu_kv;
@@ -61,6 +63,8 @@ struct BwdParams {
   const uint8_t* drop;
   int64_t drop_bytes;
   const float* slopes;
+  int32_t slope_bstride;    // 0: slopes [Nq]; Nq: slopes [B, Nq]
+  int32_t pse_sqrt;         // 1: the slopes generate pseType 3 (square-root distance)
   const float* sink;
   const int32_t* cu_q;
   const int32_t* cu_kv;
@@ -94,18 +98,28 @@ constexpr int kKvBN = 128, kKvBM = 64;
 constexpr int kDqBM = 128, kDqBN = 64;
 constexpr int kPreRowsPerBlock = 64;
 
-// Calls f(drop, alibi, mask) with each flag as a std::integral_constant<bool, .>,
-// so a launcher names one kernel instance per combination.
+// Kind of the generated position bias (the ALIBI template argument of the
+// kernels): none, pseType 2 (linear distance) or pseType 3 (square-root distance).
+constexpr int kPseNone = 0, kPseLinear = 1, kPseSqrt = 2;
+template <typename P>
+int pse_kind(const P& p) {
+  return p.slopes == nullptr ? kPseNone : (p.pse_sqrt ? kPseSqrt : kPseLinear);
+}
+
+// Calls f(drop, pse, mask) with drop and mask as std::integral_constant<bool, .>
+// and pse (a kPse* kind) as std::integral_constant<int, .>, so a launcher names
+// one kernel instance per combination.
 template <typename F>
-hipError_t with_flags(bool drop, bool alibi, bool mask, F&& f) {
-  using T = std::true_type;
-  using N = std::false_type;
-  if (drop) {
-    if (alibi) return mask ? f(T{}, T{}, T{}) : f(T{}, T{}, N{});
-    return mask ? f(T{}, N{}, T{}) : f(T{}, N{}, N{});
-  }
-  if (alibi) return mask ? f(N{}, T{}, T{}) : f(N{}, T{}, N{});
-  return mask ? f(N{}, N{}, T{}) : f(N{}, N{}, N{});
+hipError_t with_flags(bool drop, int pse, bool mask, F&& f) {
+  auto by_mask = [&](auto d, auto a) {
+    return mask ? f(d, a, std::true_type{}) : f(d, a, std::false_type{});
+  };
+  auto by_pse = [&](auto d) {
+    if (pse == kPseSqrt) return by_mask(d, std::integral_constant<int, kPseSqrt>{});
+    if (pse == kPseLinear) return by_mask(d, std::integral_constant<int, kPseLinear>{});
+    return by_mask(d, std::integral_constant<int, kPseNone>{});
+  };
+  return drop ? by_pse(std::true_type{}) : by_pse(std::false_type{});
 }
 
 hipError_t launch_fwd(int dtype, int d, const FwdParams& p, hipStream_t s);

@@ -69,6 +69,15 @@ typedef int32_t fa_status;
 
 #define FA_TOKENS_DEFAULT 2147483647 /* preTokens / nextTokens default of the pages */
 
+/* fa_config.flags bits: how alibi_slopes generate the position bias (pse) of
+   aclnnFlashAttentionScoreV2 (pseType table: types 2 and 3 generate the pse
+   inside the operator from FLOAT32 slopes of shape [B,N] or [N]; the bias is added
+   after scaling and needs Lq_b == Lkv_b).  Ignored when alibi_slopes is NULL. */
+#define FA_FLAG_PSE_SQRT 1u          /* pseType 3: pse = -slope * sqrt(|i - j|); without
+                                        this bit pseType 2: pse = -slope * (i - j)      */
+#define FA_FLAG_SLOPES_PER_BATCH 2u  /* alibi_slopes is [B, Nq] (one row per sequence)
+                                        instead of [Nq]                                 */
+
 typedef struct fa_config {
   int64_t batch;                 /* B >= 1 sequences                                          */
   const int64_t* cu_seqlens_q;   /* HOST, B+1 entries: [0] = 0, non-decreasing, [B] = T_q     */
@@ -86,7 +95,7 @@ typedef struct fa_config {
                                     0 = fp32 atomic dQ accumulation where available (fp32
                                     with D = 128, and bf16 with D = 128 and alibi, always
                                     take the deterministic passes)                            */
-  int32_t flags;                 /* reserved, must be 0                                       */
+  int32_t flags;                 /* FA_FLAG_* bits; any other bit -> FA_ERR_PARAM_INVALID     */
   const int64_t* prefix;         /* HOST, B entries, read in FA_SPARSE_PREFIX only (ignored
                                     otherwise): N_b of the prefix-compressed mask
                                     (aclnnFlashAttentionUnpaddingScoreGrad "prefixOptional";
@@ -117,8 +126,10 @@ fa_status fa_fwd_workspace_size(const fa_config* cfg, uint64_t* bytes);
  *   aclnnFlashAttentionUnpaddingScoreGrad "dropMaskOptional", one flat stream of
  *   Nq * sum_b Lq_b*Lkv_b bits ordered (sequence, query head, row, key), bit n in
  *   byte n/8 at position n%8 (LSB first), 1 = keep; ceil(bits/8) bytes, 4-byte aligned.
- * alibi_slopes: device fp32 [Nq] or NULL: adds -slope_h*(i-j) after scaling
- *   (pseType 2, i and j local to the sequence; requires Lq_b == Lkv_b).
+ * alibi_slopes: device fp32 [Nq] (or [B, Nq] with FA_FLAG_SLOPES_PER_BATCH) or NULL:
+ *   adds -slope*(i-j) (pseType 2) or, with FA_FLAG_PSE_SQRT, -slope*sqrt(|i-j|)
+ *   (pseType 3) after scaling, i and j local to the sequence; requires
+ *   Lq_b == Lkv_b > 0 for every sequence.
  * sink: device fp32 [Nq] or NULL: per-head sink logit in the softmax denominator.
  * Outputs (device): out [T_q,Nq,D] of cfg->dtype; softmax_max, softmax_sum fp32 [T_q,Nq].
  * All tensor pointers must be 16-byte aligned.

@@ -26,8 +26,11 @@ the design notes):
     taken before dropout.  Keep bits: one flat stream over batch, query head,
     query row, key (the page's size formula), LSB first in each byte.
   * "scale" replaces 1/sqrt(d) everywhere (scaleValue is "the Muls scalar").
-  * ALiBi (pseType 2, slopes per query head): pse = -slope_h * (i - j) with
-    i, j local to the sequence.
+  * Generated pse (aclnnFlashAttentionScoreV2, pseType table: types 2 and 3
+    build the bias inside the operator from FLOAT32 slopes of shape [N] or
+    [B, N]): pseType 2 is ALiBi, pse = -slope_h * (i - j); pseType 3 passes the
+    distance through a square root, pse = -slope_h * sqrt(|i - j|); i, j local
+    to the sequence, the slope per query head (and per sequence for [B, N]).
   * The sink logit is compared with the scaled, biased logits and is not
     itself scaled.
   * GQA: query head h uses kv head h // (Nq / Nkv).
@@ -76,11 +79,16 @@ def allowed(lq: int, lkv: int, sparse_mode: int, pre_tokens: int = INT_MAX_TOKEN
     raise ValueError(f"sparse_mode {sparse_mode} not covered")
 
 
-def alibi_pse(lq: int, lkv: int, slope: float) -> np.ndarray:
-    """pseType 2 bias for one head: -slope * (i - j), local row/key indices."""
+def alibi_pse(lq: int, lkv: int, slope: float, pse_type: int = 2) -> np.ndarray:
+    """Generated bias for one (sequence, head), local row/key indices:
+    pseType 2: -slope * (i - j);  pseType 3: -slope * sqrt(|i - j|)."""
     i = np.arange(lq, dtype=np.float64)[:, None]
     j = np.arange(lkv, dtype=np.float64)[None, :]
-    return -float(slope) * (i - j)
+    if pse_type == 2:
+        return -float(slope) * (i - j)
+    if pse_type == 3:
+        return -float(slope) * np.sqrt(np.abs(i - j))
+    raise ValueError(f"pse_type {pse_type} is not a generated pse")
 
 
 def keep_bits(drop_mask: np.ndarray, bit_base: int, lq: int, lkv: int) -> np.ndarray:
@@ -95,7 +103,8 @@ class _Problem:
     """Inputs of one call, upcast to fp64, with the per-sequence bookkeeping."""
 
     def __init__(self, q, k, v, cu_q, cu_kv, head_num, kv_heads, scale, keep_prob, sparse_mode,
-                 pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix=None, atten_mask=None):
+                 pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix=None, atten_mask=None,
+                 pse_type=2):
         # kept in their given precision; each (sequence, head) slice is upcast to fp64 when used
         self.q = np.asarray(q)
         self.k = np.asarray(k)
@@ -113,7 +122,9 @@ class _Problem:
         self.pre = int(pre_tokens)
         self.next = int(next_tokens)
         self.drop_mask = None if drop_mask is None else np.asarray(drop_mask, dtype=np.uint8)
+        # slopes [Nq] (shared by the sequences) or [B, Nq]
         self.slopes = None if alibi_slopes is None else np.asarray(alibi_slopes, dtype=np.float32).astype(np.float64)
+        self.pse_type = int(pse_type)
         self.sink = None if sink is None else np.asarray(sink, dtype=np.float32).astype(np.float64)
         self.batch = len(self.cu_q) - 1
         self.prefix = np.zeros(self.batch, dtype=np.int64) if prefix is None else np.asarray(prefix, dtype=np.int64)
@@ -133,7 +144,8 @@ class _Problem:
         kb = self.k[k0:k1, g, :].astype(np.float64)
         s = self.scale * (qb @ kb.T)
         if self.slopes is not None:
-            s = s + alibi_pse(lq, lkv, self.slopes[h])
+            slope = self.slopes[b, h] if self.slopes.ndim == 2 else self.slopes[h]
+            s = s + alibi_pse(lq, lkv, slope, self.pse_type)
         ok = allowed(lq, lkv, self.mode, self.pre, self.next, int(self.prefix[b]), self.atten_mask)
         s = np.where(ok, s, -np.inf)
         m = s.max(axis=1) if lkv > 0 else np.full(lq, -np.inf)
@@ -162,9 +174,10 @@ class _Problem:
 
 def _problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob=1.0,
              sparse_mode=0, pre_tokens=INT_MAX_TOKENS, next_tokens=INT_MAX_TOKENS, drop_mask=None,
-             alibi_slopes=None, sink=None, prefix=None, atten_mask=None):
+             alibi_slopes=None, sink=None, prefix=None, atten_mask=None, pse_type=2):
     return _Problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob,
-                    sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix, atten_mask)
+                    sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix, atten_mask,
+                    pse_type)
 
 
 def _selected(subset, n):
@@ -173,12 +186,14 @@ def _selected(subset, n):
 
 def forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob=1.0,
             sparse_mode=0, pre_tokens=INT_MAX_TOKENS, next_tokens=INT_MAX_TOKENS, drop_mask=None,
-            alibi_slopes=None, sink=None, batches=None, heads=None, prefix=None, atten_mask=None):
+            alibi_slopes=None, sink=None, batches=None, heads=None, prefix=None, atten_mask=None,
+            pse_type=2):
     """Attention forward.  Returns O [T_q, Nq, D], softmax max m [T_q, Nq] and
     softmax sum l [T_q, Nq] (fp64).  With `batches` / `heads`, only those
     sequences / query heads are computed and every other entry is NaN."""
     pr = _problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob,
-                  sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix, atten_mask)
+                  sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix, atten_mask,
+                  pse_type)
     tq, d = pr.q.shape[0], pr.v.shape[2]
     out = np.full((tq, pr.nq, d), np.nan)
     mx = np.full((tq, pr.nq), np.nan)
@@ -194,14 +209,16 @@ def forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, kee
 
 def backward(q, k, v, dy, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob=1.0,
              sparse_mode=0, pre_tokens=INT_MAX_TOKENS, next_tokens=INT_MAX_TOKENS, drop_mask=None,
-             alibi_slopes=None, sink=None, batches=None, heads=None, prefix=None, atten_mask=None):
+             alibi_slopes=None, sink=None, batches=None, heads=None, prefix=None, atten_mask=None,
+             pse_type=2):
     """Attention backward.  Returns dQ [T_q, Nq, D], dK, dV [T_kv, Nkv, D] and
     dSink [Nq] (None without a sink).  With `batches` / `heads`, only those
     sequences / query heads contribute: rows and keys of other sequences are NaN,
     dK/dV of a kv head are complete only if all of its query heads are chosen,
     and dSink sums the chosen sequences."""
     pr = _problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob,
-                  sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix, atten_mask)
+                  sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix, atten_mask,
+                  pse_type)
     dy = np.asarray(dy)
     dq = np.full(pr.q.shape, np.nan)
     dk = np.full(pr.k.shape, np.nan)

@@ -27,7 +27,8 @@ def config_of(case: wl.Case, deterministic: bool = True, mask=None) -> fa.Config
     """mask: the case's attenMask as a device tensor (required when the case has one)."""
     return fa.Config(case.cu_seqlens_q, case.cu_seqlens_kv, case.head_num, case.kv_heads, case.head_dim,
                      case.dtype, case.scale, case.keep_prob, case.sparse_mode, case.pre_tokens,
-                     case.next_tokens, deterministic, prefix=case.prefix, atten_mask=mask)
+                     case.next_tokens, deterministic, prefix=case.prefix, atten_mask=mask, pse_type=case.pse_type,
+                     slopes_per_batch=case.alibi_slopes is not None and case.alibi_slopes.ndim == 2)
 
 
 def device_inputs(case: wl.Case, device="cuda"):
@@ -63,7 +64,8 @@ def run_oracle(case: wl.Case, batches=None, heads=None, backward: bool = True):
     q, k, v = host_f32(case.q), host_f32(case.k), host_f32(case.v)
     kw = dict(keep_prob=case.keep_prob, sparse_mode=case.sparse_mode, pre_tokens=case.pre_tokens,
               next_tokens=case.next_tokens, drop_mask=case.drop_mask, alibi_slopes=case.alibi_slopes,
-              sink=case.sink, batches=batches, heads=heads, prefix=case.prefix, atten_mask=case.atten_mask)
+              sink=case.sink, batches=batches, heads=heads, prefix=case.prefix, atten_mask=case.atten_mask,
+              pse_type=case.pse_type)
     o, m, l = oracle.forward(q, k, v, case.cu_seqlens_q, case.cu_seqlens_kv, case.head_num, case.kv_heads,
                              case.scale, **kw)
     res = dict(out=o, m=m, l=l)

@@ -103,9 +103,18 @@ def test_element_types_accepted():
 
 
 def test_bad_flags_and_batch_limits():
-    cfg = _cfg()
-    cfg.c.flags = 1
-    assert _fwd(cfg) == fa.FA_ERR_PARAM_INVALID
+    for bad in (4, 1 << 30, -1):
+        cfg = _cfg()
+        cfg.c.flags = bad
+        assert _fwd(cfg) == fa.FA_ERR_PARAM_INVALID, bad
+    n = ctypes.c_uint64(0)
+    for good in (fa.FA_FLAG_PSE_SQRT, fa.FA_FLAG_SLOPES_PER_BATCH, fa.FA_FLAG_PSE_SQRT | fa.FA_FLAG_SLOPES_PER_BATCH):
+        cfg = _cfg()
+        cfg.c.flags = good
+        assert fa.lib().fa_fwd_workspace_size(cfg.ref, ctypes.byref(n)) == fa.FA_OK, good
+    assert _cfg(pse_type=3, slopes_per_batch=True).c.flags == fa.FA_FLAG_PSE_SQRT | fa.FA_FLAG_SLOPES_PER_BATCH
+    with pytest.raises(ValueError):
+        _cfg(pse_type=1)
     cfg = _cfg()
     cfg.c.deterministic = 2
     assert _bwd(cfg) == fa.FA_ERR_PARAM_INVALID

@@ -46,6 +46,14 @@ EDGE_CASES = {
                                 pre_tokens=50, next_tokens=3, keep_prob=0.8, sink=True, mask=(0.2, [])),
     "mask_mode0_alibi_gqa": dict(lens_q=[150, 300], head_num=4, kv_heads=1, head_dim=128, sparse_mode=0,
                                  alibi=True, mask=(0.5, [7])),
+    # generated pse: pseType 3 (square-root distance) and [B, N] slopes
+    "pse_sqrt_causal_gqa": dict(lens_q=[150, 300, 37], head_num=4, kv_heads=2, head_dim=128, sparse_mode=3,
+                                alibi=True, pse_type=3),
+    "pse_sqrt_batch_slopes_drop_sink": dict(lens_q=[190, 67, 129], head_num=2, kv_heads=1, head_dim=64,
+                                            sparse_mode=2, alibi=True, pse_type=3, slopes_per_batch=True,
+                                            keep_prob=0.8, sink=True),
+    "alibi_batch_slopes_band": dict(lens_q=[257, 64], head_num=4, kv_heads=4, head_dim=128, sparse_mode=4,
+                                    pre_tokens=40, next_tokens=0, alibi=True, slopes_per_batch=True),
 }
 
 

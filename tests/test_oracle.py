@@ -125,6 +125,63 @@ def test_q_zero_alibi_geometric_weights():
         np.testing.assert_allclose(l[i, 0], w.sum() / r ** i, rtol=1e-12)
 
 
+def test_pse_sqrt_on_square_distances_equals_linear():
+    # pseType 3 turns distance d into sqrt(d); keys at distances 0, 1, 4, 9 of row 9
+    # (all others masked out) then carry the pseType 2 biases of distances 0, 1, 2, 3,
+    # i.e. of every key of row 3 in a causal sequence of length 4 holding those keys
+    d, slope = 3, np.array([0.61], np.float32)
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((10, 1, d))
+    k, v = rng.standard_normal((10, 1, d)), rng.standard_normal((10, 1, d))
+    dy = rng.standard_normal((10, 1, d))
+    mask = np.ones((10, 10), np.uint8)
+    mask[:, 9] = 0                                   # every row keeps its diagonal-free key 9 ...
+    mask[9, :] = 1
+    mask[9, [9, 8, 5, 0]] = 0                        # ... and row 9 keeps exactly distances 0, 1, 4, 9
+    for r in range(9):
+        mask[r, :] = 1
+        mask[r, 0] = 0
+    kw3 = dict(sparse_mode=1, atten_mask=mask, alibi_slopes=slope, pse_type=3)
+    o3, m3, l3 = oracle.forward(q, k, v, [0, 10], [0, 10], 1, 1, 0.7, **kw3)
+    sel = [0, 5, 8, 9]                               # key j' of the short sequence = key sel[j']
+    q4 = np.concatenate([q[[0, 1, 2]], q[[9]]])      # row 3 of the short sequence is row 9
+    dy4 = np.concatenate([np.zeros((3, 1, d)), dy[[9]]])
+    kw2 = dict(sparse_mode=3, alibi_slopes=slope, pse_type=2)
+    o2, m2, l2 = oracle.forward(q4, k[sel], v[sel], [0, 4], [0, 4], 1, 1, 0.7, **kw2)
+    np.testing.assert_allclose(o3[9], o2[3], rtol=1e-13)
+    np.testing.assert_allclose([m3[9, 0], l3[9, 0]], [m2[3, 0], l2[3, 0]], rtol=1e-13)
+    # the gradient reaching row 9's query and the four keys agrees too
+    dy3 = np.zeros_like(dy)
+    dy3[9] = dy[9]
+    dq3, dk3, dv3, _ = oracle.backward(q, k, v, dy3, [0, 10], [0, 10], 1, 1, 0.7, **kw3)
+    dq2, dk2, dv2, _ = oracle.backward(q4, k[sel], v[sel], dy4, [0, 4], [0, 4], 1, 1, 0.7, **kw2)
+    np.testing.assert_allclose(dq3[9], dq2[3], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dk3[sel], dk2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(dv3[sel], dv2, rtol=1e-12, atol=1e-14)
+
+
+def test_batch_slopes_equal_per_sequence_calls():
+    # [B, N] slopes: sequence b uses row b, as a call on that sequence alone with [N] slopes
+    lens = [7, 12, 5]
+    cu = _cu(lens)
+    rng = np.random.default_rng(8)
+    q, k, v = (rng.standard_normal((cu[-1], 2, 4)) for _ in range(3))
+    dy = rng.standard_normal((cu[-1], 2, 4))
+    slopes = wl.batch_alibi_slopes(3, 3, 2)
+    assert not np.allclose(slopes[0], slopes[1])
+    for pt in (2, 3):
+        o, m, l = oracle.forward(q, k, v, cu, cu, 2, 2, 0.5, sparse_mode=3, alibi_slopes=slopes, pse_type=pt)
+        dq, dk, dv, _ = oracle.backward(q, k, v, dy, cu, cu, 2, 2, 0.5, sparse_mode=3, alibi_slopes=slopes,
+                                        pse_type=pt)
+        for b, L in enumerate(lens):
+            s = slice(cu[b], cu[b + 1])
+            kw = dict(sparse_mode=3, alibi_slopes=slopes[b], pse_type=pt)
+            ob, mb, lb = oracle.forward(q[s], k[s], v[s], [0, L], [0, L], 2, 2, 0.5, **kw)
+            dqb, dkb, dvb, _ = oracle.backward(q[s], k[s], v[s], dy[s], [0, L], [0, L], 2, 2, 0.5, **kw)
+            for got, ref in ((o[s], ob), (m[s], mb), (l[s], lb), (dq[s], dqb), (dk[s], dkb), (dv[s], dvb)):
+                np.testing.assert_array_equal(got, ref)
+
+
 # --------------------------------------------------------------------------- library routine (SDPA)
 
 def _sdpa(q, k, v, scale, attn_mask=None, is_causal=False, gqa=False):
@@ -349,7 +406,7 @@ def test_dv_is_pt_transpose_dy():
 # --------------------------------------------------------------------------- autograd + finite differences
 
 def _torch_attention(q, k, v, sink, cu_q, cu_kv, nq, nkv, scale, mode, pre, nxt, keep, bits, slopes, prefix=None,
-                     atten_mask=None):
+                     atten_mask=None, pse_type=2):
     """A second, plainly written attention in torch: the sink enters as an extra
     softmax column that is dropped afterwards; masks come from tril/triu."""
     outs = []
@@ -364,7 +421,11 @@ def _torch_attention(q, k, v, sink, cu_q, cu_kv, nq, nkv, scale, mode, pre, nxt,
             if slopes is not None:
                 ii = torch.arange(lq, dtype=torch.float64)[:, None]
                 jj = torch.arange(lkv, dtype=torch.float64)[None, :]
-                s = s + float(slopes[h]) * (jj - ii)
+                slope = float(slopes[b][h] if np.ndim(slopes) == 2 else slopes[h])
+                if pse_type == 3:
+                    s = s - slope * torch.sqrt(torch.abs(ii - jj))
+                else:
+                    s = s + slope * (jj - ii)
             ones = torch.ones(lq, lkv, dtype=torch.bool)
             if mode == 0:
                 ok = ones
@@ -436,6 +497,29 @@ def test_backward_matches_autograd(mode, pre, nxt):
     np.testing.assert_allclose(dk, tk.grad.numpy(), rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(dv, tv.grad.numpy(), rtol=1e-11, atol=1e-12)
     np.testing.assert_allclose(ds, ts.grad.numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_backward_matches_autograd_pse_sqrt_batch_slopes():
+    # pseType 3 with [B, N] slopes (aclnnFlashAttentionScoreV2, pseType table), causal, dropout and sink
+    c = _feature_case(61)
+    scale = 0.45
+    slopes = wl.batch_alibi_slopes(61, 2, c["nq"])
+    tq = torch.tensor(c["q"], requires_grad=True)
+    tk = torch.tensor(c["k"], requires_grad=True)
+    tv = torch.tensor(c["v"], requires_grad=True)
+    ts = torch.tensor(c["sink"].astype(np.float64), requires_grad=True)
+    bits = np.unpackbits(c["mask"], bitorder="little")
+    out = _torch_attention(tq, tk, tv, ts, c["cq"], c["ck"], c["nq"], c["nkv"], scale, 3, 0, 0, c["keep"], bits,
+                           slopes, pse_type=3)
+    (out * torch.from_numpy(c["dy"])).sum().backward()
+    kw = dict(sparse_mode=3, keep_prob=c["keep"], drop_mask=c["mask"], alibi_slopes=slopes, sink=c["sink"],
+              pse_type=3)
+    o, _, _ = oracle.forward(c["q"], c["k"], c["v"], c["cq"], c["ck"], c["nq"], c["nkv"], scale, **kw)
+    np.testing.assert_allclose(o, out.detach().numpy(), rtol=1e-12, atol=1e-13)
+    dq, dk, dv, ds = oracle.backward(c["q"], c["k"], c["v"], c["dy"], c["cq"], c["ck"], c["nq"], c["nkv"],
+                                     scale, **kw)
+    for got, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad), (ds, ts.grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=1e-11, atol=1e-12)
 
 
 def test_backward_matches_finite_differences():

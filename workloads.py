@@ -58,7 +58,8 @@ class Case:
     pre_tokens: int = INT_MAX_TOKENS
     next_tokens: int = INT_MAX_TOKENS
     drop_mask: Optional[np.ndarray] = None     # uint8 packed bits
-    alibi_slopes: Optional[np.ndarray] = None  # float32 [Nq]
+    alibi_slopes: Optional[np.ndarray] = None  # float32 [Nq] or [B, Nq]
+    pse_type: int = 2                          # 2: -slope*(i-j); 3: -slope*sqrt(|i-j|)
     sink: Optional[np.ndarray] = None          # float32 [Nq]
     prefix: Optional[np.ndarray] = None        # int64 [B]: prefix N per sequence (sparse mode 6)
     atten_mask: Optional[np.ndarray] = None    # uint8 [S1Max, S2Max], nonzero = masked (modes 0/1/4)
@@ -117,6 +118,13 @@ def alibi_slopes(head_num: int) -> np.ndarray:
     return np.power(2.0, -8.0 * (h + 1.0) / head_num).astype(np.float32)
 
 
+def batch_alibi_slopes(seed, batch: int, head_num: int) -> np.ndarray:
+    """[B, Nq] slopes: the geometric slopes of alibi_slopes scaled per sequence by
+    a factor drawn uniformly from [0.5, 1.5), rounded to fp32."""
+    f = np.random.default_rng([seed, 8]).uniform(0.5, 1.5, (batch, 1))
+    return (alibi_slopes(head_num).astype(np.float64)[None, :] * f).astype(np.float32)
+
+
 def lognormal_lengths(seed, total: int, batch: int, median: float, lo: int, hi: int) -> np.ndarray:
     """Lognormal lengths (median `median`, sigma sqrt(2 ln 2) so the mean is 2*median),
     clipped to [lo, hi], rescaled to sum to `total`, rounded, and the residual
@@ -146,8 +154,9 @@ def lognormal_lengths(seed, total: int, batch: int, median: float, lo: int, hi: 
 def make_case(name, lens_q, lens_kv=None, *, head_num, kv_heads, head_dim, dtype=torch.bfloat16,
               scale=None, keep_prob=1.0, sparse_mode=MODE_NONE, pre_tokens=INT_MAX_TOKENS,
               next_tokens=INT_MAX_TOKENS, alibi=False, sink=False, seed=0, dy_mult=1.0,
-              drop_mask=None, prefix=None, atten_mask=None) -> Case:
-    """A case built from explicit lengths; every tensor is drawn from default_rng([seed, t])."""
+              drop_mask=None, prefix=None, atten_mask=None, pse_type=2, slopes_per_batch=False) -> Case:
+    """A case built from explicit lengths; every tensor is drawn from default_rng([seed, t]).
+    alibi=True adds generated-pse slopes ([Nq], or [B, Nq] with slopes_per_batch) of pseType pse_type."""
     lens_q = np.asarray(lens_q, dtype=np.int64)
     lens_kv = lens_q.copy() if lens_kv is None else np.asarray(lens_kv, dtype=np.int64)
     cu_q, cu_kv = cu_from_lengths(lens_q), cu_from_lengths(lens_kv)
@@ -163,11 +172,14 @@ def make_case(name, lens_q, lens_kv=None, *, head_num, kv_heads, head_dim, dtype
         sink_v = np.random.default_rng([seed, 5]).standard_normal(head_num, dtype=np.float32)
     if keep_prob < 1.0 and drop_mask is None:
         drop_mask = draw_keep_mask([seed, 6], dropout_bits_total(lens_q, lens_kv, head_num), keep_prob)
+    slopes = None
+    if alibi:
+        slopes = batch_alibi_slopes(seed, len(lens_q), head_num) if slopes_per_batch else alibi_slopes(head_num)
     return Case(name=name, dtype=dtype, cu_seqlens_q=cu_q, cu_seqlens_kv=cu_kv, head_num=head_num,
                 kv_heads=kv_heads, head_dim=head_dim, scale=float(scale), q=q, k=k, v=v, dy=dy,
                 keep_prob=float(keep_prob), sparse_mode=sparse_mode, pre_tokens=int(pre_tokens),
                 next_tokens=int(next_tokens), drop_mask=drop_mask,
-                alibi_slopes=alibi_slopes(head_num) if alibi else None, sink=sink_v,
+                alibi_slopes=slopes, pse_type=int(pse_type), sink=sink_v,
                 prefix=None if prefix is None else np.asarray(prefix, dtype=np.int64),
                 atten_mask=None if atten_mask is None else np.ascontiguousarray(atten_mask, dtype=np.uint8))
 
