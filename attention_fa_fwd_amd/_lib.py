@@ -30,9 +30,13 @@ FA_DTYPE_FP16 = 2
 FA_FLAG_PSE_SQRT = 1
 FA_FLAG_SLOPES_PER_BATCH = 2
 TOKENS_DEFAULT = 2147483647
+FA_LAYOUT_BSH = 0
+FA_LAYOUT_BSND = 1
+FA_LAYOUT_BNSD = 2
 
 EXPORTED = ("fa_fwd_workspace_size", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd", "fa_status_string",
-            "fa_debug_schedule", "fa_profile_enable", "fa_profile_read", "fa_profile_kernel_count")
+            "fa_debug_schedule", "fa_profile_enable", "fa_profile_read", "fa_profile_kernel_count",
+            "fa_decode_workspace_size", "fa_decode")
 
 
 class FaConfig(ctypes.Structure):
@@ -55,6 +59,22 @@ class FaConfig(ctypes.Structure):
         ("atten_mask", ctypes.c_void_p),
         ("mask_rows", ctypes.c_int64),
         ("mask_cols", ctypes.c_int64),
+    ]
+
+
+class FaDecodeConfig(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("max_seq_len", ctypes.c_int64),
+        ("actual_seq_lengths", ctypes.POINTER(ctypes.c_int64)),
+        ("num_heads", ctypes.c_int64),
+        ("num_kv_heads", ctypes.c_int64),
+        ("head_dim", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+        ("layout", ctypes.c_int32),
+        ("scale", ctypes.c_double),
+        ("atten_mask", ctypes.c_void_p),
+        ("flags", ctypes.c_int32),
     ]
 
 
@@ -89,8 +109,11 @@ def lib() -> ctypes.CDLL:
         L.fa_profile_read.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_char_p),
                                       ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
         L.fa_profile_kernel_count.restype = ctypes.c_int32
+        decp = ctypes.POINTER(FaDecodeConfig)
+        L.fa_decode_workspace_size.argtypes = [decp, u64p]
+        L.fa_decode.argtypes = [decp, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
         for name in ("fa_fwd_workspace_size", "fa_bwd_workspace_size", "fa_fwd", "fa_bwd", "fa_debug_schedule",
-                     "fa_profile_enable", "fa_profile_read"):
+                     "fa_profile_enable", "fa_profile_read", "fa_decode_workspace_size", "fa_decode"):
             getattr(L, name).restype = ctypes.c_int32
         _lib = L
     return _lib
@@ -281,3 +304,66 @@ def fa_profile_read() -> dict:
         _check(lib().fa_profile_read(k, ctypes.byref(name), ctypes.byref(ms), ctypes.byref(cnt)), "fa_profile_read")
         res[name.value.decode()] = (ms.value, cnt.value)
     return res
+
+
+_LAYOUTS = {"BSH": FA_LAYOUT_BSH, "BSND": FA_LAYOUT_BSND, "BNSD": FA_LAYOUT_BNSD}
+
+
+class DecodeConfig:
+    """Owns the host actual_seq_lengths array for the lifetime of a fa_decode_config.
+    layout: "BSH", "BSND" or "BNSD" (inputLayout); atten_mask: device bool / uint8 [B, S] or None."""
+
+    def __init__(self, batch, max_seq_len, num_heads, num_kv_heads, head_dim, dtype, scale, layout="BSND",
+                 actual_seq_lengths=None, atten_mask=None):
+        self.lens = None if actual_seq_lengths is None else np.ascontiguousarray(
+            np.asarray(actual_seq_lengths, dtype=np.int64))
+        if self.lens is not None and self.lens.shape != (int(batch),):
+            raise ValueError("actual_seq_lengths must hold one length per sequence")
+        self.atten_mask = atten_mask
+        if atten_mask is not None:
+            if (atten_mask.dim() != 2 or tuple(atten_mask.shape) != (int(batch), int(max_seq_len))
+                    or atten_mask.dtype not in (torch.uint8, torch.bool) or not atten_mask.is_contiguous()):
+                raise ValueError("atten_mask must be a contiguous bool or uint8 tensor [B, S]")
+        if isinstance(dtype, torch.dtype):
+            dtype = {torch.bfloat16: FA_DTYPE_BF16, torch.float16: FA_DTYPE_FP16}.get(dtype, -1)
+        self.layout_name = layout
+        self.c = FaDecodeConfig(
+            batch=int(batch), max_seq_len=int(max_seq_len),
+            actual_seq_lengths=(None if self.lens is None else self.lens.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))),
+            num_heads=int(num_heads), num_kv_heads=int(num_kv_heads), head_dim=int(head_dim), dtype=int(dtype),
+            layout=_LAYOUTS.get(layout, -1), scale=float(scale),
+            atten_mask=(None if atten_mask is None else atten_mask.data_ptr()), flags=0)
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.c)
+
+    def kv_shape(self):
+        b, s, nkv, d = self.c.batch, self.c.max_seq_len, self.c.num_kv_heads or self.c.num_heads, self.c.head_dim
+        return {"BSH": (b, s, nkv * d), "BSND": (b, s, nkv, d), "BNSD": (b, nkv, s, d)}[self.layout_name]
+
+
+def fa_decode_workspace_size(cfg: DecodeConfig) -> int:
+    n = ctypes.c_uint64(0)
+    _check(lib().fa_decode_workspace_size(cfg.ref, ctypes.byref(n)), "fa_decode_workspace_size")
+    return n.value
+
+
+def fa_decode(cfg: DecodeConfig, q, k, v, out=None, workspace=None):
+    """Decode attention through libfa.so on the current stream; q, out [B, Nq, D]
+    (any view of those elements, e.g. [B, 1, Nq*D]), k, v in cfg's layout.  Returns out."""
+    dev = q.device
+    c = cfg.c
+    qshape = (c.batch, c.num_heads, c.head_dim)
+    if q.numel() != c.batch * c.num_heads * c.head_dim or not q.is_contiguous():
+        raise ValueError(f"q must be a contiguous tensor of {qshape} elements")
+    for name, t in (("k", k), ("v", v)):
+        _check_tensor(name, t, cfg.kv_shape(), q.dtype, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, tuple(q.shape), q.dtype, dev)
+    ws = _workspace(fa_decode_workspace_size(cfg), dev, workspace)
+    st = lib().fa_decode(cfg.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ws), ctypes.c_uint64(ws.numel()),
+                         _stream_handle(dev))
+    _check(st, "fa_decode")
+    return out

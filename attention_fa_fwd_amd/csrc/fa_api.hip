@@ -252,9 +252,10 @@ Layout bwd_layout_bound(const Problem& pr) {
 }
 
 // ---- kernel timing (measurement hook) ----
-enum KernelId { K_FWD = 0, K_PRE, K_KV, K_DQ, K_CONVERT, K_DSINK, K_ZERO, K_MASK, K_COUNT };
-const char* kKernelNames[K_COUNT] = {"fa_fwd", "fa_bwd_preprocess", "fa_bwd_dkdv", "fa_bwd_dq",
-                                     "fa_bwd_dq_convert", "fa_bwd_dsink_reduce", "fa_zero_f32", "fa_mask_pack"};
+enum KernelId { K_FWD = 0, K_PRE, K_KV, K_DQ, K_CONVERT, K_DSINK, K_ZERO, K_MASK, K_DEC, K_DEC_REDUCE, K_COUNT };
+const char* kKernelNames[K_COUNT] = {"fa_fwd",         "fa_bwd_preprocess", "fa_bwd_dkdv",  "fa_bwd_dq",
+                                     "fa_bwd_dq_convert", "fa_bwd_dsink_reduce", "fa_zero_f32", "fa_mask_pack",
+                                     "fa_decode",      "fa_decode_reduce"};
 struct ProfState {
   std::mutex mu;
   bool on = false;
@@ -312,6 +313,102 @@ std::vector<char> stage_block(const Problem& pr, const Layout& L, const std::vec
   std::memcpy(host.data() + L.items0, i0.data(), sizeof(WorkItem) * i0.size());
   if (i1) std::memcpy(host.data() + L.items1, i1->data(), sizeof(WorkItem) * i1->size());
   return host;
+}
+
+// ---- decode attention (aclnnIncreFlashAttentionV2) ----
+constexpr int64_t kMaxDecBatch = 65536;            // B limit of the decode page ("B <= 65536")
+constexpr int64_t kMaxDecSeq = 1 << 24;            // padded cache length limit (keys index in int32)
+constexpr int64_t kMaxDecGroup = 64;               // numHeads / numKeyValueHeads <= 64
+constexpr int64_t kDecTargetItems = 2048;          // split the keys until about this many work items remain
+constexpr int64_t kDecMinChunk = 128, kDecMaxChunk = 8192;   // keys per work item (4 waves x 32-key steps)
+
+struct DecProblem {
+  int64_t batch = 0, s = 0, nq = 0, nkv = 0, d = 0;
+  int dtype = 0, layout = 0;
+  double scale = 0;
+  const uint8_t* mask = nullptr;
+  std::vector<int32_t> lens;   // actual key length of each sequence
+};
+
+fa_status parse_decode(const fa_decode_config* cfg, DecProblem* pr) {
+  if (!cfg) return FA_ERR_PARAM_NULLPTR;
+  if (cfg->batch < 1 || cfg->batch > kMaxDecBatch) return FA_ERR_PARAM_INVALID;
+  if (cfg->max_seq_len < 1 || cfg->max_seq_len > kMaxDecSeq) return FA_ERR_PARAM_INVALID;
+  if (cfg->num_heads < 1 || cfg->num_heads > kMaxHeads) return FA_ERR_PARAM_INVALID;
+  const int64_t nkv = cfg->num_kv_heads == 0 ? cfg->num_heads : cfg->num_kv_heads;
+  if (nkv < 1 || cfg->num_heads % nkv != 0 || cfg->num_heads / nkv > kMaxDecGroup) return FA_ERR_PARAM_INVALID;
+  if (cfg->head_dim != 64 && cfg->head_dim != 128) return FA_ERR_PARAM_INVALID;
+  if (cfg->dtype != FA_DTYPE_BF16 && cfg->dtype != FA_DTYPE_FP16) return FA_ERR_PARAM_INVALID;
+  if (cfg->layout != FA_LAYOUT_BSH && cfg->layout != FA_LAYOUT_BSND && cfg->layout != FA_LAYOUT_BNSD)
+    return FA_ERR_PARAM_INVALID;
+  if (!std::isfinite(cfg->scale) || cfg->flags != 0) return FA_ERR_PARAM_INVALID;
+  pr->batch = cfg->batch;
+  pr->s = cfg->max_seq_len;
+  pr->nq = cfg->num_heads;
+  pr->nkv = nkv;
+  pr->d = cfg->head_dim;
+  pr->dtype = cfg->dtype;
+  pr->layout = cfg->layout;
+  pr->scale = cfg->scale;
+  pr->mask = cfg->atten_mask;
+  pr->lens.assign((size_t)cfg->batch, (int32_t)cfg->max_seq_len);
+  if (cfg->actual_seq_lengths) {
+    for (int64_t b = 0; b < cfg->batch; ++b) {
+      const int64_t L = cfg->actual_seq_lengths[b];
+      if (L < 0 || L > cfg->max_seq_len) return FA_ERR_PARAM_INVALID;
+      pr->lens[(size_t)b] = (int32_t)L;
+    }
+  }
+  return FA_OK;
+}
+
+// Work split: every (sequence, kv head) gets ceil(L_b / chunk) items (at least one,
+// so empty sequences still write zeros); the chunk doubles from 128 keys until at
+// most about kDecTargetItems items remain, so short batches still fill the chip.
+struct DecPlan {
+  int64_t chunk = kDecMinChunk;
+  std::vector<fa::DecItem> items;
+  std::vector<int32_t> first_slot, n_split;
+  int64_t n_slots = 0;
+  size_t off_items = 0, off_first = 0, off_nsplit = 0, staged = 0;
+  size_t off_o = 0, off_m = 0, off_l = 0, total = 0;
+};
+
+DecPlan plan_decode(const DecProblem& pr) {
+  DecPlan P;
+  int64_t keys = 0;
+  for (int32_t L : pr.lens) keys += std::max<int64_t>(L, 1);
+  while (P.chunk < kDecMaxChunk && keys * pr.nkv > kDecTargetItems * P.chunk) P.chunk *= 2;
+  P.first_slot.assign((size_t)(pr.batch * pr.nkv), -1);
+  P.n_split.assign((size_t)pr.batch, 1);
+  for (int64_t b = 0; b < pr.batch; ++b) {
+    const int64_t L = pr.lens[(size_t)b];
+    const int64_t n = std::max<int64_t>(1, (L + P.chunk - 1) / P.chunk);
+    P.n_split[(size_t)b] = (int32_t)n;
+    for (int64_t g = 0; g < pr.nkv; ++g) {
+      if (n > 1) P.first_slot[(size_t)(b * pr.nkv + g)] = (int32_t)P.n_slots;
+      for (int64_t c = 0; c < n; ++c) {
+        fa::DecItem it;
+        it.b = (int32_t)b;
+        it.g = (int32_t)g;
+        it.lo = (int32_t)(c * P.chunk);
+        it.hi = (int32_t)std::min(L, (c + 1) * P.chunk);
+        it.slot = n > 1 ? (int32_t)(P.n_slots++) : -1;
+        P.items.push_back(it);
+      }
+    }
+  }
+  const int64_t group = pr.nq / pr.nkv;
+  size_t off = 0;
+  P.off_items = off; off = align_up(off + sizeof(fa::DecItem) * P.items.size());
+  P.off_first = off; off = align_up(off + 4 * P.first_slot.size());
+  P.off_nsplit = off; off = align_up(off + 4 * P.n_split.size());
+  P.staged = off;
+  P.off_o = off; off = align_up(off + 4 * (size_t)(P.n_slots * group * pr.d));
+  P.off_m = off; off = align_up(off + 4 * (size_t)(P.n_slots * group));
+  P.off_l = off; off = align_up(off + 4 * (size_t)(P.n_slots * group));
+  P.total = std::max<size_t>(off, 256);
+  return P;
 }
 
 }  // namespace
@@ -512,6 +609,60 @@ fa_status fa_debug_schedule(const fa_config* cfg, int32_t pass, int64_t* items, 
     }
   }
   return FA_OK;
+}
+
+fa_status fa_decode_workspace_size(const fa_decode_config* cfg, uint64_t* bytes) {
+  if (!bytes) return FA_ERR_PARAM_NULLPTR;
+  DecProblem pr;
+  fa_status st = parse_decode(cfg, &pr);
+  if (st != FA_OK) return st;
+  *bytes = plan_decode(pr).total;
+  return FA_OK;
+}
+
+fa_status fa_decode(const fa_decode_config* cfg, const void* q, const void* k, const void* v, void* out,
+                    void* workspace, uint64_t workspace_bytes, void* stream) {
+  DecProblem pr;
+  fa_status st = parse_decode(cfg, &pr);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !out || !workspace) return FA_ERR_PARAM_NULLPTR;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FA_ERR_PARAM_INVALID;
+  const DecPlan P = plan_decode(pr);
+  if (workspace_bytes < P.total) return FA_ERR_WORKSPACE;
+
+  std::vector<char> host(P.staged, 0);
+  std::memcpy(host.data() + P.off_items, P.items.data(), sizeof(fa::DecItem) * P.items.size());
+  std::memcpy(host.data() + P.off_first, P.first_slot.data(), 4 * P.first_slot.size());
+  std::memcpy(host.data() + P.off_nsplit, P.n_split.data(), 4 * P.n_split.size());
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* ws = reinterpret_cast<char*>(workspace);
+  if (hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, s) != hipSuccess) return FA_ERR_HIP;
+
+  fa::DecParams p{};
+  p.q = q; p.k = k; p.v = v; p.out = out;
+  p.mask = pr.mask;
+  p.mask_stride = pr.s;
+  p.items = reinterpret_cast<const fa::DecItem*>(ws + P.off_items);
+  p.first_slot = reinterpret_cast<const int32_t*>(ws + P.off_first);
+  p.n_split = reinterpret_cast<const int32_t*>(ws + P.off_nsplit);
+  p.part_o = reinterpret_cast<float*>(ws + P.off_o);
+  p.part_m = reinterpret_cast<float*>(ws + P.off_m);
+  p.part_l = reinterpret_cast<float*>(ws + P.off_l);
+  // KV cache strides (elements): BSH and BSND are [B, S, Nkv, D], BNSD is [B, Nkv, S, D]
+  p.kv_bstride = pr.s * pr.nkv * pr.d;
+  p.kv_tstride = pr.layout == FA_LAYOUT_BNSD ? pr.d : pr.nkv * pr.d;
+  p.kv_hstride = pr.layout == FA_LAYOUT_BNSD ? pr.s * pr.d : pr.d;
+  p.nq = (int32_t)pr.nq;
+  p.nkv = (int32_t)pr.nkv;
+  p.group = (int32_t)(pr.nq / pr.nkv);
+  p.keys_per_wave = (int32_t)(P.chunk / 4);
+  p.batch = (int32_t)pr.batch;
+  p.scale_log2 = (float)(pr.scale * 1.4426950408889634);
+  const int n_items = (int)P.items.size();
+  hipError_t e = timed(K_DEC, s, [&] { return fa::launch_decode(pr.dtype, (int)pr.d, n_items, p, s); });
+  if (e == hipSuccess && P.n_slots > 0)
+    e = timed(K_DEC_REDUCE, s, [&] { return fa::launch_decode_reduce(pr.dtype, (int)pr.d, p, s); });
+  return hip_status(e);
 }
 
 fa_status fa_profile_enable(int32_t on) {

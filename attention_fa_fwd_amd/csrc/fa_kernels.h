@@ -87,6 +87,32 @@ struct BwdParams {
   int32_t n_pre_blocks;
 };
 
+// Decode attention: one work item = a key range [lo, hi) of one (sequence b,
+// kv head g); slot >= 0 names its partial-result row when the sequence is split
+// over several items, slot < 0 means the item covers the sequence and writes
+// the output itself.
+struct DecItem {
+  int32_t b, g, lo, hi, slot;
+};
+
+struct DecParams {
+  const void* q;            // [B, Nq, D]
+  const void* k;            // KV cache, element (b, s, g, d) at b*kv_bstride + s*kv_tstride + g*kv_hstride + d
+  const void* v;
+  void* out;                // [B, Nq, D]
+  const uint8_t* mask;      // [B, mask_stride] (nonzero = masked), or null
+  int64_t mask_stride;
+  const DecItem* items;
+  const int32_t* first_slot;   // [B * Nkv]: slot of the first item of (b, g), -1 when not split
+  const int32_t* n_split;      // [B]: items per (b, g)
+  float* part_o;               // [slots, group, D] unnormalised partial outputs
+  float* part_m;               // [slots, group] log2-domain row maxima
+  float* part_l;               // [slots, group] row sums
+  int64_t kv_bstride, kv_tstride, kv_hstride;   // in elements
+  int32_t nq, nkv, group, keys_per_wave, batch;
+  float scale_log2;            // scale * log2(e)
+};
+
 // Tile shapes (rows x keys) of each pass; the host scheduler uses the same numbers.
 // Forward workgroup: 4 waves of 32 query rows each; bf16 runs two workgroups
 // per CU, fp32 one (its tiles fill the LDS).
@@ -130,6 +156,8 @@ hipError_t launch_bwd_dq(int dtype, int d, const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_dq_convert(int dtype, int d, const BwdParams& p, hipStream_t s);
 hipError_t launch_bwd_dsink(const BwdParams& p, hipStream_t s);
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t s);
+hipError_t launch_decode(int dtype, int d, int n_items, const DecParams& p, hipStream_t s);
+hipError_t launch_decode_reduce(int dtype, int d, const DecParams& p, hipStream_t s);
 hipError_t launch_mask_pack(const uint8_t* mask, int64_t rows, int64_t cols, uint32_t* bits, hipStream_t s);
 
 }  // namespace fa

@@ -100,6 +100,116 @@ def cpu_baseline(case, budget_s: float = 12.0):
     }
 
 
+def decode_cpu_baseline(case, budget_s: float = 10.0):
+    """The fp64 decode oracle on whole sequences of the decode workload (nearest the
+    median length first) until the time budget is spent; rate in K/V bytes read."""
+    import oracle
+    cores = len(os.sched_getaffinity(0))
+    order = np.argsort(np.abs(case.lens - np.median(case.lens)), kind="stable")
+    t_total, done, nbytes = 0.0, [], 0
+    row_bytes = 2 * case.num_kv_heads * case.head_dim * 2
+    for b in order:
+        k = case.padded_cache("k", "cpu", [int(b)]).float().numpy()
+        v = case.padded_cache("v", "cpu", [int(b)]).float().numpy()
+        q = case.q[[int(b)]].float().numpy()
+        t0 = time.perf_counter()
+        oracle.decode(q, k, v, case.num_heads, case.num_kv_heads, case.scale, case.layout, case.lens[[int(b)]])
+        t_total += time.perf_counter() - t0
+        done.append(int(case.lens[b]))
+        nbytes += int(case.lens[b]) * row_bytes
+        if t_total >= budget_s:
+            break
+    return {
+        "value": nbytes / t_total / 1e9,
+        "unit": "GB/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"fp64 numpy decode oracle on {len(done)} whole sequences of this workload (key lengths "
+                   f"{sorted(done)}), {nbytes} bytes of K/V rows in {t_total:.1f} s"),
+    }
+
+
+def decode_bench(args):
+    """Decode attention over the decode workload: one step = one fa_decode call over
+    every sequence (host split planning, the decode kernel, the split reduction)."""
+    import torch
+    import attention_fa_fwd_amd as fa
+    import workloads as wl
+
+    fa.lib()
+    dev = torch.device("cuda:0")
+    log("generating the decode workload")
+    case = wl.make_decode_workload(torch.float16 if args.dtype == "fp16" else None)
+    cfg = fa.DecodeConfig(case.batch, case.max_seq_len, case.num_heads, case.num_kv_heads, case.head_dim,
+                          case.dtype, case.scale, case.layout, case.lens)
+    q = case.q.to(dev)
+    k, v = case.padded_cache("k", dev), case.padded_cache("v", dev)
+    out = torch.empty_like(q)
+    ws = torch.empty(fa.fa_decode_workspace_size(cfg), dtype=torch.uint8, device=dev)
+
+    def step():
+        fa.fa_decode(cfg, q, k, v, out, workspace=ws)
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    steps = max(args.steps, 1) * 20          # a decode step is short: time 20 calls per requested step
+    log(f"timing {steps} calls")
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = e0.elapsed_time(e1) / steps
+    fa.fa_profile_read()
+    fa.fa_profile_enable(True)
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    kern = {n: (ms, c) for n, (ms, c) in fa.fa_profile_read().items() if c > 0}
+    fa.fa_profile_enable(False)
+    kv = case.kv_bytes
+    io = 2 * case.q.numel() * case.q.element_size()       # q in, out written
+    dec_ms = kern["fa_decode"][0] / kern["fa_decode"][1]
+    achieved = (kv + io) / (dec_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        ent = json.load(open(TRAFFIC_FILE)).get("decode" + ("_fp16" if args.dtype == "fp16" else ""), {})
+        ent = ent.get("fa_decode")
+        if ent and ent.get("source_hash") == kernel_source_hash():
+            traffic = ent.get("bytes_per_launch")
+    dt_name = "fp16" if args.dtype == "fp16" else "bf16"
+    res = {
+        "metric": f"decode attention K/V read bandwidth {dt_name} D=128 (valid cache rows / time)",
+        "value": round((kv + io) / (ms_step * 1e-3) / 1e9, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dt_name,
+        "data": "synthetic",
+        "config": {"workload": case.name, "sequences": case.batch, "cache_len": case.max_seq_len,
+                   "keys": int(case.lens.sum()), "heads_q": case.num_heads, "heads_kv": case.num_kv_heads,
+                   "head_dim": case.head_dim, "layout": case.layout, "kv_bytes": kv},
+        "kernels_ms": {n: round(ms / c, 5) for n, (ms, c) in kern.items()},
+        "roofline": {"bound": "hbm", "kernel": "fa_decode", "achieved": round(achieved, 1), "peak": HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_GBS, 4), "traffic": traffic},
+        "note": "the pages give API constraints but no throughput figures of their own",
+    }
+    if not args.no_cpu_baseline:
+        log("cpu baseline (fp64 decode oracle, bounded sample)")
+        res["cpu_baseline"] = decode_cpu_baseline(case)
+    print(json.dumps(res), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -110,17 +220,22 @@ def main():
     ap.add_argument("--dtype", choices=("bf16", "fp16"), default="bf16",
                     help="16-bit element type of workloads 2-5 (fp16 draws the same samples in fp16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode", action="store_true",
+                    help="time decode attention (fa_decode) over the decode workload instead")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (calibrates the HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: the path is a single-GPU kernel library and no multi-GPU "
-              f"run is part of this build (asked for --gpus {args.gpus}).", file=sys.stderr)
+        print(f"bench.py measures one GPU only: the path is a single-GPU kernel library whose multi-GPU "
+              f"sharding is a design, not code (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
     import torch
     import attention_fa_fwd_amd as fa
     import workloads as wl
+
+    if args.decode:
+        return decode_bench(args)
 
     fa.lib()   # fail loudly if libfa.so was not built
     dev = torch.device("cuda:0")

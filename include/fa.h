@@ -154,6 +154,56 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
                  void* dq, void* dk, void* dv, float* dsink,
                  void* workspace, uint64_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Decode attention: aclnnIncreFlashAttentionV2 (incremental inference).  Each
+ * of the B sequences brings one query token (the page fixes the query S axis at
+ * 1) and attends to the first L_b keys of a padded KV cache:
+ *   out[b, h] = Softmax(scale * q[b, h] K_b^T) V_b      (keys 0 .. L_b - 1)
+ * with query head h reading kv head h / (Nq / Nkv) (GQA).  The page's int8
+ * quantisation parameters and its reserved pseShift are not part of this call.
+ * ------------------------------------------------------------------------ */
+
+/* inputLayout of the decode page: query [B,1,H] / [B,1,N,D] / [B,N,1,D] and
+   key, value [B,S,H] / [B,S,N,D] / [B,N,S,D] (H = N*D).  The query and the
+   output are [B, Nq, D] in memory under every layout. */
+#define FA_LAYOUT_BSH 0
+#define FA_LAYOUT_BSND 1
+#define FA_LAYOUT_BNSD 2
+
+typedef struct fa_decode_config {
+  int64_t batch;                      /* B in [1, 65536]                                          */
+  int64_t max_seq_len;                /* S: padded key length of the cache, in [1, 2^24]           */
+  const int64_t* actual_seq_lengths;  /* HOST, B entries in [0, S] (actualSeqLengths), or NULL
+                                         for L_b = S.  A sequence with L_b = 0 (or every key
+                                         masked) gets out = 0.                                   */
+  int64_t num_heads;                  /* Nq in [1, 256] (numHeads)                                */
+  int64_t num_kv_heads;               /* Nkv (numKeyValueHeads); 0 means Nkv = Nq;
+                                         Nq % Nkv == 0 and Nq / Nkv <= 64                         */
+  int64_t head_dim;                   /* D in {64, 128}                                           */
+  int32_t dtype;                      /* FA_DTYPE_BF16 or FA_DTYPE_FP16 (q, k, v, out)            */
+  int32_t layout;                     /* FA_LAYOUT_*                                              */
+  double scale;                       /* scaleValue, multiplies q K^T                             */
+  const uint8_t* atten_mask;          /* DEVICE, optional BOOL / UINT8 [B, S] row-major; nonzero
+                                         masks key s out of sequence b.  NULL = no mask.          */
+  int32_t flags;                      /* reserved, must be 0                                      */
+} fa_decode_config;
+
+/* Device workspace bytes needed by fa_decode for this configuration (depends on
+   actual_seq_lengths: query again when they change).  >= 256. */
+fa_status fa_decode_workspace_size(const fa_decode_config* cfg, uint64_t* bytes);
+
+/*
+ * Decode.  Inputs (device, cfg->dtype): q [B, Nq, D]; k, v: the cache in
+ * cfg->layout with S = max_seq_len key rows per sequence (rows at or beyond L_b
+ * are never read).  Output (device): out [B, Nq, D] of cfg->dtype, fully
+ * overwritten.  q, k, v, out 16-byte aligned; the workspace is caller-owned and
+ * enqueued work uses it until it completes on `stream`.  Errors as fa_fwd:
+ * FA_ERR_PARAM_NULLPTR, FA_ERR_PARAM_INVALID (limits above, misalignment),
+ * FA_ERR_WORKSPACE, FA_ERR_HIP; nothing is enqueued on a validation error.
+ */
+fa_status fa_decode(const fa_decode_config* cfg, const void* q, const void* k, const void* v, void* out,
+                    void* workspace, uint64_t workspace_bytes, void* stream);
+
 /* Static text for a status code. */
 const char* fa_status_string(fa_status status);
 

@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for varlen FlashAttention forward/backward.
+"""fp64 CPU oracle for varlen FlashAttention forward/backward and decode attention.
 
 TEST INFRASTRUCTURE ONLY: imported by tests/, __graft_entry__.smoke() and the
 CPU-baseline leg of bench.py, never by the product library.  It shares no code
@@ -10,5 +10,7 @@ leave open (keep-mask bit order, band alignment when Lq != Lkv), which are
 """
 from .attention import (INT_MAX_TOKENS, allowed, alibi_pse, keep_bits, forward, backward,
                         probabilities)
+from .decode import cache_as_bsnd, decode
 
-__all__ = ["INT_MAX_TOKENS", "allowed", "alibi_pse", "keep_bits", "forward", "backward", "probabilities"]
+__all__ = ["INT_MAX_TOKENS", "allowed", "alibi_pse", "keep_bits", "forward", "backward", "probabilities",
+           "cache_as_bsnd", "decode"]

@@ -298,3 +298,66 @@ def test_build_rejects_spilling_kernels_with_lds_dma(tmp_path):
     bad.write_text(body + meta.format(a=3, b=0))
     with pytest.raises(RuntimeError, match="_Zk1"):
         check_no_spill_with_dma(str(bad))
+
+
+def _dcfg(**over):
+    base = dict(batch=3, max_seq_len=100, num_heads=8, num_kv_heads=2, head_dim=128, dtype=torch.bfloat16,
+                scale=0.1, layout="BSND", actual_seq_lengths=[100, 0, 37])
+    base.update(over)
+    return fa.DecodeConfig(**base)
+
+
+def _dec(cfg, **ptr):
+    p = dict(q=FAKE, k=FAKE, v=FAKE, out=FAKE, ws=FAKE, ws_bytes=1 << 40)
+    p.update(ptr)
+    return fa.lib().fa_decode(None if cfg is None else cfg.ref, p["q"], p["k"], p["v"], p["out"], p["ws"],
+                              ctypes.c_uint64(p["ws_bytes"]), None)
+
+
+DECODE_INVALID = {
+    "fp32": dict(dtype=torch.float32),
+    "head_dim_96": dict(head_dim=96),
+    "group_over_64": dict(num_heads=130, num_kv_heads=2),
+    "gqa_not_divisible": dict(num_heads=8, num_kv_heads=3),
+    "too_many_heads": dict(num_heads=512, num_kv_heads=512),
+    "bad_layout": dict(layout="SBH"),
+    "length_beyond_cache": dict(actual_seq_lengths=[101, 0, 1]),
+    "negative_length": dict(actual_seq_lengths=[-1, 0, 1]),
+    "zero_cache": dict(max_seq_len=0, actual_seq_lengths=None),
+    "batch_over_limit": dict(batch=65537, actual_seq_lengths=None),
+    "scale_nan": dict(scale=float("nan")),
+}
+
+
+@pytest.mark.parametrize("name", list(DECODE_INVALID))
+def test_decode_invalid_configs_rejected(name):
+    cfg = _dcfg(**DECODE_INVALID[name])
+    n = ctypes.c_uint64(0)
+    assert fa.lib().fa_decode_workspace_size(cfg.ref, ctypes.byref(n)) == fa.FA_ERR_PARAM_INVALID
+    assert _dec(cfg) == fa.FA_ERR_PARAM_INVALID
+
+
+def test_decode_validation_and_workspace():
+    n = ctypes.c_uint64(0)
+    assert fa.lib().fa_decode_workspace_size(None, ctypes.byref(n)) == fa.FA_ERR_PARAM_NULLPTR
+    assert fa.lib().fa_decode_workspace_size(_dcfg().ref, None) == fa.FA_ERR_PARAM_NULLPTR
+    for key in ("q", "k", "v", "out", "ws"):
+        assert _dec(_dcfg(), **{key: None}) == fa.FA_ERR_PARAM_NULLPTR, key
+    assert _dec(_dcfg(), q=ctypes.c_void_p(0x10008)) == fa.FA_ERR_PARAM_INVALID   # 8-byte aligned only
+    cfg = _dcfg()
+    cfg.c.flags = 1
+    assert _dec(cfg) == fa.FA_ERR_PARAM_INVALID
+    assert fa.lib().fa_decode_workspace_size(_dcfg().ref, ctypes.byref(n)) == fa.FA_OK
+    assert _dec(_dcfg(), ws_bytes=n.value - 1) == fa.FA_ERR_WORKSPACE
+    # the workspace grows with the split: one long sequence over many heads needs partials
+    small = ctypes.c_uint64(0)
+    big = ctypes.c_uint64(0)
+    assert fa.lib().fa_decode_workspace_size(_dcfg(actual_seq_lengths=[1, 1, 1]).ref, ctypes.byref(small)) == 0
+    cfg = _dcfg(batch=1, max_seq_len=1 << 20, actual_seq_lengths=[1 << 20])
+    assert fa.lib().fa_decode_workspace_size(cfg.ref, ctypes.byref(big)) == 0
+    assert big.value > small.value >= 256
+    # every layout and both 16-bit types are accepted; MQA with 64 query heads too
+    for layout in ("BSH", "BSND", "BNSD"):
+        for dt in (torch.bfloat16, torch.float16):
+            assert fa.lib().fa_decode_workspace_size(_dcfg(layout=layout, dtype=dt).ref, ctypes.byref(n)) == 0
+    assert fa.lib().fa_decode_workspace_size(_dcfg(num_heads=64, num_kv_heads=1).ref, ctypes.byref(n)) == 0

@@ -275,3 +275,91 @@ def allowed_pairs(lens_q, lens_kv, head_num, sparse_mode, pre_tokens=INT_MAX_TOK
         lo = np.maximum(lo, 0); hi = np.minimum(hi, lkv - 1)
         total += int(np.sum(np.maximum(hi - lo + 1, 0)))
     return total * int(head_num)
+
+
+# ---------------------------------------------------------------------------- decode attention
+
+@dataclass
+class DecodeCase:
+    """One decode problem: a query token per sequence and the valid rows of its KV
+    cache, stored compactly (sequence-major [sum L_b, Nkv, D]); padded_cache()
+    lays them out in the cache format of `layout`, zeros beyond each length."""
+    name: str
+    dtype: torch.dtype
+    lens: np.ndarray                  # int64 [B] actual key lengths
+    max_seq_len: int                  # S of the padded cache
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    scale: float
+    layout: str                       # "BSH", "BSND" or "BNSD"
+    q: torch.Tensor                   # [B, Nq, D] (cpu)
+    k_rows: torch.Tensor              # [sum L_b, Nkv, D] (cpu)
+    v_rows: torch.Tensor
+    atten_mask: Optional[np.ndarray] = None   # uint8 [B, S], nonzero = masked
+    meta: dict = field(default_factory=dict)
+
+    @property
+    def batch(self) -> int:
+        return len(self.lens)
+
+    def padded_cache(self, which: str, device="cpu", batches=None) -> torch.Tensor:
+        """K ('k') or V ('v') as the padded cache of `layout` for the listed sequences
+        (all by default), built on `device`."""
+        rows = self.k_rows if which == "k" else self.v_rows
+        bl = list(range(self.batch)) if batches is None else list(batches)
+        starts = np.concatenate([[0], np.cumsum(self.lens)])
+        cache = torch.zeros((len(bl), self.max_seq_len, self.num_kv_heads, self.head_dim), dtype=self.dtype,
+                            device=device)
+        for i, b in enumerate(bl):
+            L = int(self.lens[b])
+            if L:
+                cache[i, :L] = rows[int(starts[b]):int(starts[b]) + L].to(device)
+        if self.layout == "BSND":
+            return cache
+        if self.layout == "BSH":
+            return cache.reshape(len(bl), self.max_seq_len, self.num_kv_heads * self.head_dim)
+        return cache.permute(0, 2, 1, 3).contiguous()   # BNSD
+
+    @property
+    def kv_bytes(self) -> int:
+        """Bytes of K and V the pass must read: the valid rows only."""
+        return int(2 * self.lens.sum() * self.num_kv_heads * self.head_dim * torch.finfo(self.dtype).bits // 8)
+
+
+def make_decode_case(name, lens, max_seq_len=None, *, num_heads, num_kv_heads, head_dim, dtype=torch.bfloat16,
+                     layout="BSND", scale=None, seed=0, mask_p=0.0) -> DecodeCase:
+    """Decode case from explicit lengths: q, K rows, V rows drawn from default_rng([seed, t])
+    (t = 11, 12, 13), the optional [B, S] mask (each key masked with probability mask_p)
+    from default_rng([seed, 14])."""
+    lens = np.asarray(lens, dtype=np.int64)
+    s_max = int(max(1, lens.max())) if max_seq_len is None else int(max_seq_len)
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    total = int(lens.sum())
+    q = _normal([seed, 11], (len(lens), num_heads, head_dim), dtype)
+    k = _normal([seed, 12], (total, num_kv_heads, head_dim), dtype)
+    v = _normal([seed, 13], (total, num_kv_heads, head_dim), dtype)
+    mask = None
+    if mask_p > 0.0:
+        mask = (np.random.default_rng([seed, 14]).random((len(lens), s_max)) < mask_p).astype(np.uint8)
+    return DecodeCase(name=name, dtype=dtype, lens=lens, max_seq_len=s_max, num_heads=num_heads,
+                      num_kv_heads=num_kv_heads, head_dim=head_dim, scale=float(scale), layout=layout, q=q,
+                      k_rows=k, v_rows=v, atten_mask=mask)
+
+
+DECODE_WORKLOAD_NAME = ("decode bf16 B=128 S=16384 lognormal lengths (median 1024, sum 262144) "
+                        "Nq=64 Nkv=8 D=128 BSND")
+
+
+def make_decode_workload(dtype: Optional[torch.dtype] = None) -> DecodeCase:
+    """The decode workload: 128 sequences whose cache lengths follow the packed-varlen
+    length law (lognormal, median 1024, in [64, 16384], summing to 262144) over a
+    cache padded to 16384, GQA 64/8, D = 128, BSND."""
+    lens = lognormal_lengths(21, 262144, 128, 1024.0, 64, 16384)
+    dt = torch.bfloat16 if dtype is None else dtype
+    name = DECODE_WORKLOAD_NAME if dt == torch.bfloat16 else DECODE_WORKLOAD_NAME.replace("bf16", "fp16")
+    c = make_decode_case(name, lens, 16384, num_heads=64, num_kv_heads=8, head_dim=128, dtype=dt, layout="BSND",
+                         seed=21)
+    c.meta["workload"] = "decode"
+    return c
