@@ -320,7 +320,8 @@ constexpr int64_t kMaxDecBatch = 65536;            // B limit of the decode page
 constexpr int64_t kMaxDecSeq = 1 << 24;            // padded cache length limit (keys index in int32)
 constexpr int64_t kMaxDecGroup = 64;               // numHeads / numKeyValueHeads <= 64
 constexpr int64_t kDecTargetItems = 2048;          // split the keys until about this many work items remain
-constexpr int64_t kDecMinChunk = 128, kDecMaxChunk = 8192;   // keys per work item (4 waves x 32-key steps)
+constexpr int64_t kDecMinChunk = 32 * fa::kDecWaves;          // keys per work item: whole 32-key steps
+constexpr int64_t kDecMaxChunk = 8192;                         //   for every wave
 
 struct DecProblem {
   int64_t batch = 0, s = 0, nq = 0, nkv = 0, d = 0;
@@ -385,18 +386,22 @@ DecPlan plan_decode(const DecProblem& pr) {
     const int64_t L = pr.lens[(size_t)b];
     const int64_t n = std::max<int64_t>(1, (L + P.chunk - 1) / P.chunk);
     P.n_split[(size_t)b] = (int32_t)n;
-    for (int64_t g = 0; g < pr.nkv; ++g) {
-      if (n > 1) P.first_slot[(size_t)(b * pr.nkv + g)] = (int32_t)P.n_slots;
+    // the slots of one (b, g) are consecutive, and so are its items
+    const int64_t base = P.n_slots;
+    if (n > 1) {
+      for (int64_t g = 0; g < pr.nkv; ++g) P.first_slot[(size_t)(b * pr.nkv + g)] = (int32_t)(base + g * n);
+      P.n_slots += pr.nkv * n;
+    }
+    for (int64_t g = 0; g < pr.nkv; ++g)
       for (int64_t c = 0; c < n; ++c) {
         fa::DecItem it;
         it.b = (int32_t)b;
         it.g = (int32_t)g;
         it.lo = (int32_t)(c * P.chunk);
         it.hi = (int32_t)std::min(L, (c + 1) * P.chunk);
-        it.slot = n > 1 ? (int32_t)(P.n_slots++) : -1;
+        it.slot = n > 1 ? (int32_t)(base + g * n + c) : -1;
         P.items.push_back(it);
       }
-    }
   }
   const int64_t group = pr.nq / pr.nkv;
   size_t off = 0;
@@ -655,7 +660,7 @@ fa_status fa_decode(const fa_decode_config* cfg, const void* q, const void* k, c
   p.nq = (int32_t)pr.nq;
   p.nkv = (int32_t)pr.nkv;
   p.group = (int32_t)(pr.nq / pr.nkv);
-  p.keys_per_wave = (int32_t)(P.chunk / 4);
+  p.keys_per_wave = (int32_t)(P.chunk / fa::kDecWaves);
   p.batch = (int32_t)pr.batch;
   p.scale_log2 = (float)(pr.scale * 1.4426950408889634);
   const int n_items = (int)P.items.size();

@@ -4,15 +4,16 @@
 // query heads of one kv head share its K and V) and an optional per-sequence
 // key mask.
 //
-// The pass streams K and V from HBM once.  One workgroup (4 waves) takes a key
-// range of one (sequence, kv head); each wave walks its quarter of the range in
-// 32-key blocks with its own two-stage LDS ring (no barrier inside the loop):
+// The pass streams K and V from HBM once.  One workgroup (kDecWaves = 3 waves)
+// takes a key range of one (sequence, kv head); each wave walks its third of the
+// range in 32-key blocks through its own three-stage LDS ring, filled by LDS DMA
+// two blocks ahead (no barrier inside the loop):
 //   S^T (32 keys x 32 query heads) = K Q^T   A = K rows from LDS, B = Q in registers
 //   O^T (D x 32 query heads)      += V^T P^T  A = V via the transposing LDS read,
 //                                              B = P taken straight from S^T
 // The query heads of the group fill the MFMA's row side (zero rows pad a group
 // below 32; groups of 33-64 heads take two row blocks against the same K/V
-// operands).  The four waves' (max, sum, O) merge through LDS; a sequence split
+// operands).  The waves' (max, sum, O) merge through LDS; a sequence split
 // over several workgroups leaves fp32 partials that fa_decode_reduce_kernel
 // combines in a fixed order.
 #include "fa_device.h"
@@ -20,24 +21,33 @@
 
 namespace fa {
 
-constexpr int kDecWaves = 4;
-constexpr int kDecBlock = 32;   // keys per step
-
 template <typename E, int D>
 struct DecShape {
   static constexpr int RB = D * 2;                 // bytes per K/V row
   static constexpr int TILE = kDecBlock * RB;      // one K (or V) block, swizzled, unpadded
   static constexpr int STAGE = 2 * TILE;           // K | V
-  static constexpr int WAVE_LDS = 2 * STAGE;       // two stages per wave
+  static constexpr int WAVE_LDS = kDecStages * STAGE;   // the wave's ring
   static constexpr int NQ = D / 16;                // Q operand registers (16-wide d chunks)
   static constexpr int NDB = D / 32;               // 32-wide d blocks of O
+  static constexpr int DMA_PER_TILE = TILE / 1024;  // 1 KB LDS copies per K (or V) block
 };
+
+// s_waitcnt vmcnt(PER * n) for n in [0, 2]: wait until at most n blocks' copies
+// (PER memory instructions each, issued after the awaited block's) are in flight.
+template <int PER>
+__device__ __forceinline__ void dma_wait_blocks(int n) {
+  static_assert(2 * PER <= 63, "vmcnt range");
+  if (n <= 0) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  else if (n == 1) asm volatile("s_waitcnt vmcnt(%0)" ::"n"(PER) : "memory");
+  else asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * PER) : "memory");
+}
 
 template <typename E, int D, int NRB, bool MASK>
 __global__ __launch_bounds__(64 * kDecWaves, 1) void fa_decode_kernel(DecParams p) {
   using S = DecShape<E, D>;
   using V8 = typename Vec16<E>::v8;
   static_assert(NRB * 32 * D * 4 <= S::WAVE_LDS, "merge buffer fits the wave's ring");
+  static_assert(kDecStages >= 2 && kDecStages <= 4, "ring depth");
   __shared__ __attribute__((aligned(16))) char lds[kDecWaves * S::WAVE_LDS];
   __shared__ float mls[2][kDecWaves][32 * NRB];   // per wave and query head: max (log2 domain), sum
 
@@ -98,18 +108,23 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void fa_decode_kernel(DecParams 
   }
 
   auto copy_block = [&](int t) {
-    char* st = ring + (t & 1) * S::STAGE;
+    char* st = ring + (t % kDecStages) * S::STAGE;
     const int c0 = wlo + kDecBlock * t;
     dma_tile_swz<kDecBlock, S::RB, 1>(st, kbase, tstride, c0, whi, 0, lane);
     dma_tile_swz<kDecBlock, S::RB, 1>(st + S::TILE, vbase, tstride, c0, whi, 0, lane);
   };
 
   const uint8_t* mrow = MASK ? p.mask + (int64_t)b * p.mask_stride : nullptr;
-  if (nblk > 0) copy_block(0);
+  // blocks run kDecStages - 1 ahead of the one being computed
+#pragma unroll
+  for (int t = 0; t < kDecStages - 1; ++t)
+    if (t < nblk) copy_block(t);
   for (int t = 0; t < nblk; ++t) {
-    dma_wait();                       // block t has landed (only this wave reads its ring)
-    if (t + 1 < nblk) copy_block(t + 1);
-    const char* ks = ring + (t & 1) * S::STAGE;
+    // block t has landed once at most the copies of the blocks after it are in flight
+    // (only this wave reads its ring)
+    dma_wait_blocks<2 * S::DMA_PER_TILE>(min(kDecStages - 2, nblk - 1 - t));
+    if (t + kDecStages - 1 < nblk) copy_block(t + kDecStages - 1);
+    const char* ks = ring + (t % kDecStages) * S::STAGE;
     const char* vs = ks + S::TILE;
     const int c0 = wlo + kDecBlock * t;
 
@@ -185,7 +200,7 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void fa_decode_kernel(DecParams 
         for (int db = 0; db < S::NDB; ++db) o[rb][db] = mfma32(av[c2][db], pb[rb][c2], o[rb][db]);
   }
 
-  // ---- merge the four waves: each writes (max, sum, O) into its own ring ----
+  // ---- merge the waves: each writes (max, sum, O) into its own ring ----
   float* ow = reinterpret_cast<float*>(ring);   // [32*NRB heads][D]
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {

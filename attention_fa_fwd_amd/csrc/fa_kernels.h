@@ -95,6 +95,13 @@ struct DecItem {
   int32_t b, g, lo, hi, slot;
 };
 
+// Decode workgroup: kDecWaves waves, each streaming its own share of the item's
+// keys through a kDecStages-deep LDS ring of 32-key K/V blocks (two blocks in
+// flight per wave; at D = 128 the three rings take 144 KB of the CU's 160 KB).
+constexpr int kDecWaves = 3;
+constexpr int kDecStages = 3;
+constexpr int kDecBlock = 32;   // keys per step
+
 struct DecParams {
   const void* q;            // [B, Nq, D]
   const void* k;            // KV cache, element (b, s, g, d) at b*kv_bstride + s*kv_tstride + g*kv_hstride + d

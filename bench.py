@@ -139,7 +139,7 @@ def decode_bench(args):
     fa.lib()
     dev = torch.device("cuda:0")
     log("generating the decode workload")
-    case = wl.make_decode_workload(torch.float16 if args.dtype == "fp16" else None)
+    case = wl.make_decode_workload(torch.float16 if args.dtype == "fp16" else None, args.decode_layout)
     cfg = fa.DecodeConfig(case.batch, case.max_seq_len, case.num_heads, case.num_kv_heads, case.head_dim,
                           case.dtype, case.scale, case.layout, case.lens)
     q = case.q.to(dev)
@@ -222,6 +222,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--decode", action="store_true",
                     help="time decode attention (fa_decode) over the decode workload instead")
+    ap.add_argument("--decode-layout", choices=("BSND", "BSH", "BNSD"), default="BSND",
+                    help="KV cache layout of the decode workload")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (calibrates the HBM byte counters)")
     args = ap.parse_args()

@@ -352,14 +352,15 @@ DECODE_WORKLOAD_NAME = ("decode bf16 B=128 S=16384 lognormal lengths (median 102
                         "Nq=64 Nkv=8 D=128 BSND")
 
 
-def make_decode_workload(dtype: Optional[torch.dtype] = None) -> DecodeCase:
+def make_decode_workload(dtype: Optional[torch.dtype] = None, layout: str = "BSND") -> DecodeCase:
     """The decode workload: 128 sequences whose cache lengths follow the packed-varlen
     length law (lognormal, median 1024, in [64, 16384], summing to 262144) over a
-    cache padded to 16384, GQA 64/8, D = 128, BSND."""
+    cache padded to 16384, GQA 64/8, D = 128, BSND (or the given layout)."""
     lens = lognormal_lengths(21, 262144, 128, 1024.0, 64, 16384)
     dt = torch.bfloat16 if dtype is None else dtype
     name = DECODE_WORKLOAD_NAME if dt == torch.bfloat16 else DECODE_WORKLOAD_NAME.replace("bf16", "fp16")
-    c = make_decode_case(name, lens, 16384, num_heads=64, num_kv_heads=8, head_dim=128, dtype=dt, layout="BSND",
+    name = name.replace("BSND", layout)
+    c = make_decode_case(name, lens, 16384, num_heads=64, num_kv_heads=8, head_dim=128, dtype=dt, layout=layout,
                          seed=21)
     c.meta["workload"] = "decode"
     return c
