@@ -30,9 +30,11 @@ FA_DTYPE_FP16 = 2
 FA_FLAG_PSE_SQRT = 1
 FA_FLAG_SLOPES_PER_BATCH = 2
 TOKENS_DEFAULT = 2147483647
-FA_LAYOUT_BSH = 0
-FA_LAYOUT_BSND = 1
-FA_LAYOUT_BNSD = 2
+FA_LAYOUT_TND = 0
+FA_LAYOUT_BSH = 1
+FA_LAYOUT_BSND = 2
+FA_LAYOUT_BNSD = 3
+FA_LAYOUT_SBH = 4
 
 EXPORTED = ("fa_fwd_workspace_size", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd", "fa_status_string",
             "fa_debug_schedule", "fa_profile_enable", "fa_profile_read", "fa_profile_kernel_count",
@@ -59,6 +61,7 @@ class FaConfig(ctypes.Structure):
         ("atten_mask", ctypes.c_void_p),
         ("mask_rows", ctypes.c_int64),
         ("mask_cols", ctypes.c_int64),
+        ("layout", ctypes.c_int32),
     ]
 
 
@@ -128,7 +131,7 @@ class Config:
 
     def __init__(self, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, head_dim, dtype, scale, keep_prob=1.0,
                  sparse_mode=0, pre_tokens=TOKENS_DEFAULT, next_tokens=TOKENS_DEFAULT, deterministic=True,
-                 prefix=None, atten_mask=None, pse_type=2, slopes_per_batch=False):
+                 prefix=None, atten_mask=None, pse_type=2, slopes_per_batch=False, layout="TND"):
         self.cu_q = np.ascontiguousarray(np.asarray(cu_seqlens_q, dtype=np.int64))
         self.cu_kv = np.ascontiguousarray(np.asarray(cu_seqlens_kv, dtype=np.int64))
         # per-sequence prefix N of sparse mode 6 (prefixOptional); NULL when None
@@ -142,6 +145,9 @@ class Config:
         if pse_type not in (2, 3):
             raise ValueError("pse_type must be 2 or 3 (generated from alibi slopes)")
         self.slopes_per_batch = bool(slopes_per_batch)
+        # inputLayout of Q, K, V, dY, O and the gradients; the fixed-length layouts take
+        # cu_seqlens with one common length per side
+        self.layout_name = layout
         flags = (FA_FLAG_PSE_SQRT if pse_type == 3 else 0) | (FA_FLAG_SLOPES_PER_BATCH if slopes_per_batch else 0)
         if isinstance(dtype, torch.dtype):
             dtype = {torch.float32: FA_DTYPE_FP32, torch.bfloat16: FA_DTYPE_BF16,
@@ -157,7 +163,8 @@ class Config:
             prefix=(None if self.prefix is None else self.prefix.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))),
             atten_mask=(None if atten_mask is None else atten_mask.data_ptr()),
             mask_rows=(0 if atten_mask is None else int(atten_mask.shape[0])),
-            mask_cols=(0 if atten_mask is None else int(atten_mask.shape[1])))
+            mask_cols=(0 if atten_mask is None else int(atten_mask.shape[1])),
+            layout=_LAYOUTS.get(layout, -1))
 
     @property
     def ref(self):
@@ -208,13 +215,25 @@ def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
+def layout_shape(cfg: Config, q_side: bool):
+    """Shape of a query-side (q, dy, out, dq) or key-side (k, v, dk, dv) tensor in cfg's layout."""
+    n = cfg.c.head_num if q_side else (cfg.c.num_kv_heads or cfg.c.head_num)
+    cu = cfg.cu_q if q_side else cfg.cu_kv
+    d, t, b = cfg.c.head_dim, int(cu[-1]), len(cu) - 1
+    s = int(cu[1]) if b > 0 else 0
+    return {"TND": (t, n, d), "BSND": (b, s, n, d), "BSH": (b, s, n * d), "BNSD": (b, n, s, d),
+            "SBH": (s, b, n * d)}[cfg.layout_name]
+
+
 def _common_checks(q, k, v, cfg: Config):
     dev = q.device
     tq, tkv = int(cfg.cu_q[-1]), int(cfg.cu_kv[-1])
     nq, nkv, d = cfg.c.head_num, cfg.c.num_kv_heads or cfg.c.head_num, cfg.c.head_dim
-    _check_tensor("q", q, (tq, nq, d), q.dtype, dev)
-    _check_tensor("k", k, (tkv, nkv, d), q.dtype, dev)
-    _check_tensor("v", v, (tkv, nkv, d), q.dtype, dev)
+    if cfg.layout_name not in _LAYOUTS:
+        raise ValueError(f"unknown layout {cfg.layout_name}")
+    _check_tensor("q", q, layout_shape(cfg, True), q.dtype, dev)
+    _check_tensor("k", k, layout_shape(cfg, False), q.dtype, dev)
+    _check_tensor("v", v, layout_shape(cfg, False), q.dtype, dev)
     return dev, tq, tkv, nq, nkv, d
 
 
@@ -236,7 +255,7 @@ def fa_fwd(cfg: Config, q, k, v, drop_mask=None, alibi_slopes=None, sink=None, o
         softmax_max = torch.empty((tq, nq), dtype=torch.float32, device=dev)
     if softmax_sum is None:
         softmax_sum = torch.empty((tq, nq), dtype=torch.float32, device=dev)
-    _check_tensor("out", out, (tq, nq, d), q.dtype, dev)
+    _check_tensor("out", out, layout_shape(cfg, True), q.dtype, dev)
     _check_tensor("softmax_max", softmax_max, (tq, nq), torch.float32, dev)
     _check_tensor("softmax_sum", softmax_sum, (tq, nq), torch.float32, dev)
     _check_slopes_sink(cfg, alibi_slopes, sink, nq, dev)
@@ -254,8 +273,8 @@ def fa_bwd(cfg: Config, q, k, v, dy, out, softmax_max, softmax_sum, drop_mask=No
            dq=None, dk=None, dv=None, dsink=None, workspace=None):
     """Backward through libfa.so on the current stream; returns (dq, dk, dv, dsink or None)."""
     dev, tq, tkv, nq, nkv, d = _common_checks(q, k, v, cfg)
-    _check_tensor("dy", dy, (tq, nq, d), q.dtype, dev)
-    _check_tensor("out", out, (tq, nq, d), q.dtype, dev)
+    _check_tensor("dy", dy, layout_shape(cfg, True), q.dtype, dev)
+    _check_tensor("out", out, layout_shape(cfg, True), q.dtype, dev)
     _check_tensor("softmax_max", softmax_max, (tq, nq), torch.float32, dev)
     _check_tensor("softmax_sum", softmax_sum, (tq, nq), torch.float32, dev)
     _check_slopes_sink(cfg, alibi_slopes, sink, nq, dev)
@@ -267,9 +286,9 @@ def fa_bwd(cfg: Config, q, k, v, dy, out, softmax_max, softmax_sum, drop_mask=No
         dv = torch.empty_like(v)
     if sink is not None and dsink is None:
         dsink = torch.empty((nq,), dtype=torch.float32, device=dev)
-    _check_tensor("dq", dq, (tq, nq, d), q.dtype, dev)
-    _check_tensor("dk", dk, (tkv, nkv, d), q.dtype, dev)
-    _check_tensor("dv", dv, (tkv, nkv, d), q.dtype, dev)
+    _check_tensor("dq", dq, layout_shape(cfg, True), q.dtype, dev)
+    _check_tensor("dk", dk, layout_shape(cfg, False), q.dtype, dev)
+    _check_tensor("dv", dv, layout_shape(cfg, False), q.dtype, dev)
     ws = _workspace(fa_bwd_workspace_size(cfg), dev, workspace)
     st = lib().fa_bwd(cfg.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(dy), _ptr(out), _ptr(softmax_max),
                       _ptr(softmax_sum), _ptr(drop_mask), _ptr(alibi_slopes), _ptr(sink), _ptr(dq), _ptr(dk),
@@ -306,7 +325,8 @@ def fa_profile_read() -> dict:
     return res
 
 
-_LAYOUTS = {"BSH": FA_LAYOUT_BSH, "BSND": FA_LAYOUT_BSND, "BNSD": FA_LAYOUT_BNSD}
+_LAYOUTS = {"TND": FA_LAYOUT_TND, "BSH": FA_LAYOUT_BSH, "BSND": FA_LAYOUT_BSND, "BNSD": FA_LAYOUT_BNSD,
+            "SBH": FA_LAYOUT_SBH}
 
 
 class DecodeConfig:

@@ -14,7 +14,8 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libfa.so")
-SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_kv.hip", "fa_bwd_kv_atomic.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_kv.hip", "fa_bwd_kv_atomic.hip", "fa_decode.hip",
+           "fa_layout.hip"]
 # sources whose MFMA results are kept in VGPRs (see common_flags)
 VGPR_FORM_SOURCES = {s for s in os.environ.get("FA_VGPR_FORM", "fa_fwd.hip,fa_bwd.hip,fa_bwd_kv_atomic.hip,fa_decode.hip").split(",") if s}
 ARCH = "gfx950"

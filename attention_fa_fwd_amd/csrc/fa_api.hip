@@ -27,6 +27,8 @@ struct Problem {
   double scale = 0, keep = 1;
   int64_t pre = 0, next = 0;
   bool deterministic = true;
+  int layout = FA_LAYOUT_TND;      // fa_config.layout
+  int64_t sq = 0, skv = 0;         // common sequence lengths of the fixed-length layouts
   bool pse_sqrt = false;           // FA_FLAG_PSE_SQRT: the slopes generate pseType 3
   bool slopes_per_batch = false;   // FA_FLAG_SLOPES_PER_BATCH: slopes are [B, Nq]
   std::vector<int32_t> cu_q, cu_kv;
@@ -36,6 +38,10 @@ struct Problem {
   int64_t mask_rows = 0, mask_cols = 0, mask_words = 0;   // words: 32-key words per packed row
   int64_t drop_bits = 0;
 };
+
+static_assert(fa::kLayoutBNSD == FA_LAYOUT_BNSD && fa::kLayoutSBH == FA_LAYOUT_SBH, "layout codes");
+bool relayout(const Problem& pr) { return pr.layout == FA_LAYOUT_BNSD || pr.layout == FA_LAYOUT_SBH; }
+int64_t elem_bytes(const Problem& pr) { return pr.dtype == FA_DTYPE_FP32 ? 4 : 2; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
@@ -107,6 +113,15 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   }
   pr->tq = cq[pr->batch];
   pr->tkv = ck[pr->batch];
+  if (cfg->layout < FA_LAYOUT_TND || cfg->layout > FA_LAYOUT_SBH) return FA_ERR_PARAM_INVALID;
+  pr->layout = cfg->layout;
+  if (pr->layout != FA_LAYOUT_TND) {
+    // the fixed-length layouts hold B sequences of one length per side
+    pr->sq = cq[1];
+    pr->skv = ck[1];
+    for (int64_t b = 0; b <= pr->batch; ++b)
+      if (cq[b] != b * pr->sq || ck[b] != b * pr->skv) return FA_ERR_PARAM_INVALID;
+  }
   if (pr->tq < 1 || pr->tkv < 1) return FA_ERR_PARAM_INVALID;
   const bool uses_mask = mode == FA_SPARSE_NONE || mode == FA_SPARSE_ALL_MASK || mode == FA_SPARSE_BAND;
   if (cfg->atten_mask && uses_mask) {
@@ -190,6 +205,8 @@ struct Layout {
   uint64_t cu_q = 0, cu_kv = 0, bit_base = 0, prefix = 0, items0 = 0, items1 = 0;   // host-staged block
   uint64_t staged_bytes = 0;
   uint64_t delta = 0, lse = 0, dsink_part = 0, dq_acc = 0, mbits = 0;
+  // TND copies of the BNSD / SBH tensors
+  uint64_t rq = 0, rk = 0, rv = 0, rdy = 0, ro = 0, rdq = 0, rdk = 0, rdv = 0;
   uint64_t total = 0;
   int64_t n_items0 = 0, n_items1 = 0;
   int n_pre_blocks = 0;
@@ -208,6 +225,14 @@ Layout layout_fwd(const Problem& pr, int64_t n_items) {
   if (pr.mask) {
     L.mbits = off;
     off = align_up(off + 4 * (uint64_t)pr.mask_rows * pr.mask_words);
+  }
+  if (relayout(pr)) {
+    const uint64_t qb = (uint64_t)(pr.tq * pr.nq * pr.d * elem_bytes(pr));
+    const uint64_t kb = (uint64_t)(pr.tkv * pr.nkv * pr.d * elem_bytes(pr));
+    L.rq = off; off = align_up(off + qb);
+    L.rk = off; off = align_up(off + kb);
+    L.rv = off; off = align_up(off + kb);
+    L.ro = off; off = align_up(off + qb);
   }
   L.total = std::max<uint64_t>(off, kAlign);
   return L;
@@ -240,6 +265,18 @@ Layout layout_bwd(const Problem& pr, int64_t n_kv_items, int64_t n_dq_items) {
     L.mbits = off;
     off = align_up(off + 4 * (uint64_t)pr.mask_rows * pr.mask_words);
   }
+  if (relayout(pr)) {
+    const uint64_t qb = (uint64_t)(pr.tq * pr.nq * pr.d * elem_bytes(pr));
+    const uint64_t kb = (uint64_t)(pr.tkv * pr.nkv * pr.d * elem_bytes(pr));
+    L.rq = off; off = align_up(off + qb);
+    L.rk = off; off = align_up(off + kb);
+    L.rv = off; off = align_up(off + kb);
+    L.rdy = off; off = align_up(off + qb);
+    L.ro = off; off = align_up(off + qb);
+    L.rdq = off; off = align_up(off + qb);
+    L.rdk = off; off = align_up(off + kb);
+    L.rdv = off; off = align_up(off + kb);
+  }
   L.total = off;
   return L;
 }
@@ -252,10 +289,11 @@ Layout bwd_layout_bound(const Problem& pr) {
 }
 
 // ---- kernel timing (measurement hook) ----
-enum KernelId { K_FWD = 0, K_PRE, K_KV, K_DQ, K_CONVERT, K_DSINK, K_ZERO, K_MASK, K_DEC, K_DEC_REDUCE, K_COUNT };
+enum KernelId { K_FWD = 0, K_PRE, K_KV, K_DQ, K_CONVERT, K_DSINK, K_ZERO, K_MASK, K_DEC, K_DEC_REDUCE, K_RELAYOUT,
+                K_COUNT };
 const char* kKernelNames[K_COUNT] = {"fa_fwd",         "fa_bwd_preprocess", "fa_bwd_dkdv",  "fa_bwd_dq",
                                      "fa_bwd_dq_convert", "fa_bwd_dsink_reduce", "fa_zero_f32", "fa_mask_pack",
-                                     "fa_decode",      "fa_decode_reduce"};
+                                     "fa_decode",      "fa_decode_reduce",    "fa_relayout"};
 struct ProfState {
   std::mutex mu;
   bool on = false;
@@ -289,6 +327,16 @@ hipError_t timed(KernelId id, hipStream_t s, F&& launch) {
 }
 
 fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
+
+// One BNSD / SBH tensor of the query side (q = true: B sequences of Sq rows, Nq
+// heads) or the key side to or from its TND copy.
+hipError_t relayout_tensor(const Problem& pr, bool q_side, const void* src, void* dst, bool to_tnd,
+                           hipStream_t s) {
+  return timed(K_RELAYOUT, s, [&] {
+    return fa::launch_relayout(src, dst, pr.batch, q_side ? pr.sq : pr.skv, q_side ? pr.nq : pr.nkv, pr.d,
+                               (int)elem_bytes(pr), pr.layout, to_tnd, s);
+  });
+}
 
 void fill_common_fwd(const Problem& pr, fa::FwdParams& p) {
   p.nq = (int32_t)pr.nq;
@@ -477,6 +525,13 @@ fa_status fa_fwd(const fa_config* cfg, const void* q, const void* k, const void*
   fa::FwdParams p{};
   fill_common_fwd(pr, p);
   p.q = q; p.k = k; p.v = v; p.o = out;
+  if (relayout(pr)) {
+    if ((e = relayout_tensor(pr, true, q, ws + L.rq, true, s)) != hipSuccess ||
+        (e = relayout_tensor(pr, false, k, ws + L.rk, true, s)) != hipSuccess ||
+        (e = relayout_tensor(pr, false, v, ws + L.rv, true, s)) != hipSuccess)
+      return FA_ERR_HIP;
+    p.q = ws + L.rq; p.k = ws + L.rk; p.v = ws + L.rv; p.o = ws + L.ro;
+  }
   p.m_out = softmax_max; p.l_out = softmax_sum;
   p.drop = pr.keep < 1.0 ? drop_mask : nullptr;
   p.drop_bytes = (pr.drop_bits + 7) / 8;
@@ -497,7 +552,9 @@ fa_status fa_fwd(const fa_config* cfg, const void* q, const void* k, const void*
     });
     if (e != hipSuccess) return FA_ERR_HIP;
   }
-  return hip_status(timed(K_FWD, s, [&] { return fa::launch_fwd(pr.dtype, (int)pr.d, p, s); }));
+  e = timed(K_FWD, s, [&] { return fa::launch_fwd(pr.dtype, (int)pr.d, p, s); });
+  if (e == hipSuccess && relayout(pr)) e = relayout_tensor(pr, true, ws + L.ro, out, false, s);
+  return hip_status(e);
 }
 
 fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void* v, const void* dy, const void* out,
@@ -539,6 +596,16 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
   p.q = q; p.k = k; p.v = v; p.dy = dy; p.o = out;
   p.m_in = softmax_max; p.l_in = softmax_sum;
   p.dq = dq; p.dk = dk; p.dv = dv; p.dsink = sink ? dsink : nullptr;
+  if (relayout(pr)) {
+    if ((e = relayout_tensor(pr, true, q, ws + L.rq, true, s)) != hipSuccess ||
+        (e = relayout_tensor(pr, false, k, ws + L.rk, true, s)) != hipSuccess ||
+        (e = relayout_tensor(pr, false, v, ws + L.rv, true, s)) != hipSuccess ||
+        (e = relayout_tensor(pr, true, dy, ws + L.rdy, true, s)) != hipSuccess ||
+        (e = relayout_tensor(pr, true, out, ws + L.ro, true, s)) != hipSuccess)
+      return FA_ERR_HIP;
+    p.q = ws + L.rq; p.k = ws + L.rk; p.v = ws + L.rv; p.dy = ws + L.rdy; p.o = ws + L.ro;
+    p.dq = ws + L.rdq; p.dk = ws + L.rdk; p.dv = ws + L.rdv;
+  }
   p.delta = reinterpret_cast<float*>(ws + L.delta);
   p.lse = reinterpret_cast<float*>(ws + L.lse);
   p.dsink_part = reinterpret_cast<float*>(ws + L.dsink_part);
@@ -589,6 +656,11 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
       e = timed(K_CONVERT, s, [&] { return fa::launch_bwd_dq_convert(dt, d, p, s); });
   }
   if (e == hipSuccess && sink) e = timed(K_DSINK, s, [&] { return fa::launch_bwd_dsink(p, s); });
+  if (e == hipSuccess && relayout(pr)) {
+    e = relayout_tensor(pr, true, ws + L.rdq, dq, false, s);
+    if (e == hipSuccess) e = relayout_tensor(pr, false, ws + L.rdk, dk, false, s);
+    if (e == hipSuccess) e = relayout_tensor(pr, false, ws + L.rdv, dv, false, s);
+  }
   return hip_status(e);
 }
 

@@ -220,6 +220,8 @@ def main():
     ap.add_argument("--dtype", choices=("bf16", "fp16"), default="bf16",
                     help="16-bit element type of workloads 2-5 (fp16 draws the same samples in fp16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--layout", choices=("TND", "BSND", "BSH", "BNSD", "SBH"), default="TND",
+                    help="input layout of the training path (fixed-length workloads 3 and 4 for the non-TND ones)")
     ap.add_argument("--decode", action="store_true",
                     help="time decode attention (fa_decode) over the decode workload instead")
     ap.add_argument("--decode-layout", choices=("BSND", "BSH", "BNSD"), default="BSND",
@@ -255,13 +257,24 @@ def main():
     deterministic = not args.atomic_dq
     cfg = fa.Config(case.cu_seqlens_q, case.cu_seqlens_kv, case.head_num, case.kv_heads, case.head_dim,
                     case.dtype, case.scale, case.keep_prob, case.sparse_mode, case.pre_tokens, case.next_tokens,
-                    deterministic)
+                    deterministic, layout=args.layout)
     q, k, v, dy = (t.to(dev) for t in (case.q, case.k, case.v, case.dy))
+    if args.layout != "TND":
+        # the same values in the fixed-length layout (workloads with one common length)
+        def lay(x):
+            b = case.batch
+            x4 = x.reshape(b, x.shape[0] // b, x.shape[1], x.shape[2])
+            if args.layout == "BNSD":
+                return x4.permute(0, 2, 1, 3).contiguous()
+            if args.layout == "SBH":
+                return x4.permute(1, 0, 2, 3).reshape(x4.shape[1], b, -1).contiguous()
+            return x4 if args.layout == "BSND" else x4.reshape(b, x4.shape[1], -1)
+        q, k, v, dy = (lay(t) for t in (q, k, v, dy))
     drop = torch.from_numpy(case.drop_mask).to(dev) if case.drop_mask is not None else None
     slopes = torch.from_numpy(case.alibi_slopes).to(dev) if case.alibi_slopes is not None else None
     sink = torch.from_numpy(case.sink).to(dev) if case.sink is not None else None
     out = torch.empty_like(q)
-    tq = q.shape[0]
+    tq = int(case.cu_seqlens_q[-1])
     m = torch.empty((tq, case.head_num), dtype=torch.float32, device=dev)
     l = torch.empty_like(m)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
@@ -339,7 +352,7 @@ def main():
         "config": {"workload": wl.workload_name(args.workload, case.dtype), "total_tokens": int(tq),
                    "sequences": int(case.batch), "heads_q": case.head_num, "heads_kv": case.kv_heads,
                    "head_dim": d, "allowed_pairs": int(pairs),
-                   "dq_variant": "deterministic" if deterministic else "atomic"},
+                   "dq_variant": "deterministic" if deterministic else "atomic", "layout": args.layout},
         "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
         "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
         "kernels_ms": {n: round(ms / c, 4) for n, (ms, c) in kern.items()},

@@ -59,6 +59,15 @@ typedef int32_t fa_status;
 #define FA_DTYPE_BF16 1
 #define FA_DTYPE_FP16 2
 
+/* inputLayout (aclnnFlashAttentionScoreV2, "inputLayout"): TND packs sequences of
+   any lengths; the others hold B sequences of one common length S per side
+   (H = N*D).  fa_config.layout selects it for Q, K, V, dY, O, dQ, dK, dV. */
+#define FA_LAYOUT_TND 0   /* [T, N, D]                                         */
+#define FA_LAYOUT_BSH 1   /* [B, S, H]      (same bytes as TND with L_b = S)   */
+#define FA_LAYOUT_BSND 2  /* [B, S, N, D]   (same bytes as TND with L_b = S)   */
+#define FA_LAYOUT_BNSD 3  /* [B, N, S, D]                                      */
+#define FA_LAYOUT_SBH 4   /* [S, B, H]                                         */
+
 /* sparse modes (aclnnFlashAttentionUnpaddingScoreGrad, "sparseMode" parameter) */
 #define FA_SPARSE_NONE 0             /* every pair allowed (or those the attenMask keeps)    */
 #define FA_SPARSE_ALL_MASK 1         /* the pairs the attenMask keeps (mask required)        */
@@ -115,6 +124,13 @@ typedef struct fa_config {
                                     ignore it.  NULL = no mask.                               */
   int64_t mask_rows;             /* S1Max >= every Lq_b (with atten_mask)                     */
   int64_t mask_cols;             /* S2Max >= every Lkv_b (with atten_mask)                    */
+  int32_t layout;                /* FA_LAYOUT_* of Q, K, V, dY, O and the gradients; 0 = TND.
+                                    Other layouts need cu_seqlens with one common length
+                                    per side (cu[b] = b*S), else FA_ERR_PARAM_INVALID.  BNSD
+                                    and SBH are gathered into TND copies in the workspace
+                                    (the size query accounts for them) and the outputs
+                                    scattered back.  softmax_max / softmax_sum stay
+                                    [T, Nq] with T = B*Sq, row t = b*Sq + s.                 */
 } fa_config;
 
 /* Device workspace bytes needed by fa_fwd for this configuration (>= 256). */
@@ -165,11 +181,8 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
 
 /* inputLayout of the decode page: query [B,1,H] / [B,1,N,D] / [B,N,1,D] and
    key, value [B,S,H] / [B,S,N,D] / [B,N,S,D] (H = N*D).  The query and the
-   output are [B, Nq, D] in memory under every layout. */
-#define FA_LAYOUT_BSH 0
-#define FA_LAYOUT_BSND 1
-#define FA_LAYOUT_BNSD 2
-
+   output are [B, Nq, D] in memory under every layout.  (The FA_LAYOUT_* values
+   are shared with fa_config.layout.) */
 typedef struct fa_decode_config {
   int64_t batch;                      /* B in [1, 65536]                                          */
   int64_t max_seq_len;                /* S: padded key length of the cache, in [1, 2^24]           */

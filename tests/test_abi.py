@@ -361,3 +361,24 @@ def test_decode_validation_and_workspace():
         for dt in (torch.bfloat16, torch.float16):
             assert fa.lib().fa_decode_workspace_size(_dcfg(layout=layout, dtype=dt).ref, ctypes.byref(n)) == 0
     assert fa.lib().fa_decode_workspace_size(_dcfg(num_heads=64, num_kv_heads=1).ref, ctypes.byref(n)) == 0
+
+
+def test_layout_validation():
+    n = ctypes.c_uint64(0)
+    uniform = dict(cu_seqlens_q=[0, 6, 12], cu_seqlens_kv=[0, 9, 18])
+    sizes = {}
+    for layout in ("TND", "BSND", "BSH", "BNSD", "SBH"):
+        cfg = _cfg(layout=layout, **uniform)
+        assert fa.lib().fa_bwd_workspace_size(cfg.ref, ctypes.byref(n)) == fa.FA_OK, layout
+        sizes[layout] = n.value
+    # BSH / BSND are TND in memory; BNSD / SBH add TND copies of the eight tensors
+    assert sizes["BSND"] == sizes["BSH"] == sizes["TND"]
+    assert sizes["BNSD"] == sizes["SBH"] > sizes["TND"]
+    # the fixed-length layouts need one common length per side
+    for layout in ("BSND", "BNSD", "SBH"):
+        assert _fwd(_cfg(layout=layout)) == fa.FA_ERR_PARAM_INVALID   # lengths 5 and 7
+    cfg = _cfg(**uniform)
+    cfg.c.layout = 5
+    assert _fwd(cfg) == fa.FA_ERR_PARAM_INVALID
+    assert fa.layout_shape(_cfg(layout="SBH", **uniform), True) == (6, 2, 4 * 128)
+    assert fa.layout_shape(_cfg(layout="BNSD", **uniform), False) == (2, 2, 9, 128)
