@@ -62,6 +62,11 @@ class FaConfig(ctypes.Structure):
         ("mask_rows", ctypes.c_int64),
         ("mask_cols", ctypes.c_int64),
         ("layout", ctypes.c_int32),
+        ("pse", ctypes.c_void_p),
+        ("pse_batch", ctypes.c_int64),
+        ("pse_rows", ctypes.c_int64),
+        ("pse_cols", ctypes.c_int64),
+        ("pse_type", ctypes.c_int32),
     ]
 
 
@@ -131,7 +136,7 @@ class Config:
 
     def __init__(self, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, head_dim, dtype, scale, keep_prob=1.0,
                  sparse_mode=0, pre_tokens=TOKENS_DEFAULT, next_tokens=TOKENS_DEFAULT, deterministic=True,
-                 prefix=None, atten_mask=None, pse_type=2, slopes_per_batch=False, layout="TND"):
+                 prefix=None, atten_mask=None, pse_type=2, slopes_per_batch=False, layout="TND", pse=None):
         self.cu_q = np.ascontiguousarray(np.asarray(cu_seqlens_q, dtype=np.int64))
         self.cu_kv = np.ascontiguousarray(np.asarray(cu_seqlens_kv, dtype=np.int64))
         # per-sequence prefix N of sparse mode 6 (prefixOptional); NULL when None
@@ -142,13 +147,20 @@ class Config:
             if atten_mask.dim() != 2 or atten_mask.dtype not in (torch.uint8, torch.bool) or not atten_mask.is_contiguous():
                 raise ValueError("atten_mask must be a contiguous 2-D bool or uint8 tensor [S1Max, S2Max]")
         # pseType of the slopes passed to fa_fwd / fa_bwd: 2 (linear distance) or 3 (square root)
-        if pse_type not in (2, 3):
-            raise ValueError("pse_type must be 2 or 3 (generated from alibi slopes)")
+        # pse: optional device tensor [1 or B, Nq, rows, cols] of the input type (pseType 0 / 1);
+        # without it pse_type names how alibi slopes generate the bias (2 / 3)
+        self.pse = pse
+        if pse is not None:
+            if pse.dim() != 4 or not pse.is_contiguous() or pse_type not in (0, 1):
+                raise ValueError("pse must be a contiguous [1 or B, Nq, rows, cols] tensor with pse_type 0 or 1")
+        elif pse_type not in (2, 3):
+            raise ValueError("pse_type must be 2 or 3 (generated from alibi slopes) without a pse tensor")
         self.slopes_per_batch = bool(slopes_per_batch)
         # inputLayout of Q, K, V, dY, O and the gradients; the fixed-length layouts take
         # cu_seqlens with one common length per side
         self.layout_name = layout
-        flags = (FA_FLAG_PSE_SQRT if pse_type == 3 else 0) | (FA_FLAG_SLOPES_PER_BATCH if slopes_per_batch else 0)
+        flags = ((FA_FLAG_PSE_SQRT if pse_type == 3 and pse is None else 0)
+                 | (FA_FLAG_SLOPES_PER_BATCH if slopes_per_batch else 0))
         if isinstance(dtype, torch.dtype):
             dtype = {torch.float32: FA_DTYPE_FP32, torch.bfloat16: FA_DTYPE_BF16,
                      torch.float16: FA_DTYPE_FP16}.get(dtype, -1)
@@ -164,7 +176,12 @@ class Config:
             atten_mask=(None if atten_mask is None else atten_mask.data_ptr()),
             mask_rows=(0 if atten_mask is None else int(atten_mask.shape[0])),
             mask_cols=(0 if atten_mask is None else int(atten_mask.shape[1])),
-            layout=_LAYOUTS.get(layout, -1))
+            layout=_LAYOUTS.get(layout, -1),
+            pse=(None if pse is None else pse.data_ptr()),
+            pse_batch=(0 if pse is None else int(pse.shape[0])),
+            pse_rows=(0 if pse is None else int(pse.shape[2])),
+            pse_cols=(0 if pse is None else int(pse.shape[3])),
+            pse_type=(int(pse_type) if pse is not None else 0))
 
     @property
     def ref(self):

@@ -28,6 +28,9 @@ struct Problem {
   int64_t pre = 0, next = 0;
   bool deterministic = true;
   int layout = FA_LAYOUT_TND;      // fa_config.layout
+  const void* pse = nullptr;       // external pse (device) and its shape
+  int64_t pse_batch = 0, pse_rows = 0, pse_cols = 0;
+  int pse_type = 0, pse_mode = 0;  // mode: 0 row i, 1 single row, 2 1024-row compression
   int64_t sq = 0, skv = 0;         // common sequence lengths of the fixed-length layouts
   bool pse_sqrt = false;           // FA_FLAG_PSE_SQRT: the slopes generate pseType 3
   bool slopes_per_batch = false;   // FA_FLAG_SLOPES_PER_BATCH: slopes are [B, Nq]
@@ -113,6 +116,36 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   }
   pr->tq = cq[pr->batch];
   pr->tkv = ck[pr->batch];
+  if (cfg->pse) {
+    // the 16-bit kernels' external-pse instances are switched off: a bf16 run of them
+    // faulted on the device and the cause is not yet shown; fp32 inputs only
+    if (cfg->dtype != FA_DTYPE_FP32) return FA_ERR_PARAM_INVALID;
+    int64_t max_q = 0, max_kv = 0;
+    for (int64_t b = 0; b < pr->batch; ++b) {
+      max_q = std::max<int64_t>(max_q, cq[b + 1] - cq[b]);
+      max_kv = std::max<int64_t>(max_kv, ck[b + 1] - ck[b]);
+    }
+    if (cfg->pse_type != 0 && cfg->pse_type != 1) return FA_ERR_PARAM_INVALID;
+    if (cfg->pse_batch != 1 && cfg->pse_batch != pr->batch) return FA_ERR_PARAM_INVALID;
+    if (cfg->pse_cols < max_kv || cfg->pse_cols > kMaxTokens || cfg->pse_rows < 1) return FA_ERR_PARAM_INVALID;
+    int pmode;
+    if (cfg->pse_rows == 1) pmode = 1;
+    else if (cfg->pse_rows >= max_q && cfg->pse_rows <= kMaxTokens) pmode = 0;
+    else if (cfg->pse_rows == 1024) pmode = 2;
+    else return FA_ERR_PARAM_INVALID;
+    if (pmode == 2) {
+      // the compressed form holds a lower-triangle bias of square sequences
+      if (mode != FA_SPARSE_LEFT_UP_CAUSAL && mode != FA_SPARSE_RIGHT_DOWN_CAUSAL) return FA_ERR_PARAM_INVALID;
+      for (int64_t b = 0; b < pr->batch; ++b)
+        if (cq[b + 1] - cq[b] != ck[b + 1] - ck[b]) return FA_ERR_PARAM_INVALID;
+    }
+    pr->pse = cfg->pse;
+    pr->pse_batch = cfg->pse_batch;
+    pr->pse_rows = cfg->pse_rows;
+    pr->pse_cols = cfg->pse_cols;
+    pr->pse_type = cfg->pse_type;
+    pr->pse_mode = pmode;
+  }
   if (cfg->layout < FA_LAYOUT_TND || cfg->layout > FA_LAYOUT_SBH) return FA_ERR_PARAM_INVALID;
   pr->layout = cfg->layout;
   if (pr->layout != FA_LAYOUT_TND) {
@@ -138,6 +171,8 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
     pr->mask_cols = cfg->mask_cols;
     pr->mask_words = (cfg->mask_cols + 31) / 32;
   }
+  // the kernels have no instances of an external pse with an attenMask
+  if (pr->pse && pr->mask) return FA_ERR_PARAM_INVALID;
   pr->drop_bits = bits;
   return FA_OK;
 }
@@ -328,6 +363,17 @@ hipError_t timed(KernelId id, hipStream_t s, F&& launch) {
 
 fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+template <typename P>
+void fill_pse(const Problem& pr, P& p) {
+  p.pse = pr.pse;
+  if (!pr.pse) return;
+  p.pse_hstride = pr.pse_rows * pr.pse_cols;
+  p.pse_bstride = pr.pse_batch == 1 ? 0 : pr.nq * p.pse_hstride;
+  p.pse_cols = (int32_t)pr.pse_cols;
+  p.pse_mode = pr.pse_mode;
+  p.pse_coef = (float)((pr.pse_type == 1 ? pr.scale : 1.0) * 1.4426950408889634);
+}
+
 // One BNSD / SBH tensor of the query side (q = true: B sequences of Sq rows, Nq
 // heads) or the key side to or from its TND copy.
 hipError_t relayout_tensor(const Problem& pr, bool q_side, const void* src, void* dst, bool to_tnd,
@@ -510,6 +556,8 @@ fa_status fa_fwd(const fa_config* cfg, const void* q, const void* k, const void*
       (sink && !aligned(sink, 4)))
     return FA_ERR_PARAM_INVALID;
   if (alibi_slopes && (st = check_alibi(pr)) != FA_OK) return st;
+  if (alibi_slopes && pr.pse) return FA_ERR_PARAM_INVALID;
+  if (pr.pse && !aligned(pr.pse, 4)) return FA_ERR_PARAM_INVALID;
   const Layout bound = fwd_layout_bound(pr);
   if (!workspace) return FA_ERR_PARAM_NULLPTR;
   if (workspace_bytes < bound.total) return FA_ERR_WORKSPACE;
@@ -538,6 +586,7 @@ fa_status fa_fwd(const fa_config* cfg, const void* q, const void* k, const void*
   p.slopes = alibi_slopes; p.sink = sink;
   p.slope_bstride = pr.slopes_per_batch ? (int32_t)pr.nq : 0;
   p.pse_sqrt = pr.pse_sqrt ? 1 : 0;
+  fill_pse(pr, p);
   p.cu_q = reinterpret_cast<const int32_t*>(ws + L.cu_q);
   p.cu_kv = reinterpret_cast<const int32_t*>(ws + L.cu_kv);
   p.bit_base = reinterpret_cast<const int64_t*>(ws + L.bit_base);
@@ -574,13 +623,15 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
       (alibi_slopes && !aligned(alibi_slopes, 4)) || (sink && !aligned(sink, 4)) || (dsink && !aligned(dsink, 4)))
     return FA_ERR_PARAM_INVALID;
   if (alibi_slopes && (st = check_alibi(pr)) != FA_OK) return st;
+  if (alibi_slopes && pr.pse) return FA_ERR_PARAM_INVALID;
+  if (pr.pse && !aligned(pr.pse, 4)) return FA_ERR_PARAM_INVALID;
   const Layout bound = bwd_layout_bound(pr);
   if (!workspace) return FA_ERR_PARAM_NULLPTR;
   if (workspace_bytes < bound.total) return FA_ERR_WORKSPACE;
 
-  // the atomic dK/dV kernel for 16-bit D = 128 has no alibi variant (its registers
+  // the atomic dK/dV kernel for 16-bit D = 128 has no pse variant (its registers
   // do not fit one): run the deterministic passes, which need less workspace
-  if (alibi_slopes && pr.dtype != FA_DTYPE_FP32 && pr.d == 128) pr.deterministic = true;
+  if ((alibi_slopes || pr.pse) && pr.dtype != FA_DTYPE_FP32 && pr.d == 128) pr.deterministic = true;
   // the attenMask is read by the deterministic passes only (the atomic kernels have no mask instances)
   if (pr.mask) pr.deterministic = true;
   std::vector<WorkItem> kv_items = schedule(pr, 1, nullptr, nullptr);
@@ -615,6 +666,7 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
   p.slopes = alibi_slopes; p.sink = sink;
   p.slope_bstride = pr.slopes_per_batch ? (int32_t)pr.nq : 0;
   p.pse_sqrt = pr.pse_sqrt ? 1 : 0;
+  fill_pse(pr, p);
   p.cu_q = reinterpret_cast<const int32_t*>(ws + L.cu_q);
   p.cu_kv = reinterpret_cast<const int32_t*>(ws + L.cu_kv);
   p.bit_base = reinterpret_cast<const int64_t*>(ws + L.bit_base);

@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
   }
   const float lse2 = row_ok ? p.lse[rowg * p.nq + h] : __builtin_inff();
   const float di = row_ok ? p.delta[rowg * p.nq + h] : 0.f;
-  const float slope_l2 = ALIBI ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
+  const float slope_l2 = pse_slopes(ALIBI) ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
   f32x16 acc[S::NDB];
 #pragma unroll
   for (int db = 0; db < S::NDB; ++db) acc[db] = f32x16{};
@@ -286,7 +286,10 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
           pr = fast_exp2(__builtin_fmaf(s[r], p.scale_log2, -lse2));
         } else {
           float x = s[r] * p.scale_log2;
-          if constexpr (ALIBI != 0) x = add_pse<ALIBI>(x, slope_l2, jmi + (float)(8 * (r >> 2) + (r & 3)));
+          if constexpr (ALIBI == kPseExt)
+            x = __builtin_fmaf(p.pse_coef, (row_ok && jj < lkv) ? pse_value<T>(p, b, h, i, jj, lq) : 0.f, x);
+          else if constexpr (ALIBI != 0)
+            x = add_pse<ALIBI>(x, slope_l2, jmi + (float)(8 * (r >> 2) + (r & 3)));
           if (!full) {
             const bool ok = row_ok & (jj < lkv) & (jj >= fa_row_lo(win, i)) & (jj <= fa_row_hi(win, i)) &
                             !((mwk >> (kk - 32 * kb)) & 1u);

@@ -249,7 +249,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
   };
   // P~ and dS of one block as 16-bit A operands (lane = key, registers = rows)
   auto elem = [&](auto full_c, const char* st, int r0, int rb, const f32x16& s, const f32x16& dp, float slope_l2,
-                  V8 (&pa)[2], V8 (&da)[2]) {
+                  int h, V8 (&pa)[2], V8 (&da)[2]) {
     constexpr bool plain = !ALIBI && decltype(full_c)::value;
     const float* lse_s = reinterpret_cast<const float*>(st + S::OFF_LSE);
     const float* del_s = reinterpret_cast<const float*>(st + S::OFF_DEL);
@@ -273,7 +273,10 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
           pr = fast_exp2(__builtin_fmaf(s[r], sc, -lse4[e]));
         } else {
           float x = s[r] * sc;
-          if constexpr (ALIBI != 0) x = add_pse<ALIBI>(x, slope_l2, jmi - (float)e);
+          if constexpr (ALIBI == kPseExt)
+            x = __builtin_fmaf(p.pse_coef, (i < lq && key_ok) ? pse_value<T>(p, b, h, i, j, lq) : 0.f, x);
+          else if constexpr (ALIBI != 0)
+            x = add_pse<ALIBI>(x, slope_l2, jmi - (float)e);
           if constexpr (!decltype(full_c)::value) {
             const bool ok = (i < lq) & key_ok & (j >= fa_row_lo(win, i)) & (j <= fa_row_hi(win, i)) &
                             !((mb4[e] >> lrow) & 1u);
@@ -311,7 +314,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
 
   auto compute_16 = [&](const char* st, auto n) {
     const int h = step_head(n), r0 = step_row0(n);
-    const float slope_l2 = ALIBI ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
+    const float slope_l2 = pse_slopes(ALIBI) ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
     // with an attenMask every block takes the masked path
     const bool full0 = fa_tile_full(win, r0, 32, wc0, 32, lq, lkv) && !MASK;
     const bool full1 = fa_tile_full(win, r0 + 32, 32, wc0, 32, lq, lkv) && !MASK;
@@ -323,8 +326,8 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
       __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
       sched_alternate<kSdpMfma, 0x008, 0x100>();
       __builtin_amdgcn_sched_barrier(0);
-      if (full) elem(std::true_type{}, st, r0, rb, sx, dpx, slope_l2, pax, dax);
-      else elem(std::false_type{}, st, r0, rb, sx, dpx, slope_l2, pax, dax);
+      if (full) elem(std::true_type{}, st, r0, rb, sx, dpx, slope_l2, h, pax, dax);
+      else elem(std::false_type{}, st, r0, rb, sx, dpx, slope_l2, h, pax, dax);
       if constexpr (ATOMIC) store_ds(rb, dax);
       __builtin_amdgcn_sched_barrier(0);
       grads(st, rb, pax, dax);
@@ -339,7 +342,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
 
   auto compute = [&](const char* st, int n) {
     const int h = step_head(n), r0 = step_row0(n);
-    const float slope_l2 = ALIBI ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
+    const float slope_l2 = pse_slopes(ALIBI) ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
     const float* lse_s = reinterpret_cast<const float*>(st + S::OFF_LSE);
     const float* del_s = reinterpret_cast<const float*>(st + S::OFF_DEL);
     const uint32_t* bits_s = reinterpret_cast<const uint32_t*>(st + S::OFF_BITS);
@@ -381,7 +384,10 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
       for (int r = 0; r < 16; ++r) {
         const int rr = 32 * rb + 8 * (r >> 2) + 4 * hh + (r & 3);
         float x = s[r] * p.scale_log2;
-        if constexpr (ALIBI != 0) x = add_pse<ALIBI>(x, slope_l2, (float)(j - (r0 + rr)));
+        if constexpr (ALIBI == kPseExt)
+          x = __builtin_fmaf(p.pse_coef, (r0 + rr < lq && key_ok) ? pse_value<T>(p, b, h, r0 + rr, j, lq) : 0.f, x);
+        else if constexpr (ALIBI != 0)
+          x = add_pse<ALIBI>(x, slope_l2, (float)(j - (r0 + rr)));
         if (!full && (!fa_allowed(win, r0 + rr, j, lq, lkv) ||
                       (MASK && ((reinterpret_cast<const uint32_t*>(st + S::OFF_MBITS)[wave * kKvBM + rr] >> lrow) & 1u))))
           x = kNegInf;
@@ -692,7 +698,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
 
   auto compute = [&](const char* st, int n) {
     const int h = step_head(n), r0 = step_row0(n);
-    const float slope_l2 = ALIBI ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
+    const float slope_l2 = pse_slopes(ALIBI) ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
     const float sc = p.scale_log2;
     const int rb = half;                     // the row block whose P~ / dS this wave forms
     // ---- S = Q K^T, dP~ = dY V^T for rows block rb (lane = key, registers = rows) ----
@@ -736,7 +742,10 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
               pr = fast_exp2(__builtin_fmaf(s[r], sc, -lse4[e]));
             } else {
               float x = s[r] * sc;
-              if constexpr (ALIBI != 0) x = add_pse<ALIBI>(x, slope_l2, jmi - (float)e);
+                  if constexpr (ALIBI == kPseExt)
+                x = __builtin_fmaf(p.pse_coef, (i < lq && key_ok) ? pse_value<E>(p, b, h, i, j, lq) : 0.f, x);
+              else if constexpr (ALIBI != 0)
+                x = add_pse<ALIBI>(x, slope_l2, jmi - (float)e);
               if constexpr (!decltype(full_c)::value) {
                 const bool ok = (i < lq) & key_ok & (j >= fa_row_lo(win, i)) & (j <= fa_row_hi(win, i)) &
                                 !((mb4[e] >> lrow) & 1u);

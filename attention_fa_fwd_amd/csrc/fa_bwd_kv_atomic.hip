@@ -10,7 +10,7 @@ static hipError_t launch_kv_t(const BwdParams& p, hipStream_t s) {
   const dim3 grid((unsigned)blocks), block(256);
   // no alibi instance of the atomic 16-bit D = 128 kernel (see launch_bwd_kv)
   constexpr bool kAlibi = !(ATOMIC && sizeof(T) == 2 && D == 128);
-  if (!kAlibi && p.slopes != nullptr) return hipErrorInvalidValue;
+  if (!kAlibi && (p.slopes != nullptr || p.pse != nullptr)) return hipErrorInvalidValue;
   // no attenMask instances: the host routes masked problems to the deterministic passes
   if (p.mbits != nullptr) return hipErrorInvalidValue;
   return with_flags(p.use_dropout != 0, kAlibi ? pse_kind(p) : kPseNone, false, [&](auto dr, auto al, auto mk) {

@@ -101,6 +101,30 @@ __device__ __forceinline__ float add_pse(float x, float slope_l2, float jmi) {
   else return __builtin_fmaf(slope_l2, jmi, x);
 }
 
+// External pse (pseShiftOptional of the grad page, realShiftOptional of the
+// ScoreV2 page) of local row i, key j of (sequence b, query head h), stored as
+// [batch or 1, Nq, rows, pse_cols] in the input type.  The stored row of i:
+//   mode 0: row i;  mode 1: the single row (shared by every query row);
+//   mode 2 (1024-row alibi compression, the last 1024 rows of the full pse):
+//     row i - max(0, Lq - 1024); a row above the stored block repeats the first
+//     stored row shifted along its diagonal (value(i, j) = value(i + t, j + t)).
+// The caller keeps i < Lq and j < Lkv.
+template <typename T, typename P>
+__device__ __forceinline__ float pse_value(const P& p, int b, int h, int i, int j, int lq) {
+  int r = i, c = j;
+  if (p.pse_mode == 1) {
+    r = 0;
+  } else if (p.pse_mode == 2) {
+    r = i - (lq > 1024 ? lq - 1024 : 0);
+    if (r < 0) {
+      c = j - r;
+      r = 0;
+    }
+  }
+  const T* base = reinterpret_cast<const T*>(p.pse) + (int64_t)b * p.pse_bstride + (int64_t)h * p.pse_hstride;
+  return (float)base[(int64_t)r * p.pse_cols + c];
+}
+
 // f32 -> 16-bit element (round to nearest even) and 16-bit element bits -> f32
 template <typename E>
 __device__ __forceinline__ E cvt16(float f) { return (E)f; }

@@ -122,7 +122,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
     }
   }
 
-  const float slope_l2 = ALIBI ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
+  const float slope_l2 = pse_slopes(ALIBI) ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
   const bool has_sink = p.sink != nullptr;
   float m_run = has_sink ? p.sink[h] * kLog2e : kNegInf;   // exponent offset
   float m_true = m_run;                                     // running maximum
@@ -229,7 +229,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
         for (int r = 0; r < 16; ++r) {
           const int j = c0 + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
           float x = s[kb][r] * sc;
-          if constexpr (ALIBI != 0) x = add_pse<ALIBI>(x, slope_l2, (float)(j - i));
+          if constexpr (ALIBI == kPseExt)
+            x = __builtin_fmaf(p.pse_coef, (row_ok && j < lkv) ? pse_value<T>(p, b, h, i, j, lq) : 0.f, x);
+          else if constexpr (ALIBI != 0)
+            x = add_pse<ALIBI>(x, slope_l2, (float)(j - i));
           if (!decltype(full_c)::value &&
               (!fa_allowed(win, i, j, lq, lkv) || (MASK && ((rt.mw[kb] >> (8 * (r >> 2) + 4 * hh + (r & 3))) & 1u))))
             x = kNegInf;

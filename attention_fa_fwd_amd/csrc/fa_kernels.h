@@ -27,6 +27,12 @@ struct FwdParams {
   const float* slopes;
   int32_t slope_bstride;    // 0: slopes [Nq]; Nq: slopes [B, Nq]
   int32_t pse_sqrt;         // 1: the slopes generate pseType 3 (square-root distance)
+  const void* pse;          // external pse [pse batch, Nq, rows, pse_cols] of the input type, or null
+  int64_t pse_bstride;      // elements between sequences' blocks (0: one block for every sequence)
+  int64_t pse_hstride;      // elements between heads' blocks (rows * pse_cols)
+  int32_t pse_cols;
+  int32_t pse_mode;         // row of local row i: 0 row i; 1 the only row; 2 1024-row alibi compression
+  float pse_coef;           // log2(e) (pseType 0) or scale * log2(e) (pseType 1)
   const float* sink;
   const int32_t* cu_q;
   const int32_t* cu_kv;
@@ -65,6 +71,12 @@ struct BwdParams {
   const float* slopes;
   int32_t slope_bstride;    // 0: slopes [Nq]; Nq: slopes [B, Nq]
   int32_t pse_sqrt;         // 1: the slopes generate pseType 3 (square-root distance)
+  const void* pse;          // external pse [pse batch, Nq, rows, pse_cols] of the input type, or null
+  int64_t pse_bstride;      // elements between sequences' blocks (0: one block for every sequence)
+  int64_t pse_hstride;      // elements between heads' blocks (rows * pse_cols)
+  int32_t pse_cols;
+  int32_t pse_mode;         // row of local row i: 0 row i; 1 the only row; 2 1024-row alibi compression
+  float pse_coef;           // log2(e) (pseType 0) or scale * log2(e) (pseType 1)
   const float* sink;
   const int32_t* cu_q;
   const int32_t* cu_kv;
@@ -131,23 +143,34 @@ constexpr int kKvBN = 128, kKvBM = 64;
 constexpr int kDqBM = 128, kDqBN = 64;
 constexpr int kPreRowsPerBlock = 64;
 
-// Kind of the generated position bias (the ALIBI template argument of the
-// kernels): none, pseType 2 (linear distance) or pseType 3 (square-root distance).
-constexpr int kPseNone = 0, kPseLinear = 1, kPseSqrt = 2;
+// Kind of the position bias (the ALIBI template argument of the kernels): none,
+// generated pseType 2 (linear distance) or 3 (square-root distance), or an
+// external pse tensor (pseType 0 / 1).
+constexpr int kPseNone = 0, kPseLinear = 1, kPseSqrt = 2, kPseExt = 3;
+constexpr bool pse_slopes(int kind) { return kind == kPseLinear || kind == kPseSqrt; }
 template <typename P>
 int pse_kind(const P& p) {
+  if (p.pse != nullptr) return kPseExt;
   return p.slopes == nullptr ? kPseNone : (p.pse_sqrt ? kPseSqrt : kPseLinear);
 }
 
 // Calls f(drop, pse, mask) with drop and mask as std::integral_constant<bool, .>
 // and pse (a kPse* kind) as std::integral_constant<int, .>, so a launcher names
-// one kernel instance per combination.
+// one kernel instance per combination.  An external pse together with an
+// attenMask has no instances (the heaviest of them would not fit the registers);
+// the host rejects that combination.
 template <typename F>
 hipError_t with_flags(bool drop, int pse, bool mask, F&& f) {
-  auto by_mask = [&](auto d, auto a) {
-    return mask ? f(d, a, std::true_type{}) : f(d, a, std::false_type{});
+  auto by_mask = [&](auto d, auto a) -> hipError_t {
+    if constexpr (decltype(a)::value == kPseExt) {
+      if (mask) return hipErrorInvalidValue;
+      return f(d, a, std::false_type{});
+    } else {
+      return mask ? f(d, a, std::true_type{}) : f(d, a, std::false_type{});
+    }
   };
   auto by_pse = [&](auto d) {
+    if (pse == kPseExt) return by_mask(d, std::integral_constant<int, kPseExt>{});
     if (pse == kPseSqrt) return by_mask(d, std::integral_constant<int, kPseSqrt>{});
     if (pse == kPseLinear) return by_mask(d, std::integral_constant<int, kPseLinear>{});
     return by_mask(d, std::integral_constant<int, kPseNone>{});

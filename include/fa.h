@@ -131,6 +131,24 @@ typedef struct fa_config {
                                     (the size query accounts for them) and the outputs
                                     scattered back.  softmax_max / softmax_sum stay
                                     [T, Nq] with T = B*Sq, row t = b*Sq + s.                 */
+  const void* pse;               /* DEVICE, optional external pse of cfg->dtype (grad page
+                                    "pseShiftOptional", ScoreV2 page "realShiftOptional"),
+                                    row-major [pse_batch, Nq, pse_rows, pse_cols], indexed by
+                                    the sequence's local row i and key j.  pse_rows selects
+                                    the form: 1 = one row for every query row ([B,N,1,Skv]);
+                                    >= every Lq = the full [S1, S2] block; 1024 below some Lq
+                                    = alibi compression (the last 1024 rows of the full pse,
+                                    Lq == Lkv and sparse mode 2 or 3 required; a row i above
+                                    the stored block reads the first stored row shifted along
+                                    the diagonal).  Not with alibi_slopes or an attenMask;
+                                    FA_DTYPE_FP32 inputs only for now (16-bit inputs ->
+                                    FA_ERR_PARAM_INVALID).  NULL = none.                      */
+  int64_t pse_batch;             /* 1 (shared by the sequences) or B                          */
+  int64_t pse_rows;              /* see pse                                                   */
+  int64_t pse_cols;              /* S2 >= every Lkv                                           */
+  int32_t pse_type;              /* with pse: 0 = mul then add, S = scale*QK^T + pse;
+                                    1 = add then mul, S = scale*(QK^T + pse) (the grad page's
+                                    formula; ScoreV2 pseType table)                           */
 } fa_config;
 
 /* Device workspace bytes needed by fa_fwd for this configuration (>= 256). */

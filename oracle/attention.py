@@ -26,6 +26,14 @@ the design notes):
     taken before dropout.  Keep bits: one flat stream over batch, query head,
     query row, key (the page's size formula), LSB first in each byte.
   * "scale" replaces 1/sqrt(d) everywhere (scaleValue is "the Muls scalar").
+  * External pse (grad page "pseShiftOptional", ScoreV2 page "realShiftOptional"
+    and pseType table): pseType 1 adds it before scaling, S = scale*(QK^T + pse)
+    (the grad page's formula); pseType 0 after, S = scale*QK^T + pse.  The
+    tensor is [1 or B, N, rows, cols] indexed by local (row, key): one row for
+    every query row, the full block, or the ScoreV2 page's alibi compression
+    (only the last 1024 rows of the full bias; a row above them is the first
+    stored row shifted along its diagonal, which holds for the Toeplitz alibi
+    bias the compression is meant for).
   * Generated pse (aclnnFlashAttentionScoreV2, pseType table: types 2 and 3
     build the bias inside the operator from FLOAT32 slopes of shape [N] or
     [B, N]): pseType 2 is ALiBi, pse = -slope_h * (i - j); pseType 3 passes the
@@ -91,6 +99,28 @@ def alibi_pse(lq: int, lkv: int, slope: float, pse_type: int = 2) -> np.ndarray:
     raise ValueError(f"pse_type {pse_type} is not a generated pse")
 
 
+def pse_block(pse: np.ndarray, b: int, h: int, lq: int, lkv: int) -> np.ndarray:
+    """Bias of local rows 0..lq-1, keys 0..lkv-1 of (sequence b, head h) from an
+    external pse [1 or B, N, rows, cols]; entries the tensor does not define
+    (compressed form, above-diagonal keys of rows before the stored block) are NaN."""
+    blk = np.asarray(pse[0 if pse.shape[0] == 1 else b, h], dtype=np.float64)
+    rows, cols = blk.shape
+    if rows == 1:
+        return np.repeat(blk[:1, :lkv], lq, axis=0)
+    if rows >= lq:
+        return blk[:lq, :lkv].copy()
+    # alibi compression: the stored rows are full rows lq - rows .. lq - 1
+    first = lq - rows
+    out = np.full((lq, lkv), np.nan)
+    out[first:] = blk[:, :lkv]
+    for i in range(first):
+        t = first - i                       # value(i, j) = value(i + t, j + t): stored row 0
+        j = np.arange(lkv)
+        ok = j + t < cols
+        out[i, ok] = blk[0, j[ok] + t]
+    return out
+
+
 def keep_bits(drop_mask: np.ndarray, bit_base: int, lq: int, lkv: int) -> np.ndarray:
     """Keep bits z[i, j] for one (sequence, head) block starting at bit `bit_base`
     of the packed mask; bit n lives in byte n // 8 at position n % 8 (LSB first)."""
@@ -104,7 +134,7 @@ class _Problem:
 
     def __init__(self, q, k, v, cu_q, cu_kv, head_num, kv_heads, scale, keep_prob, sparse_mode,
                  pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix=None, atten_mask=None,
-                 pse_type=2):
+                 pse_type=2, pse=None):
         # kept in their given precision; each (sequence, head) slice is upcast to fp64 when used
         self.q = np.asarray(q)
         self.k = np.asarray(k)
@@ -125,6 +155,7 @@ class _Problem:
         # slopes [Nq] (shared by the sequences) or [B, Nq]
         self.slopes = None if alibi_slopes is None else np.asarray(alibi_slopes, dtype=np.float32).astype(np.float64)
         self.pse_type = int(pse_type)
+        self.pse = None if pse is None else np.asarray(pse)
         self.sink = None if sink is None else np.asarray(sink, dtype=np.float32).astype(np.float64)
         self.batch = len(self.cu_q) - 1
         self.prefix = np.zeros(self.batch, dtype=np.int64) if prefix is None else np.asarray(prefix, dtype=np.int64)
@@ -143,7 +174,10 @@ class _Problem:
         qb = self.q[q0:q1, h, :].astype(np.float64)
         kb = self.k[k0:k1, g, :].astype(np.float64)
         s = self.scale * (qb @ kb.T)
-        if self.slopes is not None:
+        if self.pse is not None:
+            bias = pse_block(self.pse, b, h, lq, lkv)
+            s = self.scale * (qb @ kb.T + bias) if self.pse_type == 1 else s + bias
+        elif self.slopes is not None:
             slope = self.slopes[b, h] if self.slopes.ndim == 2 else self.slopes[h]
             s = s + alibi_pse(lq, lkv, slope, self.pse_type)
         ok = allowed(lq, lkv, self.mode, self.pre, self.next, int(self.prefix[b]), self.atten_mask)
@@ -174,10 +208,10 @@ class _Problem:
 
 def _problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob=1.0,
              sparse_mode=0, pre_tokens=INT_MAX_TOKENS, next_tokens=INT_MAX_TOKENS, drop_mask=None,
-             alibi_slopes=None, sink=None, prefix=None, atten_mask=None, pse_type=2):
+             alibi_slopes=None, sink=None, prefix=None, atten_mask=None, pse_type=2, pse=None):
     return _Problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob,
                     sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix, atten_mask,
-                    pse_type)
+                    pse_type, pse)
 
 
 def _selected(subset, n):
@@ -187,13 +221,13 @@ def _selected(subset, n):
 def forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob=1.0,
             sparse_mode=0, pre_tokens=INT_MAX_TOKENS, next_tokens=INT_MAX_TOKENS, drop_mask=None,
             alibi_slopes=None, sink=None, batches=None, heads=None, prefix=None, atten_mask=None,
-            pse_type=2):
+            pse_type=2, pse=None):
     """Attention forward.  Returns O [T_q, Nq, D], softmax max m [T_q, Nq] and
     softmax sum l [T_q, Nq] (fp64).  With `batches` / `heads`, only those
     sequences / query heads are computed and every other entry is NaN."""
     pr = _problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob,
                   sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix, atten_mask,
-                  pse_type)
+                  pse_type, pse)
     tq, d = pr.q.shape[0], pr.v.shape[2]
     out = np.full((tq, pr.nq, d), np.nan)
     mx = np.full((tq, pr.nq), np.nan)
@@ -210,7 +244,7 @@ def forward(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, kee
 def backward(q, k, v, dy, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob=1.0,
              sparse_mode=0, pre_tokens=INT_MAX_TOKENS, next_tokens=INT_MAX_TOKENS, drop_mask=None,
              alibi_slopes=None, sink=None, batches=None, heads=None, prefix=None, atten_mask=None,
-             pse_type=2):
+             pse_type=2, pse=None):
     """Attention backward.  Returns dQ [T_q, Nq, D], dK, dV [T_kv, Nkv, D] and
     dSink [Nq] (None without a sink).  With `batches` / `heads`, only those
     sequences / query heads contribute: rows and keys of other sequences are NaN,
@@ -218,7 +252,7 @@ def backward(q, k, v, dy, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale
     and dSink sums the chosen sequences."""
     pr = _problem(q, k, v, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, scale, keep_prob,
                   sparse_mode, pre_tokens, next_tokens, drop_mask, alibi_slopes, sink, prefix, atten_mask,
-                  pse_type)
+                  pse_type, pse)
     dy = np.asarray(dy)
     dq = np.full(pr.q.shape, np.nan)
     dk = np.full(pr.k.shape, np.nan)

@@ -23,12 +23,12 @@ def say(msg: str):
     sys.stdout.flush()
 
 
-def config_of(case: wl.Case, deterministic: bool = True, mask=None) -> fa.Config:
-    """mask: the case's attenMask as a device tensor (required when the case has one)."""
+def config_of(case: wl.Case, deterministic: bool = True, mask=None, pse=None) -> fa.Config:
+    """mask, pse: the case's attenMask and external pse as device tensors (required when the case has them)."""
     return fa.Config(case.cu_seqlens_q, case.cu_seqlens_kv, case.head_num, case.kv_heads, case.head_dim,
                      case.dtype, case.scale, case.keep_prob, case.sparse_mode, case.pre_tokens,
                      case.next_tokens, deterministic, prefix=case.prefix, atten_mask=mask, pse_type=case.pse_type,
-                     slopes_per_batch=case.alibi_slopes is not None and case.alibi_slopes.ndim == 2)
+                     slopes_per_batch=case.alibi_slopes is not None and case.alibi_slopes.ndim == 2, pse=pse)
 
 
 def device_inputs(case: wl.Case, device="cuda"):
@@ -38,13 +38,14 @@ def device_inputs(case: wl.Case, device="cuda"):
     d["slopes"] = torch.from_numpy(case.alibi_slopes).to(dev) if case.alibi_slopes is not None else None
     d["sink"] = torch.from_numpy(case.sink).to(dev) if case.sink is not None else None
     d["mask"] = torch.from_numpy(case.atten_mask).to(dev) if case.atten_mask is not None else None
+    d["pse"] = case.pse.to(dev) if case.pse is not None else None
     return d
 
 
 def run_gpu(case: wl.Case, deterministic: bool = True, backward: bool = True, inputs=None):
     """fa_fwd (+ fa_bwd) on cuda:0; returns numpy fp64 copies of every output."""
     x = inputs if inputs is not None else device_inputs(case)
-    cfg = config_of(case, deterministic, x.get("mask"))
+    cfg = config_of(case, deterministic, x.get("mask"), x.get("pse"))
     out, m, l = fa.fa_fwd(cfg, x["q"], x["k"], x["v"], x["drop"], x["slopes"], x["sink"])
     res = dict(out=out, m=m, l=l)
     if backward:
@@ -65,7 +66,7 @@ def run_oracle(case: wl.Case, batches=None, heads=None, backward: bool = True):
     kw = dict(keep_prob=case.keep_prob, sparse_mode=case.sparse_mode, pre_tokens=case.pre_tokens,
               next_tokens=case.next_tokens, drop_mask=case.drop_mask, alibi_slopes=case.alibi_slopes,
               sink=case.sink, batches=batches, heads=heads, prefix=case.prefix, atten_mask=case.atten_mask,
-              pse_type=case.pse_type)
+              pse_type=case.pse_type, pse=None if case.pse is None else host_f32(case.pse))
     o, m, l = oracle.forward(q, k, v, case.cu_seqlens_q, case.cu_seqlens_kv, case.head_num, case.kv_heads,
                              case.scale, **kw)
     res = dict(out=o, m=m, l=l)

@@ -382,3 +382,46 @@ def test_layout_validation():
     assert _fwd(cfg) == fa.FA_ERR_PARAM_INVALID
     assert fa.layout_shape(_cfg(layout="SBH", **uniform), True) == (6, 2, 4 * 128)
     assert fa.layout_shape(_cfg(layout="BNSD", **uniform), False) == (2, 2, 9, 128)
+
+
+def test_external_pse_validation():
+    import torch as _t
+    n = ctypes.c_uint64(0)
+
+    def cfg(**pse_over):
+        c = _cfg(cu_seqlens_q=[0, 6, 12], cu_seqlens_kv=[0, 6, 12], dtype=fa.FA_DTYPE_FP32)
+        c.c.pse = 0x10000
+        c.c.pse_batch, c.c.pse_rows, c.c.pse_cols, c.c.pse_type = 2, 6, 6, 1
+        for key, val in pse_over.items():
+            setattr(c.c, key, val)
+        return c
+
+    def size(c):
+        return fa.lib().fa_fwd_workspace_size(c.ref, ctypes.byref(n))
+
+    assert size(cfg()) == fa.FA_OK
+    for good in (dict(pse_batch=1), dict(pse_rows=1), dict(pse_rows=1024), dict(pse_type=0), dict(pse_cols=9)):
+        assert size(cfg(**good)) == fa.FA_OK, good
+    for bad in (dict(pse_type=2), dict(pse_batch=3), dict(pse_rows=5), dict(pse_cols=5), dict(pse_rows=0)):
+        assert size(cfg(**bad)) == fa.FA_ERR_PARAM_INVALID, bad
+    # the 1024-row compression needs a lower-triangle mode and square sequences
+    c = cfg(pse_rows=1024)
+    c.c.sparse_mode = 0
+    c.c.cu_seqlens_q = (ctypes.c_int64 * 3)(0, 1100, 1101)
+    c.c.cu_seqlens_kv = (ctypes.c_int64 * 3)(0, 1100, 1101)
+    c.c.pse_cols = 1100
+    assert size(c) == fa.FA_ERR_PARAM_INVALID
+    c.c.sparse_mode = 3
+    assert size(c) == fa.FA_OK
+    c.c.cu_seqlens_kv = (ctypes.c_int64 * 3)(0, 1100, 1102)
+    assert size(c) == fa.FA_ERR_PARAM_INVALID
+    # not with alibi slopes, not with an attenMask
+    assert _fwd(cfg(), slopes=FAKE) == fa.FA_ERR_PARAM_INVALID
+    c = cfg()
+    c.c.sparse_mode, c.c.atten_mask, c.c.mask_rows, c.c.mask_cols = 1, 0x20000, 6, 6
+    assert size(c) == fa.FA_ERR_PARAM_INVALID
+    with pytest.raises(ValueError):
+        _cfg(pse=_t.zeros(1, 4, 1, 7), pse_type=2)
+    # 16-bit inputs with an external pse are rejected for now
+    assert size(cfg(dtype=fa.FA_DTYPE_BF16)) == fa.FA_ERR_PARAM_INVALID
+    assert size(cfg(dtype=fa.FA_DTYPE_FP16)) == fa.FA_ERR_PARAM_INVALID

@@ -54,6 +54,15 @@ EDGE_CASES = {
                                             keep_prob=0.8, sink=True),
     "alibi_batch_slopes_band": dict(lens_q=[257, 64], head_num=4, kv_heads=4, head_dim=128, sparse_mode=4,
                                     pre_tokens=40, next_tokens=0, alibi=True, slopes_per_batch=True),
+    "cross_nomask_d128": dict(lens_q=[200, 77, 129], lens_kv=[130, 300, 129], head_num=4, kv_heads=2,
+                              head_dim=128, sparse_mode=0),
+    # external pse (pseType 1: before scaling, 0: after): full block, one shared row, 1024-row compression
+    "pse_full_type1_cross": dict(lens_q=[200, 77, 129], lens_kv=[130, 300, 129], head_num=4, kv_heads=2,
+                                 head_dim=128, sparse_mode=0, pse=("full", False), pse_type=1),
+    "pse_row_type0_drop_sink": dict(lens_q=[190, 67], head_num=2, kv_heads=1, head_dim=64, sparse_mode=3,
+                                    pse=("row", True), pse_type=0, keep_prob=0.8, sink=True),
+    "pse_compressed_causal": dict(lens_q=[1100, 300], head_num=2, kv_heads=2, head_dim=64, sparse_mode=3,
+                                  pse=("compressed", False), pse_type=1),
 }
 
 
@@ -71,6 +80,9 @@ def _edge(name, dtype, seed):
 @pytest.mark.parametrize("dtype", [F32, BF16, F16])
 @pytest.mark.parametrize("name", list(EDGE_CASES))
 def test_edge_case(name, dtype, deterministic):
+    if "pse" in EDGE_CASES[name] and dtype != F32:
+        pytest.skip("external pse with 16-bit inputs is switched off: a bf16 run faulted on the device and the "
+                    "cause is not yet shown (the library rejects it)")
     seed = 100 + list(EDGE_CASES).index(name)
     case = _edge(name, dtype, seed)
     say(f"edge {name} dtype={dtype} det={deterministic} seed={seed} lens={list(case.lens_q)}/{list(case.lens_kv)}")

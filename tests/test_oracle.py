@@ -160,6 +160,82 @@ def test_pse_sqrt_on_square_distances_equals_linear():
     np.testing.assert_allclose(dv3[sel], dv2, rtol=1e-12, atol=1e-14)
 
 
+def _alibi_tensor(slopes, rows, cols, first_row=0):
+    """[1, N, rows, cols] holding -slope_h * (i - j) for full rows first_row .. first_row + rows - 1."""
+    i = np.arange(first_row, first_row + rows, dtype=np.float64)[:, None]
+    j = np.arange(cols, dtype=np.float64)[None, :]
+    return np.stack([-float(s) * (i - j) for s in slopes])[None]
+
+
+def test_external_pse_reproduces_the_generated_alibi():
+    # pseType 0 (add after scaling) with the ALiBi bias written out as a full [S1, S2]
+    # tensor gives the pseType 2 result; pseType 1 (add before scaling) needs the bias / scale;
+    # a pse shared by the batch equals per-sequence copies
+    lens = [9, 14, 5]
+    cu = _cu(lens)
+    rng = np.random.default_rng(12)
+    q, k, v = (rng.standard_normal((cu[-1], 2, 4)) for _ in range(3))
+    dy = rng.standard_normal((cu[-1], 2, 4))
+    slopes = wl.alibi_slopes(2)
+    scale = 0.6
+    kw = dict(sparse_mode=3)
+    ref = oracle.forward(q, k, v, cu, cu, 2, 2, scale, alibi_slopes=slopes, **kw)
+    gref = oracle.backward(q, k, v, dy, cu, cu, 2, 2, scale, alibi_slopes=slopes, **kw)
+    full = _alibi_tensor(slopes.astype(np.float64), 14, 14)
+    for pse, ptype in ((full, 0), (full / scale, 1), (np.repeat(full, 3, axis=0), 0)):
+        got = oracle.forward(q, k, v, cu, cu, 2, 2, scale, pse=pse, pse_type=ptype, **kw)
+        ggot = oracle.backward(q, k, v, dy, cu, cu, 2, 2, scale, pse=pse, pse_type=ptype, **kw)
+        for a, r in zip(got + ggot[:3], ref + gref[:3]):
+            np.testing.assert_allclose(a, r, rtol=1e-12, atol=1e-14)
+
+
+def test_external_pse_row_broadcast_and_compression():
+    # a single row is every query row's bias; the 1024-row alibi compression of a
+    # Toeplitz bias (lower triangle, Lq = Lkv > 1024) equals the full bias
+    rng = np.random.default_rng(13)
+    row = rng.standard_normal((1, 1, 1, 6))
+    assert np.array_equal(oracle.pse_block(row, 0, 0, 4, 6), np.repeat(row[0, 0], 4, axis=0))
+    lq = 1030
+    full = _alibi_tensor([0.013], lq, lq)
+    comp = full[:, :, -1024:, :]
+    got = oracle.pse_block(comp, 0, 0, lq, lq)
+    lower = np.tril(np.ones((lq, lq), bool))
+    np.testing.assert_array_equal(got[lower], full[0, 0][lower])
+    # shorter sequences read the stored rows from the top
+    np.testing.assert_array_equal(oracle.pse_block(comp, 0, 0, 700, 700), comp[0, 0, :700, :700])
+    # through the whole pass: 6 rows of a 1030-token causal sequence, D = 2
+    q = rng.standard_normal((lq, 1, 2))
+    k, v = rng.standard_normal((lq, 1, 2)), rng.standard_normal((lq, 1, 2))
+    sel = [0, 3, 5, 6, 700, 1029]
+    kw = dict(sparse_mode=3, pse_type=0)
+    a = oracle.forward(q, k, v, [0, lq], [0, lq], 1, 1, 0.5, pse=full, **kw)
+    c = oracle.forward(q, k, v, [0, lq], [0, lq], 1, 1, 0.5, pse=comp, **kw)
+    for x, y in zip(a, c):
+        np.testing.assert_array_equal(x[sel], y[sel])
+
+
+def test_backward_matches_autograd_external_pse():
+    # pseType 1 with a random full pse, dropout and sink, rectangular sequences in mode 0
+    c = _feature_case(63)
+    scale = 0.45
+    pse = np.random.default_rng(64).standard_normal((2, c["nq"], 9, 9)) * 0.5
+    tq = torch.tensor(c["q"], requires_grad=True)
+    tk = torch.tensor(c["k"], requires_grad=True)
+    tv = torch.tensor(c["v"], requires_grad=True)
+    ts = torch.tensor(c["sink"].astype(np.float64), requires_grad=True)
+    bits = np.unpackbits(c["mask"], bitorder="little")
+    out = _torch_attention(tq, tk, tv, ts, c["cq"], c["ck"], c["nq"], c["nkv"], scale, 0, 0, 0, c["keep"], bits,
+                           None, ext_pse=pse)
+    (out * torch.from_numpy(c["dy"])).sum().backward()
+    kw = dict(sparse_mode=0, keep_prob=c["keep"], drop_mask=c["mask"], sink=c["sink"], pse=pse, pse_type=1)
+    o, _, _ = oracle.forward(c["q"], c["k"], c["v"], c["cq"], c["ck"], c["nq"], c["nkv"], scale, **kw)
+    np.testing.assert_allclose(o, out.detach().numpy(), rtol=1e-12, atol=1e-13)
+    dq, dk, dv, ds = oracle.backward(c["q"], c["k"], c["v"], c["dy"], c["cq"], c["ck"], c["nq"], c["nkv"],
+                                     scale, **kw)
+    for got, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad), (ds, ts.grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=1e-11, atol=1e-12)
+
+
 def test_batch_slopes_equal_per_sequence_calls():
     # [B, N] slopes: sequence b uses row b, as a call on that sequence alone with [N] slopes
     lens = [7, 12, 5]
@@ -406,7 +482,7 @@ def test_dv_is_pt_transpose_dy():
 # --------------------------------------------------------------------------- autograd + finite differences
 
 def _torch_attention(q, k, v, sink, cu_q, cu_kv, nq, nkv, scale, mode, pre, nxt, keep, bits, slopes, prefix=None,
-                     atten_mask=None, pse_type=2):
+                     atten_mask=None, pse_type=2, ext_pse=None):
     """A second, plainly written attention in torch: the sink enters as an extra
     softmax column that is dropped afterwards; masks come from tril/triu."""
     outs = []
@@ -418,6 +494,8 @@ def _torch_attention(q, k, v, sink, cu_q, cu_kv, nq, nkv, scale, mode, pre, nxt,
         heads = []
         for h in range(nq):
             s = scale * q[q0:q1, h] @ k[k0:k1, h // g].T
+            if ext_pse is not None:   # pseType 1, a full [B, N, S1, S2] block: scale * (QK^T + pse)
+                s = scale * (q[q0:q1, h] @ k[k0:k1, h // g].T + torch.from_numpy(ext_pse[b, h, :lq, :lkv]))
             if slopes is not None:
                 ii = torch.arange(lq, dtype=torch.float64)[:, None]
                 jj = torch.arange(lkv, dtype=torch.float64)[None, :]

@@ -59,7 +59,8 @@ class Case:
     next_tokens: int = INT_MAX_TOKENS
     drop_mask: Optional[np.ndarray] = None     # uint8 packed bits
     alibi_slopes: Optional[np.ndarray] = None  # float32 [Nq] or [B, Nq]
-    pse_type: int = 2                          # 2: -slope*(i-j); 3: -slope*sqrt(|i-j|)
+    pse_type: int = 2                          # 2: -slope*(i-j); 3: -slope*sqrt(|i-j|); 0 / 1 with pse
+    pse: Optional[torch.Tensor] = None         # external pse [1 or B, Nq, rows, cols] (cpu, input dtype)
     sink: Optional[np.ndarray] = None          # float32 [Nq]
     prefix: Optional[np.ndarray] = None        # int64 [B]: prefix N per sequence (sparse mode 6)
     atten_mask: Optional[np.ndarray] = None    # uint8 [S1Max, S2Max], nonzero = masked (modes 0/1/4)
@@ -154,9 +155,13 @@ def lognormal_lengths(seed, total: int, batch: int, median: float, lo: int, hi: 
 def make_case(name, lens_q, lens_kv=None, *, head_num, kv_heads, head_dim, dtype=torch.bfloat16,
               scale=None, keep_prob=1.0, sparse_mode=MODE_NONE, pre_tokens=INT_MAX_TOKENS,
               next_tokens=INT_MAX_TOKENS, alibi=False, sink=False, seed=0, dy_mult=1.0,
-              drop_mask=None, prefix=None, atten_mask=None, pse_type=2, slopes_per_batch=False) -> Case:
+              drop_mask=None, prefix=None, atten_mask=None, pse_type=2, slopes_per_batch=False,
+              pse=None) -> Case:
     """A case built from explicit lengths; every tensor is drawn from default_rng([seed, t]).
-    alibi=True adds generated-pse slopes ([Nq], or [B, Nq] with slopes_per_batch) of pseType pse_type."""
+    alibi=True adds generated-pse slopes ([Nq], or [B, Nq] with slopes_per_batch) of pseType pse_type.
+    pse=(form, shared) adds an external pse of pseType pse_type (0 or 1) drawn from
+    default_rng([seed, 9]) (normal, x0.5): form "full" [.., max Lq, max Lkv], "row"
+    [.., 1, max Lkv] or "compressed" [.., 1024, max Lkv]; shared -> batch dimension 1."""
     lens_q = np.asarray(lens_q, dtype=np.int64)
     lens_kv = lens_q.copy() if lens_kv is None else np.asarray(lens_kv, dtype=np.int64)
     cu_q, cu_kv = cu_from_lengths(lens_q), cu_from_lengths(lens_kv)
@@ -172,6 +177,11 @@ def make_case(name, lens_q, lens_kv=None, *, head_num, kv_heads, head_dim, dtype
         sink_v = np.random.default_rng([seed, 5]).standard_normal(head_num, dtype=np.float32)
     if keep_prob < 1.0 and drop_mask is None:
         drop_mask = draw_keep_mask([seed, 6], dropout_bits_total(lens_q, lens_kv, head_num), keep_prob)
+    pse_t = None
+    if pse is not None:
+        form, shared = pse
+        rows = {"full": int(lens_q.max()), "row": 1, "compressed": 1024}[form]
+        pse_t = _normal([seed, 9], (1 if shared else len(lens_q), head_num, rows, int(lens_kv.max())), dtype, 0.5)
     slopes = None
     if alibi:
         slopes = batch_alibi_slopes(seed, len(lens_q), head_num) if slopes_per_batch else alibi_slopes(head_num)
@@ -179,7 +189,7 @@ def make_case(name, lens_q, lens_kv=None, *, head_num, kv_heads, head_dim, dtype
                 kv_heads=kv_heads, head_dim=head_dim, scale=float(scale), q=q, k=k, v=v, dy=dy,
                 keep_prob=float(keep_prob), sparse_mode=sparse_mode, pre_tokens=int(pre_tokens),
                 next_tokens=int(next_tokens), drop_mask=drop_mask,
-                alibi_slopes=slopes, pse_type=int(pse_type), sink=sink_v,
+                alibi_slopes=slopes, pse_type=int(pse_type), pse=pse_t, sink=sink_v,
                 prefix=None if prefix is None else np.asarray(prefix, dtype=np.int64),
                 atten_mask=None if atten_mask is None else np.ascontiguousarray(atten_mask, dtype=np.uint8))
 
