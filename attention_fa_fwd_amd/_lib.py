@@ -67,6 +67,7 @@ class FaConfig(ctypes.Structure):
         ("pse_rows", ctypes.c_int64),
         ("pse_cols", ctypes.c_int64),
         ("pse_type", ctypes.c_int32),
+        ("strides", ctypes.POINTER(ctypes.c_int64)),
     ]
 
 
@@ -201,7 +202,7 @@ def _stream_handle(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _check_tensor(name, t, shape, dtype, device):
+def _check_tensor(name, t, shape, dtype, device, strided=False):
     if not isinstance(t, torch.Tensor):
         raise ValueError(f"{name} must be a torch.Tensor")
     if t.device != device:
@@ -210,8 +211,34 @@ def _check_tensor(name, t, shape, dtype, device):
         raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if tuple(t.shape) != tuple(shape):
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
-    if not t.is_contiguous():
+    if strided:
+        # TND tensors may be strided views: the D axis contiguous, rows 16-byte aligned
+        if t.stride(2) != 1 or any((st * t.element_size()) % 16 for st in t.stride()[:2]):
+            raise ValueError(f"{name} needs a contiguous last axis and 16-byte multiples as its other strides")
+    elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+
+
+_SLOTS = ("q", "k", "v", "dy", "out", "dq", "dk", "dv")
+
+
+def _set_strides(cfg: "Config", tensors: dict):
+    """Fills cfg's (token, head) strides of the TND tensors of this call; NULL when all are packed."""
+    if cfg.layout_name != "TND":
+        cfg.c.strides = None
+        return
+    vals, packed = [], True
+    for name in _SLOTS:
+        t = tensors.get(name)
+        n = cfg.c.head_num if name in ("q", "dy", "out", "dq") else (cfg.c.num_kv_heads or cfg.c.head_num)
+        st = (n * cfg.c.head_dim, cfg.c.head_dim) if t is None else (t.stride(0), t.stride(1))
+        packed = packed and st == (n * cfg.c.head_dim, cfg.c.head_dim)
+        vals += list(st)
+    if packed:
+        cfg.c.strides = None
+        return
+    cfg._strides = np.ascontiguousarray(np.asarray(vals, dtype=np.int64))
+    cfg.c.strides = cfg._strides.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
 
 
 def fa_fwd_workspace_size(cfg: Config) -> int:
@@ -248,9 +275,10 @@ def _common_checks(q, k, v, cfg: Config):
     nq, nkv, d = cfg.c.head_num, cfg.c.num_kv_heads or cfg.c.head_num, cfg.c.head_dim
     if cfg.layout_name not in _LAYOUTS:
         raise ValueError(f"unknown layout {cfg.layout_name}")
-    _check_tensor("q", q, layout_shape(cfg, True), q.dtype, dev)
-    _check_tensor("k", k, layout_shape(cfg, False), q.dtype, dev)
-    _check_tensor("v", v, layout_shape(cfg, False), q.dtype, dev)
+    tnd = cfg.layout_name == "TND"
+    _check_tensor("q", q, layout_shape(cfg, True), q.dtype, dev, tnd)
+    _check_tensor("k", k, layout_shape(cfg, False), q.dtype, dev, tnd)
+    _check_tensor("v", v, layout_shape(cfg, False), q.dtype, dev, tnd)
     return dev, tq, tkv, nq, nkv, d
 
 
@@ -267,17 +295,18 @@ def fa_fwd(cfg: Config, q, k, v, drop_mask=None, alibi_slopes=None, sink=None, o
     """Forward through libfa.so on the current stream; returns (out, softmax_max, softmax_sum)."""
     dev, tq, tkv, nq, nkv, d = _common_checks(q, k, v, cfg)
     if out is None:
-        out = torch.empty_like(q)
+        out = torch.empty(layout_shape(cfg, True), dtype=q.dtype, device=dev)
     if softmax_max is None:
         softmax_max = torch.empty((tq, nq), dtype=torch.float32, device=dev)
     if softmax_sum is None:
         softmax_sum = torch.empty((tq, nq), dtype=torch.float32, device=dev)
-    _check_tensor("out", out, layout_shape(cfg, True), q.dtype, dev)
+    _check_tensor("out", out, layout_shape(cfg, True), q.dtype, dev, cfg.layout_name == "TND")
     _check_tensor("softmax_max", softmax_max, (tq, nq), torch.float32, dev)
     _check_tensor("softmax_sum", softmax_sum, (tq, nq), torch.float32, dev)
     _check_slopes_sink(cfg, alibi_slopes, sink, nq, dev)
     if drop_mask is not None and (drop_mask.dtype != torch.uint8 or drop_mask.device != dev):
         raise ValueError("drop_mask must be a uint8 tensor on the same device")
+    _set_strides(cfg, dict(q=q, k=k, v=v, out=out))
     ws = _workspace(fa_fwd_workspace_size(cfg), dev, workspace)
     st = lib().fa_fwd(cfg.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(drop_mask), _ptr(alibi_slopes), _ptr(sink),
                       _ptr(out), _ptr(softmax_max), _ptr(softmax_sum), _ptr(ws),
@@ -290,22 +319,24 @@ def fa_bwd(cfg: Config, q, k, v, dy, out, softmax_max, softmax_sum, drop_mask=No
            dq=None, dk=None, dv=None, dsink=None, workspace=None):
     """Backward through libfa.so on the current stream; returns (dq, dk, dv, dsink or None)."""
     dev, tq, tkv, nq, nkv, d = _common_checks(q, k, v, cfg)
-    _check_tensor("dy", dy, layout_shape(cfg, True), q.dtype, dev)
-    _check_tensor("out", out, layout_shape(cfg, True), q.dtype, dev)
+    _check_tensor("dy", dy, layout_shape(cfg, True), q.dtype, dev, cfg.layout_name == "TND")
+    _check_tensor("out", out, layout_shape(cfg, True), q.dtype, dev, cfg.layout_name == "TND")
     _check_tensor("softmax_max", softmax_max, (tq, nq), torch.float32, dev)
     _check_tensor("softmax_sum", softmax_sum, (tq, nq), torch.float32, dev)
     _check_slopes_sink(cfg, alibi_slopes, sink, nq, dev)
     if dq is None:
-        dq = torch.empty_like(q)
+        dq = torch.empty(layout_shape(cfg, True), dtype=q.dtype, device=dev)
     if dk is None:
-        dk = torch.empty_like(k)
+        dk = torch.empty(layout_shape(cfg, False), dtype=q.dtype, device=dev)
     if dv is None:
-        dv = torch.empty_like(v)
+        dv = torch.empty(layout_shape(cfg, False), dtype=q.dtype, device=dev)
     if sink is not None and dsink is None:
         dsink = torch.empty((nq,), dtype=torch.float32, device=dev)
-    _check_tensor("dq", dq, layout_shape(cfg, True), q.dtype, dev)
-    _check_tensor("dk", dk, layout_shape(cfg, False), q.dtype, dev)
-    _check_tensor("dv", dv, layout_shape(cfg, False), q.dtype, dev)
+    tnd = cfg.layout_name == "TND"
+    _check_tensor("dq", dq, layout_shape(cfg, True), q.dtype, dev, tnd)
+    _check_tensor("dk", dk, layout_shape(cfg, False), q.dtype, dev, tnd)
+    _check_tensor("dv", dv, layout_shape(cfg, False), q.dtype, dev, tnd)
+    _set_strides(cfg, dict(q=q, k=k, v=v, dy=dy, out=out, dq=dq, dk=dk, dv=dv))
     ws = _workspace(fa_bwd_workspace_size(cfg), dev, workspace)
     st = lib().fa_bwd(cfg.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(dy), _ptr(out), _ptr(softmax_max),
                       _ptr(softmax_sum), _ptr(drop_mask), _ptr(alibi_slopes), _ptr(sink), _ptr(dq), _ptr(dk),

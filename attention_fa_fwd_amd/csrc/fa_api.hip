@@ -28,6 +28,10 @@ struct Problem {
   int64_t pre = 0, next = 0;
   bool deterministic = true;
   int layout = FA_LAYOUT_TND;      // fa_config.layout
+  // strided TND tensors, index T_Q .. T_DV: (token, head) element strides and whether they
+  // differ from the packed ones
+  int64_t ts[8] = {}, hs[8] = {};
+  bool strided[8] = {};
   const void* pse = nullptr;       // external pse (device) and its shape
   int64_t pse_batch = 0, pse_rows = 0, pse_cols = 0;
   int pse_type = 0, pse_mode = 0;  // mode: 0 row i, 1 single row, 2 1024-row compression
@@ -43,7 +47,17 @@ struct Problem {
 };
 
 static_assert(fa::kLayoutBNSD == FA_LAYOUT_BNSD && fa::kLayoutSBH == FA_LAYOUT_SBH, "layout codes");
-bool relayout(const Problem& pr) { return pr.layout == FA_LAYOUT_BNSD || pr.layout == FA_LAYOUT_SBH; }
+enum TensorId { T_Q = 0, T_K, T_V, T_DY, T_O, T_DQ, T_DK, T_DV };
+bool layout_copies(const Problem& pr) { return pr.layout == FA_LAYOUT_BNSD || pr.layout == FA_LAYOUT_SBH; }
+// tensor `id` goes through a packed TND copy in the workspace
+bool copied(const Problem& pr, int id) { return layout_copies(pr) || pr.strided[id]; }
+// any tensor does (the workspace then holds copies of all eight)
+bool relayout(const Problem& pr) {
+  if (layout_copies(pr)) return true;
+  for (bool st : pr.strided)
+    if (st) return true;
+  return false;
+}
 int64_t elem_bytes(const Problem& pr) { return pr.dtype == FA_DTYPE_FP32 ? 4 : 2; }
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
@@ -147,6 +161,21 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
     pr->pse_mode = pmode;
   }
   if (cfg->layout < FA_LAYOUT_TND || cfg->layout > FA_LAYOUT_SBH) return FA_ERR_PARAM_INVALID;
+  if (cfg->strides) {
+    if (cfg->layout != FA_LAYOUT_TND) return FA_ERR_PARAM_INVALID;
+    const int64_t eb = cfg->dtype == FA_DTYPE_FP32 ? 4 : 2;
+    for (int id = 0; id < 8; ++id) {
+      const int64_t n = (id == T_K || id == T_V || id == T_DK || id == T_DV) ? nkv : cfg->head_num;
+      const int64_t t = cfg->strides[2 * id], h = cfg->strides[2 * id + 1];
+      const bool output = id >= T_DQ || id == T_O;   // O is the forward's output
+      // 16-byte rows (the copies move 16-byte chunks); outputs need distinct rows
+      if (t < 0 || h < 0 || (t * eb) % 16 != 0 || (h * eb) % 16 != 0) return FA_ERR_PARAM_INVALID;
+      if (output && (t == 0 || (h == 0 && n > 1))) return FA_ERR_PARAM_INVALID;
+      pr->ts[id] = t;
+      pr->hs[id] = h;
+      pr->strided[id] = !(t == n * cfg->head_dim && h == cfg->head_dim);
+    }
+  }
   pr->layout = cfg->layout;
   if (pr->layout != FA_LAYOUT_TND) {
     // the fixed-length layouts hold B sequences of one length per side
@@ -375,13 +404,24 @@ void fill_pse(const Problem& pr, P& p) {
 }
 
 // One BNSD / SBH tensor of the query side (q = true: B sequences of Sq rows, Nq
-// heads) or the key side to or from its TND copy.
-hipError_t relayout_tensor(const Problem& pr, bool q_side, const void* src, void* dst, bool to_tnd,
-                           hipStream_t s) {
+// heads) or the key side, or one strided TND tensor (id), to or from its packed
+// TND copy.
+hipError_t relayout_tensor(const Problem& pr, int id, const void* src, void* dst, bool to_tnd, hipStream_t s) {
+  const bool q_side = !(id == T_K || id == T_V || id == T_DK || id == T_DV);
   return timed(K_RELAYOUT, s, [&] {
+    if (!layout_copies(pr))
+      return fa::launch_relayout(src, dst, 1, q_side ? pr.tq : pr.tkv, q_side ? pr.nq : pr.nkv, pr.d,
+                                 (int)elem_bytes(pr), fa::kLayoutStrided, to_tnd, s, pr.ts[id], pr.hs[id]);
     return fa::launch_relayout(src, dst, pr.batch, q_side ? pr.sq : pr.skv, q_side ? pr.nq : pr.nkv, pr.d,
                                (int)elem_bytes(pr), pr.layout, to_tnd, s);
   });
+}
+
+// Gathers the tensor into its workspace copy when it has one; returns the pointer the kernels read.
+const void* gather(const Problem& pr, int id, const void* src, char* copy, hipStream_t s, hipError_t* e) {
+  if (!copied(pr, id) || *e != hipSuccess) return copied(pr, id) ? copy : src;
+  *e = relayout_tensor(pr, id, src, copy, true, s);
+  return copy;
 }
 
 void fill_common_fwd(const Problem& pr, fa::FwdParams& p) {
@@ -574,11 +614,11 @@ fa_status fa_fwd(const fa_config* cfg, const void* q, const void* k, const void*
   fill_common_fwd(pr, p);
   p.q = q; p.k = k; p.v = v; p.o = out;
   if (relayout(pr)) {
-    if ((e = relayout_tensor(pr, true, q, ws + L.rq, true, s)) != hipSuccess ||
-        (e = relayout_tensor(pr, false, k, ws + L.rk, true, s)) != hipSuccess ||
-        (e = relayout_tensor(pr, false, v, ws + L.rv, true, s)) != hipSuccess)
-      return FA_ERR_HIP;
-    p.q = ws + L.rq; p.k = ws + L.rk; p.v = ws + L.rv; p.o = ws + L.ro;
+    p.q = gather(pr, T_Q, q, ws + L.rq, s, &e);
+    p.k = gather(pr, T_K, k, ws + L.rk, s, &e);
+    p.v = gather(pr, T_V, v, ws + L.rv, s, &e);
+    if (e != hipSuccess) return FA_ERR_HIP;
+    if (copied(pr, T_O)) p.o = ws + L.ro;
   }
   p.m_out = softmax_max; p.l_out = softmax_sum;
   p.drop = pr.keep < 1.0 ? drop_mask : nullptr;
@@ -602,7 +642,7 @@ fa_status fa_fwd(const fa_config* cfg, const void* q, const void* k, const void*
     if (e != hipSuccess) return FA_ERR_HIP;
   }
   e = timed(K_FWD, s, [&] { return fa::launch_fwd(pr.dtype, (int)pr.d, p, s); });
-  if (e == hipSuccess && relayout(pr)) e = relayout_tensor(pr, true, ws + L.ro, out, false, s);
+  if (e == hipSuccess && copied(pr, T_O)) e = relayout_tensor(pr, T_O, ws + L.ro, out, false, s);
   return hip_status(e);
 }
 
@@ -648,14 +688,15 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
   p.m_in = softmax_max; p.l_in = softmax_sum;
   p.dq = dq; p.dk = dk; p.dv = dv; p.dsink = sink ? dsink : nullptr;
   if (relayout(pr)) {
-    if ((e = relayout_tensor(pr, true, q, ws + L.rq, true, s)) != hipSuccess ||
-        (e = relayout_tensor(pr, false, k, ws + L.rk, true, s)) != hipSuccess ||
-        (e = relayout_tensor(pr, false, v, ws + L.rv, true, s)) != hipSuccess ||
-        (e = relayout_tensor(pr, true, dy, ws + L.rdy, true, s)) != hipSuccess ||
-        (e = relayout_tensor(pr, true, out, ws + L.ro, true, s)) != hipSuccess)
-      return FA_ERR_HIP;
-    p.q = ws + L.rq; p.k = ws + L.rk; p.v = ws + L.rv; p.dy = ws + L.rdy; p.o = ws + L.ro;
-    p.dq = ws + L.rdq; p.dk = ws + L.rdk; p.dv = ws + L.rdv;
+    p.q = gather(pr, T_Q, q, ws + L.rq, s, &e);
+    p.k = gather(pr, T_K, k, ws + L.rk, s, &e);
+    p.v = gather(pr, T_V, v, ws + L.rv, s, &e);
+    p.dy = gather(pr, T_DY, dy, ws + L.rdy, s, &e);
+    p.o = gather(pr, T_O, out, ws + L.ro, s, &e);
+    if (e != hipSuccess) return FA_ERR_HIP;
+    if (copied(pr, T_DQ)) p.dq = ws + L.rdq;
+    if (copied(pr, T_DK)) p.dk = ws + L.rdk;
+    if (copied(pr, T_DV)) p.dv = ws + L.rdv;
   }
   p.delta = reinterpret_cast<float*>(ws + L.delta);
   p.lse = reinterpret_cast<float*>(ws + L.lse);
@@ -708,11 +749,9 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
       e = timed(K_CONVERT, s, [&] { return fa::launch_bwd_dq_convert(dt, d, p, s); });
   }
   if (e == hipSuccess && sink) e = timed(K_DSINK, s, [&] { return fa::launch_bwd_dsink(p, s); });
-  if (e == hipSuccess && relayout(pr)) {
-    e = relayout_tensor(pr, true, ws + L.rdq, dq, false, s);
-    if (e == hipSuccess) e = relayout_tensor(pr, false, ws + L.rdk, dk, false, s);
-    if (e == hipSuccess) e = relayout_tensor(pr, false, ws + L.rdv, dv, false, s);
-  }
+  if (e == hipSuccess && copied(pr, T_DQ)) e = relayout_tensor(pr, T_DQ, ws + L.rdq, dq, false, s);
+  if (e == hipSuccess && copied(pr, T_DK)) e = relayout_tensor(pr, T_DK, ws + L.rdk, dk, false, s);
+  if (e == hipSuccess && copied(pr, T_DV)) e = relayout_tensor(pr, T_DV, ws + L.rdv, dv, false, s);
   return hip_status(e);
 }
 

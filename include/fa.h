@@ -149,6 +149,13 @@ typedef struct fa_config {
   int32_t pse_type;              /* with pse: 0 = mul then add, S = scale*QK^T + pse;
                                     1 = add then mul, S = scale*(QK^T + pse) (the grad page's
                                     formula; ScoreV2 pseType table)                           */
+  const int64_t* strides;        /* HOST, optional, TND only: 16 element strides, (token, head)
+                                    for q, k, v, dy, out, dq, dk, dv in that order; the D
+                                    axis stays contiguous.  Each stride times the element size
+                                    must be a multiple of 16 bytes; output rows must not
+                                    overlap.  Tensors whose strides differ from the packed
+                                    ones (N*D, D) are gathered into packed copies in the
+                                    workspace (outputs scattered back).  NULL = packed.       */
 } fa_config;
 
 /* Device workspace bytes needed by fa_fwd for this configuration (>= 256). */

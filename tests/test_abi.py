@@ -425,3 +425,30 @@ def test_external_pse_validation():
     # 16-bit inputs with an external pse are rejected for now
     assert size(cfg(dtype=fa.FA_DTYPE_BF16)) == fa.FA_ERR_PARAM_INVALID
     assert size(cfg(dtype=fa.FA_DTYPE_FP16)) == fa.FA_ERR_PARAM_INVALID
+
+
+def test_strides_validation():
+    n = ctypes.c_uint64(0)
+    uniform = dict(cu_seqlens_q=[0, 6, 12], cu_seqlens_kv=[0, 9, 18])
+
+    def with_strides(vals, **over):
+        c = _cfg(**{**uniform, **over})
+        c._arr = (ctypes.c_int64 * 16)(*vals)
+        c.c.strides = ctypes.cast(c._arr, ctypes.POINTER(ctypes.c_int64))
+        return c
+
+    packed = [4 * 128, 128, 2 * 128, 128, 2 * 128, 128, 4 * 128, 128, 4 * 128, 128, 4 * 128, 128,
+              2 * 128, 128, 2 * 128, 128]
+    base = ctypes.c_uint64(0)
+    assert fa.lib().fa_bwd_workspace_size(_cfg(**uniform).ref, ctypes.byref(base)) == 0
+    assert fa.lib().fa_bwd_workspace_size(with_strides(packed).ref, ctypes.byref(n)) == 0
+    assert n.value == base.value          # packed strides need no copies
+    wide = list(packed)
+    wide[0] = 4 * 136                     # q rows padded to 136 elements
+    assert fa.lib().fa_bwd_workspace_size(with_strides(wide).ref, ctypes.byref(n)) == 0
+    assert n.value > base.value
+    for bad_index, bad in ((0, 4 * 128 + 4), (1, 3), (10, 0), (2, -128)):
+        vals = list(packed)
+        vals[bad_index] = bad              # misaligned, output token stride 0, negative
+        assert _fwd(with_strides(vals)) == fa.FA_ERR_PARAM_INVALID, (bad_index, bad)
+    assert _fwd(with_strides(packed, layout="BSND")) == fa.FA_ERR_PARAM_INVALID

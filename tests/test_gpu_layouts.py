@@ -68,3 +68,45 @@ def test_layout_against_the_oracle():
     case = _case(torch.bfloat16, 32, sparse_mode=4, pre_tokens=64, next_tokens=16)
     say("layout SBH vs oracle")
     compare(_run(case, "SBH", deterministic=False), run_oracle(case), TOL[torch.bfloat16])
+
+
+def _views(x, kind):
+    """The same values as a strided TND view: padded D rows, every other head of a wider
+    tensor, or a head-major (transposed) storage."""
+    t, n, d = x.shape
+    if kind == "padded":
+        buf = torch.full((t, n, d + 8), float("nan"), dtype=x.dtype, device=x.device)
+        buf[:, :, :d] = x
+        return buf[:, :, :d]
+    if kind == "every_other_head":
+        buf = torch.full((t, 2 * n, d), float("nan"), dtype=x.dtype, device=x.device)
+        buf[:, ::2] = x
+        return buf[:, ::2]
+    return x.permute(1, 0, 2).contiguous().permute(1, 0, 2)   # head-major storage
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_strided_tnd_views_are_bitwise_the_packed_result(dtype):
+    case = wl.make_case("strided", [37, 200, 129], [90, 200, 64], head_num=4, kv_heads=2, head_dim=128,
+                        dtype=dtype, seed=33, sparse_mode=0, keep_prob=0.9, sink=True)
+    say(f"strided TND views dtype={dtype}")
+    dev = torch.device("cuda")
+    cfg = fa.Config(case.cu_seqlens_q, case.cu_seqlens_kv, case.head_num, case.kv_heads, case.head_dim, dtype,
+                    case.scale, case.keep_prob, case.sparse_mode, deterministic=True)
+    q, k, v, dy = (t.to(dev) for t in (case.q, case.k, case.v, case.dy))
+    drop = torch.from_numpy(case.drop_mask).to(dev)
+    sink = torch.from_numpy(case.sink).to(dev)
+    out, m, l = fa.fa_fwd(cfg, q, k, v, drop, None, sink)
+    ref = fa.fa_bwd(cfg, q, k, v, dy, out, m, l, drop, None, sink)
+    torch.cuda.synchronize()
+    # strided inputs and strided outputs (views into larger buffers)
+    qs, ks, vs, dys = _views(q, "padded"), _views(k, "every_other_head"), _views(v, "head_major"), _views(dy, "padded")
+    outs = _views(torch.zeros_like(q), "every_other_head")
+    outs, ms, ls = fa.fa_fwd(cfg, qs, ks, vs, drop, None, sink, out=outs)
+    dqs, dks, dvs = (_views(torch.zeros_like(t), kind) for t, kind in ((q, "head_major"), (k, "padded"),
+                                                                      (v, "every_other_head")))
+    got = fa.fa_bwd(cfg, qs, ks, vs, dys, outs, ms, ls, drop, None, sink, dq=dqs, dk=dks, dv=dvs)
+    torch.cuda.synchronize()
+    assert torch.equal(outs, out) and torch.equal(ms, m) and torch.equal(ls, l)
+    for a, b in zip(got, ref):
+        assert torch.equal(a, b)
