@@ -23,6 +23,7 @@ constexpr int64_t kMaxPrefixBatch = 1024;          // B limit with prefixOptiona
 
 struct Problem {
   int64_t batch = 0, nq = 0, nkv = 0, d = 0, tq = 0, tkv = 0;
+  int64_t du = 0;                  // the tensors' head dim; d is the kernels' (64 or 128, du <= d)
   int dtype = 0, mode = 0;
   double scale = 0, keep = 1;
   int64_t pre = 0, next = 0;
@@ -50,10 +51,10 @@ static_assert(fa::kLayoutBNSD == FA_LAYOUT_BNSD && fa::kLayoutSBH == FA_LAYOUT_S
 enum TensorId { T_Q = 0, T_K, T_V, T_DY, T_O, T_DQ, T_DK, T_DV };
 bool layout_copies(const Problem& pr) { return pr.layout == FA_LAYOUT_BNSD || pr.layout == FA_LAYOUT_SBH; }
 // tensor `id` goes through a packed TND copy in the workspace
-bool copied(const Problem& pr, int id) { return layout_copies(pr) || pr.strided[id]; }
+bool copied(const Problem& pr, int id) { return layout_copies(pr) || pr.strided[id] || pr.du != pr.d; }
 // any tensor does (the workspace then holds copies of all eight)
 bool relayout(const Problem& pr) {
-  if (layout_copies(pr)) return true;
+  if (layout_copies(pr) || pr.du != pr.d) return true;
   for (bool st : pr.strided)
     if (st) return true;
   return false;
@@ -68,9 +69,12 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   if (cfg->head_num < 1 || cfg->head_num > kMaxHeads) return FA_ERR_PARAM_INVALID;
   const int64_t nkv = cfg->num_kv_heads == 0 ? cfg->head_num : cfg->num_kv_heads;
   if (nkv < 1 || cfg->head_num % nkv != 0) return FA_ERR_PARAM_INVALID;
-  if (cfg->head_dim != 64 && cfg->head_dim != 128) return FA_ERR_PARAM_INVALID;
   if (cfg->dtype != FA_DTYPE_FP32 && cfg->dtype != FA_DTYPE_BF16 && cfg->dtype != FA_DTYPE_FP16)
     return FA_ERR_PARAM_INVALID;
+  // D <= 128 with rows of whole 16-byte chunks; the kernels run D = 64 and 128, other
+  // head dims go through copies zero-padded to the next of them
+  const int64_t ebytes = cfg->dtype == FA_DTYPE_FP32 ? 4 : 2;
+  if (cfg->head_dim < 1 || cfg->head_dim > 128 || (cfg->head_dim * ebytes) % 16 != 0) return FA_ERR_PARAM_INVALID;
   const int mode = cfg->sparse_mode;
   if (mode != FA_SPARSE_NONE && mode != FA_SPARSE_ALL_MASK && mode != FA_SPARSE_LEFT_UP_CAUSAL &&
       mode != FA_SPARSE_RIGHT_DOWN_CAUSAL && mode != FA_SPARSE_BAND && mode != FA_SPARSE_PREFIX)
@@ -87,7 +91,8 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   pr->batch = cfg->batch;
   pr->nq = cfg->head_num;
   pr->nkv = nkv;
-  pr->d = cfg->head_dim;
+  pr->du = cfg->head_dim;
+  pr->d = cfg->head_dim <= 64 ? 64 : 128;
   pr->dtype = cfg->dtype;
   pr->mode = mode;
   pr->pse_sqrt = (cfg->flags & FA_FLAG_PSE_SQRT) != 0;
@@ -99,7 +104,8 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   // The fp32-atomic dQ variant is built for bf16, fp16 and for fp32 with D = 64; fp32 with
   // D = 128 runs the deterministic passes, whose result is one of the results the
   // non-deterministic mode allows.
-  pr->deterministic = cfg->deterministic != 0 || (cfg->dtype == FA_DTYPE_FP32 && cfg->head_dim == 128);
+  // (the kernels' D: head dims above 64 run the D = 128 kernels)
+  pr->deterministic = cfg->deterministic != 0 || (cfg->dtype == FA_DTYPE_FP32 && cfg->head_dim > 64);
   const int64_t* cq = cfg->cu_seqlens_q;
   const int64_t* ck = cfg->cu_seqlens_kv;
   if (cq[0] != 0 || ck[0] != 0) return FA_ERR_PARAM_INVALID;
@@ -161,6 +167,11 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
     pr->pse_mode = pmode;
   }
   if (cfg->layout < FA_LAYOUT_TND || cfg->layout > FA_LAYOUT_SBH) return FA_ERR_PARAM_INVALID;
+  for (int id = 0; id < 8; ++id) {   // packed TND strides unless given
+    const int64_t n = (id == T_K || id == T_V || id == T_DK || id == T_DV) ? nkv : cfg->head_num;
+    pr->ts[id] = n * cfg->head_dim;
+    pr->hs[id] = cfg->head_dim;
+  }
   if (cfg->strides) {
     if (cfg->layout != FA_LAYOUT_TND) return FA_ERR_PARAM_INVALID;
     const int64_t eb = cfg->dtype == FA_DTYPE_FP32 ? 4 : 2;
@@ -410,9 +421,9 @@ hipError_t relayout_tensor(const Problem& pr, int id, const void* src, void* dst
   const bool q_side = !(id == T_K || id == T_V || id == T_DK || id == T_DV);
   return timed(K_RELAYOUT, s, [&] {
     if (!layout_copies(pr))
-      return fa::launch_relayout(src, dst, 1, q_side ? pr.tq : pr.tkv, q_side ? pr.nq : pr.nkv, pr.d,
+      return fa::launch_relayout(src, dst, 1, q_side ? pr.tq : pr.tkv, q_side ? pr.nq : pr.nkv, pr.du, pr.d,
                                  (int)elem_bytes(pr), fa::kLayoutStrided, to_tnd, s, pr.ts[id], pr.hs[id]);
-    return fa::launch_relayout(src, dst, pr.batch, q_side ? pr.sq : pr.skv, q_side ? pr.nq : pr.nkv, pr.d,
+    return fa::launch_relayout(src, dst, pr.batch, q_side ? pr.sq : pr.skv, q_side ? pr.nq : pr.nkv, pr.du, pr.d,
                                (int)elem_bytes(pr), pr.layout, to_tnd, s);
   });
 }

@@ -191,8 +191,8 @@ hipError_t launch_decode_reduce(int dtype, int d, const DecParams& p, hipStream_
 // layouts the relayout kernel converts to and from TND (values of FA_LAYOUT_BNSD / _SBH;
 // kLayoutStrided: a TND tensor with its own token / head strides, B = 1)
 constexpr int kLayoutBNSD = 3, kLayoutSBH = 4, kLayoutStrided = 100;
-hipError_t launch_relayout(const void* src, void* dst, int64_t B, int64_t S, int64_t N, int64_t D, int ebytes,
-                           int layout, bool to_tnd, hipStream_t s, int64_t ts = 0, int64_t hs = 0);
+hipError_t launch_relayout(const void* src, void* dst, int64_t B, int64_t S, int64_t N, int64_t D, int64_t DK,
+                           int ebytes, int layout, bool to_tnd, hipStream_t s, int64_t ts = 0, int64_t hs = 0);
 hipError_t launch_mask_pack(const uint8_t* mask, int64_t rows, int64_t cols, uint32_t* bits, hipStream_t s);
 
 }  // namespace fa

@@ -1,6 +1,6 @@
 // Layout adapters for the fixed-length layouts of aclnnFlashAttentionScoreV2
-// ("inputLayout": BSH, SBH, BSND, BNSD) and for strided (non-contiguous) TND
-// tensors.  The attention kernels read and write
+// ("inputLayout": BSH, SBH, BSND, BNSD), for strided (non-contiguous) TND
+// tensors, and for head dims the kernels do not have (zero-padded to 64 or 128).  The attention kernels read and write
 // the packed TND layout; BSH and BSND batches with one common length are
 // already TND in memory, while BNSD and SBH tensors are gathered into TND
 // buffers in the workspace before the kernels and the kernels' outputs are
@@ -21,33 +21,41 @@ __device__ __forceinline__ int64_t layout_row(int layout, int64_t b, int64_t s, 
 }
 
 // TND index t = b*S + s; each thread moves one 16-byte chunk of one (t, n) row.
+// The TND copy has rows of DK elements, the tensor rows of D <= DK: gathering
+// fills columns D .. DK-1 with zeros, scattering moves the first D only.
 __global__ __launch_bounds__(256) void fa_relayout_kernel(const char* src, char* dst, int64_t B, int64_t S,
-                                                          int64_t N, int64_t D, int ebytes, int layout,
+                                                          int64_t N, int64_t D, int64_t DK, int ebytes, int layout,
                                                           int to_tnd, int64_t ts, int64_t hs) {
-  const int64_t cpr = D * ebytes / 16;   // chunks per (t, n) row
+  const int64_t cpr = DK * ebytes / 16;   // chunks per (t, n) row of the TND copy
+  const int64_t cdata = D * ebytes / 16;  // of them holding the tensor's columns
   const int64_t total = B * S * N * cpr;
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < total; i += (int64_t)gridDim.x * 256) {
     const int64_t c = i % cpr;
     const int64_t row = i / cpr;         // (t, n) in TND order
+    const int64_t tnd = row * DK * ebytes + 16 * c;
+    if (c >= cdata) {
+      if (to_tnd) *reinterpret_cast<u32x4*>(dst + tnd) = u32x4{0u, 0u, 0u, 0u};
+      continue;
+    }
     const int64_t n = row % N, t = row / N;
     const int64_t b = t / S, s = t - b * S;
-    const int64_t tnd = row * D * ebytes + 16 * c;
     const int64_t lay = layout_row(layout, b, s, n, B, S, N, D, ts, hs) * ebytes + 16 * c;
     const int64_t so = to_tnd ? lay : tnd, dof = to_tnd ? tnd : lay;
     *reinterpret_cast<u32x4*>(dst + dof) = *reinterpret_cast<const u32x4*>(src + so);
   }
 }
 
-hipError_t launch_relayout(const void* src, void* dst, int64_t B, int64_t S, int64_t N, int64_t D, int ebytes,
-                           int layout, bool to_tnd, hipStream_t s, int64_t ts, int64_t hs) {
+hipError_t launch_relayout(const void* src, void* dst, int64_t B, int64_t S, int64_t N, int64_t D, int64_t DK,
+                           int ebytes, int layout, bool to_tnd, hipStream_t s, int64_t ts, int64_t hs) {
+  if (D > DK || (D * ebytes) % 16 != 0 || (DK * ebytes) % 16 != 0) return hipErrorInvalidValue;
   if (layout != kLayoutBNSD && layout != kLayoutSBH && layout != kLayoutStrided) return hipErrorInvalidValue;
   if (layout == kLayoutStrided && B != 1) return hipErrorInvalidValue;
-  const int64_t chunks = B * S * N * (D * ebytes / 16);
+  const int64_t chunks = B * S * N * (DK * ebytes / 16);
   if (chunks == 0) return hipSuccess;
   const int64_t need = (chunks + 255) / 256;
   const int64_t blocks = need < 65536 ? need : 65536;
   hipLaunchKernelGGL(fa_relayout_kernel, dim3((unsigned)blocks), dim3(256), 0, s, reinterpret_cast<const char*>(src),
-                     reinterpret_cast<char*>(dst), B, S, N, D, ebytes, layout, to_tnd ? 1 : 0, ts, hs);
+                     reinterpret_cast<char*>(dst), B, S, N, D, DK, ebytes, layout, to_tnd ? 1 : 0, ts, hs);
   return hipGetLastError();
 }
 

@@ -63,7 +63,8 @@ def _bwd(cfg, **ptr):
 
 
 INVALID_CONFIGS = {
-    "head_dim_96": dict(head_dim=96),
+    "head_dim_100": dict(head_dim=100),      # bf16 rows of 200 bytes: not whole 16-byte chunks
+    "head_dim_136": dict(head_dim=136),
     "gqa_not_divisible": dict(head_num=4, kv_heads=3),
     "too_many_heads": dict(head_num=512, kv_heads=512),
     "keep_zero": dict(keep_prob=0.0),
@@ -452,3 +453,17 @@ def test_strides_validation():
         vals[bad_index] = bad              # misaligned, output token stride 0, negative
         assert _fwd(with_strides(vals)) == fa.FA_ERR_PARAM_INVALID, (bad_index, bad)
     assert _fwd(with_strides(packed, layout="BSND")) == fa.FA_ERR_PARAM_INVALID
+
+
+def test_padded_head_dims_accepted():
+    # D <= 128 with 16-byte rows: 64 and 128 run natively, the others through zero-padded copies
+    n = ctypes.c_uint64(0)
+    sizes = {}
+    for d in (8, 32, 64, 80, 96, 120, 128):
+        assert fa.lib().fa_bwd_workspace_size(_cfg(head_dim=d).ref, ctypes.byref(n)) == fa.FA_OK, d
+        sizes[d] = n.value
+    assert sizes[96] > sizes[128] and sizes[32] > sizes[64]   # the padded copies live in the workspace
+    for d, dt in ((36, fa.FA_DTYPE_FP32), (12, fa.FA_DTYPE_FP32)):
+        assert fa.lib().fa_fwd_workspace_size(_cfg(head_dim=d, dtype=dt).ref, ctypes.byref(n)) == fa.FA_OK, d
+    for d, dt in ((36, fa.FA_DTYPE_BF16), (6, fa.FA_DTYPE_FP32), (0, fa.FA_DTYPE_BF16)):
+        assert fa.lib().fa_fwd_workspace_size(_cfg(head_dim=d, dtype=dt).ref, ctypes.byref(n)) == fa.FA_ERR_PARAM_INVALID, d

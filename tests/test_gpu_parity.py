@@ -56,6 +56,12 @@ EDGE_CASES = {
                                     pre_tokens=40, next_tokens=0, alibi=True, slopes_per_batch=True),
     "cross_nomask_d128": dict(lens_q=[200, 77, 129], lens_kv=[130, 300, 129], head_num=4, kv_heads=2,
                               head_dim=128, sparse_mode=0),
+    # head dims the kernels pad (to 128 and to 64)
+    "d96_causal_drop_sink": dict(lens_q=[150, 67, 300], head_num=4, kv_heads=2, head_dim=96, sparse_mode=3,
+                                 keep_prob=0.85, sink=True),
+    "d32_band_alibi": dict(lens_q=[200, 129], head_num=2, kv_heads=1, head_dim=32, sparse_mode=4, pre_tokens=40,
+                           next_tokens=5, alibi=True),
+    "d80_cross": dict(lens_q=[90, 200], lens_kv=[300, 65], head_num=2, kv_heads=2, head_dim=80, sparse_mode=0),
     # external pse (pseType 1: before scaling, 0: after): full block, one shared row, 1024-row compression
     "pse_full_type1_cross": dict(lens_q=[200, 77, 129], lens_kv=[130, 300, 129], head_num=4, kv_heads=2,
                                  head_dim=128, sparse_mode=0, pse=("full", False), pse_type=1),
