@@ -93,7 +93,7 @@ typedef struct fa_config {
   const int64_t* cu_seqlens_kv;  /* HOST, B+1 entries, same rules, [B] = T_kv               */
   int64_t head_num;              /* Nq in [1, 256] (headNum)                                  */
   int64_t num_kv_heads;          /* Nkv; 0 means Nkv = Nq; Nq % Nkv == 0 (GQA)                */
-  int64_t head_dim;              /* D <= 128, D * element size a multiple of 16 bytes (64, 128 
+  int64_t head_dim;              /* D <= 128, D * element size a multiple of 16 bytes (64, 128
                                     native; others zero-padded to 64 or 128 in the workspace) */
   int32_t dtype;                 /* FA_DTYPE_*                                                */
   int32_t sparse_mode;           /* FA_SPARSE_*                                               */
