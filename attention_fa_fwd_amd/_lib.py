@@ -29,6 +29,7 @@ FA_DTYPE_BF16 = 1
 FA_DTYPE_FP16 = 2
 FA_FLAG_PSE_SQRT = 1
 FA_FLAG_SLOPES_PER_BATCH = 2
+FA_FLAG_ATOMIC_DQ = 4
 TOKENS_DEFAULT = 2147483647
 FA_LAYOUT_TND = 0
 FA_LAYOUT_BSH = 1
@@ -137,7 +138,8 @@ class Config:
 
     def __init__(self, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, head_dim, dtype, scale, keep_prob=1.0,
                  sparse_mode=0, pre_tokens=TOKENS_DEFAULT, next_tokens=TOKENS_DEFAULT, deterministic=True,
-                 prefix=None, atten_mask=None, pse_type=2, slopes_per_batch=False, layout="TND", pse=None):
+                 prefix=None, atten_mask=None, pse_type=2, slopes_per_batch=False, layout="TND", pse=None,
+                 atomic_dq=False):
         self.cu_q = np.ascontiguousarray(np.asarray(cu_seqlens_q, dtype=np.int64))
         self.cu_kv = np.ascontiguousarray(np.asarray(cu_seqlens_kv, dtype=np.int64))
         # per-sequence prefix N of sparse mode 6 (prefixOptional); NULL when None
@@ -160,8 +162,9 @@ class Config:
         # inputLayout of Q, K, V, dY, O and the gradients; the fixed-length layouts take
         # cu_seqlens with one common length per side
         self.layout_name = layout
+        # atomic_dq: with deterministic=False, the fp32-atomic dQ scheme instead of the (faster) separate pass
         flags = ((FA_FLAG_PSE_SQRT if pse_type == 3 and pse is None else 0)
-                 | (FA_FLAG_SLOPES_PER_BATCH if slopes_per_batch else 0))
+                 | (FA_FLAG_SLOPES_PER_BATCH if slopes_per_batch else 0) | (FA_FLAG_ATOMIC_DQ if atomic_dq else 0))
         if isinstance(dtype, torch.dtype):
             dtype = {torch.float32: FA_DTYPE_FP32, torch.bfloat16: FA_DTYPE_BF16,
                      torch.float16: FA_DTYPE_FP16}.get(dtype, -1)

@@ -86,7 +86,8 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   if (!std::isfinite(cfg->scale)) return FA_ERR_PARAM_INVALID;
   if (mode == FA_SPARSE_BAND && cfg->pre_tokens + cfg->next_tokens < 0) return FA_ERR_PARAM_INVALID;
   if (cfg->deterministic != 0 && cfg->deterministic != 1) return FA_ERR_PARAM_INVALID;
-  if ((cfg->flags & ~(FA_FLAG_PSE_SQRT | FA_FLAG_SLOPES_PER_BATCH)) != 0) return FA_ERR_PARAM_INVALID;
+  if ((cfg->flags & ~(FA_FLAG_PSE_SQRT | FA_FLAG_SLOPES_PER_BATCH | FA_FLAG_ATOMIC_DQ)) != 0)
+    return FA_ERR_PARAM_INVALID;
 
   pr->batch = cfg->batch;
   pr->nq = cfg->head_num;
@@ -101,11 +102,12 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   pr->keep = cfg->keep_prob;
   pr->pre = cfg->pre_tokens;
   pr->next = cfg->next_tokens;
-  // The fp32-atomic dQ variant is built for bf16, fp16 and for fp32 with D = 64; fp32 with
-  // D = 128 runs the deterministic passes, whose result is one of the results the
-  // non-deterministic mode allows.
-  // (the kernels' D: head dims above 64 run the D = 128 kernels)
-  pr->deterministic = cfg->deterministic != 0 || (cfg->dtype == FA_DTYPE_FP32 && cfg->head_dim > 64);
+  // The non-deterministic mode allows the deterministic passes' result, and they are the
+  // faster scheme here, so they run unless FA_FLAG_ATOMIC_DQ asks for atomic dQ.  That
+  // variant is built for bf16, fp16 and for fp32 with D = 64 (head dims above 64 run the
+  // D = 128 kernels).
+  pr->deterministic = cfg->deterministic != 0 || (cfg->flags & FA_FLAG_ATOMIC_DQ) == 0 ||
+                      (cfg->dtype == FA_DTYPE_FP32 && cfg->head_dim > 64);
   const int64_t* cq = cfg->cu_seqlens_q;
   const int64_t* ck = cfg->cu_seqlens_kv;
   if (cq[0] != 0 || ck[0] != 0) return FA_ERR_PARAM_INVALID;

@@ -257,7 +257,7 @@ def main():
     deterministic = not args.atomic_dq
     cfg = fa.Config(case.cu_seqlens_q, case.cu_seqlens_kv, case.head_num, case.kv_heads, case.head_dim,
                     case.dtype, case.scale, case.keep_prob, case.sparse_mode, case.pre_tokens, case.next_tokens,
-                    deterministic, layout=args.layout)
+                    deterministic, layout=args.layout, atomic_dq=args.atomic_dq)
     q, k, v, dy = (t.to(dev) for t in (case.q, case.k, case.v, case.dy))
     if args.layout != "TND":
         # the same values in the fixed-length layout (workloads with one common length)

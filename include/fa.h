@@ -86,6 +86,8 @@ typedef int32_t fa_status;
                                         this bit pseType 2: pse = -slope * (i - j)      */
 #define FA_FLAG_SLOPES_PER_BATCH 2u  /* alibi_slopes is [B, Nq] (one row per sequence)
                                         instead of [Nq]                                 */
+#define FA_FLAG_ATOMIC_DQ 4u         /* with deterministic = 0: accumulate dQ with fp32
+                                        atomics inside the dK/dV pass                  */
 
 typedef struct fa_config {
   int64_t batch;                 /* B >= 1 sequences                                          */
@@ -101,10 +103,12 @@ typedef struct fa_config {
   double keep_prob;              /* keepProb in (0, 1]; < 1 needs drop_mask                   */
   int64_t pre_tokens;            /* band only: keys allowed left of the diagonal              */
   int64_t next_tokens;           /* band only: keys allowed right of the diagonal             */
-  int32_t deterministic;         /* bwd: 1 = separate dQ pass (bitwise reproducible),
-                                    0 = fp32 atomic dQ accumulation where available (fp32
-                                    with D = 128, and bf16 with D = 128 and alibi, always
-                                    take the deterministic passes)                            */
+  int32_t deterministic;         /* bwd: 1 = separate dQ pass (bitwise reproducible); 0 = the
+                                    pages' non-deterministic mode, which allows any result of
+                                    either scheme: it runs the same passes (faster here than
+                                    atomic accumulation), or, with FA_FLAG_ATOMIC_DQ, fp32
+                                    atomic dQ in the dK/dV pass where that variant exists
+                                    (not fp32 with D > 64, nor 16-bit D = 128 with a pse)   */
   int32_t flags;                 /* FA_FLAG_* bits; any other bit -> FA_ERR_PARAM_INVALID     */
   const int64_t* prefix;         /* HOST, B entries, read in FA_SPARSE_PREFIX only (ignored
                                     otherwise): N_b of the prefix-compressed mask

@@ -24,11 +24,13 @@ def say(msg: str):
 
 
 def config_of(case: wl.Case, deterministic: bool = True, mask=None, pse=None) -> fa.Config:
-    """mask, pse: the case's attenMask and external pse as device tensors (required when the case has them)."""
+    """mask, pse: the case's attenMask and external pse as device tensors (required when the case has them).
+    deterministic=False selects the fp32-atomic dQ scheme, so the tests cover both backward variants."""
     return fa.Config(case.cu_seqlens_q, case.cu_seqlens_kv, case.head_num, case.kv_heads, case.head_dim,
                      case.dtype, case.scale, case.keep_prob, case.sparse_mode, case.pre_tokens,
                      case.next_tokens, deterministic, prefix=case.prefix, atten_mask=mask, pse_type=case.pse_type,
-                     slopes_per_batch=case.alibi_slopes is not None and case.alibi_slopes.ndim == 2, pse=pse)
+                     slopes_per_batch=case.alibi_slopes is not None and case.alibi_slopes.ndim == 2, pse=pse,
+                     atomic_dq=not deterministic)
 
 
 def device_inputs(case: wl.Case, device="cuda"):

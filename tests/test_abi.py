@@ -104,7 +104,7 @@ def test_element_types_accepted():
 
 
 def test_bad_flags_and_batch_limits():
-    for bad in (4, 1 << 30, -1):
+    for bad in (8, 1 << 30, -1):
         cfg = _cfg()
         cfg.c.flags = bad
         assert _fwd(cfg) == fa.FA_ERR_PARAM_INVALID, bad
@@ -200,12 +200,15 @@ def test_alignment_alibi_and_workspace_rules():
     assert _fwd(_cfg(cu_seqlens_q=[0, 0, 12], cu_seqlens_kv=[0, 0, 12]), slopes=FAKE) == fa.FA_ERR_PARAM_INVALID
     assert _fwd(_cfg(), ws_bytes=16) == fa.FA_ERR_WORKSPACE
     assert _bwd(_cfg(), ws_bytes=16) == fa.FA_ERR_WORKSPACE
-    assert _bwd(_cfg(deterministic=False), ws_bytes=fa.fa_bwd_workspace_size(_cfg())) == fa.FA_ERR_WORKSPACE
+    # the fp32-atomic dQ scheme needs its accumulator on top of the deterministic workspace
+    assert _bwd(_cfg(deterministic=False, atomic_dq=True),
+                ws_bytes=fa.fa_bwd_workspace_size(_cfg())) == fa.FA_ERR_WORKSPACE
+    assert fa.fa_bwd_workspace_size(_cfg(deterministic=False)) == fa.fa_bwd_workspace_size(_cfg())
 
 
 def test_atomic_variant_needs_a_larger_workspace():
     det = fa.fa_bwd_workspace_size(_cfg(deterministic=True))
-    atom = fa.fa_bwd_workspace_size(_cfg(deterministic=False))
+    atom = fa.fa_bwd_workspace_size(_cfg(deterministic=False, atomic_dq=True))
     assert atom >= det + 4 * 12 * 4 * 128
 
 

@@ -38,7 +38,7 @@ def _run(case, layout, deterministic=True):
     dev = torch.device("cuda")
     cfg = fa.Config(case.cu_seqlens_q, case.cu_seqlens_kv, case.head_num, case.kv_heads, case.head_dim, case.dtype,
                     case.scale, case.keep_prob, case.sparse_mode, case.pre_tokens, case.next_tokens, deterministic,
-                    layout=layout)
+                    layout=layout, atomic_dq=not deterministic)
     q = to_layout(case.q, layout, B, SQ).to(dev)
     k = to_layout(case.k, layout, B, SKV).to(dev)
     v = to_layout(case.v, layout, B, SKV).to(dev)
