@@ -110,3 +110,26 @@ def test_strided_tnd_views_are_bitwise_the_packed_result(dtype):
     assert torch.equal(outs, out) and torch.equal(ms, m) and torch.equal(ls, l)
     for a, b in zip(got, ref):
         assert torch.equal(a, b)
+
+
+def test_autograd_binding_matches_the_direct_calls():
+    from attention_fa_fwd_amd.autograd import varlen_attention
+    case = wl.make_case("autograd", [37, 200], head_num=4, kv_heads=2, head_dim=128, dtype=torch.bfloat16,
+                        seed=34, sparse_mode=3, keep_prob=0.9, sink=True, alibi=True)
+    say("autograd binding")
+    dev = torch.device("cuda")
+    cfg = fa.Config(case.cu_seqlens_q, case.cu_seqlens_kv, case.head_num, case.kv_heads, case.head_dim,
+                    case.dtype, case.scale, case.keep_prob, case.sparse_mode, deterministic=True)
+    q, k, v, dy = (t.to(dev) for t in (case.q, case.k, case.v, case.dy))
+    drop = torch.from_numpy(case.drop_mask).to(dev)
+    slopes = torch.from_numpy(case.alibi_slopes).to(dev)
+    sink = torch.from_numpy(case.sink).to(dev)
+    out, m, l = fa.fa_fwd(cfg, q, k, v, drop, slopes, sink)
+    ref = fa.fa_bwd(cfg, q, k, v, dy, out, m, l, drop, slopes, sink)
+    qg, kg, vg, sg = (t.clone().requires_grad_(True) for t in (q, k, v, sink))
+    o2 = varlen_attention(qg, kg, vg, cfg, sink=sg, alibi_slopes=slopes, drop_mask=drop)
+    o2.backward(dy)
+    torch.cuda.synchronize()
+    assert torch.equal(o2.detach(), out)
+    for got, want in ((qg.grad, ref[0]), (kg.grad, ref[1]), (vg.grad, ref[2]), (sg.grad, ref[3])):
+        assert torch.equal(got, want)
