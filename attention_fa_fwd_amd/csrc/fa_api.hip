@@ -4,6 +4,8 @@
 
 #include <algorithm>
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <vector>
@@ -405,6 +407,25 @@ hipError_t timed(KernelId id, hipStream_t s, F&& launch) {
 
 fa_status hip_status(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// FA_LOG=1 in the environment prints one line per call describing the plan (stderr).
+bool log_on() {
+  static const bool on = [] {
+    const char* v = std::getenv("FA_LOG");
+    return v && v[0] == '1';
+  }();
+  return on;
+}
+
+void log_plan(const char* what, const Problem& pr, int64_t n0, int64_t n1) {
+  if (!log_on()) return;
+  std::fprintf(stderr,
+               "[fa] %s: B=%lld Tq=%lld Tkv=%lld Nq=%lld Nkv=%lld D=%lld (kernel D=%lld) dtype=%d mode=%d "
+               "keep=%.3f layout=%d det=%d items=%lld/%lld\n",
+               what, (long long)pr.batch, (long long)pr.tq, (long long)pr.tkv, (long long)pr.nq, (long long)pr.nkv,
+               (long long)pr.du, (long long)pr.d, pr.dtype, pr.mode, pr.keep, pr.layout, pr.deterministic ? 1 : 0,
+               (long long)n0, (long long)n1);
+}
+
 template <typename P>
 void fill_pse(const Problem& pr, P& p) {
   p.pse = pr.pse;
@@ -616,6 +637,7 @@ fa_status fa_fwd(const fa_config* cfg, const void* q, const void* k, const void*
   if (workspace_bytes < bound.total) return FA_ERR_WORKSPACE;
 
   std::vector<WorkItem> items = schedule(pr, 0, nullptr, nullptr);
+  log_plan("fa_fwd", pr, (int64_t)items.size(), 0);
   const Layout L = layout_fwd(pr, (int64_t)items.size());
   std::vector<char> host = stage_block(pr, L, items, nullptr);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -689,6 +711,7 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
   if (pr.mask) pr.deterministic = true;
   std::vector<WorkItem> kv_items = schedule(pr, 1, nullptr, nullptr);
   std::vector<WorkItem> dq_items = schedule(pr, 2, nullptr, nullptr);
+  log_plan("fa_bwd", pr, (int64_t)kv_items.size(), (int64_t)dq_items.size());
   const Layout L = layout_bwd(pr, (int64_t)kv_items.size(), (int64_t)dq_items.size());
   std::vector<char> host = stage_block(pr, L, kv_items, &dq_items);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
@@ -840,6 +863,10 @@ fa_status fa_decode(const fa_decode_config* cfg, const void* q, const void* k, c
   p.batch = (int32_t)pr.batch;
   p.scale_log2 = (float)(pr.scale * 1.4426950408889634);
   const int n_items = (int)P.items.size();
+  if (log_on())
+    std::fprintf(stderr, "[fa] fa_decode: B=%lld S=%lld Nq=%lld Nkv=%lld D=%lld layout=%d chunk=%lld items=%d "
+                 "split slots=%lld\n", (long long)pr.batch, (long long)pr.s, (long long)pr.nq, (long long)pr.nkv,
+                 (long long)pr.d, pr.layout, (long long)P.chunk, n_items, (long long)P.n_slots);
   hipError_t e = timed(K_DEC, s, [&] { return fa::launch_decode(pr.dtype, (int)pr.d, n_items, p, s); });
   if (e == hipSuccess && P.n_slots > 0)
     e = timed(K_DEC_REDUCE, s, [&] { return fa::launch_decode_reduce(pr.dtype, (int)pr.d, p, s); });
