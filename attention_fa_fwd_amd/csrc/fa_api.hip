@@ -487,9 +487,9 @@ std::vector<char> stage_block(const Problem& pr, const Layout& L, const std::vec
 constexpr int64_t kMaxDecBatch = 65536;            // B limit of the decode page ("B <= 65536")
 constexpr int64_t kMaxDecSeq = 1 << 24;            // padded cache length limit (keys index in int32)
 constexpr int64_t kMaxDecGroup = 64;               // numHeads / numKeyValueHeads <= 64
-constexpr int64_t kDecTargetItems = 2048;          // split the keys until about this many work items remain
-constexpr int64_t kDecMinChunk = 32 * fa::kDecWaves;          // keys per work item: whole 32-key steps
-constexpr int64_t kDecMaxChunk = 8192;                         //   for every wave
+constexpr int64_t kDecMinChunk = 32 * fa::kDecWaves * 8;      // keys per work item: whole 32-key steps for
+                                                               //   every wave, at least 256 per wave
+constexpr int64_t kDecSlots = 256;                             // work items the chip runs at once (one per CU)
 
 struct DecProblem {
   int64_t batch = 0, s = 0, nq = 0, nkv = 0, d = 0;
@@ -532,8 +532,12 @@ fa_status parse_decode(const fa_decode_config* cfg, DecProblem* pr) {
 }
 
 // Work split: every (sequence, kv head) gets ceil(L_b / chunk) items (at least one,
-// so empty sequences still write zeros); the chunk doubles from 128 keys until at
-// most about kDecTargetItems items remain, so short batches still fill the chip.
+// so empty sequences still write zeros).  An item costs a pipeline fill of a few
+// microseconds on top of its keys, and one item's block takes a CU's LDS, so fewer,
+// longer items win while the chip stays busy: the chunk doubles from 768 keys until
+// the items number at most one per CU or two per (sequence, kv head), whichever is
+// more.  Items stay in (sequence, kv head, chunk) order: neighbouring blocks then
+// read neighbouring cache rows.
 struct DecPlan {
   int64_t chunk = kDecMinChunk;
   std::vector<fa::DecItem> items;
@@ -545,9 +549,15 @@ struct DecPlan {
 
 DecPlan plan_decode(const DecProblem& pr) {
   DecPlan P;
-  int64_t keys = 0;
-  for (int32_t L : pr.lens) keys += std::max<int64_t>(L, 1);
-  while (P.chunk < kDecMaxChunk && keys * pr.nkv > kDecTargetItems * P.chunk) P.chunk *= 2;
+  int64_t longest = 1;
+  for (int32_t L : pr.lens) longest = std::max<int64_t>(longest, L);
+  const int64_t limit = std::max<int64_t>(kDecSlots, 2 * pr.batch * pr.nkv);
+  auto n_items = [&](int64_t chunk) {
+    int64_t n = 0;
+    for (int32_t L : pr.lens) n += std::max<int64_t>(1, (L + chunk - 1) / chunk);
+    return n * pr.nkv;
+  };
+  while (P.chunk < longest && n_items(P.chunk) > limit) P.chunk *= 2;
   P.first_slot.assign((size_t)(pr.batch * pr.nkv), -1);
   P.n_split.assign((size_t)pr.batch, 1);
   for (int64_t b = 0; b < pr.batch; ++b) {

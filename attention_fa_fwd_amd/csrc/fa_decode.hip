@@ -244,23 +244,58 @@ __global__ __launch_bounds__(64 * kDecWaves, 1) void fa_decode_kernel(DecParams 
 }
 
 // One workgroup of D threads per (sequence, query head) of a split sequence:
-// O = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c over its items, in item order.
+// O = sum_c 2^(m_c - m) O_c / sum_c 2^(m_c - m) l_c over its items.  The threads
+// share the items for the maximum and the weighted sum of l (fixed-order tree
+// sums, so the result is reproducible); then thread d accumulates column d over
+// the items in item order, D items' weights at a time staged in LDS, with the
+// loads of several items in flight.
+template <int D>
+__device__ __forceinline__ float block_tree(float* red, float v, bool is_max) {
+  const int d = threadIdx.x;
+  red[d] = v;
+  __syncthreads();
+#pragma unroll
+  for (int s = D / 2; s > 0; s >>= 1) {
+    if (d < s) red[d] = is_max ? fmaxf(red[d], red[d + s]) : red[d] + red[d + s];
+    __syncthreads();
+  }
+  const float r = red[0];
+  __syncthreads();
+  return r;
+}
+
 template <typename E, int D>
 __global__ __launch_bounds__(D) void fa_decode_reduce_kernel(DecParams p) {
+  __shared__ float red[D];
+  __shared__ float wts[D];
   const int b = blockIdx.x / p.nq, h = blockIdx.x - b * p.nq;
   const int g = h / p.group, n = h - g * p.group;
   const int first = p.first_slot[b * p.nkv + g];
-  if (first < 0) return;   // written by its only item
+  if (first < 0) return;   // written by its only item (uniform over the workgroup)
   const int cnt = p.n_split[b];
   const int d = threadIdx.x;
+  const int64_t row0 = (int64_t)first * p.group + n;   // partial row of item c: row0 + c * group
   float mx = kNegInf;
-  for (int c = 0; c < cnt; ++c) mx = fmaxf(mx, p.part_m[(int64_t)(first + c) * p.group + n]);
-  float L = 0.f, O = 0.f;
-  for (int c = 0; c < cnt; ++c) {
-    const int64_t row = (int64_t)(first + c) * p.group + n;
-    const float f = mx == kNegInf ? 0.f : fast_exp2(p.part_m[row] - mx);
-    L += p.part_l[row] * f;
-    O += p.part_o[row * D + d] * f;
+  for (int c = d; c < cnt; c += D) mx = fmaxf(mx, p.part_m[row0 + (int64_t)c * p.group]);
+  mx = block_tree<D>(red, mx, true);
+  float ls = 0.f;
+  if (mx != kNegInf)
+    for (int c = d; c < cnt; c += D) {
+      const int64_t row = row0 + (int64_t)c * p.group;
+      ls += p.part_l[row] * fast_exp2(p.part_m[row] - mx);
+    }
+  const float L = block_tree<D>(red, ls, false);
+  float O = 0.f;
+  for (int c0 = 0; c0 < cnt; c0 += D) {
+    const int c = c0 + d;
+    wts[d] = (c < cnt && mx != kNegInf) ? fast_exp2(p.part_m[row0 + (int64_t)c * p.group] - mx) : 0.f;
+    __syncthreads();
+    const int nc = min(D, cnt - c0);
+    const float* po = p.part_o + (row0 + (int64_t)c0 * p.group) * D + d;
+    const int64_t step = (int64_t)p.group * D;
+#pragma unroll 8
+    for (int k = 0; k < nc; ++k) O += po[k * step] * wts[k];
+    __syncthreads();
   }
   reinterpret_cast<E*>(p.out)[((int64_t)b * p.nq + h) * D + d] = cvt16<E>(L > 0.f ? O / L : 0.f);
 }

@@ -142,7 +142,14 @@ def decode_bench(args):
     fa.lib()
     dev = torch.device("cuda:0")
     log("generating the decode workload")
-    case = wl.make_decode_workload(torch.float16 if args.dtype == "fp16" else None, args.decode_layout)
+    dt = torch.float16 if args.dtype == "fp16" else torch.bfloat16
+    if args.decode_batch > 0:
+        case = wl.make_decode_case(f"decode {args.dtype} B={args.decode_batch} L={args.decode_len} Nq=64 Nkv=8 "
+                                   f"D=128 {args.decode_layout}", [args.decode_len] * args.decode_batch,
+                                   args.decode_len, num_heads=64, num_kv_heads=8, head_dim=128, dtype=dt,
+                                   layout=args.decode_layout, seed=22)
+    else:
+        case = wl.make_decode_workload(dt, args.decode_layout)
     cfg = fa.DecodeConfig(case.batch, case.max_seq_len, case.num_heads, case.num_kv_heads, case.head_dim,
                           case.dtype, case.scale, case.layout, case.lens)
     q = case.q.to(dev)
@@ -229,6 +236,9 @@ def main():
                     help="time decode attention (fa_decode) over the decode workload instead")
     ap.add_argument("--decode-layout", choices=("BSND", "BSH", "BNSD"), default="BSND",
                     help="KV cache layout of the decode workload")
+    ap.add_argument("--decode-batch", type=int, default=0, metavar="B",
+                    help="decode over B sequences of --decode-len keys each instead of the decode workload")
+    ap.add_argument("--decode-len", type=int, default=16384)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES bytes (calibrates the HBM byte counters)")
     args = ap.parse_args()
