@@ -150,8 +150,16 @@ struct DqShape {
   static constexpr int NDB = D / 32;
 };
 
+// Two workgroups per CU need at most 256 registers per lane.  The 16-bit dropout
+// instances fit that only without a bias or an attenMask, and only with the LDS
+// operand reads of the matrix phases kept two (not four) ahead of their MFMAs; the
+// other dropout instances run one workgroup per CU rather than spill.
+template <typename T, bool DROP, int ALIBI, bool MASK>
+constexpr int dq_occupancy() { return DROP && (sizeof(T) == 4 || ALIBI != 0 || MASK) ? 1 : 2; }
+
 template <typename T, int D, bool DROP, int ALIBI, bool MASK>
-__global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, (dq_occupancy<T, DROP, ALIBI, MASK>())) void fa_bwd_dq_kernel(BwdParams p) {
+  constexpr int kReadAhead = DROP ? 2 : 4;   // LDS operand reads issued before the first MFMA of a phase
   using S = DqShape<T, D>;
   using E = typename std::conditional<sizeof(T) == 2, T, __bf16>::type;   // 16-bit element type
   using V8 = typename Vec16<E>::v8;
@@ -255,7 +263,7 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
           s = mfma32(ka, qf[c], s);
           dp = mfma32(va, df[c], dp);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);
         sched_alternate<2 * S::NOP, 0x008, 0x100>();
         __builtin_amdgcn_sched_barrier(0);
       } else {
@@ -316,7 +324,7 @@ __global__ __launch_bounds__(256, DROP ? 1 : 2) void fa_bwd_dq_kernel(BwdParams 
           for (int db = 0; db < S::NDB; ++db)
             acc[db] = mfma32(lds_read_tr_x2<V8>(base + toff[0][db], base + toff[1][db]), bs[c], acc[db]);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);
         sched_alternate<2 * S::NDB, 0x008, 0x100, 2>();
         __builtin_amdgcn_sched_barrier(0);
       } else {

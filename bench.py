@@ -48,6 +48,15 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def alibi_pse(slopes, s_len, rows):
+    """Workload 4's ALiBi bias as an external pse tensor [1, N, rows, S] (pseType 0, added after
+    scaling): -slope_h * (i - j) for the last `rows` query rows i of an S x S block."""
+    import torch
+    i = torch.arange(s_len - rows, s_len, device=slopes.device, dtype=torch.float64)[:, None]
+    j = torch.arange(s_len, device=slopes.device, dtype=torch.float64)[None, :]
+    return (-slopes.double()[:, None, None] * (i - j)).float()[None].contiguous()
+
+
 def flops_of(case):
     import workloads as wl
     pairs = wl.allowed_pairs(case.lens_q, case.lens_kv, case.head_num, case.sparse_mode, case.pre_tokens,
@@ -135,6 +144,8 @@ def decode_cpu_baseline(case, budget_s: float = 10.0):
 def decode_bench(args):
     """Decode attention over the decode workload: one step = one fa_decode call over
     every sequence (host split planning, the decode kernel, the split reduction)."""
+    if args.dtype == "fp32":
+        sys.exit("decode attention takes bf16 or fp16 inputs")
     import torch
     import attention_fa_fwd_amd as fa
     import workloads as wl
@@ -227,8 +238,12 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=5)
     ap.add_argument("--atomic-dq", action="store_true", help="time the fp32-atomic dQ variant")
-    ap.add_argument("--dtype", choices=("bf16", "fp16"), default="bf16",
-                    help="16-bit element type of workloads 2-5 (fp16 draws the same samples in fp16)")
+    ap.add_argument("--dtype", choices=("bf16", "fp16", "fp32"), default="bf16",
+                    help="element type of workloads 2-5 (fp16 / fp32 draw the same samples in that type; "
+                         "decode: bf16 or fp16)")
+    ap.add_argument("--pse", choices=("alibi", "full", "compressed"), default="alibi",
+                    help="workload 4's bias: generated from the ALiBi slopes, or the same values passed as an "
+                         "external pse tensor, full [1, N, S, S] or 1024-row compressed [1, N, 1024, S] (fp32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layout", choices=("TND", "BSND", "BSH", "BNSD", "SBH"), default="TND",
                     help="input layout of the training path (fixed-length workloads 3 and 4 for the non-TND ones)")
@@ -265,12 +280,20 @@ def main():
         print(json.dumps({"copy_bytes": args.copy_calibration}), flush=True)
         return
     log(f"generating workload {args.workload}")
-    case = wl.make_workload(args.workload, torch.float16 if args.dtype == "fp16" else None)
+    case = wl.make_workload(args.workload, {"fp16": torch.float16, "fp32": torch.float32}.get(args.dtype))
     pairs, f_fwd, f_bwd = flops_of(case)
     deterministic = not args.atomic_dq
+    pse = None
+    if args.pse != "alibi":
+        # the external pse kernels take fp32 inputs; workload 4 is the one with a bias
+        if args.workload != 4 or args.dtype != "fp32" or args.layout != "TND":
+            sys.exit("--pse full / compressed: workload 4 with --dtype fp32 in TND only")
+        s_len = int(case.lens_q[0])
+        pse = alibi_pse(torch.from_numpy(case.alibi_slopes).to(dev), s_len, s_len if args.pse == "full" else 1024)
     cfg = fa.Config(case.cu_seqlens_q, case.cu_seqlens_kv, case.head_num, case.kv_heads, case.head_dim,
                     case.dtype, case.scale, case.keep_prob, case.sparse_mode, case.pre_tokens, case.next_tokens,
-                    deterministic, layout=args.layout, atomic_dq=args.atomic_dq)
+                    deterministic, layout=args.layout, atomic_dq=args.atomic_dq,
+                    **({} if pse is None else dict(pse=pse, pse_type=0)))
     q, k, v, dy = (t.to(dev) for t in (case.q, case.k, case.v, case.dy))
     if args.layout != "TND":
         # the same values in the fixed-length layout (workloads with one common length)
@@ -284,7 +307,7 @@ def main():
             return x4 if args.layout == "BSND" else x4.reshape(b, x4.shape[1], -1)
         q, k, v, dy = (lay(t) for t in (q, k, v, dy))
     drop = torch.from_numpy(case.drop_mask).to(dev) if case.drop_mask is not None else None
-    slopes = torch.from_numpy(case.alibi_slopes).to(dev) if case.alibi_slopes is not None else None
+    slopes = torch.from_numpy(case.alibi_slopes).to(dev) if case.alibi_slopes is not None and pse is None else None
     sink = torch.from_numpy(case.sink).to(dev) if case.sink is not None else None
     out = torch.empty_like(q)
     tq = int(case.cu_seqlens_q[-1])
@@ -342,7 +365,8 @@ def main():
     traffic = None
     if os.path.exists(TRAFFIC_FILE):
         tf = json.load(open(TRAFFIC_FILE))
-        ent = tf.get(f"workload{args.workload}" + ("_fp16" if args.dtype == "fp16" else ""), {}).get(dom)
+        key = f"workload{args.workload}" + ("" if args.dtype == "bf16" else "_" + args.dtype)
+        ent = tf.get(key + ("" if args.pse == "alibi" else "_pse_" + args.pse), {}).get(dom)
         if ent and ent.get("source_hash") == kernel_source_hash():
             traffic = ent.get("bytes_per_launch")
 
@@ -365,8 +389,9 @@ def main():
         "config": {"workload": wl.workload_name(args.workload, case.dtype), "total_tokens": int(tq),
                    "sequences": int(case.batch), "heads_q": case.head_num, "heads_kv": case.kv_heads,
                    "head_dim": d, "allowed_pairs": int(pairs),
-                   "dq_variant": "deterministic" if deterministic else "atomic", "layout": args.layout},
-        "frac_of_peak": round(value / PEAK_BF16_TFLOPS, 4),
+                   "dq_variant": "deterministic" if deterministic else "atomic", "layout": args.layout,
+                   **({} if args.pse == "alibi" else {"pse": f"external {args.pse} (the ALiBi bias)"})},
+        "frac_of_peak": round(value / peak, 4),
         "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
         "kernels_ms": {n: round(ms / c, 4) for n, (ms, c) in kern.items()},
         "roofline": {"bound": bound, "kernel": dom,

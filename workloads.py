@@ -227,16 +227,18 @@ def workload_lengths(k: int) -> np.ndarray:
 
 
 def workload_name(k: int, dtype: Optional[torch.dtype] = None) -> str:
-    """Name of workload k; dtype float16 renames the 16-bit workloads."""
+    """Name of workload k; dtype float16 / float32 renames the 16-bit workloads."""
     name = WORKLOAD_NAMES[k]
-    return name.replace("bf16", "fp16") if dtype == torch.float16 else name
+    if dtype == torch.float16:
+        return name.replace("bf16", "fp16")
+    return name.replace("bf16", "fp32") if dtype == torch.float32 and k != 1 else name
 
 
 def make_workload(k: int, dtype: Optional[torch.dtype] = None) -> Case:
     """The five fixed workloads (sizes, masks and features as listed in WORKLOAD_NAMES).
-    dtype=torch.float16 draws the 16-bit workloads (2-5) in fp16 instead of bf16:
-    the same normal samples, rounded to the other 16-bit type."""
-    if dtype not in (None, torch.bfloat16, torch.float16) or (dtype == torch.float16 and k == 1):
+    dtype=torch.float16 (or torch.float32) draws the 16-bit workloads (2-5) in fp16
+    (fp32) instead of bf16: the same normal samples, rounded to the other type."""
+    if dtype not in (None, torch.bfloat16, torch.float16, torch.float32) or (dtype == torch.float16 and k == 1):
         raise ValueError(f"workload {k} has no {dtype} variant")
     lens = workload_lengths(k)
     dt = dict(dtype=dtype) if dtype is not None else {}
