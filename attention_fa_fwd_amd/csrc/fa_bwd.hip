@@ -151,14 +151,17 @@ struct DqShape {
 };
 
 // Two workgroups per CU need at most 256 registers per lane.  The 16-bit dropout
-// instances fit that only without a bias or an attenMask, and only with the LDS
-// operand reads of the matrix phases kept two (not four) ahead of their MFMAs; the
-// other dropout instances run one workgroup per CU rather than spill.
-template <typename T, bool DROP, int ALIBI, bool MASK>
-constexpr int dq_occupancy() { return DROP && (sizeof(T) == 4 || ALIBI != 0 || MASK) ? 1 : 2; }
+// instances fit that with the LDS operand reads of the matrix phases kept two (not
+// four) ahead of their MFMAs and the swizzled offsets formed per use (kLean below),
+// except D = 128 with an attenMask or an external pse: those, and fp32 with
+// dropout, run one workgroup per CU rather than spill.
+template <typename T, int D, bool DROP, int ALIBI, bool MASK>
+constexpr int dq_occupancy() {
+  return DROP && (sizeof(T) == 4 || (D == 128 && (MASK || ALIBI == kPseExt))) ? 1 : 2;
+}
 
 template <typename T, int D, bool DROP, int ALIBI, bool MASK>
-__global__ __launch_bounds__(256, (dq_occupancy<T, DROP, ALIBI, MASK>())) void fa_bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256, (dq_occupancy<T, D, DROP, ALIBI, MASK>())) void fa_bwd_dq_kernel(BwdParams p) {
   constexpr int kReadAhead = DROP ? 2 : 4;   // LDS operand reads issued before the first MFMA of a phase
   using S = DqShape<T, D>;
   using E = typename std::conditional<sizeof(T) == 2, T, __bf16>::type;   // 16-bit element type
@@ -216,7 +219,12 @@ __global__ __launch_bounds__(256, (dq_occupancy<T, DROP, ALIBI, MASK>())) void f
   const int t_lane = (4 * (grp >> 1) + (sl >> 2)) * S::P + (16 * (grp & 1) + 4 * (sl & 3)) * 2;
   // swizzled 16-bit tiles: row reads of chunk 2c + hh of row lrow (+32 per key
   // block), transposing reads of rows rv and rv + 8 (+16 per step), chunk 4db + qv
+  // The chunk index enters an offset only through bits the rest of it leaves
+  // clear, so koff[c] == kx ^ 32c and toff[hf][db] == tx[hf] ^ 64db.  The dropout
+  // instances, short of registers, form the offsets per use from kx, tx (kLean).
+  constexpr bool kLean = DROP;
   int koff[S::kSwz ? S::NOP : 1], toff[2][S::kSwz ? S::NDB : 1];
+  int kx = 0, tx[2] = {0, 0};
   if constexpr (S::kSwz) {
 #pragma unroll
     for (int c = 0; c < S::NOP; ++c) koff[c] = lrow * S::RB + 16 * ((2 * c + hh) ^ tile_swz<S::RB>(lrow));
@@ -226,6 +234,9 @@ __global__ __launch_bounds__(256, (dq_occupancy<T, DROP, ALIBI, MASK>())) void f
 #pragma unroll
       for (int db = 0; db < S::NDB; ++db)
         toff[hf][db] = (rv + 8 * hf) * S::RB + 16 * ((4 * db + qv) ^ tile_swz<S::RB>(rv + 8 * hf)) + bv;
+    kx = lrow * S::RB + ((16 * hh) ^ (16 * tile_swz<S::RB>(lrow)));
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) tx[hf] = (rv + 8 * hf) * S::RB + ((16 * qv) ^ (16 * tile_swz<S::RB>(rv + 8 * hf))) + bv;
   }
 
   auto load = [&](char* st, int t) {
@@ -253,13 +264,17 @@ __global__ __launch_bounds__(256, (dq_occupancy<T, DROP, ALIBI, MASK>())) void f
     for (int kb = 0; kb < kDqBN / 32; ++kb) {
       // ---- S^T = K Q^T, dP~^T = V dY^T for 32 keys (lane = row, registers = keys) ----
       f32x16 s = f32x16{}, dp = f32x16{};
+      // lean offsets: fresh copies per key block, so their XORs are not hoisted
+      int kxl = kx, tx0 = tx[0], tx1 = tx[1];
+      if constexpr (kLean) asm volatile("" : "+v"(kxl), "+v"(tx0), "+v"(tx1));
       if constexpr (sizeof(T) == 2) {
         // K and V reads run a few MFMAs ahead of their use
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < S::NOP; ++c) {
-          const V8 ka = lds_read_b128<V8>(ks + koff[c] + 32 * kb * S::RB);
-          const V8 va = lds_read_b128<V8>(vs + koff[c] + 32 * kb * S::RB);
+          const int ko = kLean ? (kxl ^ (32 * c)) : koff[c];
+          const V8 ka = lds_read_b128<V8>(ks + ko + 32 * kb * S::RB);
+          const V8 va = lds_read_b128<V8>(vs + ko + 32 * kb * S::RB);
           s = mfma32(ka, qf[c], s);
           dp = mfma32(va, df[c], dp);
         }
@@ -322,7 +337,9 @@ __global__ __launch_bounds__(256, (dq_occupancy<T, DROP, ALIBI, MASK>())) void f
           const char* base = ks + (32 * kb + 16 * c) * S::RB;
 #pragma unroll
           for (int db = 0; db < S::NDB; ++db)
-            acc[db] = mfma32(lds_read_tr_x2<V8>(base + toff[0][db], base + toff[1][db]), bs[c], acc[db]);
+            acc[db] = mfma32(kLean ? lds_read_tr_x2<V8>(base + (tx0 ^ (64 * db)), base + (tx1 ^ (64 * db)))
+                                   : lds_read_tr_x2<V8>(base + toff[0][db], base + toff[1][db]),
+                             bs[c], acc[db]);
         }
         __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);
         sched_alternate<2 * S::NDB, 0x008, 0x100, 2>();
