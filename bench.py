@@ -279,15 +279,15 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": args.copy_calibration}), flush=True)
         return
+    # the external pse kernels take fp32 inputs; workload 4 is the one with a bias
+    if args.pse != "alibi" and (args.workload != 4 or args.dtype != "fp32" or args.layout != "TND"):
+        sys.exit("--pse full / compressed: workload 4 with --dtype fp32 in TND only")
     log(f"generating workload {args.workload}")
     case = wl.make_workload(args.workload, {"fp16": torch.float16, "fp32": torch.float32}.get(args.dtype))
     pairs, f_fwd, f_bwd = flops_of(case)
     deterministic = not args.atomic_dq
     pse = None
     if args.pse != "alibi":
-        # the external pse kernels take fp32 inputs; workload 4 is the one with a bias
-        if args.workload != 4 or args.dtype != "fp32" or args.layout != "TND":
-            sys.exit("--pse full / compressed: workload 4 with --dtype fp32 in TND only")
         s_len = int(case.lens_q[0])
         pse = alibi_pse(torch.from_numpy(case.alibi_slopes).to(dev), s_len, s_len if args.pse == "full" else 1024)
     cfg = fa.Config(case.cu_seqlens_q, case.cu_seqlens_kv, case.head_num, case.kv_heads, case.head_dim,
