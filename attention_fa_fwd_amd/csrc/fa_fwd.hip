@@ -341,17 +341,21 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
   char* kn = kst[1];
   char* vc = vst[0];
   char* vn = vst[1];
-  // a tile is classified (its keep-mask and attenMask words fetched) one tile
+  // with keep-mask or attenMask words to fetch, a tile is classified one tile
   // ahead, beside its copies, so those loads are in flight during the tile before
+  // (without them, classifying in place is the faster schedule)
+  constexpr bool kAhead = DROP || MASK;
   RowTile rt_next{};
-  if (t_lo < t_hi) rt_next = classify(t_lo);
+  if (kAhead && t_lo < t_hi) rt_next = classify(t_lo);
   for (int t = t_lo; t < t_hi; ++t) {
-    const RowTile rt = rt_next;
+    RowTile rt;
+    if constexpr (kAhead) rt = rt_next;
     if (t + 1 < t_hi) {
       load_k(kn, t + 1);
       load_v(vn, t + 1);
-      rt_next = classify(t + 1);
+      if constexpr (kAhead) rt_next = classify(t + 1);
     }
+    if constexpr (!kAhead) rt = classify(t);
     if (rt.live) {
       f32x16 s[2];
       scores(kc, s);
