@@ -24,6 +24,11 @@ DECODE_CASES = {
     "long_split": dict(lens=[16384, 7000, 31], s=16384, nq=8, nkv=8, d=128, layout="BSND"),
     "masked_rows_bnsd": dict(lens=[300, 77], s=320, nq=8, nkv=2, d=64, layout="BNSD", mask_p=0.2,
                              full_rows=[1]),
+    # one long sequence over 4 kv heads: the split rule grows the chunk to 3072 keys (1024 per wave)
+    "chunk_growth": dict(lens=[100000], s=100000, nq=16, nkv=4, d=128, layout="BSND"),
+    # a large batch of short sequences (empty ones included), one item each
+    "many_short": dict(lens=[int(x) for x in np.random.default_rng(7).integers(0, 41, 512)], s=40, nq=8, nkv=2,
+                       d=64, layout="BSH"),
 }
 
 
