@@ -15,8 +15,7 @@ import numpy as np
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-# FA_LIBRARY selects another build of the same library (tuning experiments)
-LIB_PATH = os.environ.get("FA_LIBRARY") or os.path.join(_PKG, "libfa.so")
+LIB_PATH = os.path.join(_PKG, "libfa.so")
 
 FA_OK = 0
 FA_ERR_PARAM_NULLPTR = 161001
@@ -69,6 +68,8 @@ class FaConfig(ctypes.Structure):
         ("pse_cols", ctypes.c_int64),
         ("pse_type", ctypes.c_int32),
         ("strides", ctypes.POINTER(ctypes.c_int64)),
+        ("q_start_idx", ctypes.POINTER(ctypes.c_int64)),
+        ("kv_start_idx", ctypes.POINTER(ctypes.c_int64)),
     ]
 
 
@@ -139,11 +140,14 @@ class Config:
     def __init__(self, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, head_dim, dtype, scale, keep_prob=1.0,
                  sparse_mode=0, pre_tokens=TOKENS_DEFAULT, next_tokens=TOKENS_DEFAULT, deterministic=True,
                  prefix=None, atten_mask=None, pse_type=2, slopes_per_batch=False, layout="TND", pse=None,
-                 atomic_dq=False):
+                 atomic_dq=False, q_start_idx=None, kv_start_idx=None):
         self.cu_q = np.ascontiguousarray(np.asarray(cu_seqlens_q, dtype=np.int64))
         self.cu_kv = np.ascontiguousarray(np.asarray(cu_seqlens_kv, dtype=np.int64))
         # per-sequence prefix N of sparse mode 6 (prefixOptional); NULL when None
         self.prefix = None if prefix is None else np.ascontiguousarray(np.asarray(prefix, dtype=np.int64))
+        # qStartIdx / kvStartIdx (sparse mode 8): one host value each, or None
+        self.q_start = None if q_start_idx is None else np.array([int(q_start_idx)], dtype=np.int64)
+        self.kv_start = None if kv_start_idx is None else np.array([int(kv_start_idx)], dtype=np.int64)
         # attenMask: a device tensor of bool / uint8 [S1Max, S2Max], nonzero = masked out (kept alive here)
         self.atten_mask = atten_mask
         if atten_mask is not None:
@@ -185,7 +189,10 @@ class Config:
             pse_batch=(0 if pse is None else int(pse.shape[0])),
             pse_rows=(0 if pse is None else int(pse.shape[2])),
             pse_cols=(0 if pse is None else int(pse.shape[3])),
-            pse_type=(int(pse_type) if pse is not None else 0))
+            pse_type=(int(pse_type) if pse is not None else 0),
+            q_start_idx=(None if self.q_start is None else self.q_start.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))),
+            kv_start_idx=(None if self.kv_start is None else
+                          self.kv_start.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
 
     @property
     def ref(self):
@@ -420,9 +427,7 @@ def fa_decode_workspace_size(cfg: DecodeConfig) -> int:
     return n.value
 
 
-def fa_decode(cfg: DecodeConfig, q, k, v, out=None, workspace=None):
-    """Decode attention through libfa.so on the current stream; q, out [B, Nq, D]
-    (any view of those elements, e.g. [B, 1, Nq*D]), k, v in cfg's layout.  Returns out."""
+def _decode_checks(cfg: DecodeConfig, q, k, v, out):
     dev = q.device
     c = cfg.c
     qshape = (c.batch, c.num_heads, c.head_dim)
@@ -433,6 +438,13 @@ def fa_decode(cfg: DecodeConfig, q, k, v, out=None, workspace=None):
     if out is None:
         out = torch.empty_like(q)
     _check_tensor("out", out, tuple(q.shape), q.dtype, dev)
+    return dev, out
+
+
+def fa_decode(cfg: DecodeConfig, q, k, v, out=None, workspace=None):
+    """Decode attention through libfa.so on the current stream; q, out [B, Nq, D]
+    (any view of those elements, e.g. [B, 1, Nq*D]), k, v in cfg's layout.  Returns out."""
+    dev, out = _decode_checks(cfg, q, k, v, out)
     ws = _workspace(fa_decode_workspace_size(cfg), dev, workspace)
     st = lib().fa_decode(cfg.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(ws), ctypes.c_uint64(ws.numel()),
                          _stream_handle(dev))

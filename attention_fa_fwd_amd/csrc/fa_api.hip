@@ -47,6 +47,8 @@ struct Problem {
   const uint8_t* mask = nullptr;   // attenMask (device) when the mode uses it
   int64_t mask_rows = 0, mask_cols = 0, mask_words = 0;   // words: 32-key words per packed row
   int64_t drop_bits = 0;
+  int64_t q_start = 0, kv_start = 0;   // mode 8: positions of sequence 0 in its unsplit sequence
+  bool has_start = false;
 };
 
 static_assert(fa::kLayoutBNSD == FA_LAYOUT_BNSD && fa::kLayoutSBH == FA_LAYOUT_SBH, "layout codes");
@@ -79,14 +81,21 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   if (cfg->head_dim < 1 || cfg->head_dim > 128 || (cfg->head_dim * ebytes) % 16 != 0) return FA_ERR_PARAM_INVALID;
   const int mode = cfg->sparse_mode;
   if (mode != FA_SPARSE_NONE && mode != FA_SPARSE_ALL_MASK && mode != FA_SPARSE_LEFT_UP_CAUSAL &&
-      mode != FA_SPARSE_RIGHT_DOWN_CAUSAL && mode != FA_SPARSE_BAND && mode != FA_SPARSE_PREFIX)
+      mode != FA_SPARSE_RIGHT_DOWN_CAUSAL && mode != FA_SPARSE_BAND && mode != FA_SPARSE_PREFIX &&
+      mode != FA_SPARSE_RIGHT_DOWN_CAUSAL_BAND && mode != FA_SPARSE_BAND_LEFT_UP_CAUSAL)
     return FA_ERR_PARAM_INVALID;
+  const bool band_mode = mode == FA_SPARSE_BAND || mode == FA_SPARSE_RIGHT_DOWN_CAUSAL_BAND ||
+                         mode == FA_SPARSE_BAND_LEFT_UP_CAUSAL;
   if (mode == FA_SPARSE_ALL_MASK && !cfg->atten_mask) return FA_ERR_PARAM_NULLPTR;
   if (mode == FA_SPARSE_PREFIX && !cfg->prefix) return FA_ERR_PARAM_NULLPTR;
   if (mode == FA_SPARSE_PREFIX && cfg->batch > kMaxPrefixBatch) return FA_ERR_PARAM_INVALID;
   if (!(cfg->keep_prob > 0.0 && cfg->keep_prob <= 1.0)) return FA_ERR_PARAM_INVALID;
   if (!std::isfinite(cfg->scale)) return FA_ERR_PARAM_INVALID;
-  if (mode == FA_SPARSE_BAND && cfg->pre_tokens + cfg->next_tokens < 0) return FA_ERR_PARAM_INVALID;
+  if (band_mode && cfg->pre_tokens + cfg->next_tokens < 0) return FA_ERR_PARAM_INVALID;
+  // start indices belong to the split of mode 8; modes 7 and 8 take no pse tensor
+  if ((cfg->q_start_idx || cfg->kv_start_idx) && mode != FA_SPARSE_BAND_LEFT_UP_CAUSAL) return FA_ERR_PARAM_INVALID;
+  if (cfg->pse && (mode == FA_SPARSE_RIGHT_DOWN_CAUSAL_BAND || mode == FA_SPARSE_BAND_LEFT_UP_CAUSAL))
+    return FA_ERR_PARAM_INVALID;
   if (cfg->deterministic != 0 && cfg->deterministic != 1) return FA_ERR_PARAM_INVALID;
   if ((cfg->flags & ~(FA_FLAG_PSE_SQRT | FA_FLAG_SLOPES_PER_BATCH | FA_FLAG_ATOMIC_DQ)) != 0)
     return FA_ERR_PARAM_INVALID;
@@ -140,6 +149,16 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   }
   pr->tq = cq[pr->batch];
   pr->tkv = ck[pr->batch];
+  if (cfg->q_start_idx || cfg->kv_start_idx) {
+    // the pages' constraint for a split in the query direction:
+    // Lq_0 - Lkv_0 + qStartIdx - kvStartIdx == 0 (the chunk's last row meets its last key)
+    pr->q_start = cfg->q_start_idx ? *cfg->q_start_idx : 0;
+    pr->kv_start = cfg->kv_start_idx ? *cfg->kv_start_idx : 0;
+    if (pr->q_start < 0 || pr->kv_start < 0 || pr->q_start > (int64_t(1) << 30) || pr->kv_start > (int64_t(1) << 30))
+      return FA_ERR_PARAM_INVALID;
+    if ((cq[1] - cq[0]) - (ck[1] - ck[0]) + pr->q_start - pr->kv_start != 0) return FA_ERR_PARAM_INVALID;
+    pr->has_start = true;
+  }
   if (cfg->pse) {
     // the 16-bit kernels' external-pse instances are switched off: a bf16 run of them
     // faulted on the device and the cause is not yet shown; fp32 inputs only
@@ -222,17 +241,21 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
 }
 
 fa_status check_alibi(const Problem& pr) {
-  // pseType 2 needs Sq == Skv per sequence, and no zero-length sequence carries a pse
+  // pseType 2 needs Sq == Skv per sequence, and no zero-length sequence carries a pse;
+  // mode 7 takes no pse; in mode 8 the first sequence may be a chunk split off a longer
+  // one, whose positions the start indices give (checked in parse)
+  if (pr.mode == FA_SPARSE_RIGHT_DOWN_CAUSAL_BAND) return FA_ERR_PARAM_INVALID;
   for (int64_t b = 0; b < pr.batch; ++b) {
     const int32_t lq = pr.cu_q[b + 1] - pr.cu_q[b], lkv = pr.cu_kv[b + 1] - pr.cu_kv[b];
-    if (lq != lkv || lq == 0) return FA_ERR_PARAM_INVALID;
+    if (lq == 0 || lkv == 0) return FA_ERR_PARAM_INVALID;
+    if (lq != lkv && !(b == 0 && pr.has_start)) return FA_ERR_PARAM_INVALID;
   }
   return FA_OK;
 }
 
 FaWindow window_of(const Problem& pr, int64_t b) {
   const int32_t lq = pr.cu_q[b + 1] - pr.cu_q[b], lkv = pr.cu_kv[b + 1] - pr.cu_kv[b];
-  return fa_make_window(pr.mode, pr.pre, pr.next, lq, lkv, pr.prefix[b]);
+  return fa_make_window(fa_seq_mode(pr.mode, b, pr.batch), pr.pre, pr.next, lq, lkv, pr.prefix[b]);
 }
 
 // Work list of one pass.  The items of one sequence are consecutive, so the
@@ -469,6 +492,8 @@ void fill_common_fwd(const Problem& pr, fa::FwdParams& p) {
   p.inv_keep = (float)(1.0 / pr.keep);
   p.use_dropout = pr.keep < 1.0 ? 1 : 0;
   p.head_swizzle = (pr.nq % 8 == 0) ? 1 : 0;
+  p.nseq = (int32_t)pr.batch;
+  p.pse_off0 = (int32_t)(pr.q_start - pr.kv_start);
 }
 
 std::vector<char> stage_block(const Problem& pr, const Layout& L, const std::vector<WorkItem>& i0,
@@ -774,6 +799,8 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
   p.inv_keep = (float)(1.0 / pr.keep);
   p.use_dropout = pr.keep < 1.0 ? 1 : 0;
   p.head_swizzle = (pr.nq % 8 == 0) ? 1 : 0;
+  p.nseq = (int32_t)pr.batch;
+  p.pse_off0 = (int32_t)(pr.q_start - pr.kv_start);
   p.n_pre_blocks = L.n_pre_blocks;
   p.mbits = pr.mask ? reinterpret_cast<const uint32_t*>(ws + L.mbits) : nullptr;
   p.mwords = (int32_t)pr.mask_words;
@@ -834,22 +861,15 @@ fa_status fa_decode_workspace_size(const fa_decode_config* cfg, uint64_t* bytes)
   return FA_OK;
 }
 
-fa_status fa_decode(const fa_decode_config* cfg, const void* q, const void* k, const void* v, void* out,
-                    void* workspace, uint64_t workspace_bytes, void* stream) {
-  DecProblem pr;
-  fa_status st = parse_decode(cfg, &pr);
-  if (st != FA_OK) return st;
-  if (!q || !k || !v || !out || !workspace) return FA_ERR_PARAM_NULLPTR;
-  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FA_ERR_PARAM_INVALID;
-  const DecPlan P = plan_decode(pr);
-  if (workspace_bytes < P.total) return FA_ERR_WORKSPACE;
+namespace {
 
+// One decode call on a validated problem and its plan; ws holds at least P.total bytes.
+fa_status decode_run(const DecProblem& pr, const DecPlan& P, const void* q, const void* k, const void* v, void* out,
+                     char* ws, hipStream_t s) {
   std::vector<char> host(P.staged, 0);
   std::memcpy(host.data() + P.off_items, P.items.data(), sizeof(fa::DecItem) * P.items.size());
   std::memcpy(host.data() + P.off_first, P.first_slot.data(), 4 * P.first_slot.size());
   std::memcpy(host.data() + P.off_nsplit, P.n_split.data(), 4 * P.n_split.size());
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  char* ws = reinterpret_cast<char*>(workspace);
   if (hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, s) != hipSuccess) return FA_ERR_HIP;
 
   fa::DecParams p{};
@@ -881,6 +901,20 @@ fa_status fa_decode(const fa_decode_config* cfg, const void* q, const void* k, c
   if (e == hipSuccess && P.n_slots > 0)
     e = timed(K_DEC_REDUCE, s, [&] { return fa::launch_decode_reduce(pr.dtype, (int)pr.d, p, s); });
   return hip_status(e);
+}
+
+}  // namespace
+
+fa_status fa_decode(const fa_decode_config* cfg, const void* q, const void* k, const void* v, void* out,
+                    void* workspace, uint64_t workspace_bytes, void* stream) {
+  DecProblem pr;
+  fa_status st = parse_decode(cfg, &pr);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !out || !workspace) return FA_ERR_PARAM_NULLPTR;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FA_ERR_PARAM_INVALID;
+  const DecPlan P = plan_decode(pr);
+  if (workspace_bytes < P.total) return FA_ERR_WORKSPACE;
+  return decode_run(pr, P, q, k, v, out, reinterpret_cast<char*>(workspace), reinterpret_cast<hipStream_t>(stream));
 }
 
 fa_status fa_profile_enable(int32_t on) {

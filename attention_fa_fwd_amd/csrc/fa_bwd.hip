@@ -182,7 +182,7 @@ __global__ __launch_bounds__(256, (dq_occupancy<T, D, DROP, ALIBI, MASK>())) voi
   const int b = it.b;
   const int q0 = p.cu_q[b], lq = p.cu_q[b + 1] - q0;
   const int k0 = p.cu_kv[b], lkv = p.cu_kv[b + 1] - k0;
-  const FaWindow win = fa_make_window(p.mode, p.pre, p.next, lq, lkv, p.prefix[b]);
+  const FaWindow win = fa_make_window(fa_seq_mode(p.mode, b, p.nseq), p.pre, p.next, lq, lkv, p.prefix[b]);
   const int wr0 = it.tile * kDqBM + 32 * wave;
   const int i = wr0 + lrow;
   const bool row_ok = i < lq;
@@ -208,6 +208,7 @@ __global__ __launch_bounds__(256, (dq_occupancy<T, D, DROP, ALIBI, MASK>())) voi
   const float lse2 = row_ok ? p.lse[rowg * p.nq + h] : __builtin_inff();
   const float di = row_ok ? p.delta[rowg * p.nq + h] : 0.f;
   const float slope_l2 = pse_slopes(ALIBI) ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
+  const int poff = b == 0 ? p.pse_off0 : 0;   // sequence 0 of mode 8: pse row i + qStartIdx - kvStartIdx
   f32x16 acc[S::NDB];
 #pragma unroll
   for (int db = 0; db < S::NDB; ++db) acc[db] = f32x16{};
@@ -299,7 +300,7 @@ __global__ __launch_bounds__(256, (dq_occupancy<T, D, DROP, ALIBI, MASK>())) voi
         }
       }
       f32x16 ds;
-      const float jmi = (float)(c0 + 32 * kb + 4 * hh - i);   // j - i of register 0
+      const float jmi = (float)(c0 + 32 * kb + 4 * hh - i - poff);   // j - i of register 0 (pse position)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int kk = 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);

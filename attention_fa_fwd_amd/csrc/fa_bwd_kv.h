@@ -68,7 +68,8 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
   const int b = it.b;
   const int q0 = p.cu_q[b], lq = p.cu_q[b + 1] - q0;
   const int k0 = p.cu_kv[b], lkv = p.cu_kv[b + 1] - k0;
-  const FaWindow win = fa_make_window(p.mode, p.pre, p.next, lq, lkv, p.prefix[b]);
+  const FaWindow win = fa_make_window(fa_seq_mode(p.mode, b, p.nseq), p.pre, p.next, lq, lkv, p.prefix[b]);
+  const int poff = b == 0 ? p.pse_off0 : 0;   // sequence 0 of mode 8: pse row i + qStartIdx - kvStartIdx
   const int c0 = it.tile * kKvBN;          // first key of the workgroup tile
   const int wc0 = c0 + 32 * wave;          // first key of this wave
   const int j = wc0 + lrow;                // this lane's key
@@ -264,7 +265,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
       if constexpr (DROP) bits4 = *reinterpret_cast<const u32x4*>(bits_s + wave * kKvBM + rq);
       if constexpr (!decltype(full_c)::value && MASK)
         mb4 = *reinterpret_cast<const u32x4*>(st + S::OFF_MBITS + 4 * (wave * kKvBM + rq));
-      const float jmi = (float)(j - r0 - rq);   // j - i of register 4a; minus e for register 4a + e
+      const float jmi = (float)(j - r0 - rq - poff);   // j - i of register 4a (pse position); minus e for 4a + e
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int r = 4 * a + e, rr = rq + e, i = r0 + rr;
@@ -387,7 +388,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
         if constexpr (ALIBI == kPseExt)
           x = __builtin_fmaf(p.pse_coef, (r0 + rr < lq && key_ok) ? pse_value<T>(p, b, h, r0 + rr, j, lq) : 0.f, x);
         else if constexpr (ALIBI != 0)
-          x = add_pse<ALIBI>(x, slope_l2, (float)(j - (r0 + rr)));
+          x = add_pse<ALIBI>(x, slope_l2, (float)(j - (r0 + rr) - poff));
         if (!full && (!fa_allowed(win, r0 + rr, j, lq, lkv) ||
                       (MASK && ((reinterpret_cast<const uint32_t*>(st + S::OFF_MBITS)[wave * kKvBM + rr] >> lrow) & 1u))))
           x = kNegInf;
@@ -613,7 +614,8 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
   const int b = it.b;
   const int q0 = p.cu_q[b], lq = p.cu_q[b + 1] - q0;
   const int k0 = p.cu_kv[b], lkv = p.cu_kv[b + 1] - k0;
-  const FaWindow win = fa_make_window(p.mode, p.pre, p.next, lq, lkv, p.prefix[b]);
+  const FaWindow win = fa_make_window(fa_seq_mode(p.mode, b, p.nseq), p.pre, p.next, lq, lkv, p.prefix[b]);
+  const int poff = b == 0 ? p.pse_off0 : 0;   // sequence 0 of mode 8: pse row i + qStartIdx - kvStartIdx
   const int c0 = it.tile * kKvBN;          // first key of the workgroup tile
   const int wc0 = c0 + 32 * kg;            // first key of this wave's group
   const int j = wc0 + lrow;                // this lane's key
@@ -733,7 +735,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
           if constexpr (DROP) bits4 = *reinterpret_cast<const u32x4*>(bits_s + kg * kKvBM + rq);
           if constexpr (!decltype(full_c)::value && MASK)
             mb4 = *reinterpret_cast<const u32x4*>(st + S::OFF_MBITS + 4 * (kg * kKvBM + rq));
-          const float jmi = (float)(j - r0 - rq);   // j - i of register 4a; minus e for register 4a + e
+          const float jmi = (float)(j - r0 - rq - poff);   // j - i of register 4a (pse position); minus e for 4a + e
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             const int r = 4 * a + e, i = r0 + rq + e;

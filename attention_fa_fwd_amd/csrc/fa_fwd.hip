@@ -93,7 +93,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
   const int b = it.b;
   const int q0 = p.cu_q[b], lq = p.cu_q[b + 1] - q0;
   const int k0 = p.cu_kv[b], lkv = p.cu_kv[b + 1] - k0;
-  const FaWindow win = fa_make_window(p.mode, p.pre, p.next, lq, lkv, p.prefix[b]);
+  const FaWindow win = fa_make_window(fa_seq_mode(p.mode, b, p.nseq), p.pre, p.next, lq, lkv, p.prefix[b]);
 
   const int wr0 = it.tile * BM + wave * 32;       // first row of this wave (in sequence)
   const int i = wr0 + lrow;                        // this lane's row
@@ -123,6 +123,9 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
   }
 
   const float slope_l2 = pse_slopes(ALIBI) ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
+  // generated pse on positions in the unsplit sequence: sequence 0 of mode 8 starts qStartIdx -
+  // kvStartIdx rows after its keys, so its bias uses j - (i + poff)
+  const int poff = b == 0 ? p.pse_off0 : 0;
   const bool has_sink = p.sink != nullptr;
   float m_run = has_sink ? p.sink[h] * kLog2e : kNegInf;   // exponent offset
   float m_true = m_run;                                     // running maximum
@@ -232,7 +235,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
           if constexpr (ALIBI == kPseExt)
             x = __builtin_fmaf(p.pse_coef, (row_ok && j < lkv) ? pse_value<T>(p, b, h, i, j, lq) : 0.f, x);
           else if constexpr (ALIBI != 0)
-            x = add_pse<ALIBI>(x, slope_l2, (float)(j - i));
+            x = add_pse<ALIBI>(x, slope_l2, (float)(j - i - poff));
           if (!decltype(full_c)::value &&
               (!fa_allowed(win, i, j, lq, lkv) || (MASK && ((rt.mw[kb] >> (8 * (r >> 2) + 4 * hh + (r & 3))) & 1u))))
             x = kNegInf;

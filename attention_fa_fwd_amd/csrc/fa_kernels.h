@@ -44,6 +44,8 @@ struct FwdParams {
   int32_t n_items;
   int32_t nq, nkv, group;
   int32_t mode, pre, next;
+  int32_t nseq;       // sequences (sparse modes 7 and 8 pick a mask per sequence)
+  int32_t pse_off0;   // sequence 0's generated pse uses row i + pse_off0 (qStartIdx - kvStartIdx, mode 8)
   float scale_log2;   // scale * log2(e)
   float inv_keep;     // 1 / keep_prob
   int32_t use_dropout;
@@ -91,6 +93,8 @@ struct BwdParams {
   int32_t total_q;
   int32_t nq, nkv, group;
   int32_t mode, pre, next;
+  int32_t nseq;       // sequences (sparse modes 7 and 8 pick a mask per sequence)
+  int32_t pse_off0;   // sequence 0's generated pse uses row i + pse_off0 (qStartIdx - kvStartIdx, mode 8)
   float scale;
   float scale_log2;
   float inv_keep;

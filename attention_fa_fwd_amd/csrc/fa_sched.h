@@ -12,6 +12,7 @@
 //   mode 4 (band)             : pre, next as given,        delta = Lkv - Lq
 //   mode 6 (prefix N)         : as mode 3, and hi(i) >= N - 1 ("floor"): the
 //                               sequence's first N keys are visible to every row
+//   modes 7, 8                : one of the above per sequence (fa_seq_mode)
 // Both interval ends are non-decreasing in the row and every non-empty row
 // interval meets its neighbours' (they grow by one per row; the prefix floor
 // only raises hi where lo is unbounded), so the allowed set of a rectangular
@@ -36,6 +37,19 @@ struct FaWindow {
   int32_t next;   // keys allowed to the right of the diagonal
   int32_t floor;  // every row may also see keys [0, floor] (prefix mode: N - 1; else -1)
 };
+
+// Sparse modes 7 and 8 (aclnnFlashAttentionUnpaddingScoreGrad, sparseMode list:
+// both arise when long sequences are split outside the operator) combine two of
+// the masks above over the batch:
+//   mode 7 (rightDownCausal_Band): the last sequence takes the band (mode 4),
+//                                  every other one rightDownCausal (mode 3);
+//   mode 8 (band_LeftUpCausal):    the first sequence takes the band, every
+//                                  other one leftUpCausal (mode 2).
+FA_HD int fa_seq_mode(int mode, int64_t b, int64_t nseq) {
+  if (mode == 7) return b == nseq - 1 ? 4 : 3;
+  if (mode == 8) return b == 0 ? 4 : 2;
+  return mode;
+}
 
 FA_HD int64_t fa_clamp_window(int64_t w) {
   return w > FA_WINDOW_INF ? FA_WINDOW_INF : (w < -FA_WINDOW_INF ? -FA_WINDOW_INF : w);

@@ -57,6 +57,38 @@ def alibi_pse(slopes, s_len, rows):
     return (-slopes.double()[:, None, None] * (i - j)).float()[None].contiguous()
 
 
+def timed_steps(step, steps, stream, cold_cache, dev):
+    """Times `steps` calls of step() with HIP events on `stream`: one event between
+    consecutive steps, so each step's duration is known.  Returns (mean ms per step
+    over the whole bracket, wall seconds, per-step ms).  With cold_cache, a 1 GiB
+    buffer is overwritten between steps (outside each step's events) so that no step
+    finds its inputs in the 256 MB last-level cache; the mean is then the mean of the
+    per-step durations."""
+    import torch
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev) if cold_cache else None
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps if cold_cache else steps + 1)]
+    torch.cuda.synchronize()
+    w0 = time.perf_counter()
+    if cold_cache:
+        for i in range(steps):
+            scratch.fill_(float(i))
+            ev[2 * i].record(stream)
+            step()
+            ev[2 * i + 1].record(stream)
+    else:
+        ev[0].record(stream)
+        for i in range(steps):
+            step()
+            ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    if cold_cache:
+        per = [ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)]
+        return float(np.mean(per)), wall, per
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return ev[0].elapsed_time(ev[steps]) / steps, wall, per
+
+
 def flops_of(case):
     import workloads as wl
     pairs = wl.allowed_pairs(case.lens_q, case.lens_kv, case.head_num, case.sparse_mode, case.pre_tokens,
@@ -245,6 +277,11 @@ def main():
                     help="workload 4's bias: generated from the ALiBi slopes, or the same values passed as an "
                          "external pse tensor, full [1, N, S, S] or 1024-row compressed [1, N, 1024, S] (fp32)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-cache", action="store_true",
+                    help="overwrite a 1 GiB buffer between timed steps (no step finds its inputs in the MALL)")
+    ap.add_argument("--variant-steps", type=int, default=3,
+                    help="steps timed for the atomic-dQ variant reported beside the deterministic headline "
+                         "(0: skip it)")
     ap.add_argument("--layout", choices=("TND", "BSND", "BSH", "BNSD", "SBH"), default="TND",
                     help="input layout of the training path (fixed-length workloads 3 and 4 for the non-TND ones)")
     ap.add_argument("--decode", action="store_true",
@@ -327,18 +364,9 @@ def main():
         step()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    log(f"timing {args.steps} steps")
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms_step = e0.elapsed_time(e1) / args.steps
-    log(f"{ms_step:.3f} ms/step (wall {1e3 * wall / args.steps:.3f})")
+    ms_step, wall, step_ms = timed_steps(step, args.steps, stream, args.cold_cache, dev)
+    log(f"{ms_step:.3f} ms/step (median {np.median(step_ms):.3f}, min {min(step_ms):.3f}; "
+        f"wall {1e3 * wall / args.steps:.3f})")
 
     # per-kernel durations: HIP events the library records around each launch, over the same
     # number of steps, on the stream each kernel is launched on
@@ -381,6 +409,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(float(np.median(step_ms)), 4),
+        "ms_per_step_min": round(float(min(step_ms)), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -390,6 +420,7 @@ def main():
                    "sequences": int(case.batch), "heads_q": case.head_num, "heads_kv": case.kv_heads,
                    "head_dim": d, "allowed_pairs": int(pairs),
                    "dq_variant": "deterministic" if deterministic else "atomic", "layout": args.layout,
+                   "cache": "cold (1 GiB written between steps)" if args.cold_cache else "warm",
                    **({} if args.pse == "alibi" else {"pse": f"external {args.pse} (the ALiBi bias)"})},
         "frac_of_peak": round(value / peak, 4),
         "fwd_tflops": round(f_fwd / (fwd_ms * 1e-3) / 1e12, 2),
@@ -401,6 +432,36 @@ def main():
                      "traffic": traffic},
         "note": "the pages give API constraints but no throughput figures of their own",
     }
+    if deterministic and args.variant_steps > 0:
+        # the pages' other backward scheme, timed beside the headline: dQ accumulated with fp32
+        # atomics inside the dK/dV pass (where that variant exists; otherwise the library runs
+        # the deterministic passes and the record says so)
+        acfg = fa.Config(case.cu_seqlens_q, case.cu_seqlens_kv, case.head_num, case.kv_heads, case.head_dim,
+                         case.dtype, case.scale, case.keep_prob, case.sparse_mode, case.pre_tokens,
+                         case.next_tokens, False, layout=args.layout, atomic_dq=True,
+                         **({} if pse is None else dict(pse=pse, pse_type=0)))
+        del ws_b
+        ws_a = torch.empty(fa.fa_bwd_workspace_size(acfg), dtype=torch.uint8, device=dev)
+
+        def astep():
+            fa.fa_fwd(acfg, q, k, v, drop, slopes, sink, out, m, l, workspace=ws_f)
+            fa.fa_bwd(acfg, q, k, v, dy, out, m, l, drop, slopes, sink, dq, dk, dv, dsink, workspace=ws_a)
+
+        log(f"atomic-dQ variant: {args.variant_steps} steps")
+        astep()
+        a_ms, _, a_per = timed_steps(astep, args.variant_steps, stream, args.cold_cache, dev)
+        fa.fa_profile_read()
+        fa.fa_profile_enable(True)
+        astep()
+        torch.cuda.synchronize()
+        ak = {n: ms / c for n, (ms, c) in fa.fa_profile_read().items() if c > 0}
+        fa.fa_profile_enable(False)
+        res["variants"] = {"atomic_dq": {
+            "value": round(total_flops / (a_ms * 1e-3) / 1e12, 2), "ms_per_step": round(a_ms, 4),
+            "ms_per_step_median": round(float(np.median(a_per)), 4), "steps": args.variant_steps,
+            "kernels_ms": {n: round(x, 4) for n, x in ak.items()},
+            "ran_atomic_kernel": "fa_bwd_dq_convert" in ak}}
+        del ws_a
     if not args.no_cpu_baseline:
         log("cpu baseline (fp64 oracle, bounded sample)")
         res["cpu_baseline"] = cpu_baseline(case)

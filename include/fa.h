@@ -75,6 +75,10 @@ typedef int32_t fa_status;
 #define FA_SPARSE_RIGHT_DOWN_CAUSAL 3 /* j <= i + (Lkv - Lq)                                  */
 #define FA_SPARSE_BAND 4             /* i+(Lkv-Lq)-pre <= j <= i+(Lkv-Lq)+next (inclusive)    */
 #define FA_SPARSE_PREFIX 6           /* j <= i + (Lkv - Lq)  or  j < N_b (prefix, see below)  */
+/* modes 7 and 8 (same list: produced when long sequences are split outside the operator)
+   give the band to one sequence and a causal triangle to the others; pre/next as in mode 4 */
+#define FA_SPARSE_RIGHT_DOWN_CAUSAL_BAND 7  /* last sequence: band; the others: mode 3     */
+#define FA_SPARSE_BAND_LEFT_UP_CAUSAL 8     /* first sequence: band; the others: mode 2    */
 
 #define FA_TOKENS_DEFAULT 2147483647 /* preTokens / nextTokens default of the pages */
 
@@ -98,7 +102,9 @@ typedef struct fa_config {
   int64_t head_dim;              /* D <= 128, D * element size a multiple of 16 bytes (64, 128
                                     native; others zero-padded to 64 or 128 in the workspace) */
   int32_t dtype;                 /* FA_DTYPE_*                                                */
-  int32_t sparse_mode;           /* FA_SPARSE_*                                               */
+  int32_t sparse_mode;           /* FA_SPARSE_*; modes 7 and 8 take no pse tensor, and mode 7
+                                    no alibi_slopes either (the grad pages' sparse_mode=7/8
+                                    constraints)                                              */
   double scale;                  /* scaleValue: multiplies Q K^T (usually D^-0.5)             */
   double keep_prob;              /* keepProb in (0, 1]; < 1 needs drop_mask                   */
   int64_t pre_tokens;            /* band only: keys allowed left of the diagonal              */
@@ -161,6 +167,18 @@ typedef struct fa_config {
                                     overlap.  Tensors whose strides differ from the packed
                                     ones (N*D, D) are gathered into packed copies in the
                                     workspace (outputs scattered back).  NULL = packed.       */
+  const int64_t* q_start_idx;    /* HOST, optional, one value (qStartIdxOptional of
+                                    aclnnFlashAttentionScoreV2: where the query rows of a chunk
+                                    of a long sequence split outside the operator start in that
+                                    sequence).  Sparse mode 8 only: the first sequence's query
+                                    row i sits at q_start_idx + i, its key j at kv_start_idx + j,
+                                    and its generated pse (alibi_slopes) is formed on those
+                                    positions.  Given in mode 8, the pages' constraint
+                                    Lq_0 - Lkv_0 + q_start_idx - kv_start_idx == 0 must hold.
+                                    Non-NULL in another mode, negative, or off the constraint
+                                    -> FA_ERR_PARAM_INVALID.  NULL = 0.                       */
+  const int64_t* kv_start_idx;   /* HOST, optional, one value (kvStartIdxOptional): as above
+                                    for the first sequence's keys.  NULL = 0.                  */
 } fa_config;
 
 /* Device workspace bytes needed by fa_fwd for this configuration (>= 256). */
@@ -175,7 +193,8 @@ fa_status fa_fwd_workspace_size(const fa_config* cfg, uint64_t* bytes);
  * alibi_slopes: device fp32 [Nq] (or [B, Nq] with FA_FLAG_SLOPES_PER_BATCH) or NULL:
  *   adds -slope*(i-j) (pseType 2) or, with FA_FLAG_PSE_SQRT, -slope*sqrt(|i-j|)
  *   (pseType 3) after scaling, i and j local to the sequence; requires
- *   Lq_b == Lkv_b > 0 for every sequence.
+ *   Lq_b == Lkv_b > 0 for every sequence (in mode 8 the first sequence may instead
+ *   satisfy the start-index constraint, its positions then being global).
  * sink: device fp32 [Nq] or NULL: per-head sink logit in the softmax denominator.
  * Outputs (device): out [T_q,Nq,D] of cfg->dtype; softmax_max, softmax_sum fp32 [T_q,Nq].
  * All tensor pointers must be 16-byte aligned.

@@ -9,8 +9,8 @@ leave open (keep-mask bit order, band alignment when Lq != Lkv), which are
 "parity unpinned" by the pages and only checked for self-consistency.
 """
 from .attention import (INT_MAX_TOKENS, allowed, alibi_pse, keep_bits, forward, backward,
-                        probabilities, pse_block)
+                        probabilities, pse_block, sequence_mode)
 from .decode import cache_as_bsnd, decode
 
 __all__ = ["INT_MAX_TOKENS", "allowed", "alibi_pse", "keep_bits", "forward", "backward", "probabilities",
-           "pse_block", "cache_as_bsnd", "decode"]
+           "pse_block", "sequence_mode", "cache_as_bsnd", "decode"]

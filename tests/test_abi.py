@@ -70,8 +70,12 @@ INVALID_CONFIGS = {
     "keep_zero": dict(keep_prob=0.0),
     "keep_above_one": dict(keep_prob=1.5),
     "mode_5": dict(sparse_mode=5),
-    "mode_7": dict(sparse_mode=7),
-    "mode_8": dict(sparse_mode=8),
+    "mode_9": dict(sparse_mode=9),
+    "mode_7_band_without_intersection": dict(sparse_mode=7, pre_tokens=-3, next_tokens=2),
+    # start indices: mode 8 only, non-negative, and Lq_0 - Lkv_0 + qStartIdx - kvStartIdx == 0
+    "start_idx_outside_mode_8": dict(sparse_mode=4, q_start_idx=3, kv_start_idx=3),
+    "start_idx_off_constraint": dict(sparse_mode=8, q_start_idx=3, kv_start_idx=0),
+    "start_idx_negative": dict(sparse_mode=8, q_start_idx=-2, kv_start_idx=-2),
     "band_without_intersection": dict(sparse_mode=4, pre_tokens=-3, next_tokens=2),
     "cu_not_monotone": dict(cu_seqlens_q=[0, 7, 5], cu_seqlens_kv=[0, 7, 5]),
     "cu_not_starting_at_zero": dict(cu_seqlens_q=[1, 5, 12]),
@@ -215,7 +219,7 @@ def test_atomic_variant_needs_a_larger_workspace():
 # --------------------------------------------------------------------------- scheduler
 
 def _brute_ranges(lq, lkv, mode, pre, nxt, bm, bn, by_kv, prefix=0):
-    ok = oracle.allowed(lq, lkv, mode, pre, nxt, prefix)
+    ok = oracle.allowed(lq, lkv, mode, pre, nxt, prefix)   # one sequence's own mode
     res = []
     if by_kv:
         for t in range((lkv + bn - 1) // bn):
@@ -243,6 +247,10 @@ SCHED_CASES = [
     ([300, 77, 129, 1000, 5], [500, 10, 129, 1000, 64], 6, 0, 0, [200, 0, 64, 0, 60]),
     ([513, 600, 64], [513, 600, 2000], 6, 0, 0, [513, 300, 1999]),
     ([700, 129], [129, 700], 6, 0, 0, [129, 650]),
+    # modes 7 / 8: the band on the last / first sequence, a causal triangle on the others
+    ([300, 77, 129, 513], [500, 77, 200, 700], 7, 100, 3),
+    ([513, 300, 64], [700, 300, 64], 8, 128, 0),
+    ([1000, 257, 5], [1000, 257, 5], 8, -20, 70),
 ]
 
 
@@ -270,8 +278,8 @@ def test_schedule_matches_brute_force(case, pass_id):
         seen[(b, tile)] = (lo, hi)
     expect_keys = set()
     for b in range(len(lq)):
-        for t, tiles in _brute_ranges(lq[b], lkv[b], mode, pre, nxt, bm, bn, by_kv=(pass_id == 1),
-                                      prefix=prefix[b]):
+        for t, tiles in _brute_ranges(lq[b], lkv[b], oracle.sequence_mode(mode, b, len(lq)), pre, nxt, bm, bn,
+                                      by_kv=(pass_id == 1), prefix=prefix[b]):
             expect_keys.add((b, t))
             lo, hi = seen[(b, t)]
             got = list(range(lo, hi))
@@ -470,3 +478,22 @@ def test_padded_head_dims_accepted():
         assert fa.lib().fa_fwd_workspace_size(_cfg(head_dim=d, dtype=dt).ref, ctypes.byref(n)) == fa.FA_OK, d
     for d, dt in ((36, fa.FA_DTYPE_BF16), (6, fa.FA_DTYPE_FP32), (0, fa.FA_DTYPE_BF16)):
         assert fa.lib().fa_fwd_workspace_size(_cfg(head_dim=d, dtype=dt).ref, ctypes.byref(n)) == fa.FA_ERR_PARAM_INVALID, d
+
+
+def test_modes_7_8_pse_rules():
+    # mode 7 takes no pse at all, mode 8 no pse tensor (the grad pages' sparse_mode=7/8 notes);
+    # mode 8's slopes need equal lengths except on a first sequence placed by start indices
+    cq, ck = [0, 5, 12], [0, 9, 16]
+    assert _fwd(_cfg(sparse_mode=7), slopes=FAKE) == fa.FA_ERR_PARAM_INVALID
+    assert _bwd(_cfg(sparse_mode=7), slopes=FAKE) == fa.FA_ERR_PARAM_INVALID
+    assert _fwd(_cfg(sparse_mode=8, cu_seqlens_q=cq, cu_seqlens_kv=ck), slopes=FAKE) == fa.FA_ERR_PARAM_INVALID
+    ok = _cfg(sparse_mode=8, cu_seqlens_q=cq, cu_seqlens_kv=ck, q_start_idx=4, kv_start_idx=0)
+    n = ctypes.c_uint64(0)
+    assert fa.lib().fa_fwd_workspace_size(ok.ref, ctypes.byref(n)) == fa.FA_OK
+    # ... but only the first sequence: a later one with Lq != Lkv still fails
+    bad = _cfg(sparse_mode=8, cu_seqlens_q=[0, 5, 12], cu_seqlens_kv=[0, 9, 17], q_start_idx=4, kv_start_idx=0)
+    assert _fwd(bad, slopes=FAKE) == fa.FA_ERR_PARAM_INVALID
+    pse = torch.zeros((1, 4, 7, 7))
+    for mode in (7, 8):
+        cfg = _cfg(sparse_mode=mode, dtype=fa.FA_DTYPE_FP32, pse=pse, pse_type=0)
+        assert fa.lib().fa_fwd_workspace_size(cfg.ref, ctypes.byref(n)) == fa.FA_ERR_PARAM_INVALID

@@ -6,7 +6,8 @@ import pytest
 import torch
 
 import workloads as wl
-from harness import TOL, compare, device_inputs, kv_heads_complete, run_gpu, run_oracle, say
+from harness import (TOL, compare, device_inputs, gpu_groups, kv_heads_complete, oracle_groups, run_gpu,
+                     run_oracle, say)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,6 +70,17 @@ EDGE_CASES = {
                                     pse=("row", True), pse_type=0, keep_prob=0.8, sink=True),
     "pse_compressed_causal": dict(lens_q=[1100, 300], head_num=2, kv_heads=2, head_dim=64, sparse_mode=3,
                                   pse=("compressed", False), pse_type=1),
+    # sparse modes 7 / 8: the band on the last / first sequence, a causal triangle on the others
+    "mode7_varlen_drop_sink": dict(lens_q=[200, 77, 300], lens_kv=[260, 77, 450], head_num=4, kv_heads=2,
+                                   head_dim=128, sparse_mode=7, pre_tokens=100, next_tokens=8, keep_prob=0.85,
+                                   sink=True),
+    # a chunk split off a 400-token sequence (rows 250..399 against keys 0..399), global alibi positions
+    "mode8_split_alibi_sink": dict(lens_q=[150, 129, 64], lens_kv=[400, 129, 64], head_num=4, kv_heads=1,
+                                   head_dim=128, sparse_mode=8, pre_tokens=180, next_tokens=0, alibi=True,
+                                   sink=True, q_start_idx=250, kv_start_idx=0),
+    "mode8_sqrt_d64_drop": dict(lens_q=[300, 40, 1], head_num=2, kv_heads=2, head_dim=64, sparse_mode=8,
+                                pre_tokens=64, next_tokens=16, alibi=True, pse_type=3, keep_prob=0.9,
+                                q_start_idx=1000, kv_start_idx=1000),
 }
 
 
@@ -94,14 +106,14 @@ def test_edge_case(name, dtype, deterministic):
     say(f"edge {name} dtype={dtype} det={deterministic} seed={seed} lens={list(case.lens_q)}/{list(case.lens_kv)}")
     gpu = run_gpu(case, deterministic)
     ref = run_oracle(case)
-    compare(gpu, ref, TOL[dtype])
+    compare(gpu, ref, TOL[dtype], case=case)
 
 
 @pytest.mark.parametrize("deterministic", [True, False])
 def test_workload1_fp32_full(deterministic):
     case = wl.make_workload(1)
     say(f"workload 1 full det={deterministic}")
-    compare(run_gpu(case, deterministic), run_oracle(case), TOL[F32])
+    compare(run_gpu(case, deterministic), run_oracle(case), TOL[F32], case=case)
 
 
 @pytest.fixture(scope="module")
@@ -109,14 +121,18 @@ def workload2():
     return wl.make_workload(2)
 
 
+@pytest.fixture(scope="module")
+def workload2_oracle(workload2):
+    # every sequence (lengths 1736, 630, 337, 701, 922, 1692, 994, 304) and every head
+    return oracle_groups(workload2, range(workload2.kv_heads))
+
+
 @pytest.mark.parametrize("deterministic", [True, False])
-def test_workload2_sampled_sequences(workload2, deterministic):
+def test_workload2_every_sequence(workload2, workload2_oracle, deterministic):
     case = workload2
-    batches = [2, 7, 1]   # lengths 337, 304, 630; every head
-    say(f"workload 2 det={deterministic} batches={batches}")
-    gpu = run_gpu(case, deterministic)
-    ref = run_oracle(case, batches=batches)
-    compare(gpu, ref, TOL[BF16])
+    say(f"workload 2 det={deterministic}: all {case.batch} sequences, all {case.head_num} heads")
+    gpu = gpu_groups(run_gpu(case, deterministic), case, range(case.kv_heads))
+    compare(gpu, workload2_oracle, TOL[BF16], case=case)
 
 
 def test_deterministic_is_bitwise_reproducible(workload2):
@@ -173,7 +189,7 @@ def test_workload3_sampled_heads(deterministic):
     say(f"workload 3 det={deterministic} batches={batches} heads={heads}")
     gpu = run_gpu(case, deterministic)
     ref = run_oracle(case, batches=batches, heads=heads)
-    compare(gpu, ref, TOL[BF16], kv_select=kv_heads_complete(case, heads))
+    compare(gpu, ref, TOL[BF16], kv_select=kv_heads_complete(case, heads), case=case)
 
 
 @pytest.mark.parametrize("deterministic", [True, False])
@@ -183,20 +199,37 @@ def test_workload4_sampled_heads(deterministic):
     say(f"workload 4 det={deterministic} batches={batches} heads={heads}")
     gpu = run_gpu(case, deterministic)
     ref = run_oracle(case, batches=batches, heads=heads)
-    compare(gpu, ref, TOL[BF16], kv_select=kv_heads_complete(case, heads))
+    compare(gpu, ref, TOL[BF16], kv_select=kv_heads_complete(case, heads), case=case)
 
 
-def test_workload5_sampled_sequences_and_dsink_identity():
-    case = wl.make_workload(5)
-    lens = case.lens_q
-    order = np.argsort(lens)
-    batches = [int(order[0]), int(order[1]), int(order[len(order) // 2])]
-    say(f"workload 5 batches={batches} lens={[int(lens[b]) for b in batches]}")
+@pytest.fixture(scope="module")
+def workload5():
+    say("generating workload 5")
+    return wl.make_workload(5)
+
+
+def test_workload5_kv_group_against_oracle(workload5):
+    # The timed workload in the benchmark's launch configuration; one whole kv group (8 query
+    # heads, all 64 sequences including the 16,384-token one) against the oracle: O, max, sum,
+    # dQ of the group's heads, dK/dV of its kv head, and dSink of its heads summed over every
+    # sequence.  The groups share every sequence and run the same kernel paths.
+    case = workload5
+    g = 3
+    G = case.head_num // case.kv_heads
+    heads = list(range(g * G, (g + 1) * G))
+    say(f"workload 5: kv group {g} (heads {heads[0]}-{heads[-1]}), all {case.batch} sequences, "
+        f"longest {int(case.lens_q.max())}")
+    gpu = run_gpu(case, True, heads=heads, kv_heads=[g])
+    ref = oracle_groups(case, [g])
+    compare(gpu, ref, TOL[BF16], case=case)
+
+
+def test_workload5_dsink_identity_every_head(workload5):
+    # dSink of all 64 heads: -sum_i exp(sink_h - m_i) / l_i * rowsum(dY * O) in fp64 from the
+    # device's own O, m, l (the group test above checks those, and dSink, against the oracle)
+    case = workload5
+    say("workload 5 dsink identity")
     gpu = run_gpu(case, True)
-    ref = run_oracle(case, batches=batches)
-    compare(gpu, ref, TOL[BF16], keys=("out", "m", "l", "dq", "dk", "dv"))
-    # dSink over the whole batch: -sum_i exp(sink_h - m_i) / l_i * rowsum(dY * O), from the
-    # device's own O, m, l (each checked against the oracle above) in fp64
     dy = case.dy.double().numpy()
     delta = np.einsum("tnd,tnd->tn", dy, gpu["out"])
     p_sink = np.exp(case.sink.astype(np.float64)[None, :] - gpu["m"]) / gpu["l"]
@@ -214,17 +247,20 @@ def test_workload4_fp16_sampled_heads(deterministic):
     say(f"workload 4 fp16 det={deterministic} batches={batches} heads={heads}")
     gpu = run_gpu(case, deterministic)
     ref = run_oracle(case, batches=batches, heads=heads)
-    compare(gpu, ref, TOL[F16], kv_select=kv_heads_complete(case, heads))
+    compare(gpu, ref, TOL[F16], kv_select=kv_heads_complete(case, heads), case=case)
 
 
-def test_workload5_fp16_sampled_sequences():
-    # the timed workload in fp16, in the launch configuration the benchmark times
+def test_workload5_fp16_longest_shortest_median():
+    # the timed workload in fp16, in the launch configuration the benchmark times: kv group 6
+    # on the longest (16,384), shortest and median sequences against the oracle
     case = wl.make_workload(5, F16)
     lens = case.lens_q
     order = np.argsort(lens)
-    batches = [int(order[0]), int(order[len(order) // 3]), int(order[len(order) // 2])]
-    say(f"workload 5 fp16 batches={batches} lens={[int(lens[b]) for b in batches]}")
-    gpu = run_gpu(case, True)
-    ref = run_oracle(case, batches=batches)
-    # dSink sums over every sequence: the sampled oracle run covers only three
-    compare(gpu, ref, TOL[F16], keys=("out", "m", "l", "dq", "dk", "dv"))
+    batches = [int(order[-1]), int(order[0]), int(order[len(order) // 2])]
+    g = 6
+    G = case.head_num // case.kv_heads
+    say(f"workload 5 fp16 group {g} batches={batches} lens={[int(lens[b]) for b in batches]}")
+    gpu = run_gpu(case, True, heads=list(range(g * G, (g + 1) * G)), kv_heads=[g])
+    ref = oracle_groups(case, [g], batches=batches)
+    # dSink sums over every sequence: the three chosen ones do not make it
+    compare(gpu, ref, TOL[F16], keys=("out", "m", "l", "dq", "dk", "dv"), case=case)

@@ -673,3 +673,101 @@ def test_subset_selection_matches_full_run():
     for a, b in ((full[1], sub[1]), (full[2], sub[2])):
         np.testing.assert_array_equal(b[rows][:, 1], a[rows][:, 1])
         assert np.all(np.isnan(b[rows][:, 0]))
+
+
+def test_row_blocks_match_the_whole_block():
+    # row-chunked materialisation (used for the long sequences of the parity tests) is the
+    # same computation: rows stand alone in the forward and in dQ, and dK, dV, dSink only
+    # add the same terms in another order
+    c = wl.make_case("rows", [37, 200, 129], head_num=4, kv_heads=2, head_dim=64, dtype=torch.float32,
+                     sparse_mode=3, keep_prob=0.8, alibi=True, sink=True, seed=3)
+    kw = dict(keep_prob=c.keep_prob, sparse_mode=3, drop_mask=c.drop_mask, alibi_slopes=c.alibi_slopes,
+              sink=c.sink)
+    a = [x.float().numpy() for x in (c.q, c.k, c.v)]
+    args = (c.cu_seqlens_q, c.cu_seqlens_kv, 4, 2, c.scale)
+    whole = oracle.forward(*a, *args, **kw) + oracle.backward(*a, c.dy.float().numpy(), *args, **kw)
+    parts = (oracle.forward(*a, *args, row_block=50, **kw) +
+             oracle.backward(*a, c.dy.float().numpy(), *args, row_block=50, **kw))
+    for x, y in zip(whole, parts):
+        np.testing.assert_allclose(y, x, rtol=1e-13, atol=1e-14)
+
+
+# --------------------------------------------------------------------------- sparse modes 7 and 8
+
+def _run(q, k, v, dy, lq, lkv, nq, nkv, scale, **kw):
+    cq, ck = _cu(lq), _cu(lkv)
+    return (oracle.forward(q, k, v, cq, ck, nq, nkv, scale, **kw) +
+            oracle.backward(q, k, v, dy, cq, ck, nq, nkv, scale, **kw))
+
+
+@pytest.mark.parametrize("mode", [7, 8])
+def test_modes_7_8_are_band_plus_causal_per_sequence(mode):
+    # mode 7: the last sequence takes the band, the others rightDownCausal; mode 8: the first
+    # takes the band, the others leftUpCausal -- each compared with a one-sequence run of the
+    # already pinned mode (rectangular sequences, so the two causal alignments differ)
+    lq, lkv = [13, 9, 17], [16, 9, 21]
+    nq, nkv, d, pre, nxt = 4, 2, 8, 5, 2
+    tq, tkv = sum(lq), sum(lkv)
+    q, k, v, dy = _rand(80, tq, nq, d), _rand(81, tkv, nkv, d), _rand(82, tkv, nkv, d), _rand(83, tq, nq, d)
+    sink = np.array([0.2, -0.5, 1.0, 0.0], np.float32)
+    got = _run(q, k, v, dy, lq, lkv, nq, nkv, 0.4, sparse_mode=mode, pre_tokens=pre, next_tokens=nxt, sink=sink)
+    cq, ck = _cu(lq), _cu(lkv)
+    for b in range(3):
+        want_mode = {7: 4 if b == 2 else 3, 8: 4 if b == 0 else 2}[mode]
+        assert oracle.sequence_mode(mode, b, 3) == want_mode
+        sl_q, sl_k = slice(cq[b], cq[b + 1]), slice(ck[b], ck[b + 1])
+        one = _run(q[sl_q], k[sl_k], v[sl_k], dy[sl_q], [lq[b]], [lkv[b]], nq, nkv, 0.4, sparse_mode=want_mode,
+                   pre_tokens=pre, next_tokens=nxt, sink=sink)
+        for x, y in zip(got[:4], one[:4]):      # O, max, sum, dQ
+            np.testing.assert_allclose(x[sl_q], y, rtol=1e-13, atol=1e-14)
+        for x, y in zip(got[4:6], one[4:6]):    # dK, dV
+            np.testing.assert_allclose(x[sl_k], y, rtol=1e-13, atol=1e-14)
+
+
+@pytest.mark.parametrize("pse_type", [2, 3])
+def test_mode8_split_rows_reproduce_the_unsplit_band(pse_type):
+    # A long band sequence split outside the operator in the query direction: chunk A holds rows
+    # [0, a) with keys [0, a), chunk B rows [a, L) with every key [0, L) (qStartIdx = a,
+    # kvStartIdx = 0, so Lq - Lkv + qStartIdx - kvStartIdx = 0).  Each chunk runs as the first
+    # sequence of a mode-8 call (a complete leftUpCausal sequence follows), with the generated
+    # pse on global positions.  Rows and row sums must equal the unsplit mode-4 run (itself
+    # pinned against SDPA and autograd); the chunks' dK, dV and dSink add up to the unsplit ones.
+    L, a, other = 37, 20, 11
+    nq, d, pre, nxt = 2, 8, 9, 0
+    q, k, v, dy = _rand(90, L, nq, d), _rand(91, L, 1, d), _rand(92, L, 1, d), _rand(93, L, nq, d)
+    qo, ko, vo, dyo = _rand(94, other, nq, d), _rand(95, other, 1, d), _rand(96, other, 1, d), _rand(97, other, nq, d)
+    slopes = np.array([0.3, 0.05], np.float32)
+    sink = np.array([-0.4, 0.7], np.float32)
+    kw = dict(pre_tokens=pre, next_tokens=nxt, alibi_slopes=slopes, pse_type=pse_type, sink=sink)
+    whole = _run(q, k, v, dy, [L], [L], nq, 1, 0.35, sparse_mode=4, **kw)
+    chunks = {}
+    for name, rows, keys, qs in (("A", slice(0, a), slice(0, a), 0), ("B", slice(a, L), slice(0, L), a)):
+        nr, nk = rows.stop - rows.start, keys.stop - keys.start
+        cat = lambda x, y: np.concatenate([x, y])
+        chunks[name] = _run(cat(q[rows], qo), cat(k[keys], ko), cat(v[keys], vo), cat(dy[rows], dyo),
+                            [nr, other], [nk, other], nq, 1, 0.35, sparse_mode=8, q_start_idx=qs,
+                            kv_start_idx=0, **kw)
+    A, B = chunks["A"], chunks["B"]
+    for i in range(4):                          # O, max, sum, dQ rows
+        np.testing.assert_allclose(A[i][:a], whole[i][:a], rtol=1e-12, atol=1e-13)
+        np.testing.assert_allclose(B[i][:L - a], whole[i][a:], rtol=1e-12, atol=1e-13)
+    for i in (4, 5):                            # dK, dV of the split sequence's keys
+        summed = B[i][:L].copy()
+        summed[:a] += A[i][:a]
+        np.testing.assert_allclose(summed, whole[i], rtol=1e-12, atol=1e-13)
+    # dSink: the chunks' own rows (the sequence after each chunk is identical in both calls)
+    ds_other = _run(qo, ko, vo, dyo, [other], [other], nq, 1, 0.35, sparse_mode=2, sink=sink,
+                    alibi_slopes=slopes, pse_type=pse_type)[6]
+    np.testing.assert_allclose(A[6] + B[6] - 2 * ds_other, whole[6], rtol=1e-12, atol=1e-13)
+
+
+def test_mode8_start_indices_shift_only_the_pse():
+    # with equal start indices the global positions differ from the local ones by the same
+    # amount on both sides, so every pseType 2 / 3 bias (a function of i - j) is unchanged
+    lq = [24, 10]
+    q, k, v, dy = _rand(100, 34, 2, 8), _rand(101, 34, 1, 8), _rand(102, 34, 1, 8), _rand(103, 34, 2, 8)
+    kw = dict(sparse_mode=8, pre_tokens=6, next_tokens=3, alibi_slopes=np.array([0.2, 0.1], np.float32))
+    base = _run(q, k, v, dy, lq, lq, 2, 1, 0.3, **kw)
+    moved = _run(q, k, v, dy, lq, lq, 2, 1, 0.3, q_start_idx=500, kv_start_idx=500, **kw)
+    for x, y in zip(base[:6], moved[:6]):
+        np.testing.assert_allclose(y, x, rtol=1e-13, atol=1e-14)

@@ -36,6 +36,8 @@ MODE_RIGHT_DOWN_CAUSAL = 3
 MODE_BAND = 4
 MODE_PREFIX = 6
 MODE_ALL_MASK = 1
+MODE_RIGHT_DOWN_CAUSAL_BAND = 7
+MODE_BAND_LEFT_UP_CAUSAL = 8
 
 
 @dataclass
@@ -64,6 +66,8 @@ class Case:
     sink: Optional[np.ndarray] = None          # float32 [Nq]
     prefix: Optional[np.ndarray] = None        # int64 [B]: prefix N per sequence (sparse mode 6)
     atten_mask: Optional[np.ndarray] = None    # uint8 [S1Max, S2Max], nonzero = masked (modes 0/1/4)
+    q_start_idx: Optional[int] = None          # mode 8: first sequence's row / key offsets in its unsplit
+    kv_start_idx: Optional[int] = None         # sequence (qStartIdx / kvStartIdx)
     meta: dict = field(default_factory=dict)
 
     @property
@@ -156,7 +160,7 @@ def make_case(name, lens_q, lens_kv=None, *, head_num, kv_heads, head_dim, dtype
               scale=None, keep_prob=1.0, sparse_mode=MODE_NONE, pre_tokens=INT_MAX_TOKENS,
               next_tokens=INT_MAX_TOKENS, alibi=False, sink=False, seed=0, dy_mult=1.0,
               drop_mask=None, prefix=None, atten_mask=None, pse_type=2, slopes_per_batch=False,
-              pse=None) -> Case:
+              pse=None, q_start_idx=None, kv_start_idx=None) -> Case:
     """A case built from explicit lengths; every tensor is drawn from default_rng([seed, t]).
     alibi=True adds generated-pse slopes ([Nq], or [B, Nq] with slopes_per_batch) of pseType pse_type.
     pse=(form, shared) adds an external pse of pseType pse_type (0 or 1) drawn from
@@ -191,7 +195,8 @@ def make_case(name, lens_q, lens_kv=None, *, head_num, kv_heads, head_dim, dtype
                 next_tokens=int(next_tokens), drop_mask=drop_mask,
                 alibi_slopes=slopes, pse_type=int(pse_type), pse=pse_t, sink=sink_v,
                 prefix=None if prefix is None else np.asarray(prefix, dtype=np.int64),
-                atten_mask=None if atten_mask is None else np.ascontiguousarray(atten_mask, dtype=np.uint8))
+                atten_mask=None if atten_mask is None else np.ascontiguousarray(atten_mask, dtype=np.uint8),
+                q_start_idx=q_start_idx, kv_start_idx=kv_start_idx)
 
 
 def random_atten_mask(seed, rows: int, cols: int, p_masked: float, full_rows=()) -> np.ndarray:
