@@ -22,6 +22,8 @@ FA_ERR_PARAM_NULLPTR = 161001
 FA_ERR_PARAM_INVALID = 161002
 FA_ERR_WORKSPACE = 1
 FA_ERR_HIP = 2
+FA_ERR_SCRATCH = 3
+FA_DECODE_NOALLOC_SCRATCH_BYTES = 32 << 20
 
 FA_DTYPE_FP32 = 0
 FA_DTYPE_BF16 = 1
@@ -38,7 +40,7 @@ FA_LAYOUT_SBH = 4
 
 EXPORTED = ("fa_fwd_workspace_size", "fa_fwd", "fa_bwd_workspace_size", "fa_bwd", "fa_status_string",
             "fa_debug_schedule", "fa_profile_enable", "fa_profile_read", "fa_profile_kernel_count",
-            "fa_decode_workspace_size", "fa_decode")
+            "fa_decode_workspace_size", "fa_decode", "fa_decode_noalloc")
 
 
 class FaConfig(ctypes.Structure):
@@ -123,8 +125,10 @@ def lib() -> ctypes.CDLL:
         decp = ctypes.POINTER(FaDecodeConfig)
         L.fa_decode_workspace_size.argtypes = [decp, u64p]
         L.fa_decode.argtypes = [decp, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
+        L.fa_decode_noalloc.argtypes = [decp, vp, vp, vp, vp, vp]
         for name in ("fa_fwd_workspace_size", "fa_bwd_workspace_size", "fa_fwd", "fa_bwd", "fa_debug_schedule",
-                     "fa_profile_enable", "fa_profile_read", "fa_decode_workspace_size", "fa_decode"):
+                     "fa_profile_enable", "fa_profile_read", "fa_decode_workspace_size", "fa_decode",
+                     "fa_decode_noalloc"):
             getattr(L, name).restype = ctypes.c_int32
         _lib = L
     return _lib
@@ -439,6 +443,17 @@ def _decode_checks(cfg: DecodeConfig, q, k, v, out):
         out = torch.empty_like(q)
     _check_tensor("out", out, tuple(q.shape), q.dtype, dev)
     return dev, out
+
+
+def fa_decode_noalloc(cfg: DecodeConfig, q, k, v, out):
+    """Allocation-free decode through libfa.so on the current stream: the library's static
+    scratch replaces the workspace, and `out` must be given (nothing is allocated)."""
+    if out is None:
+        raise ValueError("fa_decode_noalloc writes into a caller-owned out tensor")
+    dev, out = _decode_checks(cfg, q, k, v, out)
+    _check(lib().fa_decode_noalloc(cfg.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(out), _stream_handle(dev)),
+           "fa_decode_noalloc")
+    return out
 
 
 def fa_decode(cfg: DecodeConfig, q, k, v, out=None, workspace=None):

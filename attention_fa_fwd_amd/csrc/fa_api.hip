@@ -14,6 +14,14 @@
 #include "fa_kernels.h"
 #include "fa_sched.h"
 
+// Device scratch of fa_decode_noalloc: a file-scope array, so that entry point
+// allocates nothing.  Every GPU the library runs on holds its own copy for the
+// life of the process.  In host code `fa_noalloc_scratch` names a host-side
+// stand-in, never the device memory: host code uses the address that
+// hipGetSymbolAddress returns for the current device (noalloc_scratch below).
+static constexpr uint64_t kNoallocScratchBytes = FA_DECODE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char fa_noalloc_scratch[kNoallocScratchBytes];
+
 namespace {
 
 using fa::WorkItem;
@@ -619,6 +627,27 @@ DecPlan plan_decode(const DecProblem& pr) {
   return P;
 }
 
+// Address of the current device's copy of fa_noalloc_scratch, looked up once per
+// device with that device current (the first fa_decode_noalloc call on it).
+hipError_t noalloc_scratch(char** out) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static char* ptr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> g(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(fa_noalloc_scratch));
+    if (e != hipSuccess) return e;
+    ptr[dev] = static_cast<char*>(p);
+  }
+  *out = ptr[dev];
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -630,6 +659,8 @@ const char* fa_status_string(fa_status s) {
     case FA_ERR_PARAM_INVALID: return "FA_ERR_PARAM_INVALID: unsupported attribute, shape, dtype or alignment";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace smaller than the size query returned";
     case FA_ERR_HIP: return "FA_ERR_HIP: a HIP runtime call or kernel launch failed";
+    case FA_ERR_SCRATCH:
+      return "FA_ERR_SCRATCH: the call needs more scratch than the allocation-free entry point's static buffer holds";
     default: return "unknown fa_status";
   }
 }
@@ -915,6 +946,20 @@ fa_status fa_decode(const fa_decode_config* cfg, const void* q, const void* k, c
   const DecPlan P = plan_decode(pr);
   if (workspace_bytes < P.total) return FA_ERR_WORKSPACE;
   return decode_run(pr, P, q, k, v, out, reinterpret_cast<char*>(workspace), reinterpret_cast<hipStream_t>(stream));
+}
+
+fa_status fa_decode_noalloc(const fa_decode_config* cfg, const void* q, const void* k, const void* v, void* out,
+                            void* stream) {
+  DecProblem pr;
+  fa_status st = parse_decode(cfg, &pr);
+  if (st != FA_OK) return st;
+  if (!q || !k || !v || !out) return FA_ERR_PARAM_NULLPTR;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FA_ERR_PARAM_INVALID;
+  const DecPlan P = plan_decode(pr);
+  if (P.total > kNoallocScratchBytes) return FA_ERR_SCRATCH;
+  char* ws = nullptr;
+  if (noalloc_scratch(&ws) != hipSuccess) return FA_ERR_HIP;
+  return decode_run(pr, P, q, k, v, out, ws, reinterpret_cast<hipStream_t>(stream));
 }
 
 fa_status fa_profile_enable(int32_t on) {

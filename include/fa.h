@@ -50,6 +50,8 @@ typedef int32_t fa_status;
 #define FA_ERR_PARAM_INVALID 161002 /* an attribute, shape, dtype or alignment is unsupported */
 #define FA_ERR_WORKSPACE 1          /* workspace_bytes smaller than the size query returned */
 #define FA_ERR_HIP 2                /* a HIP runtime call or kernel launch failed */
+#define FA_ERR_SCRATCH 3            /* fa_decode_noalloc: the call needs more scratch than its
+                                       static buffer holds (FA_DECODE_NOALLOC_SCRATCH_BYTES) */
 
 /* element type of Q, K, V, dY, O, dQ, dK, dV (the pages list FLOAT16, BFLOAT16 and
    FLOAT32 for these tensors: aclnnFlashAttentionUnpaddingScoreGrad, parameter table).
@@ -265,6 +267,23 @@ fa_status fa_decode_workspace_size(const fa_decode_config* cfg, uint64_t* bytes)
  */
 fa_status fa_decode(const fa_decode_config* cfg, const void* q, const void* k, const void* v, void* out,
                     void* workspace, uint64_t workspace_bytes, void* stream);
+
+/*
+ * Allocation-free decode, for callers that cannot allocate device memory or
+ * hand over a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same operation, arguments, kernels and
+ * results as fa_decode, but the scratch (the staged work plan and the split
+ * partial results) lives in a static device buffer of
+ * FA_DECODE_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs
+ * on until the process ends; the call allocates nothing.  A configuration whose
+ * scratch (fa_decode_workspace_size) exceeds that size returns FA_ERR_SCRATCH
+ * before anything is enqueued.  Every call on one GPU shares that GPU's buffer:
+ * calls that may overlap on one GPU (different streams, or host threads) race,
+ * so order them on one stream.  Errors otherwise as fa_decode.
+ */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES (32ull << 20)
+fa_status fa_decode_noalloc(const fa_decode_config* cfg, const void* q, const void* k, const void* v, void* out,
+                            void* stream);
 
 /* Static text for a status code. */
 const char* fa_status_string(fa_status status);
