@@ -72,6 +72,7 @@ class FaConfig(ctypes.Structure):
         ("strides", ctypes.POINTER(ctypes.c_int64)),
         ("q_start_idx", ctypes.POINTER(ctypes.c_int64)),
         ("kv_start_idx", ctypes.POINTER(ctypes.c_int64)),
+        ("v_head_dim", ctypes.c_int64),
     ]
 
 
@@ -144,7 +145,7 @@ class Config:
     def __init__(self, cu_seqlens_q, cu_seqlens_kv, head_num, kv_heads, head_dim, dtype, scale, keep_prob=1.0,
                  sparse_mode=0, pre_tokens=TOKENS_DEFAULT, next_tokens=TOKENS_DEFAULT, deterministic=True,
                  prefix=None, atten_mask=None, pse_type=2, slopes_per_batch=False, layout="TND", pse=None,
-                 atomic_dq=False, q_start_idx=None, kv_start_idx=None):
+                 atomic_dq=False, q_start_idx=None, kv_start_idx=None, v_head_dim=None):
         self.cu_q = np.ascontiguousarray(np.asarray(cu_seqlens_q, dtype=np.int64))
         self.cu_kv = np.ascontiguousarray(np.asarray(cu_seqlens_kv, dtype=np.int64))
         # per-sequence prefix N of sparse mode 6 (prefixOptional); NULL when None
@@ -196,7 +197,8 @@ class Config:
             pse_type=(int(pse_type) if pse is not None else 0),
             q_start_idx=(None if self.q_start is None else self.q_start.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))),
             kv_start_idx=(None if self.kv_start is None else
-                          self.kv_start.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))))
+                          self.kv_start.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))),
+            v_head_dim=0 if v_head_dim is None else int(v_head_dim))
 
     @property
     def ref(self):
@@ -234,6 +236,12 @@ def _check_tensor(name, t, shape, dtype, device, strided=False):
 
 
 _SLOTS = ("q", "k", "v", "dy", "out", "dq", "dk", "dv")
+_VALUE_SIDE = ("v", "dy", "out", "dv")
+
+
+def head_dims(cfg: "Config"):
+    """(head dim of q, k, dq, dk; head dim of v, out, dy, dv)."""
+    return cfg.c.head_dim, cfg.c.v_head_dim or cfg.c.head_dim
 
 
 def _set_strides(cfg: "Config", tensors: dict):
@@ -245,8 +253,9 @@ def _set_strides(cfg: "Config", tensors: dict):
     for name in _SLOTS:
         t = tensors.get(name)
         n = cfg.c.head_num if name in ("q", "dy", "out", "dq") else (cfg.c.num_kv_heads or cfg.c.head_num)
-        st = (n * cfg.c.head_dim, cfg.c.head_dim) if t is None else (t.stride(0), t.stride(1))
-        packed = packed and st == (n * cfg.c.head_dim, cfg.c.head_dim)
+        d = head_dims(cfg)[1 if name in _VALUE_SIDE else 0]
+        st = (n * d, d) if t is None else (t.stride(0), t.stride(1))
+        packed = packed and st == (n * d, d)
         vals += list(st)
     if packed:
         cfg.c.strides = None
@@ -273,11 +282,12 @@ def _workspace(nbytes: int, device, workspace: Optional[torch.Tensor]) -> torch.
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
 
 
-def layout_shape(cfg: Config, q_side: bool):
-    """Shape of a query-side (q, dy, out, dq) or key-side (k, v, dk, dv) tensor in cfg's layout."""
+def layout_shape(cfg: Config, q_side: bool, value: bool = False):
+    """Shape of a query-side (q, dy, out, dq) or key-side (k, v, dk, dv) tensor in cfg's layout;
+    value=True for the value-side tensors (v, out, dy, dv), whose head dim may be smaller."""
     n = cfg.c.head_num if q_side else (cfg.c.num_kv_heads or cfg.c.head_num)
     cu = cfg.cu_q if q_side else cfg.cu_kv
-    d, t, b = cfg.c.head_dim, int(cu[-1]), len(cu) - 1
+    d, t, b = head_dims(cfg)[1 if value else 0], int(cu[-1]), len(cu) - 1
     s = int(cu[1]) if b > 0 else 0
     return {"TND": (t, n, d), "BSND": (b, s, n, d), "BSH": (b, s, n * d), "BNSD": (b, n, s, d),
             "SBH": (s, b, n * d)}[cfg.layout_name]
@@ -292,7 +302,7 @@ def _common_checks(q, k, v, cfg: Config):
     tnd = cfg.layout_name == "TND"
     _check_tensor("q", q, layout_shape(cfg, True), q.dtype, dev, tnd)
     _check_tensor("k", k, layout_shape(cfg, False), q.dtype, dev, tnd)
-    _check_tensor("v", v, layout_shape(cfg, False), q.dtype, dev, tnd)
+    _check_tensor("v", v, layout_shape(cfg, False, True), q.dtype, dev, tnd)
     return dev, tq, tkv, nq, nkv, d
 
 
@@ -309,12 +319,12 @@ def fa_fwd(cfg: Config, q, k, v, drop_mask=None, alibi_slopes=None, sink=None, o
     """Forward through libfa.so on the current stream; returns (out, softmax_max, softmax_sum)."""
     dev, tq, tkv, nq, nkv, d = _common_checks(q, k, v, cfg)
     if out is None:
-        out = torch.empty(layout_shape(cfg, True), dtype=q.dtype, device=dev)
+        out = torch.empty(layout_shape(cfg, True, True), dtype=q.dtype, device=dev)
     if softmax_max is None:
         softmax_max = torch.empty((tq, nq), dtype=torch.float32, device=dev)
     if softmax_sum is None:
         softmax_sum = torch.empty((tq, nq), dtype=torch.float32, device=dev)
-    _check_tensor("out", out, layout_shape(cfg, True), q.dtype, dev, cfg.layout_name == "TND")
+    _check_tensor("out", out, layout_shape(cfg, True, True), q.dtype, dev, cfg.layout_name == "TND")
     _check_tensor("softmax_max", softmax_max, (tq, nq), torch.float32, dev)
     _check_tensor("softmax_sum", softmax_sum, (tq, nq), torch.float32, dev)
     _check_slopes_sink(cfg, alibi_slopes, sink, nq, dev)
@@ -333,8 +343,8 @@ def fa_bwd(cfg: Config, q, k, v, dy, out, softmax_max, softmax_sum, drop_mask=No
            dq=None, dk=None, dv=None, dsink=None, workspace=None):
     """Backward through libfa.so on the current stream; returns (dq, dk, dv, dsink or None)."""
     dev, tq, tkv, nq, nkv, d = _common_checks(q, k, v, cfg)
-    _check_tensor("dy", dy, layout_shape(cfg, True), q.dtype, dev, cfg.layout_name == "TND")
-    _check_tensor("out", out, layout_shape(cfg, True), q.dtype, dev, cfg.layout_name == "TND")
+    _check_tensor("dy", dy, layout_shape(cfg, True, True), q.dtype, dev, cfg.layout_name == "TND")
+    _check_tensor("out", out, layout_shape(cfg, True, True), q.dtype, dev, cfg.layout_name == "TND")
     _check_tensor("softmax_max", softmax_max, (tq, nq), torch.float32, dev)
     _check_tensor("softmax_sum", softmax_sum, (tq, nq), torch.float32, dev)
     _check_slopes_sink(cfg, alibi_slopes, sink, nq, dev)
@@ -343,13 +353,13 @@ def fa_bwd(cfg: Config, q, k, v, dy, out, softmax_max, softmax_sum, drop_mask=No
     if dk is None:
         dk = torch.empty(layout_shape(cfg, False), dtype=q.dtype, device=dev)
     if dv is None:
-        dv = torch.empty(layout_shape(cfg, False), dtype=q.dtype, device=dev)
+        dv = torch.empty(layout_shape(cfg, False, True), dtype=q.dtype, device=dev)
     if sink is not None and dsink is None:
         dsink = torch.empty((nq,), dtype=torch.float32, device=dev)
     tnd = cfg.layout_name == "TND"
     _check_tensor("dq", dq, layout_shape(cfg, True), q.dtype, dev, tnd)
     _check_tensor("dk", dk, layout_shape(cfg, False), q.dtype, dev, tnd)
-    _check_tensor("dv", dv, layout_shape(cfg, False), q.dtype, dev, tnd)
+    _check_tensor("dv", dv, layout_shape(cfg, False, True), q.dtype, dev, tnd)
     _set_strides(cfg, dict(q=q, k=k, v=v, dy=dy, out=out, dq=dq, dk=dk, dv=dv))
     ws = _workspace(fa_bwd_workspace_size(cfg), dev, workspace)
     st = lib().fa_bwd(cfg.ref, _ptr(q), _ptr(k), _ptr(v), _ptr(dy), _ptr(out), _ptr(softmax_max),

@@ -33,7 +33,8 @@ constexpr int64_t kMaxPrefixBatch = 1024;          // B limit with prefixOptiona
 
 struct Problem {
   int64_t batch = 0, nq = 0, nkv = 0, d = 0, tq = 0, tkv = 0;
-  int64_t du = 0;                  // the tensors' head dim; d is the kernels' (64 or 128, du <= d)
+  int64_t du = 0;                  // head dim of Q, K, dQ, dK; d is the kernels' (64 or 128, du <= d)
+  int64_t dvu = 0;                 // head dim of V, O, dY, dV (<= du)
   int dtype = 0, mode = 0;
   double scale = 0, keep = 1;
   int64_t pre = 0, next = 0;
@@ -63,10 +64,14 @@ static_assert(fa::kLayoutBNSD == FA_LAYOUT_BNSD && fa::kLayoutSBH == FA_LAYOUT_S
 enum TensorId { T_Q = 0, T_K, T_V, T_DY, T_O, T_DQ, T_DK, T_DV };
 bool layout_copies(const Problem& pr) { return pr.layout == FA_LAYOUT_BNSD || pr.layout == FA_LAYOUT_SBH; }
 // tensor `id` goes through a packed TND copy in the workspace
-bool copied(const Problem& pr, int id) { return layout_copies(pr) || pr.strided[id] || pr.du != pr.d; }
+// head dim of tensor `id`: the value side (V, O, dY, dV) may be narrower than Q and K
+int64_t dim_of(const Problem& pr, int id) {
+  return (id == T_V || id == T_O || id == T_DY || id == T_DV) ? pr.dvu : pr.du;
+}
+bool copied(const Problem& pr, int id) { return layout_copies(pr) || pr.strided[id] || dim_of(pr, id) != pr.d; }
 // any tensor does (the workspace then holds copies of all eight)
 bool relayout(const Problem& pr) {
-  if (layout_copies(pr) || pr.du != pr.d) return true;
+  if (layout_copies(pr) || pr.du != pr.d || pr.dvu != pr.d) return true;
   for (bool st : pr.strided)
     if (st) return true;
   return false;
@@ -87,6 +92,9 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   // head dims go through copies zero-padded to the next of them
   const int64_t ebytes = cfg->dtype == FA_DTYPE_FP32 ? 4 : 2;
   if (cfg->head_dim < 1 || cfg->head_dim > 128 || (cfg->head_dim * ebytes) % 16 != 0) return FA_ERR_PARAM_INVALID;
+  // the value head dim may be smaller (grad page, Constraints: qD == kD >= vD); 0 = the same
+  const int64_t vdim = cfg->v_head_dim == 0 ? cfg->head_dim : cfg->v_head_dim;
+  if (vdim < 1 || vdim > cfg->head_dim || (vdim * ebytes) % 16 != 0) return FA_ERR_PARAM_INVALID;
   const int mode = cfg->sparse_mode;
   if (mode != FA_SPARSE_NONE && mode != FA_SPARSE_ALL_MASK && mode != FA_SPARSE_LEFT_UP_CAUSAL &&
       mode != FA_SPARSE_RIGHT_DOWN_CAUSAL && mode != FA_SPARSE_BAND && mode != FA_SPARSE_PREFIX &&
@@ -112,6 +120,7 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   pr->nq = cfg->head_num;
   pr->nkv = nkv;
   pr->du = cfg->head_dim;
+  pr->dvu = vdim;
   pr->d = cfg->head_dim <= 64 ? 64 : 128;
   pr->dtype = cfg->dtype;
   pr->mode = mode;
@@ -200,8 +209,8 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   if (cfg->layout < FA_LAYOUT_TND || cfg->layout > FA_LAYOUT_SBH) return FA_ERR_PARAM_INVALID;
   for (int id = 0; id < 8; ++id) {   // packed TND strides unless given
     const int64_t n = (id == T_K || id == T_V || id == T_DK || id == T_DV) ? nkv : cfg->head_num;
-    pr->ts[id] = n * cfg->head_dim;
-    pr->hs[id] = cfg->head_dim;
+    pr->ts[id] = n * dim_of(*pr, id);
+    pr->hs[id] = dim_of(*pr, id);
   }
   if (cfg->strides) {
     if (cfg->layout != FA_LAYOUT_TND) return FA_ERR_PARAM_INVALID;
@@ -215,7 +224,7 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
       if (output && (t == 0 || (h == 0 && n > 1))) return FA_ERR_PARAM_INVALID;
       pr->ts[id] = t;
       pr->hs[id] = h;
-      pr->strided[id] = !(t == n * cfg->head_dim && h == cfg->head_dim);
+      pr->strided[id] = !(t == n * dim_of(*pr, id) && h == dim_of(*pr, id));
     }
   }
   pr->layout = cfg->layout;
@@ -475,9 +484,10 @@ hipError_t relayout_tensor(const Problem& pr, int id, const void* src, void* dst
   const bool q_side = !(id == T_K || id == T_V || id == T_DK || id == T_DV);
   return timed(K_RELAYOUT, s, [&] {
     if (!layout_copies(pr))
-      return fa::launch_relayout(src, dst, 1, q_side ? pr.tq : pr.tkv, q_side ? pr.nq : pr.nkv, pr.du, pr.d,
+      return fa::launch_relayout(src, dst, 1, q_side ? pr.tq : pr.tkv, q_side ? pr.nq : pr.nkv, dim_of(pr, id), pr.d,
                                  (int)elem_bytes(pr), fa::kLayoutStrided, to_tnd, s, pr.ts[id], pr.hs[id]);
-    return fa::launch_relayout(src, dst, pr.batch, q_side ? pr.sq : pr.skv, q_side ? pr.nq : pr.nkv, pr.du, pr.d,
+    return fa::launch_relayout(src, dst, pr.batch, q_side ? pr.sq : pr.skv, q_side ? pr.nq : pr.nkv, dim_of(pr, id),
+                               pr.d,
                                (int)elem_bytes(pr), pr.layout, to_tnd, s);
   });
 }

@@ -181,6 +181,10 @@ typedef struct fa_config {
                                     -> FA_ERR_PARAM_INVALID.  NULL = 0.                       */
   const int64_t* kv_start_idx;   /* HOST, optional, one value (kvStartIdxOptional): as above
                                     for the first sequence's keys.  NULL = 0.                  */
+  int64_t v_head_dim;            /* head dim of V, O, dY and dV when it is smaller than
+                                    head_dim (the grad page, Constraints: qD == kD >= vD);
+                                    0 = head_dim.  Same 16-byte row rule as head_dim; Q, K,
+                                    dQ, dK keep head_dim.  Runs on zero-padded copies.         */
 } fa_config;
 
 /* Device workspace bytes needed by fa_fwd for this configuration (>= 256). */

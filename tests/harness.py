@@ -31,7 +31,8 @@ def config_of(case: wl.Case, deterministic: bool = True, mask=None, pse=None) ->
                      case.dtype, case.scale, case.keep_prob, case.sparse_mode, case.pre_tokens,
                      case.next_tokens, deterministic, prefix=case.prefix, atten_mask=mask, pse_type=case.pse_type,
                      slopes_per_batch=case.alibi_slopes is not None and case.alibi_slopes.ndim == 2, pse=pse,
-                     atomic_dq=not deterministic, q_start_idx=case.q_start_idx, kv_start_idx=case.kv_start_idx)
+                     atomic_dq=not deterministic, q_start_idx=case.q_start_idx, kv_start_idx=case.kv_start_idx,
+                     v_head_dim=case.v.shape[2] if case.v.shape[2] != case.head_dim else None)
 
 
 def device_inputs(case: wl.Case, device="cuda"):
@@ -286,13 +287,15 @@ def block_errors(got: np.ndarray, ref: np.ndarray, cu: np.ndarray):
 
 
 def compare_blocks(gpu: dict, ref: dict, tol: float, case: wl.Case, keys=("out", "m", "l", "dq", "dk", "dv"),
-                   floor: float = 0.1):
-    """Per-(sequence, head) check beside the whole-tensor one: every block's error must be
-    within tol of its own reference norm, where a block whose RMS is below `floor` times the
-    tensor's RMS is held to tol of that floor instead (a block of near-zero gradients would
-    otherwise turn rounding into a large relative error).  A wrong wave block (32 rows of
-    one head) has an error of the order of its own norm and fails.  Prints the worst block of
-    each tensor; raises AssertionError listing the blocks above the bound."""
+                   floor: float = 1.0):
+    """Per-(sequence, head) check beside the whole-tensor one: every block's RMS error must be
+    within tol of the larger of its own reference RMS and `floor` times the tensor's RMS.  The
+    floor keeps blocks whose exact value cancels to (nearly) zero -- dQ and dK of a one-token
+    sequence without a sink are exactly 0, while the device's D_i, formed from the rounded O,
+    leaves rounding noise there -- from turning that noise into a large relative error.  A
+    wrong wave block (32 rows of one head) has an error of the order of its own norm, which
+    for any block of typical size is the tensor's RMS, and fails by a factor ~1/tol.  Prints
+    the worst block of each tensor; raises AssertionError listing the blocks above the bound."""
     bad, worst = [], {}
     for key in keys:
         if key not in ref or ref[key] is None:

@@ -78,6 +78,13 @@ EDGE_CASES = {
     "mode8_split_alibi_sink": dict(lens_q=[150, 129, 64], lens_kv=[400, 129, 64], head_num=4, kv_heads=1,
                                    head_dim=128, sparse_mode=8, pre_tokens=180, next_tokens=0, alibi=True,
                                    sink=True, q_start_idx=250, kv_start_idx=0),
+    # value head dim below the query / key one (qD == kD >= vD), on zero-padded copies
+    "vd64_qd128_causal_drop_sink": dict(lens_q=[150, 67, 300], head_num=4, kv_heads=2, head_dim=128,
+                                        v_head_dim=64, sparse_mode=3, keep_prob=0.85, sink=True),
+    "vd32_qd96_band_alibi": dict(lens_q=[200, 129], head_num=2, kv_heads=1, head_dim=96, v_head_dim=32,
+                                 sparse_mode=4, pre_tokens=40, next_tokens=5, alibi=True),
+    "vd80_qd128_cross": dict(lens_q=[90, 200], lens_kv=[300, 65], head_num=2, kv_heads=2, head_dim=128,
+                             v_head_dim=80, sparse_mode=0),
     "mode8_sqrt_d64_drop": dict(lens_q=[300, 40, 1], head_num=2, kv_heads=2, head_dim=64, sparse_mode=8,
                                 pre_tokens=64, next_tokens=16, alibi=True, pse_type=3, keep_prob=0.9,
                                 q_start_idx=1000, kv_start_idx=1000),

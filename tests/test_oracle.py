@@ -771,3 +771,23 @@ def test_mode8_start_indices_shift_only_the_pse():
     moved = _run(q, k, v, dy, lq, lq, 2, 1, 0.3, q_start_idx=500, kv_start_idx=500, **kw)
     for x, y in zip(base[:6], moved[:6]):
         np.testing.assert_allclose(y, x, rtol=1e-13, atol=1e-14)
+
+
+# --------------------------------------------------------------------------- value head dim below qD
+
+def test_narrow_value_head_dim_against_sdpa_and_autograd():
+    # qD == kD >= vD (grad page, Constraints): torch SDPA takes a value head dim of its own
+    # (forward), and torch autograd of the plain expression gives the gradients
+    lq, lkv, d, dv = 13, 17, 12, 5
+    q, k, v = _rand(110, lq, 2, d), _rand(111, lkv, 2, d), _rand(112, lkv, 2, dv)
+    dy = _rand(113, lq, 2, dv)
+    o, _, _ = oracle.forward(q, k, v, [0, lq], [0, lkv], 2, 2, 0.3, sparse_mode=3)
+    from torch.nn.attention.bias import causal_lower_right
+    tq, tk, tv = (torch.from_numpy(x).permute(1, 0, 2)[None].requires_grad_(True) for x in (q, k, v))
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=causal_lower_right(lq, lkv),
+                                                           scale=0.3)
+    np.testing.assert_allclose(o, ref[0].permute(1, 0, 2).detach().numpy(), rtol=1e-12, atol=1e-13)
+    ref.backward(torch.from_numpy(dy).permute(1, 0, 2)[None])
+    dq, dk, dvv, _ = oracle.backward(q, k, v, dy, [0, lq], [0, lkv], 2, 2, 0.3, sparse_mode=3)
+    for got, t in ((dq, tq), (dk, tk), (dvv, tv)):
+        np.testing.assert_allclose(got, t.grad[0].permute(1, 0, 2).numpy(), rtol=1e-11, atol=1e-12)

@@ -160,7 +160,7 @@ def make_case(name, lens_q, lens_kv=None, *, head_num, kv_heads, head_dim, dtype
               scale=None, keep_prob=1.0, sparse_mode=MODE_NONE, pre_tokens=INT_MAX_TOKENS,
               next_tokens=INT_MAX_TOKENS, alibi=False, sink=False, seed=0, dy_mult=1.0,
               drop_mask=None, prefix=None, atten_mask=None, pse_type=2, slopes_per_batch=False,
-              pse=None, q_start_idx=None, kv_start_idx=None) -> Case:
+              pse=None, q_start_idx=None, kv_start_idx=None, v_head_dim=None) -> Case:
     """A case built from explicit lengths; every tensor is drawn from default_rng([seed, t]).
     alibi=True adds generated-pse slopes ([Nq], or [B, Nq] with slopes_per_batch) of pseType pse_type.
     pse=(form, shared) adds an external pse of pseType pse_type (0 or 1) drawn from
@@ -174,8 +174,9 @@ def make_case(name, lens_q, lens_kv=None, *, head_num, kv_heads, head_dim, dtype
         scale = 1.0 / math.sqrt(head_dim)
     q = _normal([seed, 1], (tq, head_num, head_dim), dtype)
     k = _normal([seed, 2], (tkv, kv_heads, head_dim), dtype)
-    v = _normal([seed, 3], (tkv, kv_heads, head_dim), dtype)
-    dy = _normal([seed, 4], (tq, head_num, head_dim), dtype, dy_mult)
+    dv_ = head_dim if v_head_dim is None else int(v_head_dim)   # V, O, dY head dim (<= head_dim)
+    v = _normal([seed, 3], (tkv, kv_heads, dv_), dtype)
+    dy = _normal([seed, 4], (tq, head_num, dv_), dtype, dy_mult)
     sink_v = None
     if sink:
         sink_v = np.random.default_rng([seed, 5]).standard_normal(head_num, dtype=np.float32)
