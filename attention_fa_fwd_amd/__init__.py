@@ -10,7 +10,7 @@ from ._lib import (EXPORTED, FA_DTYPE_BF16, FA_DTYPE_FP16, FA_DTYPE_FP32, FA_FLA
                    fa_profile_enable, fa_profile_read, lib, status_string, DecodeConfig, fa_decode,
                    fa_decode_workspace_size, fa_decode_noalloc, FA_ERR_SCRATCH,
                    FA_DECODE_NOALLOC_SCRATCH_BYTES, FA_LAYOUT_TND, FA_LAYOUT_BSH, FA_LAYOUT_BSND,
-                   FA_LAYOUT_BNSD, FA_LAYOUT_SBH, layout_shape)
+                   FA_LAYOUT_BNSD, FA_LAYOUT_SBH, layout_shape, trace_lib, TRACE_LIB_PATH)
 
 __all__ = ["Config", "FaError", "fa_fwd", "fa_bwd", "fa_fwd_workspace_size", "fa_bwd_workspace_size",
            "fa_debug_schedule", "fa_profile_enable", "fa_profile_read", "lib", "status_string", "EXPORTED",
@@ -18,4 +18,5 @@ __all__ = ["Config", "FaError", "fa_fwd", "fa_bwd", "fa_fwd_workspace_size", "fa
            "FA_DTYPE_FP32", "FA_DTYPE_BF16", "FA_DTYPE_FP16", "FA_FLAG_PSE_SQRT", "FA_FLAG_SLOPES_PER_BATCH", "FA_FLAG_ATOMIC_DQ",
            "TOKENS_DEFAULT", "DecodeConfig", "fa_decode", "fa_decode_workspace_size", "fa_decode_noalloc",
            "FA_ERR_SCRATCH", "FA_DECODE_NOALLOC_SCRATCH_BYTES", "FA_LAYOUT_TND", "FA_LAYOUT_BSH",
-           "FA_LAYOUT_BSND", "FA_LAYOUT_BNSD", "FA_LAYOUT_SBH", "layout_shape"]
+           "FA_LAYOUT_BSND", "FA_LAYOUT_BNSD", "FA_LAYOUT_SBH", "layout_shape", "trace_lib",
+           "TRACE_LIB_PATH"]

@@ -16,6 +16,8 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libfa.so")
+# the trace build (same sources, per-tile visit counters; include/fa_trace.h), for tests only
+TRACE_LIB_PATH = os.path.join(_PKG, "libfa_trace.so")
 
 FA_OK = 0
 FA_ERR_PARAM_NULLPTR = 161001
@@ -99,40 +101,57 @@ class FaError(RuntimeError):
 
 
 _lib = None
+_trace_lib = None
 
 
 def lib() -> ctypes.CDLL:
     """The loaded library (raises if libfa.so was not built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(LIB_PATH):
-            raise ImportError(f"{LIB_PATH} is missing: build it with `python -m attention_fa_fwd_amd.build`")
-        L = ctypes.CDLL(LIB_PATH)
-        vp, u64p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint64)
-        cfgp = ctypes.POINTER(FaConfig)
-        L.fa_fwd_workspace_size.argtypes = [cfgp, u64p]
-        L.fa_bwd_workspace_size.argtypes = [cfgp, u64p]
-        L.fa_fwd.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
-        L.fa_bwd.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
-        L.fa_status_string.argtypes = [ctypes.c_int32]
-        L.fa_status_string.restype = ctypes.c_char_p
-        L.fa_debug_schedule.argtypes = [cfgp, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
-                                        ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32),
-                                        ctypes.POINTER(ctypes.c_int32)]
-        L.fa_profile_enable.argtypes = [ctypes.c_int32]
-        L.fa_profile_read.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_char_p),
-                                      ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
-        L.fa_profile_kernel_count.restype = ctypes.c_int32
-        decp = ctypes.POINTER(FaDecodeConfig)
-        L.fa_decode_workspace_size.argtypes = [decp, u64p]
-        L.fa_decode.argtypes = [decp, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
-        L.fa_decode_noalloc.argtypes = [decp, vp, vp, vp, vp, vp]
-        for name in ("fa_fwd_workspace_size", "fa_bwd_workspace_size", "fa_fwd", "fa_bwd", "fa_debug_schedule",
-                     "fa_profile_enable", "fa_profile_read", "fa_decode_workspace_size", "fa_decode",
-                     "fa_decode_noalloc"):
-            getattr(L, name).restype = ctypes.c_int32
-        _lib = L
+        _lib = _load(LIB_PATH)
     return _lib
+
+
+def trace_lib() -> ctypes.CDLL:
+    """The trace build of the library (same C ABI plus fa_debug_trace)."""
+    global _trace_lib
+    if _trace_lib is None:
+        L = _load(TRACE_LIB_PATH)
+        L.fa_debug_trace.argtypes = [ctypes.c_int32, ctypes.c_void_p, ctypes.c_int64]
+        L.fa_debug_trace.restype = ctypes.c_int32
+        _trace_lib = L
+    return _trace_lib
+
+
+def _load(path: str) -> ctypes.CDLL:
+    """Loads one build of the library and declares its C signatures."""
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m attention_fa_fwd_amd.build`")
+    L = ctypes.CDLL(path)
+    vp, u64p = ctypes.c_void_p, ctypes.POINTER(ctypes.c_uint64)
+    cfgp = ctypes.POINTER(FaConfig)
+    L.fa_fwd_workspace_size.argtypes = [cfgp, u64p]
+    L.fa_bwd_workspace_size.argtypes = [cfgp, u64p]
+    L.fa_fwd.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
+    L.fa_bwd.argtypes = [cfgp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
+    L.fa_status_string.argtypes = [ctypes.c_int32]
+    L.fa_status_string.restype = ctypes.c_char_p
+    L.fa_debug_schedule.argtypes = [cfgp, ctypes.c_int32, ctypes.POINTER(ctypes.c_int64), ctypes.c_int64,
+                                    ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32),
+                                    ctypes.POINTER(ctypes.c_int32)]
+    L.fa_profile_enable.argtypes = [ctypes.c_int32]
+    L.fa_profile_read.argtypes = [ctypes.c_int32, ctypes.POINTER(ctypes.c_char_p),
+                                  ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    L.fa_profile_kernel_count.restype = ctypes.c_int32
+    decp = ctypes.POINTER(FaDecodeConfig)
+    L.fa_decode_workspace_size.argtypes = [decp, u64p]
+    L.fa_decode.argtypes = [decp, vp, vp, vp, vp, vp, ctypes.c_uint64, vp]
+    L.fa_decode_noalloc.argtypes = [decp, vp, vp, vp, vp, vp]
+    for name in ("fa_fwd_workspace_size", "fa_bwd_workspace_size", "fa_fwd", "fa_bwd", "fa_debug_schedule",
+                 "fa_profile_enable", "fa_profile_read", "fa_decode_workspace_size", "fa_decode",
+                 "fa_decode_noalloc"):
+        getattr(L, name).restype = ctypes.c_int32
+    return L
 
 
 def status_string(status: int) -> str:

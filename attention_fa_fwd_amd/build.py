@@ -14,6 +14,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libfa.so")
+# the trace build: the same sources with per-tile visit counters (include/fa_trace.h)
+TRACE_LIB = os.path.join(PKG, "libfa_trace.so")
+TRACE_DEFINES = ("FA_TRACE_VISITS",)
 SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_kv.hip", "fa_bwd_kv_atomic.hip", "fa_decode.hip",
            "fa_layout.hip"]
 # sources whose MFMA results are kept in VGPRs (see common_flags)
@@ -94,5 +97,10 @@ def build(verbose: bool = False, target: str = LIB, defines=()) -> str:
     return target
 
 
+def build_all(verbose: bool = False):
+    """The product library and its trace build."""
+    return build(verbose), build(verbose, TRACE_LIB, TRACE_DEFINES)
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build_all(verbose="-v" in sys.argv))

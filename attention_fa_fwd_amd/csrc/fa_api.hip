@@ -637,6 +637,44 @@ DecPlan plan_decode(const DecProblem& pr) {
   return P;
 }
 
+#if defined(FA_TRACE_VISITS)
+// Trace build: device buffers of visit counters for pass 0 (forward), 1 (dK/dV) and
+// 2 (dQ), set by fa_debug_trace; null = not traced.
+std::mutex g_trace_mu;
+uint32_t* g_trace[3] = {};
+int64_t g_trace_words[3] = {};
+#endif
+
+// Tile grid of a pass's visit counters: rows per block and keys per tile, and the
+// block / tile counts of the longest sequences.
+void trace_dims(const Problem& pr, int rows, int keys, int32_t* rb, int32_t* kt) {
+  int64_t mq = 0, mkv = 0;
+  for (int64_t b = 0; b < pr.batch; ++b) {
+    mq = std::max<int64_t>(mq, pr.cu_q[b + 1] - pr.cu_q[b]);
+    mkv = std::max<int64_t>(mkv, pr.cu_kv[b + 1] - pr.cu_kv[b]);
+  }
+  *rb = (int32_t)((mq + rows - 1) / rows);
+  *kt = (int32_t)((mkv + keys - 1) / keys);
+}
+
+// Points the pass's counters at the trace buffer (trace build); false when the buffer
+// is set but too small for this problem.
+template <typename T>
+bool attach_trace(const Problem& pr, int pass, int rows, int keys, T** ptr, int32_t* rb, int32_t* kt) {
+  trace_dims(pr, rows, keys, rb, kt);
+#if defined(FA_TRACE_VISITS)
+  std::lock_guard<std::mutex> g(g_trace_mu);
+  if (g_trace[pass]) {
+    if (pr.batch * pr.nq * (int64_t)*rb * *kt > g_trace_words[pass]) return false;
+    *ptr = g_trace[pass];
+  }
+#else
+  (void)pass;
+  *ptr = nullptr;
+#endif
+  return true;
+}
+
 // Address of the current device's copy of fa_noalloc_scratch, looked up once per
 // device with that device current (the first fa_decode_noalloc call on it).
 hipError_t noalloc_scratch(char** out) {
@@ -752,6 +790,7 @@ fa_status fa_fwd(const fa_config* cfg, const void* q, const void* k, const void*
     });
     if (e != hipSuccess) return FA_ERR_HIP;
   }
+  if (!attach_trace(pr, 0, 32, fa::kFwdBN, &p.trace, &p.trace_rb, &p.trace_kt)) return FA_ERR_PARAM_INVALID;
   e = timed(K_FWD, s, [&] { return fa::launch_fwd(pr.dtype, (int)pr.d, p, s); });
   if (e == hipSuccess && copied(pr, T_O)) e = relayout_tensor(pr, T_O, ws + L.ro, out, false, s);
   return hip_status(e);
@@ -846,6 +885,9 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
   p.mbits = pr.mask ? reinterpret_cast<const uint32_t*>(ws + L.mbits) : nullptr;
   p.mwords = (int32_t)pr.mask_words;
   const int dt = pr.dtype, d = (int)pr.d;
+  if (!attach_trace(pr, 1, fa::kKvBM, fa::kKvBN, &p.trace_kv, &p.trace_kv_rb, &p.trace_kv_kt) ||
+      !attach_trace(pr, 2, 32, fa::kDqBN, &p.trace_dq, &p.trace_dq_rb, &p.trace_dq_kt))
+    return FA_ERR_PARAM_INVALID;
 
   e = hipSuccess;
   if (pr.mask)
@@ -971,6 +1013,16 @@ fa_status fa_decode_noalloc(const fa_decode_config* cfg, const void* q, const vo
   if (noalloc_scratch(&ws) != hipSuccess) return FA_ERR_HIP;
   return decode_run(pr, P, q, k, v, out, ws, reinterpret_cast<hipStream_t>(stream));
 }
+
+#if defined(FA_TRACE_VISITS)
+fa_status fa_debug_trace(int32_t pass, uint32_t* counters, int64_t words) {
+  if (pass < 0 || pass > 2 || words < 0) return FA_ERR_PARAM_INVALID;
+  std::lock_guard<std::mutex> g(g_trace_mu);
+  g_trace[pass] = counters;
+  g_trace_words[pass] = counters ? words : 0;
+  return FA_OK;
+}
+#endif
 
 fa_status fa_profile_enable(int32_t on) {
   ProfState& P = prof();

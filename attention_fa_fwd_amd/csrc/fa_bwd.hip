@@ -254,6 +254,8 @@ __global__ __launch_bounds__(256, (dq_occupancy<T, D, DROP, ALIBI, MASK>())) voi
     const char* vs = ks + S::TILE;
     const int c0 = t * kDqBN;
     if (wr0 >= lq || fa_tile_empty(win, wr0, min(wr0 + 32, lq), c0, min(c0 + kDqBN, lkv))) return;
+    if (lane == 0)
+      FA_TRACE_VISIT(p.trace_dq, (((int64_t)b * p.nq + h) * p.trace_dq_rb + (wr0 >> 5)) * p.trace_dq_kt + t);
     // with an attenMask every tile takes the masked path
     const bool full = fa_tile_full(win, wr0, 32, c0, kDqBN, lq, lkv) && !MASK;
     uint64_t bits = ~0ull;

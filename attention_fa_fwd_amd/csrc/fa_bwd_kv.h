@@ -315,6 +315,8 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
 
   auto compute_16 = [&](const char* st, auto n) {
     const int h = step_head(n), r0 = step_row0(n);
+    if (tid == 0)
+      FA_TRACE_VISIT(p.trace_kv, (((int64_t)b * p.nq + h) * p.trace_kv_rb + r0 / kKvBM) * p.trace_kv_kt + it.tile);
     const float slope_l2 = pse_slopes(ALIBI) ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
     // with an attenMask every block takes the masked path
     const bool full0 = fa_tile_full(win, r0, 32, wc0, 32, lq, lkv) && !MASK;
@@ -343,6 +345,8 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
 
   auto compute = [&](const char* st, int n) {
     const int h = step_head(n), r0 = step_row0(n);
+    if (tid == 0)
+      FA_TRACE_VISIT(p.trace_kv, (((int64_t)b * p.nq + h) * p.trace_kv_rb + r0 / kKvBM) * p.trace_kv_kt + it.tile);
     const float slope_l2 = pse_slopes(ALIBI) ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
     const float* lse_s = reinterpret_cast<const float*>(st + S::OFF_LSE);
     const float* del_s = reinterpret_cast<const float*>(st + S::OFF_DEL);
@@ -700,6 +704,8 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
 
   auto compute = [&](const char* st, int n) {
     const int h = step_head(n), r0 = step_row0(n);
+    if (tid == 0)
+      FA_TRACE_VISIT(p.trace_kv, (((int64_t)b * p.nq + h) * p.trace_kv_rb + r0 / kKvBM) * p.trace_kv_kt + it.tile);
     const float slope_l2 = pse_slopes(ALIBI) ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
     const float sc = p.scale_log2;
     const int rb = half;                     // the row block whose P~ / dS this wave forms

@@ -360,6 +360,7 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
     }
     if constexpr (!kAhead) rt = classify(t);
     if (rt.live) {
+      if (lane == 0) FA_TRACE_VISIT(p.trace, (((int64_t)b * p.nq + h) * p.trace_rb + (wr0 >> 5)) * p.trace_kt + t);
       f32x16 s[2];
       scores(kc, s);
       finish(s, t, rt, vc);

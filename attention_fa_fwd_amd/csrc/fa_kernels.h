@@ -15,6 +15,15 @@ struct WorkItem {
   int32_t b, tile, lo, hi;
 };
 
+// Visited-tile counters of the trace build (FA_TRACE_VISITS): each pass counts every tile
+// it computes, indexed ((sequence * Nq + head) * trace_rb + row block) * trace_kt + key
+// tile; the product build leaves the pointers null and compiles the counting out.
+#if defined(FA_TRACE_VISITS)
+#define FA_TRACE_VISIT(ptr, idx) atomicAdd((ptr) + (idx), 1u)
+#else
+#define FA_TRACE_VISIT(ptr, idx) ((void)0)
+#endif
+
 struct FwdParams {
   const void* q;
   const void* k;
@@ -50,6 +59,8 @@ struct FwdParams {
   float inv_keep;     // 1 / keep_prob
   int32_t use_dropout;
   int32_t head_swizzle;
+  uint32_t* trace;    // trace build: visits per (sequence, head, 32-row block, 64-key tile)
+  int32_t trace_rb, trace_kt;
 };
 
 struct BwdParams {
@@ -101,6 +112,9 @@ struct BwdParams {
   int32_t use_dropout;
   int32_t head_swizzle;
   int32_t n_pre_blocks;
+  uint32_t* trace_kv;   // trace build: dK/dV steps per (sequence, head, 64-row tile, 128-key tile)
+  uint32_t* trace_dq;   // trace build: dQ tiles per (sequence, head, 32-row block, 64-key tile)
+  int32_t trace_kv_rb, trace_kv_kt, trace_dq_rb, trace_dq_kt;
 };
 
 // Decode attention: one work item = a key range [lo, hi) of one (sequence b,

@@ -497,3 +497,17 @@ def test_modes_7_8_pse_rules():
     for mode in (7, 8):
         cfg = _cfg(sparse_mode=mode, dtype=fa.FA_DTYPE_FP32, pse=pse, pse_type=0)
         assert fa.lib().fa_fwd_workspace_size(cfg.ref, ctypes.byref(n)) == fa.FA_ERR_PARAM_INVALID
+
+
+def test_trace_build_exports_its_debug_call_only():
+    # include/fa_trace.h declares the visit-counter hook of the trace build (libfa_trace.so);
+    # the product library does not have it
+    text = open(os.path.join(ROOT, "include", "fa_trace.h")).read()
+    declared = set(re.findall(r"^\s*fa_status\s+(fa_\w+)\s*\(", text, re.M))
+    assert declared == {"fa_debug_trace"}
+    TL = fa.trace_lib()
+    assert hasattr(TL, "fa_debug_trace") and not hasattr(fa.lib(), "fa_debug_trace")
+    for name in fa.EXPORTED:
+        assert hasattr(TL, name), name
+    assert TL.fa_debug_trace(3, None, 0) == fa.FA_ERR_PARAM_INVALID
+    assert TL.fa_debug_trace(0, None, 0) == fa.FA_OK
