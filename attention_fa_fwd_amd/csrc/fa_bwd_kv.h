@@ -854,4 +854,317 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
   }
 }
 
+// ---------------------------------------------------------------- producer / consumer waves
+// LDS operand reads issued ahead of the first MFMA of a producer / consumer matrix phase
+#ifndef FA_SPEC_READ_AHEAD_P
+#define FA_SPEC_READ_AHEAD_P 4
+#endif
+#ifndef FA_SPEC_READ_AHEAD_C
+#define FA_SPEC_READ_AHEAD_C 16
+#endif
+// 16-bit deterministic dK/dV with specialised waves (8 per workgroup, one workgroup per CU).
+//   waves 0-3, producers (key group kg = wave): hold the group's K and V rows; for step
+//     t + 1 they compute S = Q K^T and dP~ = dY V^T for both 32-row blocks, then P~ and dS
+//     as 16-bit A operands, which they write to the group's exchange area;
+//   waves 4-7, consumers (kg = wave - 4): hold dK and dV of the group's 32 keys over all
+//     of D; at the start of tick t they take step t's operands out of the exchange area
+//     into registers, then issue the tile copies of step t + 2 and accumulate
+//     dV += P~^T dY and dK += dS^T Q.
+// Wave w and wave w + 4 share a SIMD (checked on the device), so each SIMD runs one
+// producer (matrix work, then softmax / dS on the VALU) beside one consumer (matrix work
+// and LDS reads): the VALU work of one overlaps the matrix work of the other, where the
+// paired kernel's two waves of a SIMD ran the same phase at the same time.
+// Per tick: barrier A (step t's operands and tiles are in) -> consumers read the exchange
+// area -> barrier B (it may be overwritten) -> producers form step t + 1 while consumers
+// run step t.  LDS: three Q/dY stages (step t for the consumers, t + 1 for the producers,
+// t + 2 in flight) and one exchange area.  Each role runs its own loop (same barriers), so
+// neither role's registers are live in the other's.
+template <typename E, int D, bool DROP, int ALIBI, bool MASK>
+__global__ __launch_bounds__(512, 1) void fa_bwd_kv_spec_kernel(BwdParams p) {
+  using S = KvShape<E, D>;
+  using V8 = typename Vec16<E>::v8;
+  constexpr int XB = 4 * 1024;   // exchange bytes of one 32-row block of one key group (P~, dS: two operands each)
+  __shared__ __attribute__((aligned(16))) char stg[3][S::STAGE];
+  __shared__ __attribute__((aligned(16))) char xch[4 * 2 * XB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5, lrow = lane & 31;
+  const int grp = lane >> 4, sl = lane & 15;
+  const bool producer = wave < 4;
+  const int kg = wave & 3;
+
+  const int item_idx = blockIdx.x / p.nkv;
+  const int gl = blockIdx.x - item_idx * p.nkv;
+  const int g = (p.nkv % 8 == 0) ? (gl & 7) * (p.nkv >> 3) + (gl >> 3) : gl;
+  const WorkItem it = p.kv_items[item_idx];
+  const int b = it.b;
+  const int q0 = p.cu_q[b], lq = p.cu_q[b + 1] - q0;
+  const int k0 = p.cu_kv[b], lkv = p.cu_kv[b + 1] - k0;
+  const FaWindow win = fa_make_window(fa_seq_mode(p.mode, b, p.nseq), p.pre, p.next, lq, lkv, p.prefix[b]);
+  const int poff = b == 0 ? p.pse_off0 : 0;   // sequence 0 of mode 8: pse row i + qStartIdx - kvStartIdx
+  const int c0 = it.tile * kKvBN;          // first key of the workgroup tile
+  const int wc0 = c0 + 32 * kg;            // first key of this wave's group
+  const int j = wc0 + lrow;                // this lane's key
+  const bool key_ok = j < lkv;
+  const int nqt = it.hi - it.lo;
+  const int nsteps = p.group * nqt;
+  const int64_t q_stride = (int64_t)p.nq * S::RB;
+  char* const xkg = xch + kg * 2 * XB + 16 * lane;   // this lane's slots in its key group's exchange area
+
+  // steps walk the query tiles from the last one down, the heads of the group innermost
+  auto step_head = [&](int n) { return g * p.group + n % p.group; };
+  auto step_row0 = [&](int n) { return (it.hi - 1 - n / p.group) * kKvBM; };
+  auto stage = [&](int n) -> char* { return stg[n % 3]; };
+
+  if (producer) {
+    // K and V rows of the group's keys as B operands (lane = key, registers = d)
+    V8 kf[S::NOP], vf[S::NOP];
+    {
+      const int64_t kr = (int64_t)(k0 + (key_ok ? j : 0)) * p.nkv + g;
+      const E* kp = reinterpret_cast<const E*>(p.k) + kr * D;
+      const E* vp = reinterpret_cast<const E*>(p.v) + kr * D;
+#pragma unroll
+      for (int c = 0; c < S::NOP; ++c) {
+        const V8 a = *reinterpret_cast<const V8*>(kp + 16 * c + 8 * hh);
+        const V8 v = *reinterpret_cast<const V8*>(vp + 16 * c + 8 * hh);
+        kf[c] = key_ok ? a : V8{};
+        vf[c] = key_ok ? v : V8{};
+      }
+    }
+    // row reads of chunk 2c + hh of row lrow of a row block: qrow + 16 * ((2c) ^ qsw)
+    const int qrow = lrow * S::RB, qsw = tile_swz<S::RB>(lrow) ^ hh;
+
+    // S, dP~ of both row blocks, then P~ and dS written to the exchange area.  Without
+    // keep or mask bits the second block's MFMAs are issued before the first block's VALU
+    // work, so they run under it; the instances with bits (more registers per element)
+    // do one block after the other.
+    constexpr bool kSeq = DROP || MASK;
+    auto produce = [&](const char* st, int n) {
+      const int h = step_head(n), r0 = step_row0(n);
+      if (tid == 0)
+        FA_TRACE_VISIT(p.trace_kv, (((int64_t)b * p.nq + h) * p.trace_kv_rb + r0 / kKvBM) * p.trace_kv_kt + it.tile);
+      const float slope_l2 = pse_slopes(ALIBI) ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
+      const float sc = p.scale_log2;
+      f32x16 s[2], dp[2];
+      auto sdp = [&](int rb) {
+        s[rb] = f32x16{};
+        dp[rb] = f32x16{};
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int c = 0; c < S::NOP; ++c) {
+          const int qo = qrow + 16 * ((2 * c) ^ qsw) + 32 * rb * S::RB;
+          const V8 qa = lds_read_b128<V8>(st + qo);
+          const V8 ya = lds_read_b128<V8>(st + S::OFF_DY + qo);
+          s[rb] = mfma32(qa, kf[c], s[rb]);
+          dp[rb] = mfma32(ya, vf[c], dp[rb]);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x100, FA_SPEC_READ_AHEAD_P, 0);
+        sched_alternate<2 * S::NOP, 0x008, 0x100>();
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      const float* lse_s = reinterpret_cast<const float*>(st + S::OFF_LSE);
+      const float* del_s = reinterpret_cast<const float*>(st + S::OFF_DEL);
+      const uint32_t* bits_s = reinterpret_cast<const uint32_t*>(st + S::OFF_BITS);
+      auto elem = [&](auto full_c, int rb) {
+        constexpr bool plain = !ALIBI && decltype(full_c)::value;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          V8 pa, da;
+#pragma unroll
+          for (int a = 2 * c; a < 2 * c + 2; ++a) {
+            const int rq = 32 * rb + 8 * a + 4 * hh;   // rows rq .. rq+3 sit in registers 4a .. 4a+3
+            const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lse_s + rq);
+            const f32x4 del4 = *reinterpret_cast<const f32x4*>(del_s + rq);
+            u32x4 bits4, mb4 = {};
+            if constexpr (DROP) bits4 = *reinterpret_cast<const u32x4*>(bits_s + kg * kKvBM + rq);
+            if constexpr (!decltype(full_c)::value && MASK)
+              mb4 = *reinterpret_cast<const u32x4*>(st + S::OFF_MBITS + 4 * (kg * kKvBM + rq));
+            const float jmi = (float)(j - r0 - rq - poff);   // j - i of register 4a (pse position); minus e for 4a + e
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * a + e, i = r0 + rq + e;
+              float pr;
+              if constexpr (plain) {
+                pr = fast_exp2(__builtin_fmaf(s[rb][r], sc, -lse4[e]));
+              } else {
+                float x = s[rb][r] * sc;
+                if constexpr (ALIBI == kPseExt)
+                  x = __builtin_fmaf(p.pse_coef, (i < lq && key_ok) ? pse_value<E>(p, b, h, i, j, lq) : 0.f, x);
+                else if constexpr (ALIBI != 0)
+                  x = add_pse<ALIBI>(x, slope_l2, jmi - (float)e);
+                if constexpr (!decltype(full_c)::value) {
+                  const bool ok = (i < lq) & key_ok & (j >= fa_row_lo(win, i)) & (j <= fa_row_hi(win, i)) &
+                                  !((mb4[e] >> lrow) & 1u);
+                  x = ok ? x : kNegInf;
+                }
+                pr = fast_exp2(x - lse4[e]);
+              }
+              float dpv = dp[rb][r], ptv = pr;
+              if constexpr (DROP) {
+                const bool keep = (bits4[e] >> lrow) & 1u;
+                dpv = keep ? dpv * p.inv_keep : 0.f;
+                ptv = keep ? pr * p.inv_keep : 0.f;
+              }
+              const float dsv = pr * (dpv - del4[e]);
+              pa[r & 7] = cvt16<E>(ptv);
+              da[r & 7] = cvt16<E>(dsv);
+            }
+          }
+          *reinterpret_cast<V8*>(xkg + rb * XB + 1024 * c) = pa;
+          *reinterpret_cast<V8*>(xkg + rb * XB + 1024 * (2 + c)) = da;
+        }
+      };
+      // with an attenMask every block takes the masked path
+      auto softmax = [&](int rb) {
+        if (fa_tile_full(win, r0 + 32 * rb, 32, wc0, 32, lq, lkv) && !MASK) elem(std::true_type{}, rb);
+        else elem(std::false_type{}, rb);
+      };
+      if constexpr (kSeq) {
+        sdp(0);
+        softmax(0);
+        sdp(1);
+        softmax(1);
+      } else {
+        sdp(0);
+        sdp(1);
+        softmax(0);
+        softmax(1);
+      }
+    };
+
+    __syncthreads();   // A: stages of steps 0 and 1 are in
+    if (nsteps > 0) produce(stage(0), 0);
+    for (int t = 0; t < nsteps; ++t) {
+      __syncthreads();   // A: step t's operands and tiles are in
+      __syncthreads();   // B: the consumers have taken step t's operands
+      if (t + 1 < nsteps) produce(stage(t + 1), t + 1);
+    }
+  } else {
+    const int cw = wave - 4, ctid = tid - 256;
+    // transposing reads of rows rv and rv + 8 (+16 per 16-row step), chunk 4db + qv: the
+    // offset (rv + 8hf) * RB + 16 * ((4db + qv) ^ swz) + bv equals tx[hf] ^ 64db, because
+    // the chunk index enters only bits that the row and byte parts leave clear
+    int tx[2];
+    {
+      const int rv = 4 * (grp >> 1) + (sl >> 2), qv = 2 * (grp & 1) + ((sl & 3) >> 1), bv = 8 * (sl & 1);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        tx[hf] = (rv + 8 * hf) * S::RB + ((16 * qv) ^ (16 * tile_swz<S::RB>(rv + 8 * hf))) + bv;
+    }
+    f32x16 dk[S::NDB], dv[S::NDB];
+#pragma unroll
+    for (int db = 0; db < S::NDB; ++db) {
+      // zeros produced by an MFMA: the accumulators start in the MFMA register class
+      dk[db] = mfma32(V8{}, V8{}, f32x16{});
+      dv[db] = mfma32(V8{}, V8{}, f32x16{});
+    }
+    // the four consumer waves copy each step's Q and dY tiles, lse2 and D_i
+    auto load = [&](char* st, int n) {
+      const int h = step_head(n), r0 = step_row0(n);
+      const char* qb = reinterpret_cast<const char*>(p.q) + ((int64_t)q0 * p.nq + h) * S::RB;
+      const char* dyb = reinterpret_cast<const char*>(p.dy) + ((int64_t)q0 * p.nq + h) * S::RB;
+      dma_tile_swz<kKvBM, S::RB, 4>(st, qb, q_stride, r0, lq, cw, lane);
+      dma_tile_swz<kKvBM, S::RB, 4>(st + S::OFF_DY, dyb, q_stride, r0, lq, cw, lane);
+      if (cw < 2) {
+        const int rr = (r0 + lane < lq) ? r0 + lane : 0;
+        dma_dword(st + (cw == 0 ? S::OFF_LSE : S::OFF_DEL), cw == 0 ? p.lse : p.delta,
+                  (uint32_t)(((int64_t)(q0 + rr) * p.nq + h) * 4));
+      }
+    };
+    // keep bits (and attenMask bits) of a step: 64 rows x 128 keys = 256 words, one per consumer thread
+    const int bits_slot = (ctid & 3) * kKvBM + ((ctid >> 2) & (kKvBM - 1));
+    auto bits_word = [&](int n) -> uint32_t {
+      const int h = step_head(n), r0 = step_row0(n);
+      const int r = (ctid >> 2) & (kKvBM - 1), w = ctid & 3;
+      if (r0 + r >= lq) return 0u;
+      const int64_t pos = p.bit_base[b] + ((int64_t)h * lq + r0 + r) * lkv + c0 + 32 * w;
+      return (uint32_t)load_mask_window(p.drop, p.drop_bytes, pos);
+    };
+    auto mask_word = [&](int n) -> uint32_t {
+      const int r0 = step_row0(n);
+      const int r = (ctid >> 2) & (kKvBM - 1), w = (c0 >> 5) + (ctid & 3);
+      if (r0 + r >= lq || w >= p.mwords) return ~0u;
+      return p.mbits[(int64_t)(r0 + r) * p.mwords + w];
+    };
+    auto put_words = [&](char* st, uint32_t word, uint32_t mword) {
+      if constexpr (DROP) reinterpret_cast<uint32_t*>(st + S::OFF_BITS)[bits_slot] = word;
+      if constexpr (MASK) reinterpret_cast<uint32_t*>(st + S::OFF_MBITS)[bits_slot] = mword;
+    };
+    // step t's P~ and dS operands, [row block][c], taken out of the exchange area
+    V8 pt[2][2], ds[2][2];
+    auto take = [&]() {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          pt[blk][c] = *reinterpret_cast<const V8*>(xkg + blk * XB + 1024 * c);
+          ds[blk][c] = *reinterpret_cast<const V8*>(xkg + blk * XB + 1024 * (2 + c));
+        }
+    };
+    // dV += P~^T dY, dK += dS^T Q over both row blocks and all of D
+    auto consume = [&](const char* st) {
+      // fresh copies of the offset bases, so their XORs are formed per use, not hoisted into tables
+      int tx0 = tx[0], tx1 = tx[1];
+      asm volatile("" : "+v"(tx0), "+v"(tx1));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const char* base = st + (32 * blk + 16 * c) * S::RB;
+#pragma unroll
+          for (int db = 0; db < S::NDB; ++db) {
+            const int o0 = tx0 ^ (64 * db), o1 = tx1 ^ (64 * db);
+            const V8 yo = lds_read_tr_x2<V8>(base + S::OFF_DY + o0, base + S::OFF_DY + o1);
+            const V8 qo = lds_read_tr_x2<V8>(base + o0, base + o1);
+            dv[db] = mfma32(pt[blk][c], yo, dv[db]);
+            dk[db] = mfma32(ds[blk][c], qo, dk[db]);
+          }
+        }
+      __builtin_amdgcn_sched_group_barrier(0x100, FA_SPEC_READ_AHEAD_C, 0);
+      sched_alternate<8 * S::NDB, 0x008, 0x100, 2>();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    uint32_t word = 0, mword = 0;
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      if (n < nsteps) {
+        load(stage(n), n);
+        if constexpr (DROP) word = bits_word(n);
+        if constexpr (MASK) mword = mask_word(n);
+        put_words(stage(n), word, mword);
+      }
+    }
+    dma_wait();
+    __syncthreads();   // A: stages of steps 0 and 1 are in
+    for (int t = 0; t < nsteps; ++t) {
+      __syncthreads();   // A: step t's operands and tiles are in
+      take();
+      __syncthreads();   // B: the producers may overwrite the exchange area
+      if (t + 2 < nsteps) {
+        load(stage(t + 2), t + 2);
+        if constexpr (DROP) word = bits_word(t + 2);
+        if constexpr (MASK) mword = mask_word(t + 2);
+      }
+      consume(stage(t));
+      if (t + 2 < nsteps) put_words(stage(t + 2), word, mword);
+      dma_wait();
+    }
+
+    // ---- epilogue: dK *= scale; write dK, dV of the group's keys (lane = d, registers = keys) ----
+#pragma unroll
+    for (int db = 0; db < S::NDB; ++db) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int jj = wc0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (jj < lkv) {
+          const int64_t off = ((int64_t)(k0 + jj) * p.nkv + g) * D + 32 * db + lrow;
+          reinterpret_cast<E*>(p.dk)[off] = cvt16<E>(dk[db][r] * p.scale);
+          reinterpret_cast<E*>(p.dv)[off] = cvt16<E>(dv[db][r]);
+        }
+      }
+    }
+  }
+}
+
 }  // namespace fa

@@ -15,14 +15,23 @@ static hipError_t launch_kv_t(const BwdParams& p, hipStream_t s) {
   });
 }
 
+// 16-bit dK/dV: producer / consumer waves (FA_KV_SPEC, the default) or the paired waves
+#ifndef FA_KV_SPEC
+#define FA_KV_SPEC 1
+#endif
 template <typename E, int D>
 static hipError_t launch_kv_pair(const BwdParams& p, hipStream_t s) {
   const int64_t blocks = (int64_t)p.n_kv_items * p.nkv;
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(512);
   return with_flags(p.use_dropout != 0, pse_kind(p), p.mbits != nullptr, [&](auto dr, auto al, auto mk) {
+#if FA_KV_SPEC
+    hipLaunchKernelGGL((fa_bwd_kv_spec_kernel<E, D, decltype(dr)::value, decltype(al)::value, decltype(mk)::value>),
+                       grid, block, 0, s, p);
+#else
     hipLaunchKernelGGL((fa_bwd_kv_pair_kernel<E, D, decltype(dr)::value, decltype(al)::value, decltype(mk)::value>),
                        grid, block, 0, s, p);
+#endif
     return hipGetLastError();
   });
 }

@@ -17,9 +17,13 @@ struct WorkItem {
 
 // Visited-tile counters of the trace build (FA_TRACE_VISITS): each pass counts every tile
 // it computes, indexed ((sequence * Nq + head) * trace_rb + row block) * trace_kt + key
-// tile; the product build leaves the pointers null and compiles the counting out.
+// tile; a pass whose pointer is null is not counted, and the product build compiles the
+// counting out.
 #if defined(FA_TRACE_VISITS)
-#define FA_TRACE_VISIT(ptr, idx) atomicAdd((ptr) + (idx), 1u)
+#define FA_TRACE_VISIT(ptr, idx) \
+  do {                                \
+    if (ptr) atomicAdd((ptr) + (idx), 1u); \
+  } while (0)
 #else
 #define FA_TRACE_VISIT(ptr, idx) ((void)0)
 #endif
