@@ -637,6 +637,20 @@ DecPlan plan_decode(const DecProblem& pr) {
   return P;
 }
 
+// Copies the host-built plan (work lists, sequence tables) to the workspace.  Outside
+// stream capture: one hipMemcpyAsync from pageable memory, which takes the bytes
+// before it returns, so the host buffer may go right after.  A captured copy would
+// instead keep the host address and read it at every replay, after the buffer is
+// gone; under capture the bytes therefore travel as kernel arguments, which the graph
+// stores by value (fa::launch_stage).
+hipError_t stage_plan(char* ws, const std::vector<char>& host, hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  hipError_t e = hipStreamIsCapturing(s, &cs);
+  if (e != hipSuccess) return e;
+  if (cs == hipStreamCaptureStatusNone) return hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, s);
+  return fa::launch_stage(ws, host.data(), host.size(), s);
+}
+
 #if defined(FA_TRACE_VISITS)
 // Trace build: device buffers of visit counters for pass 0 (forward), 1 (dK/dV) and
 // 2 (dQ), set by fa_debug_trace; null = not traced.
@@ -748,6 +762,7 @@ fa_status fa_fwd(const fa_config* cfg, const void* q, const void* k, const void*
   if (pr.pse && !aligned(pr.pse, 4)) return FA_ERR_PARAM_INVALID;
   const Layout bound = fwd_layout_bound(pr);
   if (!workspace) return FA_ERR_PARAM_NULLPTR;
+  if (!aligned(workspace, 16)) return FA_ERR_PARAM_INVALID;
   if (workspace_bytes < bound.total) return FA_ERR_WORKSPACE;
 
   std::vector<WorkItem> items = schedule(pr, 0, nullptr, nullptr);
@@ -756,7 +771,7 @@ fa_status fa_fwd(const fa_config* cfg, const void* q, const void* k, const void*
   std::vector<char> host = stage_block(pr, L, items, nullptr);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
-  hipError_t e = hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, s);
+  hipError_t e = stage_plan(ws, host, s);
   if (e != hipSuccess) return FA_ERR_HIP;
 
   fa::FwdParams p{};
@@ -817,6 +832,7 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
   if (pr.pse && !aligned(pr.pse, 4)) return FA_ERR_PARAM_INVALID;
   const Layout bound = bwd_layout_bound(pr);
   if (!workspace) return FA_ERR_PARAM_NULLPTR;
+  if (!aligned(workspace, 16)) return FA_ERR_PARAM_INVALID;
   if (workspace_bytes < bound.total) return FA_ERR_WORKSPACE;
 
   // the atomic dK/dV kernel for 16-bit D = 128 has no pse variant (its registers
@@ -831,7 +847,7 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
   std::vector<char> host = stage_block(pr, L, kv_items, &dq_items);
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* ws = reinterpret_cast<char*>(workspace);
-  hipError_t e = hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, s);
+  hipError_t e = stage_plan(ws, host, s);
   if (e != hipSuccess) return FA_ERR_HIP;
 
   fa::BwdParams p{};
@@ -953,7 +969,7 @@ fa_status decode_run(const DecProblem& pr, const DecPlan& P, const void* q, cons
   std::memcpy(host.data() + P.off_items, P.items.data(), sizeof(fa::DecItem) * P.items.size());
   std::memcpy(host.data() + P.off_first, P.first_slot.data(), 4 * P.first_slot.size());
   std::memcpy(host.data() + P.off_nsplit, P.n_split.data(), 4 * P.n_split.size());
-  if (hipMemcpyAsync(ws, host.data(), host.size(), hipMemcpyHostToDevice, s) != hipSuccess) return FA_ERR_HIP;
+  if (stage_plan(ws, host, s) != hipSuccess) return FA_ERR_HIP;
 
   fa::DecParams p{};
   p.q = q; p.k = k; p.v = v; p.out = out;
@@ -996,6 +1012,7 @@ fa_status fa_decode(const fa_decode_config* cfg, const void* q, const void* k, c
   if (!q || !k || !v || !out || !workspace) return FA_ERR_PARAM_NULLPTR;
   if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(out, 16)) return FA_ERR_PARAM_INVALID;
   const DecPlan P = plan_decode(pr);
+  if (!aligned(workspace, 16)) return FA_ERR_PARAM_INVALID;
   if (workspace_bytes < P.total) return FA_ERR_WORKSPACE;
   return decode_run(pr, P, q, k, v, out, reinterpret_cast<char*>(workspace), reinterpret_cast<hipStream_t>(stream));
 }

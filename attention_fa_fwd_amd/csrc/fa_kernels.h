@@ -216,5 +216,10 @@ constexpr int kLayoutBNSD = 3, kLayoutSBH = 4, kLayoutStrided = 100;
 hipError_t launch_relayout(const void* src, void* dst, int64_t B, int64_t S, int64_t N, int64_t D, int64_t DK,
                            int ebytes, int layout, bool to_tnd, hipStream_t s, int64_t ts = 0, int64_t hs = 0);
 hipError_t launch_mask_pack(const uint8_t* mask, int64_t rows, int64_t cols, uint32_t* bits, hipStream_t s);
+// Copies `bytes` (a multiple of 16) of host memory to dst (16-byte aligned) through
+// the arguments of kernel launches of kStageChunkBytes each: no host memory is
+// referenced once the call returns, also when the launches are captured in a graph.
+constexpr int kStageChunkBytes = 2048;
+hipError_t launch_stage(char* dst, const char* src, size_t bytes, hipStream_t s);
 
 }  // namespace fa

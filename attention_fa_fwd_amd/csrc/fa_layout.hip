@@ -45,6 +45,31 @@ __global__ __launch_bounds__(256) void fa_relayout_kernel(const char* src, char*
   }
 }
 
+// Plan staging for calls made under stream capture: a chunk of the host-built work
+// plan travels as the kernel's by-value argument (the graph keeps a copy of the
+// arguments, not a pointer to host memory) and is stored to the workspace, 16 bytes
+// per thread.
+struct StageChunk {
+  u32x4 data[kStageChunkBytes / 16];
+};
+
+__global__ __launch_bounds__(128) void fa_stage_kernel(char* dst, uint32_t n16, StageChunk c) {
+  for (uint32_t x = threadIdx.x; x < n16; x += 128) reinterpret_cast<u32x4*>(dst)[x] = c.data[x];
+}
+
+hipError_t launch_stage(char* dst, const char* src, size_t bytes, hipStream_t s) {
+  if (bytes % 16 != 0 || reinterpret_cast<uintptr_t>(dst) % 16 != 0) return hipErrorInvalidValue;
+  for (size_t off = 0; off < bytes; off += kStageChunkBytes) {
+    const size_t n = bytes - off < (size_t)kStageChunkBytes ? bytes - off : (size_t)kStageChunkBytes;
+    StageChunk c;
+    __builtin_memcpy(&c, src + off, n);
+    hipLaunchKernelGGL(fa_stage_kernel, dim3(1), dim3(128), 0, s, dst + off, (uint32_t)(n / 16), c);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 hipError_t launch_relayout(const void* src, void* dst, int64_t B, int64_t S, int64_t N, int64_t D, int64_t DK,
                            int ebytes, int layout, bool to_tnd, hipStream_t s, int64_t ts, int64_t hs) {
   if (D > DK || (D * ebytes) % 16 != 0 || (DK * ebytes) % 16 != 0) return hipErrorInvalidValue;

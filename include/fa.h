@@ -28,7 +28,14 @@
  * on `stream` (a hipStream_t; NULL = default stream) and return without
  * synchronising.  cu_seqlens arrays are HOST memory, read during the call and
  * copied into the workspace, so they may be freed when the call returns.
- * Two calls that share a workspace must be ordered on the same stream.
+ * Two calls that share a workspace must be ordered on the same stream.  The
+ * workspace must be 16-byte aligned (else FA_ERR_PARAM_INVALID).
+ *
+ * Stream capture: every call may be captured into a HIP graph.  The work plan
+ * the call builds on the host reaches the workspace through kernel arguments
+ * while the stream is capturing (plain hipMemcpyAsync otherwise), so a graph
+ * holds no reference to host memory; each replay recomputes the outputs from
+ * the current contents of the input buffers with the captured configuration.
  *
  * Errors: every argument is validated before anything is enqueued; on error
  * nothing is written.  Codes 161001 / 161002 mirror ACLNN_ERR_PARAM_NULLPTR /
@@ -264,7 +271,7 @@ fa_status fa_decode_workspace_size(const fa_decode_config* cfg, uint64_t* bytes)
  * Decode.  Inputs (device, cfg->dtype): q [B, Nq, D]; k, v: the cache in
  * cfg->layout with S = max_seq_len key rows per sequence (rows at or beyond L_b
  * are never read).  Output (device): out [B, Nq, D] of cfg->dtype, fully
- * overwritten.  q, k, v, out 16-byte aligned; the workspace is caller-owned and
+ * overwritten.  q, k, v, out and the workspace 16-byte aligned; the workspace is caller-owned and
  * enqueued work uses it until it completes on `stream`.  Errors as fa_fwd:
  * FA_ERR_PARAM_NULLPTR, FA_ERR_PARAM_INVALID (limits above, misalignment),
  * FA_ERR_WORKSPACE, FA_ERR_HIP; nothing is enqueued on a validation error.

@@ -198,6 +198,9 @@ def test_atten_mask_validation():
 def test_alignment_alibi_and_workspace_rules():
     odd = ctypes.c_void_p(0x10008)
     assert _fwd(_cfg(), q=odd) == fa.FA_ERR_PARAM_INVALID
+    # the workspace is 16-byte aligned too (the plan and the TND copies are stored in 16-byte pieces)
+    assert _fwd(_cfg(), ws=odd) == fa.FA_ERR_PARAM_INVALID
+    assert _bwd(_cfg(), ws=odd) == fa.FA_ERR_PARAM_INVALID
     assert _fwd(_cfg(keep_prob=0.5), drop=ctypes.c_void_p(0x10002)) == fa.FA_ERR_PARAM_INVALID
     # ALiBi (pseType 2) needs Lq == Lkv per sequence and no empty sequence
     assert _fwd(_cfg(cu_seqlens_kv=[0, 6, 12]), slopes=FAKE) == fa.FA_ERR_PARAM_INVALID
@@ -356,6 +359,7 @@ def test_decode_validation_and_workspace():
     for key in ("q", "k", "v", "out", "ws"):
         assert _dec(_dcfg(), **{key: None}) == fa.FA_ERR_PARAM_NULLPTR, key
     assert _dec(_dcfg(), q=ctypes.c_void_p(0x10008)) == fa.FA_ERR_PARAM_INVALID   # 8-byte aligned only
+    assert _dec(_dcfg(), ws=ctypes.c_void_p(0x10008)) == fa.FA_ERR_PARAM_INVALID
     cfg = _dcfg()
     cfg.c.flags = 1
     assert _dec(cfg) == fa.FA_ERR_PARAM_INVALID
