@@ -18,7 +18,7 @@ LIB = os.path.join(PKG, "libfa.so")
 TRACE_LIB = os.path.join(PKG, "libfa_trace.so")
 TRACE_DEFINES = ("FA_TRACE_VISITS",)
 SOURCES = ["fa_api.hip", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_kv.hip", "fa_bwd_kv_atomic.hip", "fa_decode.hip",
-           "fa_layout.hip"]
+           "fa_layout.hip", "fa_large.hip"]
 # sources whose MFMA results are kept in VGPRs (see common_flags)
 VGPR_FORM_SOURCES = {s for s in os.environ.get("FA_VGPR_FORM", "fa_fwd.hip,fa_bwd.hip,fa_bwd_kv_atomic.hip,fa_decode.hip").split(",") if s}
 ARCH = "gfx950"

@@ -29,11 +29,12 @@ using fa::WorkItem;
 constexpr int64_t kMaxTokens = int64_t(1) << 20;   // T and S limits of the grad pages ("Constraints")
 constexpr int64_t kMaxBatch = 20000;               // B limit of the V5 grad page
 constexpr int64_t kMaxHeads = 256;                 // Nq limit ("Nq ranges from 1 to 256")
+constexpr int64_t kMaxHeadDim = 512;               // D limit of the grad page ("D 1-512")
 constexpr int64_t kMaxPrefixBatch = 1024;          // B limit with prefixOptional (grad page "Constraints")
 
 struct Problem {
   int64_t batch = 0, nq = 0, nkv = 0, d = 0, tq = 0, tkv = 0;
-  int64_t du = 0;                  // head dim of Q, K, dQ, dK; d is the kernels' (64 or 128, du <= d)
+  int64_t du = 0;                  // head dim of Q, K, dQ, dK; d is the kernels' (64 or 128, du <= d; du above 128)
   int64_t dvu = 0;                 // head dim of V, O, dY, dV (<= du)
   int dtype = 0, mode = 0;
   double scale = 0, keep = 1;
@@ -91,7 +92,7 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   // D <= 128 with rows of whole 16-byte chunks; the kernels run D = 64 and 128, other
   // head dims go through copies zero-padded to the next of them
   const int64_t ebytes = cfg->dtype == FA_DTYPE_FP32 ? 4 : 2;
-  if (cfg->head_dim < 1 || cfg->head_dim > 128 || (cfg->head_dim * ebytes) % 16 != 0) return FA_ERR_PARAM_INVALID;
+  if (cfg->head_dim < 1 || cfg->head_dim > kMaxHeadDim || (cfg->head_dim * ebytes) % 16 != 0) return FA_ERR_PARAM_INVALID;
   // the value head dim may be smaller (grad page, Constraints: qD == kD >= vD); 0 = the same
   const int64_t vdim = cfg->v_head_dim == 0 ? cfg->head_dim : cfg->v_head_dim;
   if (vdim < 1 || vdim > cfg->head_dim || (vdim * ebytes) % 16 != 0) return FA_ERR_PARAM_INVALID;
@@ -121,7 +122,9 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   pr->nkv = nkv;
   pr->du = cfg->head_dim;
   pr->dvu = vdim;
-  pr->d = cfg->head_dim <= 64 ? 64 : 128;
+  // the fused kernels take D = 64 or 128 (smaller head dims zero-padded); above 128 the
+  // materialised-score path (fa_large.hip) takes the head dim as it is
+  pr->d = cfg->head_dim <= 64 ? 64 : cfg->head_dim <= 128 ? 128 : cfg->head_dim;
   pr->dtype = cfg->dtype;
   pr->mode = mode;
   pr->pse_sqrt = (cfg->flags & FA_FLAG_PSE_SQRT) != 0;
@@ -135,7 +138,7 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   // variant is built for bf16, fp16 and for fp32 with D = 64 (head dims above 64 run the
   // D = 128 kernels).
   pr->deterministic = cfg->deterministic != 0 || (cfg->flags & FA_FLAG_ATOMIC_DQ) == 0 ||
-                      (cfg->dtype == FA_DTYPE_FP32 && cfg->head_dim > 64);
+                      (cfg->dtype == FA_DTYPE_FP32 && cfg->head_dim > 64) || cfg->head_dim > 128;
   const int64_t* cq = cfg->cu_seqlens_q;
   const int64_t* ck = cfg->cu_seqlens_kv;
   if (cq[0] != 0 || ck[0] != 0) return FA_ERR_PARAM_INVALID;
@@ -329,7 +332,36 @@ struct Layout {
   uint64_t total = 0;
   int64_t n_items0 = 0, n_items1 = 0;
   int n_pre_blocks = 0;
+  fa::LargePlan large{};          // head dims above 128
 };
+
+// Head dims above 128: chunks of query rows sized so that the scores of one chunk
+// (fp32 S, and dP in the backward; P~, and dS, in the input type) take at most about
+// kLargeScoreBytes of the workspace, plus the fp32 dK / dV accumulators.
+constexpr uint64_t kLargeScoreBytes = 256ull << 20;
+void large_layout(const Problem& pr, bool bwd, uint64_t* off, fa::LargePlan* P) {
+  int64_t mq = 1, mkv = 1;
+  for (int64_t b = 0; b < pr.batch; ++b) {
+    mq = std::max<int64_t>(mq, pr.cu_q[b + 1] - pr.cu_q[b]);
+    mkv = std::max<int64_t>(mkv, pr.cu_kv[b + 1] - pr.cu_kv[b]);
+  }
+  const int64_t G = pr.nq / pr.nkv, eb = pr.dtype == FA_DTYPE_FP32 ? 4 : 2;
+  const uint64_t per_row = (uint64_t)(G * mkv * (bwd ? 8 + 2 * eb : 4 + eb));
+  int64_t rows = (int64_t)(kLargeScoreBytes / per_row) / 64 * 64;
+  rows = std::min<int64_t>(std::max<int64_t>(rows, 64), (mq + 63) / 64 * 64);
+  const uint64_t sc = (uint64_t)(G * rows * mkv);
+  P->batch = (int32_t)pr.batch;
+  P->d = (int32_t)pr.d;
+  P->rows = (int32_t)rows;
+  P->off_s = *off; *off = align_up(*off + 4 * sc);
+  P->off_p = *off; *off = align_up(*off + (uint64_t)eb * sc);
+  if (bwd) {
+    P->off_dp = *off; *off = align_up(*off + 4 * sc);
+    P->off_ds = *off; *off = align_up(*off + (uint64_t)eb * sc);
+    P->off_dk = *off; *off = align_up(*off + 4 * (uint64_t)(mkv * pr.d));
+    P->off_dv = *off; *off = align_up(*off + 4 * (uint64_t)(mkv * pr.d));
+  }
+}
 
 Layout layout_fwd(const Problem& pr, int64_t n_items) {
   Layout L;
@@ -345,6 +377,7 @@ Layout layout_fwd(const Problem& pr, int64_t n_items) {
     L.mbits = off;
     off = align_up(off + 4 * (uint64_t)pr.mask_rows * pr.mask_words);
   }
+  if (pr.d > 128) large_layout(pr, false, &off, &L.large);
   if (relayout(pr)) {
     const uint64_t qb = (uint64_t)(pr.tq * pr.nq * pr.d * elem_bytes(pr));
     const uint64_t kb = (uint64_t)(pr.tkv * pr.nkv * pr.d * elem_bytes(pr));
@@ -384,6 +417,7 @@ Layout layout_bwd(const Problem& pr, int64_t n_kv_items, int64_t n_dq_items) {
     L.mbits = off;
     off = align_up(off + 4 * (uint64_t)pr.mask_rows * pr.mask_words);
   }
+  if (pr.d > 128) large_layout(pr, true, &off, &L.large);
   if (relayout(pr)) {
     const uint64_t qb = (uint64_t)(pr.tq * pr.nq * pr.d * elem_bytes(pr));
     const uint64_t kb = (uint64_t)(pr.tkv * pr.nkv * pr.d * elem_bytes(pr));
@@ -806,7 +840,14 @@ fa_status fa_fwd(const fa_config* cfg, const void* q, const void* k, const void*
     if (e != hipSuccess) return FA_ERR_HIP;
   }
   if (!attach_trace(pr, 0, 32, fa::kFwdBN, &p.trace, &p.trace_rb, &p.trace_kt)) return FA_ERR_PARAM_INVALID;
-  e = timed(K_FWD, s, [&] { return fa::launch_fwd(pr.dtype, (int)pr.d, p, s); });
+  if (pr.d > 128) {
+    fa::LargePlan lp = L.large;
+    lp.cu_q = pr.cu_q.data();
+    lp.cu_kv = pr.cu_kv.data();
+    e = timed(K_FWD, s, [&] { return fa::launch_large_fwd(pr.dtype, p, lp, ws, s); });
+  } else {
+    e = timed(K_FWD, s, [&] { return fa::launch_fwd(pr.dtype, (int)pr.d, p, s); });
+  }
   if (e == hipSuccess && copied(pr, T_O)) e = relayout_tensor(pr, T_O, ws + L.ro, out, false, s);
   return hip_status(e);
 }
@@ -910,15 +951,23 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
     e = timed(K_MASK, s, [&] {
       return fa::launch_mask_pack(pr.mask, pr.mask_rows, pr.mask_cols, reinterpret_cast<uint32_t*>(ws + L.mbits), s);
     });
-  if (e == hipSuccess) e = timed(K_PRE, s, [&] { return fa::launch_bwd_pre(dt, d, p, s); });
-  if (e == hipSuccess && !pr.deterministic)
-    e = timed(K_ZERO, s, [&] { return fa::launch_zero_f32(p.dq_acc, pr.tq * pr.nq * pr.d, s); });
-  if (e == hipSuccess) e = timed(K_KV, s, [&] { return fa::launch_bwd_kv(dt, d, !pr.deterministic, p, s); });
-  if (e == hipSuccess) {
-    if (pr.deterministic)
-      e = timed(K_DQ, s, [&] { return fa::launch_bwd_dq(dt, d, p, s); });
-    else
-      e = timed(K_CONVERT, s, [&] { return fa::launch_bwd_dq_convert(dt, d, p, s); });
+  if (pr.d > 128) {
+    // head dims above 128: preprocess, dK / dV and dQ of the materialised-score path
+    fa::LargePlan lp = L.large;
+    lp.cu_q = pr.cu_q.data();
+    lp.cu_kv = pr.cu_kv.data();
+    if (e == hipSuccess) e = timed(K_KV, s, [&] { return fa::launch_large_bwd(dt, p, lp, ws, s); });
+  } else {
+    if (e == hipSuccess) e = timed(K_PRE, s, [&] { return fa::launch_bwd_pre(dt, d, p, s); });
+    if (e == hipSuccess && !pr.deterministic)
+      e = timed(K_ZERO, s, [&] { return fa::launch_zero_f32(p.dq_acc, pr.tq * pr.nq * pr.d, s); });
+    if (e == hipSuccess) e = timed(K_KV, s, [&] { return fa::launch_bwd_kv(dt, d, !pr.deterministic, p, s); });
+    if (e == hipSuccess) {
+      if (pr.deterministic)
+        e = timed(K_DQ, s, [&] { return fa::launch_bwd_dq(dt, d, p, s); });
+      else
+        e = timed(K_CONVERT, s, [&] { return fa::launch_bwd_dq_convert(dt, d, p, s); });
+    }
   }
   if (e == hipSuccess && sink) e = timed(K_DSINK, s, [&] { return fa::launch_bwd_dsink(p, s); });
   if (e == hipSuccess && copied(pr, T_DQ)) e = relayout_tensor(pr, T_DQ, ws + L.rdq, dq, false, s);

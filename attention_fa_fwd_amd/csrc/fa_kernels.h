@@ -171,7 +171,7 @@ constexpr int kPreRowsPerBlock = 64;
 constexpr int kPseNone = 0, kPseLinear = 1, kPseSqrt = 2, kPseExt = 3;
 constexpr bool pse_slopes(int kind) { return kind == kPseLinear || kind == kPseSqrt; }
 template <typename P>
-int pse_kind(const P& p) {
+__host__ __device__ int pse_kind(const P& p) {
   if (p.pse != nullptr) return kPseExt;
   return p.slopes == nullptr ? kPseNone : (p.pse_sqrt ? kPseSqrt : kPseLinear);
 }
@@ -199,6 +199,21 @@ hipError_t with_flags(bool drop, int pse, bool mask, F&& f) {
   };
   return drop ? by_pse(std::true_type{}) : by_pse(std::false_type{});
 }
+
+// Head dims above 128 (fa_large.hip): the work of a call split into chunks of
+// `rows` query rows per (sequence, kv head), with the scores of a chunk in the
+// workspace.  cu_q / cu_kv are HOST copies of the sequence offsets; the off_* are
+// byte offsets into the workspace (fp32 S and dP, P~ and dS in the input type:
+// [group][rows][longest key range] each; fp32 dK and dV accumulators
+// [longest key range][d]).
+struct LargePlan {
+  int32_t batch, d, rows;
+  const int32_t* cu_q;
+  const int32_t* cu_kv;
+  uint64_t off_s, off_dp, off_p, off_ds, off_dk, off_dv;
+};
+hipError_t launch_large_fwd(int dtype, const FwdParams& p, const LargePlan& L, char* ws, hipStream_t s);
+hipError_t launch_large_bwd(int dtype, const BwdParams& p, const LargePlan& L, char* ws, hipStream_t s);
 
 hipError_t launch_fwd(int dtype, int d, const FwdParams& p, hipStream_t s);
 hipError_t launch_bwd_pre(int dtype, int d, const BwdParams& p, hipStream_t s);

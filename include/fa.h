@@ -108,8 +108,12 @@ typedef struct fa_config {
   const int64_t* cu_seqlens_kv;  /* HOST, B+1 entries, same rules, [B] = T_kv               */
   int64_t head_num;              /* Nq in [1, 256] (headNum)                                  */
   int64_t num_kv_heads;          /* Nkv; 0 means Nkv = Nq; Nq % Nkv == 0 (GQA)                */
-  int64_t head_dim;              /* D <= 128, D * element size a multiple of 16 bytes (64, 128
-                                    native; others zero-padded to 64 or 128 in the workspace) */
+  int64_t head_dim;              /* D <= 512 (the grad page's limit), D * element size a
+                                    multiple of 16 bytes.  64 and 128 run natively, other
+                                    D <= 128 on copies zero-padded to 64 or 128; D > 128 runs a
+                                    path that materialises one chunk of scores at a time in
+                                    the workspace (MFMA GEMMs and softmax kernels; slower,
+                                    always deterministic)                                     */
   int32_t dtype;                 /* FA_DTYPE_*                                                */
   int32_t sparse_mode;           /* FA_SPARSE_*; modes 7 and 8 take no pse tensor, and mode 7
                                     no alibi_slopes either (the grad pages' sparse_mode=7/8
@@ -191,7 +195,8 @@ typedef struct fa_config {
   int64_t v_head_dim;            /* head dim of V, O, dY and dV when it is smaller than
                                     head_dim (the grad page, Constraints: qD == kD >= vD);
                                     0 = head_dim.  Same 16-byte row rule as head_dim; Q, K,
-                                    dQ, dK keep head_dim.  Runs on zero-padded copies.         */
+                                    dQ, dK keep head_dim.  Runs on copies zero-padded to the
+                                    kernels' head dim.                                        */
 } fa_config;
 
 /* Device workspace bytes needed by fa_fwd for this configuration (>= 256). */

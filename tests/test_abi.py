@@ -64,7 +64,8 @@ def _bwd(cfg, **ptr):
 
 INVALID_CONFIGS = {
     "head_dim_100": dict(head_dim=100),      # bf16 rows of 200 bytes: not whole 16-byte chunks
-    "head_dim_136": dict(head_dim=136),
+    "head_dim_520": dict(head_dim=520),     # above the grad page's D limit of 512
+    "head_dim_260": dict(head_dim=260),     # bf16 rows of 520 bytes
     "gqa_not_divisible": dict(head_num=4, kv_heads=3),
     "too_many_heads": dict(head_num=512, kv_heads=512),
     "keep_zero": dict(keep_prob=0.0),
@@ -482,6 +483,24 @@ def test_padded_head_dims_accepted():
         assert fa.lib().fa_fwd_workspace_size(_cfg(head_dim=d, dtype=dt).ref, ctypes.byref(n)) == fa.FA_OK, d
     for d, dt in ((36, fa.FA_DTYPE_BF16), (6, fa.FA_DTYPE_FP32), (0, fa.FA_DTYPE_BF16)):
         assert fa.lib().fa_fwd_workspace_size(_cfg(head_dim=d, dtype=dt).ref, ctypes.byref(n)) == fa.FA_ERR_PARAM_INVALID, d
+
+
+def test_large_head_dims_accepted():
+    # D in (128, 512] with 16-byte rows runs the materialised-score path: its workspace holds one
+    # chunk of scores per call and grows with the head dim only through the dK / dV accumulators
+    n = ctypes.c_uint64(0)
+    sizes = {}
+    for d in (136, 192, 256, 512):
+        for dt in (fa.FA_DTYPE_BF16, fa.FA_DTYPE_FP16, fa.FA_DTYPE_FP32):
+            assert fa.lib().fa_bwd_workspace_size(_cfg(head_dim=d, dtype=dt).ref, ctypes.byref(n)) == fa.FA_OK, (d, dt)
+            assert fa.lib().fa_fwd_workspace_size(_cfg(head_dim=d, dtype=dt).ref, ctypes.byref(n)) == fa.FA_OK, (d, dt)
+        assert fa.lib().fa_bwd_workspace_size(_cfg(head_dim=d).ref, ctypes.byref(n)) == fa.FA_OK
+        sizes[d] = n.value
+    assert sizes[512] > sizes[256] > sizes[192]
+    # a narrower value head dim is accepted above 128 too (qD == kD >= vD)
+    assert fa.lib().fa_bwd_workspace_size(_cfg(head_dim=256, v_head_dim=128).ref, ctypes.byref(n)) == fa.FA_OK
+    assert fa.lib().fa_bwd_workspace_size(_cfg(head_dim=256, v_head_dim=264).ref, ctypes.byref(n)) == \
+        fa.FA_ERR_PARAM_INVALID
 
 
 def test_modes_7_8_pse_rules():
