@@ -39,15 +39,20 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(BwdParams p) {
   const int64_t npairs = rows * nq;
   const char* dyb = reinterpret_cast<const char*>(p.dy);
   const char* ob = reinterpret_cast<const char*>(p.o);
-  constexpr int U = 4;   // pairs in flight per thread
+  constexpr int U = 8;   // pairs in flight per thread
   for (int64_t pb = grp; pb < npairs; pb += GROUPS * U) {
     u32x4 av[U], cv[U];
+    float mv[U], lv[U];   // the softmax max / sum of the pair, loaded beside its rows
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int64_t pi = pb + (int64_t)u * GROUPS;
       const int64_t idx = row0 * nq + (pi < npairs ? pi : pb);
       av[u] = *reinterpret_cast<const u32x4*>(dyb + idx * (D * EB) + sub * 16);
       cv[u] = *reinterpret_cast<const u32x4*>(ob + idx * (D * EB) + sub * 16);
+      if (sub == 0) {
+        mv[u] = p.m_in[idx];
+        lv[u] = p.l_in[idx];
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -72,7 +77,7 @@ __global__ __launch_bounds__(256) void fa_bwd_pre_kernel(BwdParams p) {
 #pragma unroll
     for (int o = CPR / 2; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
     if (sub == 0) {
-      const float m = p.m_in[idx], l = p.l_in[idx];
+      const float m = mv[u], l = lv[u];
       p.delta[idx] = acc;
       p.lse[idx] = l > 0.f ? m * kLog2e + __log2f(l) : __builtin_inff();
       if (p.sink && l > 0.f) part[grp * nq + h] -= fast_exp2((p.sink[h] - m) * kLog2e) / l * acc;

@@ -163,7 +163,7 @@ constexpr int fwd_rows(bool dropout, bool fp32) { return 32 * fwd_waves(dropout,
 constexpr int kFwdBN = 64;
 constexpr int kKvBN = 128, kKvBM = 64;
 constexpr int kDqBM = 128, kDqBN = 64;
-constexpr int kPreRowsPerBlock = 64;
+constexpr int kPreRowsPerBlock = 16;   // small, so that short batches still spread over every CU
 
 // Kind of the position bias (the ALIBI template argument of the kernels): none,
 // generated pseType 2 (linear distance) or 3 (square-root distance), or an
