@@ -8,8 +8,8 @@
 // registers across the whole group (no atomics).
 //   fa_bwd_kv_kernel       one wave per 32-key group; fp32, and the atomic-dQ
 //                          variant (fa_bwd_kv_atomic.hip, MFMA results in VGPRs)
-//   fa_bwd_kv_pair_kernel  16-bit deterministic: two waves per 32-key group that
-//                          split the rows of S / dP and the columns of dK / dV
+//   fa_bwd_kv_spec_kernel  16-bit deterministic: producer waves (S, dP, softmax, dS)
+//                          beside consumer waves (dK, dV accumulation)
 // The deterministic instances (fa_bwd_kv.hip) are compiled with the compiler's
 // own MFMA register placement.
 #pragma once
@@ -586,282 +586,9 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
   }
 }
 
-// ---------------------------------------------------------------- paired waves
-// 16-bit (bf16, fp16) deterministic dK/dV with two waves per 32-key group (8 waves, two per
-// SIMD).  Wave w = 2*kg + half owns keys 32kg .. 32kg+31 of the tile:
-//   - it computes S, dP, P~ and dS for rows block `half` of each 64-row step,
-//   - the pair swaps those 16-bit P~ / dS operands through LDS, and
-//   - it accumulates dV, dK over both row blocks for d columns
-//     [half * D/2, (half + 1) * D/2).
-// So no MFMA is done twice, and each wave holds half of the dK/dV accumulators:
-// small enough for two waves per SIMD, whose VALU and MFMA work then overlap.
-template <typename E, int D, bool DROP, int ALIBI, bool MASK>
-__global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
-  using S = KvShape<E, D>;
-  using V8 = typename Vec16<E>::v8;
-  using V4 = typename Vec16<E>::v4;
-  constexpr int NW = 8;
-  constexpr int HDB = S::NDB / 2;   // d blocks (32 wide) of this wave's dK / dV half
-  constexpr int XB = 4 * 1024;      // exchange bytes per wave: P~ and dS, two operands each
-  __shared__ __attribute__((aligned(16))) char st0[S::STAGE];
-  __shared__ __attribute__((aligned(16))) char st1[S::STAGE];
-  __shared__ __attribute__((aligned(16))) char xch[NW * XB];
-  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hh = lane >> 5, lrow = lane & 31;
-  const int grp = lane >> 4, sl = lane & 15;
-  const int kg = wave >> 1, half = wave & 1;
-
-  const int item_idx = blockIdx.x / p.nkv;
-  const int gl = blockIdx.x - item_idx * p.nkv;
-  const int g = (p.nkv % 8 == 0) ? (gl & 7) * (p.nkv >> 3) + (gl >> 3) : gl;
-  const WorkItem it = p.kv_items[item_idx];
-  const int b = it.b;
-  const int q0 = p.cu_q[b], lq = p.cu_q[b + 1] - q0;
-  const int k0 = p.cu_kv[b], lkv = p.cu_kv[b + 1] - k0;
-  const FaWindow win = fa_make_window(fa_seq_mode(p.mode, b, p.nseq), p.pre, p.next, lq, lkv, p.prefix[b]);
-  const int poff = b == 0 ? p.pse_off0 : 0;   // sequence 0 of mode 8: pse row i + qStartIdx - kvStartIdx
-  const int c0 = it.tile * kKvBN;          // first key of the workgroup tile
-  const int wc0 = c0 + 32 * kg;            // first key of this wave's group
-  const int j = wc0 + lrow;                // this lane's key
-  const bool key_ok = j < lkv;
-
-  // K and V rows of the group's keys as B operands (lane = key, registers = d)
-  V8 kf[S::NOP], vf[S::NOP];
-  {
-    const int64_t kr = (int64_t)(k0 + (key_ok ? j : 0)) * p.nkv + g;
-    const E* kp = reinterpret_cast<const E*>(p.k) + kr * D;
-    const E* vp = reinterpret_cast<const E*>(p.v) + kr * D;
-#pragma unroll
-    for (int c = 0; c < S::NOP; ++c) {
-      const V8 a = *reinterpret_cast<const V8*>(kp + 16 * c + 8 * hh);
-      const V8 v = *reinterpret_cast<const V8*>(vp + 16 * c + 8 * hh);
-      kf[c] = key_ok ? a : V8{};
-      vf[c] = key_ok ? v : V8{};
-    }
-  }
-  f32x16 dk[HDB], dv[HDB];
-#pragma unroll
-  for (int db = 0; db < HDB; ++db) {
-    // zeros produced by an MFMA: the accumulators start in the MFMA register class
-    dk[db] = mfma32(V8{}, V8{}, f32x16{});
-    dv[db] = mfma32(V8{}, V8{}, f32x16{});
-  }
-
-  const int nqt = it.hi - it.lo;
-  const int nsteps = p.group * nqt;
-  const int64_t q_stride = (int64_t)p.nq * S::RB;
-  // swizzled tiles: row reads of chunk 2c + hh of row lrow (+32 for block 1),
-  // transposing reads of rows rv and rv + 8 (+16 per step), chunk 4db + qv
-  // (the row-read offset of chunk 2c + hh is qrow + 16 * ((2c + hh) ^ qsw), formed per read)
-  const int qrow = lrow * S::RB, qsw = tile_swz<S::RB>(lrow) ^ hh;
-  int toff[2][HDB];
-  {
-    const int rv = 4 * (grp >> 1) + (sl >> 2), qv = 2 * (grp & 1) + ((sl & 3) >> 1), bv = 8 * (sl & 1);
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-      for (int db = 0; db < HDB; ++db)
-        toff[hf][db] = (rv + 8 * hf) * S::RB + 16 * ((4 * (half * HDB + db) + qv) ^ tile_swz<S::RB>(rv + 8 * hf)) + bv;
-  }
-  char* const xmine = xch + wave * XB + 16 * lane;             // this lane's slots in its own exchange area
-  const char* const xpair = xch + 2 * kg * XB + 16 * lane;     // and in the pair's first one
-
-  // steps walk the query tiles from the last one down, the heads of the group
-  // innermost (every key tile of a sequence starts on the same rows together)
-  auto step_head = [&](int n) { return g * p.group + n % p.group; };
-  auto step_row0 = [&](int n) { return (it.hi - 1 - n / p.group) * kKvBM; };
-
-  auto load = [&](char* st, int n) {
-    const int h = step_head(n), r0 = step_row0(n);
-    const char* qb = reinterpret_cast<const char*>(p.q) + ((int64_t)q0 * p.nq + h) * S::RB;
-    const char* dyb = reinterpret_cast<const char*>(p.dy) + ((int64_t)q0 * p.nq + h) * S::RB;
-    dma_tile_swz<kKvBM, S::RB, NW>(st, qb, q_stride, r0, lq, wave, lane);
-    dma_tile_swz<kKvBM, S::RB, NW>(st + S::OFF_DY, dyb, q_stride, r0, lq, wave, lane);
-    if (wave < 2) {
-      // lse2 (wave 0) and D_i (wave 1) of the 64 rows, one dword per lane
-      const int rr = (r0 + lane < lq) ? r0 + lane : 0;
-      dma_dword(st + (wave == 0 ? S::OFF_LSE : S::OFF_DEL), wave == 0 ? p.lse : p.delta,
-                (uint32_t)(((int64_t)(q0 + rr) * p.nq + h) * 4));
-    }
-  };
-  // keep bits of a step: 64 rows x 128 keys = 256 words, loaded by the first 256
-  // threads and stored per key group and row
-  const int bits_slot = (tid & 3) * kKvBM + ((tid >> 2) & (kKvBM - 1));
-  auto bits_word = [&](int n) -> uint32_t {
-    const int h = step_head(n), r0 = step_row0(n);
-    const int r = (tid >> 2) & (kKvBM - 1), w = tid & 3;
-    if (tid >= 4 * kKvBM || r0 + r >= lq) return 0u;
-    const int64_t pos = p.bit_base[b] + ((int64_t)h * lq + r0 + r) * lkv + c0 + 32 * w;
-    return (uint32_t)load_mask_window(p.drop, p.drop_bytes, pos);
-  };
-  // attenMask bits (1 = masked) of a step, same slots (only with a mask)
-  auto mask_word = [&](int n) -> uint32_t {
-    const int r0 = step_row0(n);
-    const int r = (tid >> 2) & (kKvBM - 1), w = (c0 >> 5) + (tid & 3);
-    if (tid >= 4 * kKvBM || r0 + r >= lq || w >= p.mwords) return ~0u;
-    return p.mbits[(int64_t)(r0 + r) * p.mwords + w];
-  };
-
-  auto compute = [&](const char* st, int n) {
-    const int h = step_head(n), r0 = step_row0(n);
-    if (tid == 0)
-      FA_TRACE_VISIT(p.trace_kv, (((int64_t)b * p.nq + h) * p.trace_kv_rb + r0 / kKvBM) * p.trace_kv_kt + it.tile);
-    const float slope_l2 = pse_slopes(ALIBI) ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
-    const float sc = p.scale_log2;
-    const int rb = half;                     // the row block whose P~ / dS this wave forms
-    // ---- S = Q K^T, dP~ = dY V^T for rows block rb (lane = key, registers = rows) ----
-    f32x16 s = f32x16{}, dp = f32x16{};
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int c = 0; c < S::NOP; ++c) {
-      const int qo = qrow + 16 * ((2 * c) ^ qsw) + 32 * rb * S::RB;
-      const V8 qa = lds_read_b128<V8>(st + qo);
-      const V8 ya = lds_read_b128<V8>(st + S::OFF_DY + qo);
-      s = mfma32(qa, kf[c], s);
-      dp = mfma32(ya, vf[c], dp);
-    }
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
-    sched_alternate<2 * S::NOP, 0x008, 0x100>();
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- P~ and dS of the block as 16-bit A operands, stored to this wave's exchange area ----
-    const float* lse_s = reinterpret_cast<const float*>(st + S::OFF_LSE);
-    const float* del_s = reinterpret_cast<const float*>(st + S::OFF_DEL);
-    const uint32_t* bits_s = reinterpret_cast<const uint32_t*>(st + S::OFF_BITS);
-    auto elem = [&](auto full_c) {
-      constexpr bool plain = !ALIBI && decltype(full_c)::value;
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        V8 pa, da;
-#pragma unroll
-        for (int a = 2 * c; a < 2 * c + 2; ++a) {
-          const int rq = 32 * rb + 8 * a + 4 * hh;   // rows rq .. rq+3 sit in registers 4a .. 4a+3
-          const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lse_s + rq);
-          const f32x4 del4 = *reinterpret_cast<const f32x4*>(del_s + rq);
-          u32x4 bits4, mb4 = {};
-          if constexpr (DROP) bits4 = *reinterpret_cast<const u32x4*>(bits_s + kg * kKvBM + rq);
-          if constexpr (!decltype(full_c)::value && MASK)
-            mb4 = *reinterpret_cast<const u32x4*>(st + S::OFF_MBITS + 4 * (kg * kKvBM + rq));
-          const float jmi = (float)(j - r0 - rq - poff);   // j - i of register 4a (pse position); minus e for 4a + e
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 4 * a + e, i = r0 + rq + e;
-            float pr;
-            if constexpr (plain) {
-              pr = fast_exp2(__builtin_fmaf(s[r], sc, -lse4[e]));
-            } else {
-              float x = s[r] * sc;
-                  if constexpr (ALIBI == kPseExt)
-                x = __builtin_fmaf(p.pse_coef, (i < lq && key_ok) ? pse_value<E>(p, b, h, i, j, lq) : 0.f, x);
-              else if constexpr (ALIBI != 0)
-                x = add_pse<ALIBI>(x, slope_l2, jmi - (float)e);
-              if constexpr (!decltype(full_c)::value) {
-                const bool ok = (i < lq) & key_ok & (j >= fa_row_lo(win, i)) & (j <= fa_row_hi(win, i)) &
-                                !((mb4[e] >> lrow) & 1u);
-                x = ok ? x : kNegInf;
-              }
-              pr = fast_exp2(x - lse4[e]);
-            }
-            float dpv = dp[r], ptv = pr;
-            if constexpr (DROP) {
-              const bool keep = (bits4[e] >> lrow) & 1u;
-              dpv = keep ? dpv * p.inv_keep : 0.f;
-              ptv = keep ? pr * p.inv_keep : 0.f;
-            }
-            const float dsv = pr * (dpv - del4[e]);
-            pa[r & 7] = cvt16<E>(ptv);
-            da[r & 7] = cvt16<E>(dsv);
-          }
-        }
-        *reinterpret_cast<V8*>(xmine + 1024 * c) = pa;
-        *reinterpret_cast<V8*>(xmine + 1024 * (2 + c)) = da;
-      }
-    };
-    // with an attenMask every block takes the masked path
-    if (fa_tile_full(win, r0 + 32 * rb, 32, wc0, 32, lq, lkv) && !MASK) elem(std::true_type{});
-    else elem(std::false_type{});
-    __syncthreads();
-    // ---- dV += P~^T dY, dK += dS^T Q over both row blocks, this wave's d half ----
-    // (block blk's operands sit in the exchange area of wave 2kg + blk)
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const V8 pt = *reinterpret_cast<const V8*>(xpair + blk * XB + 1024 * c);
-        const V8 ds = *reinterpret_cast<const V8*>(xpair + blk * XB + 1024 * (2 + c));
-        const char* base = st + (32 * blk + 16 * c) * S::RB;
-#pragma unroll
-        for (int db = 0; db < HDB; ++db) {
-          const V8 yo = lds_read_tr_x2<V8>(base + S::OFF_DY + toff[0][db], base + S::OFF_DY + toff[1][db]);
-          const V8 qo = lds_read_tr_x2<V8>(base + toff[0][db], base + toff[1][db]);
-          dv[db] = mfma32(pt, yo, dv[db]);
-          dk[db] = mfma32(ds, qo, dk[db]);
-        }
-      }
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
-    sched_alternate<8 * HDB, 0x008, 0x100, 2>();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  if (nsteps > 0) load(st0, 0);
-  uint32_t word = 0, mword = 0;
-  if constexpr (DROP) {
-    if (nsteps > 0) word = bits_word(0);
-    if (tid < 4 * kKvBM) reinterpret_cast<uint32_t*>(st0 + S::OFF_BITS)[bits_slot] = word;
-  }
-  if (MASK && nsteps > 0 && tid < 4 * kKvBM) reinterpret_cast<uint32_t*>(st0 + S::OFF_MBITS)[bits_slot] = mask_word(0);
-  dma_wait();
-  __syncthreads();
-  for (int n = 0; n < nsteps; n += 2) {
-    if (n + 1 < nsteps) {
-      load(st1, n + 1);
-      if constexpr (DROP) word = bits_word(n + 1);
-      if constexpr (MASK) mword = mask_word(n + 1);
-    }
-    compute(st0, n);
-    if constexpr (DROP)
-      if (n + 1 < nsteps && tid < 4 * kKvBM) reinterpret_cast<uint32_t*>(st1 + S::OFF_BITS)[bits_slot] = word;
-    if (MASK && n + 1 < nsteps && tid < 4 * kKvBM) reinterpret_cast<uint32_t*>(st1 + S::OFF_MBITS)[bits_slot] = mword;
-    dma_wait();
-    __syncthreads();
-    if (n + 1 < nsteps) {
-      if (n + 2 < nsteps) {
-        load(st0, n + 2);
-        if constexpr (DROP) word = bits_word(n + 2);
-        if constexpr (MASK) mword = mask_word(n + 2);
-      }
-      compute(st1, n + 1);
-      if constexpr (DROP)
-        if (n + 2 < nsteps && tid < 4 * kKvBM) reinterpret_cast<uint32_t*>(st0 + S::OFF_BITS)[bits_slot] = word;
-      if (MASK && n + 2 < nsteps && tid < 4 * kKvBM) reinterpret_cast<uint32_t*>(st0 + S::OFF_MBITS)[bits_slot] = mword;
-      dma_wait();
-      __syncthreads();
-    }
-  }
-
-  // ---- epilogue: dK *= scale; write this wave's d half of dK, dV (lane = d, registers = keys) ----
-#pragma unroll
-  for (int db = 0; db < HDB; ++db) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int jj = wc0 + 8 * (r >> 2) + 4 * hh + (r & 3);
-      if (jj < lkv) {
-        const int64_t off = ((int64_t)(k0 + jj) * p.nkv + g) * D + 32 * (half * HDB + db) + lrow;
-        reinterpret_cast<E*>(p.dk)[off] = cvt16<E>(dk[db][r] * p.scale);
-        reinterpret_cast<E*>(p.dv)[off] = cvt16<E>(dv[db][r]);
-      }
-    }
-  }
-}
-
 // ---------------------------------------------------------------- producer / consumer waves
 // LDS operand reads issued ahead of the first MFMA of a producer / consumer matrix phase
-#ifndef FA_SPEC_READ_AHEAD_P
-#define FA_SPEC_READ_AHEAD_P 4
-#endif
-#ifndef FA_SPEC_READ_AHEAD_C
-#define FA_SPEC_READ_AHEAD_C 16
-#endif
+constexpr int kSpecReadAheadP = 4, kSpecReadAheadC = 16;
 // 16-bit deterministic dK/dV with specialised waves (8 per workgroup, one workgroup per CU).
 //   waves 0-3, producers (key group kg = wave): hold the group's K and V rows; for step
 //     t + 1 they compute S = Q K^T and dP~ = dY V^T for both 32-row blocks, then P~ and dS
@@ -872,8 +599,8 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_pair_kernel(BwdParams p) {
 //     dV += P~^T dY and dK += dS^T Q.
 // Wave w and wave w + 4 share a SIMD (checked on the device), so each SIMD runs one
 // producer (matrix work, then softmax / dS on the VALU) beside one consumer (matrix work
-// and LDS reads): the VALU work of one overlaps the matrix work of the other, where the
-// paired kernel's two waves of a SIMD ran the same phase at the same time.
+// and LDS reads): the VALU work of one overlaps the matrix work of the other (two
+// identical waves per SIMD would run the same phase at the same time).
 // Per tick: barrier A (step t's operands and tiles are in) -> consumers read the exchange
 // area -> barrier B (it may be overwritten) -> producers form step t + 1 while consumers
 // run step t.  LDS: three Q/dY stages (step t for the consumers, t + 1 for the producers,
@@ -957,7 +684,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_spec_kernel(BwdParams p) {
           s[rb] = mfma32(qa, kf[c], s[rb]);
           dp[rb] = mfma32(ya, vf[c], dp[rb]);
         }
-        __builtin_amdgcn_sched_group_barrier(0x100, FA_SPEC_READ_AHEAD_P, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, kSpecReadAheadP, 0);
         sched_alternate<2 * S::NOP, 0x008, 0x100>();
         __builtin_amdgcn_sched_barrier(0);
       };
@@ -1120,7 +847,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_spec_kernel(BwdParams p) {
             dk[db] = mfma32(ds[blk][c], qo, dk[db]);
           }
         }
-      __builtin_amdgcn_sched_group_barrier(0x100, FA_SPEC_READ_AHEAD_C, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, kSpecReadAheadC, 0);
       sched_alternate<8 * S::NDB, 0x008, 0x100, 2>();
       __builtin_amdgcn_sched_barrier(0);
     };

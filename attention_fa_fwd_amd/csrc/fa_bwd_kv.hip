@@ -15,33 +15,25 @@ static hipError_t launch_kv_t(const BwdParams& p, hipStream_t s) {
   });
 }
 
-// 16-bit dK/dV: producer / consumer waves (FA_KV_SPEC, the default) or the paired waves
-#ifndef FA_KV_SPEC
-#define FA_KV_SPEC 1
-#endif
+// 16-bit dK/dV: producer / consumer waves
 template <typename E, int D>
-static hipError_t launch_kv_pair(const BwdParams& p, hipStream_t s) {
+static hipError_t launch_kv_spec(const BwdParams& p, hipStream_t s) {
   const int64_t blocks = (int64_t)p.n_kv_items * p.nkv;
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(512);
   return with_flags(p.use_dropout != 0, pse_kind(p), p.mbits != nullptr, [&](auto dr, auto al, auto mk) {
-#if FA_KV_SPEC
     hipLaunchKernelGGL((fa_bwd_kv_spec_kernel<E, D, decltype(dr)::value, decltype(al)::value, decltype(mk)::value>),
                        grid, block, 0, s, p);
-#else
-    hipLaunchKernelGGL((fa_bwd_kv_pair_kernel<E, D, decltype(dr)::value, decltype(al)::value, decltype(mk)::value>),
-                       grid, block, 0, s, p);
-#endif
     return hipGetLastError();
   });
 }
 
 hipError_t launch_bwd_kv(int dtype, int d, bool atomic_dq, const BwdParams& p, hipStream_t s) {
   if (atomic_dq) return launch_bwd_kv_atomic(dtype, d, p, s);
-  if (dtype == 1 && d == 128) return launch_kv_pair<__bf16, 128>(p, s);
-  if (dtype == 1 && d == 64) return launch_kv_pair<__bf16, 64>(p, s);
-  if (dtype == 2 && d == 128) return launch_kv_pair<_Float16, 128>(p, s);
-  if (dtype == 2 && d == 64) return launch_kv_pair<_Float16, 64>(p, s);
+  if (dtype == 1 && d == 128) return launch_kv_spec<__bf16, 128>(p, s);
+  if (dtype == 1 && d == 64) return launch_kv_spec<__bf16, 64>(p, s);
+  if (dtype == 2 && d == 128) return launch_kv_spec<_Float16, 128>(p, s);
+  if (dtype == 2 && d == 64) return launch_kv_spec<_Float16, 64>(p, s);
   if (dtype == 0 && d == 128) return launch_kv_t<float, 128>(p, s);
   if (dtype == 0 && d == 64) return launch_kv_t<float, 64>(p, s);
   return hipErrorInvalidValue;
