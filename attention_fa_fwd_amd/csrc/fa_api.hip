@@ -336,30 +336,36 @@ struct Layout {
 };
 
 // Head dims above 128: chunks of query rows sized so that the scores of one chunk
-// (fp32 S, and dP in the backward; P~, and dS, in the input type) take at most about
-// kLargeScoreBytes of the workspace, plus the fp32 dK / dV accumulators.
-constexpr uint64_t kLargeScoreBytes = 256ull << 20;
+// (fp32 S, and dP in the backward; P~, and dS, in the input type; every query head)
+// take at most about kLargeScoreBytes of the workspace, plus the fp32 dK / dV
+// accumulators of every kv head.
+constexpr uint64_t kLargeScoreBytes = 4ull << 30;
+constexpr int64_t kLargeMinRows = 256;   // fewer rows per chunk make the contractions over rows too short
 void large_layout(const Problem& pr, bool bwd, uint64_t* off, fa::LargePlan* P) {
   int64_t mq = 1, mkv = 1;
   for (int64_t b = 0; b < pr.batch; ++b) {
     mq = std::max<int64_t>(mq, pr.cu_q[b + 1] - pr.cu_q[b]);
     mkv = std::max<int64_t>(mkv, pr.cu_kv[b + 1] - pr.cu_kv[b]);
   }
-  const int64_t G = pr.nq / pr.nkv, eb = pr.dtype == FA_DTYPE_FP32 ? 4 : 2;
-  const uint64_t per_row = (uint64_t)(G * mkv * (bwd ? 8 + 2 * eb : 4 + eb));
+  const int64_t eb = pr.dtype == FA_DTYPE_FP32 ? 4 : 2;
+  const int64_t ld = (mkv + 7) / 8 * 8;   // 16-byte rows in both element sizes
+  const uint64_t per_row = (uint64_t)(pr.nq * ld * (bwd ? 8 + 2 * eb : 4 + eb));
   int64_t rows = (int64_t)(kLargeScoreBytes / per_row) / 64 * 64;
-  rows = std::min<int64_t>(std::max<int64_t>(rows, 64), (mq + 63) / 64 * 64);
-  const uint64_t sc = (uint64_t)(G * rows * mkv);
+  rows = std::min<int64_t>(std::max<int64_t>(rows, kLargeMinRows), (mq + 63) / 64 * 64);
+  const uint64_t sc = (uint64_t)(pr.nq * rows * ld);
   P->batch = (int32_t)pr.batch;
   P->d = (int32_t)pr.d;
   P->rows = (int32_t)rows;
+  P->ld = (int32_t)ld;
+  P->acc_rows = (int32_t)mkv;
   P->off_s = *off; *off = align_up(*off + 4 * sc);
   P->off_p = *off; *off = align_up(*off + (uint64_t)eb * sc);
   if (bwd) {
+    const uint64_t acc = 4 * (uint64_t)(pr.nkv * mkv * pr.d);
     P->off_dp = *off; *off = align_up(*off + 4 * sc);
     P->off_ds = *off; *off = align_up(*off + (uint64_t)eb * sc);
-    P->off_dk = *off; *off = align_up(*off + 4 * (uint64_t)(mkv * pr.d));
-    P->off_dv = *off; *off = align_up(*off + 4 * (uint64_t)(mkv * pr.d));
+    P->off_dk = *off; *off = align_up(*off + acc);
+    P->off_dv = *off; *off = align_up(*off + acc);
   }
 }
 
@@ -844,6 +850,7 @@ fa_status fa_fwd(const fa_config* cfg, const void* q, const void* k, const void*
     fa::LargePlan lp = L.large;
     lp.cu_q = pr.cu_q.data();
     lp.cu_kv = pr.cu_kv.data();
+    lp.prefix = pr.prefix.data();
     e = timed(K_FWD, s, [&] { return fa::launch_large_fwd(pr.dtype, p, lp, ws, s); });
   } else {
     e = timed(K_FWD, s, [&] { return fa::launch_fwd(pr.dtype, (int)pr.d, p, s); });
@@ -956,6 +963,7 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
     fa::LargePlan lp = L.large;
     lp.cu_q = pr.cu_q.data();
     lp.cu_kv = pr.cu_kv.data();
+    lp.prefix = pr.prefix.data();
     if (e == hipSuccess) e = timed(K_KV, s, [&] { return fa::launch_large_bwd(dt, p, lp, ws, s); });
   } else {
     if (e == hipSuccess) e = timed(K_PRE, s, [&] { return fa::launch_bwd_pre(dt, d, p, s); });

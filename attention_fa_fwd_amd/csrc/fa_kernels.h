@@ -201,15 +201,17 @@ hipError_t with_flags(bool drop, int pse, bool mask, F&& f) {
 }
 
 // Head dims above 128 (fa_large.hip): the work of a call split into chunks of
-// `rows` query rows per (sequence, kv head), with the scores of a chunk in the
-// workspace.  cu_q / cu_kv are HOST copies of the sequence offsets; the off_* are
-// byte offsets into the workspace (fp32 S and dP, P~ and dS in the input type:
-// [group][rows][longest key range] each; fp32 dK and dV accumulators
-// [longest key range][d]).
+// `rows` query rows per sequence, every query head at once, with the scores of a
+// chunk in the workspace.  cu_q / cu_kv / prefix are HOST copies of the sequence
+// offsets and prefix lengths; the off_* are byte offsets into the workspace: fp32 S
+// and dP, P~ and dS in the input type, [Nq][rows][ld] each (ld: the longest key
+// range rounded up to 8); fp32 dK and dV accumulators [Nkv][acc_rows][d]
+// (acc_rows: the longest key range).
 struct LargePlan {
-  int32_t batch, d, rows;
+  int32_t batch, d, rows, ld, acc_rows;
   const int32_t* cu_q;
   const int32_t* cu_kv;
+  const int32_t* prefix;
   uint64_t off_s, off_dp, off_p, off_ds, off_dk, off_dv;
 };
 hipError_t launch_large_fwd(int dtype, const FwdParams& p, const LargePlan& L, char* ws, hipStream_t s);

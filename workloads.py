@@ -240,31 +240,37 @@ def workload_name(k: int, dtype: Optional[torch.dtype] = None) -> str:
     return name.replace("bf16", "fp32") if dtype == torch.float32 and k != 1 else name
 
 
-def make_workload(k: int, dtype: Optional[torch.dtype] = None) -> Case:
+def make_workload(k: int, dtype: Optional[torch.dtype] = None, head_dim: Optional[int] = None) -> Case:
     """The five fixed workloads (sizes, masks and features as listed in WORKLOAD_NAMES).
     dtype=torch.float16 (or torch.float32) draws the 16-bit workloads (2-5) in fp16
-    (fp32) instead of bf16: the same normal samples, rounded to the other type."""
+    (fp32) instead of bf16: the same normal samples, rounded to the other type.
+    head_dim replaces the D = 128 of workloads 2-5 (the same shapes otherwise)."""
     if dtype not in (None, torch.bfloat16, torch.float16, torch.float32) or (dtype == torch.float16 and k == 1):
         raise ValueError(f"workload {k} has no {dtype} variant")
+    if head_dim is not None and k == 1:
+        raise ValueError("workload 1 has a fixed head dim")
     lens = workload_lengths(k)
     dt = dict(dtype=dtype) if dtype is not None else {}
+    D = 128 if head_dim is None else int(head_dim)
     if k == 1:
         c = make_case(WORKLOAD_NAMES[1], lens, head_num=2, kv_heads=2, head_dim=64, dtype=torch.float32,
                       scale=1.0 / 8.0, seed=1)
     elif k == 2:
-        c = make_case(workload_name(2, dtype), lens, **dt, head_num=32, kv_heads=8, head_dim=128,
+        c = make_case(workload_name(2, dtype), lens, **dt, head_num=32, kv_heads=8, head_dim=D,
                       sparse_mode=MODE_RIGHT_DOWN_CAUSAL, seed=2)
     elif k == 3:
-        c = make_case(workload_name(3, dtype), lens, **dt, head_num=32, kv_heads=32, head_dim=128,
+        c = make_case(workload_name(3, dtype), lens, **dt, head_num=32, kv_heads=32, head_dim=D,
                       sparse_mode=MODE_BAND, pre_tokens=2048, next_tokens=0, seed=3, dy_mult=0.1)
     elif k == 4:
-        c = make_case(workload_name(4, dtype), lens, **dt, head_num=16, kv_heads=16, head_dim=128,
+        c = make_case(workload_name(4, dtype), lens, **dt, head_num=16, kv_heads=16, head_dim=D,
                       sparse_mode=MODE_RIGHT_DOWN_CAUSAL, keep_prob=0.9, alibi=True, seed=4)
     elif k == 5:
-        c = make_case(workload_name(5, dtype), lens, **dt, head_num=64, kv_heads=8, head_dim=128,
+        c = make_case(workload_name(5, dtype), lens, **dt, head_num=64, kv_heads=8, head_dim=D,
                       sparse_mode=MODE_RIGHT_DOWN_CAUSAL, sink=True, seed=5)
     else:
         raise ValueError(k)
+    if D != 128:
+        c.name = c.name.replace("D=128", f"D={D}")
     c.meta["workload"] = k
     return c
 
