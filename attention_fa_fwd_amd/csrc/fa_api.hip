@@ -59,6 +59,7 @@ struct Problem {
   int64_t drop_bits = 0;
   int64_t q_start = 0, kv_start = 0;   // mode 8: positions of sequence 0 in its unsplit sequence
   bool has_start = false;
+  bool large = false;   // the materialised-score path (fa_large.hip) runs the problem
 };
 
 static_assert(fa::kLayoutBNSD == FA_LAYOUT_BNSD && fa::kLayoutSBH == FA_LAYOUT_SBH, "layout codes");
@@ -180,9 +181,6 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
     pr->has_start = true;
   }
   if (cfg->pse) {
-    // the 16-bit kernels' external-pse instances are switched off: a bf16 run of them
-    // faulted on the device and the cause is not yet shown; fp32 inputs only
-    if (cfg->dtype != FA_DTYPE_FP32) return FA_ERR_PARAM_INVALID;
     int64_t max_q = 0, max_kv = 0;
     for (int64_t b = 0; b < pr->batch; ++b) {
       max_q = std::max<int64_t>(max_q, cq[b + 1] - cq[b]);
@@ -256,6 +254,10 @@ fa_status parse(const fa_config* cfg, Problem* pr) {
   }
   // the kernels have no instances of an external pse with an attenMask
   if (pr->pse && pr->mask) return FA_ERR_PARAM_INVALID;
+  // head dims above 128, and a 16-bit external pse (the fused 16-bit kernels have no
+  // instances of it), run the materialised-score path, whose backward is deterministic
+  pr->large = pr->d > 128 || (pr->pse && pr->dtype != FA_DTYPE_FP32);
+  if (pr->large) pr->deterministic = true;
   pr->drop_bits = bits;
   return FA_OK;
 }
@@ -332,10 +334,10 @@ struct Layout {
   uint64_t total = 0;
   int64_t n_items0 = 0, n_items1 = 0;
   int n_pre_blocks = 0;
-  fa::LargePlan large{};          // head dims above 128
+  fa::LargePlan large{};          // the materialised-score path
 };
 
-// Head dims above 128: chunks of query rows sized so that the scores of one chunk
+// The materialised-score path: chunks of query rows sized so that the scores of one chunk
 // (fp32 S, and dP in the backward; P~, and dS, in the input type; every query head)
 // take at most about kLargeScoreBytes of the workspace, plus the fp32 dK / dV
 // accumulators of every kv head.
@@ -383,7 +385,7 @@ Layout layout_fwd(const Problem& pr, int64_t n_items) {
     L.mbits = off;
     off = align_up(off + 4 * (uint64_t)pr.mask_rows * pr.mask_words);
   }
-  if (pr.d > 128) large_layout(pr, false, &off, &L.large);
+  if (pr.large) large_layout(pr, false, &off, &L.large);
   if (relayout(pr)) {
     const uint64_t qb = (uint64_t)(pr.tq * pr.nq * pr.d * elem_bytes(pr));
     const uint64_t kb = (uint64_t)(pr.tkv * pr.nkv * pr.d * elem_bytes(pr));
@@ -423,7 +425,7 @@ Layout layout_bwd(const Problem& pr, int64_t n_kv_items, int64_t n_dq_items) {
     L.mbits = off;
     off = align_up(off + 4 * (uint64_t)pr.mask_rows * pr.mask_words);
   }
-  if (pr.d > 128) large_layout(pr, true, &off, &L.large);
+  if (pr.large) large_layout(pr, true, &off, &L.large);
   if (relayout(pr)) {
     const uint64_t qb = (uint64_t)(pr.tq * pr.nq * pr.d * elem_bytes(pr));
     const uint64_t kb = (uint64_t)(pr.tkv * pr.nkv * pr.d * elem_bytes(pr));
@@ -846,7 +848,7 @@ fa_status fa_fwd(const fa_config* cfg, const void* q, const void* k, const void*
     if (e != hipSuccess) return FA_ERR_HIP;
   }
   if (!attach_trace(pr, 0, 32, fa::kFwdBN, &p.trace, &p.trace_rb, &p.trace_kt)) return FA_ERR_PARAM_INVALID;
-  if (pr.d > 128) {
+  if (pr.large) {
     fa::LargePlan lp = L.large;
     lp.cu_q = pr.cu_q.data();
     lp.cu_kv = pr.cu_kv.data();
@@ -958,8 +960,8 @@ fa_status fa_bwd(const fa_config* cfg, const void* q, const void* k, const void*
     e = timed(K_MASK, s, [&] {
       return fa::launch_mask_pack(pr.mask, pr.mask_rows, pr.mask_cols, reinterpret_cast<uint32_t*>(ws + L.mbits), s);
     });
-  if (pr.d > 128) {
-    // head dims above 128: preprocess, dK / dV and dQ of the materialised-score path
+  if (pr.large) {
+    // the materialised-score path: preprocess, dK / dV and dQ
     fa::LargePlan lp = L.large;
     lp.cu_q = pr.cu_q.data();
     lp.cu_kv = pr.cu_kv.data();

@@ -158,15 +158,16 @@ struct DqShape {
 // Two workgroups per CU need at most 256 registers per lane.  The 16-bit dropout
 // instances fit that with the LDS operand reads of the matrix phases kept two (not
 // four) ahead of their MFMAs and the swizzled offsets formed per use (kLean below),
-// except D = 128 with an attenMask or an external pse: those, and fp32 with
-// dropout, run one workgroup per CU rather than spill.
+// except D = 128 with an attenMask: those, and fp32 with dropout, run one
+// workgroup per CU rather than spill.
 template <typename T, int D, bool DROP, int ALIBI, bool MASK>
 constexpr int dq_occupancy() {
-  return DROP && (sizeof(T) == 4 || (D == 128 && (MASK || ALIBI == kPseExt))) ? 1 : 2;
+  return DROP && (sizeof(T) == 4 || (D == 128 && MASK)) ? 1 : 2;
 }
 
 template <typename T, int D, bool DROP, int ALIBI, bool MASK>
 __global__ __launch_bounds__(256, (dq_occupancy<T, D, DROP, ALIBI, MASK>())) void fa_bwd_dq_kernel(BwdParams p) {
+  static_assert(sizeof(T) == 4 || ALIBI != kPseExt, "a 16-bit external pse runs the materialised-score path");
   constexpr int kReadAhead = DROP ? 2 : 4;   // LDS operand reads issued before the first MFMA of a phase
   using S = DqShape<T, D>;
   using E = typename std::conditional<sizeof(T) == 2, T, __bf16>::type;   // 16-bit element type
@@ -440,7 +441,7 @@ static hipError_t launch_dq_t(const BwdParams& p, hipStream_t s) {
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(256);
   const bool drop = p.use_dropout != 0;
-  return with_flags(drop, pse_kind(p), p.mbits != nullptr, [&](auto dr, auto al, auto mk) {
+  return with_flags<sizeof(T) == 4>(drop, pse_kind(p), p.mbits != nullptr, [&](auto dr, auto al, auto mk) {
     hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, decltype(dr)::value, decltype(al)::value, decltype(mk)::value>),
                        grid, block, 0, s, p);
     return hipGetLastError();

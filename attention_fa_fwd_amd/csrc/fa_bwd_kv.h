@@ -48,6 +48,7 @@ struct KvShape {
 
 template <typename T, int D, bool ATOMIC, bool DROP, int ALIBI, bool MASK>
 __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
+  static_assert(sizeof(T) == 4 || ALIBI != kPseExt, "a 16-bit external pse runs the materialised-score path");
   using S = KvShape<T, D>;
   using E = typename std::conditional<sizeof(T) == 2, T, __bf16>::type;   // 16-bit element type
   using V8 = typename Vec16<E>::v8;
@@ -274,10 +275,7 @@ __global__ __launch_bounds__(256, 1) void fa_bwd_kv_kernel(BwdParams p) {
           pr = fast_exp2(__builtin_fmaf(s[r], sc, -lse4[e]));
         } else {
           float x = s[r] * sc;
-          if constexpr (ALIBI == kPseExt)
-            x = __builtin_fmaf(p.pse_coef, (i < lq && key_ok) ? pse_value<T>(p, b, h, i, j, lq) : 0.f, x);
-          else if constexpr (ALIBI != 0)
-            x = add_pse<ALIBI>(x, slope_l2, jmi - (float)e);
+          if constexpr (ALIBI != 0) x = add_pse<ALIBI>(x, slope_l2, jmi - (float)e);
           if constexpr (!decltype(full_c)::value) {
             const bool ok = (i < lq) & key_ok & (j >= fa_row_lo(win, i)) & (j <= fa_row_hi(win, i)) &
                             !((mb4[e] >> lrow) & 1u);
@@ -608,6 +606,7 @@ constexpr int kSpecReadAheadP = 4, kSpecReadAheadC = 16;
 // neither role's registers are live in the other's.
 template <typename E, int D, bool DROP, int ALIBI, bool MASK>
 __global__ __launch_bounds__(512, 1) void fa_bwd_kv_spec_kernel(BwdParams p) {
+  static_assert(ALIBI != kPseExt, "a 16-bit external pse runs the materialised-score path");
   using S = KvShape<E, D>;
   using V8 = typename Vec16<E>::v8;
   constexpr int XB = 4 * 1024;   // exchange bytes of one 32-row block of one key group (P~, dS: two operands each)
@@ -714,10 +713,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_spec_kernel(BwdParams p) {
                 pr = fast_exp2(__builtin_fmaf(s[rb][r], sc, -lse4[e]));
               } else {
                 float x = s[rb][r] * sc;
-                if constexpr (ALIBI == kPseExt)
-                  x = __builtin_fmaf(p.pse_coef, (i < lq && key_ok) ? pse_value<E>(p, b, h, i, j, lq) : 0.f, x);
-                else if constexpr (ALIBI != 0)
-                  x = add_pse<ALIBI>(x, slope_l2, jmi - (float)e);
+                if constexpr (ALIBI != 0) x = add_pse<ALIBI>(x, slope_l2, jmi - (float)e);
                 if constexpr (!decltype(full_c)::value) {
                   const bool ok = (i < lq) & key_ok & (j >= fa_row_lo(win, i)) & (j <= fa_row_hi(win, i)) &
                                   !((mb4[e] >> lrow) & 1u);

@@ -21,7 +21,7 @@ static hipError_t launch_kv_spec(const BwdParams& p, hipStream_t s) {
   const int64_t blocks = (int64_t)p.n_kv_items * p.nkv;
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(512);
-  return with_flags(p.use_dropout != 0, pse_kind(p), p.mbits != nullptr, [&](auto dr, auto al, auto mk) {
+  return with_flags<false>(p.use_dropout != 0, pse_kind(p), p.mbits != nullptr, [&](auto dr, auto al, auto mk) {
     hipLaunchKernelGGL((fa_bwd_kv_spec_kernel<E, D, decltype(dr)::value, decltype(al)::value, decltype(mk)::value>),
                        grid, block, 0, s, p);
     return hipGetLastError();

@@ -13,7 +13,8 @@ static hipError_t launch_kv_t(const BwdParams& p, hipStream_t s) {
   if (!kAlibi && (p.slopes != nullptr || p.pse != nullptr)) return hipErrorInvalidValue;
   // no attenMask instances: the host routes masked problems to the deterministic passes
   if (p.mbits != nullptr) return hipErrorInvalidValue;
-  return with_flags(p.use_dropout != 0, kAlibi ? pse_kind(p) : kPseNone, false, [&](auto dr, auto al, auto mk) {
+  const int pse = kAlibi ? pse_kind(p) : kPseNone;
+  return with_flags<sizeof(T) == 4>(p.use_dropout != 0, pse, false, [&](auto dr, auto al, auto mk) {
     constexpr int AL = kAlibi ? decltype(al)::value : kPseNone;
     hipLaunchKernelGGL((fa_bwd_kv_kernel<T, D, ATOMIC, decltype(dr)::value, AL, false>), grid, block, 0, s, p);
     return hipGetLastError();

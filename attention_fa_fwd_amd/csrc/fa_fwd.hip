@@ -68,6 +68,7 @@ struct RowTile {
 
 template <typename T, int D, int NW, int OCC, bool DROP, int ALIBI, bool MASK>
 __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
+  static_assert(sizeof(T) == 4 || ALIBI != kPseExt, "a 16-bit external pse runs the materialised-score path");
   using S = FwdShape<T, D>;
   constexpr int BM = 32 * NW;
   constexpr bool k16 = sizeof(T) == 2;
@@ -416,7 +417,7 @@ static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t s) {
   constexpr int NWD = fwd_waves(true, F32), NWP = fwd_waves(false, F32);
   constexpr int OCD = fwd_occupancy(true, F32), OCP = fwd_occupancy(false, F32);
   const dim3 grid((unsigned)blocks), block(64 * (drop ? NWD : NWP));
-  return with_flags(drop, pse_kind(p), p.mbits != nullptr, [&](auto dr, auto al, auto mk) {
+  return with_flags<sizeof(T) == 4>(drop, pse_kind(p), p.mbits != nullptr, [&](auto dr, auto al, auto mk) {
     constexpr bool DR = decltype(dr)::value;
     hipLaunchKernelGGL((fa_fwd_kernel<T, D, DR ? NWD : NWP, DR ? OCD : OCP, DR, decltype(al)::value,
                                       decltype(mk)::value>),

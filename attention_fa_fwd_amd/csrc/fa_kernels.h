@@ -180,8 +180,10 @@ __host__ __device__ int pse_kind(const P& p) {
 // and pse (a kPse* kind) as std::integral_constant<int, .>, so a launcher names
 // one kernel instance per combination.  An external pse together with an
 // attenMask has no instances (the heaviest of them would not fit the registers);
-// the host rejects that combination.
-template <typename F>
+// the host rejects that combination.  kExtPse = false builds no external-pse
+// instance at all (the 16-bit fused kernels: the host sends a 16-bit external pse
+// to the materialised-score path).
+template <bool kExtPse = true, typename F>
 hipError_t with_flags(bool drop, int pse, bool mask, F&& f) {
   auto by_mask = [&](auto d, auto a) -> hipError_t {
     if constexpr (decltype(a)::value == kPseExt) {
@@ -191,8 +193,11 @@ hipError_t with_flags(bool drop, int pse, bool mask, F&& f) {
       return mask ? f(d, a, std::true_type{}) : f(d, a, std::false_type{});
     }
   };
-  auto by_pse = [&](auto d) {
-    if (pse == kPseExt) return by_mask(d, std::integral_constant<int, kPseExt>{});
+  auto by_pse = [&](auto d) -> hipError_t {
+    if (pse == kPseExt) {
+      if constexpr (kExtPse) return by_mask(d, std::integral_constant<int, kPseExt>{});
+      else return hipErrorInvalidValue;
+    }
     if (pse == kPseSqrt) return by_mask(d, std::integral_constant<int, kPseSqrt>{});
     if (pse == kPseLinear) return by_mask(d, std::integral_constant<int, kPseLinear>{});
     return by_mask(d, std::integral_constant<int, kPseNone>{});

@@ -1,10 +1,12 @@
-// Head dims above 128 (up to 512): the forward and backward of
-// aclnnFlashAttentionScoreV2 / aclnnFlashAttentionUnpaddingScoreGrad ("Formula")
-// with the scores of a chunk of query rows materialised in the workspace.
+// Head dims above 128 (up to 512), and 16-bit inputs with an external pse: the
+// forward and backward of aclnnFlashAttentionScoreV2 /
+// aclnnFlashAttentionUnpaddingScoreGrad ("Formula") with the scores of a chunk of
+// query rows materialised in the workspace.
 //
 // The fused kernels keep a wave's Q (or K, V) rows and its O (or dK, dV, dQ) in
-// registers, which stops fitting beyond D = 128.  For larger head dims the path
-// runs, per (sequence, chunk of R query rows), over every query head at once
+// registers, which stops fitting beyond D = 128; their 16-bit instances have no
+// external-pse variant.  This path runs, per (sequence, chunk of R query rows),
+// over every query head at once
 // (query head h reads kv head h / G):
 //   forward   S = Q K^T (MFMA GEMM, fp32) -> masked softmax (m, l, P~ in the input
 //             type) -> O = P~ V (GEMM)

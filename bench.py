@@ -275,7 +275,8 @@ def main():
                          "decode: bf16 or fp16)")
     ap.add_argument("--pse", choices=("alibi", "full", "compressed"), default="alibi",
                     help="workload 4's bias: generated from the ALiBi slopes, or the same values passed as an "
-                         "external pse tensor, full [1, N, S, S] or 1024-row compressed [1, N, 1024, S] (fp32)")
+                         "external pse tensor of the input type, full [1, N, S, S] or 1024-row compressed "
+                         "[1, N, 1024, S] (16-bit inputs then run the materialised-score path)")
     ap.add_argument("--head-dim", type=int, default=None,
                     help="head dim of workloads 2-5 instead of 128 (above 128 the materialised-score path runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -318,9 +319,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": args.copy_calibration}), flush=True)
         return
-    # the external pse kernels take fp32 inputs; workload 4 is the one with a bias
-    if args.pse != "alibi" and (args.workload != 4 or args.dtype != "fp32" or args.layout != "TND"):
-        sys.exit("--pse full / compressed: workload 4 with --dtype fp32 in TND only")
+    # workload 4 is the one with a bias
+    if args.pse != "alibi" and (args.workload != 4 or args.layout != "TND"):
+        sys.exit("--pse full / compressed: workload 4 in TND only")
     log(f"generating workload {args.workload}")
     case = wl.make_workload(args.workload, {"fp16": torch.float16, "fp32": torch.float32}.get(args.dtype),
                             head_dim=args.head_dim)
@@ -330,6 +331,7 @@ def main():
     if args.pse != "alibi":
         s_len = int(case.lens_q[0])
         pse = alibi_pse(torch.from_numpy(case.alibi_slopes).to(dev), s_len, s_len if args.pse == "full" else 1024)
+        pse = pse.to(case.dtype)
     cfg = fa.Config(case.cu_seqlens_q, case.cu_seqlens_kv, case.head_num, case.kv_heads, case.head_dim,
                     case.dtype, case.scale, case.keep_prob, case.sparse_mode, case.pre_tokens, case.next_tokens,
                     deterministic, layout=args.layout, atomic_dq=args.atomic_dq,

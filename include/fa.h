@@ -127,7 +127,8 @@ typedef struct fa_config {
                                     either scheme: it runs the same passes (faster here than
                                     atomic accumulation), or, with FA_FLAG_ATOMIC_DQ, fp32
                                     atomic dQ in the dK/dV pass where that variant exists
-                                    (not fp32 with D > 64, nor 16-bit D = 128 with a pse)   */
+                                    (not fp32 with D > 64, D > 128, a 16-bit external pse,
+                                    nor 16-bit D = 128 with alibi_slopes)                    */
   int32_t flags;                 /* FA_FLAG_* bits; any other bit -> FA_ERR_PARAM_INVALID     */
   const int64_t* prefix;         /* HOST, B entries, read in FA_SPARSE_PREFIX only (ignored
                                     otherwise): N_b of the prefix-compressed mask
@@ -164,9 +165,10 @@ typedef struct fa_config {
                                     = alibi compression (the last 1024 rows of the full pse,
                                     Lq == Lkv and sparse mode 2 or 3 required; a row i above
                                     the stored block reads the first stored row shifted along
-                                    the diagonal).  Not with alibi_slopes or an attenMask;
-                                    FA_DTYPE_FP32 inputs only for now (16-bit inputs ->
-                                    FA_ERR_PARAM_INVALID).  NULL = none.                      */
+                                    the diagonal).  Not with alibi_slopes or an attenMask.
+                                    With bf16 / fp16 inputs the call runs the materialised-
+                                    score path (deterministic backward; its workspace holds
+                                    a chunk of scores, up to about 4 GiB).  NULL = none.      */
   int64_t pse_batch;             /* 1 (shared by the sequences) or B                          */
   int64_t pse_rows;              /* see pse                                                   */
   int64_t pse_cols;              /* S2 >= every Lkv                                           */

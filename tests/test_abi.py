@@ -439,9 +439,15 @@ def test_external_pse_validation():
     assert size(c) == fa.FA_ERR_PARAM_INVALID
     with pytest.raises(ValueError):
         _cfg(pse=_t.zeros(1, 4, 1, 7), pse_type=2)
-    # 16-bit inputs with an external pse are rejected for now
-    assert size(cfg(dtype=fa.FA_DTYPE_BF16)) == fa.FA_ERR_PARAM_INVALID
-    assert size(cfg(dtype=fa.FA_DTYPE_FP16)) == fa.FA_ERR_PARAM_INVALID
+    # 16-bit inputs with an external pse run the materialised-score path: accepted, and the
+    # workspace then holds a chunk of fp32 scores and 16-bit probabilities for every head
+    assert size(cfg()) == fa.FA_OK
+    fp32_bytes = n.value
+    for dt in (fa.FA_DTYPE_BF16, fa.FA_DTYPE_FP16):
+        assert size(cfg(dtype=dt)) == fa.FA_OK
+        c = cfg(dtype=dt)
+        heads, ld = c.c.head_num, 8   # 6 keys, rows of 16 bytes
+        assert n.value >= fp32_bytes + heads * 64 * ld * (4 + 2)
 
 
 def test_strides_validation():

@@ -28,7 +28,7 @@ def test_external_pse_tensor_is_the_generated_bias(s_len, rows):
         np.testing.assert_allclose(got[sel], want[sel], rtol=1e-6, atol=1e-6)
 
 
-@pytest.mark.parametrize("argv", [["--pse", "full"], ["--workload", "4", "--pse", "compressed"],
+@pytest.mark.parametrize("argv", [["--pse", "full"], ["--workload", "4", "--pse", "compressed", "--layout", "BSND"],
                                   ["--decode", "--dtype", "fp32"]])
 def test_refused_option_combinations(argv):
     r = subprocess.run([sys.executable, "bench.py", "--no-cpu-baseline"] + argv, cwd=ROOT, capture_output=True,
