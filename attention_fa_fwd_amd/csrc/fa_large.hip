@@ -102,6 +102,10 @@ struct TileLoad {
       }
     }
   }
+  // kfast: rows of PITCH elements, k contiguous.  Otherwise 16-bit tiles are stored as
+  // they arrive, k rows of 128 elements (256 bytes) with the XOR swizzle of the fused
+  // kernels (16-byte chunk q of row k at k * 256 + 16 * (q ^ tile_swz(k))), and read
+  // through the transposing LDS read; fp32 tiles are transposed element by element.
   __device__ static void store(T* lds, bool kfast, int tid, const T (&reg)[PER][CH]) {
 #pragma unroll
     for (int u = 0; u < PER; ++u) {
@@ -109,6 +113,10 @@ struct TileLoad {
       if (kfast) {
         const int r = c / (kGemmK / CH), k = (c % (kGemmK / CH)) * CH;
         *reinterpret_cast<u32x4*>(&lds[r * PITCH + k]) = *reinterpret_cast<const u32x4*>(&reg[u][0]);
+      } else if constexpr (sizeof(T) == 2) {
+        const int k = c / (kGemmM / CH), q = c % (kGemmM / CH);
+        char* row = reinterpret_cast<char*>(lds) + k * 256;
+        *reinterpret_cast<u32x4*>(row + 16 * (q ^ tile_swz<256>(k))) = *reinterpret_cast<const u32x4*>(&reg[u][0]);
       } else {
         const int k = c / (kGemmM / CH), r = (c % (kGemmM / CH)) * CH;
 #pragma unroll
@@ -118,12 +126,15 @@ struct TileLoad {
   }
 };
 
-template <typename Tin, typename Tout>
+// AK / BK: the A / B operand has unit stride along k (otherwise along m / n).
+template <typename Tin, typename Tout, bool AK, bool BK>
 __global__ __launch_bounds__(256) void fa_gemm_kernel(GemmDesc g) {
   constexpr int PITCH = kGemmK + 16 / (int)sizeof(Tin);   // padded k-contiguous rows
+  constexpr int TILE = kGemmM * PITCH;                    // >= kGemmK * kGemmM (the [k][row] layout)
+  static_assert(kGemmM == kGemmN && kGemmK * kGemmM <= TILE, "one tile size for both layouts");
   using L = TileLoad<Tin, PITCH>;
-  __shared__ __attribute__((aligned(16))) Tin as[2][kGemmM * PITCH];
-  __shared__ __attribute__((aligned(16))) Tin bs[2][kGemmN * PITCH];
+  __shared__ __attribute__((aligned(16))) Tin as[2][TILE];
+  __shared__ __attribute__((aligned(16))) Tin bs[2][TILE];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * kGemmN, m0 = blockIdx.y * kGemmM, z = blockIdx.z;
   // mask-window pruning of this tile
@@ -145,7 +156,7 @@ __global__ __launch_bounds__(256) void fa_gemm_kernel(GemmDesc g) {
   const int kstart = klo > 0 ? klo / kGemmK * kGemmK : 0;
   const Tin* A = reinterpret_cast<const Tin*>(g.a) + (int64_t)z * g.a_sz;
   const Tin* B = reinterpret_cast<const Tin*>(g.b) + (int64_t)(z / g.b_zdiv) * g.b_sz;
-  const bool a_kfast = g.a_sk == 1, b_kfast = g.b_sk == 1;
+  constexpr bool a_kfast = AK, b_kfast = BK;
   const int64_t a_sr = g.a_sm, b_sr = g.b_sn;   // strides of the row (m / n) dimension
   const bool vec = g.vec != 0;
   const int wm = 64 * (wave & 1), wn = 64 * (wave >> 1);
@@ -173,14 +184,29 @@ __global__ __launch_bounds__(256) void fa_gemm_kernel(GemmDesc g) {
     const Tin* bt = bs[buf];
     if constexpr (sizeof(Tin) == 2) {
       using V8 = typename Vec16<Tin>::v8;
+      // an operand of 32 rows (block rb of the 128) and 16 k, lane l holding row l % 32 and
+      // k = 8 (l / 32) .. + 7 in order: 16-byte row reads of the k-contiguous layout, or two
+      // transposing reads of the [k][row] layout.  In each 16-lane group, element e of a
+      // transposing read comes from the 8-byte piece addressed by lane 4e + i / 4 (element
+      // i % 4), so lane a addresses row k0 + a / 4 at rows 4 (a % 4) of its 16: k0 = 8 (l / 32)
+      // for the first read and k0 + 4 for the second.  (The fused kernels pair rows rv and
+      // rv + 8 instead, to match the k order of an accumulator turned operand.)
+      const int grp = lane >> 4, sl = lane & 15;
+      const int rv = 8 * (grp >> 1) + (sl >> 2), qv = 2 * (grp & 1) + ((sl & 3) >> 1), bv8 = 8 * (sl & 1);
+      auto opnd = [&](const Tin* t, bool kf, int rb, int kc) -> V8 {
+        if (kf) return *reinterpret_cast<const V8*>(&t[(32 * rb + (lane & 31)) * PITCH + 16 * kc + 8 * (lane >> 5)]);
+        const char* base = reinterpret_cast<const char*>(t) + 16 * kc * 256;
+        const int o0 = rv * 256 + 16 * ((4 * rb + qv) ^ tile_swz<256>(rv)) + bv8;
+        const int o1 = (rv + 4) * 256 + 16 * ((4 * rb + qv) ^ tile_swz<256>(rv + 4)) + bv8;
+        return lds_read_tr_x2<V8>(base + o0, base + o1);
+      };
 #pragma unroll
       for (int kc = 0; kc < kGemmK / 16; ++kc) {
-        const int kk = 16 * kc + 8 * (lane >> 5);
         V8 av[2], bv[2];
 #pragma unroll
         for (int x = 0; x < 2; ++x) {
-          av[x] = *reinterpret_cast<const V8*>(&at[(wm + 32 * x + (lane & 31)) * PITCH + kk]);
-          bv[x] = *reinterpret_cast<const V8*>(&bt[(wn + 32 * x + (lane & 31)) * PITCH + kk]);
+          av[x] = opnd(at, AK, wm / 32 + x, kc);
+          bv[x] = opnd(bt, BK, wn / 32 + x, kc);
         }
 #pragma unroll
         for (int x = 0; x < 2; ++x)
@@ -246,7 +272,11 @@ static hipError_t gemm(GemmDesc g, hipStream_t s) {
   g.vec = aligned16(g.a) && aligned16(g.b) && (an * eb) % 16 == 0 && (bn * eb) % 16 == 0 &&
           (g.a_sz * eb) % 16 == 0 && (g.b_sz * eb) % 16 == 0;
   const dim3 grid((unsigned)((g.n + kGemmN - 1) / kGemmN), (unsigned)((g.m + kGemmM - 1) / kGemmM), (unsigned)g.batch);
-  hipLaunchKernelGGL((fa_gemm_kernel<Tin, Tout>), grid, dim3(256), 0, s, g);
+  const bool ak = g.a_sk == 1, bk = g.b_sk == 1;
+  if (ak && bk) hipLaunchKernelGGL((fa_gemm_kernel<Tin, Tout, true, true>), grid, dim3(256), 0, s, g);
+  else if (ak) hipLaunchKernelGGL((fa_gemm_kernel<Tin, Tout, true, false>), grid, dim3(256), 0, s, g);
+  else if (bk) hipLaunchKernelGGL((fa_gemm_kernel<Tin, Tout, false, true>), grid, dim3(256), 0, s, g);
+  else hipLaunchKernelGGL((fa_gemm_kernel<Tin, Tout, false, false>), grid, dim3(256), 0, s, g);
   return hipGetLastError();
 }
 
