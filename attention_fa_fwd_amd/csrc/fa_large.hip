@@ -341,8 +341,31 @@ __device__ __forceinline__ void large_read_range(const FaWindow& win, const Larg
   *hi = zhi;
 }
 
+// Four consecutive entries of a score row in the input type (8 bytes for 16-bit types, 16 for fp32).
+template <typename T>
+__device__ __forceinline__ void store4(T* dst, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 2) {
+    using V4 = typename Vec16<T>::v4;
+    V4 v;
+    v[0] = cvt16<T>(a);
+    v[1] = cvt16<T>(b);
+    v[2] = cvt16<T>(c);
+    v[3] = cvt16<T>(d);
+    *reinterpret_cast<V4*>(dst) = v;
+  } else {
+    *reinterpret_cast<f32x4*>(dst) = f32x4{a, b, c, d};
+  }
+}
+
+// Score rows are read and written four entries per lane from key j0 = zlo rounded down
+// to 4 (rows are ld = a multiple of 8 entries long, so no access leaves the row); entries
+// outside the read range [zlo, zhi) are written as zeros, which nothing reads.
+constexpr int kSoftCache = 16;   // four-entry pieces per lane kept in registers: one pass over S up to 4,096 keys
+
 // Forward softmax: one wave per (head, row).  S -> P~ (input type; P / l with dropout
-// applied; 0 outside the mask, where S was not computed), softmax max / sum.
+// applied; 0 outside the mask, where S was not computed), softmax max / sum.  Rows whose
+// read range fits kSoftCache pieces per lane read S once (the logits stay in registers);
+// longer rows take three passes.
 template <typename T>
 __global__ __launch_bounds__(256) void fa_large_softmax_kernel(FwdParams p, LargeChunk c, const float* S, T* Pt) {
   const int lane = threadIdx.x & 63;
@@ -358,25 +381,79 @@ __global__ __launch_bounds__(256) void fa_large_softmax_kernel(FwdParams p, Larg
   T* prow = Pt + ((int64_t)h * c.rows + r) * c.ld;
   const float sink2 = p.sink ? p.sink[h] * kLog2e : kNegInf;
   const int wlo = max(0, fa_row_lo(win, i)), whi = min(c.lkv, fa_row_hi(win, i) + 1);   // the row's window
-  float mx = kNegInf;
-  for (int j = wlo + lane; j < whi; j += 64)
-    if (large_allowed(p, win, i, j, c.lq, c.lkv))
-      mx = fmaxf(mx, large_logit<T>(p, pse, b, h, i, j, c.lq, srow[j], slope_l2, poff));
-  mx = fmaxf(wave_max(mx), sink2);
-  const float mu = mx == kNegInf ? 0.f : mx;
-  float l = 0.f;
-  for (int j = wlo + lane; j < whi; j += 64)
-    if (large_allowed(p, win, i, j, c.lq, c.lkv))
-      l += fast_exp2(large_logit<T>(p, pse, b, h, i, j, c.lq, srow[j], slope_l2, poff) - mu);
-  l = wave_sum(l) + (p.sink ? fast_exp2(sink2 - mu) : 0.f);
-  const float inv = l > 0.f ? p.inv_keep / l : 0.f;
   int zlo, zhi;
   large_read_range(win, c, r, &zlo, &zhi);
-  for (int j = zlo + lane; j < zhi; j += 64) {
-    float v = 0.f;
-    if (large_allowed(p, win, i, j, c.lq, c.lkv) && keep_bit(p, b, h, i, j, c.lq, c.lkv))
-      v = fast_exp2(large_logit<T>(p, pse, b, h, i, j, c.lq, srow[j], slope_l2, poff) - mu) * inv;
-    prow[j] = from_f32<T>(v);
+  const int j0 = zlo & ~3;
+  // logit of key j, or -inf where the pair is not allowed (S there was not computed)
+  auto logit = [&](int j, float sv) {
+    return (j >= wlo && j < whi && large_allowed(p, win, i, j, c.lq, c.lkv))
+               ? large_logit<T>(p, pse, b, h, i, j, c.lq, sv, slope_l2, poff)
+               : kNegInf;
+  };
+  float mx, l;
+  if (zhi - j0 <= 256 * kSoftCache) {
+    f32x4 x[kSoftCache];
+    mx = kNegInf;
+#pragma unroll
+    for (int u = 0; u < kSoftCache; ++u) {
+      const int j = j0 + 4 * lane + 256 * u;
+      x[u] = f32x4{kNegInf, kNegInf, kNegInf, kNegInf};
+      if (j < zhi) {
+        const f32x4 sv = *reinterpret_cast<const f32x4*>(srow + j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[u][e] = logit(j + e, sv[e]);
+          mx = fmaxf(mx, x[u][e]);
+        }
+      }
+    }
+    mx = fmaxf(wave_max(mx), sink2);
+    const float mu = mx == kNegInf ? 0.f : mx;
+    l = 0.f;
+#pragma unroll
+    for (int u = 0; u < kSoftCache; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) l += fast_exp2(x[u][e] - mu);   // 0 for -inf
+    l = wave_sum(l) + (p.sink ? fast_exp2(sink2 - mu) : 0.f);
+    const float inv = l > 0.f ? p.inv_keep / l : 0.f;
+#pragma unroll
+    for (int u = 0; u < kSoftCache; ++u) {
+      const int j = j0 + 4 * lane + 256 * u;
+      if (j < zhi) {
+        float v[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          v[e] = (x[u][e] != kNegInf && keep_bit(p, b, h, i, j + e, c.lq, c.lkv)) ? fast_exp2(x[u][e] - mu) * inv : 0.f;
+        store4(prow + j, v[0], v[1], v[2], v[3]);
+      }
+    }
+  } else {
+    mx = kNegInf;
+    for (int j = j0 + 4 * lane; j < zhi; j += 256) {
+      const f32x4 sv = *reinterpret_cast<const f32x4*>(srow + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) mx = fmaxf(mx, logit(j + e, sv[e]));
+    }
+    mx = fmaxf(wave_max(mx), sink2);
+    const float mu = mx == kNegInf ? 0.f : mx;
+    l = 0.f;
+    for (int j = j0 + 4 * lane; j < zhi; j += 256) {
+      const f32x4 sv = *reinterpret_cast<const f32x4*>(srow + j);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) l += fast_exp2(logit(j + e, sv[e]) - mu);
+    }
+    l = wave_sum(l) + (p.sink ? fast_exp2(sink2 - mu) : 0.f);
+    const float inv = l > 0.f ? p.inv_keep / l : 0.f;
+    for (int j = j0 + 4 * lane; j < zhi; j += 256) {
+      const f32x4 sv = *reinterpret_cast<const f32x4*>(srow + j);
+      float v[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float xe = logit(j + e, sv[e]);
+        v[e] = (xe != kNegInf && keep_bit(p, b, h, i, j + e, c.lq, c.lkv)) ? fast_exp2(xe - mu) * inv : 0.f;
+      }
+      store4(prow + j, v[0], v[1], v[2], v[3]);
+    }
   }
   if (lane == 0) {
     const int64_t idx = (int64_t)(c.q0 + i) * p.nq + h;
@@ -385,9 +462,9 @@ __global__ __launch_bounds__(256) void fa_large_softmax_kernel(FwdParams p, Larg
   }
 }
 
-// Backward: one wave per (head, row).  S, dP (fp32) -> P~ and dS (input type):
-//   P = 2^(x - lse2), P~ = P z / keep, dS = P (dP z / keep - D_i); both 0 outside
-//   the mask, where S and dP were not computed.
+// Backward: one wave per (head, row), four entries per lane.  S, dP (fp32) -> P~ and dS
+// (input type): P = 2^(x - lse2), P~ = P z / keep, dS = P (dP z / keep - D_i); both 0
+// outside the mask, where S and dP were not computed.
 template <typename T>
 __global__ __launch_bounds__(256) void fa_large_ds_kernel(BwdParams p, LargeChunk c, const float* S, const float* dP,
                                                          T* Pt, T* dS) {
@@ -405,18 +482,27 @@ __global__ __launch_bounds__(256) void fa_large_ds_kernel(BwdParams p, LargeChun
   const int64_t o = ((int64_t)h * c.rows + r) * c.ld;
   int zlo, zhi;
   large_read_range(win, c, r, &zlo, &zhi);
-  for (int j = zlo + lane; j < zhi; j += 64) {
-    float pt = 0.f, ds = 0.f;
-    if (large_allowed(p, win, i, j, c.lq, c.lkv)) {
-      const float x = large_logit<T>(p, pse, b, h, i, j, c.lq, S[o + j], slope_l2, poff);
-      const float pr = fast_exp2(x - lse2);   // 0 for rows without any allowed key (lse2 = +inf)
-      const bool keep = keep_bit(p, b, h, i, j, c.lq, c.lkv);
-      const float dpv = keep ? dP[o + j] * p.inv_keep : 0.f;
-      pt = keep ? pr * p.inv_keep : 0.f;
-      ds = pr * (dpv - di);
+#pragma unroll 2
+  for (int j = (zlo & ~3) + 4 * lane; j < zhi; j += 256) {
+    const f32x4 sv = *reinterpret_cast<const f32x4*>(S + o + j);
+    const f32x4 dv = *reinterpret_cast<const f32x4*>(dP + o + j);
+    float pt[4], ds[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int jj = j + e;
+      pt[e] = 0.f;
+      ds[e] = 0.f;
+      if (jj >= zlo && jj < zhi && large_allowed(p, win, i, jj, c.lq, c.lkv)) {
+        const float x = large_logit<T>(p, pse, b, h, i, jj, c.lq, sv[e], slope_l2, poff);
+        const float pr = fast_exp2(x - lse2);   // 0 for rows without any allowed key (lse2 = +inf)
+        const bool keep = keep_bit(p, b, h, i, jj, c.lq, c.lkv);
+        const float dpv = keep ? dv[e] * p.inv_keep : 0.f;
+        pt[e] = keep ? pr * p.inv_keep : 0.f;
+        ds[e] = pr * (dpv - di);
+      }
     }
-    Pt[o + j] = from_f32<T>(pt);
-    dS[o + j] = from_f32<T>(ds);
+    store4(Pt + o + j, pt[0], pt[1], pt[2], pt[3]);
+    store4(dS + o + j, ds[0], ds[1], ds[2], ds[3]);
   }
 }
 
