@@ -35,13 +35,22 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
-    """Hash of the device-code sources (every csrc file but the host API, which holds no kernel)."""
+# Device-code sources of each path (csrc files); the shared headers belong to every path, and
+# the host API (fa_api.hip) holds no kernel.  Stored counters stay valid while their path's hash does.
+KERNEL_SOURCES = {
+    "training": ("fa_fwd.hip", "fa_bwd.hip", "fa_bwd_kv.h", "fa_bwd_kv.hip", "fa_bwd_kv_atomic.hip", "fa_layout.hip"),
+    "large": ("fa_large.hip",),
+    "decode": ("fa_decode.hip",),
+}
+SHARED_SOURCES = ("fa_device.h", "fa_kernels.h", "fa_sched.h")
+HOST_SOURCES = ("fa_api.hip",)
+
+
+def kernel_source_hash(path: str = "training") -> str:
+    """Hash of the device-code sources that the kernels of `path` are built from."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "attention_fa_fwd_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
-        if name == "fa_api.hip":
-            continue
+    for name in sorted(KERNEL_SOURCES[path] + SHARED_SOURCES):
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode())
             h.update(f.read())
@@ -233,7 +242,7 @@ def decode_bench(args):
     if os.path.exists(TRAFFIC_FILE):
         ent = json.load(open(TRAFFIC_FILE)).get("decode" + ("_fp16" if args.dtype == "fp16" else ""), {})
         ent = ent.get("fa_decode")
-        if ent and ent.get("source_hash") == kernel_source_hash():
+        if ent and ent.get("source_hash") == kernel_source_hash("decode"):
             traffic = ent.get("bytes_per_launch")
     dt_name = "fp16" if args.dtype == "fp16" else "bf16"
     res = {
@@ -401,8 +410,11 @@ def main():
     if os.path.exists(TRAFFIC_FILE):
         tf = json.load(open(TRAFFIC_FILE))
         key = f"workload{args.workload}" + ("" if args.dtype == "bf16" else "_" + args.dtype)
+        key += "" if case.head_dim == 128 else f"_d{case.head_dim}"
         ent = tf.get(key + ("" if args.pse == "alibi" else "_pse_" + args.pse), {}).get(dom)
-        if ent and ent.get("source_hash") == kernel_source_hash():
+        # head dims above 128 and a 16-bit external pse run the materialised-score path
+        path = "large" if case.head_dim > 128 or (pse is not None and case.dtype != torch.float32) else "training"
+        if ent and ent.get("source_hash") == kernel_source_hash(path):
             traffic = ent.get("bytes_per_launch")
 
     total_flops = f_fwd + f_bwd

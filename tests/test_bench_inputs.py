@@ -2,6 +2,7 @@
 `bench.py --pse full|compressed` builds from workload 4's slopes must be the bias the oracle
 generates from the same slopes (pseType 2), in both forms, on the lower triangle the causal
 mask keeps; and the option combinations the benchmark refuses exit with a message."""
+import os
 import subprocess
 import sys
 
@@ -35,3 +36,15 @@ def test_refused_option_combinations(argv):
                        text=True, timeout=300)
     assert r.returncode != 0
     assert "--pse" in r.stderr or "decode attention takes" in r.stderr
+
+
+def test_kernel_source_groups_cover_every_source():
+    # stored HBM counters are tied to a hash of their path's sources: every csrc file must
+    # belong to exactly one group, so that no kernel change goes unnoticed
+    import bench
+    csrc = os.path.join(ROOT, "attention_fa_fwd_amd", "csrc")
+    groups = [f for fs in bench.KERNEL_SOURCES.values() for f in fs] + list(bench.SHARED_SOURCES) + \
+        list(bench.HOST_SOURCES)
+    assert len(groups) == len(set(groups))
+    assert set(groups) == set(os.listdir(csrc))
+    assert len({bench.kernel_source_hash(p) for p in bench.KERNEL_SOURCES}) == len(bench.KERNEL_SOURCES)
