@@ -651,7 +651,14 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_spec_kernel(BwdParams p) {
 #pragma unroll
       for (int c = 0; c < S::NOP; ++c) {
         const V8 a = *reinterpret_cast<const V8*>(kp + 16 * c + 8 * hh);
-        const V8 v = *reinterpret_cast<const V8*>(vp + 16 * c + 8 * hh);
+        V8 v = *reinterpret_cast<const V8*>(vp + 16 * c + 8 * hh);
+        // without dropout V is held negated (sign bits flipped, exact) and the dP~ accumulator
+        // starts at D_i, so the MFMAs leave D_i - dP in it and dS = -P * acc
+        if constexpr (!DROP) {
+          auto u = __builtin_bit_cast(u32x4, v);
+          u ^= 0x80008000u;
+          v = __builtin_bit_cast(V8, u);
+        }
         kf[c] = key_ok ? a : V8{};
         vf[c] = key_ok ? v : V8{};
       }
@@ -671,9 +678,21 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_spec_kernel(BwdParams p) {
       const float slope_l2 = pse_slopes(ALIBI) ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
       const float sc = p.scale_log2;
       f32x16 s[2], dp[2];
+      const float* lse_s = reinterpret_cast<const float*>(st + S::OFF_LSE);
+      const float* del_s = reinterpret_cast<const float*>(st + S::OFF_DEL);
       auto sdp = [&](int rb) {
         s[rb] = f32x16{};
-        dp[rb] = f32x16{};
+        if constexpr (DROP) {
+          dp[rb] = f32x16{};
+        } else {
+          // registers 4a .. 4a + 3 hold rows 32rb + 8a + 4hh .. + 3
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const f32x4 d4 = *reinterpret_cast<const f32x4*>(del_s + 32 * rb + 8 * a + 4 * hh);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) dp[rb][4 * a + e] = d4[e];
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int c = 0; c < S::NOP; ++c) {
@@ -687,8 +706,6 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_spec_kernel(BwdParams p) {
         sched_alternate<2 * S::NOP, 0x008, 0x100>();
         __builtin_amdgcn_sched_barrier(0);
       };
-      const float* lse_s = reinterpret_cast<const float*>(st + S::OFF_LSE);
-      const float* del_s = reinterpret_cast<const float*>(st + S::OFF_DEL);
       const uint32_t* bits_s = reinterpret_cast<const uint32_t*>(st + S::OFF_BITS);
       auto elem = [&](auto full_c, int rb) {
         constexpr bool plain = !ALIBI && decltype(full_c)::value;
@@ -699,7 +716,8 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_spec_kernel(BwdParams p) {
           for (int a = 2 * c; a < 2 * c + 2; ++a) {
             const int rq = 32 * rb + 8 * a + 4 * hh;   // rows rq .. rq+3 sit in registers 4a .. 4a+3
             const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lse_s + rq);
-            const f32x4 del4 = *reinterpret_cast<const f32x4*>(del_s + rq);
+            f32x4 del4 = {};
+            if constexpr (DROP) del4 = *reinterpret_cast<const f32x4*>(del_s + rq);
             u32x4 bits4, mb4 = {};
             if constexpr (DROP) bits4 = *reinterpret_cast<const u32x4*>(bits_s + kg * kKvBM + rq);
             if constexpr (!decltype(full_c)::value && MASK)
@@ -721,13 +739,15 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_spec_kernel(BwdParams p) {
                 }
                 pr = fast_exp2(x - lse4[e]);
               }
-              float dpv = dp[rb][r], ptv = pr;
+              float ptv = pr, dsv;
               if constexpr (DROP) {
                 const bool keep = (bits4[e] >> lrow) & 1u;
-                dpv = keep ? dpv * p.inv_keep : 0.f;
+                const float dpv = keep ? dp[rb][r] * p.inv_keep : 0.f;
                 ptv = keep ? pr * p.inv_keep : 0.f;
+                dsv = pr * (dpv - del4[e]);
+              } else {
+                dsv = -(pr * dp[rb][r]);   // the accumulator holds D_i - dP
               }
-              const float dsv = pr * (dpv - del4[e]);
               pa[r & 7] = cvt16<E>(ptv);
               da[r & 7] = cvt16<E>(dsv);
             }
