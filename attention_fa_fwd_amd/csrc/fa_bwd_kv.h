@@ -910,4 +910,234 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_spec_kernel(BwdParams p) {
   }
 }
 
+// ---------------------------------------------------------------- 16 waves: two producers, two consumers per SIMD
+// LDS operand reads issued ahead of the first MFMA of a producer / consumer matrix phase
+constexpr int kQuadReadAheadP = 2, kQuadReadAheadC = 8;
+// 16-bit deterministic dK/dV without dropout, attenMask or pse: the workgroup and its tiles
+// are those of fa_bwd_kv_spec_kernel (one 128-key tile of one kv head, 64-row steps, three
+// Q/dY stages, one exchange area), run by 16 waves, four per SIMD (key group kg = wave % 4):
+//   wave kg      producer of row block 0 (rows 0-31 of a step),
+//   wave kg + 4  producer of row block 1 (rows 32-63),
+//     each holding K and V (negated) of the group's 32 keys; it forms S and D_i - dP of its
+//     block, then P~ and dS, and writes them to its half of the group's exchange area;
+//   wave kg + 8  consumer holding dV of the group's keys over all of D (dV += P~^T dY),
+//   wave kg + 12 consumer holding dK (dK += dS^T Q);
+//     the eight consumers issue the tile copies two steps ahead.
+// Each producer's serial chain (16 MFMAs, then the softmax / dS of 16 elements per lane) is
+// half that of a spec-kernel producer, and four waves per SIMD give the issue logic more to
+// interleave; each wave has 128 registers.  Same two barriers per tick.
+template <typename E, int D>
+__global__ __launch_bounds__(1024, 1) void fa_bwd_kv_quad_kernel(BwdParams p) {
+  using S = KvShape<E, D>;
+  using V8 = typename Vec16<E>::v8;
+  constexpr int XB = 4 * 1024;   // exchange bytes of one 32-row block of one key group (P~, dS: two operands each)
+  __shared__ __attribute__((aligned(16))) char stg[3][S::STAGE];
+  __shared__ __attribute__((aligned(16))) char xch[4 * 2 * XB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hh = lane >> 5, lrow = lane & 31;
+  const int grp = lane >> 4, sl = lane & 15;
+  const int role = wave >> 2;   // 0, 1: producer of that row block; 2: dV consumer; 3: dK consumer
+  const int kg = wave & 3;
+
+  const int item_idx = blockIdx.x / p.nkv;
+  const int gl = blockIdx.x - item_idx * p.nkv;
+  const int g = (p.nkv % 8 == 0) ? (gl & 7) * (p.nkv >> 3) + (gl >> 3) : gl;
+  const WorkItem it = p.kv_items[item_idx];
+  const int b = it.b;
+  const int q0 = p.cu_q[b], lq = p.cu_q[b + 1] - q0;
+  const int k0 = p.cu_kv[b], lkv = p.cu_kv[b + 1] - k0;
+  const FaWindow win = fa_make_window(fa_seq_mode(p.mode, b, p.nseq), p.pre, p.next, lq, lkv, p.prefix[b]);
+  const int c0 = it.tile * kKvBN;          // first key of the workgroup tile
+  const int wc0 = c0 + 32 * kg;            // first key of this wave's group
+  const int j = wc0 + lrow;                // this lane's key
+  const bool key_ok = j < lkv;
+  const int nqt = it.hi - it.lo;
+  const int nsteps = p.group * nqt;
+  const int64_t q_stride = (int64_t)p.nq * S::RB;
+  char* const xkg = xch + kg * 2 * XB + 16 * lane;   // this lane's slots in its key group's exchange area
+
+  // steps walk the query tiles from the last one down, the heads of the group innermost
+  auto step_head = [&](int n) { return g * p.group + n % p.group; };
+  auto step_row0 = [&](int n) { return (it.hi - 1 - n / p.group) * kKvBM; };
+  auto stage = [&](int n) -> char* { return stg[n % 3]; };
+
+  if (role < 2) {
+    const int rb = role;   // wave-uniform
+    // K and V rows of the group's keys as B operands (lane = key, registers = d); V negated
+    // (sign bits flipped, exact), so that the dP~ accumulator, started at D_i, ends at D_i - dP
+    V8 kf[S::NOP], vf[S::NOP];
+    {
+      const int64_t kr = (int64_t)(k0 + (key_ok ? j : 0)) * p.nkv + g;
+      const E* kp = reinterpret_cast<const E*>(p.k) + kr * D;
+      const E* vp = reinterpret_cast<const E*>(p.v) + kr * D;
+#pragma unroll
+      for (int c = 0; c < S::NOP; ++c) {
+        const V8 a = *reinterpret_cast<const V8*>(kp + 16 * c + 8 * hh);
+        auto u = __builtin_bit_cast(u32x4, *reinterpret_cast<const V8*>(vp + 16 * c + 8 * hh));
+        u ^= 0x80008000u;
+        kf[c] = key_ok ? a : V8{};
+        vf[c] = key_ok ? __builtin_bit_cast(V8, u) : V8{};
+      }
+    }
+    // row reads of chunk 2c + hh of row lrow of this row block sit at row * RB + 16 * ((2c) ^ qsw),
+    // qsw = swz(row) ^ hh; the chunk index only enters bits the row part leaves clear, so the
+    // offset is kx ^ 32c
+    const int kx = (32 * rb + lrow) * S::RB + 16 * (tile_swz<S::RB>(lrow) ^ hh);
+
+    auto produce = [&](const char* st, int n) {
+      const int h = step_head(n), r0 = step_row0(n);
+      if (tid == 0)
+        FA_TRACE_VISIT(p.trace_kv, (((int64_t)b * p.nq + h) * p.trace_kv_rb + r0 / kKvBM) * p.trace_kv_kt + it.tile);
+      const float sc = p.scale_log2;
+      const float* lse_s = reinterpret_cast<const float*>(st + S::OFF_LSE) + 32 * rb;
+      const float* del_s = reinterpret_cast<const float*>(st + S::OFF_DEL) + 32 * rb;
+      f32x16 sv = f32x16{}, dp;
+      // registers 4a .. 4a + 3 hold rows 8a + 4hh .. + 3 of the block
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(del_s + 8 * a + 4 * hh);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp[4 * a + e] = d4[e];
+      }
+      // a fresh copy of the offset base per step, so the XORs are formed per use, not kept in a table
+      int kxl = kx;
+      asm volatile("" : "+v"(kxl));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int c = 0; c < S::NOP; ++c) {
+        const int qo = kxl ^ (32 * c);
+        const V8 qa = lds_read_b128<V8>(st + qo);
+        const V8 ya = lds_read_b128<V8>(st + S::OFF_DY + qo);
+        sv = mfma32(qa, kf[c], sv);
+        dp = mfma32(ya, vf[c], dp);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x100, kQuadReadAheadP, 0);
+      sched_alternate<2 * S::NOP, 0x008, 0x100>();
+      __builtin_amdgcn_sched_barrier(0);
+      const int rr0 = r0 + 32 * rb;   // first row of the block
+      auto elem = [&](auto full_c) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          V8 pa, da;
+#pragma unroll
+          for (int a = 2 * c; a < 2 * c + 2; ++a) {
+            const int rq = 8 * a + 4 * hh;   // rows rq .. rq+3 of the block sit in registers 4a .. 4a+3
+            const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lse_s + rq);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 4 * a + e, i = rr0 + rq + e;
+              float pr;
+              if constexpr (decltype(full_c)::value) {
+                pr = fast_exp2(__builtin_fmaf(sv[r], sc, -lse4[e]));
+              } else {
+                const bool ok = (i < lq) & key_ok & (j >= fa_row_lo(win, i)) & (j <= fa_row_hi(win, i));
+                pr = fast_exp2((ok ? sv[r] * sc : kNegInf) - lse4[e]);
+              }
+              pa[r & 7] = cvt16<E>(pr);
+              da[r & 7] = cvt16<E>(-(pr * dp[r]));   // dS = P (dP - D_i)
+            }
+          }
+          *reinterpret_cast<V8*>(xkg + rb * XB + 1024 * c) = pa;
+          *reinterpret_cast<V8*>(xkg + rb * XB + 1024 * (2 + c)) = da;
+        }
+      };
+      if (fa_tile_full(win, rr0, 32, wc0, 32, lq, lkv)) elem(std::true_type{});
+      else elem(std::false_type{});
+    };
+
+    __syncthreads();   // A: stages of steps 0 and 1 are in
+    if (nsteps > 0) produce(stage(0), 0);
+    for (int t = 0; t < nsteps; ++t) {
+      __syncthreads();   // A: step t's operands and tiles are in
+      __syncthreads();   // B: the consumers have taken step t's operands
+      if (t + 1 < nsteps) produce(stage(t + 1), t + 1);
+    }
+  } else {
+    const int cw = wave - 8;            // copy slot of this consumer, 0 .. 7
+    const bool dv_role = role == 2;     // wave-uniform
+    const int y_off = dv_role ? S::OFF_DY : 0;   // B operand: dY (dV) or Q (dK)
+    const int x_off = dv_role ? 0 : 2 * 1024;    // A operand: P~ (dV) or dS (dK)
+    // transposing reads of rows rv and rv + 8 (+16 per 16-row step), chunk 4db + qv: the
+    // offset (rv + 8hf) * RB + 16 * ((4db + qv) ^ swz) + bv equals tx[hf] ^ 64db, because
+    // the chunk index enters only bits that the row and byte parts leave clear
+    int tx[2];
+    {
+      const int rv = 4 * (grp >> 1) + (sl >> 2), qv = 2 * (grp & 1) + ((sl & 3) >> 1), bv = 8 * (sl & 1);
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+        tx[hf] = (rv + 8 * hf) * S::RB + ((16 * qv) ^ (16 * tile_swz<S::RB>(rv + 8 * hf))) + bv;
+    }
+    f32x16 acc[S::NDB];
+#pragma unroll
+    for (int db = 0; db < S::NDB; ++db) acc[db] = mfma32(V8{}, V8{}, f32x16{});   // zeros in the MFMA register class
+    // the eight consumer waves copy each step's Q and dY tiles, lse2 and D_i
+    auto load = [&](char* st, int n) {
+      const int h = step_head(n), r0 = step_row0(n);
+      const char* qb = reinterpret_cast<const char*>(p.q) + ((int64_t)q0 * p.nq + h) * S::RB;
+      const char* dyb = reinterpret_cast<const char*>(p.dy) + ((int64_t)q0 * p.nq + h) * S::RB;
+      dma_tile_swz<kKvBM, S::RB, 8>(st, qb, q_stride, r0, lq, cw, lane);
+      dma_tile_swz<kKvBM, S::RB, 8>(st + S::OFF_DY, dyb, q_stride, r0, lq, cw, lane);
+      if (cw < 2) {
+        const int rr = (r0 + lane < lq) ? r0 + lane : 0;
+        dma_dword(st + (cw == 0 ? S::OFF_LSE : S::OFF_DEL), cw == 0 ? p.lse : p.delta,
+                  (uint32_t)(((int64_t)(q0 + rr) * p.nq + h) * 4));
+      }
+    };
+    // step t's A operands ([row block][c]), taken out of the exchange area
+    V8 op[2][2];
+    auto take = [&]() {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) op[blk][c] = *reinterpret_cast<const V8*>(xkg + blk * XB + x_off + 1024 * c);
+    };
+    // acc += op^T B over both row blocks and all of D
+    auto consume = [&](const char* st) {
+      int tx0 = tx[0], tx1 = tx[1];
+      asm volatile("" : "+v"(tx0), "+v"(tx1));
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const char* base = st + y_off + (32 * blk + 16 * c) * S::RB;
+#pragma unroll
+          for (int db = 0; db < S::NDB; ++db) {
+            const V8 bo = lds_read_tr_x2<V8>(base + (tx0 ^ (64 * db)), base + (tx1 ^ (64 * db)));
+            acc[db] = mfma32(op[blk][c], bo, acc[db]);
+          }
+        }
+      __builtin_amdgcn_sched_group_barrier(0x100, kQuadReadAheadC, 0);
+      sched_alternate<4 * S::NDB, 0x008, 0x100, 2>();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+      if (n < nsteps) load(stage(n), n);
+    dma_wait();
+    __syncthreads();   // A: stages of steps 0 and 1 are in
+    for (int t = 0; t < nsteps; ++t) {
+      __syncthreads();   // A: step t's operands and tiles are in
+      take();
+      __syncthreads();   // B: the producers may overwrite the exchange area
+      if (t + 2 < nsteps) load(stage(t + 2), t + 2);
+      consume(stage(t));
+      dma_wait();
+    }
+
+    // ---- epilogue: dK = scale * acc or dV = acc for the group's keys (lane = d, registers = keys) ----
+    E* out = reinterpret_cast<E*>(dv_role ? p.dv : p.dk);
+    const float f = dv_role ? 1.f : p.scale;
+#pragma unroll
+    for (int db = 0; db < S::NDB; ++db) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int jj = wc0 + 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (jj < lkv) out[((int64_t)(k0 + jj) * p.nkv + g) * D + 32 * db + lrow] = cvt16<E>(acc[db][r] * f);
+      }
+    }
+  }
+}
+
 }  // namespace fa

@@ -28,12 +28,22 @@ static hipError_t launch_kv_spec(const BwdParams& p, hipStream_t s) {
   });
 }
 
+// 16-bit dK/dV without dropout, attenMask or pse: two producers and two consumers per SIMD
+template <typename E, int D>
+static hipError_t launch_kv_16(const BwdParams& p, hipStream_t s) {
+  if (p.use_dropout != 0 || pse_kind(p) != kPseNone || p.mbits != nullptr) return launch_kv_spec<E, D>(p, s);
+  const int64_t blocks = (int64_t)p.n_kv_items * p.nkv;
+  if (blocks == 0) return hipSuccess;
+  hipLaunchKernelGGL((fa_bwd_kv_quad_kernel<E, D>), dim3((unsigned)blocks), dim3(1024), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_bwd_kv(int dtype, int d, bool atomic_dq, const BwdParams& p, hipStream_t s) {
   if (atomic_dq) return launch_bwd_kv_atomic(dtype, d, p, s);
-  if (dtype == 1 && d == 128) return launch_kv_spec<__bf16, 128>(p, s);
-  if (dtype == 1 && d == 64) return launch_kv_spec<__bf16, 64>(p, s);
-  if (dtype == 2 && d == 128) return launch_kv_spec<_Float16, 128>(p, s);
-  if (dtype == 2 && d == 64) return launch_kv_spec<_Float16, 64>(p, s);
+  if (dtype == 1 && d == 128) return launch_kv_16<__bf16, 128>(p, s);
+  if (dtype == 1 && d == 64) return launch_kv_16<__bf16, 64>(p, s);
+  if (dtype == 2 && d == 128) return launch_kv_16<_Float16, 128>(p, s);
+  if (dtype == 2 && d == 64) return launch_kv_16<_Float16, 64>(p, s);
   if (dtype == 0 && d == 128) return launch_kv_t<float, 128>(p, s);
   if (dtype == 0 && d == 64) return launch_kv_t<float, 64>(p, s);
   return hipErrorInvalidValue;
