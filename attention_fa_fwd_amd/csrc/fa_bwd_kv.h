@@ -912,7 +912,7 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_spec_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------- 16 waves: two producers, two consumers per SIMD
 // LDS operand reads issued ahead of the first MFMA of a producer / consumer matrix phase
-constexpr int kQuadReadAheadP = 2, kQuadReadAheadC = 8;
+constexpr int kQuadReadAheadP = 4, kQuadReadAheadC = 8;
 // 16-bit deterministic dK/dV without dropout, attenMask or pse: the workgroup and its tiles
 // are those of fa_bwd_kv_spec_kernel (one 128-key tile of one kv head, 64-row steps, three
 // Q/dY stages, one exchange area), run by 16 waves, four per SIMD (key group kg = wave % 4):
