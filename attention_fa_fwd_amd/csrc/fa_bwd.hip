@@ -246,10 +246,13 @@ __global__ __launch_bounds__(256, (dq_occupancy<T, D, DROP, ALIBI, MASK>())) voi
     for (int hf = 0; hf < 2; ++hf) tx[hf] = (rv + 8 * hf) * S::RB + ((16 * qv) ^ (16 * tile_swz<S::RB>(rv + 8 * hf))) + bv;
   }
 
+  // K and V tiles share their geometry and row stride: one set of lane offsets for both
+  SwzLane<kDqBN, S::kSwz ? S::RB : 256, 4> cp;
+  if constexpr (S::kSwz) cp.init(kv_stride, wave, lane);
   auto load = [&](char* st, int t) {
     if constexpr (S::kSwz) {
-      dma_tile_swz<kDqBN, S::RB, 4>(st, kbase, kv_stride, t * kDqBN, lkv, wave, lane);
-      dma_tile_swz<kDqBN, S::RB, 4>(st + S::TILE, vbase, kv_stride, t * kDqBN, lkv, wave, lane);
+      cp.copy(st, kbase, kv_stride, t * kDqBN, lkv, wave, lane);
+      cp.copy(st + S::TILE, vbase, kv_stride, t * kDqBN, lkv, wave, lane);
     } else {
       dma_rows<kDqBN, S::RB, S::P>(st, kbase, kv_stride, t * kDqBN, lkv, wave, lane);
       dma_rows<kDqBN, S::RB, S::P>(st + S::TILE, vbase, kv_stride, t * kDqBN, lkv, wave, lane);

@@ -800,13 +800,16 @@ __global__ __launch_bounds__(512, 1) void fa_bwd_kv_spec_kernel(BwdParams p) {
       dk[db] = mfma32(V8{}, V8{}, f32x16{});
       dv[db] = mfma32(V8{}, V8{}, f32x16{});
     }
-    // the four consumer waves copy each step's Q and dY tiles, lse2 and D_i
+    // the four consumer waves copy each step's Q and dY tiles (one set of lane offsets for
+    // both: same geometry and row stride), lse2 and D_i
+    SwzLane<kKvBM, S::RB, 4> cp;
+    cp.init(q_stride, cw, lane);
     auto load = [&](char* st, int n) {
       const int h = step_head(n), r0 = step_row0(n);
       const char* qb = reinterpret_cast<const char*>(p.q) + ((int64_t)q0 * p.nq + h) * S::RB;
       const char* dyb = reinterpret_cast<const char*>(p.dy) + ((int64_t)q0 * p.nq + h) * S::RB;
-      dma_tile_swz<kKvBM, S::RB, 4>(st, qb, q_stride, r0, lq, cw, lane);
-      dma_tile_swz<kKvBM, S::RB, 4>(st + S::OFF_DY, dyb, q_stride, r0, lq, cw, lane);
+      cp.copy(st, qb, q_stride, r0, lq, cw, lane);
+      cp.copy(st + S::OFF_DY, dyb, q_stride, r0, lq, cw, lane);
       if (cw < 2) {
         const int rr = (r0 + lane < lq) ? r0 + lane : 0;
         dma_dword(st + (cw == 0 ? S::OFF_LSE : S::OFF_DEL), cw == 0 ? p.lse : p.delta,
@@ -979,6 +982,11 @@ __global__ __launch_bounds__(1024, 1) void fa_bwd_kv_quad_kernel(BwdParams p) {
         vf[c] = key_ok ? __builtin_bit_cast(V8, u) : V8{};
       }
     }
+    // rows [i_lo, i_hi] of the sequence may see this lane's key j (j <= hi(i) holds for every row
+    // when j <= floor, else from row j - delta - next on; j >= lo(i) up to row j - delta + pre); an
+    // empty range for a key past the end, so the masked path tests a row with two compares
+    const int i_lo = j <= win.floor ? 0 : j - win.delta - win.next;
+    const int i_hi = key_ok ? min(j - win.delta + win.pre, lq - 1) : -1;
     // row reads of chunk 2c + hh of row lrow of this row block sit at row * RB + 16 * ((2c) ^ qsw),
     // qsw = swz(row) ^ hh; the chunk index only enters bits the row part leaves clear, so the
     // offset is kx ^ 32c
@@ -1030,7 +1038,7 @@ __global__ __launch_bounds__(1024, 1) void fa_bwd_kv_quad_kernel(BwdParams p) {
               if constexpr (decltype(full_c)::value) {
                 pr = fast_exp2(__builtin_fmaf(sv[r], sc, -lse4[e]));
               } else {
-                const bool ok = (i < lq) & key_ok & (j >= fa_row_lo(win, i)) & (j <= fa_row_hi(win, i));
+                const bool ok = (i >= i_lo) & (i <= i_hi);
                 pr = fast_exp2((ok ? sv[r] * sc : kNegInf) - lse4[e]);
               }
               pa[r & 7] = cvt16<E>(pr);
@@ -1070,13 +1078,16 @@ __global__ __launch_bounds__(1024, 1) void fa_bwd_kv_quad_kernel(BwdParams p) {
     f32x16 acc[S::NDB];
 #pragma unroll
     for (int db = 0; db < S::NDB; ++db) acc[db] = mfma32(V8{}, V8{}, f32x16{});   // zeros in the MFMA register class
-    // the eight consumer waves copy each step's Q and dY tiles, lse2 and D_i
+    // the eight consumer waves copy each step's Q and dY tiles (one set of lane offsets for
+    // both: same geometry and row stride), lse2 and D_i
+    SwzLane<kKvBM, S::RB, 8> cp;
+    cp.init(q_stride, cw, lane);
     auto load = [&](char* st, int n) {
       const int h = step_head(n), r0 = step_row0(n);
       const char* qb = reinterpret_cast<const char*>(p.q) + ((int64_t)q0 * p.nq + h) * S::RB;
       const char* dyb = reinterpret_cast<const char*>(p.dy) + ((int64_t)q0 * p.nq + h) * S::RB;
-      dma_tile_swz<kKvBM, S::RB, 8>(st, qb, q_stride, r0, lq, cw, lane);
-      dma_tile_swz<kKvBM, S::RB, 8>(st + S::OFF_DY, dyb, q_stride, r0, lq, cw, lane);
+      cp.copy(st, qb, q_stride, r0, lq, cw, lane);
+      cp.copy(st + S::OFF_DY, dyb, q_stride, r0, lq, cw, lane);
       if (cw < 2) {
         const int rr = (r0 + lane < lq) ? r0 + lane : 0;
         dma_dword(st + (cw == 0 ? S::OFF_LSE : S::OFF_DEL), cw == 0 ? p.lse : p.delta,

@@ -299,6 +299,36 @@ __device__ __forceinline__ void dma_tile_swz(char* lds, const char* gbase, int64
   }
 }
 
+// The same copies with the lane offsets of a whole valid tile formed once (SwzLane::init),
+// outside the caller's tile loop: a tile whose rows are all below `valid` issues its copies
+// with them directly; the sequence's last, partial tile takes the clamped offsets above.
+template <int ROWS, int RB, int NW>
+struct SwzLane {
+  static constexpr int RPI = 1024 / RB, CPR = RB / 16, IPW = ROWS / RPI / NW;
+  uint32_t voff[IPW];
+  __device__ __forceinline__ void init(int64_t gstride, int wave, int lane) {
+    const int w = __builtin_amdgcn_readfirstlane(wave);
+    const int lr = lane / CPR, slot = lane % CPR;
+#pragma unroll
+    for (int k = 0; k < IPW; ++k) {
+      const int r = (w * IPW + k) * RPI + lr;
+      voff[k] = (uint32_t)r * (uint32_t)gstride + 16u * (uint32_t)(slot ^ tile_swz<RB>(r));
+    }
+  }
+  __device__ __forceinline__ void copy(char* lds, const char* gbase, int64_t gstride, int row0, int valid, int wave,
+                                       int lane) const {
+    const int w = __builtin_amdgcn_readfirstlane(wave);
+    const int r0 = __builtin_amdgcn_readfirstlane(row0);
+    if (__builtin_amdgcn_readfirstlane(valid) - r0 >= ROWS) {
+      const char* src = gbase + (int64_t)r0 * gstride;
+#pragma unroll
+      for (int k = 0; k < IPW; ++k) dma_x4(lds + (w * IPW + k) * 1024, src, voff[k]);
+    } else {
+      dma_tile_swz<ROWS, RB, NW>(lds, gbase, gstride, row0, valid, wave, lane);
+    }
+  }
+};
+
 // Same tile layout as dma_rows, copied through registers (global load, then LDS
 // store) so that no copy is in flight once it returns.  Used by kernels that may
 // keep scratch spills, which must never coexist with in-flight LDS DMA.

@@ -123,6 +123,10 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
     }
   }
 
+  // keys [j_lo, j_hi] of this lane's row are inside the window and the sequence (an empty
+  // range for a row past the end), so the masked path tests a key with two compares
+  const int j_lo = fa_row_lo(win, i);
+  const int j_hi = row_ok ? min(fa_row_hi(win, i), lkv - 1) : j_lo - 1;
   const float slope_l2 = pse_slopes(ALIBI) ? p.slopes[b * p.slope_bstride + h] * kLog2e : 0.f;
   // generated pse on positions in the unsplit sequence: sequence 0 of mode 8 starts qStartIdx -
   // kvStartIdx rows after its keys, so its bias uses j - (i + poff)
@@ -237,9 +241,16 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
             x = __builtin_fmaf(p.pse_coef, (row_ok && j < lkv) ? pse_value<T>(p, b, h, i, j, lq) : 0.f, x);
           else if constexpr (ALIBI != 0)
             x = add_pse<ALIBI>(x, slope_l2, (float)(j - i - poff));
-          if (!decltype(full_c)::value &&
-              (!fa_allowed(win, i, j, lq, lkv) || (MASK && ((rt.mw[kb] >> (8 * (r >> 2) + 4 * hh + (r & 3))) & 1u))))
-            x = kNegInf;
+          if constexpr (DROP) {
+            // (the dropout instances keep the short-circuit form: the bounds would cost them registers)
+            if (!decltype(full_c)::value &&
+                (!fa_allowed(win, i, j, lq, lkv) || (MASK && ((rt.mw[kb] >> (8 * (r >> 2) + 4 * hh + (r & 3))) & 1u))))
+              x = kNegInf;
+          } else if constexpr (!decltype(full_c)::value) {
+            bool ok = (j >= j_lo) & (j <= j_hi);
+            if constexpr (MASK) ok &= !((rt.mw[kb] >> (8 * (r >> 2) + 4 * hh + (r & 3))) & 1u);
+            x = ok ? x : kNegInf;
+          }
           s[kb][r] = x;
           mt = fmaxf(mt, x);
         }
@@ -323,12 +334,15 @@ __global__ __launch_bounds__(64 * NW, OCC) void fa_fwd_kernel(FwdParams p) {
     pv(vs, s);
   };
 
+  // K and V tiles share their geometry and row stride, so one set of lane offsets serves both
+  SwzLane<kFwdBN, S::kSwz ? S::RB : 256, NW> cp;
+  if constexpr (S::kSwz) cp.init(kv_stride, wave, lane);
   auto load_k = [&](char* dst, int t) {
-    if constexpr (S::kSwz) dma_tile_swz<kFwdBN, S::RB, NW>(dst, kbase, kv_stride, t * kFwdBN, lkv, wave, lane);
+    if constexpr (S::kSwz) cp.copy(dst, kbase, kv_stride, t * kFwdBN, lkv, wave, lane);
     else dma_rows<kFwdBN, S::RB, S::KP, NW>(dst, kbase, kv_stride, t * kFwdBN, lkv, wave, lane);
   };
   auto load_v = [&](char* dst, int t) {
-    if constexpr (S::kSwz) dma_tile_swz<kFwdBN, S::RB, NW>(dst, vbase, kv_stride, t * kFwdBN, lkv, wave, lane);
+    if constexpr (S::kSwz) cp.copy(dst, vbase, kv_stride, t * kFwdBN, lkv, wave, lane);
     else dma_rows<kFwdBN, S::RB, S::VP, NW>(dst, vbase, kv_stride, t * kFwdBN, lkv, wave, lane);
   };
 
